@@ -1,0 +1,12 @@
+"""CPU oracle for jagged flash attention (float64 NumPy).
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's
+CPU-baseline leg may import it; the library (variable_length_flash_jaggedfa_amd)
+never imports, links or runs anything in here, and the oracle imports nothing
+from the library. The two share only the seeded input generator (jfa_inputs),
+which holds no attention arithmetic.
+
+  attention.py     exact softmax attention and its gradients, per sequence
+  schedule_ref.py  the KV-work-sorted zigzag tile deal, in plain integers
+"""
+from . import attention, schedule_ref  # noqa: F401

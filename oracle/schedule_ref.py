@@ -1,0 +1,88 @@
+"""Reference tile scheduler in plain Python integers.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+Follows the host load balancer of "Jagged Flash Attention for GEM" (section on
+GEM-specific optimisations): every tile is given its KV work, the tiles are sorted
+by that work in descending order, and they are dealt over the compute units in a
+zigzag: pass 0 fills slots left to right, pass 1 right to left, and so on.
+
+Readings of what the page leaves open:
+  * A tile is one block of query rows of one (sequence, head) for the forward,
+    one block of key rows for the backward.
+  * Work of a forward tile = number of keys it visits: L, or with causal
+    min(L, (t+1)*BM). Broadcast-Q forward tiles visit the L_b keys of their
+    sequence.
+  * Work of a backward tile = number of query rows that attend its keys: L, or
+    with causal L - n*BN. Broadcast-Q backward tiles see all Lq query rows.
+  * Ties keep generation order (sequence, then head, then tile); the sort is stable.
+  * Passes are counted from 0; pass 0 runs from slot 0 upward.
+  * "In-order" dispatch deals tiles in generation order round-robin: tile j goes
+    to slot j mod S.
+Output: slot_ptr [S+1] and tiles [N,4] = (b, h, t, work), grouped by slot, in the
+order each slot received them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+KIND_FWD, KIND_BWD = 0, 1
+ORDER_INORDER, ORDER_ZIGZAG = 0, 1
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0):
+    """All tiles in generation order: list of (b, h, t, work)."""
+    out = []
+    for b, L in enumerate(int(x) for x in lengths):
+        for h in range(num_heads):
+            if kind == KIND_FWD:
+                if lq:
+                    for t in range(ceil_div(lq, tile_rows)):
+                        out.append((b, h, t, L))
+                else:
+                    for t in range(ceil_div(L, tile_rows)):
+                        work = min(L, (t + 1) * tile_rows) if causal else L
+                        out.append((b, h, t, work))
+            else:
+                for n in range(ceil_div(L, tile_rows)):
+                    if lq:
+                        work = lq
+                    else:
+                        work = L - n * tile_rows if causal else L
+                    out.append((b, h, n, work))
+    return out
+
+
+def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0):
+    tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq)
+    if order == ORDER_ZIGZAG:
+        idx = sorted(range(len(tiles)), key=lambda g: (-tiles[g][3], g))
+    else:
+        idx = list(range(len(tiles)))
+    per_slot = [[] for _ in range(num_slots)]
+    for j, g in enumerate(idx):
+        p, r = divmod(j, num_slots)
+        if order == ORDER_ZIGZAG and p % 2 == 1:
+            slot = num_slots - 1 - r
+        else:
+            slot = r
+        per_slot[slot].append(tiles[g])
+    slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+    flat = []
+    for s in range(num_slots):
+        flat.extend(per_slot[s])
+        slot_ptr[s + 1] = len(flat)
+    arr = np.asarray(flat, dtype=np.int32).reshape(-1, 4)
+    return slot_ptr, arr
+
+
+def slot_loads(slot_ptr, tiles, cost=lambda work: work):
+    """Sum of per-tile cost in every slot."""
+    loads = []
+    for s in range(len(slot_ptr) - 1):
+        loads.append(sum(cost(int(w)) for w in tiles[slot_ptr[s]:slot_ptr[s + 1], 3]))
+    return loads

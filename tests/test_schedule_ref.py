@@ -1,0 +1,72 @@
+"""Pins of the reference tile scheduler: hand-worked examples of the page's rule
+(tests/golden/schedule_examples.json) and properties any correct deal has."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import jfa_inputs as J
+from oracle import schedule_ref as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_examples.json")
+
+
+def _per_slot(slot_ptr, tiles):
+    return [tiles[slot_ptr[s]:slot_ptr[s + 1]].tolist() for s in range(len(slot_ptr) - 1)]
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_golden(case):
+    kind = R.KIND_FWD if case["kind"] == "fwd" else R.KIND_BWD
+    for order, key in ((R.ORDER_ZIGZAG, "zigzag"), (R.ORDER_INORDER, "inorder")):
+        sp, t = R.schedule(case["lengths"], case["heads"], kind, case["tile_rows"], order,
+                           case["slots"], causal=case["causal"])
+        assert _per_slot(sp, t) == case[key]
+        assert R.slot_loads(sp, t) == case[key + "_loads"]
+
+
+def _tiles_expected(L, H, kind, rows, causal, lq):
+    n = 0
+    for x in L:
+        if kind == R.KIND_FWD:
+            n += H * R.ceil_div(lq if lq else x, rows)
+        else:
+            n += H * R.ceil_div(x, rows)
+    return n
+
+
+@pytest.mark.parametrize("name", ["tiny", "gem", "gem_causal", "broadcast", "imbalance"])
+@pytest.mark.parametrize("kind", [R.KIND_FWD, R.KIND_BWD])
+def test_properties(name, kind):
+    w = J.standard_workloads()[name]
+    L = J.lengths(w)
+    H = 2 if name == "imbalance" else w.num_heads   # keep the pure-Python run short
+    rows = 128
+    S = 256
+    sp_z, tz = R.schedule(L, H, kind, rows, R.ORDER_ZIGZAG, S, w.causal, w.lq)
+    sp_i, ti = R.schedule(L, H, kind, rows, R.ORDER_INORDER, S, w.causal, w.lq)
+    n = _tiles_expected(L, H, kind, rows, w.causal, w.lq)
+    assert len(tz) == len(ti) == n
+    # every tile exactly once, in both orders
+    key = lambda a: sorted(map(tuple, a.tolist()))
+    assert key(tz) == key(ti)
+    assert len(set(map(tuple, tz[:, :3].tolist()))) == n
+    counts = np.diff(sp_z)
+    assert counts.max() - counts.min() <= 1
+    # zigzag: each slot's list is non-increasing in work
+    for s in range(S):
+        wk = tz[sp_z[s]:sp_z[s + 1], 3]
+        assert np.all(np.diff(wk) <= 0)
+    loads = np.array(R.slot_loads(sp_z, tz))
+    assert loads.max() <= loads.mean() + tz[:, 3].max()
+    # zigzag never has a worse makespan than round-robin on these workloads
+    assert loads.max() <= max(R.slot_loads(sp_i, ti))
+
+
+def test_empty_and_zero_length():
+    sp, t = R.schedule([0, 0], 3, R.KIND_FWD, 64, R.ORDER_ZIGZAG, 4)
+    assert t.shape == (0, 4) and list(sp) == [0] * 5
+    # broadcast-Q forward keeps tiles of empty sequences (they write zeros)
+    sp, t = R.schedule([0], 1, R.KIND_FWD, 64, R.ORDER_ZIGZAG, 2, lq=100)
+    assert t.tolist() == [[0, 0, 0, 0], [0, 0, 1, 0]]
