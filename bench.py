@@ -1,0 +1,272 @@
+"""Benchmark of the jagged flash attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gem] [--order zigzag]
+                    [--compare-orders] [--no-cpu-baseline]
+
+A step is one forward and one backward pass of every variant of the workload
+over the same device-resident synthetic batch (default: the GEM-like jagged
+workload, B=256 sequences with log-uniform lengths in [16, 4096], H=8, D=128,
+non-causal and causal). The tile schedules are built on the host once per batch,
+before the timed region, and their build time is reported separately.
+
+Prints ONE JSON line: throughput in TFLOP/s counting only unpadded FLOPs
+(forward 4*N*H*D, backward 10*N*H*D, N = attended (query, key) pairs), the
+fraction of the bf16 dense MFMA peak, a roofline entry for the dominant pass and
+the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import jfa_inputs as J  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def pairs_of(lengths, causal=False, lq=0, block=0):
+    L = np.asarray(lengths, dtype=np.int64)
+    if block:
+        return int(block * L.sum())
+    if lq:
+        return int(lq * L.sum())
+    if causal:
+        return int((L * (L + 1) // 2).sum())
+    return int((L * L).sum())
+
+
+def variants_of(name):
+    wl = J.standard_workloads()
+    if name == "gem":
+        return [wl["gem"], wl["gem_causal"]]
+    return [wl[name]]
+
+
+def flags_of(w, jfa):
+    f = 0
+    if w.causal:
+        f |= jfa.CAUSAL
+    if w.kind == "broadcast":
+        f |= jfa.BROADCAST_Q
+    if w.kind == "block64":
+        f |= jfa.BLOCK_DIAG64
+    return f
+
+
+def cpu_baseline(case, variants, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of (sequence, head) units."""
+    import threadpoolctl
+    from oracle import attention as A
+    w0 = variants[0]
+    off = case.offsets.astype(np.int64)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(case.lengths))
+    flops = 0.0
+    units = 0
+    t0 = time.perf_counter()
+    f = J.bf16_bits_to_f64
+    for b in order:
+        for w in variants:
+            h = int(rng.integers(w0.num_heads))
+            s, e = int(off[b]), int(off[b + 1])
+            k_, v_ = f(case.k[s:e, h]), f(case.v[s:e, h])
+            if w.kind == "broadcast":
+                q_, do_ = f(case.q[:, h]), f(case.do[b, :, h])
+                npairs = w.lq * (e - s)
+            else:
+                q_, do_ = f(case.q[s:e, h]), f(case.do[s:e, h])
+                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block64" else 0)
+            if w.kind == "block64":
+                for r0 in range(0, e - s, 64):
+                    sl = slice(r0, r0 + 64)
+                    A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
+                    A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
+            else:
+                A.seq_forward(q_, k_, v_, case.scale, w.causal)
+                A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
+            flops += 14.0 * npairs * w.head_dim
+            units += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 fwd+bwd of {units} random (sequence, head) units of the same batch "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gem",
+                    choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
+                             "block64_d128", "imbalance"])
+    ap.add_argument("--order", default="zigzag", choices=["zigzag", "inorder"])
+    ap.add_argument("--compare-orders", action="store_true",
+                    help="also time the forward with in-order dispatch, interleaved")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sequences would shard across GPUs with no exchange except one dQ all-reduce "
+              "for broadcast-Q)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import variable_length_flash_jaggedfa_amd as jfa
+
+    dev = torch.device("cuda:0")
+    variants = [w.with_(seed=args.seed) for w in variants_of(args.workload)]
+    w0 = variants[0]
+    t_gen = time.perf_counter()
+    case = J.make_case(w0)
+    t_gen = time.perf_counter() - t_gen
+    q = J.to_torch_bf16(case.q).to(dev)
+    k = J.to_torch_bf16(case.k).to(dev)
+    v = J.to_torch_bf16(case.v).to(dev)
+    do = J.to_torch_bf16(case.do).to(dev)
+    order = jfa.ORDER_ZIGZAG if args.order == "zigzag" else jfa.ORDER_INORDER
+
+    runs = []
+    sched_ms = 0.0
+    for w in variants:
+        fl = flags_of(w, jfa)
+        t0 = time.perf_counter()
+        plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, fl, w.lq,
+                        order=order, device=dev)
+        sched_ms += (time.perf_counter() - t0) * 1e3
+        out, lse = plan.forward(q, k, v)
+        dq, dk, dv = plan.backward(q, k, v, out, do, lse)
+        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block64" else 0)
+        runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
+                         fwd_flops=4.0 * npairs * w.num_heads * w.head_dim,
+                         bwd_flops=10.0 * npairs * w.num_heads * w.head_dim,
+                         fwd_ms=[], bwd_ms=[]))
+    alt = None
+    if args.compare_orders:
+        other = jfa.ORDER_INORDER if order == jfa.ORDER_ZIGZAG else jfa.ORDER_ZIGZAG
+        alt = [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
+                        w.lq, order=other, device=dev) for w in variants]
+    torch.cuda.synchronize()
+
+    def step(record):
+        for r in runs:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            r["plan"].forward(q, k, v, out=r["out"], lse=r["lse"])
+            e1.record()
+            r["plan"].backward(q, k, v, r["out"], do, r["lse"], dq=r["dq"], dk=r["dk"], dv=r["dv"])
+            e2.record()
+            if record:
+                r["_ev"] = (e0, e1, e2)
+        return runs
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        for r in runs:
+            e0, e1, e2 = r["_ev"]
+            r["fwd_ms"].append(e0.elapsed_time(e1))
+            r["bwd_ms"].append(e1.elapsed_time(e2))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # whole-job throughput over the timed region (includes per-step sync)
+    ev_ms = sum(np.mean(r["fwd_ms"]) + np.mean(r["bwd_ms"]) for r in runs)
+    flops_step = sum(r["fwd_flops"] + r["bwd_flops"] for r in runs)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # dominant pass: the one with the largest mean duration
+    cands = []
+    for r in runs:
+        tag = r["w"].name + ("_causal" if r["w"].causal else "")
+        cands.append((np.mean(r["fwd_ms"]), "fwd", tag, r["fwd_flops"]))
+        cands.append((np.mean(r["bwd_ms"]), "bwd", tag, r["bwd_flops"]))
+    dur, which, tag, fl = max(cands)
+    achieved = fl / (dur * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": f"{which} pass ({tag})", "avg_ms": round(dur, 4)}
+    if w0.kind == "block64":
+        # memory-bound: algorithmic bytes of the pass (4 or 8 bf16 tensors of T*H*D)
+        T = int(case.offsets[-1])
+        nbytes = (4 if which == "fwd" else 8) * T * w0.num_heads * w0.head_dim * 2
+        gbs = nbytes / (dur * 1e-3) / 1e9
+        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+
+    per_variant = {}
+    for r in runs:
+        tag = "causal" if r["w"].causal else "noncausal"
+        fm, bm = float(np.median(r["fwd_ms"])), float(np.median(r["bwd_ms"]))
+        per_variant[tag] = {"fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
+                            "fwd_tflops": round(r["fwd_flops"] / fm / 1e9, 1),
+                            "bwd_tflops": round(r["bwd_flops"] / bm / 1e9, 1),
+                            "fwd_bwd_tflops": round((r["fwd_flops"] + r["bwd_flops"]) / (fm + bm) / 1e9, 1)}
+
+    compare = None
+    if alt is not None:
+        # interleave: main order then other order, forward only, per variant
+        tm, to = [], []
+        for _ in range(max(10, args.steps)):
+            for r, ap_ in zip(runs, alt):
+                for plan, sink in ((r["plan"], tm), (ap_, to)):
+                    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a_.record()
+                    plan.forward(q, k, v, out=r["out"], lse=r["lse"])
+                    b_.record()
+                    torch.cuda.synchronize()
+                    sink.append(a_.elapsed_time(b_))
+        compare = {"fwd_ms_" + args.order: [round(float(np.percentile(tm, p)), 4) for p in (25, 50, 75)],
+                   "fwd_ms_other": [round(float(np.percentile(to, p)), 4) for p in (25, 50, 75)]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, variants)
+
+    T = int(case.offsets[-1])
+    line = {
+        "metric": "jagged attn fwd+bwd TFLOP/s (bf16, unpadded FLOPs) and % of MFMA bf16 peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal bf16 inputs, lengths drawn per the workload recipe)",
+        "config": {"workload": args.workload, "B": w0.num_seqs, "H": w0.num_heads,
+                   "D": w0.head_dim, "T": T, "lq": w0.lq,
+                   "variants": [("causal" if w.causal else "noncausal") for w in variants],
+                   "order": args.order, "seed": args.seed,
+                   "flops_per_step": flops_step,
+                   "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "event_ms_per_step": round(float(ev_ms), 4),
+                   "schedule_build_ms": round(sched_ms, 3),
+                   "input_gen_s": round(t_gen, 2),
+                   "per_variant": per_variant},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if compare is not None:
+        line["config"]["order_compare"] = compare
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

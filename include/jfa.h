@@ -1,0 +1,167 @@
+/*
+ * jfa.h -- C ABI of the MI355X (gfx950) jagged flash attention library (libjfa.so).
+ *
+ * The library computes exact softmax attention, forward and backward, directly on
+ * packed bf16 Q/K/V whose sequences are concatenated with no padding and whose
+ * boundaries are given by an int32 offsets array ("Jagged Flash Attention for GEM",
+ * introduction; the packed-tensor-plus-offsets layout). Besides plain jagged
+ * self-attention it covers:
+ *   - broadcast-Q: one dense Q shared by every sequence, so dQ is a sum over the
+ *     batch ("Jagged Flash Attention for GEM", backward / dQ section);
+ *   - 64-token block-diagonal attention, where each 64-token group attends only
+ *     within itself, with a single-tile path that keeps no running statistics and
+ *     stores no log-sum-exp ("TLX Block Attention", sections 1, 2 and 4);
+ *   - a host scheduler that sorts tiles by KV work and deals them zigzag over the
+ *     persistent workgroups ("Jagged Flash Attention for GEM", section on the
+ *     GEM-specific optimisations).
+ *
+ * Conventions for every entry point
+ *   Layouts     q, k, v, out, dout, dq, dk, dv: bf16, contiguous, 16-byte aligned.
+ *               Jagged: [T, H, D] token-major, T = offsets[B].
+ *               Broadcast-Q: q and dq [Lq, H, D]; out and dout [B, Lq, H, D];
+ *               k, v, dk, dv [T, H, D].
+ *               lse (float32): jagged [H, T]; broadcast-Q [B, H, Lq]; no lse for
+ *               the block-diagonal mode. lse is the natural-log log-sum-exp of
+ *               each query row's scaled scores.
+ *               offsets: int32 [B + 1], offsets[0] = 0, non-decreasing.
+ *   Maths       S = scale * Q K^T, P = softmax(S) per query row, out = P V.
+ *               Causal: inside a sequence, query i attends keys j <= i.
+ *   Ownership   The caller allocates every host and device buffer (schedule arrays
+ *               and workspace included). The library allocates nothing, keeps no
+ *               pointer after a call returns, and enqueues work only on `stream`
+ *               (a hipStream_t; NULL is the default stream).
+ *   Async       jfa_fwd / jfa_bwd return once their kernels are enqueued.
+ *   Errors      Return codes only; nothing throws across the ABI. Arguments are
+ *               checked on the host before any HIP call, so on any error nothing
+ *               is enqueued. jfa_last_error() gives a thread-local message.
+ *   Threads     Calls are thread-safe; calls on one stream execute in order.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum jfa_status {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, bad offsets */
+  JFA_ERR_UNSUPPORTED = 2,  /* head_dim or flag combination not implemented */
+  JFA_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  JFA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} jfa_status;
+
+/* problem flags */
+#define JFA_CAUSAL       1u  /* causal mask inside each sequence (jagged self-attention only) */
+#define JFA_BROADCAST_Q  2u  /* one dense Q [Lq,H,D] shared by every sequence (non-causal) */
+#define JFA_BLOCK_DIAG64 4u  /* 64-token block-diagonal self-attention (non-causal) */
+
+/* schedule kinds and dealing orders */
+#define JFA_KIND_FWD 0
+#define JFA_KIND_BWD 1
+#define JFA_ORDER_INORDER 0  /* tiles in generation order, tile j to slot j mod S */
+#define JFA_ORDER_ZIGZAG  1  /* sorted by KV work, descending; zigzag deal */
+
+typedef struct jfa_problem {
+  int32_t num_seqs;   /* B >= 0 */
+  int32_t num_heads;  /* H >= 1 */
+  int32_t head_dim;   /* D: 64 or 128 */
+  int32_t max_len;    /* >= every sequence length (checked by jfa_schedule_count) */
+  int32_t lq;         /* BROADCAST_Q: rows of the dense Q (>= 1); otherwise 0 */
+  uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 */
+  int64_t total_kv;   /* T = offsets[B], tokens in the packed K/V */
+  float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
+  int32_t reserved;   /* must be 0 */
+} jfa_problem;
+
+/* Rows of Q per forward tile (kind FWD) or of K/V per backward tile (kind BWD)
+ * that the kernels use for this head_dim and flags; -1 if unsupported. */
+int32_t jfa_tile_rows(int32_t kind, int32_t head_dim, uint32_t flags);
+
+/* Number of persistent workgroups (slots) the schedule should be dealt over on
+ * `device`: compute units times resident workgroups per compute unit. Writes
+ * *num_slots. Queries the HIP device (the only host entry point that does). */
+jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t flags, int32_t device,
+                             int32_t* num_slots);
+
+/* Validate the host offsets against the problem and count the tiles of `kind`.
+ * Checks: offsets[0] == 0, non-decreasing, offsets[B] == total_kv, every length
+ * <= max_len, and for BLOCK_DIAG64 every length a multiple of 64. For
+ * BLOCK_DIAG64 the count is the number of (64-block, head) units; no schedule is
+ * needed for that mode. The argument `offsets_host` is host memory, B+1 ints. */
+jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
+                              int64_t* num_tiles);
+
+/* Build the tile schedule on the host ("Jagged Flash Attention for GEM",
+ * GEM-specific optimisations: sort by KV work, deal zigzag).
+ *   Forward tile (b,h,t): query rows [t*BM, t*BM+BM) of sequence b (of the dense
+ *     Q for BROADCAST_Q), head h; work = keys visited: L_b, or with CAUSAL
+ *     min(L_b, (t+1)*BM).
+ *   Backward tile (b,h,n): key rows [n*BN, n*BN+BN) of sequence b, head h;
+ *     work = query rows that attend them: L_b (Lq for BROADCAST_Q), or with
+ *     CAUSAL L_b - n*BN.
+ *   Generation order is b, then h, then t. ZIGZAG: stable sort by descending
+ *   work, sorted position j goes to pass j / S, rank r = j % S, slot r on even
+ *   passes and S-1-r on odd ones. INORDER: tile j goes to slot j % S.
+ * Outputs (host memory, caller-allocated):
+ *   slot_ptr [num_slots + 1]: tiles of slot s are tiles[slot_ptr[s] .. slot_ptr[s+1]).
+ *   tiles    [capacity][4] int32 (b, h, t, work), grouped by slot in dealing order.
+ * `capacity` must be >= the count from jfa_schedule_count. Not valid for
+ * BLOCK_DIAG64 (UNSUPPORTED). Host only; no HIP call. */
+jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
+                        int32_t order, int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
+                        int64_t capacity);
+
+/* Bytes of device workspace jfa_bwd needs: a float32 dQ accumulator of
+ * [T, H, D] (jagged) or [Lq, H, D] (broadcast-Q); 0 for BLOCK_DIAG64. */
+size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
+
+/* Forward ("TLX Block Attention", section 2: the online-softmax loop; section 3,
+ * pipeline order load -> Q K^T -> exp2 softmax -> P V -> epilogue).
+ *   q, k, v      device, bf16, layouts above.
+ *   offsets_dev  device copy of the offsets the schedule was built from.
+ *   slot_ptr_dev, tiles_dev, num_slots: device copy of a FWD schedule
+ *                (ignored, may be NULL, for BLOCK_DIAG64).
+ *   out          device, bf16, written for every valid query row.
+ *   lse          device float32; must be NULL for BLOCK_DIAG64, non-NULL otherwise.
+ * A broadcast-Q sequence with no keys gets out = 0 and lse = -inf.
+ * Precondition (not checked on the device): offsets_dev equals the host offsets
+ * the schedule was built from. */
+jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                   const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                   const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
+                   void* stream);
+
+/* Backward ("TLX Block Attention", sections 2 and 4; "Jagged Flash Attention for
+ * GEM", backward / dQ section): P is rebuilt from Q, K and lse, Di = rowsum(dO*out)
+ * is computed inside the kernel, dS = P * (dP - Di), dV = P^T dO,
+ * dK = scale dS^T Q, dQ = scale dS K (summed over sequences for BROADCAST_Q).
+ *   out, dout    device bf16 (out as written by jfa_fwd).
+ *   lse          device float32 from jfa_fwd; NULL for BLOCK_DIAG64 (the block
+ *                path recomputes the softmax statistics instead).
+ *   slot_ptr_dev, tiles_dev, num_slots: device copy of a BWD schedule (ignored for
+ *                BLOCK_DIAG64).
+ *   dq, dk, dv   device bf16 outputs (dq is [Lq,H,D] for BROADCAST_Q).
+ *   workspace    device, >= jfa_bwd_workspace_bytes(p) bytes, 256-byte aligned;
+ *                contents on entry are ignored and clobbered. May be NULL when the
+ *                size is 0. */
+jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                   const void* out, const void* dout, const float* lse,
+                   const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                   const int32_t* tiles_dev, int32_t num_slots, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* jfa_status_string(jfa_status s);
+
+/* Message describing the last error raised on the calling thread ("" if none). */
+const char* jfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H */

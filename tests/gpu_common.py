@@ -1,0 +1,121 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI binding
+and compare with the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import jfa_inputs as J
+import variable_length_flash_jaggedfa_amd as jfa
+from oracle import attention as A
+
+OUT_TOL = 1e-2      # max |out - oracle|
+GRAD_TOL = 2e-2     # max |g - oracle| / max |oracle| for dq, dk, dv
+LSE_TOL = 1e-3      # max |lse - oracle|
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def flags_of(w: J.Workload) -> int:
+    f = 0
+    if w.causal:
+        f |= jfa.CAUSAL
+    if w.kind == "broadcast":
+        f |= jfa.BROADCAST_Q
+    if w.kind == "block64":
+        f |= jfa.BLOCK_DIAG64
+    return f
+
+
+def to_dev(bits, dev):
+    return J.to_torch_bf16(bits).to(dev)
+
+
+def bf16_to_f64(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+class GpuRun:
+    """Inputs uploaded once; fwd and bwd results copied back as float64."""
+
+    def __init__(self, case: J.Case, dev, order=jfa.ORDER_ZIGZAG, num_slots=None):
+        import torch
+        w = case.w
+        self.case = case
+        self.flags = flags_of(w)
+        self.plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, self.flags,
+                             w.lq, order=order, num_slots=num_slots, device=dev)
+        self.q = to_dev(case.q, dev)
+        self.k = to_dev(case.k, dev)
+        self.v = to_dev(case.v, dev)
+        self.do = to_dev(case.do, dev) if case.do is not None else None
+        self.torch = torch
+
+    def forward(self):
+        out, lse = self.plan.forward(self.q, self.k, self.v)
+        self.torch.cuda.synchronize()
+        self.out_dev, self.lse_dev = out, lse
+        return out, lse
+
+    def backward(self):
+        dq, dk, dv = self.plan.backward(self.q, self.k, self.v, self.out_dev, self.do, self.lse_dev)
+        self.torch.cuda.synchronize()
+        return dq, dk, dv
+
+
+def f64(bits):
+    return J.bf16_bits_to_f64(bits)
+
+
+def oracle_full(case: J.Case):
+    w = case.w
+    q, k, v, do = f64(case.q), f64(case.k), f64(case.v), f64(case.do)
+    off = case.offsets.astype(np.int64)
+    if w.kind == "broadcast":
+        out, lse = A.broadcast_forward(q, k, v, off, case.scale)
+        dq, dk, dv = A.broadcast_backward(q, k, v, do, off, case.scale)
+    elif w.kind == "block64":
+        out = A.block_diag_forward(q, k, v, off, case.scale)
+        lse = None
+        dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale)
+    else:
+        out, lse = A.jagged_forward(q, k, v, off, case.scale, w.causal)
+        dq, dk, dv = A.jagged_backward(q, k, v, do, off, case.scale, w.causal)
+    return out, lse, dq, dk, dv
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def rel_err(g, o):
+    m = float(np.max(np.abs(o))) if o.size else 0.0
+    return max_abs(g, o) / m if m > 0 else max_abs(g, o)
+
+
+def assert_out(got, ref, what="out"):
+    e = max_abs(got, ref)
+    log(f"  {what}: max abs err {e:.3e} (tol {OUT_TOL})")
+    assert np.all(np.isfinite(got)), what
+    assert e <= OUT_TOL, (what, e)
+
+
+def assert_lse(got, ref):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin)
+    e = max_abs(got[fin], ref[fin])
+    log(f"  lse: max abs err {e:.3e} (tol {LSE_TOL})")
+    assert e <= LSE_TOL
+
+
+def assert_grad(got, ref, what):
+    e = rel_err(got, ref)
+    log(f"  {what}: max err / max|ref| {e:.3e} (tol {GRAD_TOL})")
+    assert np.all(np.isfinite(got)), what
+    assert e <= GRAD_TOL, (what, e)

@@ -1,0 +1,179 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol include/jfa.h
+declares, rejects bad arguments on the host (before any HIP call), and its C++
+scheduler equals the independent Python reference bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import jfa_inputs as J
+import variable_length_flash_jaggedfa_amd as jfa
+from oracle import schedule_ref as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "jfa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jfa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = jfa.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings():
+    L = jfa.lib()
+    for s in range(5):
+        assert L.jfa_status_string(s)
+
+
+def _p(**kw):
+    base = dict(num_seqs=2, num_heads=2, head_dim=64, max_len=10, total_kv=15, scale=0.125,
+                flags=0, lq=0)
+    base.update(kw)
+    return jfa.problem(**base)
+
+
+OFF = np.array([0, 10, 15], dtype=np.int32)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), jfa.ERR_UNSUPPORTED),
+    (dict(num_heads=0), jfa.ERR_INVALID_ARG),
+    (dict(scale=0.0), jfa.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), jfa.ERR_INVALID_ARG),
+    (dict(flags=8), jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.CAUSAL | jfa.BROADCAST_Q, lq=4), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BLOCK_DIAG64 | jfa.CAUSAL), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BROADCAST_Q, lq=0), jfa.ERR_INVALID_ARG),
+    (dict(lq=3), jfa.ERR_INVALID_ARG),
+    (dict(max_len=9), jfa.ERR_INVALID_ARG),
+    (dict(total_kv=16), jfa.ERR_INVALID_ARG),
+])
+def test_schedule_count_rejects(kw, status):
+    with pytest.raises(jfa.JfaError) as e:
+        jfa.schedule_count(_p(**kw), OFF, jfa.KIND_FWD)
+    assert e.value.status == status
+
+
+def test_offsets_checks():
+    with pytest.raises(jfa.JfaError):
+        jfa.schedule_count(_p(), np.array([1, 10, 15], dtype=np.int32), jfa.KIND_FWD)
+    with pytest.raises(jfa.JfaError):
+        jfa.schedule_count(_p(), np.array([0, 10, 9], dtype=np.int32), jfa.KIND_FWD)
+    # block-diagonal needs multiples of 64
+    p = _p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=100)
+    with pytest.raises(jfa.JfaError):
+        jfa.schedule_count(p, np.array([0, 28, 128], dtype=np.int32), jfa.KIND_FWD)
+    assert jfa.schedule_count(p, np.array([0, 64, 128], dtype=np.int32), jfa.KIND_FWD) == 2 * 2
+
+
+def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
+    L = jfa.lib()
+    p = _p()
+    nul = None
+    fake = 4096  # aligned non-null fake address: never dereferenced on these paths
+    # NULL q
+    s = L.jfa_fwd(ctypes.byref(p), nul, fake, fake, fake, fake, fake, 4, fake, fake, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # misaligned k
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake + 2, fake, fake, fake, fake, 4, fake, fake, None)
+    assert s == jfa.ERR_INVALID_ARG and b"aligned" in L.jfa_last_error()
+    # missing lse
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 4, fake, nul, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # zero slots
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 0, fake, fake, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # block-diagonal with an lse pointer
+    pb = _p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)
+    s = L.jfa_fwd(ctypes.byref(pb), fake, fake, fake, nul, nul, nul, 0, fake, fake, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # backward: workspace too small
+    s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, 4,
+                  fake, fake, fake, fake, 16, None)
+    assert s == jfa.ERR_WORKSPACE
+    s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, nul, fake, fake, fake, fake, 4,
+                  fake, fake, fake, fake, 1 << 20, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # empty problems are no-ops that touch nothing
+    p0 = _p(num_seqs=0, total_kv=0, max_len=0)
+    assert L.jfa_fwd(ctypes.byref(p0), nul, nul, nul, nul, nul, nul, 0, nul, nul, None) == jfa.OK
+
+
+def test_workspace_bytes():
+    assert jfa.bwd_workspace_bytes(_p()) == 15 * 2 * 64 * 4
+    assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == 7 * 2 * 64 * 4
+    assert jfa.bwd_workspace_bytes(_p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)) == 0
+
+
+def test_tile_rows():
+    assert jfa.tile_rows(jfa.KIND_FWD, 128) > 0
+    assert jfa.tile_rows(jfa.KIND_BWD, 64) > 0
+    assert jfa.tile_rows(jfa.KIND_FWD, 80) == -1
+    assert jfa.tile_rows(jfa.KIND_FWD, 128, jfa.BLOCK_DIAG64) == 64
+
+
+@pytest.mark.parametrize("name", ["tiny", "gem", "gem_causal", "broadcast", "imbalance"])
+@pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
+@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG])
+def test_cpp_schedule_equals_reference(name, kind, order):
+    w = J.standard_workloads()[name]
+    L = J.lengths(w)
+    off = J.offsets_from_lengths(L)
+    H = w.num_heads if name != "imbalance" else 4
+    flags = (jfa.CAUSAL if w.causal else 0) | (jfa.BROADCAST_Q if w.kind == "broadcast" else 0)
+    p = jfa.problem(len(L), H, w.head_dim, int(L.max()), int(off[-1]), 0.1, flags, w.lq)
+    S = 256
+    sp, tl = jfa.schedule(p, off, kind, order, S)
+    rows = jfa.tile_rows(kind, w.head_dim, flags)
+    sp2, tl2 = R.schedule(L, H, kind, rows, order, S, w.causal, w.lq)
+    assert np.array_equal(sp, sp2)
+    assert np.array_equal(tl, tl2)
+
+
+def test_cpp_schedule_golden():
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "schedule_examples.json")))["cases"]
+    for c in cases:
+        kind = jfa.KIND_FWD if c["kind"] == "fwd" else jfa.KIND_BWD
+        rows = jfa.tile_rows(kind, 64, 0)
+        if rows != c["tile_rows"]:
+            # the library's tile height differs from the hand example: scale lengths
+            f = rows // c["tile_rows"] if rows % c["tile_rows"] == 0 else None
+            if f is None:
+                continue
+            lengths = [x * f for x in c["lengths"]]
+        else:
+            f, lengths = 1, c["lengths"]
+        off = J.offsets_from_lengths(lengths)
+        p = jfa.problem(len(lengths), c["heads"], 64, max(lengths), int(off[-1]), 0.1,
+                        jfa.CAUSAL if c["causal"] else 0)
+        for order, key in ((jfa.ORDER_ZIGZAG, "zigzag"), (jfa.ORDER_INORDER, "inorder")):
+            sp, tl = jfa.schedule(p, off, kind, order, c["slots"])
+            got = [[[t[0], t[1], t[2], t[3] // f] for t in tl[sp[s]:sp[s + 1]].tolist()]
+                   for s in range(c["slots"])]
+            assert got == c[key], (c["name"], key)
+
+
+def test_schedule_rejects_block_mode_and_small_capacity():
+    L = jfa.lib()
+    p = _p()
+    sp = np.zeros(5, dtype=np.int32)
+    tl = np.zeros((2, 4), dtype=np.int32)
+    s = L.jfa_schedule(ctypes.byref(p), OFF.ctypes.data, jfa.KIND_FWD, jfa.ORDER_ZIGZAG, 4,
+                       sp.ctypes.data, tl.ctypes.data, 1)
+    assert s == jfa.ERR_INVALID_ARG
+    pb = _p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)
+    off = np.array([0, 64, 128], dtype=np.int32)
+    s = L.jfa_schedule(ctypes.byref(pb), off.ctypes.data, jfa.KIND_FWD, jfa.ORDER_ZIGZAG, 4,
+                       sp.ctypes.data, tl.ctypes.data, 8)
+    assert s == jfa.ERR_UNSUPPORTED

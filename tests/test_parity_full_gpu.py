@@ -1,0 +1,124 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default slot count, zigzag schedule). The oracle recomputes a
+sample of (sequence, head) slices one by one; broadcast-Q dQ is checked for whole
+heads (every sequence contributes to it)."""
+import numpy as np
+import pytest
+
+import jfa_inputs as J
+import variable_length_flash_jaggedfa_amd as jfa
+from oracle import attention as A
+from tests.gpu_common import (GRAD_TOL, LSE_TOL, OUT_TOL, GpuRun, bf16_to_f64, log, max_abs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pick(L, n_random, rng):
+    order = np.argsort(L)
+    pick = {int(order[-1]), int(order[0])}
+    while len(pick) < min(len(L), 2 + n_random):
+        pick.add(int(rng.integers(len(L))))
+    return sorted(pick)
+
+
+def _seq_slice(x, off, b, h):
+    return J.bf16_bits_to_f64(x[off[b]:off[b + 1], h])
+
+
+def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
+    w = J.standard_workloads()[name]
+    log(f"workload {name}: generating inputs")
+    case = J.make_case(w)
+    log(f"  B={w.num_seqs} T={int(case.offsets[-1])} H={w.num_heads} D={w.head_dim}")
+    run = GpuRun(case, gpu)
+    out, lse = run.forward()
+    dq, dk, dv = run.backward()
+    import torch
+    log("  GPU fwd+bwd done")
+    for name, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    off = case.offsets.astype(np.int64)
+    rng = np.random.default_rng(123)
+    seqs = _pick(case.lengths, n_random, rng)
+    H = w.num_heads
+    errs = {"out": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
+    refmax = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in seqs:
+        hs = range(H) if heads is None else heads
+        if long_heads is not None and case.lengths[b] > 4096:
+            hs = long_heads
+        for h in hs:
+            k_ = _seq_slice(case.k, off, b, h)
+            v_ = _seq_slice(case.v, off, b, h)
+            if w.kind == "broadcast":
+                q_ = J.bf16_bits_to_f64(case.q[:, h])
+                do_ = J.bf16_bits_to_f64(case.do[b, :, h])
+                got_o, got_l = bf16_to_f64(out[b, :, h]), lse[b, h].cpu().numpy()
+            else:
+                q_ = _seq_slice(case.q, off, b, h)
+                do_ = _seq_slice(case.do, off, b, h)
+                got_o = bf16_to_f64(out[off[b]:off[b + 1], h])
+                got_l = lse[h, off[b]:off[b + 1]].cpu().numpy() if lse is not None else None
+            if w.kind == "block64":
+                o_ref = np.zeros_like(q_)
+                gq, gk, gv = np.zeros_like(q_), np.zeros_like(k_), np.zeros_like(v_)
+                for s0 in range(0, len(q_), 64):
+                    sl = slice(s0, s0 + 64)
+                    o_ref[sl], _ = A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
+                    gq[sl], gk[sl], gv[sl] = A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
+                l_ref = None
+            else:
+                o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale, w.causal)
+                gq, gk, gv = A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
+            errs["out"] = max(errs["out"], max_abs(got_o, o_ref))
+            if l_ref is not None:
+                errs["lse"] = max(errs["lse"], max_abs(got_l, l_ref))
+            errs["dk"] = max(errs["dk"], max_abs(bf16_to_f64(dk[off[b]:off[b + 1], h]), gk))
+            errs["dv"] = max(errs["dv"], max_abs(bf16_to_f64(dv[off[b]:off[b + 1], h]), gv))
+            refmax["dk"] = max(refmax["dk"], float(np.abs(gk).max()))
+            refmax["dv"] = max(refmax["dv"], float(np.abs(gv).max()))
+            if w.kind != "broadcast":
+                errs["dq"] = max(errs["dq"], max_abs(bf16_to_f64(dq[off[b]:off[b + 1], h]), gq))
+                refmax["dq"] = max(refmax["dq"], float(np.abs(gq).max()))
+    if w.kind == "broadcast":
+        # dQ of one whole head: the sum over every sequence
+        h = 0
+        q_ = J.bf16_bits_to_f64(case.q[:, h])
+        acc = np.zeros_like(q_)
+        for b in range(w.num_seqs):
+            gq, _, _ = A.seq_backward(q_, _seq_slice(case.k, off, b, h), _seq_slice(case.v, off, b, h),
+                                      J.bf16_bits_to_f64(case.do[b, :, h]), case.scale)
+            acc += gq
+        errs["dq"] = max_abs(bf16_to_f64(dq[:, h]), acc)
+        refmax["dq"] = float(np.abs(acc).max())
+    log(f"  sampled sequences {seqs}")
+    log(f"  out {errs['out']:.3e} lse {errs['lse']:.3e} "
+        + " ".join(f"{k} {errs[k] / refmax[k]:.3e}" for k in ("dq", "dk", "dv")))
+    assert errs["out"] <= OUT_TOL
+    assert errs["lse"] <= LSE_TOL
+    for k in ("dq", "dk", "dv"):
+        assert errs[k] <= GRAD_TOL * refmax[k], k
+
+
+def test_gem_noncausal(gpu):
+    run_sampled("gem", gpu)
+
+
+def test_gem_causal(gpu):
+    run_sampled("gem_causal", gpu)
+
+
+def test_broadcast(gpu):
+    run_sampled("broadcast", gpu, heads=[0, 5])
+
+
+def test_block64_d64(gpu):
+    run_sampled("block64_d64", gpu, n_random=3)
+
+
+def test_block64_d128(gpu):
+    run_sampled("block64_d128", gpu, n_random=3)
+
+
+def test_imbalance(gpu):
+    run_sampled("imbalance", gpu, n_random=6, long_heads=[3])

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element
+by element, on small seeded cases that span several tiles and ragged tails, plus
+the edge cases (empty and length-1 sequences, one sequence, lengths at tile
+boundaries, broadcast-Q with empty K/V, identical K/V copies)."""
+import numpy as np
+import pytest
+
+import jfa_inputs as J
+import variable_length_flash_jaggedfa_amd as jfa
+from oracle import attention as A
+from tests.gpu_common import (GpuRun, assert_grad, assert_lse, assert_out, bf16_to_f64, log,
+                              oracle_full)
+
+pytestmark = pytest.mark.gpu
+
+
+def check_case(w, dev, order=jfa.ORDER_ZIGZAG, num_slots=None, bwd=True):
+    log(f"case {w.name} kind={w.kind} causal={w.causal} H={w.num_heads} D={w.head_dim} "
+        f"lq={w.lq} seed={w.seed} lengths={J.lengths(w)[:12].tolist()}")
+    case = J.make_case(w)
+    run = GpuRun(case, dev, order=order, num_slots=num_slots)
+    out, lse = run.forward()
+    ref = oracle_full(case)
+    assert_out(bf16_to_f64(out), ref[0])
+    if lse is not None:
+        assert_lse(lse.cpu().numpy().astype(np.float64), ref[1])
+    if bwd:
+        dq, dk, dv = run.backward()
+        for name, g, r in (("dq", dq, ref[2]), ("dk", dk, ref[3]), ("dv", dv, ref[4])):
+            assert_grad(bf16_to_f64(g), r, name)
+    return run
+
+
+def test_tiny_workload(gpu):
+    check_case(J.standard_workloads()["tiny"], gpu)
+
+
+def test_tiny_workload_causal(gpu):
+    check_case(J.standard_workloads()["tiny"].with_(causal=True), gpu)
+
+
+RAGGED = [300, 1, 129, 64, 0, 257, 17, 128, 2]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jagged_ragged(gpu, D, causal):
+    check_case(J.custom(RAGGED, 3, D, sigma=0.5, seed=5, causal=causal), gpu)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_broadcast_ragged(gpu, D):
+    check_case(J.custom([50, 0, 300, 1, 129, 64], 2, D, sigma=0.5, seed=6, kind="broadcast",
+                        lq=200), gpu)
+
+
+def test_broadcast_all_empty(gpu):
+    check_case(J.custom([0, 0], 2, 64, seed=7, kind="broadcast", lq=70), gpu)
+
+
+def test_broadcast_identical_copies(gpu):
+    import torch
+    w = J.custom([77], 2, 128, sigma=0.5, seed=8, kind="broadcast", lq=130)
+    case1 = J.make_case(w)
+    B = 6
+    w6 = J.custom([77] * B, 2, 128, sigma=0.5, seed=8, kind="broadcast", lq=130)
+    case6 = J.Case(w6, np.full(B, 77), J.offsets_from_lengths([77] * B), case1.q,
+                   np.concatenate([case1.k] * B), np.concatenate([case1.v] * B),
+                   np.concatenate([case1.do] * B), case1.scale)
+    r1 = GpuRun(case1, gpu)
+    o1, _ = r1.forward()
+    dq1, _, _ = r1.backward()
+    r6 = GpuRun(case6, gpu)
+    o6, _ = r6.forward()
+    dq6, _, _ = r6.backward()
+    for b in range(B):
+        assert torch.equal(o6[b], o1[0])
+    ref = B * bf16_to_f64(dq1)
+    assert_grad(bf16_to_f64(dq6), ref, "dq(B copies) vs B*dq(1)")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_diag(gpu, D):
+    check_case(J.custom([64, 192, 128, 64 * 7], 2, D, seed=9, kind="block64"), gpu)
+
+
+def test_single_long_sequence(gpu):
+    check_case(J.custom([1000], 2, 128, sigma=0.5, seed=10), gpu)
+    check_case(J.custom([1000], 2, 128, sigma=0.5, seed=10, causal=True), gpu)
+
+
+def test_tile_boundaries(gpu):
+    check_case(J.custom([64, 128, 192, 256, 127, 129, 63, 65], 1, 128, sigma=0.5, seed=11), gpu)
+    check_case(J.custom([64, 128, 192, 256, 127, 129, 63, 65], 1, 64, sigma=0.5, seed=11,
+                        causal=True), gpu)
+
+
+def test_all_length_one(gpu):
+    check_case(J.custom([1] * 40, 2, 64, seed=12), gpu)
+
+
+def test_empty_problem(gpu):
+    import torch
+    plan = jfa.Plan(np.array([0, 0, 0], dtype=np.int32), 2, 64, 0.125, device=gpu)
+    q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device=gpu)
+    out, lse = plan.forward(q, q, q)
+    assert out.shape == (0, 2, 64)
+
+
+def test_identical_keys_give_mean(gpu):
+    w = J.custom([200], 2, 128, sigma=0.5, seed=13)
+    case = J.make_case(w)
+    case.k[:] = case.k[0]
+    run = GpuRun(case, gpu)
+    out, _ = run.forward()
+    ref = J.bf16_bits_to_f64(case.v).mean(axis=0)
+    assert np.max(np.abs(bf16_to_f64(out) - ref[None])) <= 1e-2
+
+
+def test_schedule_order_does_not_change_results(gpu):
+    import torch
+    w = J.custom(RAGGED, 3, 128, sigma=0.5, seed=14, causal=True)
+    case = J.make_case(w)
+    a = GpuRun(case, gpu, order=jfa.ORDER_ZIGZAG)
+    b = GpuRun(case, gpu, order=jfa.ORDER_INORDER, num_slots=7)
+    oa, la = a.forward()
+    ob, lb = b.forward()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    _, dka, dva = a.backward()
+    _, dkb, dvb = b.backward()
+    assert torch.equal(dka, dkb) and torch.equal(dva, dvb)
+
+
+def test_run_to_run_bitwise(gpu):
+    import torch
+    w = J.custom(RAGGED, 2, 128, sigma=0.5, seed=15)
+    run = GpuRun(J.make_case(w), gpu)
+    o1, l1 = run.forward()
+    o1, l1 = o1.clone(), l1.clone()
+    _, dk1, dv1 = run.backward()
+    dk1, dv1 = dk1.clone(), dv1.clone()
+    for _ in range(3):
+        o2, l2 = run.forward()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        _, dk2, dv2 = run.backward()
+        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
+def test_block_diag_matches_jagged_path_on_refined_offsets(gpu):
+    w = J.custom([64, 256, 128], 2, 128, seed=16, kind="block64")
+    case = J.make_case(w)
+    blk = GpuRun(case, gpu)
+    ob, _ = blk.forward()
+    dqb, dkb, dvb = blk.backward()
+    ref_off = A.refine_offsets(case.offsets, 64).astype(np.int32)
+    L = np.diff(ref_off)
+    wj = J.custom(L.tolist(), 2, 128, seed=16)
+    cj = J.Case(wj, L, ref_off, case.q, case.k, case.v, case.do, case.scale)
+    jag = GpuRun(cj, gpu)
+    oj, _ = jag.forward()
+    dqj, dkj, dvj = jag.backward()
+    assert_out(bf16_to_f64(ob), bf16_to_f64(oj), "block vs jagged out")
+    for n, a_, b_ in (("dq", dqb, dqj), ("dk", dkb, dkj), ("dv", dvb, dvj)):
+        assert_grad(bf16_to_f64(a_), bf16_to_f64(b_), n + " block vs jagged")

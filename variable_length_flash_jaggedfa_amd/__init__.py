@@ -1,0 +1,234 @@
+"""MI355X-native jagged flash attention: thin Python binding over libjfa.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI declared
+in include/jfa.h; this module only marshals arguments (torch tensors supply
+device memory and the stream). If libjfa.so has not been built, every entry
+point raises: there is no fallback path.
+
+Low-level names mirror the C ABI (tile_rows, default_slots, schedule_count,
+schedule, bwd_workspace_bytes, fwd, bwd). `Plan` bundles the host schedule,
+its device copy and the workspace for one problem.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjfa.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+CAUSAL, BROADCAST_Q, BLOCK_DIAG64 = 1, 2, 4
+KIND_FWD, KIND_BWD = 0, 1
+ORDER_INORDER, ORDER_ZIGZAG = 0, 1
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"jfa status {status}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("lq", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("total_kv", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libjfa.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m variable_length_flash_jaggedfa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+        L.jfa_tile_rows.argtypes = [i32, i32, u32]
+        L.jfa_tile_rows.restype = i32
+        L.jfa_default_slots.argtypes = [i32, i32, u32, i32, ctypes.POINTER(i32)]
+        L.jfa_default_slots.restype = i32
+        L.jfa_schedule_count.argtypes = [P, vp, i32, ctypes.POINTER(i64)]
+        L.jfa_schedule_count.restype = i32
+        L.jfa_schedule.argtypes = [P, vp, i32, i32, i32, vp, vp, i64]
+        L.jfa_schedule.restype = i32
+        L.jfa_bwd_workspace_bytes.argtypes = [P]
+        L.jfa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.jfa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.jfa_fwd.restype = i32
+        L.jfa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                              ctypes.c_size_t, vp]
+        L.jfa_bwd.restype = i32
+        L.jfa_status_string.argtypes = [i32]
+        L.jfa_status_string.restype = ctypes.c_char_p
+        L.jfa_last_error.argtypes = []
+        L.jfa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise JfaError(status, lib().jfa_last_error().decode())
+
+
+def problem(num_seqs, num_heads, head_dim, max_len, total_kv, scale, flags=0, lq=0) -> Problem:
+    return Problem(int(num_seqs), int(num_heads), int(head_dim), int(max_len), int(lq),
+                   int(flags), int(total_kv), float(scale), 0)
+
+
+def tile_rows(kind: int, head_dim: int, flags: int = 0) -> int:
+    return int(lib().jfa_tile_rows(kind, head_dim, flags))
+
+
+def default_slots(kind: int, head_dim: int, flags: int = 0, device: int = 0) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().jfa_default_slots(kind, head_dim, flags, device, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _host_i32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a
+
+
+def schedule_count(p: Problem, offsets_host, kind: int) -> int:
+    off = _host_i32(offsets_host)
+    n = ctypes.c_int64(0)
+    _check(lib().jfa_schedule_count(ctypes.byref(p), off.ctypes.data, kind, ctypes.byref(n)))
+    return int(n.value)
+
+
+def schedule(p: Problem, offsets_host, kind: int, order: int, num_slots: int):
+    """Host tile schedule -> (slot_ptr int32 [S+1], tiles int32 [N,4])."""
+    off = _host_i32(offsets_host)
+    n = schedule_count(p, off, kind)
+    slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+    tiles = np.zeros((max(n, 1), 4), dtype=np.int32)
+    _check(lib().jfa_schedule(ctypes.byref(p), off.ctypes.data, kind, order, num_slots,
+                              slot_ptr.ctypes.data, tiles.ctypes.data, n))
+    return slot_ptr, tiles[:n]
+
+
+def bwd_workspace_bytes(p: Problem) -> int:
+    return int(lib().jfa_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def fwd(p: Problem, q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
+        stream=None):
+    _check(lib().jfa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets_dev),
+                         _ptr(slot_ptr_dev), _ptr(tiles_dev), int(num_slots), _ptr(out),
+                         _ptr(lse), _stream(stream)))
+
+
+def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
+        dq, dk, dv, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().jfa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                         _ptr(lse), _ptr(offsets_dev), _ptr(slot_ptr_dev), _ptr(tiles_dev),
+                         int(num_slots), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                         ws_bytes, _stream(stream)))
+
+
+@dataclass
+class Schedule:
+    slot_ptr: np.ndarray
+    tiles: np.ndarray
+    num_slots: int
+    slot_ptr_dev: object = None
+    tiles_dev: object = None
+
+
+class Plan:
+    """Everything one jagged problem needs on the device, built once.
+
+    offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q.
+    Builds the FWD and BWD schedules on the host (zigzag by default), copies them
+    and the offsets to the device, and allocates the dQ workspace.
+    """
+
+    def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
+                 order=ORDER_ZIGZAG, num_slots=None, device="cuda"):
+        import torch
+        off = _host_i32(offsets_host)
+        L = np.diff(off.astype(np.int64))
+        self.offsets_host = off
+        self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
+                         int(off[-1]), scale, flags, lq)
+        self.device = torch.device(device)
+        self.offsets_dev = torch.from_numpy(off.copy()).to(self.device)
+        self.block = bool(flags & BLOCK_DIAG64)
+        self.sched = {}
+        if self.block:
+            schedule_count(self.p, off, KIND_FWD)  # validates the offsets
+        else:
+            for kind in (KIND_FWD, KIND_BWD):
+                S = num_slots or default_slots(kind, head_dim, flags, self.device.index or 0)
+                sp, tl = schedule(self.p, off, kind, order, S)
+                sch = Schedule(sp, tl, S)
+                sch.slot_ptr_dev = torch.from_numpy(sp).to(self.device)
+                sch.tiles_dev = torch.from_numpy(np.ascontiguousarray(tl)).to(self.device) \
+                    if len(tl) else torch.zeros((1, 4), dtype=torch.int32, device=self.device)
+                self.sched[kind] = sch
+        nbytes = bwd_workspace_bytes(self.p)
+        self.workspace = (torch.empty(nbytes // 4, dtype=torch.float32, device=self.device)
+                          if nbytes else None)
+
+    @property
+    def num_q_rows(self):
+        return self.p.lq if self.p.flags & BROADCAST_Q else self.p.total_kv
+
+    def _out_shape(self):
+        H, D = self.p.num_heads, self.p.head_dim
+        if self.p.flags & BROADCAST_Q:
+            return (self.p.num_seqs, self.p.lq, H, D)
+        return (self.p.total_kv, H, D)
+
+    def _lse_shape(self):
+        H = self.p.num_heads
+        if self.p.flags & BROADCAST_Q:
+            return (self.p.num_seqs, H, self.p.lq)
+        return (H, self.p.total_kv)
+
+    def forward(self, q, k, v, out=None, lse=None, stream=None):
+        import torch
+        out = out if out is not None else torch.empty(self._out_shape(), dtype=torch.bfloat16,
+                                                      device=self.device)
+        if not self.block and lse is None:
+            lse = torch.empty(self._lse_shape(), dtype=torch.float32, device=self.device)
+        s = self.sched.get(KIND_FWD)
+        fwd(self.p, q, k, v, self.offsets_dev, s.slot_ptr_dev if s else None,
+            s.tiles_dev if s else None, s.num_slots if s else 0, out,
+            None if self.block else lse, stream)
+        return out, (None if self.block else lse)
+
+    def backward(self, q, k, v, out, dout, lse=None, dq=None, dk=None, dv=None, stream=None):
+        import torch
+        dq = dq if dq is not None else torch.empty_like(q)
+        dk = dk if dk is not None else torch.empty_like(k)
+        dv = dv if dv is not None else torch.empty_like(v)
+        s = self.sched.get(KIND_BWD)
+        bwd(self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
+            s.slot_ptr_dev if s else None, s.tiles_dev if s else None, s.num_slots if s else 0,
+            dq, dk, dv, self.workspace, stream)
+        return dq, dk, dv

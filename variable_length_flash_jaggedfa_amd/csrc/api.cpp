@@ -1,0 +1,136 @@
+// C ABI entry points jfa_fwd, jfa_bwd and jfa_default_slots: argument checks on
+// the host (nothing is enqueued when a check fails), then kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "jfa_internal.h"
+
+using namespace jfa;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+jfa_status need(const void* p, const char* name, uintptr_t align = 16) {
+  if (!p) return fail(JFA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(JFA_ERR_INVALID_ARG, std::string(name) + " is not " + std::to_string(align) +
+                                         "-byte aligned");
+  return JFA_OK;
+}
+
+// rows of Q / out for the problem (dense Q rows for broadcast-Q)
+int64_t q_rows(const jfa_problem* p) {
+  return (p->flags & JFA_BROADCAST_Q) ? int64_t(p->lq) : p->total_kv;
+}
+
+jfa_status check_schedule_args(const jfa_problem* p, const int32_t* offsets, const int32_t* slot_ptr,
+                               const int32_t* tiles, int32_t num_slots) {
+  if (jfa_status s = need(offsets, "offsets_dev", 4)) return s;
+  if (jfa_status s = need(slot_ptr, "slot_ptr_dev", 4)) return s;
+  if (jfa_status s = need(tiles, "tiles_dev", 16)) return s;
+  if (num_slots < 1) return fail(JFA_ERR_INVALID_ARG, "num_slots < 1");
+  (void)p;
+  return JFA_OK;
+}
+
+}  // namespace
+
+extern "C" jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t flags,
+                                        int32_t device, int32_t* num_slots) {
+  set_error("");
+  if (!num_slots) return fail(JFA_ERR_INVALID_ARG, "num_slots is NULL");
+  if (kind != JFA_KIND_FWD && kind != JFA_KIND_BWD) return fail(JFA_ERR_INVALID_ARG, "bad kind");
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (flags & JFA_BLOCK_DIAG64) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 runs without a schedule");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess || cus <= 0)
+    return fail(JFA_ERR_HIP, std::string("device query failed: ") + hipGetErrorString(e));
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(JFA_ERR_HIP, "hipGetDevice failed");
+  if (cur != device && hipSetDevice(device) != hipSuccess) return fail(JFA_ERR_HIP, "hipSetDevice failed");
+  int per_cu = 0;
+  jfa_status s = kind == JFA_KIND_FWD ? fwd_slots_per_cu(head_dim, flags, &per_cu)
+                                      : bwd_slots_per_cu(head_dim, flags, &per_cu);
+  if (cur != device) (void)hipSetDevice(cur);
+  if (s) return s;
+  *num_slots = cus * per_cu;
+  return JFA_OK;
+}
+
+extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                              const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
+                              void* stream) {
+  set_error("");
+  if (jfa_status s = check_problem(p)) return s;
+  const bool blk = p->flags & JFA_BLOCK_DIAG64;
+  if (p->num_seqs == 0 || (q_rows(p) == 0 && p->total_kv == 0)) return JFA_OK;  // nothing to do
+  if (q_rows(p) > 0) {
+    if (jfa_status s = need(q, "q")) return s;
+    if (jfa_status s = need(out, "out")) return s;
+  }
+  if (p->total_kv > 0) {
+    if (jfa_status s = need(k, "k")) return s;
+    if (jfa_status s = need(v, "v")) return s;
+  }
+  FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
+              p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
+              stream};
+  if (blk) {
+    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is stored)");
+    if (p->total_kv == 0) return JFA_OK;
+    return launch_block_fwd(a);
+  }
+  if (jfa_status s = need(lse, "lse", 4)) return s;
+  if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
+  return launch_fwd(a);
+}
+
+extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse,
+                              const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                              const int32_t* tiles_dev, int32_t num_slots, void* dq, void* dk,
+                              void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  set_error("");
+  if (jfa_status s = check_problem(p)) return s;
+  const bool blk = p->flags & JFA_BLOCK_DIAG64;
+  const bool bq = p->flags & JFA_BROADCAST_Q;
+  if (p->num_seqs == 0) return JFA_OK;
+  if (q_rows(p) > 0) {
+    if (jfa_status s = need(q, "q")) return s;
+    if (jfa_status s = need(out, "out")) return s;
+    if (jfa_status s = need(dout, "dout")) return s;
+    if (jfa_status s = need(dq, "dq")) return s;
+  }
+  if (p->total_kv > 0) {
+    if (jfa_status s = need(k, "k")) return s;
+    if (jfa_status s = need(v, "v")) return s;
+    if (jfa_status s = need(dk, "dk")) return s;
+    if (jfa_status s = need(dv, "dv")) return s;
+  }
+  BwdLaunch a{q, k, v, out, dout, lse, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, dq, dk, dv,
+              static_cast<float*>(workspace), p->num_seqs, p->num_heads, p->head_dim, p->lq,
+              p->total_kv, p->scale, p->flags, stream};
+  if (blk) {
+    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is read)");
+    if (p->total_kv == 0) return JFA_OK;
+    return launch_block_bwd(a);
+  }
+  if (q_rows(p) > 0 && !lse) return fail(JFA_ERR_INVALID_ARG, "lse is NULL");
+  if (lse && !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  const size_t ws = jfa_bwd_workspace_bytes(p);
+  if (ws > 0) {
+    if (!workspace || workspace_bytes < ws)
+      return fail(JFA_ERR_WORKSPACE, "workspace needs " + std::to_string(ws) + " bytes, got " +
+                                         std::to_string(workspace_bytes));
+    if (!aligned(workspace, 256)) return fail(JFA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  }
+  if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
+  if (q_rows(p) == 0 && p->total_kv == 0) return JFA_OK;
+  (void)bq;
+  return launch_bwd(a);
+}

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host-side translation units of libjfa.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/jfa.h"
+
+namespace jfa {
+
+// Tile shapes the kernels are compiled for.
+constexpr int kFwdBM = 128;    // query rows per forward tile (4 waves x 32 rows)
+constexpr int kFwdBN = 64;     // keys per forward KV step
+constexpr int kBwdBN = 128;    // key rows per backward tile (4 waves x 32 keys)
+constexpr int kBwdBM = 64;     // query rows per backward Q step
+constexpr int kBlock = 64;     // block-diagonal group size
+
+// thread-local error text
+void set_error(const std::string& msg);
+jfa_status fail(jfa_status s, const std::string& msg);
+
+// host validation of the problem descriptor (no HIP calls)
+jfa_status check_problem(const jfa_problem* p);
+
+// kernel launchers (defined in the .hip files); all arguments already validated
+struct FwdLaunch {
+  const void* q; const void* k; const void* v;
+  const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
+  int32_t num_slots;
+  void* out; float* lse;
+  int32_t num_seqs, num_heads, head_dim, lq;
+  int64_t total_kv;
+  float scale;
+  uint32_t flags;
+  void* stream;
+};
+
+struct BwdLaunch {
+  const void* q; const void* k; const void* v; const void* out; const void* dout;
+  const float* lse;
+  const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
+  int32_t num_slots;
+  void* dq; void* dk; void* dv;
+  float* dq_acc;
+  int32_t num_seqs, num_heads, head_dim, lq;
+  int64_t total_kv;
+  float scale;
+  uint32_t flags;
+  void* stream;
+};
+
+jfa_status launch_fwd(const FwdLaunch& a);
+jfa_status launch_bwd(const BwdLaunch& a);
+jfa_status launch_block_fwd(const FwdLaunch& a);
+jfa_status launch_block_bwd(const BwdLaunch& a);
+jfa_status fwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
+jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
+
+}  // namespace jfa

@@ -1,0 +1,206 @@
+// Host tile scheduler ("Jagged Flash Attention for GEM", GEM-specific
+// optimisations): enumerate the tiles of a jagged problem with their KV work,
+// sort them by that work in descending order and deal them zigzag over the
+// persistent workgroups. Pure host code; no HIP call.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "jfa_internal.h"
+
+namespace jfa {
+
+namespace {
+thread_local std::string g_error;
+}
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+jfa_status fail(jfa_status s, const std::string& msg) {
+  g_error = msg;
+  return s;
+}
+
+jfa_status check_problem(const jfa_problem* p) {
+  if (!p) return fail(JFA_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->num_seqs < 0) return fail(JFA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (p->num_heads < 1) return fail(JFA_ERR_INVALID_ARG, "num_heads < 1");
+  if (p->max_len < 0) return fail(JFA_ERR_INVALID_ARG, "max_len < 0");
+  if (p->total_kv < 0) return fail(JFA_ERR_INVALID_ARG, "total_kv < 0");
+  if (p->reserved != 0) return fail(JFA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (!(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(JFA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64;
+  if (p->flags & ~known) return fail(JFA_ERR_INVALID_ARG, "unknown flag bits");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const bool causal = p->flags & JFA_CAUSAL, bq = p->flags & JFA_BROADCAST_Q,
+             blk = p->flags & JFA_BLOCK_DIAG64;
+  if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
+  if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 with other flags");
+  if (bq && p->lq < 1) return fail(JFA_ERR_INVALID_ARG, "BROADCAST_Q needs lq >= 1");
+  if (!bq && p->lq != 0) return fail(JFA_ERR_INVALID_ARG, "lq must be 0 without BROADCAST_Q");
+  if (blk && (p->total_kv % kBlock))
+    return fail(JFA_ERR_INVALID_ARG, "BLOCK_DIAG64 needs total_kv % 64 == 0");
+  // element counts must stay addressable with 64-bit offsets and tiles in int32
+  const double elems = double(std::max<int64_t>(p->total_kv, p->lq)) * p->num_heads * p->head_dim;
+  if (elems > 4.0e15) return fail(JFA_ERR_INVALID_ARG, "problem too large");
+  if (p->total_kv > INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "total_kv exceeds int32");
+  return JFA_OK;
+}
+
+namespace {
+
+struct Tile {
+  int32_t b, h, t, work;
+};
+
+int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+jfa_status check_offsets(const jfa_problem* p, const int32_t* off) {
+  if (p->num_seqs > 0 && !off) return fail(JFA_ERR_INVALID_ARG, "offsets_host is NULL");
+  if (!off) return p->total_kv == 0 ? JFA_OK : fail(JFA_ERR_INVALID_ARG, "offsets_host is NULL");
+  if (off[0] != 0) return fail(JFA_ERR_INVALID_ARG, "offsets[0] != 0");
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int64_t L = int64_t(off[b + 1]) - off[b];
+    if (L < 0) return fail(JFA_ERR_INVALID_ARG, "offsets decrease at sequence " + std::to_string(b));
+    if (L > p->max_len)
+      return fail(JFA_ERR_INVALID_ARG, "sequence " + std::to_string(b) + " longer than max_len");
+    if ((p->flags & JFA_BLOCK_DIAG64) && (L % kBlock))
+      return fail(JFA_ERR_INVALID_ARG,
+                  "BLOCK_DIAG64: length of sequence " + std::to_string(b) + " is not a multiple of 64");
+  }
+  if (off[p->num_seqs] != p->total_kv) return fail(JFA_ERR_INVALID_ARG, "offsets[B] != total_kv");
+  return JFA_OK;
+}
+
+// Tiles in generation order (b, then h, then t).
+std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t kind) {
+  const bool causal = p->flags & JFA_CAUSAL;
+  const int32_t lq = (p->flags & JFA_BROADCAST_Q) ? p->lq : 0;
+  const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
+  std::vector<Tile> tiles;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int32_t L = off[b + 1] - off[b];
+    for (int32_t h = 0; h < p->num_heads; ++h) {
+      if (kind == JFA_KIND_FWD) {
+        if (lq) {
+          for (int32_t t = 0, n = ceil_div(lq, rows); t < n; ++t) tiles.push_back({b, h, t, L});
+        } else {
+          for (int32_t t = 0, n = ceil_div(L, rows); t < n; ++t) {
+            const int64_t end = int64_t(t + 1) * rows;
+            tiles.push_back({b, h, t, causal ? int32_t(std::min<int64_t>(L, end)) : L});
+          }
+        }
+      } else {
+        for (int32_t n = 0, m = ceil_div(L, rows); n < m; ++n) {
+          const int32_t work = lq ? lq : (causal ? L - n * rows : L);
+          tiles.push_back({b, h, n, work});
+        }
+      }
+    }
+  }
+  return tiles;
+}
+
+}  // namespace
+}  // namespace jfa
+
+using namespace jfa;
+
+extern "C" int32_t jfa_tile_rows(int32_t kind, int32_t head_dim, uint32_t flags) {
+  if (head_dim != 64 && head_dim != 128) return -1;
+  if (flags & JFA_BLOCK_DIAG64) return kBlock;
+  if (kind == JFA_KIND_FWD) return kFwdBM;
+  if (kind == JFA_KIND_BWD) return kBwdBN;
+  return -1;
+}
+
+extern "C" jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host,
+                                         int32_t kind, int64_t* num_tiles) {
+  set_error("");
+  if (jfa_status s = check_problem(p)) return s;
+  if (!num_tiles) return fail(JFA_ERR_INVALID_ARG, "num_tiles is NULL");
+  if (kind != JFA_KIND_FWD && kind != JFA_KIND_BWD) return fail(JFA_ERR_INVALID_ARG, "bad kind");
+  if (jfa_status s = check_offsets(p, offsets_host)) return s;
+  if (p->flags & JFA_BLOCK_DIAG64) {
+    *num_tiles = (p->total_kv / kBlock) * p->num_heads;
+    return JFA_OK;
+  }
+  const bool lqmode = (p->flags & JFA_BROADCAST_Q) && kind == JFA_KIND_FWD;
+  const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
+  int64_t n = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int64_t L = int64_t(offsets_host[b + 1]) - offsets_host[b];
+    n += int64_t(p->num_heads) * ceil_div(lqmode ? p->lq : L, rows);
+  }
+  if (n > INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "too many tiles");
+  *num_tiles = n;
+  return JFA_OK;
+}
+
+extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
+                                   int32_t order, int32_t num_slots, int32_t* slot_ptr,
+                                   int32_t* tiles_out, int64_t capacity) {
+  int64_t count = 0;
+  if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
+  if (p->flags & JFA_BLOCK_DIAG64)
+    return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 runs without a schedule");
+  if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG)
+    return fail(JFA_ERR_INVALID_ARG, "bad order");
+  if (num_slots < 1) return fail(JFA_ERR_INVALID_ARG, "num_slots < 1");
+  if (!slot_ptr) return fail(JFA_ERR_INVALID_ARG, "slot_ptr is NULL");
+  if (count > 0 && !tiles_out) return fail(JFA_ERR_INVALID_ARG, "tiles is NULL");
+  if (capacity < count) return fail(JFA_ERR_INVALID_ARG, "tiles capacity too small");
+
+  const std::vector<Tile> tiles = enumerate(p, offsets_host, kind);
+  std::vector<int32_t> idx(tiles.size());
+  std::iota(idx.begin(), idx.end(), 0);
+  if (order == JFA_ORDER_ZIGZAG) {
+    // descending work; ties keep generation order
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int32_t a, int32_t b) { return tiles[a].work > tiles[b].work; });
+  }
+  // deal: sorted position j -> pass j / S, rank r = j % S
+  std::vector<int32_t> slot_of(idx.size());
+  std::vector<int32_t> count_of(num_slots, 0);
+  for (size_t j = 0; j < idx.size(); ++j) {
+    const int64_t pass = int64_t(j) / num_slots;
+    const int32_t r = int32_t(int64_t(j) % num_slots);
+    const int32_t s = (order == JFA_ORDER_ZIGZAG && (pass & 1)) ? num_slots - 1 - r : r;
+    slot_of[j] = s;
+    ++count_of[s];
+  }
+  slot_ptr[0] = 0;
+  for (int32_t s = 0; s < num_slots; ++s) slot_ptr[s + 1] = slot_ptr[s] + count_of[s];
+  std::vector<int32_t> fill(slot_ptr, slot_ptr + num_slots);
+  for (size_t j = 0; j < idx.size(); ++j) {
+    const Tile& t = tiles[idx[j]];
+    int32_t* dst = tiles_out + 4 * int64_t(fill[slot_of[j]]++);
+    dst[0] = t.b; dst[1] = t.h; dst[2] = t.t; dst[3] = t.work;
+  }
+  return JFA_OK;
+}
+
+extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
+  if (!p || check_problem(p) != JFA_OK) return 0;
+  if (p->flags & JFA_BLOCK_DIAG64) return 0;
+  const int64_t rows = (p->flags & JFA_BROADCAST_Q) ? p->lq : p->total_kv;
+  return size_t(rows) * p->num_heads * p->head_dim * sizeof(float);
+}
+
+extern "C" const char* jfa_status_string(jfa_status s) {
+  switch (s) {
+    case JFA_OK: return "ok";
+    case JFA_ERR_INVALID_ARG: return "invalid argument";
+    case JFA_ERR_UNSUPPORTED: return "unsupported";
+    case JFA_ERR_WORKSPACE: return "workspace too small";
+    case JFA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* jfa_last_error(void) { return jfa::g_error.c_str(); }
