@@ -119,6 +119,9 @@ def main():
                     help="also time the forward with in-order dispatch, interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one elementwise copy of this many MiB first (reads N, writes N): "
+                         "the reference for scaling HBM byte counters")
     args = ap.parse_args()
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
@@ -131,6 +134,13 @@ def main():
     import variable_length_flash_jaggedfa_amd as jfa
 
     dev = torch.device("cuda:0")
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     variants = [w.with_(seed=args.seed) for w in variants_of(args.workload)]
     w0 = variants[0]
     t_gen = time.perf_counter()

@@ -115,8 +115,9 @@ jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32
                         int32_t order, int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
                         int64_t capacity);
 
-/* Bytes of device workspace jfa_bwd needs: a float32 dQ accumulator of
- * [T, H, D] (jagged) or [Lq, H, D] (broadcast-Q); 0 for BLOCK_DIAG64. */
+/* Bytes of device workspace jfa_bwd needs: Di (float32, laid out like lse) and,
+ * for BROADCAST_Q, float32 dQ partials of [G][Lq][H][D] where the B sequences are
+ * split into G = min(B, 64) contiguous groups; 0 for BLOCK_DIAG64. */
 size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
 
 /* Forward ("TLX Block Attention", section 2: the online-softmax loop; section 3,
@@ -137,22 +138,29 @@ jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const voi
 
 /* Backward ("TLX Block Attention", sections 2 and 4; "Jagged Flash Attention for
  * GEM", backward / dQ section): P is rebuilt from Q, K and lse, Di = rowsum(dO*out)
- * is computed inside the kernel, dS = P * (dP - Di), dV = P^T dO,
+ * is computed inside the kernels, dS = P * (dP - Di), dV = P^T dO,
  * dK = scale dS^T Q, dQ = scale dS K (summed over sequences for BROADCAST_Q).
+ * No memory atomics are used: dQ is produced by a pass over query tiles and
+ * dK/dV by a pass over key tiles, so dK and dV (and dQ) are bitwise reproducible.
  *   out, dout    device bf16 (out as written by jfa_fwd).
  *   lse          device float32 from jfa_fwd; NULL for BLOCK_DIAG64 (the block
  *                path recomputes the softmax statistics instead).
- *   slot_ptr_dev, tiles_dev, num_slots: device copy of a BWD schedule (ignored for
- *                BLOCK_DIAG64).
+ *   q_slot_ptr_dev, q_tiles_dev, q_num_slots: device copy of a FWD schedule; the
+ *                dQ pass walks these query tiles. Ignored for BROADCAST_Q and
+ *                BLOCK_DIAG64 (may be NULL).
+ *   kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots: device copy of a BWD schedule;
+ *                the dK/dV pass walks these key tiles. Ignored for BLOCK_DIAG64.
  *   dq, dk, dv   device bf16 outputs (dq is [Lq,H,D] for BROADCAST_Q).
  *   workspace    device, >= jfa_bwd_workspace_bytes(p) bytes, 256-byte aligned;
  *                contents on entry are ignored and clobbered. May be NULL when the
  *                size is 0. */
 jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
                    const void* out, const void* dout, const float* lse,
-                   const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
-                   const int32_t* tiles_dev, int32_t num_slots, void* dq, void* dk, void* dv,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
+                   const int32_t* q_tiles_dev, int32_t q_num_slots,
+                   const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                   int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* jfa_status_string(jfa_status s);

@@ -99,10 +99,15 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
     assert s == jfa.ERR_INVALID_ARG
     # backward: workspace too small
     s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, 4,
-                  fake, fake, fake, fake, 16, None)
+                  fake, fake, 4, fake, fake, fake, fake, 16, None)
     assert s == jfa.ERR_WORKSPACE
+    # backward: NULL dout
     s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, nul, fake, fake, fake, fake, 4,
-                  fake, fake, fake, fake, 1 << 20, None)
+                  fake, fake, 4, fake, fake, fake, fake, 1 << 20, None)
+    assert s == jfa.ERR_INVALID_ARG
+    # backward: missing query-tile schedule for the dQ pass
+    s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, nul, nul, 0,
+                  fake, fake, 4, fake, fake, fake, fake, 1 << 20, None)
     assert s == jfa.ERR_INVALID_ARG
     # empty problems are no-ops that touch nothing
     p0 = _p(num_seqs=0, total_kv=0, max_len=0)
@@ -110,8 +115,12 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
 
 
 def test_workspace_bytes():
-    assert jfa.bwd_workspace_bytes(_p()) == 15 * 2 * 64 * 4
-    assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == 7 * 2 * 64 * 4
+    r256 = lambda n: (n + 255) // 256 * 256
+    # jagged: Di [H, T]
+    assert jfa.bwd_workspace_bytes(_p()) == r256(2 * 15 * 4)
+    # broadcast: Di [B, H, Lq] + min(B, 64) partials of [Lq, H, D]
+    assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == \
+        r256(2 * 2 * 7 * 4) + 2 * 7 * 2 * 64 * 4
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)) == 0
 
 

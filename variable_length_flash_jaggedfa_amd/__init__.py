@@ -66,8 +66,8 @@ def lib():
         L.jfa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.jfa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.jfa_fwd.restype = i32
-        L.jfa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
-                              ctypes.c_size_t, vp]
+        L.jfa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
+                              vp, vp, ctypes.c_size_t, vp]
         L.jfa_bwd.restype = i32
         L.jfa_status_string.argtypes = [i32]
         L.jfa_status_string.restype = ctypes.c_char_p
@@ -141,12 +141,14 @@ def fwd(p: Problem, q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, ou
                          _ptr(lse), _stream(stream)))
 
 
-def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
-        dq, dk, dv, workspace, stream=None):
+def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+        q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv, workspace,
+        stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().jfa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                         _ptr(lse), _ptr(offsets_dev), _ptr(slot_ptr_dev), _ptr(tiles_dev),
-                         int(num_slots), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                         _ptr(lse), _ptr(offsets_dev), _ptr(q_slot_ptr_dev), _ptr(q_tiles_dev),
+                         int(q_num_slots), _ptr(kv_slot_ptr_dev), _ptr(kv_tiles_dev),
+                         int(kv_num_slots), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                          ws_bytes, _stream(stream)))
 
 
@@ -191,7 +193,7 @@ class Plan:
                     if len(tl) else torch.zeros((1, 4), dtype=torch.int32, device=self.device)
                 self.sched[kind] = sch
         nbytes = bwd_workspace_bytes(self.p)
-        self.workspace = (torch.empty(nbytes // 4, dtype=torch.float32, device=self.device)
+        self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=self.device)
                           if nbytes else None)
 
     @property
@@ -227,8 +229,10 @@ class Plan:
         dq = dq if dq is not None else torch.empty_like(q)
         dk = dk if dk is not None else torch.empty_like(k)
         dv = dv if dv is not None else torch.empty_like(v)
-        s = self.sched.get(KIND_BWD)
+        sq, skv = self.sched.get(KIND_FWD), self.sched.get(KIND_BWD)
         bwd(self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
-            s.slot_ptr_dev if s else None, s.tiles_dev if s else None, s.num_slots if s else 0,
+            sq.slot_ptr_dev if sq else None, sq.tiles_dev if sq else None,
+            sq.num_slots if sq else 0, skv.slot_ptr_dev if skv else None,
+            skv.tiles_dev if skv else None, skv.num_slots if skv else 0,
             dq, dk, dv, self.workspace, stream)
         return dq, dk, dv

@@ -92,9 +92,11 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
 
 extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
                               const void* out, const void* dout, const float* lse,
-                              const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
-                              const int32_t* tiles_dev, int32_t num_slots, void* dq, void* dk,
-                              void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                              const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
+                              const int32_t* q_tiles_dev, int32_t q_num_slots,
+                              const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                              int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   set_error("");
   if (jfa_status s = check_problem(p)) return s;
   const bool blk = p->flags & JFA_BLOCK_DIAG64;
@@ -112,9 +114,14 @@ extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k
     if (jfa_status s = need(dk, "dk")) return s;
     if (jfa_status s = need(dv, "dv")) return s;
   }
-  BwdLaunch a{q, k, v, out, dout, lse, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, dq, dk, dv,
-              static_cast<float*>(workspace), p->num_seqs, p->num_heads, p->head_dim, p->lq,
-              p->total_kv, p->scale, p->flags, stream};
+  BwdLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.offsets = offsets_dev;
+  a.q_slot_ptr = q_slot_ptr_dev; a.q_tiles = q_tiles_dev; a.q_num_slots = q_num_slots;
+  a.kv_slot_ptr = kv_slot_ptr_dev; a.kv_tiles = kv_tiles_dev; a.kv_num_slots = kv_num_slots;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
+  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.stream = stream;
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is read)");
     if (p->total_kv == 0) return JFA_OK;
@@ -129,8 +136,19 @@ extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k
                                          std::to_string(workspace_bytes));
     if (!aligned(workspace, 256)) return fail(JFA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   }
-  if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
+  if (p->total_kv > 0) {
+    if (jfa_status s = check_schedule_args(p, offsets_dev, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots))
+      return s;
+    if (!bq) {
+      if (jfa_status s = check_schedule_args(p, offsets_dev, q_slot_ptr_dev, q_tiles_dev, q_num_slots))
+        return s;
+    }
+  } else if (bq) {
+    if (jfa_status s = need(offsets_dev, "offsets_dev", 4)) return s;
+  }
   if (q_rows(p) == 0 && p->total_kv == 0) return JFA_OK;
-  (void)bq;
+  a.di = static_cast<float*>(workspace);
+  a.groups = bcast_groups(p->num_seqs);
+  a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p)) : nullptr;
   return launch_bwd(a);
 }

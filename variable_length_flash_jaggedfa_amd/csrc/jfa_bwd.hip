@@ -1,83 +1,424 @@
-// Jagged flash attention backward for gfx950 (persistent, MFMA bf16).
+// Jagged flash attention backward for gfx950 (MFMA bf16), without atomics.
 //
-// A tile is 128 keys of one (sequence, head); each of the 4 waves keeps 32 keys
-// of K and V in registers together with its dK^T and dV^T accumulators. The
-// workgroup walks the 64-row query steps that can attend those keys. Per step:
-//   - Q, dO (row-major and transposed) go to LDS; Di = rowsum(dO * out) is summed
-//     while they are staged, so no separate preprocessing pass runs ("TLX Block
-//     Attention", sections 2 and 4);
-//   - S = Q K^T and dP = dO V^T (lane = key, registers = query rows);
-//   - P = 2^(S*scale*log2e - lse*log2e) rebuilt from the saved lse;
-//     dS = P * (dP - Di);
-//   - dV^T += dO^T P and dK^T += Q^T dS, P and dS fed from the accumulators;
-//   - dS goes to LDS so the whole workgroup forms dQ = dS K over its 128 keys
-//     (the staging of the dQ partial before the global sum), and one fp32 atomic
-//     per element adds it into the dQ accumulator ("Jagged Flash Attention for
-//     GEM", backward / dQ section). For broadcast-Q every tile of a head adds into
-//     the same [Lq, D] slice.
-// A finalize pass converts the accumulator to bf16 and applies the scale.
-#include "jfa_device.h"
+// The backward rebuilds P from Q, K and the saved lse, forms Di = rowsum(dO*out)
+// inline ("TLX Block Attention", sections 2 and 4) and produces dQ, dK and dV.
+// It runs as two passes over the same tiles the host scheduler deals
+// ("Jagged Flash Attention for GEM", backward / dQ section):
+//
+//   dQ pass (query-tile outer, forward schedule). Each wave keeps 32 query rows
+//     of Q and dO in registers, computes Di for them, and streams the keys of
+//     its sequence through a 3-stage LDS ring: S^T = K Q^T and dP^T = V dO^T,
+//     P = 2^(S*scale*log2e - lse*log2e), dS = P * (dP - Di), dQ^T += K^T dS^T.
+//     dQ stays in registers and is written once; Di is written for the other pass.
+//   dK/dV pass (key-tile outer, backward schedule). Each wave keeps 32 keys of K
+//     and V in registers with its dK^T and dV^T accumulators and streams the
+//     query rows (Q, dO, lse, Di) through a 3-stage LDS ring: S = Q K^T and
+//     dP = dO V^T, P and dS as above, dV^T += dO^T P and dK^T += Q^T dS.
+//
+// Each pass recomputes S and dP, so the backward runs 7 matrix products instead
+// of 5; in exchange no partial result is ever summed through memory atomics.
+// For broadcast-Q every sequence adds into the same dQ: the dQ pass gives each
+// workgroup a (query tile, head, group of sequences), accumulates on chip over
+// the group, stores one float32 partial per group, and a last kernel sums the
+// partials in a fixed order.
 #include "jfa_internal.h"
+#include "jfa_tiles.h"
 
 using namespace jfa_dev;
 
 namespace {
 
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------- dQ pass
 template <int D>
-struct BwdCfg {
-  static constexpr int BN = jfa::kBwdBN;  // 128 keys per tile
-  static constexpr int BM = jfa::kBwdBM;  // 64 query rows per step
-  static constexpr int NT = 256;
-  static constexpr int QS = D + 8;        // row stride of Q / dO tiles [BM][D]
-  static constexpr int TS = BM + 8;       // row stride of Q^T / dO^T tiles [D][BM]
-  static constexpr int SS = BN + 8;       // row stride of the dS tile [BM][BN]
-  static constexpr int KS = D + 8;        // row stride of the K staging tile [BN][D]
+struct DqCfg {
+  static constexpr int BM = jfa::kFwdBM;         // query rows per tile (forward tiles)
+  static constexpr int NW = BM / 32;             // waves, 32 rows each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BN = D == 128 ? 32 : 64;  // keys per step
+  static constexpr int KB = BN / 32;
+  static constexpr int NS = 3;                   // LDS ring stages
   static constexpr int DS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int GRP = (BM / 4) * CH;       // (4-row group, chunk) pairs of a step
-  // LDS carve-up (elements of 16 bits)
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + BM * QS;
-  static constexpr int OFF_QT = OFF_DO + BM * QS;
-  static constexpr int OFF_DOT = OFF_QT + D * TS;
-  static constexpr int OFF_DS = OFF_DOT + D * TS;
-  static constexpr int OFF_F32 = OFF_DS + BM * SS;        // lse[BM], Di[2][BM] as floats
-  static constexpr int ELEMS = OFF_F32 + 2 * 3 * BM;
-  static_assert(BN * KS <= OFF_DS, "K staging tile must fit below the dS tile");
-  // dQ work split: (BM/32) x NB blocks of 32x32 over 4 waves
-  static constexpr int DQ_BLOCKS = (BM / 32) * NB / 4;
+  static constexpr int TILE = BN * D;
+  static constexpr int STAGE = 2 * TILE;         // K then V
+  static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;
 };
 
-struct BwdParams {
+struct DqParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* o; const uint16_t* dout;
   const float* lse;
+  float* di;                  // Di out, same layout as lse
   const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
-  uint16_t* dk; uint16_t* dv;
-  float* dq_acc;
-  int32_t H, lq, total_kv;
-  float c;      // scale * log2(e)
-  float scale;
+  uint16_t* dq;               // jagged: bf16 dQ
+  float* dq_part;             // broadcast: [groups][Lq][H][D] float32 partials
+  int32_t H, lq, total_kv, num_seqs, groups;
+  float c, scale;
 };
 
-template <int D, bool CAUSAL, bool BCAST>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-bwd_kernel(BwdParams P) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::ELEMS];
-  uint16_t* Qs = lds + C::OFF_Q;
-  uint16_t* dOs = lds + C::OFF_DO;
-  uint16_t* QTs = lds + C::OFF_QT;
-  uint16_t* dOTs = lds + C::OFF_DOT;
-  uint16_t* dSs = lds + C::OFF_DS;
-  float* lse_s = reinterpret_cast<float*>(lds + C::OFF_F32);
-  float* di_s = lse_s + C::BM;  // two buffers of BM
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
+                                        const u32x4 (&qf)[DqCfg<D>::DS],
+                                        const u32x4 (&dof)[DqCfg<D>::DS],
+                                        f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
+                                        float c, int lane, int key0, int n_keys, int qpos) {
+  using C = DqCfg<D>;
+  constexpr int KB = C::KB;
+  const int g = lane >> 5, li = lane & 31;
+  f32x16 s[KB], dp[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    s[kb] = f32x16{};
+    dp[kb] = f32x16{};
+  }
+  // S^T = K Q^T and dP^T = V dO^T; row fragments one k-step ahead
+  u32x4 ka[KB], va[KB], kn[KB], vn[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    ka[kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
+    va[kb] = frag_rows<D>(vs, kb * 32, 0, li, g);
+  }
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d) {
+    if (d + 1 < C::DS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        kn[kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
+        vn[kb] = frag_rows<D>(vs, kb * 32, d + 1, li, g);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = mfma32(ka[kb], qf[d], s[kb]);
+      dp[kb] = mfma32(va[kb], dof[d], dp[kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      ka[kb] = kn[kb];
+      va[kb] = vn[kb];
+    }
+  }
+  // P = 2^(S c - lse2), dS = P (dP - Di), packed with keys along the registers
+  u32x4 pds[2 * KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -lse2));
+      float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -lse2));
+      if (MASK) {
+        const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+        p0 = (key >= n_keys || (CAUSAL && key > qpos)) ? 0.f : p0;
+        p1 = (key + 1 >= n_keys || (CAUSAL && key + 1 > qpos)) ? 0.f : p1;
+      }
+      pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
+    }
+  }
+  // dQ^T += K^T dS^T; column fragments of K one step ahead
+  constexpr int NX = 2 * KB * C::NB;
+  u32x4 fa = frag_cols<D>(ks, 0, 0, lane), fn;
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int st = x / C::NB, nb = x % C::NB;
+    if (x + 1 < NX) fn = frag_cols<D>(ks, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+    acc[nb] = mfma32(fa, pds[st], acc[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    fa = fn;
+  }
+}
 
+// Stream the keys [0, n_keys) of one (sequence, head) past one query tile.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
+                                          int64_t rstride, int L, int n_keys, int n_free,
+                                          const u32x4 (&qf)[DqCfg<D>::DS],
+                                          const u32x4 (&dof)[DqCfg<D>::DS],
+                                          f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
+                                          float c, int w, int lane, int qpos) {
+  using C = DqCfg<D>;
+  const int n_steps = ceil_div(n_keys, C::BN);
+  const int rowbytes = int(rstride * 2);
+  auto load_stage = [&](int st, uint16_t* buf) {
+    const int64_t r0 = int64_t(st) * C::BN * rstride;
+    tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
+    tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, L - st * C::BN),
+                               rowbytes, w, lane);
+  };
+#pragma unroll
+  for (int st = 0; st < C::NS - 1; ++st)
+    if (st < n_steps) load_stage(st, lds + st * C::STAGE);
+  for (int kt = 0; kt < n_steps; ++kt) {
+    if (kt + 1 < n_steps)
+      wait_vmem_le<C::LOADS>();
+    else
+      wait_vmem();
+    __syncthreads();
+    if (kt + C::NS - 1 < n_steps) {
+      const int nk = kt + C::NS - 1;
+      load_stage(nk, lds + (nk % C::NS) * C::STAGE);
+    }
+    const uint16_t* cur = lds + (kt % C::NS) * C::STAGE;
+    if (kt < n_free)
+      dq_step<D, false, CAUSAL>(cur, cur + C::TILE, qf, dof, acc, lse2, di, c, lane, kt * C::BN, n_keys, qpos);
+    else
+      dq_step<D, true, CAUSAL>(cur, cur + C::TILE, qf, dof, acc, lse2, di, c, lane, kt * C::BN, n_keys, qpos);
+  }
+  __syncthreads();  // the next stream's first loads overwrite the first stages
+}
+
+// Q and dO fragments of one query row (zero past the end) and its Di.
+template <int D>
+__device__ __forceinline__ float load_row(const uint16_t* qrow, const uint16_t* orow,
+                                          const uint16_t* dorow, bool ok, int g,
+                                          u32x4 (&qf)[DqCfg<D>::DS], u32x4 (&dof)[DqCfg<D>::DS]) {
+  float di = 0.f;
+#pragma unroll
+  for (int d = 0; d < DqCfg<D>::DS; ++d) {
+    qf[d] = ok ? ld16(qrow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    dof[d] = ok ? ld16(dorow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    const u32x4 of = ok ? ld16(orow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      di += bf16_lo(dof[d][e2]) * bf16_lo(of[e2]) + bf16_hi(dof[d][e2]) * bf16_hi(of[e2]);
+  }
+  return pair_sum(di);  // Di = rowsum(dO * out)
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+dq_kernel(DqParams P) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 5;
+  const int slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
+  const int64_t rstride = int64_t(P.H) * D;
+  for (int ti = t_begin; ti < t_end; ++ti) {
+    const int b = P.tiles[4 * ti + 0], h = P.tiles[4 * ti + 1], t = P.tiles[4 * ti + 2];
+    const int kv0 = P.offsets[b];
+    const int L = P.offsets[b + 1] - kv0;
+    const int q_first = t * C::BM;
+    const int q_rows = min(C::BM, L - q_first);
+    const int n_keys = CAUSAL ? min(L, q_first + q_rows) : L;
+    const int n_free = min(ceil_div(n_keys, C::BN), (CAUSAL ? q_first : L) / C::BN);
+    const int qpos = q_first + w * 32 + (lane & 31);
+    const bool ok = qpos < L;
+    const int64_t row = int64_t(kv0) + qpos;
+    const int64_t eoff = row * rstride + int64_t(h) * D;
+    u32x4 qf[C::DS], dof[C::DS];
+    const float di = load_row<D>(P.q + eoff, P.o + eoff, P.dout + eoff, ok, g, qf, dof);
+    const int64_t vidx = int64_t(h) * P.total_kv + row;
+    const float lse2 = ok ? P.lse[vidx] * kLog2e : 0.f;
+    if (ok && g == 0) P.di[vidx] = di;
+    f32x16 acc[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+    dq_stream<D, CAUSAL>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
+                         P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, n_keys, n_free,
+                         qf, dof, acc, lse2, di, P.c, w, lane, qpos);
+    if (ok) {
+      uint16_t* dqrow = P.dq + eoff;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 wv;
+          wv[0] = pack_bf16(acc[nb][q4 * 4 + 0] * P.scale, acc[nb][q4 * 4 + 1] * P.scale);
+          wv[1] = pack_bf16(acc[nb][q4 * 4 + 2] * P.scale, acc[nb][q4 * 4 + 3] * P.scale);
+          st8(dqrow + nb * 32 + q4 * 8 + g * 4, wv);
+        }
+    }
+  }
+}
+
+// Broadcast-Q: workgroup (query tile, head, sequence group).
+template <int D>
+__global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+dq_bcast_kernel(DqParams P) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 5;
+  const int n_qt = ceil_div(P.lq, C::BM);
+  const int t = blockIdx.x % n_qt, h = (blockIdx.x / n_qt) % P.H, grp = blockIdx.x / (n_qt * P.H);
+  const int b0 = int(int64_t(grp) * P.num_seqs / P.groups);
+  const int b1 = int(int64_t(grp + 1) * P.num_seqs / P.groups);
+  const int64_t rstride = int64_t(P.H) * D;
+  const int qpos = t * C::BM + w * 32 + (lane & 31);
+  const bool ok = qpos < P.lq;
+  const uint16_t* qrow = P.q + int64_t(qpos) * rstride + int64_t(h) * D;
+  f32x16 acc[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+  for (int b = b0; b < b1; ++b) {
+    const int kv0 = P.offsets[b];
+    const int L = P.offsets[b + 1] - kv0;
+    const int64_t oeff = (int64_t(b) * P.lq + qpos) * rstride + int64_t(h) * D;
+    u32x4 qf[C::DS], dof[C::DS];
+    const float di = load_row<D>(qrow, P.o + oeff, P.dout + oeff, ok, g, qf, dof);
+    const int64_t vidx = (int64_t(b) * P.H + h) * P.lq + qpos;
+    const float lse2 = ok ? P.lse[vidx] * kLog2e : 0.f;
+    if (ok && g == 0) P.di[vidx] = di;
+    if (L > 0)
+      dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
+                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, L / C::BN,
+                          qf, dof, acc, lse2, di, P.c, w, lane, qpos);
+  }
+  if (ok) {
+    float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(prow + nb * 32 + q4 * 8 + g * 4) =
+            f32x4{acc[nb][q4 * 4 + 0], acc[nb][q4 * 4 + 1], acc[nb][q4 * 4 + 2], acc[nb][q4 * 4 + 3]};
+  }
+}
+
+// dq = bf16(scale * sum over groups of the partials), groups summed in order.
+__global__ void __launch_bounds__(256) dq_reduce_kernel(const float* __restrict__ part,
+                                                       uint16_t* __restrict__ dq, int64_t n4,
+                                                       int groups, float scale) {
+  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
+    f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
+    for (int gi = 1; gi < groups; ++gi) a += reinterpret_cast<const f32x4*>(part)[gi * n4 + i];
+    u32x2 o;
+    o[0] = pack_bf16(a[0] * scale, a[1] * scale);
+    o[1] = pack_bf16(a[2] * scale, a[3] * scale);
+    reinterpret_cast<u32x2*>(dq)[i] = o;
+  }
+}
+
+// ---------------------------------------------------------------- dK/dV pass
+template <int D>
+struct KvCfg {
+  static constexpr int BN = jfa::kBwdBN;  // keys per tile
+  static constexpr int NW = BN / 32;      // waves, 32 keys each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = jfa::kBwdBM;  // query rows per step
+  static constexpr int IB = BM / 32;
+  static constexpr int NS = 3;
+  static constexpr int DS = D / 16;
+  static constexpr int NB = D / 32;
+  static constexpr int TILE = BM * D;
+  static constexpr int STAGE = 2 * TILE;  // Q then dO
+  static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;
+  static constexpr int WPE = 1;           // waves per SIMD the registers allow
+};
+
+struct KvParams {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dout;
+  const float* lse; const float* di;
+  const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
+  uint16_t* dk; uint16_t* dv;
+  int32_t H, lq, total_kv;
+  float c, scale;
+};
+
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos, const float* lse_s,
+                                        const float* di_s, const u32x4 (&kf)[KvCfg<D>::DS],
+                                        const u32x4 (&vf)[KvCfg<D>::DS],
+                                        f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB],
+                                        float c, int lane, int q0, int jw) {
+  using C = KvCfg<D>;
+  constexpr int IB = C::IB;
+  const int g = lane >> 5, li = lane & 31;
+  f32x16 s[IB], dp[IB];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+    s[ib] = f32x16{};
+    dp[ib] = f32x16{};
+  }
+  // S = Q K^T and dP = dO V^T (lane = key); row fragments one k-step ahead
+  u32x4 qa[IB], da[IB], qn[IB], dn[IB];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+    qa[ib] = frag_rows<D>(qs, ib * 32, 0, li, g);
+    da[ib] = frag_rows<D>(dos, ib * 32, 0, li, g);
+  }
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d) {
+    if (d + 1 < C::DS) {
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+        qn[ib] = frag_rows<D>(qs, ib * 32, d + 1, li, g);
+        dn[ib] = frag_rows<D>(dos, ib * 32, d + 1, li, g);
+      }
+    }
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      s[ib] = mfma32(qa[ib], kf[d], s[ib]);
+      dp[ib] = mfma32(da[ib], vf[d], dp[ib]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      qa[ib] = qn[ib];
+      da[ib] = dn[ib];
+    }
+  }
+  // P and dS with query rows along the registers
+  u32x4 pp[2 * IB], pd[2 * IB];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i0 = ib * 32 + q4 * 8 + g * 4;
+      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + i0);
+      const f32x4 di4 = *reinterpret_cast<const f32x4*>(di_s + i0);
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = q4 * 4 + e;
+        float p = exp2_fast(__builtin_fmaf(s[ib][r], c, -lse4[e] * kLog2e));
+        if (MASK && CAUSAL) p = jw > q0 + i0 + e ? 0.f : p;
+        pv[e] = p;
+        dsv[e] = p * (dp[ib][r] - di4[e]);
+      }
+      const int st = ib * 2 + q4 / 2, hw = (q4 % 2) * 2;
+      pp[st][hw] = pack_bf16(pv[0], pv[1]);
+      pp[st][hw + 1] = pack_bf16(pv[2], pv[3]);
+      pd[st][hw] = pack_bf16(dsv[0], dsv[1]);
+      pd[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
+    }
+  }
+  // dV^T += dO^T P, dK^T += Q^T dS; column fragments one step ahead
+  constexpr int NX = 2 * IB * C::NB;
+  u32x4 fa = frag_cols<D>(dos, 0, 0, lane), fb = frag_cols<D>(qs, 0, 0, lane), fan, fbn;
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int st = x / C::NB, nb = x % C::NB;
+    if (x + 1 < NX) {
+      fan = frag_cols<D>(dos, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+      fbn = frag_cols<D>(qs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+    }
+    dv[nb] = mfma32(fa, pp[st], dv[nb]);
+    dk[nb] = mfma32(fb, pd[st], dk[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    fa = fan;
+    fb = fbn;
+  }
+}
+
+template <int D, bool CAUSAL, bool BCAST>
+__global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(KvCfg<D>::WPE)))
+dkdv_kernel(KvParams P) {
+  using C = KvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // lse, Di per stage
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
+  const int rowbytes = int(rstride * 2);
 
   for (int ti = t_begin; ti < t_end; ++ti) {
     const int b = P.tiles[4 * ti + 0], h = P.tiles[4 * ti + 1], n = P.tiles[4 * ti + 2];
@@ -85,244 +426,80 @@ bwd_kernel(BwdParams P) {
     const int L = P.offsets[b + 1] - kv0;
     const int key0 = n * C::BN;
     const int rows_total = BCAST ? P.lq : L;
-    const int jw = key0 + w * 32 + li;  // this lane's key (inside the sequence)
+    const int jw = key0 + w * 32 + li;  // this lane's key
     const bool key_ok = jw < L;
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
-
-    // resident K / V fragments (B operands of S = Q K^T and dP = dO V^T)
     u32x4 kf[C::DS], vf[C::DS];
 #pragma unroll
     for (int d = 0; d < C::DS; ++d) {
       kf[d] = key_ok ? ld16(kbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
       vf[d] = key_ok ? ld16(vbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
     }
-    // K tile through LDS to build the K^T-side fragments of dQ = dS K
-    for (int c = tid; c < C::BN * C::CH; c += C::NT) {
-      const int j = c / C::CH, cc = c % C::CH;
-      const int row = key0 + j;
-      st16(lds + j * C::KS + cc * 8,
-           row < L ? ld16(kbase + int64_t(row) * rstride + cc * 8) : u32x4{0, 0, 0, 0});
-    }
-    __syncthreads();
-    // dQ blocks of this wave: column block db of D, row blocks ib0 .. ib0+DQ_BLOCKS-1
-    const int dq_db = w % C::NB;
-    const int dq_ib0 = (w / C::NB) * C::DQ_BLOCKS;
-    u32x4 ktf[C::BN / 16];
-#pragma unroll
-    for (int s = 0; s < C::BN / 16; ++s) {
-      u32x4 f;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int j0 = s * 16 + g * 8 + 2 * e2;
-        const uint32_t lo = lds[j0 * C::KS + dq_db * 32 + li];
-        const uint32_t hi = lds[(j0 + 1) * C::KS + dq_db * 32 + li];
-        f[e2] = lo | (hi << 16);
-      }
-      ktf[s] = f;
-    }
-    __syncthreads();
-
-    f32x16 dvacc[C::NB], dkacc[C::NB];
+    f32x16 dv[C::NB], dk[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
-      dvacc[nb] = f32x16{};
-      dkacc[nb] = f32x16{};
+      dv[nb] = f32x16{};
+      dk[nb] = f32x16{};
     }
-
-    const int qt_lo = CAUSAL ? key0 / C::BM : 0;
-    const int qt_hi = ceil_div(rows_total, C::BM);
-    for (int qt = qt_lo; qt < qt_hi; ++qt) {
-      const int par = (qt - qt_lo) & 1;
-      float* di_cur = di_s + par * C::BM;
-      const int q_first = qt * C::BM;
-      // ---- stage Q, dO (row-major + transposed), lse, Di into LDS. The CH chunks
-      // of a 4-row group sit on CH consecutive lanes of one wave, so each row's Di
-      // is reduced with fixed-order lane swaps (deterministic, no atomics).
-      for (int pidx = tid; pidx < C::GRP; pidx += C::NT) {
-        const int cc = pidx % C::CH, jg = pidx / C::CH;
-        u32x4 qv[4], dv4[4];
-        float di_part[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qpos = q_first + 4 * jg + r;
-          const bool ok = qpos < rows_total;
-          const int64_t qrow = BCAST ? int64_t(qpos) : int64_t(kv0) + qpos;
-          const int64_t orow = BCAST ? int64_t(b) * P.lq + qpos : int64_t(kv0) + qpos;
-          qv[r] = ok ? ld16(P.q + qrow * rstride + int64_t(h) * D + cc * 8) : u32x4{0, 0, 0, 0};
-          dv4[r] = ok ? ld16(P.dout + orow * rstride + int64_t(h) * D + cc * 8) : u32x4{0, 0, 0, 0};
-          const u32x4 ov = ok ? ld16(P.o + orow * rstride + int64_t(h) * D + cc * 8) : u32x4{0, 0, 0, 0};
-          float acc = 0.f;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            acc += bf16_lo(dv4[r][e2]) * bf16_lo(ov[e2]);
-            acc += bf16_hi(dv4[r][e2]) * bf16_hi(ov[e2]);
-          }
-#pragma unroll
-          for (int m = 1; m < C::CH; m <<= 1) acc += __shfl_xor(acc, m);
-          di_part[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          st16(Qs + (4 * jg + r) * C::QS + cc * 8, qv[r]);
-          st16(dOs + (4 * jg + r) * C::QS + cc * 8, dv4[r]);
-        }
-        if (cc == 0) *reinterpret_cast<f32x4*>(di_cur + 4 * jg) = f32x4{di_part[0], di_part[1], di_part[2], di_part[3]};
-        const int col = kperm(4 * jg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          u32x2 a, bb;
-          a[0] = half_of(qv[0], e) | (half_of(qv[1], e) << 16);
-          a[1] = half_of(qv[2], e) | (half_of(qv[3], e) << 16);
-          bb[0] = half_of(dv4[0], e) | (half_of(dv4[1], e) << 16);
-          bb[1] = half_of(dv4[2], e) | (half_of(dv4[3], e) << 16);
-          st8(QTs + (cc * 8 + e) * C::TS + col, a);
-          st8(dOTs + (cc * 8 + e) * C::TS + col, bb);
-        }
+    const uint16_t* qbase = BCAST ? P.q + int64_t(h) * D : P.q + int64_t(kv0) * rstride + int64_t(h) * D;
+    const uint16_t* dobase = BCAST ? P.dout + int64_t(b) * P.lq * rstride + int64_t(h) * D
+                                   : P.dout + int64_t(kv0) * rstride + int64_t(h) * D;
+    const int64_t voff = BCAST ? (int64_t(b) * P.H + h) * P.lq : int64_t(h) * P.total_kv + kv0;
+    const int qs_lo = CAUSAL ? key0 / C::BM : 0;
+    const int n_steps = ceil_div(rows_total, C::BM) - qs_lo;
+    auto load_stage = [&](int st, int buf) {
+      const int q_first = (qs_lo + st) * C::BM;
+      const int left = rows_total - q_first;
+      uint16_t* dst = lds + buf * C::STAGE;
+      tile_load<D, C::BM, C::NW>(dst, rows_rsrc<D>(qbase + int64_t(q_first) * rstride, rstride, left),
+                                 rowbytes, w, lane);
+      tile_load<D, C::BM, C::NW>(dst + C::TILE,
+                                 rows_rsrc<D>(dobase + int64_t(q_first) * rstride, rstride, left),
+                                 rowbytes, w, lane);
+      if (w < 2 && lane < C::BM) {
+        const float* src = (w == 0 ? P.lse : P.di) + voff + q_first;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vec_rsrc(src, left), (lds_void_t*)vecs[buf][w], 4,
+                                                 lane * 4, 0, 0, 0);
       }
-      if (tid < C::BM) {
-        const int qpos = q_first + tid;
-        float x = INFINITY;  // rows past the end get P = 0
-        if (qpos < rows_total)
-          x = (BCAST ? P.lse[(int64_t(b) * P.H + h) * P.lq + qpos]
-                     : P.lse[int64_t(h) * P.total_kv + kv0 + qpos]) * kLog2e;
-        lse_s[tid] = x;
-      }
+    };
+#pragma unroll
+    for (int st = 0; st < C::NS - 1; ++st)
+      if (st < n_steps) load_stage(st, st);
+    for (int it = 0; it < n_steps; ++it) {
+      if (it + 1 < n_steps)
+        wait_vmem_le<C::LOADS>();
+      else
+        wait_vmem();
       __syncthreads();
-
-      // ---- S = Q K^T, dP = dO V^T for this wave's 32 keys
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        sacc[ib] = f32x16{};
-        dpacc[ib] = f32x16{};
-      }
-#pragma unroll 2
-      for (int d = 0; d < C::DS; ++d) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const u32x4 aq = ld16(Qs + (ib * 32 + li) * C::QS + d * 16 + g * 8);
-          sacc[ib] = mfma32(aq, kf[d], sacc[ib]);
-          const u32x4 ad = ld16(dOs + (ib * 32 + li) * C::QS + d * 16 + g * 8);
-          dpacc[ib] = mfma32(ad, vf[d], dpacc[ib]);
-        }
-      }
-
-      const bool mask = (CAUSAL && q_first < key0 + C::BN) || (key0 + C::BN > L);
-      u32x4 pp[4], pds[4];
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int i0 = ib * 32 + q4 * 8 + g * 4;
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + i0);
-          const f32x4 di4 = *reinterpret_cast<const f32x4*>(di_cur + i0);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = q4 * 4 + e;
-            float p = exp2_fast(sacc[ib][r] * P.c - lse4[e]);
-            if (mask) {
-              const int qpos = q_first + i0 + e;
-              const bool dead = !key_ok || (CAUSAL && jw > qpos);
-              p = dead ? 0.f : p;
-            }
-            pv[e] = p;
-            dsv[e] = p * (dpacc[ib][r] - di4[e]);
-          }
-          // step s = ib*2 + q4/2 covers rows ib*32 + 16*(q4/2) .. +15
-          const int s = ib * 2 + q4 / 2;
-          const int hw = (q4 % 2) * 2;
-          pp[s][hw] = pack_bf16(pv[0], pv[1]);
-          pp[s][hw + 1] = pack_bf16(pv[2], pv[3]);
-          pds[s][hw] = pack_bf16(dsv[0], dsv[1]);
-          pds[s][hw + 1] = pack_bf16(dsv[2], dsv[3]);
-        }
-      }
-      // ---- dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll 2
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const u32x4 a = ld16(dOTs + (nb * 32 + li) * C::TS + s * 16 + g * 8);
-          dvacc[nb] = mfma32(a, pp[s], dvacc[nb]);
-          const u32x4 aq = ld16(QTs + (nb * 32 + li) * C::TS + s * 16 + g * 8);
-          dkacc[nb] = mfma32(aq, pds[s], dkacc[nb]);
-        }
-      }
-      // ---- dS tile to LDS as [row i][key j]
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          // register pair x of step s holds rows (s/2)*32 + ((s%2)*2 + x/2)*8 + g*4 + 2*(x%2) + {0,1}
-          const int i0 = (s / 2) * 32 + ((s % 2) * 2 + x / 2) * 8 + g * 4 + 2 * (x % 2);
-          dSs[i0 * C::SS + w * 32 + li] = uint16_t(pds[s][x] & 0xffffu);
-          dSs[(i0 + 1) * C::SS + w * 32 + li] = uint16_t(pds[s][x] >> 16);
-        }
-      }
-      __syncthreads();
-
-      // ---- dQ partial over the workgroup's 128 keys, then fp32 atomics
-#pragma unroll
-      for (int x = 0; x < C::DQ_BLOCKS; ++x) {
-        const int ib = dq_ib0 + x;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < C::BN / 16; ++s) {
-          const u32x4 a = ld16(dSs + (ib * 32 + li) * C::SS + s * 16 + g * 8);
-          acc = mfma32(a, ktf[s], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = ib * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          const int qpos = q_first + i;
-          if (qpos < rows_total) {
-            const int64_t row = BCAST ? int64_t(qpos) : int64_t(kv0) + qpos;
-            unsafeAtomicAdd(P.dq_acc + row * rstride + int64_t(h) * D + dq_db * 32 + li, acc[r]);
-          }
-        }
-      }
+      if (it + C::NS - 1 < n_steps) load_stage(it + C::NS - 1, (it + C::NS - 1) % C::NS);
+      const int buf = it % C::NS;
+      const uint16_t* cur = lds + buf * C::STAGE;
+      const int q0 = (qs_lo + it) * C::BM;
+      // only causal steps that reach the diagonal need a mask; rows past the end
+      // read as zeros and contribute nothing
+      if (CAUSAL && q0 < key0 + C::BN)
+        kv_step<D, true, CAUSAL>(cur, cur + C::TILE, vecs[buf][0], vecs[buf][1], kf, vf, dv, dk, P.c, lane, q0, jw);
+      else
+        kv_step<D, false, CAUSAL>(cur, cur + C::TILE, vecs[buf][0], vecs[buf][1], kf, vf, dv, dk, P.c, lane, q0, jw);
     }
-    __syncthreads();  // the next tile reuses the Q/dO region for its K staging
-
-    // ---- dK = scale * dK^T, dV = dV^T (bf16)
+    __syncthreads();  // the next tile's first loads overwrite the first stages
     if (key_ok) {
       uint16_t* dkrow = P.dk + (int64_t(kv0) + jw) * rstride + int64_t(h) * D;
       uint16_t* dvrow = P.dv + (int64_t(kv0) + jw) * rstride + int64_t(h) * D;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           u32x2 a, bb;
-          a[0] = pack_bf16(dkacc[nb][q4 * 4 + 0] * P.scale, dkacc[nb][q4 * 4 + 1] * P.scale);
-          a[1] = pack_bf16(dkacc[nb][q4 * 4 + 2] * P.scale, dkacc[nb][q4 * 4 + 3] * P.scale);
-          bb[0] = pack_bf16(dvacc[nb][q4 * 4 + 0], dvacc[nb][q4 * 4 + 1]);
-          bb[1] = pack_bf16(dvacc[nb][q4 * 4 + 2], dvacc[nb][q4 * 4 + 3]);
+          a[0] = pack_bf16(dk[nb][q4 * 4 + 0] * P.scale, dk[nb][q4 * 4 + 1] * P.scale);
+          a[1] = pack_bf16(dk[nb][q4 * 4 + 2] * P.scale, dk[nb][q4 * 4 + 3] * P.scale);
+          bb[0] = pack_bf16(dv[nb][q4 * 4 + 0], dv[nb][q4 * 4 + 1]);
+          bb[1] = pack_bf16(dv[nb][q4 * 4 + 2], dv[nb][q4 * 4 + 3]);
           st8(dkrow + nb * 32 + q4 * 8 + g * 4, a);
           st8(dvrow + nb * 32 + q4 * 8 + g * 4, bb);
         }
-      }
     }
-  }
-}
-
-// zero a float buffer (n is a multiple of 4)
-__global__ void __launch_bounds__(256) zero_kernel(float* __restrict__ x, int64_t n4) {
-  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256)
-    reinterpret_cast<f32x4*>(x)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// dq = bf16(scale * acc), 4 elements per thread step
-__global__ void __launch_bounds__(256) dq_finalize_kernel(const float* __restrict__ acc,
-                                                         uint16_t* __restrict__ dq, int64_t n4,
-                                                         float scale) {
-  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[i];
-    u32x2 o;
-    o[0] = pack_bf16(a[0] * scale, a[1] * scale);
-    o[1] = pack_bf16(a[2] * scale, a[3] * scale);
-    reinterpret_cast<u32x2*>(dq)[i] = o;
   }
 }
 
@@ -333,43 +510,69 @@ int grid_for(int64_t n4) {
 
 template <int D, bool CAUSAL, bool BCAST>
 jfa_status launch_t(const jfa::BwdLaunch& a) {
-  BwdParams P;
-  P.q = static_cast<const uint16_t*>(a.q);
-  P.k = static_cast<const uint16_t*>(a.k);
-  P.v = static_cast<const uint16_t*>(a.v);
-  P.o = static_cast<const uint16_t*>(a.out);
-  P.dout = static_cast<const uint16_t*>(a.dout);
-  P.lse = a.lse;
-  P.offsets = a.offsets;
-  P.slot_ptr = a.slot_ptr;
-  P.tiles = a.tiles;
-  P.dk = static_cast<uint16_t*>(a.dk);
-  P.dv = static_cast<uint16_t*>(a.dv);
-  P.dq_acc = a.dq_acc;
-  P.H = a.num_heads;
-  P.lq = a.lq;
-  P.total_kv = int32_t(a.total_kv);
-  P.c = a.scale * kLog2e;
-  P.scale = a.scale;
   hipStream_t st = static_cast<hipStream_t>(a.stream);
-  const int64_t rows = BCAST ? int64_t(a.lq) : a.total_kv;
-  const int64_t n4 = rows * a.num_heads * D / 4;
-  if (n4 > 0) hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_acc, n4);
-  if (a.total_kv > 0)
-    hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, BCAST>), dim3(a.num_slots), dim3(256), 0, st, P);
-  if (n4 > 0)
-    hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_acc,
-                       static_cast<uint16_t*>(a.dq), n4, a.scale);
+  const float c = a.scale * kLog2e;
+  DqParams dp{};
+  dp.q = static_cast<const uint16_t*>(a.q);
+  dp.k = static_cast<const uint16_t*>(a.k);
+  dp.v = static_cast<const uint16_t*>(a.v);
+  dp.o = static_cast<const uint16_t*>(a.out);
+  dp.dout = static_cast<const uint16_t*>(a.dout);
+  dp.lse = a.lse;
+  dp.di = a.di;
+  dp.offsets = a.offsets;
+  dp.slot_ptr = a.q_slot_ptr;
+  dp.tiles = a.q_tiles;
+  dp.dq = static_cast<uint16_t*>(a.dq);
+  dp.dq_part = a.dq_part;
+  dp.H = a.num_heads;
+  dp.lq = a.lq;
+  dp.total_kv = int32_t(a.total_kv);
+  dp.num_seqs = a.num_seqs;
+  dp.groups = a.groups;
+  dp.c = c;
+  dp.scale = a.scale;
+  if (BCAST) {
+    const int n_qt = (a.lq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+    hipLaunchKernelGGL(dq_bcast_kernel<D>, dim3(n_qt * a.num_heads * a.groups), dim3(DqCfg<D>::NT),
+                       0, st, dp);
+    const int64_t n4 = int64_t(a.lq) * a.num_heads * D / 4;
+    hipLaunchKernelGGL(dq_reduce_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_part,
+                       static_cast<uint16_t*>(a.dq), n4, a.groups, a.scale);
+  } else if (a.total_kv > 0) {
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st, dp);
+  }
+  if (a.total_kv > 0) {
+    KvParams kp{};
+    kp.q = dp.q;
+    kp.k = dp.k;
+    kp.v = dp.v;
+    kp.dout = dp.dout;
+    kp.lse = a.lse;
+    kp.di = a.di;
+    kp.offsets = a.offsets;
+    kp.slot_ptr = a.kv_slot_ptr;
+    kp.tiles = a.kv_tiles;
+    kp.dk = static_cast<uint16_t*>(a.dk);
+    kp.dv = static_cast<uint16_t*>(a.dv);
+    kp.H = a.num_heads;
+    kp.lq = a.lq;
+    kp.total_kv = int32_t(a.total_kv);
+    kp.c = c;
+    kp.scale = a.scale;
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST>), dim3(a.kv_num_slots), dim3(KvCfg<D>::NT), 0,
+                       st, kp);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("bwd launch: ") + hipGetErrorString(e));
   return JFA_OK;
 }
 
 template <int D, bool CAUSAL, bool BCAST>
-int occupancy() {
+int occupancy_kv() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_kernel<D, CAUSAL, BCAST>, 256, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_kernel<D, CAUSAL, BCAST>, KvCfg<D>::NT,
+                                                   0) != hipSuccess)
     return 0;
   return n;
 }
@@ -392,10 +595,10 @@ jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu) {
   const bool causal = flags & JFA_CAUSAL, bq = flags & JFA_BROADCAST_Q;
   int n;
   if (head_dim == 128)
-    n = bq ? occupancy<128, false, true>() : causal ? occupancy<128, true, false>() : occupancy<128, false, false>();
+    n = bq ? occupancy_kv<128, false, true>() : causal ? occupancy_kv<128, true, false>() : occupancy_kv<128, false, false>();
   else
-    n = bq ? occupancy<64, false, true>() : causal ? occupancy<64, true, false>() : occupancy<64, false, false>();
-  if (n <= 0) return fail(JFA_ERR_HIP, "occupancy query failed for the backward kernel");
+    n = bq ? occupancy_kv<64, false, true>() : causal ? occupancy_kv<64, true, false>() : occupancy_kv<64, false, false>();
+  if (n <= 0) return fail(JFA_ERR_HIP, "occupancy query failed for the dK/dV kernel");
   *per_cu = n;
   return JFA_OK;
 }

@@ -13,7 +13,7 @@ namespace jfa {
 constexpr int kFwdBM = 128;    // query rows per forward tile (4 waves x 32 rows)
 constexpr int kFwdBN = 64;     // keys per forward KV step
 constexpr int kBwdBN = 128;    // key rows per backward tile (4 waves x 32 keys)
-constexpr int kBwdBM = 64;     // query rows per backward Q step
+constexpr int kBwdBM = 64;     // query rows per backward query step
 constexpr int kBlock = 64;     // block-diagonal group size
 
 // thread-local error text
@@ -39,16 +39,24 @@ struct FwdLaunch {
 struct BwdLaunch {
   const void* q; const void* k; const void* v; const void* out; const void* dout;
   const float* lse;
-  const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
-  int32_t num_slots;
+  const int32_t* offsets;
+  const int32_t* q_slot_ptr; const int32_t* q_tiles; int32_t q_num_slots;    // forward tiles
+  const int32_t* kv_slot_ptr; const int32_t* kv_tiles; int32_t kv_num_slots; // backward tiles
   void* dq; void* dk; void* dv;
-  float* dq_acc;
+  float* di;        // workspace: Di, laid out like lse
+  float* dq_part;   // workspace: broadcast-Q dQ partials [groups][Lq][H][D]
+  int32_t groups;   // broadcast-Q sequence groups
   int32_t num_seqs, num_heads, head_dim, lq;
   int64_t total_kv;
   float scale;
   uint32_t flags;
   void* stream;
 };
+
+// broadcast-Q backward: sequences are split into this many contiguous groups
+int bcast_groups(int num_seqs);
+// bytes of the Di part of the backward workspace (rounded up to 256)
+size_t di_bytes(const jfa_problem* p);
 
 jfa_status launch_fwd(const FwdLaunch& a);
 jfa_status launch_bwd(const BwdLaunch& a);

@@ -1,0 +1,105 @@
+// LDS tile helpers for the gfx950 kernels: swizzled row-major tiles filled by
+// direct global->LDS loads, and the two ways an MFMA fragment is read back.
+//
+// A tile holds ROWS x D bf16 values row-major with no padding. Each row is D/8
+// chunks of 16 bytes; chunk c of row r is stored at position c ^ f(r). f is
+// chosen so that (a) 16 consecutive rows reading the same chunk, and (b) 4
+// consecutive rows reading two neighbouring chunks, all land in distinct 16-byte
+// bank groups.
+//
+// Fragment reads (lane = 32*g + li, see jfa_device.h):
+//   frag_rows: 8 consecutive columns (chunk 2*kc+g) of row r0+li -- an A or B
+//     operand whose 32-index runs down the rows and whose k runs along a row.
+//   frag_cols: rows k0..k0+15 of column c0+li, in the order an accumulator tile
+//     hands its rows to the next product (row (e/4)*8 + 4*g + e%4 for element e),
+//     built from two ds_read_b64_tr_b16. That instruction works on groups of 16
+//     lanes: if lane s of a group loads the 4 values X[a + s/4][b + 4*(s%4) .. +3],
+//     lane j of the group receives X[a + e][b + j] for e = 0..3.
+#pragma once
+
+#include "jfa_device.h"
+
+namespace jfa_dev {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+typedef __fp16 f16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) f16x4_t lds_f16x4_t;
+
+template <int D>
+struct Swz {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __device__ static __forceinline__ int f(int r) {
+    const int m = CPR == 16 ? r : (r >> 1);
+    return (2 * m + m / (CPR / 2)) & (CPR - 1);
+  }
+  // element offset of logical chunk c of row r
+  __device__ static __forceinline__ int chunk(int r, int c) { return r * D + ((c ^ f(r)) << 3); }
+};
+
+// Buffer resource over rows [0, nrows) of a bf16 matrix whose rows are `rstride`
+// elements apart and D elements wide. Loads past the last row return zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t rstride,
+                                                            int nrows) {
+  const int nbytes = nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+}
+
+// Buffer resource over n floats.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t vec_rsrc(const float* base, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, n > 0 ? n * 4 : 0,
+                                           0x00020000);
+}
+
+// Fill a ROWS x D tile from the rows [0, ROWS) of `rsrc` with direct buffer->LDS
+// 16-byte loads issued by the NW waves of the workgroup (rows the resource does
+// not cover arrive as zeros).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load(uint16_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
+                                          int rowbytes, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int INSTR = ROWS * CPR / 64;  // one instruction moves 64 chunks
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < INSTR / NW; ++i) {
+    const int blk = wave * (INSTR / NW) + i;
+    const int q = blk * 64 + lane;  // LDS chunk index within the tile
+    const int r = q / CPR;
+    const int c = (q % CPR) ^ Swz<D>::f(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + blk * 512), 16,
+                                             r * rowbytes + c * 16, 0, 0, 0);
+  }
+}
+
+// 64 floats (entries [0, 64) of `rsrc`) with direct 4-byte loads by one wave.
+__device__ __forceinline__ void vec64_load(float* lds_vec, __amdgpu_buffer_rsrc_t rsrc, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_vec, 4, lane * 4, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Row-major fragment: row r0 + li, columns (2*kc + g)*8 .. +7.
+template <int D>
+__device__ __forceinline__ u32x4 frag_rows(const uint16_t* tile, int r0, int kc, int li, int g) {
+  return ld16(tile + Swz<D>::chunk(r0 + li, 2 * kc + g));
+}
+
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  const f16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Column fragment: rows k0 + (e/4)*8 + 4*g + e%4 (e = 0..7) of column c0 + li.
+template <int D>
+__device__ __forceinline__ u32x4 frag_cols(const uint16_t* tile, int k0, int c0, int lane) {
+  const int G = lane >> 4, j = lane & 15, g = lane >> 5;
+  const int col = c0 + (G & 1) * 16 + 4 * (j & 3);
+  const int r = k0 + g * 4 + (j >> 2);
+  const int cc = col >> 3, within = col & 7;
+  const u32x2 lo = ld_tr(tile + Swz<D>::chunk(r, cc) + within);
+  const u32x2 hi = ld_tr(tile + Swz<D>::chunk(r + 8, cc) + within);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+}  // namespace jfa_dev

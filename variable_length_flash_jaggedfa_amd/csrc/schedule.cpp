@@ -185,11 +185,25 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   return JFA_OK;
 }
 
+namespace jfa {
+
+int bcast_groups(int num_seqs) { return num_seqs < 1 ? 1 : (num_seqs < 64 ? num_seqs : 64); }
+
+size_t di_bytes(const jfa_problem* p) {
+  const int64_t n = (p->flags & JFA_BROADCAST_Q) ? int64_t(p->num_seqs) * p->num_heads * p->lq
+                                                 : int64_t(p->num_heads) * p->total_kv;
+  return (size_t(n) * sizeof(float) + 255) / 256 * 256;
+}
+
+}  // namespace jfa
+
 extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
   if (!p || check_problem(p) != JFA_OK) return 0;
   if (p->flags & JFA_BLOCK_DIAG64) return 0;
-  const int64_t rows = (p->flags & JFA_BROADCAST_Q) ? p->lq : p->total_kv;
-  return size_t(rows) * p->num_heads * p->head_dim * sizeof(float);
+  size_t bytes = di_bytes(p);
+  if (p->flags & JFA_BROADCAST_Q)
+    bytes += size_t(bcast_groups(p->num_seqs)) * p->lq * p->num_heads * p->head_dim * sizeof(float);
+  return bytes;
 }
 
 extern "C" const char* jfa_status_string(jfa_status s) {
