@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
                              "block64_d128", "imbalance"])
-    ap.add_argument("--order", default="zigzag", choices=["zigzag", "inorder"])
+    ap.add_argument("--order", default="zigzag", choices=["zigzag", "inorder", "xcd"])
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time the forward with in-order dispatch, interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -150,7 +150,8 @@ def main():
     k = J.to_torch_bf16(case.k).to(dev)
     v = J.to_torch_bf16(case.v).to(dev)
     do = J.to_torch_bf16(case.do).to(dev)
-    order = jfa.ORDER_ZIGZAG if args.order == "zigzag" else jfa.ORDER_INORDER
+    order = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
+             "xcd": jfa.ORDER_XCD_ZIGZAG}[args.order]
 
     runs = []
     sched_ms = 0.0

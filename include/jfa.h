@@ -64,6 +64,9 @@ typedef enum jfa_status {
 #define JFA_KIND_BWD 1
 #define JFA_ORDER_INORDER 0  /* tiles in generation order, tile j to slot j mod S */
 #define JFA_ORDER_ZIGZAG  1  /* sorted by KV work, descending; zigzag deal */
+#define JFA_ORDER_XCD_ZIGZAG 2 /* the same deal inside each of the 8 XCDs, after whole
+                                  (sequence, head) units are dealt zigzag by total
+                                  work over the XCDs; num_slots % 8 == 0 */
 
 typedef struct jfa_problem {
   int32_t num_seqs;   /* B >= 0 */
@@ -106,6 +109,11 @@ jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host,
  *   Generation order is b, then h, then t. ZIGZAG: stable sort by descending
  *   work, sorted position j goes to pass j / S, rank r = j % S, slot r on even
  *   passes and S-1-r on odd ones. INORDER: tile j goes to slot j % S.
+ *   XCD_ZIGZAG: the (b, h) units, with work = sum of their tiles' work, are
+ *   stable-sorted by descending work and dealt zigzag over 8 groups; group x
+ *   owns slots [x*S/8, (x+1)*S/8) (the kernels run those slots on XCD x, so the
+ *   tiles of one sequence share an L2), and its tiles are dealt with the ZIGZAG
+ *   rule over those slots.
  * Outputs (host memory, caller-allocated):
  *   slot_ptr [num_slots + 1]: tiles of slot s are tiles[slot_ptr[s] .. slot_ptr[s+1]).
  *   tiles    [capacity][4] int32 (b, h, t, work), grouped by slot in dealing order.

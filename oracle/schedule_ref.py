@@ -19,6 +19,9 @@ Readings of what the page leaves open:
   * Passes are counted from 0; pass 0 runs from slot 0 upward.
   * "In-order" dispatch deals tiles in generation order round-robin: tile j goes
     to slot j mod S.
+  * The XCD variant (an MI355X refinement: eight dies with separate L2s) first
+    deals whole (sequence, head) units, weighted by their total work, zigzag over
+    the dies, then applies the same rule inside each die's slots.
 Output: slot_ptr [S+1] and tiles [N,4] = (b, h, t, work), grouped by slot, in the
 order each slot received them.
 """
@@ -27,7 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 KIND_FWD, KIND_BWD = 0, 1
-ORDER_INORDER, ORDER_ZIGZAG = 0, 1
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG = 0, 1, 2
 
 
 def ceil_div(a, b):
@@ -57,8 +60,42 @@ def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0):
     return out
 
 
-def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0):
+def _zigzag_rank(j, n):
+    """Position j of a zigzag deal over n places: pass j // n, rank j % n."""
+    p, r = divmod(j, n)
+    return n - 1 - r if p % 2 else r
+
+
+def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0,
+             groups=8):
     tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq)
+    if order == ORDER_XCD_ZIGZAG:
+        # Units are (sequence, head) pairs with the summed work of their tiles;
+        # they are sorted by that work and dealt zigzag over the groups, then each
+        # group's tiles are sorted and dealt zigzag over the group's own slots.
+        assert num_slots % groups == 0
+        per = num_slots // groups
+        units = {}
+        for g, t in enumerate(tiles):
+            units.setdefault((t[0], t[1]), []).append(g)
+        keys = list(units)                      # insertion order = generation order
+        work = {u: sum(tiles[g][3] for g in units[u]) for u in keys}
+        ranked = sorted(range(len(keys)), key=lambda i: (-work[keys[i]], i))
+        group_of = {}
+        for j, i in enumerate(ranked):
+            group_of[keys[i]] = _zigzag_rank(j, groups)
+        per_slot = [[] for _ in range(num_slots)]
+        for x in range(groups):
+            mine = [g for u in keys if group_of[u] == x for g in units[u]]
+            mine.sort(key=lambda g: (-tiles[g][3], g))
+            for j, g in enumerate(mine):
+                per_slot[x * per + _zigzag_rank(j, per)].append(tiles[g])
+        slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+        flat = []
+        for s in range(num_slots):
+            flat.extend(per_slot[s])
+            slot_ptr[s + 1] = len(flat)
+        return slot_ptr, np.asarray(flat, dtype=np.int32).reshape(-1, 4)
     if order == ORDER_ZIGZAG:
         idx = sorted(range(len(tiles)), key=lambda g: (-tiles[g][3], g))
     else:

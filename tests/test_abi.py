@@ -133,7 +133,7 @@ def test_tile_rows():
 
 @pytest.mark.parametrize("name", ["tiny", "gem", "gem_causal", "broadcast", "imbalance"])
 @pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
-@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG])
+@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG])
 def test_cpp_schedule_equals_reference(name, kind, order):
     w = J.standard_workloads()[name]
     L = J.lengths(w)
@@ -141,7 +141,7 @@ def test_cpp_schedule_equals_reference(name, kind, order):
     H = w.num_heads if name != "imbalance" else 4
     flags = (jfa.CAUSAL if w.causal else 0) | (jfa.BROADCAST_Q if w.kind == "broadcast" else 0)
     p = jfa.problem(len(L), H, w.head_dim, int(L.max()), int(off[-1]), 0.1, flags, w.lq)
-    S = 256
+    S = 512
     sp, tl = jfa.schedule(p, off, kind, order, S)
     rows = jfa.tile_rows(kind, w.head_dim, flags)
     sp2, tl2 = R.schedule(L, H, kind, rows, order, S, w.causal, w.lq)

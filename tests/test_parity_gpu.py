@@ -122,28 +122,28 @@ def test_schedule_order_does_not_change_results(gpu):
     w = J.custom(RAGGED, 3, 128, sigma=0.5, seed=14, causal=True)
     case = J.make_case(w)
     a = GpuRun(case, gpu, order=jfa.ORDER_ZIGZAG)
-    b = GpuRun(case, gpu, order=jfa.ORDER_INORDER, num_slots=7)
     oa, la = a.forward()
-    ob, lb = b.forward()
-    assert torch.equal(oa, ob) and torch.equal(la, lb)
-    _, dka, dva = a.backward()
-    _, dkb, dvb = b.backward()
-    assert torch.equal(dka, dkb) and torch.equal(dva, dvb)
+    dqa, dka, dva = (x.clone() for x in a.backward())
+    for order, slots in ((jfa.ORDER_INORDER, 7), (jfa.ORDER_XCD_ZIGZAG, None)):
+        b = GpuRun(case, gpu, order=order, num_slots=slots)
+        ob, lb = b.forward()
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
+        dqb, dkb, dvb = b.backward()
+        assert torch.equal(dqa, dqb) and torch.equal(dka, dkb) and torch.equal(dva, dvb)
 
 
 def test_run_to_run_bitwise(gpu):
     import torch
-    w = J.custom(RAGGED, 2, 128, sigma=0.5, seed=15)
-    run = GpuRun(J.make_case(w), gpu)
-    o1, l1 = run.forward()
-    o1, l1 = o1.clone(), l1.clone()
-    _, dk1, dv1 = run.backward()
-    dk1, dv1 = dk1.clone(), dv1.clone()
-    for _ in range(3):
-        o2, l2 = run.forward()
-        assert torch.equal(o1, o2) and torch.equal(l1, l2)
-        _, dk2, dv2 = run.backward()
-        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    for w in (J.custom(RAGGED, 2, 128, sigma=0.5, seed=15),
+              J.custom([50, 0, 300, 129], 2, 128, sigma=0.5, seed=15, kind="broadcast", lq=130)):
+        run = GpuRun(J.make_case(w), gpu)
+        o1, l1 = (x.clone() for x in run.forward())
+        dq1, dk1, dv1 = (x.clone() for x in run.backward())
+        for _ in range(3):
+            o2, l2 = run.forward()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+            dq2, dk2, dv2 = run.backward()
+            assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
 
 
 def test_block_diag_matches_jagged_path_on_refined_offsets(gpu):

@@ -70,3 +70,31 @@ def test_empty_and_zero_length():
     # broadcast-Q forward keeps tiles of empty sequences (they write zeros)
     sp, t = R.schedule([0], 1, R.KIND_FWD, 64, R.ORDER_ZIGZAG, 2, lq=100)
     assert t.tolist() == [[0, 0, 0, 0], [0, 0, 1, 0]]
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["xcd_cases"], ids=lambda c: c["name"])
+def test_golden_xcd(case):
+    kind = R.KIND_FWD if case["kind"] == "fwd" else R.KIND_BWD
+    sp, t = R.schedule(case["lengths"], case["heads"], kind, case["tile_rows"], R.ORDER_XCD_ZIGZAG,
+                       case["slots"], causal=case["causal"], groups=case["groups"])
+    assert _per_slot(sp, t) == case["schedule"]
+    assert R.slot_loads(sp, t) == case["loads"]
+
+
+@pytest.mark.parametrize("name", ["gem", "gem_causal", "broadcast"])
+def test_xcd_properties(name):
+    w = J.standard_workloads()[name]
+    L = J.lengths(w)
+    S, X = 512, 8
+    sp, t = R.schedule(L, w.num_heads, R.KIND_FWD, 128, R.ORDER_XCD_ZIGZAG, S, w.causal, w.lq)
+    sp0, t0 = R.schedule(L, w.num_heads, R.KIND_FWD, 128, R.ORDER_ZIGZAG, S, w.causal, w.lq)
+    key = lambda a: sorted(map(tuple, a.tolist()))
+    assert key(t) == key(t0)
+    per = S // X
+    home = {}
+    for s in range(S):
+        for b, h, _, _ in t[sp[s]:sp[s + 1]].tolist():
+            assert home.setdefault((b, h), s // per) == s // per   # a unit stays on one XCD
+        assert np.all(np.diff(t[sp[s]:sp[s + 1], 3]) <= 0)
+    group_load = [int(t[sp[x * per]:sp[(x + 1) * per], 3].sum()) for x in range(X)]
+    assert max(group_load) <= 1.1 * np.mean(group_load)

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libjfa.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 CAUSAL, BROADCAST_Q, BLOCK_DIAG64 = 1, 2, 4
 KIND_FWD, KIND_BWD = 0, 1
-ORDER_INORDER, ORDER_ZIGZAG = 0, 1
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG = 0, 1, 2
 
 
 class JfaError(RuntimeError):

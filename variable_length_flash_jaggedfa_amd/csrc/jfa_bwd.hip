@@ -67,6 +67,8 @@ __device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
                                         f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
                                         float c, int lane, int key0, int n_keys, int qpos) {
   using C = DqCfg<D>;
+  // recompute lane-derived LDS addresses here rather than keep them live across steps
+  asm volatile("" : "+v"(lane));
   constexpr int KB = C::KB;
   const int g = lane >> 5, li = lane & 31;
   f32x16 s[KB], dp[KB];
@@ -328,6 +330,8 @@ __device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos,
                                         f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB],
                                         float c, int lane, int q0, int jw) {
   using C = KvCfg<D>;
+  // recompute lane-derived LDS addresses here rather than keep them live across steps
+  asm volatile("" : "+v"(lane));
   constexpr int IB = C::IB;
   const int g = lane >> 5, li = lane & 31;
   f32x16 s[IB], dp[IB];

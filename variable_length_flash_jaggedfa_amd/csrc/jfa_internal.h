@@ -15,6 +15,7 @@ constexpr int kFwdBN = 64;     // keys per forward KV step
 constexpr int kBwdBN = 128;    // key rows per backward tile (4 waves x 32 keys)
 constexpr int kBwdBM = 64;     // query rows per backward query step
 constexpr int kBlock = 64;     // block-diagonal group size
+constexpr int kXcds = 8;       // accelerator complex dies (separate L2s) on MI355X
 
 // thread-local error text
 void set_error(const std::string& msg);

@@ -149,7 +149,7 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
   if (p->flags & JFA_BLOCK_DIAG64)
     return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 runs without a schedule");
-  if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG)
+  if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG)
     return fail(JFA_ERR_INVALID_ARG, "bad order");
   if (num_slots < 1) return fail(JFA_ERR_INVALID_ARG, "num_slots < 1");
   if (!slot_ptr) return fail(JFA_ERR_INVALID_ARG, "slot_ptr is NULL");
@@ -157,23 +157,61 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   if (capacity < count) return fail(JFA_ERR_INVALID_ARG, "tiles capacity too small");
 
   const std::vector<Tile> tiles = enumerate(p, offsets_host, kind);
-  std::vector<int32_t> idx(tiles.size());
-  std::iota(idx.begin(), idx.end(), 0);
-  if (order == JFA_ORDER_ZIGZAG) {
+  std::vector<int32_t> idx;      // tiles in dealing order
+  std::vector<int32_t> slot_of;  // slot of idx[j]
+  auto by_work = [&](int32_t a, int32_t b) { return tiles[a].work > tiles[b].work; };
+  if (order == JFA_ORDER_XCD_ZIGZAG) {
+    constexpr int32_t X = kXcds;
+    if (num_slots % X) return fail(JFA_ERR_INVALID_ARG, "XCD_ZIGZAG needs num_slots % 8 == 0");
+    const int32_t sx = num_slots / X;
+    // units = (sequence, head) pairs, in generation order, with their total work
+    std::vector<int32_t> unit_first, unit_work;
+    for (size_t i = 0; i < tiles.size(); ++i) {
+      if (i == 0 || tiles[i].b != tiles[i - 1].b || tiles[i].h != tiles[i - 1].h) {
+        unit_first.push_back(int32_t(i));
+        unit_work.push_back(0);
+      }
+      unit_work.back() += tiles[i].work;
+    }
+    unit_first.push_back(int32_t(tiles.size()));
+    const int32_t nu = int32_t(unit_work.size());
+    std::vector<int32_t> uorder(nu);
+    std::iota(uorder.begin(), uorder.end(), 0);
+    std::stable_sort(uorder.begin(), uorder.end(),
+                     [&](int32_t a, int32_t b) { return unit_work[a] > unit_work[b]; });
+    std::vector<int32_t> group_of(nu);
+    for (int32_t j = 0; j < nu; ++j) {
+      const int32_t pass = j / X, r = j % X;
+      group_of[uorder[j]] = (pass & 1) ? X - 1 - r : r;
+    }
+    for (int32_t x = 0; x < X; ++x) {
+      std::vector<int32_t> gt;  // this group's tiles, generation order
+      for (int32_t u = 0; u < nu; ++u)
+        if (group_of[u] == x)
+          for (int32_t i = unit_first[u]; i < unit_first[u + 1]; ++i) gt.push_back(i);
+      std::stable_sort(gt.begin(), gt.end(), by_work);
+      for (size_t j = 0; j < gt.size(); ++j) {
+        const int64_t pass = int64_t(j) / sx;
+        const int32_t r = int32_t(int64_t(j) % sx);
+        idx.push_back(gt[j]);
+        slot_of.push_back(x * sx + ((pass & 1) ? sx - 1 - r : r));
+      }
+    }
+  } else {
+    idx.resize(tiles.size());
+    std::iota(idx.begin(), idx.end(), 0);
     // descending work; ties keep generation order
-    std::stable_sort(idx.begin(), idx.end(),
-                     [&](int32_t a, int32_t b) { return tiles[a].work > tiles[b].work; });
+    if (order == JFA_ORDER_ZIGZAG) std::stable_sort(idx.begin(), idx.end(), by_work);
+    // deal: sorted position j -> pass j / S, rank r = j % S
+    slot_of.resize(idx.size());
+    for (size_t j = 0; j < idx.size(); ++j) {
+      const int64_t pass = int64_t(j) / num_slots;
+      const int32_t r = int32_t(int64_t(j) % num_slots);
+      slot_of[j] = (order == JFA_ORDER_ZIGZAG && (pass & 1)) ? num_slots - 1 - r : r;
+    }
   }
-  // deal: sorted position j -> pass j / S, rank r = j % S
-  std::vector<int32_t> slot_of(idx.size());
   std::vector<int32_t> count_of(num_slots, 0);
-  for (size_t j = 0; j < idx.size(); ++j) {
-    const int64_t pass = int64_t(j) / num_slots;
-    const int32_t r = int32_t(int64_t(j) % num_slots);
-    const int32_t s = (order == JFA_ORDER_ZIGZAG && (pass & 1)) ? num_slots - 1 - r : r;
-    slot_of[j] = s;
-    ++count_of[s];
-  }
+  for (int32_t sl : slot_of) ++count_of[sl];
   slot_ptr[0] = 0;
   for (int32_t s = 0; s < num_slots; ++s) slot_ptr[s + 1] = slot_ptr[s] + count_of[s];
   std::vector<int32_t> fill(slot_ptr, slot_ptr + num_slots);
