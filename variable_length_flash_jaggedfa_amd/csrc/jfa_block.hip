@@ -10,8 +10,8 @@
 // and 32 keys in the dK/dV phase. The kernels are bound by HBM traffic (the page
 // puts the arithmetic intensity far below the ridge point), so each unit reads
 // its operands once and writes its outputs once.
-#include "jfa_device.h"
 #include "jfa_internal.h"
+#include "jfa_tiles.h"
 
 using namespace jfa_dev;
 
@@ -21,12 +21,11 @@ constexpr int kBS = jfa::kBlock;  // 64
 
 template <int D>
 struct BlkCfg {
-  static constexpr int NT = 128;          // two waves
-  static constexpr int TS = kBS + 8;      // row stride of transposed tiles [D][64]
+  static constexpr int NW = 2;        // waves: 32 query rows (then 32 keys) each
+  static constexpr int NT = 64 * NW;
   static constexpr int DS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int GRP = (kBS / 4) * CH;   // (4-row group, chunk) pairs of a tile
+  static constexpr int TILE = kBS * D;  // one 64 x D tile
 };
 
 struct BlkParams {
@@ -37,223 +36,190 @@ struct BlkParams {
   float scale;
 };
 
-// Write a 64 x D bf16 tile (rows tok0.., head h) transposed into LDS as [D][64],
-// keys permuted by kperm inside each 16-group.
-template <int D>
-__device__ __forceinline__ void load_transposed(uint16_t* dst, const uint16_t* base, int64_t rstride,
-                                                int tid) {
-  using C = BlkCfg<D>;
-  for (int pidx = tid; pidx < C::GRP; pidx += C::NT) {
-    const int jg = pidx % (kBS / 4), cc = pidx / (kBS / 4);
-    u32x4 x[4];
+// Store a 32 x 32 accumulator block (rows of the output along the registers,
+// one output row per lane) as bf16, times `mul`.
+__device__ __forceinline__ void store_block(uint16_t* row, const f32x16& a, int col0, int g, float mul) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = ld16(base + int64_t(4 * jg + r) * rstride + cc * 8);
-    const int col = kperm(4 * jg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x2 wv;
-      wv[0] = half_of(x[0], e) | (half_of(x[1], e) << 16);
-      wv[1] = half_of(x[2], e) | (half_of(x[3], e) << 16);
-      st8(dst + (cc * 8 + e) * C::TS + col, wv);
-    }
+  for (int q4 = 0; q4 < 4; ++q4) {
+    u32x2 wv;
+    wv[0] = pack_bf16(a[q4 * 4 + 0] * mul, a[q4 * 4 + 1] * mul);
+    wv[1] = pack_bf16(a[q4 * 4 + 2] * mul, a[q4 * 4 + 3] * mul);
+    st8(row + col0 + q4 * 8 + g * 4, wv);
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
-  using C = BlkCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * C::TS];
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
-  const int64_t rstride = int64_t(P.H) * D;
-  const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
-
-  load_transposed<D>(vt, P.v + base, rstride, tid);
-  u32x4 qf[C::DS];
-#pragma unroll
-  for (int d = 0; d < C::DS; ++d) qf[d] = ld16(P.q + base + int64_t(w * 32 + li) * rstride + d * 16 + g * 8);
-  // S^T = K Q^T (64 keys x this wave's 32 queries), fresh accumulators
-  f32x16 s[2];
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-#pragma unroll
-  for (int d = 0; d < C::DS; ++d) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 a = ld16(P.k + base + int64_t(kb * 32 + li) * rstride + d * 16 + g * 8);
-      s[kb] = mfma32(a, qf[d], s[kb]);
-    }
-  }
-  // exact softmax of the one tile: no running max, no correction factor
+// Exact softmax of one 64-key tile held as S^T (keys along the registers, one
+// query per lane pair): returns P packed to bf16 as MFMA operands (keys in the
+// order of an accumulator tile) and keeps P in `s`.
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], float c) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = pair_max(mx) * P.c;
+  mx = pair_max(mx) * c;  // scale > 0, so the max commutes with it
   float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(__builtin_fmaf(s[kb][r], c, -mx));
+      s[kb][r] = p;
+      rs += p;
+    }
+  const float inv = 1.f / pair_sum(rs);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] *= inv;
+}
+
+template <int D>
+__global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
+  using C = BlkCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::TILE];  // K, V
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
+  const int64_t rstride = int64_t(P.H) * D;
+  const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
+  const int rowbytes = int(rstride * 2);
+  tile_load<D, kBS, C::NW>(lds, rows_rsrc<D>(P.k + base, rstride, kBS), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D>(P.v + base, rstride, kBS), rowbytes, w, lane);
+  u32x4 qf[C::DS];
+  const uint16_t* qrow = P.q + base + int64_t(w * 32 + li) * rstride;
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d) qf[d] = ld16(qrow + d * 16 + g * 8);
+  wait_vmem();
+  __syncthreads();
+  // S^T = K Q^T for the 64 keys and this wave's 32 queries, fresh accumulators
+  f32x16 s[2];
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(frag_rows<D>(lds, kb * 32, d, li, g), qf[d], s[kb]);
+  // one tile: the row max and sum are exact at once, nothing is rescaled
+  tile_softmax(s, P.c);
   u32x4 pf[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(s[kb][r] * P.c - mx);
-      const float p1 = exp2_fast(s[kb][r + 1] * P.c - mx);
-      rs += p0 + p1;
-      pf[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0, p1);
-    }
-  }
-  const float inv = 1.f / pair_sum(rs);
-  __syncthreads();
-  // O^T = V^T P^T, one fresh product per 32-column block
+    for (int r = 0; r < 16; r += 2) pf[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(s[kb][r], s[kb][r + 1]);
   uint16_t* orow = P.out + base + int64_t(w * 32 + li) * rstride;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     f32x16 o = f32x16{};
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const u32x4 a = ld16(vt + (nb * 32 + li) * C::TS + step * 16 + g * 8);
-      o = mfma32(a, pf[step], o);
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 wv;
-      wv[0] = pack_bf16(o[q4 * 4 + 0] * inv, o[q4 * 4 + 1] * inv);
-      wv[1] = pack_bf16(o[q4 * 4 + 2] * inv, o[q4 * 4 + 3] * inv);
-      st8(orow + nb * 32 + q4 * 8 + g * 4, wv);
-    }
+    for (int st = 0; st < 4; ++st) o = mfma32(frag_cols<D>(lds + C::TILE, st * 16, nb * 32, lane), pf[st], o);
+    store_block(orow, o, nb * 32, g, 1.f);
   }
 }
 
 template <int D>
 __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * D * C::TS + 2 * kBS * C::TS];
-  uint16_t* KT = lds;
-  uint16_t* QT = KT + D * C::TS;
-  uint16_t* dOT = QT + D * C::TS;
-  uint16_t* Pm = dOT + D * C::TS;      // P as [key][query], queries permuted by kperm
-  uint16_t* dSm = Pm + kBS * C::TS;    // dS as [key][query]
+  // K, V, Q, dO tiles (64 x D) and P^T, dS^T tiles (64 queries x 64 keys)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * C::TILE + 2 * kBS * kBS];
+  uint16_t* Kt = lds;
+  uint16_t* Vt = Kt + C::TILE;
+  uint16_t* Qt = Vt + C::TILE;
+  uint16_t* dOt = Qt + C::TILE;
+  uint16_t* Pt = dOt + C::TILE;
+  uint16_t* dSt = Pt + kBS * kBS;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
-
-  load_transposed<D>(KT, P.k + base, rstride, tid);
-  load_transposed<D>(QT, P.q + base, rstride, tid);
-  load_transposed<D>(dOT, P.dout + base, rstride, tid);
-
-  // ---- phase 1: this wave's 32 query rows (lane = query)
+  const int rowbytes = int(rstride * 2);
+  tile_load<D, kBS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, kBS), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, kBS), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, kBS), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, kBS), rowbytes, w, lane);
+  // out fragments of this lane's query row, for Di = rowsum(dO * out)
   const int i = w * 32 + li;
-  u32x4 qf[C::DS], dof[C::DS];
-  float di = 0.f;
+  u32x4 of[C::DS];
+  const uint16_t* orow = P.o + base + int64_t(i) * rstride;
 #pragma unroll
-  for (int d = 0; d < C::DS; ++d) {
-    qf[d] = ld16(P.q + base + int64_t(i) * rstride + d * 16 + g * 8);
-    dof[d] = ld16(P.dout + base + int64_t(i) * rstride + d * 16 + g * 8);
-    const u32x4 of = ld16(P.o + base + int64_t(i) * rstride + d * 16 + g * 8);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2)
-      di += bf16_lo(dof[d][e2]) * bf16_lo(of[e2]) + bf16_hi(dof[d][e2]) * bf16_hi(of[e2]);
-  }
-  di = pair_sum(di);  // Di = rowsum(dO * out), computed inline
+  for (int d = 0; d < C::DS; ++d) of[d] = ld16(orow + d * 16 + g * 8);
+  wait_vmem();
+  __syncthreads();
+
+  // ---- query side (lane = query): S^T, dP^T, exact softmax, dS^T, dQ^T
   f32x16 s[2], dp[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     s[kb] = f32x16{};
     dp[kb] = f32x16{};
   }
+  float di = 0.f;
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
+    const u32x4 qf = frag_rows<D>(Qt, w * 32, d, li, g);
+    const u32x4 dof = frag_rows<D>(dOt, w * 32, d, li, g);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      di += bf16_lo(dof[e2]) * bf16_lo(of[d][e2]) + bf16_hi(dof[e2]) * bf16_hi(of[d][e2]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 ak = ld16(P.k + base + int64_t(kb * 32 + li) * rstride + d * 16 + g * 8);
-      s[kb] = mfma32(ak, qf[d], s[kb]);
-      const u32x4 av = ld16(P.v + base + int64_t(kb * 32 + li) * rstride + d * 16 + g * 8);
-      dp[kb] = mfma32(av, dof[d], dp[kb]);
+      s[kb] = mfma32(frag_rows<D>(Kt, kb * 32, d, li, g), qf, s[kb]);
+      dp[kb] = mfma32(frag_rows<D>(Vt, kb * 32, d, li, g), dof, dp[kb]);
     }
   }
-  // recompute the exact softmax statistics of the tile (no stored lse)
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = pair_max(mx) * P.c;
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(s[kb][r] * P.c - mx);
-      s[kb][r] = p;
-      rs += p;
-    }
-  const float inv = 1.f / pair_sum(rs);
-  u32x4 pdsT[4];
-  const int ip = kperm(i);
+  di = pair_sum(di);
+  tile_softmax(s, P.c);  // statistics recomputed here: no lse is stored or read
+  u32x4 pds[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = s[kb][r] * inv, p1 = s[kb][r + 1] * inv;
-      const float d0 = p0 * (dp[kb][r] - di), d1 = p1 * (dp[kb][r + 1] - di);
-      const uint32_t pk = pack_bf16(p0, p1), dk2 = pack_bf16(d0, d1);
-      pdsT[kb * 2 + r / 8][(r % 8) / 2] = dk2;
-      // P and dS to LDS as [key][query] for the key-side products
-      const int j0 = kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-      Pm[j0 * C::TS + ip] = uint16_t(pk & 0xffffu);
-      Pm[(j0 + 1) * C::TS + ip] = uint16_t(pk >> 16);
-      dSm[j0 * C::TS + ip] = uint16_t(dk2 & 0xffffu);
-      dSm[(j0 + 1) * C::TS + ip] = uint16_t(dk2 >> 16);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsv[e] = s[kb][q4 * 4 + e] * (dp[kb][q4 * 4 + e] - di);
+      const uint32_t p01 = pack_bf16(s[kb][q4 * 4 + 0], s[kb][q4 * 4 + 1]);
+      const uint32_t p23 = pack_bf16(s[kb][q4 * 4 + 2], s[kb][q4 * 4 + 3]);
+      const uint32_t d01 = pack_bf16(dsv[0], dsv[1]), d23 = pack_bf16(dsv[2], dsv[3]);
+      const int st = kb * 2 + q4 / 2, hw = (q4 % 2) * 2;
+      pds[st][hw] = d01;
+      pds[st][hw + 1] = d23;
+      // P^T and dS^T rows (query i, keys j0..j0+3) for the key-side products
+      const int j0 = kb * 32 + q4 * 8 + g * 4;
+      st8(Pt + Swz<kBS>::chunk(i, j0 >> 3) + (j0 & 7), u32x2{p01, p23});
+      st8(dSt + Swz<kBS>::chunk(i, j0 >> 3) + (j0 & 7), u32x2{d01, d23});
     }
   }
-  __syncthreads();
-  // dQ^T = K^T dS^T (32-column blocks), dq = scale * dQ
   uint16_t* dqrow = P.dq + base + int64_t(i) * rstride;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const u32x4 a = ld16(KT + (nb * 32 + li) * C::TS + step * 16 + g * 8);
-      acc = mfma32(a, pdsT[step], acc);
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 wv;
-      wv[0] = pack_bf16(acc[q4 * 4 + 0] * P.scale, acc[q4 * 4 + 1] * P.scale);
-      wv[1] = pack_bf16(acc[q4 * 4 + 2] * P.scale, acc[q4 * 4 + 3] * P.scale);
-      st8(dqrow + nb * 32 + q4 * 8 + g * 4, wv);
-    }
+    for (int st = 0; st < 4; ++st) acc = mfma32(frag_cols<D>(Kt, st * 16, nb * 32, lane), pds[st], acc);
+    store_block(dqrow, acc, nb * 32, g, P.scale);
   }
+  __syncthreads();
 
-  // ---- phase 2: this wave's 32 keys (lane = key): dV^T = dO^T P, dK^T = Q^T dS
+  // ---- key side (lane = key): dV^T = dO^T P, dK^T = Q^T dS
   const int j = w * 32 + li;
+  u32x4 pb[4], db[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    pb[st] = frag_cols<kBS>(Pt, st * 16, w * 32, lane);
+    db[st] = frag_cols<kBS>(dSt, st * 16, w * 32, lane);
+  }
   uint16_t* dvrow = P.dv + base + int64_t(j) * rstride;
   uint16_t* dkrow = P.dk + base + int64_t(j) * rstride;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     f32x16 av = f32x16{}, ak = f32x16{};
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const u32x4 bp = ld16(Pm + j * C::TS + step * 16 + g * 8);
-      const u32x4 bd = ld16(dSm + j * C::TS + step * 16 + g * 8);
-      av = mfma32(ld16(dOT + (nb * 32 + li) * C::TS + step * 16 + g * 8), bp, av);
-      ak = mfma32(ld16(QT + (nb * 32 + li) * C::TS + step * 16 + g * 8), bd, ak);
+    for (int st = 0; st < 4; ++st) {
+      av = mfma32(frag_cols<D>(dOt, st * 16, nb * 32, lane), pb[st], av);
+      ak = mfma32(frag_cols<D>(Qt, st * 16, nb * 32, lane), db[st], ak);
     }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 a, bb;
-      a[0] = pack_bf16(av[q4 * 4 + 0], av[q4 * 4 + 1]);
-      a[1] = pack_bf16(av[q4 * 4 + 2], av[q4 * 4 + 3]);
-      bb[0] = pack_bf16(ak[q4 * 4 + 0] * P.scale, ak[q4 * 4 + 1] * P.scale);
-      bb[1] = pack_bf16(ak[q4 * 4 + 2] * P.scale, ak[q4 * 4 + 3] * P.scale);
-      st8(dvrow + nb * 32 + q4 * 8 + g * 4, a);
-      st8(dkrow + nb * 32 + q4 * 8 + g * 4, bb);
-    }
+    store_block(dvrow, av, nb * 32, g, 1.f);
+    store_block(dkrow, ak, nb * 32, g, P.scale);
   }
 }
 
@@ -269,7 +235,7 @@ jfa_status launch_fwd_t(const jfa::FwdLaunch& a) {
   P.scale = a.scale;
   const int64_t units = (a.total_kv / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
-  hipLaunchKernelGGL(block_fwd_kernel<D>, dim3(unsigned(units)), dim3(128), 0,
+  hipLaunchKernelGGL(block_fwd_kernel<D>, dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0,
                      static_cast<hipStream_t>(a.stream), P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block fwd launch: ") + hipGetErrorString(e));
@@ -292,7 +258,7 @@ jfa_status launch_bwd_t(const jfa::BwdLaunch& a) {
   P.scale = a.scale;
   const int64_t units = (a.total_kv / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
-  hipLaunchKernelGGL(block_bwd_kernel<D>, dim3(unsigned(units)), dim3(128), 0,
+  hipLaunchKernelGGL(block_bwd_kernel<D>, dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0,
                      static_cast<hipStream_t>(a.stream), P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block bwd launch: ") + hipGetErrorString(e));
