@@ -106,6 +106,35 @@ def cpu_baseline(case, variants, budget_s=15.0):
                       f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "variable_length_flash_jaggedfa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, variant):
+    """HBM bytes per launch of `kernel` on `variant`, from the scaled FETCH_SIZE +
+    WRITE_SIZE counters recorded in profiles/hbm_traffic.txt, or None when no
+    record exists or the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = kernel_source_digest()
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        # record: traffic <kernel-name-without-spaces> <variant> <bytes> <source-digest>
+        if len(f) == 5 and f[0] == "traffic" and f[1] == kernel.replace(" ", "") \
+                and f[2] == variant:
+            return int(f[3]) if f[4] == digest else None
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,13 +145,18 @@ def main():
                              "block64_d128", "imbalance"])
     ap.add_argument("--order", default="zigzag", choices=["zigzag", "inorder", "xcd"])
     ap.add_argument("--compare-orders", action="store_true",
-                    help="also time the forward with in-order dispatch, interleaved")
+                    help="also time forward + backward under all three dealing orders, interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--digest", action="store_true",
+                    help="print the kernel-source digest that traffic records are keyed by")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one elementwise copy of this many MiB first (reads N, writes N): "
                          "the reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.digest:
+        print(kernel_source_digest())
+        return
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -150,8 +184,9 @@ def main():
     k = J.to_torch_bf16(case.k).to(dev)
     v = J.to_torch_bf16(case.v).to(dev)
     do = J.to_torch_bf16(case.do).to(dev)
-    order = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
-             "xcd": jfa.ORDER_XCD_ZIGZAG}[args.order]
+    ORDERS = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
+              "xcd": jfa.ORDER_XCD_ZIGZAG}
+    order = ORDERS[args.order]
 
     runs = []
     sched_ms = 0.0
@@ -164,27 +199,39 @@ def main():
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
         npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block64" else 0)
+        nhd = float(npairs) * w.num_heads * w.head_dim
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
-                         fwd_flops=4.0 * npairs * w.num_heads * w.head_dim,
-                         bwd_flops=10.0 * npairs * w.num_heads * w.head_dim,
-                         fwd_ms=[], bwd_ms=[]))
+                         block=w.kind == "block64", fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
+                         dq_flops=6.0 * nhd, dkdv_flops=8.0 * nhd,
+                         fwd_ms=[], bwd_ms=[], dq_ms=[], dkdv_ms=[]))
     alt = None
     if args.compare_orders:
-        other = jfa.ORDER_INORDER if order == jfa.ORDER_ZIGZAG else jfa.ORDER_ZIGZAG
-        alt = [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
-                        w.lq, order=other, device=dev) for w in variants]
+        alt = {name: [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
+                               w.lq, order=code, device=dev) for w in variants]
+               for name, code in ORDERS.items()}
     torch.cuda.synchronize()
 
     def step(record):
+        # every launch is bracketed by events on the stream the library launches on
+        # (torch's current stream); the backward runs as its two passes so that each
+        # kernel's duration is seen on its own
         for r in runs:
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
             r["plan"].forward(q, k, v, out=r["out"], lse=r["lse"])
-            e1.record()
-            r["plan"].backward(q, k, v, r["out"], do, r["lse"], dq=r["dq"], dk=r["dk"], dv=r["dv"])
-            e2.record()
+            ev[1].record()
+            bargs = (q, k, v, r["out"], do, r["lse"])
+            bkw = dict(dq=r["dq"], dk=r["dk"], dv=r["dv"])
+            if r["block"]:
+                r["plan"].backward(*bargs, **bkw)
+                ev[2].record()
+            else:
+                r["plan"].backward(*bargs, **bkw, passes=jfa.PASS_DQ)
+                ev[2].record()
+                r["plan"].backward(*bargs, **bkw, passes=jfa.PASS_DKDV)
+            ev[3].record()
             if record:
-                r["_ev"] = (e0, e1, e2)
+                r["_ev"] = ev
         return runs
 
     for _ in range(args.warmup):
@@ -195,9 +242,12 @@ def main():
         step(True)
         torch.cuda.synchronize()
         for r in runs:
-            e0, e1, e2 = r["_ev"]
+            e0, e1, e2, e3 = r["_ev"]
             r["fwd_ms"].append(e0.elapsed_time(e1))
-            r["bwd_ms"].append(e1.elapsed_time(e2))
+            r["bwd_ms"].append(e1.elapsed_time(e3))
+            if not r["block"]:
+                r["dq_ms"].append(e1.elapsed_time(e2))
+                r["dkdv_ms"].append(e2.elapsed_time(e3))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # whole-job throughput over the timed region (includes per-step sync)
@@ -206,24 +256,36 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # dominant pass: the one with the largest mean duration
+    # dominant kernel: the launch with the largest mean duration. Algorithmic work
+    # per launch: fwd 4*N*H*D (Q K^T, P V); dQ pass 6*N*H*D (S, dP, dQ); dK/dV pass
+    # 8*N*H*D (S, dP, dV, dK); the fused 64-token block kernels are HBM-bound and
+    # are credited with the bytes of the bf16 tensors they must move.
+    T = int(case.offsets[-1])
     cands = []
     for r in runs:
-        tag = r["w"].name + ("_causal" if r["w"].causal else "")
-        cands.append((np.mean(r["fwd_ms"]), "fwd", tag, r["fwd_flops"]))
-        cands.append((np.mean(r["bwd_ms"]), "bwd", tag, r["bwd_flops"]))
-    dur, which, tag, fl = max(cands)
-    achieved = fl / (dur * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": f"{which} pass ({tag})", "avg_ms": round(dur, 4)}
-    if w0.kind == "block64":
-        # memory-bound: algorithmic bytes of the pass (4 or 8 bf16 tensors of T*H*D)
-        T = int(case.offsets[-1])
-        nbytes = (4 if which == "fwd" else 8) * T * w0.num_heads * w0.head_dim * 2
-        gbs = nbytes / (dur * 1e-3) / 1e9
-        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        w = r["w"]
+        tag = w.name + ("_causal" if w.causal else "")
+        if r["block"]:
+            tb = T * w.num_heads * w.head_dim * 2
+            cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
+            cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
+        else:
+            bc = "_bcast" if w.kind == "broadcast" else ""
+            cands.append((np.mean(r["fwd_ms"]), "fwd_kernel", tag, "mfma", r["fwd_flops"]))
+            cands.append((np.mean(r["dq_ms"]), f"dq{bc}_kernel" + (" + dq_reduce_kernel" if bc else ""),
+                          tag, "mfma", r["dq_flops"]))
+            cands.append((np.mean(r["dkdv_ms"]), "dkdv_kernel", tag, "mfma", r["dkdv_flops"]))
+    dur, kname, tag, bound, work = max(cands, key=lambda c: c[0])
+    if bound == "mfma":
+        achieved = work / (dur * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = work / (dur * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": measured_traffic(kname, tag), "kernel": kname, "variant": tag,
+                     "avg_ms": round(float(dur), 4), "work_per_launch": work})
 
     per_variant = {}
     for r in runs:
@@ -233,28 +295,51 @@ def main():
                             "fwd_tflops": round(r["fwd_flops"] / fm / 1e9, 1),
                             "bwd_tflops": round(r["bwd_flops"] / bm / 1e9, 1),
                             "fwd_bwd_tflops": round((r["fwd_flops"] + r["bwd_flops"]) / (fm + bm) / 1e9, 1)}
+        if not r["block"]:
+            per_variant[tag]["dq_ms"] = round(float(np.median(r["dq_ms"])), 4)
+            per_variant[tag]["dkdv_ms"] = round(float(np.median(r["dkdv_ms"])), 4)
 
     compare = None
     if alt is not None:
-        # interleave: main order then other order, forward only, per variant
-        tm, to = [], []
-        for _ in range(max(10, args.steps)):
-            for r, ap_ in zip(runs, alt):
-                for plan, sink in ((r["plan"], tm), (ap_, to)):
-                    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a_.record()
+        # the three dealing orders on the same batch, interleaved round by round so
+        # that clock and thermal drift hit them alike; forward and backward of every
+        # variant per round; medians over rounds
+        samples = {name: {"fwd": [], "bwd": [], "total": []} for name in alt}
+        for _ in range(max(5, args.steps)):
+            for name, plans in alt.items():
+                tf = tb = 0.0
+                for r, plan in zip(runs, plans):
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    ev[0].record()
                     plan.forward(q, k, v, out=r["out"], lse=r["lse"])
-                    b_.record()
+                    ev[1].record()
+                    plan.backward(q, k, v, r["out"], do, r["lse"], dq=r["dq"], dk=r["dk"], dv=r["dv"])
+                    ev[2].record()
                     torch.cuda.synchronize()
-                    sink.append(a_.elapsed_time(b_))
-        compare = {"fwd_ms_" + args.order: [round(float(np.percentile(tm, p)), 4) for p in (25, 50, 75)],
-                   "fwd_ms_other": [round(float(np.percentile(to, p)), 4) for p in (25, 50, 75)]}
+                    tf += ev[0].elapsed_time(ev[1])
+                    tb += ev[1].elapsed_time(ev[2])
+                samples[name]["fwd"].append(tf)
+                samples[name]["bwd"].append(tb)
+                samples[name]["total"].append(tf + tb)
+        compare = {name: {k_: round(float(np.median(v_)), 4) for k_, v_ in d.items()}
+                   for name, d in samples.items()}
+        for name, plans in alt.items():
+            # predicted balance: busiest slot's KV work over the mean, per schedule kind
+            for kind, tag in ((jfa.KIND_FWD, "fwd"), (jfa.KIND_BWD, "bwd")):
+                sc = plans[0].sched.get(kind)
+                if sc is None or len(sc.tiles) == 0:
+                    continue
+                w_ = np.concatenate([[0], np.cumsum(sc.tiles[:, 3].astype(np.int64))])
+                loads = w_[sc.slot_ptr[1:]] - w_[sc.slot_ptr[:-1]]
+                compare[name][f"{tag}_max_over_mean_load"] = round(float(loads.max() / loads.mean()), 4)
+        base = compare["inorder"]["total"]
+        for name in compare:
+            compare[name]["speedup_vs_inorder"] = round(base / compare[name]["total"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, variants)
 
-    T = int(case.offsets[-1])
     line = {
         "metric": "jagged attn fwd+bwd TFLOP/s (bf16, unpadded FLOPs) and % of MFMA bf16 peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

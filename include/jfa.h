@@ -170,6 +170,26 @@ jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const voi
                    int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* The two passes of the backward, for jfa_bwd_passes. */
+#define JFA_PASS_DQ   1u  /* dQ pass over query tiles; also writes Di into the workspace */
+#define JFA_PASS_DKDV 2u  /* dK/dV pass over key tiles; reads Di from the workspace */
+#define JFA_PASS_ALL  3u
+
+/* jfa_bwd restricted to some of its passes, so that each can be timed or
+ * overlapped on its own. Same arguments as jfa_bwd plus `passes`, a non-zero
+ * mask of JFA_PASS_*. JFA_PASS_DKDV alone is valid only after a JFA_PASS_DQ call
+ * with the same problem, inputs and workspace on the same stream (it reads the Di
+ * that pass left in the workspace); the library cannot check this. BLOCK_DIAG64
+ * runs one fused kernel and accepts JFA_PASS_ALL only (JFA_ERR_INVALID_ARG
+ * otherwise). jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
+jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, const void* v,
+                          const void* out, const void* dout, const float* lse,
+                          const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
+                          const int32_t* q_tiles_dev, int32_t q_num_slots,
+                          const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                          int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, uint32_t passes, void* stream);
+
 /* Static text for a status code. */
 const char* jfa_status_string(jfa_status s);
 

@@ -109,6 +109,14 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
     s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, nul, nul, 0,
                   fake, fake, 4, fake, fake, fake, fake, 1 << 20, None)
     assert s == jfa.ERR_INVALID_ARG
+    # backward passes: an empty or unknown mask, and a single pass of the fused block path
+    for bad in (0, 4, 7):
+        s = L.jfa_bwd_passes(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                             4, fake, fake, 4, fake, fake, fake, fake, 1 << 20, bad, None)
+        assert s == jfa.ERR_INVALID_ARG and b"passes" in L.jfa_last_error()
+    s = L.jfa_bwd_passes(ctypes.byref(pb), fake, fake, fake, fake, fake, nul, fake, nul, nul, 0,
+                         nul, nul, 0, fake, fake, fake, nul, 0, jfa.PASS_DQ, None)
+    assert s == jfa.ERR_INVALID_ARG and b"BLOCK_DIAG64" in L.jfa_last_error()
     # empty problems are no-ops that touch nothing
     p0 = _p(num_seqs=0, total_kv=0, max_len=0)
     assert L.jfa_fwd(ctypes.byref(p0), nul, nul, nul, nul, nul, nul, 0, nul, nul, None) == jfa.OK

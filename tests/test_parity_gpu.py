@@ -162,3 +162,21 @@ def test_block_diag_matches_jagged_path_on_refined_offsets(gpu):
     assert_out(bf16_to_f64(ob), bf16_to_f64(oj), "block vs jagged out")
     for n, a_, b_ in (("dq", dqb, dqj), ("dk", dkb, dkj), ("dv", dvb, dvj)):
         assert_grad(bf16_to_f64(a_), bf16_to_f64(b_), n + " block vs jagged")
+
+
+def test_backward_passes_match_fused_call(gpu):
+    """jfa_bwd_passes(DQ) then (DKDV) gives the bits of one jfa_bwd call."""
+    import torch
+    for w in (J.custom(RAGGED, 2, 128, sigma=0.5, seed=17, causal=True),
+              J.custom([50, 0, 300, 129], 2, 64, sigma=0.5, seed=17, kind="broadcast", lq=130)):
+        log(f"case passes {w.kind} causal={w.causal} D={w.head_dim}")
+        run = GpuRun(J.make_case(w), gpu)
+        run.forward()
+        dq1, dk1, dv1 = (x.clone() for x in run.backward())
+        plan = run.plan
+        q, k, v, out, do, lse = run.q, run.k, run.v, run.out_dev, run.do, run.lse_dev
+        dq2, dk2, dv2 = (torch.full_like(x, float("nan")) for x in (dq1, dk1, dv1))
+        plan.backward(q, k, v, out, do, lse, dq=dq2, dk=dk2, dv=dv2, passes=jfa.PASS_DQ)
+        plan.backward(q, k, v, out, do, lse, dq=dq2, dk=dk2, dv=dv2, passes=jfa.PASS_DKDV)
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)

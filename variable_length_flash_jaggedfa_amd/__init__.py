@@ -25,6 +25,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 CAUSAL, BROADCAST_Q, BLOCK_DIAG64 = 1, 2, 4
 KIND_FWD, KIND_BWD = 0, 1
 ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG = 0, 1, 2
+PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
 
 
 class JfaError(RuntimeError):
@@ -69,6 +70,9 @@ def lib():
         L.jfa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                               vp, vp, ctypes.c_size_t, vp]
         L.jfa_bwd.restype = i32
+        L.jfa_bwd_passes.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp,
+                                     vp, vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp]
+        L.jfa_bwd_passes.restype = i32
         L.jfa_status_string.argtypes = [i32]
         L.jfa_status_string.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
@@ -152,6 +156,18 @@ def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tile
                          ws_bytes, _stream(stream)))
 
 
+def bwd_passes(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+               q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv, workspace,
+               passes, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().jfa_bwd_passes(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(dout), _ptr(lse), _ptr(offsets_dev), _ptr(q_slot_ptr_dev),
+                                _ptr(q_tiles_dev), int(q_num_slots), _ptr(kv_slot_ptr_dev),
+                                _ptr(kv_tiles_dev), int(kv_num_slots), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(workspace), ws_bytes, int(passes),
+                                _stream(stream)))
+
+
 @dataclass
 class Schedule:
     slot_ptr: np.ndarray
@@ -224,15 +240,22 @@ class Plan:
             None if self.block else lse, stream)
         return out, (None if self.block else lse)
 
-    def backward(self, q, k, v, out, dout, lse=None, dq=None, dk=None, dv=None, stream=None):
+    def backward(self, q, k, v, out, dout, lse=None, dq=None, dk=None, dv=None, stream=None,
+                 passes=PASS_ALL):
+        """dQ, dK, dV. `passes` selects the backward passes (PASS_DQ must run before
+        PASS_DKDV on the same inputs: the second reads Di from the plan's workspace)."""
         import torch
         dq = dq if dq is not None else torch.empty_like(q)
         dk = dk if dk is not None else torch.empty_like(k)
         dv = dv if dv is not None else torch.empty_like(v)
         sq, skv = self.sched.get(KIND_FWD), self.sched.get(KIND_BWD)
-        bwd(self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
-            sq.slot_ptr_dev if sq else None, sq.tiles_dev if sq else None,
-            sq.num_slots if sq else 0, skv.slot_ptr_dev if skv else None,
-            skv.tiles_dev if skv else None, skv.num_slots if skv else 0,
-            dq, dk, dv, self.workspace, stream)
+        args = (self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
+                sq.slot_ptr_dev if sq else None, sq.tiles_dev if sq else None,
+                sq.num_slots if sq else 0, skv.slot_ptr_dev if skv else None,
+                skv.tiles_dev if skv else None, skv.num_slots if skv else 0,
+                dq, dk, dv, self.workspace)
+        if passes == PASS_ALL:
+            bwd(*args, stream)
+        else:
+            bwd_passes(*args, passes, stream)
         return dq, dk, dv

@@ -90,15 +90,20 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   return launch_fwd(a);
 }
 
-extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
-                              const void* out, const void* dout, const float* lse,
-                              const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
-                              const int32_t* q_tiles_dev, int32_t q_num_slots,
-                              const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
-                              int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k,
+                                     const void* v, const void* out, const void* dout,
+                                     const float* lse, const int32_t* offsets_dev,
+                                     const int32_t* q_slot_ptr_dev, const int32_t* q_tiles_dev,
+                                     int32_t q_num_slots, const int32_t* kv_slot_ptr_dev,
+                                     const int32_t* kv_tiles_dev, int32_t kv_num_slots, void* dq,
+                                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     uint32_t passes, void* stream) {
   set_error("");
   if (jfa_status s = check_problem(p)) return s;
+  if (passes == 0 || (passes & ~JFA_PASS_ALL))
+    return fail(JFA_ERR_INVALID_ARG, "passes must be a non-zero mask of JFA_PASS_DQ | JFA_PASS_DKDV");
+  if ((p->flags & JFA_BLOCK_DIAG64) && passes != JFA_PASS_ALL)
+    return fail(JFA_ERR_INVALID_ARG, "BLOCK_DIAG64 runs one fused backward kernel: passes must be JFA_PASS_ALL");
   const bool blk = p->flags & JFA_BLOCK_DIAG64;
   const bool bq = p->flags & JFA_BROADCAST_Q;
   if (p->num_seqs == 0) return JFA_OK;
@@ -121,7 +126,8 @@ extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k
   a.kv_slot_ptr = kv_slot_ptr_dev; a.kv_tiles = kv_tiles_dev; a.kv_num_slots = kv_num_slots;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
-  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.stream = stream;
+  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.passes = passes;
+  a.stream = stream;
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is read)");
     if (p->total_kv == 0) return JFA_OK;
@@ -151,4 +157,16 @@ extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k
   a.groups = bcast_groups(p->num_seqs);
   a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p)) : nullptr;
   return launch_bwd(a);
+}
+
+extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse,
+                              const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
+                              const int32_t* q_tiles_dev, int32_t q_num_slots,
+                              const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                              int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return jfa_bwd_passes(p, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+                        q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv,
+                        workspace, workspace_bytes, JFA_PASS_ALL, stream);
 }

@@ -78,32 +78,27 @@ __device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
     dp[kb] = f32x16{};
   }
   // S^T = K Q^T and dP^T = V dO^T; row fragments one k-step ahead
-  u32x4 ka[KB], va[KB], kn[KB], vn[KB];
+  u32x4 kfr[2][KB], vfr[2][KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    ka[kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
-    va[kb] = frag_rows<D>(vs, kb * 32, 0, li, g);
+    kfr[0][kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
+    vfr[0][kb] = frag_rows<D>(vs, kb * 32, 0, li, g);
   }
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
     if (d + 1 < C::DS) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        kn[kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
-        vn[kb] = frag_rows<D>(vs, kb * 32, d + 1, li, g);
+        kfr[(d + 1) & 1][kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
+        vfr[(d + 1) & 1][kb] = frag_rows<D>(vs, kb * 32, d + 1, li, g);
       }
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = mfma32(ka[kb], qf[d], s[kb]);
-      dp[kb] = mfma32(va[kb], dof[d], dp[kb]);
+      s[kb] = mfma32(kfr[d & 1][kb], qf[d], s[kb]);
+      dp[kb] = mfma32(vfr[d & 1][kb], dof[d], dp[kb]);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      ka[kb] = kn[kb];
-      va[kb] = vn[kb];
-    }
   }
   // P = 2^(S c - lse2), dS = P (dP - Di), packed with keys along the registers
   u32x4 pds[2 * KB];
@@ -123,14 +118,14 @@ __device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
   }
   // dQ^T += K^T dS^T; column fragments of K one step ahead
   constexpr int NX = 2 * KB * C::NB;
-  u32x4 fa = frag_cols<D>(ks, 0, 0, lane), fn;
+  u32x4 fr[2];
+  fr[0] = frag_cols<D>(ks, 0, 0, lane);
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const int st = x / C::NB, nb = x % C::NB;
-    if (x + 1 < NX) fn = frag_cols<D>(ks, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
-    acc[nb] = mfma32(fa, pds[st], acc[nb]);
+    if (x + 1 < NX) fr[(x + 1) & 1] = frag_cols<D>(ks, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+    acc[nb] = mfma32(fr[x & 1], pds[st], acc[nb]);
     __builtin_amdgcn_sched_barrier(0);
-    fa = fn;
   }
 }
 
@@ -341,32 +336,27 @@ __device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos,
     dp[ib] = f32x16{};
   }
   // S = Q K^T and dP = dO V^T (lane = key); row fragments one k-step ahead
-  u32x4 qa[IB], da[IB], qn[IB], dn[IB];
+  u32x4 qfr[2][IB], dfr[2][IB];
 #pragma unroll
   for (int ib = 0; ib < IB; ++ib) {
-    qa[ib] = frag_rows<D>(qs, ib * 32, 0, li, g);
-    da[ib] = frag_rows<D>(dos, ib * 32, 0, li, g);
+    qfr[0][ib] = frag_rows<D>(qs, ib * 32, 0, li, g);
+    dfr[0][ib] = frag_rows<D>(dos, ib * 32, 0, li, g);
   }
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
     if (d + 1 < C::DS) {
 #pragma unroll
       for (int ib = 0; ib < IB; ++ib) {
-        qn[ib] = frag_rows<D>(qs, ib * 32, d + 1, li, g);
-        dn[ib] = frag_rows<D>(dos, ib * 32, d + 1, li, g);
+        qfr[(d + 1) & 1][ib] = frag_rows<D>(qs, ib * 32, d + 1, li, g);
+        dfr[(d + 1) & 1][ib] = frag_rows<D>(dos, ib * 32, d + 1, li, g);
       }
     }
 #pragma unroll
     for (int ib = 0; ib < IB; ++ib) {
-      s[ib] = mfma32(qa[ib], kf[d], s[ib]);
-      dp[ib] = mfma32(da[ib], vf[d], dp[ib]);
+      s[ib] = mfma32(qfr[d & 1][ib], kf[d], s[ib]);
+      dp[ib] = mfma32(dfr[d & 1][ib], vf[d], dp[ib]);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-      qa[ib] = qn[ib];
-      da[ib] = dn[ib];
-    }
   }
   // P and dS with query rows along the registers
   u32x4 pp[2 * IB], pd[2 * IB];
@@ -395,19 +385,19 @@ __device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos,
   }
   // dV^T += dO^T P, dK^T += Q^T dS; column fragments one step ahead
   constexpr int NX = 2 * IB * C::NB;
-  u32x4 fa = frag_cols<D>(dos, 0, 0, lane), fb = frag_cols<D>(qs, 0, 0, lane), fan, fbn;
+  u32x4 fa[2], fb[2];
+  fa[0] = frag_cols<D>(dos, 0, 0, lane);
+  fb[0] = frag_cols<D>(qs, 0, 0, lane);
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const int st = x / C::NB, nb = x % C::NB;
     if (x + 1 < NX) {
-      fan = frag_cols<D>(dos, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
-      fbn = frag_cols<D>(qs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+      fa[(x + 1) & 1] = frag_cols<D>(dos, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+      fb[(x + 1) & 1] = frag_cols<D>(qs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
     }
-    dv[nb] = mfma32(fa, pp[st], dv[nb]);
-    dk[nb] = mfma32(fb, pd[st], dk[nb]);
+    dv[nb] = mfma32(fa[x & 1], pp[st], dv[nb]);
+    dk[nb] = mfma32(fb[x & 1], pd[st], dk[nb]);
     __builtin_amdgcn_sched_barrier(0);
-    fa = fan;
-    fb = fbn;
   }
 }
 
@@ -536,7 +526,9 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   dp.groups = a.groups;
   dp.c = c;
   dp.scale = a.scale;
-  if (BCAST) {
+  const bool run_dq = a.passes & JFA_PASS_DQ, run_kv = a.passes & JFA_PASS_DKDV;
+  if (!run_dq) {
+  } else if (BCAST) {
     const int n_qt = (a.lq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
     hipLaunchKernelGGL(dq_bcast_kernel<D>, dim3(n_qt * a.num_heads * a.groups), dim3(DqCfg<D>::NT),
                        0, st, dp);
@@ -546,7 +538,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   } else if (a.total_kv > 0) {
     hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st, dp);
   }
-  if (a.total_kv > 0) {
+  if (run_kv && a.total_kv > 0) {
     KvParams kp{};
     kp.q = dp.q;
     kp.k = dp.k;

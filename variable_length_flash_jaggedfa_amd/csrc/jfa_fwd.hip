@@ -68,22 +68,20 @@ __device__ __forceinline__ void fwd_step(const uint16_t* ks, const uint16_t* vs,
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16{};
   // S^T: K fragments are read one k-step ahead of the MFMAs that use them
-  u32x4 ka[KB], kn[KB];
+  u32x4 kf[2][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) ka[kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
+  for (int kb = 0; kb < KB; ++kb) kf[0][kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
     if (d + 1 < C::DS) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kn[kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
+      for (int kb = 0; kb < KB; ++kb) kf[(d + 1) & 1][kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(ka[kb], qf[qb][d], s[qb][kb]);
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(kf[d & 1][kb], qf[qb][d], s[qb][kb]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) ka[kb] = kn[kb];
   }
   // masks, step max, reference-max update
   float mx[QB];
@@ -107,6 +105,7 @@ __device__ __forceinline__ void fwd_step(const uint16_t* ks, const uint16_t* vs,
     move = move || (mx[qb] > m[qb] + kRescaleSlack);
   }
   if (__builtin_amdgcn_ballot_w64(move)) {
+    asm volatile("" ::: "memory");  // keep this rare path a branch, not a select
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float m_new = fmaxf(m[qb], mx[qb]);
@@ -136,15 +135,15 @@ __device__ __forceinline__ void fwd_step(const uint16_t* ks, const uint16_t* vs,
   }
   // O^T += V^T P^T: V^T fragments one (step, block) ahead of their MFMAs
   constexpr int NX = 2 * KB * C::NB;
-  u32x4 va = frag_cols<D>(vs, 0, 0, lane), vn;
+  u32x4 vf[2];
+  vf[0] = frag_cols<D>(vs, 0, 0, lane);
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const int st = x / C::NB, nb = x % C::NB;
-    if (x + 1 < NX) vn = frag_cols<D>(vs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+    if (x + 1 < NX) vf[(x + 1) & 1] = frag_cols<D>(vs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) o[qb][nb] = mfma32(va, pf[qb][st], o[qb][nb]);
+    for (int qb = 0; qb < QB; ++qb) o[qb][nb] = mfma32(vf[x & 1], pf[qb][st], o[qb][nb]);
     __builtin_amdgcn_sched_barrier(0);
-    va = vn;
   }
 }
 

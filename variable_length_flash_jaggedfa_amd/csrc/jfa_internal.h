@@ -51,6 +51,7 @@ struct BwdLaunch {
   int64_t total_kv;
   float scale;
   uint32_t flags;
+  uint32_t passes;  // JFA_PASS_* mask
   void* stream;
 };
 

@@ -2,10 +2,8 @@
 // direct global->LDS loads, and the two ways an MFMA fragment is read back.
 //
 // A tile holds ROWS x D bf16 values row-major with no padding. Each row is D/8
-// chunks of 16 bytes; chunk c of row r is stored at position c ^ f(r). f is
-// chosen so that (a) 16 consecutive rows reading the same chunk, and (b) 4
-// consecutive rows reading two neighbouring chunks, all land in distinct 16-byte
-// bank groups.
+// chunks of 16 bytes; chunk c of row r is stored at position c ^ f(r), with f
+// chosen so that both fragment reads below are free of bank conflicts.
 //
 // Fragment reads (lane = 32*g + li, see jfa_device.h):
 //   frag_rows: 8 consecutive columns (chunk 2*kc+g) of row r0+li -- an A or B
@@ -29,10 +27,12 @@ typedef __attribute__((address_space(3))) f16x4_t lds_f16x4_t;
 template <int D>
 struct Swz {
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  __device__ static __forceinline__ int f(int r) {
-    const int m = CPR == 16 ? r : (r >> 1);
-    return (2 * m + m / (CPR / 2)) & (CPR - 1);
-  }
+  // LDS has 32 four-byte banks (128 bytes). A 16-byte read is served 8 lanes at
+  // a time, so 8 consecutive rows reading one chunk need 8 distinct 16-byte
+  // slots mod 128 B: f(r) & 7 takes 8 values over any aligned 8 rows. A transpose
+  // read is served 16 lanes (4 rows x 32 bytes) at a time, so 4 aligned rows need
+  // distinct 32-byte slot pairs: f(r) & 6 takes 4 values over any aligned 4 rows.
+  __device__ static __forceinline__ int f(int r) { return ((2 * r) & 6) | ((r >> 2) & 1); }
   // element offset of logical chunk c of row r
   __device__ static __forceinline__ int chunk(int r, int c) { return r * D + ((c ^ f(r)) << 3); }
 };
