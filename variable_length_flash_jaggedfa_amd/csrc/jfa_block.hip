@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::TILE];  // K, V
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   uint16_t* Pt = dOt + C::TILE;
   uint16_t* dSt = Pt + kBS * kBS;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;

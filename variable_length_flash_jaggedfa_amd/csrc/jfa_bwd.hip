@@ -192,7 +192,7 @@ dq_kernel(DqParams P) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
@@ -241,7 +241,7 @@ dq_bcast_kernel(DqParams P) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
   const int n_qt = ceil_div(P.lq, C::BM);
   const int t = blockIdx.x % n_qt, h = (blockIdx.x / n_qt) % P.H, grp = blockIdx.x / (n_qt * P.H);
   const int b0 = int(int64_t(grp) * P.num_seqs / P.groups);
@@ -408,7 +408,7 @@ dkdv_kernel(KvParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // lse, Di per stage
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
@@ -453,8 +453,7 @@ dkdv_kernel(KvParams P) {
                                  rowbytes, w, lane);
       if (w < 2 && lane < C::BM) {
         const float* src = (w == 0 ? P.lse : P.di) + voff + q_first;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vec_rsrc(src, left), (lds_void_t*)vecs[buf][w], 4,
-                                                 lane * 4, 0, 0, 0);
+        vec64_load(vecs[buf][w], vec_rsrc(src, left), lane);
       }
     };
 #pragma unroll

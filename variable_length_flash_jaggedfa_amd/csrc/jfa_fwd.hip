@@ -26,14 +26,14 @@ namespace {
 template <int D>
 struct FwdCfg {
   static constexpr int BM = jfa::kFwdBM;  // 128 query rows per tile
-  static constexpr int QB = 1;            // 32-row blocks per wave
   static constexpr int BN = D == 128 ? 32 : 64;  // keys per step
   static constexpr int KB = BN / 32;      // 32-key blocks per step
-  static constexpr int NW = BM / (32 * QB);  // waves
+  static constexpr int NW = BM / 32;      // waves, 32 query rows each
   static constexpr int NT = 64 * NW;
-  static constexpr int NS = 3;            // LDS ring stages (prefetch distance 2)
+  static constexpr int NS = 4;            // LDS ring stages
   static constexpr int DS = D / 16;       // MFMA k-steps over the head dim
   static constexpr int NB = D / 32;       // 32-column blocks of the head dim
+  static constexpr int NX = 2 * KB * NB;  // P V products per step
   static constexpr int TILE = BN * D;     // elements of one K or V tile
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;  // load instructions per wave per stage
@@ -52,99 +52,152 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-// One step of BN keys for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void fwd_step(const uint16_t* ks, const uint16_t* vs,
-                                         const u32x4 (&qf)[FwdCfg<D>::QB][FwdCfg<D>::DS],
-                                         f32x16 (&o)[FwdCfg<D>::QB][FwdCfg<D>::NB],
-                                         float (&m)[FwdCfg<D>::QB], float (&l)[FwdCfg<D>::QB],
-                                         float c, int lane, int key0, int n_keys, int qpos0) {
+// Scores of one step whose keys fall past the sequence end or, with CAUSAL,
+// after the lane's query position are set to -inf.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[FwdCfg<D>::KB], int g, int key0, int n_keys,
+                                            int qpos) {
+#pragma unroll
+  for (int kb = 0; kb < FwdCfg<D>::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+      const bool dead = key >= n_keys || (CAUSAL && key > qpos);
+      s[kb][r] = dead ? -INFINITY : s[kb][r];
+    }
+}
+
+// Row max of one step's scores (raw, before scaling), per lane pair.
+template <int D>
+__device__ __forceinline__ float row_max(const f32x16 (&s)[FwdCfg<D>::KB]) {
+  float x = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < FwdCfg<D>::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
+  return x;
+}
+
+// S^T = K Q^T for one step with no other work to overlap (the first step).
+template <int D>
+__device__ __forceinline__ void scores(const uint16_t* ks, const u32x4 (&qf)[FwdCfg<D>::DS],
+                                       f32x16 (&s)[FwdCfg<D>::KB], int li, int g) {
   using C = FwdCfg<D>;
-  constexpr int KB = C::KB, QB = C::QB;
-  const int g = lane >> 5, li = lane & 31;
-  f32x16 s[QB][KB];
+  u32x4 kf[C::KB][C::DS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16{};
-  // S^T: K fragments are read one k-step ahead of the MFMAs that use them
-  u32x4 kf[2][KB];
+    for (int d = 0; d < C::DS; ++d) kf[kb][d] = frag_rows<D>(ks, kb * 32, d, li, g);
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) kf[0][kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
+  for (int kb = 0; kb < C::KB; ++kb) {
+    s[kb] = f32x16{};
 #pragma unroll
-  for (int d = 0; d < C::DS; ++d) {
-    if (d + 1 < C::DS) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[(d + 1) & 1][kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(kf[d & 1][kb], qf[qb][d], s[qb][kb]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int d = 0; d < C::DS; ++d) s[kb] = mfma32(kf[kb][d], qf[d], s[kb]);
   }
-  // masks, step max, reference-max update
-  float mx[QB];
-  bool move = false;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float x = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MASK) {
-          const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          const bool dead = key >= n_keys || (CAUSAL && key > qpos0 + qb * 32);
-          s[qb][kb][r] = dead ? -INFINITY : s[qb][kb][r];
-        }
-        x = fmaxf(x, s[qb][kb][r]);
-      }
-    }
-    mx[qb] = pair_max(x) * c;
-    move = move || (mx[qb] > m[qb] + kRescaleSlack);
-  }
-  if (__builtin_amdgcn_ballot_w64(move)) {
+}
+
+// Move the reference max of each row if the new step's max exceeds it by more
+// than the slack, rescaling l and O by the correction factor 2^(m_old - m_new).
+template <int D>
+__device__ __forceinline__ void update_max(float mx, float& m, float& l,
+                                           f32x16 (&o)[FwdCfg<D>::NB]) {
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
     asm volatile("" ::: "memory");  // keep this rare path a branch, not a select
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m - m_new);
+    m = m_new;
+    l *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_new = fmaxf(m[qb], mx[qb]);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m[qb] - m_new);
-      m[qb] = m_new;
-      l[qb] *= alpha;
+    for (int nb = 0; nb < FwdCfg<D>::NB; ++nb) o[nb] *= alpha;
+  }
+}
+
+// One pipelined step for one wave. On entry `sc` holds this step's scores and m
+// its (already moved) reference max. The step
+//   A: reads this step's V^T fragments and the next step's K fragments from LDS,
+//      then issues the next step's S^T = K Q^T MFMAs interleaved with the exp2
+//      and bf16 packing of this step's probabilities;
+//   B: issues O^T += V^T P^T interleaved with the masking and row max of the
+//      next step's scores.
+// Returns the next step's scaled row max (or -inf when there is no next step).
+template <int D, bool NEXT, bool MASK_NEXT, bool CAUSAL>
+__device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks_next,
+                                          const u32x4 (&qf)[FwdCfg<D>::DS],
+                                          const f32x16 (&sc)[FwdCfg<D>::KB],
+                                          f32x16 (&sn)[FwdCfg<D>::KB], f32x16 (&o)[FwdCfg<D>::NB],
+                                          float m, float& l, float c, int lane, int key_next,
+                                          int n_keys, int qpos) {
+  using C = FwdCfg<D>;
+  const int g = lane >> 5, li = lane & 31;
+  // --- A
+  u32x4 kf[C::KB][C::DS];
+  if (NEXT) {
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[qb][nb] *= alpha;
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int d = 0; d < C::DS; ++d) kf[kb][d] = frag_rows<D>(ks_next, kb * 32, d, li, g);
+  }
+  const float m_use = m == -INFINITY ? 0.f : m;
+  u32x4 pf[2 * C::KB];
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(sc[kb][r], c, -m_use));
+      const float p1 = exp2_fast(__builtin_fmaf(sc[kb][r + 1], c, -m_use));
+      rs += p0 + p1;
+      pf[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0, p1);
     }
   }
-  u32x4 pf[QB][2 * KB];
+  l += rs;
+  if (NEXT) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float m_use = m[qb] == -INFINITY ? 0.f : m[qb];
-    float rs = 0.f;
+    for (int kb = 0; kb < C::KB; ++kb) {
+      sn[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(__builtin_fmaf(s[qb][kb][r], c, -m_use));
-        const float p1 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 1], c, -m_use));
-        rs += p0 + p1;
-        pf[qb][kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0, p1);
-      }
+      for (int d = 0; d < C::DS; ++d) sn[kb] = mfma32(kf[kb][d], qf[d], sn[kb]);
     }
-    l[qb] += rs;
   }
-  // O^T += V^T P^T: V^T fragments one (step, block) ahead of their MFMAs
-  constexpr int NX = 2 * KB * C::NB;
-  u32x4 vf[2];
-  vf[0] = frag_cols<D>(vs, 0, 0, lane);
+  // V^T fragments: the first two are read at the end of A, the rest in B, each
+  // two MFMAs ahead of its use
+  u32x4 vf[C::NX];
 #pragma unroll
-  for (int x = 0; x < NX; ++x) {
-    const int st = x / C::NB, nb = x % C::NB;
-    if (x + 1 < NX) vf[(x + 1) & 1] = frag_cols<D>(vs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+  for (int x = 0; x < 2; ++x)
+    vf[x] = frag_cols<D>(vs, (x / C::NB) * 16, (x % C::NB) * 32, lane);
+  if (NEXT) {
+    // each MFMA with a share of the VALU work and the K read two MFMAs ahead,
+    // then the V reads
+    constexpr int NK = C::KB * C::DS;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) o[qb][nb] = mfma32(vf[x & 1], pf[qb][st], o[qb][nb]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6 * C::KB, 0);
+      if (i + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // --- B
+#pragma unroll
+  for (int x = 2; x < C::NX; ++x)
+    vf[x] = frag_cols<D>(vs, (x / C::NB) * 16, (x % C::NB) * 32, lane);
+#pragma unroll
+  for (int x = 0; x < C::NX; ++x) o[x % C::NB] = mfma32(vf[x], pf[x / C::NB], o[x % C::NB]);
+  float mx = -INFINITY;
+  if (NEXT) {
+    if (MASK_NEXT) mask_scores<D, CAUSAL>(sn, g, key_next, n_keys, qpos);
+    mx = row_max<D>(sn);
+  }
+#pragma unroll
+  for (int i = 0; i < C::NX; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (NEXT) __builtin_amdgcn_sched_group_barrier(0x002, MASK_NEXT ? 6 * C::KB : 2 * C::KB, 0);
+    if (i + 2 < C::NX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return NEXT ? pair_max(mx) * c : -INFINITY;
 }
 
 template <int N>
@@ -153,13 +206,13 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ void __launch_bounds__(FwdCfg<D>::NT)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::QB == 1 ? 2 : 1)))
+__global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
   using C = FwdCfg<D>;
+  static_assert(C::NS == 4, "the waits below assume a four-stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;  // elements between consecutive tokens
@@ -174,88 +227,103 @@ fwd_kernel(FwdParams P) {
     const int n_keys = CAUSAL ? min(L, q_first + q_rows) : L;
     const int n_steps = ceil_div(n_keys, C::BN);
     const int n_free = min(n_steps, (CAUSAL ? q_first : L) / C::BN);  // steps without a mask
-    const int qpos0 = q_first + w * 32 * C::QB + li;  // query position of block 0 in this lane
+    const int qpos = q_first + w * 32 + li;  // query position of this lane
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
     const int rowbytes = int(rstride * 2);
     // stage st holds keys [st*BN, st*BN + BN): a resource starting at that row,
     // covering the rest of the sequence (keys past the end read as zero)
-    auto load_stage = [&](int st, uint16_t* buf) {
+    auto load_stage = [&](int st) {
+      uint16_t* buf = lds + (st % C::NS) * C::STAGE;
       const int64_t r0 = int64_t(st) * C::BN * rstride;
       tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
       tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, L - st * C::BN),
                                  rowbytes, w, lane);
     };
+    auto stage_ptr = [&](int st) { return lds + (st % C::NS) * C::STAGE; };
 
-    // Q fragments first, then the first two K/V stages (older loads complete first)
-    u32x4 qf[C::QB][C::DS];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int qpos = qpos0 + qb * 32;
+    // Q fragments first, then the first three K/V stages (older loads complete first)
+    u32x4 qf[C::DS];
+    {
       const bool ok = qpos < rows_total;
       const int64_t qrow = BCAST ? int64_t(qpos) : int64_t(kv0) + qpos;
 #pragma unroll
       for (int d = 0; d < C::DS; ++d)
-        qf[qb][d] = ok ? ld16(P.q + qrow * rstride + int64_t(h) * D + d * 16 + g * 8)
-                       : u32x4{0, 0, 0, 0};
+        qf[d] = ok ? ld16(P.q + qrow * rstride + int64_t(h) * D + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st) {
-      if (st < n_steps) load_stage(st, lds + st * C::STAGE);
-    }
-    f32x16 o[C::QB][C::NB];
-    float m[C::QB], l[C::QB];
+    for (int st = 0; st < C::NS - 1; ++st)
+      if (st < n_steps) load_stage(st);
+    f32x16 o[C::NB];
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      m[qb] = -INFINITY;
-      l[qb] = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[qb][nb] = f32x16{};
-    }
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x16{};
+    float m = -INFINITY, l = 0.f;
 
-    for (int kt = 0; kt < n_steps; ++kt) {
-      if (C::NS > 2 && kt + 1 < n_steps)
-        wait_vmem_le<C::LOADS>();  // stage kt landed; stage kt+1 may still be in flight
-      else
-        wait_vmem();
+    if (n_steps > 0) {
+      // first step's scores: wait for stage 0 only
+      if (n_steps >= 3) wait_vmem_le<2 * C::LOADS>();
+      else if (n_steps == 2) wait_vmem_le<C::LOADS>();
+      else wait_vmem();
       __syncthreads();
-      if (kt + C::NS - 1 < n_steps) {
-        const int nk = kt + C::NS - 1;
-        load_stage(nk, lds + (nk % C::NS) * C::STAGE);
+      f32x16 sc[C::KB], sn[C::KB];
+      scores<D>(stage_ptr(0), qf, sc, li, g);
+      if (n_free == 0) mask_scores<D, CAUSAL>(sc, g, 0, n_keys, qpos);
+      m = pair_max(row_max<D>(sc)) * P.c;
+
+      // before step kt (kt + 1 < n_steps): stage kt+1 must have landed, stage
+      // kt+2 may still be in flight; the barrier also means every wave is done
+      // with stage kt-1, whose buffer the load of stage kt+3 reuses
+      auto advance = [&](int kt) {
+        if (kt + 2 < n_steps) wait_vmem_le<C::LOADS>();
+        else wait_vmem();
+        __syncthreads();
+        if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
+      };
+      int kt = 0;
+      for (; kt + 1 < n_free; ++kt) {  // the next step needs no mask
+        advance(kt);
+        const float mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                         qf, sc, sn, o, m, l, P.c, lane,
+                                                         (kt + 1) * C::BN, n_keys, qpos);
+        update_max<D>(mx, m, l, o);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
       }
-      const uint16_t* cur = lds + (kt % C::NS) * C::STAGE;
-      if (kt < n_free)
-        fwd_step<D, false, CAUSAL>(cur, cur + C::TILE, qf, o, m, l, P.c, lane, kt * C::BN, n_keys, qpos0);
-      else
-        fwd_step<D, true, CAUSAL>(cur, cur + C::TILE, qf, o, m, l, P.c, lane, kt * C::BN, n_keys, qpos0);
+      for (; kt + 1 < n_steps; ++kt) {  // the next step is the tail or on the diagonal
+        advance(kt);
+        const float mx = fwd_step<D, true, true, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                        qf, sc, sn, o, m, l, P.c, lane,
+                                                        (kt + 1) * C::BN, n_keys, qpos);
+        update_max<D>(mx, m, l, o);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
+      }
+      fwd_step<D, false, false, CAUSAL>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
+                                        lane, 0, n_keys, qpos);
     }
 
     // epilogue: out = O / l (bf16), lse = (m + log2 l) * ln 2
+    const float lt = pair_sum(l);
+    if (qpos < rows_total) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* orow = BCAST ? P.out + ((int64_t(b) * P.lq + qpos) * P.H + h) * D
+                             : P.out + (int64_t(kv0) + qpos) * rstride + int64_t(h) * D;
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int qpos = qpos0 + qb * 32;
-      const float lt = pair_sum(l[qb]);
-      if (qpos < rows_total) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t* orow = BCAST ? P.out + ((int64_t(b) * P.lq + qpos) * P.H + h) * D
-                               : P.out + (int64_t(kv0) + qpos) * rstride + int64_t(h) * D;
+      for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            u32x2 wv;
-            wv[0] = pack_bf16(o[qb][nb][q4 * 4 + 0] * inv, o[qb][nb][q4 * 4 + 1] * inv);
-            wv[1] = pack_bf16(o[qb][nb][q4 * 4 + 2] * inv, o[qb][nb][q4 * 4 + 3] * inv);
-            st8(orow + nb * 32 + q4 * 8 + g * 4, wv);
-          }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 wv;
+          wv[0] = pack_bf16(o[nb][q4 * 4 + 0] * inv, o[nb][q4 * 4 + 1] * inv);
+          wv[1] = pack_bf16(o[nb][q4 * 4 + 2] * inv, o[nb][q4 * 4 + 3] * inv);
+          st8(orow + nb * 32 + q4 * 8 + g * 4, wv);
         }
-        if (g == 0) {
-          const float lse = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
-          if (BCAST)
-            P.lse[(int64_t(b) * P.H + h) * P.lq + qpos] = lse;
-          else
-            P.lse[int64_t(h) * P.total_kv + kv0 + qpos] = lse;
-        }
+      }
+      if (g == 0) {
+        const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+        if (BCAST)
+          P.lse[(int64_t(b) * P.H + h) * P.lq + qpos] = lse;
+        else
+          P.lse[int64_t(h) * P.total_kv + kv0 + qpos] = lse;
       }
     }
     __syncthreads();  // the next tile's first loads overwrite the first stages

@@ -37,27 +37,66 @@ struct Swz {
   __device__ static __forceinline__ int chunk(int r, int c) { return r * D + ((c ^ f(r)) << 3); }
 };
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (four scalar words): base address, stride 0, size in bytes and
+// the configuration word for raw dword access. Loads at offsets >= nbytes return
+// zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
 // Buffer resource over rows [0, nrows) of a bf16 matrix whose rows are `rstride`
-// elements apart and D elements wide. Loads past the last row return zeros.
+// elements apart and D elements wide.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t rstride,
-                                                            int nrows) {
-  const int nbytes = nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, nbytes, 0x00020000);
+__device__ __forceinline__ i32x4 rows_rsrc(const uint16_t* base, int64_t rstride, int nrows) {
+  return make_rsrc(base, nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0);
 }
 
 // Buffer resource over n floats.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t vec_rsrc(const float* base, int n) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, n > 0 ? n * 4 : 0,
-                                           0x00020000);
+__device__ __forceinline__ i32x4 vec_rsrc(const float* base, int n) {
+  return make_rsrc(base, n > 0 ? n * 4 : 0);
+}
+
+// LDS byte address of a pointer into __shared__ memory: the low 32 bits of its
+// generic address (the shared aperture keeps the LDS offset there).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Direct buffer->LDS copies: lane i of the wave writes its 16 (4) loaded bytes to
+// LDS at dst + 16*i (dst + 4*i). They are issued from inline assembly on purpose:
+// the compiler orders LDS reads after an LDS-writing load it knows of by waiting
+// for every outstanding vector memory operation, which would stall each pipeline
+// step on the prefetch it has just issued. Completion is instead awaited
+// explicitly by the kernels (s_waitcnt vmcnt, then a workgroup barrier) before a
+// stage is read. The LDS base goes in M0 (set by the compiler from the operand);
+// one wait state separates that write from the load that reads it.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, void* dst, int voffset) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr(dst))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4& rsrc, void* dst, int voffset) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr(dst))
+               : "memory");
 }
 
 // Fill a ROWS x D tile from the rows [0, ROWS) of `rsrc` with direct buffer->LDS
 // 16-byte loads issued by the NW waves of the workgroup (rows the resource does
 // not cover arrive as zeros).
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void tile_load(uint16_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
-                                          int rowbytes, int wave, int lane) {
+__device__ __forceinline__ void tile_load(uint16_t* lds_tile, const i32x4& rsrc, int rowbytes,
+                                          int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int INSTR = ROWS * CPR / 64;  // one instruction moves 64 chunks
   static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
@@ -67,14 +106,13 @@ __device__ __forceinline__ void tile_load(uint16_t* lds_tile, __amdgpu_buffer_rs
     const int q = blk * 64 + lane;  // LDS chunk index within the tile
     const int r = q / CPR;
     const int c = (q % CPR) ^ Swz<D>::f(r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + blk * 512), 16,
-                                             r * rowbytes + c * 16, 0, 0, 0);
+    dma16(rsrc, lds_tile + blk * 512, r * rowbytes + c * 16);
   }
 }
 
 // 64 floats (entries [0, 64) of `rsrc`) with direct 4-byte loads by one wave.
-__device__ __forceinline__ void vec64_load(float* lds_vec, __amdgpu_buffer_rsrc_t rsrc, int lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_vec, 4, lane * 4, 0, 0, 0);
+__device__ __forceinline__ void vec64_load(float* lds_vec, const i32x4& rsrc, int lane) {
+  dma4(rsrc, lds_vec, lane * 4);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
