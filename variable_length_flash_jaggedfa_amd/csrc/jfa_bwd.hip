@@ -21,6 +21,8 @@
 // workgroup a (query tile, head, group of sequences), accumulates on chip over
 // the group, stores one float32 partial per group, and a last kernel sums the
 // partials in a fixed order.
+#include <type_traits>
+
 #include "jfa_internal.h"
 #include "jfa_tiles.h"
 
@@ -300,9 +302,10 @@ struct KvCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int BM = jfa::kBwdBM;  // query rows per step
   static constexpr int IB = BM / 32;
-  static constexpr int NS = 3;
+  static constexpr int NS = 4;            // LDS ring stages
   static constexpr int DS = D / 16;
   static constexpr int NB = D / 32;
+  static constexpr int NX = 2 * IB * NB;  // dV (or dK) products per step
   static constexpr int TILE = BM * D;
   static constexpr int STAGE = 2 * TILE;  // Q then dO
   static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;
@@ -318,50 +321,71 @@ struct KvParams {
   float c, scale;
 };
 
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos, const float* lse_s,
-                                        const float* di_s, const u32x4 (&kf)[KvCfg<D>::DS],
-                                        const u32x4 (&vf)[KvCfg<D>::DS],
-                                        f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB],
-                                        float c, int lane, int q0, int jw) {
+// S = Q K^T and dP = dO V^T for one step of BM query rows (lane = key); all row
+// fragments of one k-step are read before its MFMAs.
+template <int D>
+__device__ __forceinline__ void kv_scores(uint32_t qs, uint32_t dos, const LaneOffsets<D>& lo,
+                                          const u32x4 (&kf)[KvCfg<D>::DS],
+                                          const u32x4 (&vf)[KvCfg<D>::DS],
+                                          f32x16 (&s)[KvCfg<D>::IB], f32x16 (&dp)[KvCfg<D>::IB]) {
   using C = KvCfg<D>;
-  // recompute lane-derived LDS addresses here rather than keep them live across steps
-  asm volatile("" : "+v"(lane));
-  constexpr int IB = C::IB;
-  const int g = lane >> 5, li = lane & 31;
-  f32x16 s[IB], dp[IB];
 #pragma unroll
-  for (int ib = 0; ib < IB; ++ib) {
+  for (int ib = 0; ib < C::IB; ++ib) {
     s[ib] = f32x16{};
     dp[ib] = f32x16{};
   }
-  // S = Q K^T and dP = dO V^T (lane = key); row fragments one k-step ahead
-  u32x4 qfr[2][IB], dfr[2][IB];
-#pragma unroll
-  for (int ib = 0; ib < IB; ++ib) {
-    qfr[0][ib] = frag_rows<D>(qs, ib * 32, 0, li, g);
-    dfr[0][ib] = frag_rows<D>(dos, ib * 32, 0, li, g);
-  }
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
-    if (d + 1 < C::DS) {
+    u32x4 qa[C::IB], da[C::IB];
 #pragma unroll
-      for (int ib = 0; ib < IB; ++ib) {
-        qfr[(d + 1) & 1][ib] = frag_rows<D>(qs, ib * 32, d + 1, li, g);
-        dfr[(d + 1) & 1][ib] = frag_rows<D>(dos, ib * 32, d + 1, li, g);
-      }
+    for (int ib = 0; ib < C::IB; ++ib) {
+      qa[ib] = rows_at<D>(qs, lo, ib * 32, d);
+      da[ib] = rows_at<D>(dos, lo, ib * 32, d);
     }
 #pragma unroll
-    for (int ib = 0; ib < IB; ++ib) {
-      s[ib] = mfma32(qfr[d & 1][ib], kf[d], s[ib]);
-      dp[ib] = mfma32(dfr[d & 1][ib], vf[d], dp[ib]);
+    for (int ib = 0; ib < C::IB; ++ib) {
+      s[ib] = mfma32(qa[ib], kf[d], s[ib]);
+      dp[ib] = mfma32(da[ib], vf[d], dp[ib]);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  // P and dS with query rows along the registers
-  u32x4 pp[2 * IB], pd[2 * IB];
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS for one step whose P and dS are packed with
+// query rows along the registers.
+template <int D>
+__device__ __forceinline__ void kv_accumulate(uint32_t qs, uint32_t dos, const LaneOffsets<D>& lo,
+                                              const u32x4 (&pp)[2 * KvCfg<D>::IB],
+                                              const u32x4 (&pd)[2 * KvCfg<D>::IB],
+                                              f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
+  using C = KvCfg<D>;
 #pragma unroll
-  for (int ib = 0; ib < IB; ++ib) {
+  for (int x = 0; x < C::NX; ++x) {
+    const int st = x / C::NB, nb = x % C::NB;
+    const u32x4 fa = cols_at<D>(dos, lo, st * 16, nb * 32);
+    const u32x4 fb = cols_at<D>(qs, lo, st * 16, nb * 32);
+    dv[nb] = mfma32(fa, pp[st], dv[nb]);
+    dk[nb] = mfma32(fb, pd[st], dk[nb]);
+  }
+}
+
+// P = 2^(S c - lse log2 e) and dS = P (dP - Di) for one step, packed to bf16
+// (keys past the diagonal masked with CAUSAL). With PREV, the dV/dK products of
+// the previous step are issued in the same region so that these VALU
+// instructions run under them.
+template <int D, bool MASK, bool PREV>
+__device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
+                                           const f32x16 (&dp)[KvCfg<D>::IB], const float* lse_s,
+                                           const float* di_s, float c, int g, int q0, int jw,
+                                           u32x4 (&pp)[2 * KvCfg<D>::IB], u32x4 (&pd)[2 * KvCfg<D>::IB],
+                                           uint32_t qs_prev, uint32_t dos_prev,
+                                           const LaneOffsets<D>& lo,
+                                           const u32x4 (&pp_prev)[2 * KvCfg<D>::IB],
+                                           const u32x4 (&pd_prev)[2 * KvCfg<D>::IB],
+                                           f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
+  using C = KvCfg<D>;
+  if (PREV) kv_accumulate<D>(qs_prev, dos_prev, lo, pp_prev, pd_prev, dv, dk);
+#pragma unroll
+  for (int ib = 0; ib < C::IB; ++ib) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int i0 = ib * 32 + q4 * 8 + g * 4;
@@ -372,7 +396,7 @@ __device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos,
       for (int e = 0; e < 4; ++e) {
         const int r = q4 * 4 + e;
         float p = exp2_fast(__builtin_fmaf(s[ib][r], c, -lse4[e] * kLog2e));
-        if (MASK && CAUSAL) p = jw > q0 + i0 + e ? 0.f : p;
+        if (MASK) p = jw > q0 + i0 + e ? 0.f : p;
         pv[e] = p;
         dsv[e] = p * (dp[ib][r] - di4[e]);
       }
@@ -383,28 +407,24 @@ __device__ __forceinline__ void kv_step(const uint16_t* qs, const uint16_t* dos,
       pd[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
     }
   }
-  // dV^T += dO^T P, dK^T += Q^T dS; column fragments one step ahead
-  constexpr int NX = 2 * IB * C::NB;
-  u32x4 fa[2], fb[2];
-  fa[0] = frag_cols<D>(dos, 0, 0, lane);
-  fb[0] = frag_cols<D>(qs, 0, 0, lane);
+  if (PREV) {
+    // two products (dV, dK) per column-fragment pair, VALU work spread between
 #pragma unroll
-  for (int x = 0; x < NX; ++x) {
-    const int st = x / C::NB, nb = x % C::NB;
-    if (x + 1 < NX) {
-      fa[(x + 1) & 1] = frag_cols<D>(dos, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
-      fb[(x + 1) & 1] = frag_cols<D>(qs, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
+    for (int x = 0; x < C::NX; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
     }
-    dv[nb] = mfma32(fa[x & 1], pp[st], dv[nb]);
-    dk[nb] = mfma32(fb[x & 1], pd[st], dk[nb]);
-    __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool CAUSAL, bool BCAST>
 __global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(KvCfg<D>::WPE)))
 dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
+  static_assert(C::NS == 4, "the waits below assume a four-stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // lse, Di per stage
   const int tid = threadIdx.x;
@@ -413,6 +433,8 @@ dkdv_kernel(KvParams P) {
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
   const int rowbytes = int(rstride * 2);
+  const LaneOffsets<D> lo(lane);
+  const uint32_t lds0 = lds_addr(lds);
 
   for (int ti = t_begin; ti < t_end; ++ti) {
     const int b = P.tiles[4 * ti + 0], h = P.tiles[4 * ti + 1], n = P.tiles[4 * ti + 2];
@@ -424,57 +446,92 @@ dkdv_kernel(KvParams P) {
     const bool key_ok = jw < L;
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
-    u32x4 kf[C::DS], vf[C::DS];
-#pragma unroll
-    for (int d = 0; d < C::DS; ++d) {
-      kf[d] = key_ok ? ld16(kbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
-      vf[d] = key_ok ? ld16(vbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    }
-    f32x16 dv[C::NB], dk[C::NB];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      dv[nb] = f32x16{};
-      dk[nb] = f32x16{};
-    }
     const uint16_t* qbase = BCAST ? P.q + int64_t(h) * D : P.q + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* dobase = BCAST ? P.dout + int64_t(b) * P.lq * rstride + int64_t(h) * D
                                    : P.dout + int64_t(kv0) * rstride + int64_t(h) * D;
     const int64_t voff = BCAST ? (int64_t(b) * P.H + h) * P.lq : int64_t(h) * P.total_kv + kv0;
     const int qs_lo = CAUSAL ? key0 / C::BM : 0;
     const int n_steps = ceil_div(rows_total, C::BM) - qs_lo;
-    auto load_stage = [&](int st, int buf) {
+    // causal steps that reach the diagonal need a mask; rows past the end read as
+    // zeros and contribute nothing
+    const int n_mask = CAUSAL ? min(n_steps, C::BN / C::BM) : 0;
+    auto load_stage = [&](int st) {
       const int q_first = (qs_lo + st) * C::BM;
       const int left = rows_total - q_first;
+      const int buf = st % C::NS;
       uint16_t* dst = lds + buf * C::STAGE;
       tile_load<D, C::BM, C::NW>(dst, rows_rsrc<D>(qbase + int64_t(q_first) * rstride, rstride, left),
                                  rowbytes, w, lane);
       tile_load<D, C::BM, C::NW>(dst + C::TILE,
                                  rows_rsrc<D>(dobase + int64_t(q_first) * rstride, rstride, left),
                                  rowbytes, w, lane);
-      if (w < 2 && lane < C::BM) {
+      if (w < 2) {
         const float* src = (w == 0 ? P.lse : P.di) + voff + q_first;
         vec64_load(vecs[buf][w], vec_rsrc(src, left), lane);
       }
     };
-#pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st)
-      if (st < n_steps) load_stage(st, st);
-    for (int it = 0; it < n_steps; ++it) {
-      if (it + 1 < n_steps)
-        wait_vmem_le<C::LOADS>();
-      else
-        wait_vmem();
+    auto qs_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
+    // stage st is read once it has landed (stage st+1 may still be in flight)
+    auto arrive = [&](int st) {
+      if (st + 1 < n_steps) wait_vmem_le<C::LOADS>();
+      else wait_vmem();
       __syncthreads();
-      if (it + C::NS - 1 < n_steps) load_stage(it + C::NS - 1, (it + C::NS - 1) % C::NS);
-      const int buf = it % C::NS;
-      const uint16_t* cur = lds + buf * C::STAGE;
-      const int q0 = (qs_lo + it) * C::BM;
-      // only causal steps that reach the diagonal need a mask; rows past the end
-      // read as zeros and contribute nothing
-      if (CAUSAL && q0 < key0 + C::BN)
-        kv_step<D, true, CAUSAL>(cur, cur + C::TILE, vecs[buf][0], vecs[buf][1], kf, vf, dv, dk, P.c, lane, q0, jw);
+    };
+
+    // K, V of this wave's 32 keys, then the first two stages. Step it reads the
+    // rows of stage it and the columns of stage it-1, so the load issued at step it
+    // (stage it+2) goes to the buffer of stage it-2.
+    u32x4 kf[C::DS], vf[C::DS];
+#pragma unroll
+    for (int d = 0; d < C::DS; ++d) {
+      kf[d] = key_ok ? ld16(kbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+      vf[d] = key_ok ? ld16(vbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int st = 0; st < C::NS - 2; ++st)
+      if (st < n_steps) load_stage(st);
+    f32x16 dv[C::NB], dk[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      dv[nb] = f32x16{};
+      dk[nb] = f32x16{};
+    }
+
+    if (n_steps > 0) {
+      f32x16 s[C::IB], dp[C::IB];
+      u32x4 pp[2 * C::IB], pd[2 * C::IB], ppv[2 * C::IB], pdv[2 * C::IB];
+      // step 0
+      arrive(0);
+      if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
+      kv_scores<D>(qs_of(0), qs_of(0) + C::TILE * 2, lo, kf, vf, s, dp);
+      const int q00 = qs_lo * C::BM;
+      if (n_mask > 0)
+        kv_softmax<D, true, false>(s, dp, vecs[0][0], vecs[0][1], P.c, g, q00, jw, pp, pd, 0, 0, lo,
+                                   ppv, pdv, dv, dk);
       else
-        kv_step<D, false, CAUSAL>(cur, cur + C::TILE, vecs[buf][0], vecs[buf][1], kf, vf, dv, dk, P.c, lane, q0, jw);
+        kv_softmax<D, false, false>(s, dp, vecs[0][0], vecs[0][1], P.c, g, q00, jw, pp, pd, 0, 0,
+                                    lo, ppv, pdv, dv, dk);
+      // step it: its scores, then its softmax under the previous step's products
+      auto step = [&](int it, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int x = 0; x < 2 * C::IB; ++x) {
+          ppv[x] = pp[x];
+          pdv[x] = pd[x];
+        }
+        arrive(it);  // also: every wave is done with stage it-2
+        if (it + C::NS - 2 < n_steps) load_stage(it + C::NS - 2);
+        const uint32_t qs = qs_of(it), qp = qs_of(it - 1);
+        kv_scores<D>(qs, qs + C::TILE * 2, lo, kf, vf, s, dp);
+        const int buf = it % C::NS;
+        kv_softmax<D, MASK, true>(s, dp, vecs[buf][0], vecs[buf][1], P.c, g, (qs_lo + it) * C::BM, jw,
+                                  pp, pd, qp, qp + C::TILE * 2, lo, ppv, pdv, dv, dk);
+      };
+      int it = 1;
+      for (; it < n_mask; ++it) step(it, std::true_type{});
+      for (; it < n_steps; ++it) step(it, std::false_type{});
+      const uint32_t ql = qs_of(n_steps - 1);
+      kv_accumulate<D>(ql, ql + C::TILE * 2, lo, pp, pd, dv, dk);
     }
     __syncthreads();  // the next tile's first loads overwrite the first stages
     if (key_ok) {

@@ -166,15 +166,14 @@ __device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks
   for (int x = 0; x < 2; ++x)
     vf[x] = frag_cols<D>(vs, (x / C::NB) * 16, (x % C::NB) * 32, lane);
   if (NEXT) {
-    // each MFMA with a share of the VALU work and the K read two MFMAs ahead,
-    // then the V reads
+    // all K reads first (their latency is paid once), then each MFMA with a
+    // share of the VALU work, then the first V reads
     constexpr int NK = C::KB * C::DS;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6 * C::KB, 0);
-      if (i + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
   }

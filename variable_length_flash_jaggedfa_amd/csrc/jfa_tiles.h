@@ -140,4 +140,52 @@ __device__ __forceinline__ u32x4 frag_cols(const uint16_t* tile, int k0, int c0,
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// ---- fragment reads from precomputed per-lane byte offsets
+//
+// Because f(r) depends on r mod 8 only, the swizzled position of any fragment
+// splits into a per-lane part that is the same for every block of a tile and a
+// block part that is a compile-time constant. The kernels compute the lane parts
+// once and every read is one address add plus an immediate offset.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
+
+template <int D>
+struct LaneOffsets {
+  uint32_t row[4];  // frag_rows, k-chunk kc (kc & 3); kc >= 4 adds 128 bytes
+  int32_t col[2];   // frag_cols, for c0/8 with bit 2 clear / set
+  __device__ __forceinline__ explicit LaneOffsets(int lane) {
+    const int g = lane >> 5, li = lane & 31;
+    const int fl = Swz<D>::f(li);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) row[kc] = uint32_t((li * D + (((2 * kc + g) ^ fl) << 3)) * 2);
+    const int G = lane >> 4, j = lane & 15;
+    const int fr = Swz<D>::f(g * 4 + (j >> 2));
+    const int x = (G & 1) * 2 + ((j & 3) >> 1);
+    const int lo = (g * 4 + (j >> 2)) * D + (((x ^ fr) & 3) << 3) + 4 * (j & 1);
+    const int s4 = fr & 4;
+    col[0] = (lo + (s4 << 3)) * 2;
+    col[1] = (lo - (s4 << 3)) * 2;
+  }
+};
+
+__device__ __forceinline__ u32x4 lds_ld16(uint32_t addr) {
+  return *(lds_u32x4_t*)(size_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_tr8(uint32_t addr) {
+  const f16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)(size_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// frag_rows of a tile at LDS byte address tb (r0 a multiple of 8).
+template <int D>
+__device__ __forceinline__ u32x4 rows_at(uint32_t tb, const LaneOffsets<D>& lo, int r0, int kc) {
+  return lds_ld16(tb + lo.row[kc & 3] + uint32_t(r0 * D * 2 + (kc >> 2) * 128));
+}
+// frag_cols of a tile at LDS byte address tb (k0 a multiple of 16, c0 of 32).
+template <int D>
+__device__ __forceinline__ u32x4 cols_at(uint32_t tb, const LaneOffsets<D>& lo, int k0, int c0) {
+  const uint32_t a = tb + uint32_t(lo.col[(c0 >> 5) & 1] + k0 * D * 2 + (c0 / 8) * 16);
+  const u32x2 x = lds_tr8(a), y = lds_tr8(a + 8 * D * 2);
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
 }  // namespace jfa_dev
