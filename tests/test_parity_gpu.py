@@ -180,3 +180,31 @@ def test_backward_passes_match_fused_call(gpu):
         plan.backward(q, k, v, out, do, lse, dq=dq2, dk=dk2, dv=dv2, passes=jfa.PASS_DKDV)
         torch.cuda.synchronize()
         assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
+@pytest.mark.parametrize("D,L", [(128, 129), (64, 300), (128, 128)])
+def test_broadcast_one_sequence_matches_jagged(gpu, D, L):
+    """Broadcast-Q with one sequence and Lq = L is jagged self-attention on the same
+    tensors: both paths must agree with the oracle, on repeated runs, at lengths
+    that stream several LDS stages (a hazard in the global->LDS copies once made
+    the broadcast dQ pass read stale tiles there)."""
+    import torch
+    wb = J.custom([L], 1, D, sigma=0.5, seed=18, kind="broadcast", lq=L)
+    cb = J.make_case(wb)
+    ref = oracle_full(cb)
+    wj = J.custom([L], 1, D, sigma=0.5, seed=18)
+    cj = J.Case(wj, np.array([L]), cb.offsets, cb.q, cb.k, cb.v, cb.do[0], cb.scale)
+    rj = GpuRun(cj, gpu)
+    rj.forward()
+    dqj, _, _ = rj.backward()
+    assert_grad(bf16_to_f64(dqj), ref[2], "jagged dq")
+    first = None
+    for _ in range(3):
+        rb = GpuRun(cb, gpu)
+        rb.forward()
+        dqb, dkb, dvb = (x.clone() for x in rb.backward())
+        assert_grad(bf16_to_f64(dqb), ref[2], "broadcast dq")
+        assert_grad(bf16_to_f64(dkb), ref[3], "broadcast dk")
+        if first is None:
+            first = dqb
+        assert torch.equal(first, dqb)

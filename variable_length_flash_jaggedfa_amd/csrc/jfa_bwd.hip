@@ -43,9 +43,10 @@ struct DqCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int BN = D == 128 ? 32 : 64;  // keys per step
   static constexpr int KB = BN / 32;
-  static constexpr int NS = 3;                   // LDS ring stages
+  static constexpr int NS = 4;                   // LDS ring stages
   static constexpr int DS = D / 16;
   static constexpr int NB = D / 32;
+  static constexpr int NX = 2 * KB * NB;         // dQ products per step
   static constexpr int TILE = BN * D;
   static constexpr int STAGE = 2 * TILE;         // K then V
   static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;
@@ -62,50 +63,63 @@ struct DqParams {
   float c, scale;
 };
 
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
-                                        const u32x4 (&qf)[DqCfg<D>::DS],
-                                        const u32x4 (&dof)[DqCfg<D>::DS],
-                                        f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
-                                        float c, int lane, int key0, int n_keys, int qpos) {
+// S^T = K Q^T and dP^T = V dO^T for one step of BN keys (lane = query row).
+template <int D>
+__device__ __forceinline__ void dq_scores(uint32_t ks, uint32_t vs, const LaneOffsets<D>& lo,
+                                          const u32x4 (&qf)[DqCfg<D>::DS],
+                                          const u32x4 (&dof)[DqCfg<D>::DS],
+                                          f32x16 (&s)[DqCfg<D>::KB], f32x16 (&dp)[DqCfg<D>::KB]) {
   using C = DqCfg<D>;
-  // recompute lane-derived LDS addresses here rather than keep them live across steps
-  asm volatile("" : "+v"(lane));
-  constexpr int KB = C::KB;
-  const int g = lane >> 5, li = lane & 31;
-  f32x16 s[KB], dp[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int kb = 0; kb < C::KB; ++kb) {
     s[kb] = f32x16{};
     dp[kb] = f32x16{};
   }
-  // S^T = K Q^T and dP^T = V dO^T; row fragments one k-step ahead
-  u32x4 kfr[2][KB], vfr[2][KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    kfr[0][kb] = frag_rows<D>(ks, kb * 32, 0, li, g);
-    vfr[0][kb] = frag_rows<D>(vs, kb * 32, 0, li, g);
-  }
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
-    if (d + 1 < C::DS) {
+    u32x4 ka[C::KB], va[C::KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        kfr[(d + 1) & 1][kb] = frag_rows<D>(ks, kb * 32, d + 1, li, g);
-        vfr[(d + 1) & 1][kb] = frag_rows<D>(vs, kb * 32, d + 1, li, g);
-      }
+    for (int kb = 0; kb < C::KB; ++kb) {
+      ka[kb] = rows_at<D>(ks, lo, kb * 32, d);
+      va[kb] = rows_at<D>(vs, lo, kb * 32, d);
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = mfma32(kfr[d & 1][kb], qf[d], s[kb]);
-      dp[kb] = mfma32(vfr[d & 1][kb], dof[d], dp[kb]);
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = mfma32(ka[kb], qf[d], s[kb]);
+      dp[kb] = mfma32(va[kb], dof[d], dp[kb]);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  // P = 2^(S c - lse2), dS = P (dP - Di), packed with keys along the registers
-  u32x4 pds[2 * KB];
+}
+
+// dQ^T += K^T dS^T for one step whose dS is packed with keys along the registers.
+template <int D>
+__device__ __forceinline__ void dq_accumulate(uint32_t ks, const LaneOffsets<D>& lo,
+                                              const u32x4 (&pds)[2 * DqCfg<D>::KB],
+                                              f32x16 (&acc)[DqCfg<D>::NB]) {
+  using C = DqCfg<D>;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int x = 0; x < C::NX; ++x) {
+    const int st = x / C::NB, nb = x % C::NB;
+    acc[nb] = mfma32(cols_at<D>(ks, lo, st * 16, nb * 32), pds[st], acc[nb]);
+  }
+}
+
+// P = 2^(S c - lse2) and dS = P (dP - Di) for one step, packed to bf16 (keys past
+// the sequence end or, with CAUSAL, after the lane's query masked). With PREV the
+// dQ products of the previous step are issued in the same region so that these
+// VALU instructions run under them.
+template <int D, bool MASK, bool CAUSAL, bool PREV>
+__device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
+                                           const f32x16 (&dp)[DqCfg<D>::KB], float lse2, float di,
+                                           float c, int g, int key0, int n_keys, int qpos,
+                                           u32x4 (&pds)[2 * DqCfg<D>::KB], uint32_t ks_prev,
+                                           const LaneOffsets<D>& lo,
+                                           const u32x4 (&pds_prev)[2 * DqCfg<D>::KB],
+                                           f32x16 (&acc)[DqCfg<D>::NB]) {
+  using C = DqCfg<D>;
+  if (PREV) dq_accumulate<D>(ks_prev, lo, pds_prev, acc);
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -lse2));
@@ -118,54 +132,76 @@ __device__ __forceinline__ void dq_step(const uint16_t* ks, const uint16_t* vs,
       pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
     }
   }
-  // dQ^T += K^T dS^T; column fragments of K one step ahead
-  constexpr int NX = 2 * KB * C::NB;
-  u32x4 fr[2];
-  fr[0] = frag_cols<D>(ks, 0, 0, lane);
+  if (PREV) {
 #pragma unroll
-  for (int x = 0; x < NX; ++x) {
-    const int st = x / C::NB, nb = x % C::NB;
-    if (x + 1 < NX) fr[(x + 1) & 1] = frag_cols<D>(ks, ((x + 1) / C::NB) * 16, ((x + 1) % C::NB) * 32, lane);
-    acc[nb] = mfma32(fr[x & 1], pds[st], acc[nb]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int x = 0; x < C::NX; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, MASK ? 10 : 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2 * C::KB, 0);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stream the keys [0, n_keys) of one (sequence, head) past one query tile.
+// Stream the keys [0, n_keys) of one (sequence, head) past one query tile. Step kt
+// reads the rows of stage kt and the columns of stage kt-1 of a four-stage ring,
+// so the load issued at step kt (stage kt+2) goes to the buffer of stage kt-2.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
                                           int64_t rstride, int L, int n_keys, int n_free,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
-                                          float c, int w, int lane, int qpos) {
+                                          float c, int w, int lane, int qpos,
+                                          const LaneOffsets<D>& lo) {
   using C = DqCfg<D>;
+  static_assert(C::NS == 4, "the ring below assumes four stages");
+  const int g = lane >> 5;
   const int n_steps = ceil_div(n_keys, C::BN);
   const int rowbytes = int(rstride * 2);
-  auto load_stage = [&](int st, uint16_t* buf) {
+  const uint32_t lds0 = lds_addr(lds);
+  auto load_stage = [&](int st) {
+    uint16_t* buf = lds + (st % C::NS) * C::STAGE;
     const int64_t r0 = int64_t(st) * C::BN * rstride;
     tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
     tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, L - st * C::BN),
                                rowbytes, w, lane);
   };
-#pragma unroll
-  for (int st = 0; st < C::NS - 1; ++st)
-    if (st < n_steps) load_stage(st, lds + st * C::STAGE);
-  for (int kt = 0; kt < n_steps; ++kt) {
-    if (kt + 1 < n_steps)
-      wait_vmem_le<C::LOADS>();
-    else
-      wait_vmem();
+  auto ks_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
+  auto arrive = [&](int st) {
+    if (st + 1 < n_steps) wait_vmem_le<C::LOADS>();
+    else wait_vmem();
     __syncthreads();
-    if (kt + C::NS - 1 < n_steps) {
-      const int nk = kt + C::NS - 1;
-      load_stage(nk, lds + (nk % C::NS) * C::STAGE);
-    }
-    const uint16_t* cur = lds + (kt % C::NS) * C::STAGE;
-    if (kt < n_free)
-      dq_step<D, false, CAUSAL>(cur, cur + C::TILE, qf, dof, acc, lse2, di, c, lane, kt * C::BN, n_keys, qpos);
+  };
+#pragma unroll
+  for (int st = 0; st < C::NS - 2; ++st)
+    if (st < n_steps) load_stage(st);
+  if (n_steps > 0) {
+    f32x16 s[C::KB], dp[C::KB];
+    u32x4 pds[2 * C::KB], pdv[2 * C::KB];
+    arrive(0);
+    if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
+    dq_scores<D>(ks_of(0), ks_of(0) + C::TILE * 2, lo, qf, dof, s, dp);
+    if (n_free == 0)
+      dq_softmax<D, true, CAUSAL, false>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv, acc);
     else
-      dq_step<D, true, CAUSAL>(cur, cur + C::TILE, qf, dof, acc, lse2, di, c, lane, kt * C::BN, n_keys, qpos);
+      dq_softmax<D, false, CAUSAL, false>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv, acc);
+    auto step = [&](int kt, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+      for (int x = 0; x < 2 * C::KB; ++x) pdv[x] = pds[x];
+      arrive(kt);  // also: every wave is done with stage kt-2
+      if (kt + C::NS - 2 < n_steps) load_stage(kt + C::NS - 2);
+      const uint32_t ks = ks_of(kt);
+      dq_scores<D>(ks, ks + C::TILE * 2, lo, qf, dof, s, dp);
+      dq_softmax<D, MASK, CAUSAL, true>(s, dp, lse2, di, c, g, kt * C::BN, n_keys, qpos, pds,
+                                        ks_of(kt - 1), lo, pdv, acc);
+    };
+    int kt = 1;
+    for (; kt < n_free; ++kt) step(kt, std::false_type{});
+    for (; kt < n_steps; ++kt) step(kt, std::true_type{});
+    dq_accumulate<D>(ks_of(n_steps - 1), lo, pds, acc);
   }
   __syncthreads();  // the next stream's first loads overwrite the first stages
 }
@@ -195,6 +231,7 @@ dq_kernel(DqParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
+  const LaneOffsets<D> lo(lane);
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
@@ -220,7 +257,7 @@ dq_kernel(DqParams P) {
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
     dq_stream<D, CAUSAL>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, n_keys, n_free,
-                         qf, dof, acc, lse2, di, P.c, w, lane, qpos);
+                         qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
     if (ok) {
       uint16_t* dqrow = P.dq + eoff;
 #pragma unroll
@@ -244,6 +281,7 @@ dq_bcast_kernel(DqParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
+  const LaneOffsets<D> lo(lane);
   const int n_qt = ceil_div(P.lq, C::BM);
   const int t = blockIdx.x % n_qt, h = (blockIdx.x / n_qt) % P.H, grp = blockIdx.x / (n_qt * P.H);
   const int b0 = int(int64_t(grp) * P.num_seqs / P.groups);
@@ -267,7 +305,7 @@ dq_bcast_kernel(DqParams P) {
     if (L > 0)
       dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
                           P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, L / C::BN,
-                          qf, dof, acc, lse2, di, P.c, w, lane, qpos);
+                          qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;

@@ -76,16 +76,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // for every outstanding vector memory operation, which would stall each pipeline
 // step on the prefetch it has just issued. Completion is instead awaited
 // explicitly by the kernels (s_waitcnt vmcnt, then a workgroup barrier) before a
-// stage is read. The LDS base goes in M0 (set by the compiler from the operand);
-// one wait state separates that write from the load that reads it.
+// stage is read. The LDS base goes in M0 (set by the compiler from the operand).
+// The compiler cannot see the vector memory instruction inside the assembly, so
+// it does not pad the hazards that instruction has on its scalar operands: the
+// descriptor words may have just been written by v_readfirstlane (a VALU write
+// of an SGPR needs 5 wait states before a vector memory instruction reads it)
+// and M0 by s_mov. s_nop 4 provides those 5 wait states.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, void* dst, int voffset) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr(dst))
                : "memory");
 }
 __device__ __forceinline__ void dma4(const i32x4& rsrc, void* dst, int voffset) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr(dst))
                : "memory");
