@@ -111,10 +111,14 @@ KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "
 
 
 def kernel_source_digest():
+    """Digest of the kernel sources, or None when they are not present."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "variable_length_flash_jaggedfa_amd", "csrc", name), "rb") as f:
+        p = os.path.join(ROOT, "variable_length_flash_jaggedfa_amd", "csrc", name)
+        if not os.path.exists(p):
+            return None
+        with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -126,6 +130,8 @@ def measured_traffic(kernel, variant):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     digest = kernel_source_digest()
+    if digest is None:
+        return None
     for line in open(TRAFFIC_FILE):
         f = line.split()
         # record: traffic <kernel-name-without-spaces> <variant> <bytes> <source-digest>

@@ -407,9 +407,11 @@ __device__ __forceinline__ void kv_accumulate(uint32_t qs, uint32_t dos, const L
 }
 
 // P = 2^(S c - lse log2 e) and dS = P (dP - Di) for one step, packed to bf16
-// (keys past the diagonal masked with CAUSAL). With PREV, the dV/dK products of
-// the previous step are issued in the same region so that these VALU
-// instructions run under them.
+// (keys past the diagonal masked with CAUSAL). The work is cut into IB*4 groups
+// of four query rows. With PREV, each group is issued together with a share of
+// the previous step's dV/dK products, between scheduling fences, so that the
+// VALU work runs while those MFMAs execute; their column fragments and the
+// group's lse/Di values are read one group ahead.
 template <int D, bool MASK, bool PREV>
 __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
                                            const f32x16 (&dp)[KvCfg<D>::IB], const float* lse_s,
@@ -421,41 +423,59 @@ __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
                                            const u32x4 (&pd_prev)[2 * KvCfg<D>::IB],
                                            f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
   using C = KvCfg<D>;
-  if (PREV) kv_accumulate<D>(qs_prev, dos_prev, lo, pp_prev, pd_prev, dv, dk);
+  constexpr int NG = C::IB * 4;      // groups of 4 query rows (per lane: 4 registers)
+  constexpr int XPG = C::NX / NG;    // dV/dK product pairs per group
+  static_assert(XPG * NG == C::NX, "products must split evenly over the groups");
+  u32x4 fa[2][XPG], fb[2][XPG];
+  f32x4 lse4[2], di4[2];
+  auto read_cols = [&](int grp, int buf) {
 #pragma unroll
-  for (int ib = 0; ib < C::IB; ++ib) {
+    for (int xx = 0; xx < XPG; ++xx) {
+      const int x = grp * XPG + xx, st = x / C::NB, nb = x % C::NB;
+      fa[buf][xx] = cols_at<D>(dos_prev, lo, st * 16, nb * 32);
+      fb[buf][xx] = cols_at<D>(qs_prev, lo, st * 16, nb * 32);
+    }
+  };
+  auto read_vec = [&](int grp, int buf) {
+    const int i0 = (grp / 4) * 32 + (grp % 4) * 8 + g * 4;
+    lse4[buf] = *reinterpret_cast<const f32x4*>(lse_s + i0);
+    di4[buf] = *reinterpret_cast<const f32x4*>(di_s + i0);
+  };
+  if (PREV) read_cols(0, 0);
+  read_vec(0, 0);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int i0 = ib * 32 + q4 * 8 + g * 4;
-      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + i0);
-      const f32x4 di4 = *reinterpret_cast<const f32x4*>(di_s + i0);
-      float pv[4], dsv[4];
+  for (int grp = 0; grp < NG; ++grp) {
+    const int cur = grp & 1;
+    if (grp + 1 < NG) {
+      if (PREV) read_cols(grp + 1, cur ^ 1);
+      read_vec(grp + 1, cur ^ 1);
+    }
+    if (PREV) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = q4 * 4 + e;
-        float p = exp2_fast(__builtin_fmaf(s[ib][r], c, -lse4[e] * kLog2e));
-        if (MASK) p = jw > q0 + i0 + e ? 0.f : p;
-        pv[e] = p;
-        dsv[e] = p * (dp[ib][r] - di4[e]);
+      for (int xx = 0; xx < XPG; ++xx) {
+        const int x = grp * XPG + xx, st = x / C::NB, nb = x % C::NB;
+        dv[nb] = mfma32(fa[cur][xx], pp_prev[st], dv[nb]);
+        dk[nb] = mfma32(fb[cur][xx], pd_prev[st], dk[nb]);
       }
-      const int st = ib * 2 + q4 / 2, hw = (q4 % 2) * 2;
-      pp[st][hw] = pack_bf16(pv[0], pv[1]);
-      pp[st][hw + 1] = pack_bf16(pv[2], pv[3]);
-      pd[st][hw] = pack_bf16(dsv[0], dsv[1]);
-      pd[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
     }
-  }
-  if (PREV) {
-    // two products (dV, dK) per column-fragment pair, VALU work spread between
+    const int ib = grp / 4, q4 = grp % 4;
+    const int i0 = ib * 32 + q4 * 8 + g * 4;
+    float pv[4], dsv[4];
 #pragma unroll
-    for (int x = 0; x < C::NX; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+    for (int e = 0; e < 4; ++e) {
+      const int r = q4 * 4 + e;
+      float p = exp2_fast(__builtin_fmaf(s[ib][r], c, -lse4[cur][e] * kLog2e));
+      if (MASK) p = jw > q0 + i0 + e ? 0.f : p;
+      pv[e] = p;
+      dsv[e] = p * (dp[ib][r] - di4[cur][e]);
     }
+    const int st = ib * 2 + q4 / 2, hw = (q4 % 2) * 2;
+    pp[st][hw] = pack_bf16(pv[0], pv[1]);
+    pp[st][hw + 1] = pack_bf16(pv[2], pv[3]);
+    pd[st][hw] = pack_bf16(dsv[0], dsv[1]);
+    pd[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool CAUSAL, bool BCAST>

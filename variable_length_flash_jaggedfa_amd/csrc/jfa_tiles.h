@@ -26,13 +26,23 @@ typedef __attribute__((address_space(3))) f16x4_t lds_f16x4_t;
 
 template <int D>
 struct Swz {
+  static_assert(D == 64 || D == 128, "rows of 64 or 128 bf16");
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  // LDS has 32 four-byte banks (128 bytes). A 16-byte read is served 8 lanes at
-  // a time, so 8 consecutive rows reading one chunk need 8 distinct 16-byte
-  // slots mod 128 B: f(r) & 7 takes 8 values over any aligned 8 rows. A transpose
-  // read is served 16 lanes (4 rows x 32 bytes) at a time, so 4 aligned rows need
-  // distinct 32-byte slot pairs: f(r) & 6 takes 4 values over any aligned 4 rows.
-  __device__ static __forceinline__ int f(int r) { return ((2 * r) & 6) | ((r >> 2) & 1); }
+  // The gfx950 LDS has 64 four-byte banks (256 bytes per cycle). A 16-byte read
+  // is served 16 lanes at a time and frag_rows gives those lanes 16 consecutive
+  // rows (aligned to 16) and one logical chunk, so the 16 rows must land on 16
+  // distinct 16-byte slots mod 256 bytes. A transpose read serves 32 lanes at a
+  // time: 4 consecutive rows (aligned to 4) x 4 consecutive chunks (aligned to
+  // 4) x 8 bytes, so the 4 rows must put their aligned block of 4 chunks on 4
+  // distinct 64-byte quarters mod 256 bytes. f depends on r mod 16 only.
+  //   D = 128 (one row per 256 bytes): f = (r1 r0 r3 r2), a bijection on r mod
+  //     16, whose bits 2-3 take 4 values over 4 aligned rows.
+  //   D = 64 (two rows per 256 bytes, r0 picks the half): f = (r1 r3 r2), a
+  //     bijection on the 8 rows of each parity, whose bit 2 differs between
+  //     rows r and r+2.
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
   // element offset of logical chunk c of row r
   __device__ static __forceinline__ int chunk(int r, int c) { return r * D + ((c ^ f(r)) << 3); }
 };
@@ -146,28 +156,29 @@ __device__ __forceinline__ u32x4 frag_cols(const uint16_t* tile, int k0, int c0,
 
 // ---- fragment reads from precomputed per-lane byte offsets
 //
-// Because f(r) depends on r mod 8 only, the swizzled position of any fragment
-// splits into a per-lane part that is the same for every block of a tile and a
-// block part that is a compile-time constant. The kernels compute the lane parts
-// once and every read is one address add plus an immediate offset.
+// f depends on r mod 16 only, so for blocks that start at a row that is a
+// multiple of 16 the swizzled position of a fragment is a per-lane part, the
+// same for every such block, plus the block's row offset. The kernels compute
+// the lane parts once; every read is then one address add and an immediate.
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
 
 template <int D>
 struct LaneOffsets {
-  uint32_t row[4];  // frag_rows, k-chunk kc (kc & 3); kc >= 4 adds 128 bytes
-  int32_t col[2];   // frag_cols, for c0/8 with bit 2 clear / set
+  static constexpr int DS = D / 16, NB = D / 32;
+  uint32_t row[DS];     // frag_rows, k-chunk kc, rows 0..31 of a block
+  uint32_t col[NB][2];  // frag_cols, column block nb, rows 0..7 and 8..15 of a k-block
   __device__ __forceinline__ explicit LaneOffsets(int lane) {
     const int g = lane >> 5, li = lane & 31;
-    const int fl = Swz<D>::f(li);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) row[kc] = uint32_t((li * D + (((2 * kc + g) ^ fl) << 3)) * 2);
+    for (int kc = 0; kc < DS; ++kc) row[kc] = uint32_t(Swz<D>::chunk(li, 2 * kc + g) * 2);
     const int G = lane >> 4, j = lane & 15;
-    const int fr = Swz<D>::f(g * 4 + (j >> 2));
-    const int x = (G & 1) * 2 + ((j & 3) >> 1);
-    const int lo = (g * 4 + (j >> 2)) * D + (((x ^ fr) & 3) << 3) + 4 * (j & 1);
-    const int s4 = fr & 4;
-    col[0] = (lo + (s4 << 3)) * 2;
-    col[1] = (lo - (s4 << 3)) * 2;
+    const int r = g * 4 + (j >> 2);
+    const int cin = (G & 1) * 2 + ((j & 3) >> 1), within = 4 * (j & 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      col[nb][0] = uint32_t((Swz<D>::chunk(r, nb * 4 + cin) + within) * 2);
+      col[nb][1] = uint32_t((Swz<D>::chunk(r + 8, nb * 4 + cin) + within) * 2);
+    }
   }
 };
 
@@ -179,16 +190,17 @@ __device__ __forceinline__ u32x2 lds_tr8(uint32_t addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// frag_rows of a tile at LDS byte address tb (r0 a multiple of 8).
+// frag_rows of a tile at LDS byte address tb (r0 a multiple of 16).
 template <int D>
 __device__ __forceinline__ u32x4 rows_at(uint32_t tb, const LaneOffsets<D>& lo, int r0, int kc) {
-  return lds_ld16(tb + lo.row[kc & 3] + uint32_t(r0 * D * 2 + (kc >> 2) * 128));
+  return lds_ld16(tb + lo.row[kc] + uint32_t(r0 * D * 2));
 }
 // frag_cols of a tile at LDS byte address tb (k0 a multiple of 16, c0 of 32).
 template <int D>
 __device__ __forceinline__ u32x4 cols_at(uint32_t tb, const LaneOffsets<D>& lo, int k0, int c0) {
-  const uint32_t a = tb + uint32_t(lo.col[(c0 >> 5) & 1] + k0 * D * 2 + (c0 / 8) * 16);
-  const u32x2 x = lds_tr8(a), y = lds_tr8(a + 8 * D * 2);
+  const int nb = c0 / 32;
+  const u32x2 x = lds_tr8(tb + lo.col[nb][0] + uint32_t(k0 * D * 2));
+  const u32x2 y = lds_tr8(tb + lo.col[nb][1] + uint32_t(k0 * D * 2));
   return u32x4{x[0], x[1], y[0], y[1]};
 }
 
