@@ -129,7 +129,10 @@ __device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks
                                           int n_keys, int qpos) {
   using C = FwdCfg<D>;
   const int g = lane >> 5, li = lane & 31;
-  // --- A
+  // --- A. The step runs at raised wave priority: of the two waves sharing a
+  // SIMD, the one inside its step issues first, the other one's update and
+  // barrier wait go underneath.
+  __builtin_amdgcn_s_setprio(1);
   u32x4 kf[C::KB][C::DS];
   if (NEXT) {
 #pragma unroll
@@ -196,6 +199,7 @@ __device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks
     if (i + 2 < C::NX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   return NEXT ? pair_max(mx) * c : -INFINITY;
 }
 
@@ -279,6 +283,19 @@ fwd_kernel(FwdParams P) {
         if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
       };
       int kt = 0;
+      // two unmasked steps per iteration, the score registers swapping roles
+      for (; kt + 2 < n_free; kt += 2) {
+        advance(kt);
+        float mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                   qf, sc, sn, o, m, l, P.c, lane,
+                                                   (kt + 1) * C::BN, n_keys, qpos);
+        update_max<D>(mx, m, l, o);
+        advance(kt + 1);
+        mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt + 1) + C::TILE, stage_ptr(kt + 2),
+                                             qf, sn, sc, o, m, l, P.c, lane,
+                                             (kt + 2) * C::BN, n_keys, qpos);
+        update_max<D>(mx, m, l, o);
+      }
       for (; kt + 1 < n_free; ++kt) {  // the next step needs no mask
         advance(kt);
         const float mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
