@@ -149,9 +149,9 @@ def main():
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
                              "block64_d128", "imbalance"])
-    ap.add_argument("--order", default="zigzag", choices=["zigzag", "inorder", "xcd"])
+    ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
-                    help="also time forward + backward under all three dealing orders, interleaved")
+                    help="also time forward + backward under every dealing order, interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--digest", action="store_true",
@@ -191,7 +191,7 @@ def main():
     v = J.to_torch_bf16(case.v).to(dev)
     do = J.to_torch_bf16(case.do).to(dev)
     ORDERS = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
-              "xcd": jfa.ORDER_XCD_ZIGZAG}
+              "xcd": jfa.ORDER_XCD_ZIGZAG, "folded": jfa.ORDER_FOLDED_ZIGZAG}
     order = ORDERS[args.order]
 
     runs = []

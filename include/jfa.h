@@ -67,6 +67,8 @@ typedef enum jfa_status {
 #define JFA_ORDER_XCD_ZIGZAG 2 /* the same deal inside each of the 8 XCDs, after whole
                                   (sequence, head) units are dealt zigzag by total
                                   work over the XCDs; num_slots % 8 == 0 */
+#define JFA_ORDER_FOLDED_ZIGZAG 3 /* ZIGZAG over items; with CAUSAL an item is the pair
+                                     of tiles a and n-1-a of one (sequence, head) */
 
 typedef struct jfa_problem {
   int32_t num_seqs;   /* B >= 0 */
@@ -114,6 +116,15 @@ jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host,
  *   owns slots [x*S/8, (x+1)*S/8) (the kernels run those slots on XCD x, so the
  *   tiles of one sequence share an L2), and its tiles are dealt with the ZIGZAG
  *   rule over those slots.
+ *   FOLDED_ZIGZAG (an MI355X refinement for causal problems): the tiles of one
+ *   (b, h), indices 0..n-1 in generation order, are folded into items {a, n-1-a}
+ *   for a < n/2, plus {n/2} when n is odd, each with the summed work; without
+ *   CAUSAL every tile is its own item. Items in generation order of their first
+ *   tile are dealt with the ZIGZAG rule, and an item's tiles go to one slot in
+ *   that order. Under CAUSAL the items of one (b, h) have nearly equal work, so
+ *   the sort keeps them adjacent and they run side by side on neighbouring
+ *   slots, sharing the sequence's K/V (or Q/dO) in L2, where the plain ZIGZAG
+ *   spreads its tiles, whose works differ, over the whole kernel.
  * Outputs (host memory, caller-allocated):
  *   slot_ptr [num_slots + 1]: tiles of slot s are tiles[slot_ptr[s] .. slot_ptr[s+1]).
  *   tiles    [capacity][4] int32 (b, h, t, work), grouped by slot in dealing order.

@@ -22,6 +22,11 @@ Readings of what the page leaves open:
   * The XCD variant (an MI355X refinement: eight dies with separate L2s) first
     deals whole (sequence, head) units, weighted by their total work, zigzag over
     the dies, then applies the same rule inside each die's slots.
+  * The folded variant (an MI355X refinement for causal problems) applies the
+    same rule to items instead of tiles: with causal masking, tiles a and n-1-a
+    of one (sequence, head) form one item whose work is their sum (the middle
+    tile of an odd count stands alone); an item's tiles go to one slot, in that
+    order. Without causal masking every tile is an item.
 Output: slot_ptr [S+1] and tiles [N,4] = (b, h, t, work), grouped by slot, in the
 order each slot received them.
 """
@@ -30,7 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 KIND_FWD, KIND_BWD = 0, 1
-ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG = 0, 1, 2
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 
 
 def ceil_div(a, b):
@@ -90,6 +95,32 @@ def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False
             mine.sort(key=lambda g: (-tiles[g][3], g))
             for j, g in enumerate(mine):
                 per_slot[x * per + _zigzag_rank(j, per)].append(tiles[g])
+        slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+        flat = []
+        for s in range(num_slots):
+            flat.extend(per_slot[s])
+            slot_ptr[s + 1] = len(flat)
+        return slot_ptr, np.asarray(flat, dtype=np.int32).reshape(-1, 4)
+    if order == ORDER_FOLDED_ZIGZAG:
+        items = []   # lists of tile indices, in generation order of their first tile
+        g = 0
+        while g < len(tiles):
+            e = g
+            while e < len(tiles) and tiles[e][:2] == tiles[g][:2]:
+                e += 1
+            n = e - g
+            if causal:
+                items += [[g + a, g + n - 1 - a] for a in range(n // 2)]
+                if n % 2:
+                    items.append([g + n // 2])
+            else:
+                items += [[g + a] for a in range(n)]
+            g = e
+        work = [sum(tiles[i][3] for i in it) for it in items]
+        ranked = sorted(range(len(items)), key=lambda k: (-work[k], k))
+        per_slot = [[] for _ in range(num_slots)]
+        for j, k in enumerate(ranked):
+            per_slot[_zigzag_rank(j, num_slots)].extend(tiles[i] for i in items[k])
         slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
         flat = []
         for s in range(num_slots):

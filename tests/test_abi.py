@@ -141,7 +141,8 @@ def test_tile_rows():
 
 @pytest.mark.parametrize("name", ["tiny", "gem", "gem_causal", "broadcast", "imbalance"])
 @pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
-@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG])
+@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
+                                   jfa.ORDER_FOLDED_ZIGZAG])
 def test_cpp_schedule_equals_reference(name, kind, order):
     w = J.standard_workloads()[name]
     L = J.lengths(w)
@@ -179,6 +180,23 @@ def test_cpp_schedule_golden():
             got = [[[t[0], t[1], t[2], t[3] // f] for t in tl[sp[s]:sp[s + 1]].tolist()]
                    for s in range(c["slots"])]
             assert got == c[key], (c["name"], key)
+
+
+def test_cpp_schedule_golden_folded():
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "schedule_examples.json")))
+    for c in cases["folded_cases"]:
+        kind = jfa.KIND_FWD if c["kind"] == "fwd" else jfa.KIND_BWD
+        rows = jfa.tile_rows(kind, 64, jfa.CAUSAL)
+        assert rows % c["tile_rows"] == 0
+        f = rows // c["tile_rows"]          # scale the hand example to the library's tiles
+        lengths = [x * f for x in c["lengths"]]
+        off = J.offsets_from_lengths(lengths)
+        p = jfa.problem(len(lengths), c["heads"], 64, max(lengths), int(off[-1]), 0.1, jfa.CAUSAL)
+        sp, tl = jfa.schedule(p, off, kind, jfa.ORDER_FOLDED_ZIGZAG, c["slots"])
+        got = [[[t[0], t[1], t[2], t[3] // f] for t in tl[sp[s]:sp[s + 1]].tolist()]
+               for s in range(c["slots"])]
+        assert got == c["schedule"], c["name"]
 
 
 def test_schedule_rejects_block_mode_and_small_capacity():

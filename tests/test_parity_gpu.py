@@ -124,7 +124,8 @@ def test_schedule_order_does_not_change_results(gpu):
     a = GpuRun(case, gpu, order=jfa.ORDER_ZIGZAG)
     oa, la = a.forward()
     dqa, dka, dva = (x.clone() for x in a.backward())
-    for order, slots in ((jfa.ORDER_INORDER, 7), (jfa.ORDER_XCD_ZIGZAG, None)):
+    for order, slots in ((jfa.ORDER_INORDER, 7), (jfa.ORDER_XCD_ZIGZAG, None),
+                         (jfa.ORDER_FOLDED_ZIGZAG, 5)):
         b = GpuRun(case, gpu, order=order, num_slots=slots)
         ob, lb = b.forward()
         assert torch.equal(oa, ob) and torch.equal(la, lb)

@@ -98,3 +98,46 @@ def test_xcd_properties(name):
         assert np.all(np.diff(t[sp[s]:sp[s + 1], 3]) <= 0)
     group_load = [int(t[sp[x * per]:sp[(x + 1) * per], 3].sum()) for x in range(X)]
     assert max(group_load) <= 1.1 * np.mean(group_load)
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["folded_cases"], ids=lambda c: c["name"])
+def test_golden_folded(case):
+    kind = R.KIND_FWD if case["kind"] == "fwd" else R.KIND_BWD
+    sp, t = R.schedule(case["lengths"], case["heads"], kind, case["tile_rows"],
+                       R.ORDER_FOLDED_ZIGZAG, case["slots"], causal=case["causal"])
+    assert _per_slot(sp, t) == case["schedule"]
+    assert R.slot_loads(sp, t) == case["loads"]
+
+
+@pytest.mark.parametrize("name", ["gem", "gem_causal", "broadcast"])
+@pytest.mark.parametrize("kind", [R.KIND_FWD, R.KIND_BWD])
+def test_folded_properties(name, kind):
+    w = J.standard_workloads()[name]
+    L = J.lengths(w)
+    S = 512
+    sp, t = R.schedule(L, w.num_heads, kind, 128, R.ORDER_FOLDED_ZIGZAG, S, w.causal, w.lq)
+    sp0, t0 = R.schedule(L, w.num_heads, kind, 128, R.ORDER_ZIGZAG, S, w.causal, w.lq)
+    key = lambda a: sorted(map(tuple, a.tolist()))
+    assert key(t) == key(t0)                       # every tile exactly once
+    if not w.causal:                              # nothing to fold: plain zigzag
+        assert np.array_equal(sp, sp0) and np.array_equal(t, t0)
+        return
+    # the two tiles of a folded pair sit next to each other in one slot, and
+    # their indices sum to n - 1 for the (sequence, head) they belong to
+    n_of = {}
+    for b, h, i, _ in t0.tolist():
+        n_of[(b, h)] = max(n_of.get((b, h), 0), i + 1)
+    for s in range(S):
+        lst = t[sp[s]:sp[s + 1]].tolist()
+        k = 0
+        while k < len(lst):
+            b, h, i, _ = lst[k]
+            n = n_of[(b, h)]
+            if 2 * i + 1 == n:                        # middle tile of an odd count
+                k += 1
+                continue
+            assert i < n - 1 - i and lst[k + 1][:3] == [b, h, n - 1 - i]
+            k += 2
+    loads = np.array(R.slot_loads(sp, t))
+    assert loads.max() <= loads.mean() + 2 * t[:, 3].max()
+    assert loads.max() / loads.mean() < 1.06

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libjfa.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 CAUSAL, BROADCAST_Q, BLOCK_DIAG64 = 1, 2, 4
 KIND_FWD, KIND_BWD = 0, 1
-ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG = 0, 1, 2
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
 
 
@@ -181,12 +181,14 @@ class Plan:
     """Everything one jagged problem needs on the device, built once.
 
     offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q.
-    Builds the FWD and BWD schedules on the host (zigzag by default), copies them
+    Builds the FWD and BWD schedules on the host (folded zigzag by default: the
+    work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired so
+    that they run side by side), copies them
     and the offsets to the device, and allocates the dQ workspace.
     """
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
-                 order=ORDER_ZIGZAG, num_slots=None, device="cuda"):
+                 order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda"):
         import torch
         off = _host_i32(offsets_host)
         L = np.diff(off.astype(np.int64))

@@ -149,7 +149,8 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
   if (p->flags & JFA_BLOCK_DIAG64)
     return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 runs without a schedule");
-  if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG)
+  if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG &&
+      order != JFA_ORDER_FOLDED_ZIGZAG)
     return fail(JFA_ERR_INVALID_ARG, "bad order");
   if (num_slots < 1) return fail(JFA_ERR_INVALID_ARG, "num_slots < 1");
   if (!slot_ptr) return fail(JFA_ERR_INVALID_ARG, "slot_ptr is NULL");
@@ -195,6 +196,54 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
         const int32_t r = int32_t(int64_t(j) % sx);
         idx.push_back(gt[j]);
         slot_of.push_back(x * sx + ((pass & 1) ? sx - 1 - r : r));
+      }
+    }
+  } else if (order == JFA_ORDER_FOLDED_ZIGZAG) {
+    // items: with CAUSAL, tiles a and n-1-a of one (sequence, head) form one item
+    // (the middle tile of an odd count stands alone); otherwise one tile each.
+    // Items in generation order of their first tile, stable-sorted by their
+    // summed work, descending, and dealt zigzag; an item's tiles go to one slot.
+    const bool fold = p->flags & JFA_CAUSAL;
+    std::vector<int32_t> item_first, item_tiles, item_work;  // CSR of tile indices
+    size_t u0 = 0;
+    while (u0 < tiles.size()) {
+      size_t u1 = u0 + 1;
+      while (u1 < tiles.size() && tiles[u1].b == tiles[u0].b && tiles[u1].h == tiles[u0].h) ++u1;
+      const int32_t n = int32_t(u1 - u0);
+      if (fold) {
+        for (int32_t a = 0; a < n / 2; ++a) {
+          item_first.push_back(int32_t(item_tiles.size()));
+          item_tiles.push_back(int32_t(u0) + a);
+          item_tiles.push_back(int32_t(u0) + n - 1 - a);
+          item_work.push_back(tiles[u0 + a].work + tiles[u0 + n - 1 - a].work);
+        }
+        if (n % 2) {
+          item_first.push_back(int32_t(item_tiles.size()));
+          item_tiles.push_back(int32_t(u0) + n / 2);
+          item_work.push_back(tiles[u0 + n / 2].work);
+        }
+      } else {
+        for (int32_t a = 0; a < n; ++a) {
+          item_first.push_back(int32_t(item_tiles.size()));
+          item_tiles.push_back(int32_t(u0) + a);
+          item_work.push_back(tiles[u0 + a].work);
+        }
+      }
+      u0 = u1;
+    }
+    const int32_t ni = int32_t(item_work.size());
+    item_first.push_back(int32_t(item_tiles.size()));
+    std::vector<int32_t> iorder(ni);
+    std::iota(iorder.begin(), iorder.end(), 0);
+    std::stable_sort(iorder.begin(), iorder.end(),
+                     [&](int32_t a, int32_t b) { return item_work[a] > item_work[b]; });
+    for (int32_t j = 0; j < ni; ++j) {
+      const int32_t pass = j / num_slots, r = j % num_slots;
+      const int32_t sl = (pass & 1) ? num_slots - 1 - r : r;
+      const int32_t it = iorder[j];
+      for (int32_t k = item_first[it]; k < item_first[it + 1]; ++k) {
+        idx.push_back(item_tiles[k]);
+        slot_of.push_back(sl);
       }
     }
   } else {
