@@ -36,15 +36,33 @@ struct BlkParams {
   float scale;
 };
 
-// Store a 32 x 32 accumulator block (rows of the output along the registers,
-// one output row per lane) as bf16, times `mul`.
-__device__ __forceinline__ void store_block(uint16_t* row, const f32x16& a, int col0, int g, float mul) {
+// Output of one wave: 32 rows x D, one row per lane pair, held as NB transposed
+// 32 x 32 accumulator blocks (lane li has row li; register r is column
+// nb*32 + (r/4)*8 + 4g + r%4). Written straight from the registers, every store
+// instruction would touch 16 bytes in each of 32 rows; instead the rows go
+// through a wave-private swizzled LDS tile (32 x D bf16) and leave as whole rows,
+// 16 lanes per row, 16 bytes per lane. `stage` is the wave's LDS tile, `row0`
+// the global address of the wave's first row, `rstride` elements between rows.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* stage, const f32x16 (&a)[D / 32], float mul,
+                                           uint16_t* row0, int64_t rstride, int lane) {
+  const int g = lane >> 5, li = lane & 31;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    u32x2 wv;
-    wv[0] = pack_bf16(a[q4 * 4 + 0] * mul, a[q4 * 4 + 1] * mul);
-    wv[1] = pack_bf16(a[q4 * 4 + 2] * mul, a[q4 * 4 + 3] * mul);
-    st8(row + col0 + q4 * 8 + g * 4, wv);
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 wv;
+      wv[0] = pack_bf16(a[nb][q4 * 4 + 0] * mul, a[nb][q4 * 4 + 1] * mul);
+      wv[1] = pack_bf16(a[nb][q4 * 4 + 2] * mul, a[nb][q4 * 4 + 3] * mul);
+      st8(stage + Swz<D>::chunk(li, nb * 4 + q4) + g * 4, wv);
+    }
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per store instruction
+  const int c = lane % CPR, r = lane / CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + r;
+    st16(row0 + int64_t(row) * rstride + c * 8, ld16(stage + Swz<D>::chunk(row, c)));
   }
 }
 
@@ -77,10 +95,13 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], float c) {
 template <int D>
 __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::TILE];  // K, V
+  // K, V, then the two waves' output staging tiles (32 x D each)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * C::TILE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
+  // head-major order: neighbouring workgroups take neighbouring blocks of a head
+  const int nblk = gridDim.x / P.H;
+  const int blk = blockIdx.x % nblk, h = blockIdx.x / nblk;
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
@@ -107,14 +128,15 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) pf[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(s[kb][r], s[kb][r + 1]);
-  uint16_t* orow = P.out + base + int64_t(w * 32 + li) * rstride;
+  f32x16 o[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    f32x16 o = f32x16{};
+    o[nb] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) o = mfma32(frag_cols<D>(lds + C::TILE, st * 16, nb * 32, lane), pf[st], o);
-    store_block(orow, o, nb * 32, g, 1.f);
+    for (int st = 0; st < 4; ++st) o[nb] = mfma32(frag_cols<D>(lds + C::TILE, st * 16, nb * 32, lane), pf[st], o[nb]);
   }
+  store_rows<D>(lds + 2 * C::TILE + w * (C::TILE / 2), o, 1.f, P.out + base + int64_t(w * 32) * rstride,
+                rstride, lane);
 }
 
 template <int D>
@@ -130,7 +152,8 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   uint16_t* dSt = Pt + kBS * kBS;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int blk = blockIdx.x / P.H, h = blockIdx.x % P.H;
+  const int nblk = gridDim.x / P.H;
+  const int blk = blockIdx.x % nblk, h = blockIdx.x / nblk;  // head-major order
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
@@ -190,37 +213,40 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
       st8(dSt + Swz<kBS>::chunk(i, j0 >> 3) + (j0 & 7), u32x2{d01, d23});
     }
   }
-  uint16_t* dqrow = P.dq + base + int64_t(i) * rstride;
+  f32x16 dqa[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    f32x16 acc = f32x16{};
+    dqa[nb] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) acc = mfma32(frag_cols<D>(Kt, st * 16, nb * 32, lane), pds[st], acc);
-    store_block(dqrow, acc, nb * 32, g, P.scale);
+    for (int st = 0; st < 4; ++st) dqa[nb] = mfma32(frag_cols<D>(Kt, st * 16, nb * 32, lane), pds[st], dqa[nb]);
   }
   __syncthreads();
+  // K and V are not read after this point: their tiles stage the outputs (each
+  // wave a private 32 x D half of K for dQ, and of V for dV, then dK)
+  store_rows<D>(Kt + w * (C::TILE / 2), dqa, P.scale, P.dq + base + int64_t(w * 32) * rstride, rstride,
+                lane);
 
   // ---- key side (lane = key): dV^T = dO^T P, dK^T = Q^T dS
-  const int j = w * 32 + li;
   u32x4 pb[4], db[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     pb[st] = frag_cols<kBS>(Pt, st * 16, w * 32, lane);
     db[st] = frag_cols<kBS>(dSt, st * 16, w * 32, lane);
   }
-  uint16_t* dvrow = P.dv + base + int64_t(j) * rstride;
-  uint16_t* dkrow = P.dk + base + int64_t(j) * rstride;
+  f32x16 av[C::NB], ak[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    f32x16 av = f32x16{}, ak = f32x16{};
+    av[nb] = f32x16{};
+    ak[nb] = f32x16{};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      av = mfma32(frag_cols<D>(dOt, st * 16, nb * 32, lane), pb[st], av);
-      ak = mfma32(frag_cols<D>(Qt, st * 16, nb * 32, lane), db[st], ak);
+      av[nb] = mfma32(frag_cols<D>(dOt, st * 16, nb * 32, lane), pb[st], av[nb]);
+      ak[nb] = mfma32(frag_cols<D>(Qt, st * 16, nb * 32, lane), db[st], ak[nb]);
     }
-    store_block(dvrow, av, nb * 32, g, 1.f);
-    store_block(dkrow, ak, nb * 32, g, P.scale);
   }
+  uint16_t* vst = Vt + w * (C::TILE / 2);
+  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, lane);
+  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, lane);
 }
 
 template <int D>
