@@ -36,36 +36,6 @@ struct BlkParams {
   float scale;
 };
 
-// Output of one wave: 32 rows x D, one row per lane pair, held as NB transposed
-// 32 x 32 accumulator blocks (lane li has row li; register r is column
-// nb*32 + (r/4)*8 + 4g + r%4). Written straight from the registers, every store
-// instruction would touch 16 bytes in each of 32 rows; instead the rows go
-// through a wave-private swizzled LDS tile (32 x D bf16) and leave as whole rows,
-// 16 lanes per row, 16 bytes per lane. `stage` is the wave's LDS tile, `row0`
-// the global address of the wave's first row, `rstride` elements between rows.
-template <int D>
-__device__ __forceinline__ void store_rows(uint16_t* stage, const f32x16 (&a)[D / 32], float mul,
-                                           uint16_t* row0, int64_t rstride, int lane) {
-  const int g = lane >> 5, li = lane & 31;
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 wv;
-      wv[0] = pack_bf16(a[nb][q4 * 4 + 0] * mul, a[nb][q4 * 4 + 1] * mul);
-      wv[1] = pack_bf16(a[nb][q4 * 4 + 2] * mul, a[nb][q4 * 4 + 3] * mul);
-      st8(stage + Swz<D>::chunk(li, nb * 4 + q4) + g * 4, wv);
-    }
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;     // rows per store instruction
-  const int c = lane % CPR, r = lane / CPR;
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = i * RPI + r;
-    st16(row0 + int64_t(row) * rstride + c * 8, ld16(stage + Swz<D>::chunk(row, c)));
-  }
-}
-
 // Exact softmax of one 64-key tile held as S^T (keys along the registers, one
 // query per lane pair): returns P packed to bf16 as MFMA operands (keys in the
 // order of an accumulator tile) and keeps P in `s`.
@@ -136,7 +106,7 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
     for (int st = 0; st < 4; ++st) o[nb] = mfma32(frag_cols<D>(lds + C::TILE, st * 16, nb * 32, lane), pf[st], o[nb]);
   }
   store_rows<D>(lds + 2 * C::TILE + w * (C::TILE / 2), o, 1.f, P.out + base + int64_t(w * 32) * rstride,
-                rstride, lane);
+                rstride, 32, lane);
 }
 
 template <int D>
@@ -224,7 +194,7 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   // K and V are not read after this point: their tiles stage the outputs (each
   // wave a private 32 x D half of K for dQ, and of V for dV, then dK)
   store_rows<D>(Kt + w * (C::TILE / 2), dqa, P.scale, P.dq + base + int64_t(w * 32) * rstride, rstride,
-                lane);
+                32, lane);
 
   // ---- key side (lane = key): dV^T = dO^T P, dK^T = Q^T dS
   u32x4 pb[4], db[4];
@@ -245,8 +215,8 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
     }
   }
   uint16_t* vst = Vt + w * (C::TILE / 2);
-  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, lane);
-  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, lane);
+  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, 32, lane);
+  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, 32, lane);
 }
 
 template <int D>

@@ -262,18 +262,10 @@ dq_kernel(DqParams P) {
     dq_stream<D, CAUSAL>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, n_keys, n_free,
                          qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
-    if (ok) {
-      uint16_t* dqrow = P.dq + eoff;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 wv;
-          wv[0] = pack_bf16(acc[nb][q4 * 4 + 0] * P.scale, acc[nb][q4 * 4 + 1] * P.scale);
-          wv[1] = pack_bf16(acc[nb][q4 * 4 + 2] * P.scale, acc[nb][q4 * 4 + 3] * P.scale);
-          st8(dqrow + nb * 32 + q4 * 8 + g * 4, wv);
-        }
-    }
+    // dq_stream ended with a barrier: the ring is free to stage the output rows
+    const int row0 = q_first + w * 32;
+    store_rows<D>(lds + w * 32 * D, acc, P.scale,
+                  P.dq + (int64_t(kv0) + row0) * rstride + int64_t(h) * D, rstride, L - row0, lane);
   }
 }
 
@@ -595,23 +587,15 @@ dkdv_kernel(KvParams P) {
       const uint32_t ql = qs_of(n_steps - 1);
       kv_accumulate<D>(ql, ql + C::TILE * 2, lo, pp, pd, dv, dk);
     }
-    __syncthreads();  // the next tile's first loads overwrite the first stages
-    if (key_ok) {
-      uint16_t* dkrow = P.dk + (int64_t(kv0) + jw) * rstride + int64_t(h) * D;
-      uint16_t* dvrow = P.dv + (int64_t(kv0) + jw) * rstride + int64_t(h) * D;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 a, bb;
-          a[0] = pack_bf16(dk[nb][q4 * 4 + 0] * P.scale, dk[nb][q4 * 4 + 1] * P.scale);
-          a[1] = pack_bf16(dk[nb][q4 * 4 + 2] * P.scale, dk[nb][q4 * 4 + 3] * P.scale);
-          bb[0] = pack_bf16(dv[nb][q4 * 4 + 0], dv[nb][q4 * 4 + 1]);
-          bb[1] = pack_bf16(dv[nb][q4 * 4 + 2], dv[nb][q4 * 4 + 3]);
-          st8(dkrow + nb * 32 + q4 * 8 + g * 4, a);
-          st8(dvrow + nb * 32 + q4 * 8 + g * 4, bb);
-        }
+    __syncthreads();  // every wave is done with the ring: it stages the output rows
+    {
+      const int row0 = key0 + w * 32;
+      const int64_t e0 = (int64_t(kv0) + row0) * rstride + int64_t(h) * D;
+      uint16_t* stage = lds + w * 32 * D;
+      store_rows<D>(stage, dv, 1.f, P.dv + e0, rstride, L - row0, lane);
+      store_rows<D>(stage, dk, P.scale, P.dk + e0, rstride, L - row0, lane);
     }
+    __syncthreads();  // the next tile's first loads overwrite the first stages
   }
 }
 

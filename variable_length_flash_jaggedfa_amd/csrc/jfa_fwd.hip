@@ -318,29 +318,26 @@ fwd_kernel(FwdParams P) {
                                         lane, 0, n_keys, qpos);
     }
 
-    // epilogue: out = O / l (bf16), lse = (m + log2 l) * ln 2
+    // epilogue: out = O / l (bf16) through the wave's LDS staging tile, lse =
+    // (m + log2 l) * ln 2. The barrier makes the ring free for the staging.
     const float lt = pair_sum(l);
-    if (qpos < rows_total) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* orow = BCAST ? P.out + ((int64_t(b) * P.lq + qpos) * P.H + h) * D
-                             : P.out + (int64_t(kv0) + qpos) * rstride + int64_t(h) * D;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    __syncthreads();
+    {
+      const int row0 = q_first + w * 32;
+      uint16_t* orow0 = BCAST ? P.out + ((int64_t(b) * P.lq + row0) * P.H + h) * D
+                              : P.out + (int64_t(kv0) + row0) * rstride + int64_t(h) * D;
+      // 1/l belongs to the lane's row: fold it in before staging
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 wv;
-          wv[0] = pack_bf16(o[nb][q4 * 4 + 0] * inv, o[nb][q4 * 4 + 1] * inv);
-          wv[1] = pack_bf16(o[nb][q4 * 4 + 2] * inv, o[nb][q4 * 4 + 3] * inv);
-          st8(orow + nb * 32 + q4 * 8 + g * 4, wv);
-        }
-      }
-      if (g == 0) {
-        const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-        if (BCAST)
-          P.lse[(int64_t(b) * P.H + h) * P.lq + qpos] = lse;
-        else
-          P.lse[int64_t(h) * P.total_kv + kv0 + qpos] = lse;
-      }
+      for (int nb = 0; nb < C::NB; ++nb) o[nb] *= inv;
+      store_rows<D>(lds + w * 32 * D, o, 1.f, orow0, rstride, rows_total - row0, lane);
+    }
+    if (qpos < rows_total && g == 0) {
+      const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+      if (BCAST)
+        P.lse[(int64_t(b) * P.H + h) * P.lq + qpos] = lse;
+      else
+        P.lse[int64_t(h) * P.total_kv + kv0 + qpos] = lse;
     }
     __syncthreads();  // the next tile's first loads overwrite the first stages
   }

@@ -204,4 +204,41 @@ __device__ __forceinline__ u32x4 cols_at(uint32_t tb, const LaneOffsets<D>& lo, 
   return u32x4{x[0], x[1], y[0], y[1]};
 }
 
+// ---- output rows through LDS
+//
+// The output of one wave is 32 rows x D, one row per lane pair, held as D/32
+// transposed 32 x 32 accumulator blocks (lane li has row li; register r is column
+// nb*32 + (r/4)*8 + 4g + r%4). Stored straight from the registers, every store
+// instruction would touch 16 bytes in each of 32 rows; instead the rows go
+// through a wave-private swizzled LDS tile (32 x D bf16) and leave as whole rows,
+// 16 bytes per lane. `stage` is the wave's LDS tile (nothing else may use it
+// meanwhile), `row0` the global address of the wave's first row, `rstride`
+// elements between rows; rows >= nrows are not written.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* stage, const f32x16 (&a)[D / 32], float mul,
+                                           uint16_t* row0, int64_t rstride, int nrows, int lane) {
+  // derive the addresses here, not before the caller's main loop (where the
+  // compiler would otherwise hoist them and keep them live across it)
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5, li = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 wv;
+      wv[0] = pack_bf16(a[nb][q4 * 4 + 0] * mul, a[nb][q4 * 4 + 1] * mul);
+      wv[1] = pack_bf16(a[nb][q4 * 4 + 2] * mul, a[nb][q4 * 4 + 3] * mul);
+      st8(stage + Swz<D>::chunk(li, nb * 4 + q4) + g * 4, wv);
+    }
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR, r = lane / CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + r;
+    const u32x4 v = ld16(stage + Swz<D>::chunk(row, c));
+    if (row < nrows) st16(row0 + int64_t(row) * rstride + c * 8, v);
+  }
+}
+
 }  // namespace jfa_dev
