@@ -1,7 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (default slot count, zigzag schedule). The oracle recomputes a
-sample of (sequence, head) slices one by one; broadcast-Q dQ is checked for whole
-heads (every sequence contributes to it)."""
+benchmark times (default slot count, folded zigzag schedule). The oracle
+recomputes a sample of (sequence, head) slices one by one; broadcast-Q dQ is
+checked for whole heads (every sequence contributes to it). On the imbalance
+workload every short sequence is compared in full, and identities that hold at
+any size are checked over the whole output on the GPU."""
 import numpy as np
 import pytest
 
@@ -122,3 +124,73 @@ def test_block64_d128(gpu):
 
 def test_imbalance(gpu):
     run_sampled("imbalance", gpu, n_random=6, long_heads=[3])
+
+
+def test_imbalance_all_short_and_invariants(gpu):
+    """Every short sequence x head against the oracle; six seeded long (sequence,
+    head) pairs including the longest sequence; and over every (sequence, head):
+    sum_j dK_j = 0, sum_j dV_j = sum_i dO_i (rows of P sum to one) and each out
+    row inside the per-column range of its V rows (a convex combination)."""
+    import torch
+    w = J.standard_workloads()["imbalance"]
+    log("workload imbalance: generating inputs")
+    case = J.make_case(w)
+    run = GpuRun(case, gpu)
+    out, lse = run.forward()
+    dq, dk, dv = run.backward()
+    off = case.offsets.astype(np.int64)
+    L = case.lengths
+    H = w.num_heads
+    # --- full-tensor identities, per (sequence, head), on the GPU in float32
+    T = int(off[-1])
+    seg = torch.repeat_interleave(torch.arange(len(L), device=gpu),
+                                  torch.as_tensor(L, device=gpu))
+    def seg_sum(x):
+        return torch.zeros((len(L), H, w.head_dim), dtype=torch.float32,
+                           device=gpu).index_add_(0, seg, x.float())
+    sdk, sdv, sdo = seg_sum(dk), seg_sum(dv), seg_sum(run.do)
+    sabs_dk = seg_sum(dk.abs())
+    e_dk = float(((sdk.abs()) / (sabs_dk + 1e-30)).max())
+    e_dv = float(((sdv - sdo).abs().max() / sdo.abs().max()))
+    log(f"  sum dK / sum |dK| max {e_dk:.3e}; |sum dV - sum dO| / max|sum dO| {e_dv:.3e}")
+    assert e_dk <= 2e-2
+    assert e_dv <= 2e-2
+    idx = seg.view(T, 1, 1).expand(T, H, w.head_dim)
+    vmin = torch.full((len(L), H, w.head_dim), float("inf"), device=gpu).scatter_reduce(
+        0, idx, run.v.float(), "amin")
+    vmax = torch.full((len(L), H, w.head_dim), float("-inf"), device=gpu).scatter_reduce(
+        0, idx, run.v.float(), "amax")
+    # bf16 P and bf16 out put a row up to a few bf16 ulps of |v| outside the range
+    o = out.float()
+    tol = 3e-2
+    lo_ok = (o >= vmin[seg] - tol).all()
+    hi_ok = (o <= vmax[seg] + tol).all()
+    assert bool(lo_ok) and bool(hi_ok)
+    # --- every short sequence, every head
+    short = [b for b in range(len(L)) if L[b] <= 64]
+    rng = np.random.default_rng(7)
+    long_ = [b for b in range(len(L)) if L[b] > 64]
+    longest = int(np.argmax(L))
+    pairs = [(longest, 0)] + [(int(b), int(rng.integers(H)))
+                              for b in rng.choice([b for b in long_ if b != longest], 5, replace=False)]
+    out_h, dq_h, dk_h, dv_h = (bf16_to_f64(x) for x in (out, dq, dk, dv))
+    lse_h = lse.cpu().numpy()
+    worst = {"out": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
+    ref = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    todo = [(b, h) for b in short for h in range(H)] + pairs
+    log(f"  comparing {len(todo)} (sequence, head) slices ({len(short)} short sequences, "
+        f"long pairs {pairs})")
+    for b, h in todo:
+        s, e = int(off[b]), int(off[b + 1])
+        q_, k_, v_, do_ = (J.bf16_bits_to_f64(x[s:e, h]) for x in (case.q, case.k, case.v, case.do))
+        o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale)
+        gq, gk, gv = A.seq_backward(q_, k_, v_, do_, case.scale)
+        worst["out"] = max(worst["out"], max_abs(out_h[s:e, h], o_ref))
+        worst["lse"] = max(worst["lse"], max_abs(lse_h[h, s:e], l_ref))
+        for k, got, r in (("dq", dq_h[s:e, h], gq), ("dk", dk_h[s:e, h], gk), ("dv", dv_h[s:e, h], gv)):
+            worst[k] = max(worst[k], max_abs(got, r))
+            ref[k] = max(ref[k], float(np.abs(r).max()))
+    log("  " + " ".join(f"{k} {v:.3e}" for k, v in worst.items()))
+    assert worst["out"] <= OUT_TOL and worst["lse"] <= LSE_TOL
+    for k in ("dq", "dk", "dv"):
+        assert worst[k] <= GRAD_TOL * ref[k], k

@@ -14,7 +14,7 @@ from tests.gpu_common import (GpuRun, assert_grad, assert_lse, assert_out, bf16_
 pytestmark = pytest.mark.gpu
 
 
-def check_case(w, dev, order=jfa.ORDER_ZIGZAG, num_slots=None, bwd=True):
+def check_case(w, dev, order=jfa.ORDER_FOLDED_ZIGZAG, num_slots=None, bwd=True):
     log(f"case {w.name} kind={w.kind} causal={w.causal} H={w.num_heads} D={w.head_dim} "
         f"lq={w.lq} seed={w.seed} lengths={J.lengths(w)[:12].tolist()}")
     case = J.make_case(w)
@@ -125,7 +125,7 @@ def test_schedule_order_does_not_change_results(gpu):
     oa, la = a.forward()
     dqa, dka, dva = (x.clone() for x in a.backward())
     for order, slots in ((jfa.ORDER_INORDER, 7), (jfa.ORDER_XCD_ZIGZAG, None),
-                         (jfa.ORDER_FOLDED_ZIGZAG, 5)):
+                         (jfa.ORDER_FOLDED_ZIGZAG, 5), (jfa.ORDER_FOLDED_ZIGZAG, None)):
         b = GpuRun(case, gpu, order=order, num_slots=slots)
         ob, lb = b.forward()
         assert torch.equal(oa, ob) and torch.equal(la, lb)
