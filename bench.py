@@ -62,6 +62,22 @@ def flags_of(w, jfa):
     return f
 
 
+def padded_ratio(case, w):
+    """Attended pairs with every sequence padded to the longest, over the unpadded
+    count (the waste the jagged layout avoids)."""
+    L = np.asarray(case.lengths, dtype=np.int64)
+    if len(L) == 0 or L.sum() == 0:
+        return 1.0
+    m = int(L.max())
+    if w.kind == "block64":
+        return float(len(L) * m * 64) / float(64 * L.sum())
+    if w.kind == "broadcast":
+        return float(len(L) * m * w.lq) / float(w.lq * L.sum())
+    if w.causal:
+        return float(len(L) * m * (m + 1) // 2) / float((L * (L + 1) // 2).sum())
+    return float(len(L) * m * m) / float((L * L).sum())
+
+
 def cpu_baseline(case, variants, budget_s=15.0):
     """The fp64 oracle on a bounded sample of (sequence, head) units."""
     import threadpoolctl
@@ -301,6 +317,10 @@ def main():
                             "fwd_tflops": round(r["fwd_flops"] / fm / 1e9, 1),
                             "bwd_tflops": round(r["bwd_flops"] / bm / 1e9, 1),
                             "fwd_bwd_tflops": round((r["fwd_flops"] + r["bwd_flops"]) / (fm + bm) / 1e9, 1)}
+        per_variant[tag]["fwd_ms_min_max"] = [round(float(np.min(r["fwd_ms"])), 4),
+                                              round(float(np.max(r["fwd_ms"])), 4)]
+        per_variant[tag]["bwd_ms_min_max"] = [round(float(np.min(r["bwd_ms"])), 4),
+                                              round(float(np.max(r["bwd_ms"])), 4)]
         if not r["block"]:
             per_variant[tag]["dq_ms"] = round(float(np.median(r["dq_ms"])), 4)
             per_variant[tag]["dkdv_ms"] = round(float(np.median(r["dkdv_ms"])), 4)
@@ -329,6 +349,9 @@ def main():
                 samples[name]["total"].append(tf + tb)
         compare = {name: {k_: round(float(np.median(v_)), 4) for k_, v_ in d.items()}
                    for name, d in samples.items()}
+        for name, d in samples.items():
+            compare[name]["total_iqr"] = [round(float(np.percentile(d["total"], 25)), 4),
+                                          round(float(np.percentile(d["total"], 75)), 4)]
         for name, plans in alt.items():
             # predicted balance: busiest slot's KV work over the mean, per schedule kind
             for kind, tag in ((jfa.KIND_FWD, "fwd"), (jfa.KIND_BWD, "bwd")):
@@ -341,6 +364,9 @@ def main():
         base = compare["inorder"]["total"]
         for name in compare:
             compare[name]["speedup_vs_inorder"] = round(base / compare[name]["total"], 4)
+            # faster than in-order with inter-quartile ranges that do not overlap
+            compare[name]["beats_inorder_iqr"] = bool(
+                compare[name]["total_iqr"][1] < compare["inorder"]["total_iqr"][0])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -360,6 +386,8 @@ def main():
                    "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
                    "event_ms_per_step": round(float(ev_ms), 4),
                    "schedule_build_ms": round(sched_ms, 3),
+                   # attention FLOPs if every sequence were padded to the longest
+                   "padding_flops_ratio": round(padded_ratio(case, w0), 2),
                    "input_gen_s": round(t_gen, 2),
                    "per_variant": per_variant},
         "roofline": roofline,
