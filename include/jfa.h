@@ -134,9 +134,11 @@ jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32
                         int32_t order, int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
                         int64_t capacity);
 
-/* Bytes of device workspace jfa_bwd needs: Di (float32, laid out like lse) and,
- * for BROADCAST_Q, float32 dQ partials of [G][Lq][H][D] where the B sequences are
- * split into G = min(B, 64) contiguous groups; 0 for BLOCK_DIAG64. */
+/* Bytes of device workspace jfa_bwd needs: two float32 row vectors laid out like
+ * lse, each rounded up to 256 bytes (-Di and -lse/scale, written by the dQ pass
+ * and read by the dK/dV pass) and, for BROADCAST_Q, float32 dQ partials of
+ * [G][Lq][H][D] where the B sequences are split into G = min(B, 64) contiguous
+ * groups; 0 for BLOCK_DIAG64. */
 size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
 
 /* Forward ("TLX Block Attention", section 2: the online-softmax loop; section 3,

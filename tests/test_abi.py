@@ -124,11 +124,11 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
 
 def test_workspace_bytes():
     r256 = lambda n: (n + 255) // 256 * 256
-    # jagged: Di [H, T]
-    assert jfa.bwd_workspace_bytes(_p()) == r256(2 * 15 * 4)
-    # broadcast: Di [B, H, Lq] + min(B, 64) partials of [Lq, H, D]
+    # jagged: -Di and -lse/scale, each [H, T]
+    assert jfa.bwd_workspace_bytes(_p()) == 2 * r256(2 * 15 * 4)
+    # broadcast: two [B, H, Lq] vectors + min(B, 64) partials of [Lq, H, D]
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == \
-        r256(2 * 2 * 7 * 4) + 2 * 7 * 2 * 64 * 4
+        2 * r256(2 * 2 * 7 * 4) + 2 * 7 * 2 * 64 * 4
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)) == 0
 
 

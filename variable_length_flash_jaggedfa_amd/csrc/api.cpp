@@ -154,8 +154,9 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   }
   if (q_rows(p) == 0 && p->total_kv == 0) return JFA_OK;
   a.di = static_cast<float*>(workspace);
+  a.nls = reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p));
   a.groups = bcast_groups(p->num_seqs);
-  a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p)) : nullptr;
+  a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * di_bytes(p)) : nullptr;
   return launch_bwd(a);
 }
 

@@ -55,7 +55,8 @@ struct DqCfg {
 struct DqParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* o; const uint16_t* dout;
   const float* lse;
-  float* di;                  // Di out, same layout as lse
+  float* di;                  // -Di out, same layout as lse
+  float* nls;                 // -lse / scale out, same layout as lse
   const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
   uint16_t* dq;               // jagged: bf16 dQ
   float* dq_part;             // broadcast: [groups][Lq][H][D] float32 partials
@@ -254,8 +255,12 @@ dq_kernel(DqParams P) {
     u32x4 qf[C::DS], dof[C::DS];
     const float di = load_row<D>(P.q + eoff, P.o + eoff, P.dout + eoff, ok, g, qf, dof);
     const int64_t vidx = int64_t(h) * P.total_kv + row;
-    const float lse2 = ok ? P.lse[vidx] * kLog2e : 0.f;
-    if (ok && g == 0) P.di[vidx] = di;
+    const float lse = ok ? P.lse[vidx] : 0.f;
+    const float lse2 = lse * kLog2e;
+    if (ok && g == 0) {
+      P.di[vidx] = -di;
+      P.nls[vidx] = -lse / P.scale;
+    }
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
@@ -296,8 +301,12 @@ dq_bcast_kernel(DqParams P) {
     u32x4 qf[C::DS], dof[C::DS];
     const float di = load_row<D>(qrow, P.o + oeff, P.dout + oeff, ok, g, qf, dof);
     const int64_t vidx = (int64_t(b) * P.H + h) * P.lq + qpos;
-    const float lse2 = ok ? P.lse[vidx] * kLog2e : 0.f;
-    if (ok && g == 0) P.di[vidx] = di;
+    const float lse = ok ? P.lse[vidx] : 0.f;
+    const float lse2 = lse * kLog2e;
+    if (ok && g == 0) {
+      P.di[vidx] = -di;
+      P.nls[vidx] = -lse / P.scale;
+    }
     if (L > 0)
       dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
                           P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, L / C::BN,
@@ -348,26 +357,38 @@ struct KvCfg {
 
 struct KvParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* dout;
-  const float* lse; const float* di;
+  const float* nls; const float* di;  // -lse / scale and -Di from the dQ pass
   const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
   uint16_t* dk; uint16_t* dv;
   int32_t H, lq, total_kv;
   float c, scale;
 };
 
-// S = Q K^T and dP = dO V^T for one step of BM query rows (lane = key); all row
-// fragments of one k-step are read before its MFMAs.
+// S' = Q K^T - lse/scale and dP' = dO V^T - Di for one step of BM query rows
+// (lane = key): the accumulators start from the per-row constants the dQ pass
+// left in the stage's vectors, so that P = 2^(c S') and dS = P dP' need no
+// further per-element terms. All row fragments of one k-step are read before its
+// MFMAs.
 template <int D>
 __device__ __forceinline__ void kv_scores(uint32_t qs, uint32_t dos, const LaneOffsets<D>& lo,
                                           const u32x4 (&kf)[KvCfg<D>::DS],
-                                          const u32x4 (&vf)[KvCfg<D>::DS],
-                                          f32x16 (&s)[KvCfg<D>::IB], f32x16 (&dp)[KvCfg<D>::IB]) {
+                                          const u32x4 (&vf)[KvCfg<D>::DS], const float* nls_s,
+                                          const float* ndi_s, int g, f32x16 (&s)[KvCfg<D>::IB],
+                                          f32x16 (&dp)[KvCfg<D>::IB]) {
   using C = KvCfg<D>;
 #pragma unroll
-  for (int ib = 0; ib < C::IB; ++ib) {
-    s[ib] = f32x16{};
-    dp[ib] = f32x16{};
-  }
+  for (int ib = 0; ib < C::IB; ++ib)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // register q4*4 + e holds row ib*32 + q4*8 + 4g + e
+      const f32x4 a = *reinterpret_cast<const f32x4*>(nls_s + ib * 32 + q4 * 8 + g * 4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(ndi_s + ib * 32 + q4 * 8 + g * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[ib][q4 * 4 + e] = a[e];
+        dp[ib][q4 * 4 + e] = b[e];
+      }
+    }
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
     u32x4 qa[C::IB], da[C::IB];
@@ -402,19 +423,18 @@ __device__ __forceinline__ void kv_accumulate(uint32_t qs, uint32_t dos, const L
   }
 }
 
-// P = 2^(S c - lse log2 e) and dS = P (dP - Di) for one step, packed to bf16
-// (keys past the diagonal masked with CAUSAL). The work is cut into IB*4 groups
-// of four query rows. With PREV, each group is issued together with a share of
-// the previous step's dV/dK products, between scheduling fences, so that the
-// VALU work runs while those MFMAs execute; their column fragments and the
-// group's lse/Di values are read one group ahead.
+// P = 2^(c S') and dS = P dP' for one step (S' and dP' already carry -lse/scale
+// and -Di), packed to bf16 (keys past the diagonal masked with CAUSAL). The work
+// is cut into IB*4 groups of four query rows. With PREV, each group is issued
+// together with a share of the previous step's dV/dK products, between
+// scheduling fences, so that the VALU work runs while those MFMAs execute; their
+// column fragments are read one group ahead.
 template <int D, bool MASK, bool PREV>
 __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
-                                           const f32x16 (&dp)[KvCfg<D>::IB], const float* lse_s,
-                                           const float* di_s, float c, int g, int q0, int jw,
-                                           u32x4 (&pp)[2 * KvCfg<D>::IB], u32x4 (&pd)[2 * KvCfg<D>::IB],
-                                           uint32_t qs_prev, uint32_t dos_prev,
-                                           const LaneOffsets<D>& lo,
+                                           const f32x16 (&dp)[KvCfg<D>::IB], float c, int g, int q0,
+                                           int jw, u32x4 (&pp)[2 * KvCfg<D>::IB],
+                                           u32x4 (&pd)[2 * KvCfg<D>::IB], uint32_t qs_prev,
+                                           uint32_t dos_prev, const LaneOffsets<D>& lo,
                                            const u32x4 (&pp_prev)[2 * KvCfg<D>::IB],
                                            const u32x4 (&pd_prev)[2 * KvCfg<D>::IB],
                                            f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
@@ -423,7 +443,6 @@ __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
   constexpr int XPG = C::NX / NG;    // dV/dK product pairs per group
   static_assert(XPG * NG == C::NX, "products must split evenly over the groups");
   u32x4 fa[2][XPG], fb[2][XPG];
-  f32x4 lse4[2], di4[2];
   auto read_cols = [&](int grp, int buf) {
 #pragma unroll
     for (int xx = 0; xx < XPG; ++xx) {
@@ -432,20 +451,11 @@ __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
       fb[buf][xx] = cols_at<D>(qs_prev, lo, st * 16, nb * 32);
     }
   };
-  auto read_vec = [&](int grp, int buf) {
-    const int i0 = (grp / 4) * 32 + (grp % 4) * 8 + g * 4;
-    lse4[buf] = *reinterpret_cast<const f32x4*>(lse_s + i0);
-    di4[buf] = *reinterpret_cast<const f32x4*>(di_s + i0);
-  };
   if (PREV) read_cols(0, 0);
-  read_vec(0, 0);
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
     const int cur = grp & 1;
-    if (grp + 1 < NG) {
-      if (PREV) read_cols(grp + 1, cur ^ 1);
-      read_vec(grp + 1, cur ^ 1);
-    }
+    if (PREV && grp + 1 < NG) read_cols(grp + 1, cur ^ 1);
     if (PREV) {
 #pragma unroll
       for (int xx = 0; xx < XPG; ++xx) {
@@ -460,10 +470,10 @@ __device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = q4 * 4 + e;
-      float p = exp2_fast(__builtin_fmaf(s[ib][r], c, -lse4[cur][e] * kLog2e));
+      float p = exp2_fast(s[ib][r] * c);
       if (MASK) p = jw > q0 + i0 + e ? 0.f : p;
       pv[e] = p;
-      dsv[e] = p * (dp[ib][r] - di4[cur][e]);
+      dsv[e] = p * dp[ib][r];
     }
     const int st = ib * 2 + q4 / 2, hw = (q4 % 2) * 2;
     pp[st][hw] = pack_bf16(pv[0], pv[1]);
@@ -480,7 +490,7 @@ dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
   static_assert(C::NS == 4, "the waits below assume a four-stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // lse, Di per stage
+  __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // -lse/scale, -Di per stage
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -520,7 +530,7 @@ dkdv_kernel(KvParams P) {
                                  rows_rsrc<D>(dobase + int64_t(q_first) * rstride, rstride, left),
                                  rowbytes, w, lane);
       if (w < 2) {
-        const float* src = (w == 0 ? P.lse : P.di) + voff + q_first;
+        const float* src = (w == 0 ? P.nls : P.di) + voff + q_first;
         vec64_load(vecs[buf][w], vec_rsrc(src, left), lane);
       }
     };
@@ -557,14 +567,12 @@ dkdv_kernel(KvParams P) {
       // step 0
       arrive(0);
       if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
-      kv_scores<D>(qs_of(0), qs_of(0) + C::TILE * 2, lo, kf, vf, s, dp);
+      kv_scores<D>(qs_of(0), qs_of(0) + C::TILE * 2, lo, kf, vf, vecs[0][0], vecs[0][1], g, s, dp);
       const int q00 = qs_lo * C::BM;
       if (n_mask > 0)
-        kv_softmax<D, true, false>(s, dp, vecs[0][0], vecs[0][1], P.c, g, q00, jw, pp, pd, 0, 0, lo,
-                                   ppv, pdv, dv, dk);
+        kv_softmax<D, true, false>(s, dp, P.c, g, q00, jw, pp, pd, 0, 0, lo, ppv, pdv, dv, dk);
       else
-        kv_softmax<D, false, false>(s, dp, vecs[0][0], vecs[0][1], P.c, g, q00, jw, pp, pd, 0, 0,
-                                    lo, ppv, pdv, dv, dk);
+        kv_softmax<D, false, false>(s, dp, P.c, g, q00, jw, pp, pd, 0, 0, lo, ppv, pdv, dv, dk);
       // step it: its scores, then its softmax under the previous step's products
       auto step = [&](int it, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -576,10 +584,10 @@ dkdv_kernel(KvParams P) {
         arrive(it);  // also: every wave is done with stage it-2
         if (it + C::NS - 2 < n_steps) load_stage(it + C::NS - 2);
         const uint32_t qs = qs_of(it), qp = qs_of(it - 1);
-        kv_scores<D>(qs, qs + C::TILE * 2, lo, kf, vf, s, dp);
         const int buf = it % C::NS;
-        kv_softmax<D, MASK, true>(s, dp, vecs[buf][0], vecs[buf][1], P.c, g, (qs_lo + it) * C::BM, jw,
-                                  pp, pd, qp, qp + C::TILE * 2, lo, ppv, pdv, dv, dk);
+        kv_scores<D>(qs, qs + C::TILE * 2, lo, kf, vf, vecs[buf][0], vecs[buf][1], g, s, dp);
+        kv_softmax<D, MASK, true>(s, dp, P.c, g, (qs_lo + it) * C::BM, jw, pp, pd, qp,
+                                  qp + C::TILE * 2, lo, ppv, pdv, dv, dk);
       };
       int it = 1;
       for (; it < n_mask; ++it) step(it, std::true_type{});
@@ -616,6 +624,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   dp.dout = static_cast<const uint16_t*>(a.dout);
   dp.lse = a.lse;
   dp.di = a.di;
+  dp.nls = a.nls;
   dp.offsets = a.offsets;
   dp.slot_ptr = a.q_slot_ptr;
   dp.tiles = a.q_tiles;
@@ -646,7 +655,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     kp.k = dp.k;
     kp.v = dp.v;
     kp.dout = dp.dout;
-    kp.lse = a.lse;
+    kp.nls = a.nls;
     kp.di = a.di;
     kp.offsets = a.offsets;
     kp.slot_ptr = a.kv_slot_ptr;

@@ -44,7 +44,8 @@ struct BwdLaunch {
   const int32_t* q_slot_ptr; const int32_t* q_tiles; int32_t q_num_slots;    // forward tiles
   const int32_t* kv_slot_ptr; const int32_t* kv_tiles; int32_t kv_num_slots; // backward tiles
   void* dq; void* dk; void* dv;
-  float* di;        // workspace: Di, laid out like lse
+  float* di;        // workspace: -Di, laid out like lse
+  float* nls;       // workspace: -lse / scale, laid out like lse
   float* dq_part;   // workspace: broadcast-Q dQ partials [groups][Lq][H][D]
   int32_t groups;   // broadcast-Q sequence groups
   int32_t num_seqs, num_heads, head_dim, lq;

@@ -287,7 +287,7 @@ size_t di_bytes(const jfa_problem* p) {
 extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
   if (!p || check_problem(p) != JFA_OK) return 0;
   if (p->flags & JFA_BLOCK_DIAG64) return 0;
-  size_t bytes = di_bytes(p);
+  size_t bytes = 2 * di_bytes(p);  // -Di and -lse/scale, each laid out like lse
   if (p->flags & JFA_BROADCAST_Q)
     bytes += size_t(bcast_groups(p->num_seqs)) * p->lq * p->num_heads * p->head_dim * sizeof(float);
   return bytes;
