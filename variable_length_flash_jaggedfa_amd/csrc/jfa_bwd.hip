@@ -10,10 +10,11 @@
 //     its sequence through a 3-stage LDS ring: S^T = K Q^T and dP^T = V dO^T,
 //     P = 2^(S*scale*log2e - lse*log2e), dS = P * (dP - Di), dQ^T += K^T dS^T.
 //     dQ stays in registers and is written once; Di is written for the other pass.
-//   dK/dV pass (key-tile outer, backward schedule). Each wave keeps 32 keys of K
-//     and V in registers with its dK^T and dV^T accumulators and streams the
-//     query rows (Q, dO, lse, Di) through a 3-stage LDS ring: S = Q K^T and
-//     dP = dO V^T, P and dS as above, dV^T += dO^T P and dK^T += Q^T dS.
+//   dK/dV pass (key-tile outer, backward schedule). Each 32-key block of a tile
+//     belongs to a pair of waves that stream the query rows (Q, dO, -lse/scale,
+//     -Di) through a 3-stage LDS ring: one wave keeps K and dV^T (S = Q K^T, P,
+//     dV^T += dO^T P), the other V and dK^T (dP = dO V^T, dS = P (dP - Di) with
+//     the P its partner leaves in LDS, dK^T += Q^T dS).
 //
 // Each pass recomputes S and dP, so the backward runs 7 matrix products instead
 // of 5; in exchange no partial result is ever summed through memory atomics.
@@ -338,21 +339,33 @@ __global__ void __launch_bounds__(256) dq_reduce_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- dK/dV pass
+//
+// A tile is BN keys of one (sequence, head); it walks the query rows in steps of
+// BM. Each 32-key block of the tile belongs to a pair of waves that split the four
+// products of a step between them:
+//   P wave:  S' = Q K^T - lse/scale, P = 2^(c S'), dV^T += dO^T P;
+//   dS wave: dP' = dO V^T - Di, dS = P dP' (P handed over through LDS),
+//            dK^T += Q^T dS.
+// Each wave holds one 32-key operand (K or V) and one accumulator (dV^T or dK^T),
+// which lets two waves share a SIMD. The dS wave works one step behind its
+// partner, and the two alternate between MFMA work and VALU work: while the P
+// wave runs its products the dS wave forms dS, and while the P wave forms P the
+// dS wave runs its products.
 template <int D>
 struct KvCfg {
   static constexpr int BN = jfa::kBwdBN;  // keys per tile
-  static constexpr int NW = BN / 32;      // waves, 32 keys each
+  static constexpr int NP = BN / 32;      // wave pairs, 32 keys each
+  static constexpr int NW = 2 * NP;       // P waves 0..NP-1, dS waves NP..2NP-1
   static constexpr int NT = 64 * NW;
   static constexpr int BM = jfa::kBwdBM;  // query rows per step
   static constexpr int IB = BM / 32;
-  static constexpr int NS = 4;            // LDS ring stages
+  static constexpr int NS = 3;            // ring stages
   static constexpr int DS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int NX = 2 * IB * NB;  // dV (or dK) products per step
-  static constexpr int TILE = BM * D;
-  static constexpr int STAGE = 2 * TILE;  // Q then dO
-  static constexpr int LOADS = 2 * TILE / 8 / 64 / NW;
-  static constexpr int WPE = 1;           // waves per SIMD the registers allow
+  static constexpr int PK = 2 * IB;       // packed P (or dS) operands per step
+  static constexpr int TILE = BM * D;     // elements of one Q or dO tile
+  static constexpr int TB = TILE * 2;     // its bytes
 };
 
 struct KvParams {
@@ -364,152 +377,158 @@ struct KvParams {
   float c, scale;
 };
 
-// S' = Q K^T - lse/scale and dP' = dO V^T - Di for one step of BM query rows
-// (lane = key): the accumulators start from the per-row constants the dQ pass
-// left in the stage's vectors, so that P = 2^(c S') and dS = P dP' need no
-// further per-element terms. All row fragments of one k-step are read before its
-// MFMAs.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_rw_t;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4_t;
+
+// Per-lane LDS addresses of one wave of a pair for the current tile. The wave
+// reads row fragments of one tensor and column fragments of the other (P wave:
+// rows of Q, columns of dO; dS wave: rows of dO, columns of Q); every access to
+// ring stage S adds S*TB, a compile-time offset.
 template <int D>
-__device__ __forceinline__ void kv_scores(uint32_t qs, uint32_t dos, const LaneOffsets<D>& lo,
-                                          const u32x4 (&kf)[KvCfg<D>::DS],
-                                          const u32x4 (&vf)[KvCfg<D>::DS], const float* nls_s,
-                                          const float* ndi_s, int g, f32x16 (&s)[KvCfg<D>::IB],
-                                          f32x16 (&dp)[KvCfg<D>::IB]) {
+struct KvAddr {
+  uint32_t row[D / 16];     // row fragments, k-chunk kc, rows 0..31 of stage 0
+  uint32_t col[D / 32][2];  // column fragments, column block nb, rows 0..7 / 8..15
+  uint32_t xch;             // this lane's slot of the pair's exchange, stage 0
+  uint32_t vec;             // this lane's rows of the stage-0 vector
+};
+
+// Scores of one step with lane = key: S' = Q K^T - lse/scale (P wave, `op` = K)
+// or dP' = dO V^T - Di (dS wave, `op` = V), from ring stage S. The accumulators
+// start from the per-row constant the dQ pass left in the stage's vector; row
+// fragments are read one k-step ahead of their MFMAs.
+template <int D, int S>
+__device__ __forceinline__ void kv_scores(const KvAddr<D>& a, const u32x4 (&op)[KvCfg<D>::DS],
+                                          f32x16 (&s)[KvCfg<D>::IB]) {
   using C = KvCfg<D>;
 #pragma unroll
   for (int ib = 0; ib < C::IB; ++ib)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       // register q4*4 + e holds row ib*32 + q4*8 + 4g + e
-      const f32x4 a = *reinterpret_cast<const f32x4*>(nls_s + ib * 32 + q4 * 8 + g * 4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ndi_s + ib * 32 + q4 * 8 + g * 4);
+      const f32x4 v = *(lds_f32x4_t*)(size_t)(a.vec + uint32_t((S * 2 * C::BM + ib * 32 + q4 * 8) * 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[ib][q4 * 4 + e] = a[e];
-        dp[ib][q4 * 4 + e] = b[e];
-      }
+      for (int e = 0; e < 4; ++e) s[ib][q4 * 4 + e] = v[e];
     }
+  u32x4 fr[2][C::IB];
+  auto read = [&](int d, int buf) {
+#pragma unroll
+    for (int ib = 0; ib < C::IB; ++ib)
+      fr[buf][ib] = lds_ld16(a.row[d] + uint32_t(S * C::TB + ib * 32 * D * 2));
+  };
+  read(0, 0);
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
-    u32x4 qa[C::IB], da[C::IB];
+    if (d + 1 < C::DS) read(d + 1, (d + 1) & 1);
 #pragma unroll
-    for (int ib = 0; ib < C::IB; ++ib) {
-      qa[ib] = rows_at<D>(qs, lo, ib * 32, d);
-      da[ib] = rows_at<D>(dos, lo, ib * 32, d);
-    }
-#pragma unroll
-    for (int ib = 0; ib < C::IB; ++ib) {
-      s[ib] = mfma32(qa[ib], kf[d], s[ib]);
-      dp[ib] = mfma32(da[ib], vf[d], dp[ib]);
-    }
-  }
-}
-
-// dV^T += dO^T P and dK^T += Q^T dS for one step whose P and dS are packed with
-// query rows along the registers.
-template <int D>
-__device__ __forceinline__ void kv_accumulate(uint32_t qs, uint32_t dos, const LaneOffsets<D>& lo,
-                                              const u32x4 (&pp)[2 * KvCfg<D>::IB],
-                                              const u32x4 (&pd)[2 * KvCfg<D>::IB],
-                                              f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
-  using C = KvCfg<D>;
-#pragma unroll
-  for (int x = 0; x < C::NX; ++x) {
-    const int st = x / C::NB, nb = x % C::NB;
-    const u32x4 fa = cols_at<D>(dos, lo, st * 16, nb * 32);
-    const u32x4 fb = cols_at<D>(qs, lo, st * 16, nb * 32);
-    dv[nb] = mfma32(fa, pp[st], dv[nb]);
-    dk[nb] = mfma32(fb, pd[st], dk[nb]);
-  }
-}
-
-// P = 2^(c S') and dS = P dP' for one step (S' and dP' already carry -lse/scale
-// and -Di), packed to bf16 (keys past the diagonal masked with CAUSAL). The work
-// is cut into IB*4 groups of four query rows. With PREV, each group is issued
-// together with a share of the previous step's dV/dK products, between
-// scheduling fences, so that the VALU work runs while those MFMAs execute; their
-// column fragments are read one group ahead.
-template <int D, bool MASK, bool PREV>
-__device__ __forceinline__ void kv_softmax(const f32x16 (&s)[KvCfg<D>::IB],
-                                           const f32x16 (&dp)[KvCfg<D>::IB], float c, int g, int q0,
-                                           int jw, u32x4 (&pp)[2 * KvCfg<D>::IB],
-                                           u32x4 (&pd)[2 * KvCfg<D>::IB], uint32_t qs_prev,
-                                           uint32_t dos_prev, const LaneOffsets<D>& lo,
-                                           const u32x4 (&pp_prev)[2 * KvCfg<D>::IB],
-                                           const u32x4 (&pd_prev)[2 * KvCfg<D>::IB],
-                                           f32x16 (&dv)[KvCfg<D>::NB], f32x16 (&dk)[KvCfg<D>::NB]) {
-  using C = KvCfg<D>;
-  constexpr int NG = C::IB * 4;      // groups of 4 query rows (per lane: 4 registers)
-  constexpr int XPG = C::NX / NG;    // dV/dK product pairs per group
-  static_assert(XPG * NG == C::NX, "products must split evenly over the groups");
-  u32x4 fa[2][XPG], fb[2][XPG];
-  auto read_cols = [&](int grp, int buf) {
-#pragma unroll
-    for (int xx = 0; xx < XPG; ++xx) {
-      const int x = grp * XPG + xx, st = x / C::NB, nb = x % C::NB;
-      fa[buf][xx] = cols_at<D>(dos_prev, lo, st * 16, nb * 32);
-      fb[buf][xx] = cols_at<D>(qs_prev, lo, st * 16, nb * 32);
-    }
-  };
-  if (PREV) read_cols(0, 0);
-#pragma unroll
-  for (int grp = 0; grp < NG; ++grp) {
-    const int cur = grp & 1;
-    if (PREV && grp + 1 < NG) read_cols(grp + 1, cur ^ 1);
-    if (PREV) {
-#pragma unroll
-      for (int xx = 0; xx < XPG; ++xx) {
-        const int x = grp * XPG + xx, st = x / C::NB, nb = x % C::NB;
-        dv[nb] = mfma32(fa[cur][xx], pp_prev[st], dv[nb]);
-        dk[nb] = mfma32(fb[cur][xx], pd_prev[st], dk[nb]);
-      }
-    }
-    const int ib = grp / 4, q4 = grp % 4;
-    const int i0 = ib * 32 + q4 * 8 + g * 4;
-    float pv[4], dsv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = q4 * 4 + e;
-      float p = exp2_fast(s[ib][r] * c);
-      if (MASK) p = jw > q0 + i0 + e ? 0.f : p;
-      pv[e] = p;
-      dsv[e] = p * dp[ib][r];
-    }
-    const int st = ib * 2 + q4 / 2, hw = (q4 % 2) * 2;
-    pp[st][hw] = pack_bf16(pv[0], pv[1]);
-    pp[st][hw + 1] = pack_bf16(pv[2], pv[3]);
-    pd[st][hw] = pack_bf16(dsv[0], dsv[1]);
-    pd[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
+    for (int ib = 0; ib < C::IB; ++ib) s[ib] = mfma32(fr[d & 1][ib], op[d], s[ib]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// acc^T += X^T Y for the step in ring stage S: X = dO (P wave: acc = dV, Y = P)
+// or Q (dS wave: acc = dK, Y = dS), Y packed with query rows along the registers.
+// Column fragments are read two products ahead of their MFMAs.
+template <int D, int S>
+__device__ __forceinline__ void kv_products(const KvAddr<D>& a, const u32x4 (&y)[KvCfg<D>::PK],
+                                            f32x16 (&acc)[KvCfg<D>::NB]) {
+  using C = KvCfg<D>;
+  constexpr int AH = 2;
+  u32x4 f[AH + 1];
+  auto read = [&](int x) {
+    const int st = x / C::NB, nb = x % C::NB;
+    const uint32_t off = uint32_t(S * C::TB + st * 16 * D * 2);
+    const u32x2 lo = lds_tr8(a.col[nb][0] + off), hi = lds_tr8(a.col[nb][1] + off);
+    f[x % (AH + 1)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+#pragma unroll
+  for (int x = 0; x < AH; ++x) read(x);
+#pragma unroll
+  for (int x = 0; x < C::NX; ++x) {
+    if (x + AH < C::NX) read(x + AH);
+    acc[x % C::NB] = mfma32(f[x % (AH + 1)], y[x / C::NB], acc[x % C::NB]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P = 2^(c S') packed to bf16 (keys after the query masked with MASK). Operand st
+// element k holds rows (st%2)*8 + 2k, +1 of 32-row block st/2.
+template <int D, bool MASK>
+__device__ __forceinline__ void kv_probs(const f32x16 (&s)[KvCfg<D>::IB], float c, int g, int q0,
+                                         int jw, u32x4 (&pk)[KvCfg<D>::PK]) {
+  using C = KvCfg<D>;
+#pragma unroll
+  for (int st = 0; st < C::PK; ++st)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ib = st / 2, r = (st % 2) * 8 + 2 * k;
+      // register r holds row (r/4)*8 + 4g + r%4 of the block
+      const int i = q0 + ib * 32 + (r / 4) * 8 + 4 * g + r % 4;
+      float p0 = exp2_fast(s[ib][r] * c), p1 = exp2_fast(s[ib][r + 1] * c);
+      if (MASK) {
+        p0 = jw > i ? 0.f : p0;
+        p1 = jw > i + 1 ? 0.f : p1;
+      }
+      pk[st][k] = pack_bf16(p0, p1);
+    }
+}
+
+// dS = P dP' packed to bf16, from the partner's packed P (same layout).
+template <int D>
+__device__ __forceinline__ void kv_dsoft(const f32x16 (&dp)[KvCfg<D>::IB],
+                                         const u32x4 (&pp)[KvCfg<D>::PK],
+                                         u32x4 (&pk)[KvCfg<D>::PK]) {
+  using C = KvCfg<D>;
+#pragma unroll
+  for (int st = 0; st < C::PK; ++st)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ib = st / 2, r = (st % 2) * 8 + 2 * k;
+      pk[st][k] = pack_bf16(bf16_lo(pp[st][k]) * dp[ib][r], bf16_hi(pp[st][k]) * dp[ib][r + 1]);
+    }
+}
+
+template <int D, int S>
+__device__ __forceinline__ void xch_put(const KvAddr<D>& a, const u32x4 (&pk)[KvCfg<D>::PK]) {
+  using C = KvCfg<D>;
+#pragma unroll
+  for (int x = 0; x < C::PK; ++x)
+    *(lds_u32x4_rw_t*)(size_t)(a.xch + uint32_t((S * C::NP * C::PK + x) * 64 * 16)) = pk[x];
+}
+template <int D, int S>
+__device__ __forceinline__ void xch_get(const KvAddr<D>& a, u32x4 (&pp)[KvCfg<D>::PK]) {
+  using C = KvCfg<D>;
+#pragma unroll
+  for (int x = 0; x < C::PK; ++x)
+    pp[x] = lds_ld16(a.xch + uint32_t((S * C::NP * C::PK + x) * 64 * 16));
+}
+
 template <int D, bool CAUSAL, bool BCAST>
-__global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(KvCfg<D>::WPE)))
+__global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
-  static_assert(C::NS == 4, "the waits below assume a four-stage ring");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+  static_assert(C::NS == 3, "the ring below loads one stage ahead and unrolls by three");
+  // Q ring then dO ring; the output rows are staged over both at the end of a tile
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * C::NS * C::TILE];
   __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // -lse/scale, -Di per stage
+  __shared__ u32x4 xch[C::NS][C::NP][C::PK * 64];  // packed P per stage and pair
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const bool pwave = w < C::NP;
+  const int kw = pwave ? w : w - C::NP;  // 32-key block of the pair
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
   const int rowbytes = int(rstride * 2);
-  const LaneOffsets<D> lo(lane);
-  const uint32_t lds0 = lds_addr(lds);
 
   for (int ti = t_begin; ti < t_end; ++ti) {
-    const int b = P.tiles[4 * ti + 0], h = P.tiles[4 * ti + 1], n = P.tiles[4 * ti + 2];
-    const int kv0 = P.offsets[b];
-    const int L = P.offsets[b + 1] - kv0;
+    const int b = uniform(P.tiles[4 * ti + 0]), h = uniform(P.tiles[4 * ti + 1]);
+    const int n = uniform(P.tiles[4 * ti + 2]);
+    const int kv0 = uniform(P.offsets[b]);
+    const int L = uniform(P.offsets[b + 1]) - kv0;
     const int key0 = n * C::BN;
     const int rows_total = BCAST ? P.lq : L;
-    const int jw = key0 + w * 32 + li;  // this lane's key
-    const bool key_ok = jw < L;
-    const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
-    const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
+    const int row0 = key0 + kw * 32;
+    const int jw = row0 + li;  // this lane's key
     const uint16_t* qbase = BCAST ? P.q + int64_t(h) * D : P.q + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* dobase = BCAST ? P.dout + int64_t(b) * P.lq * rstride + int64_t(h) * D
                                    : P.dout + int64_t(kv0) * rstride + int64_t(h) * D;
@@ -522,88 +541,111 @@ dkdv_kernel(KvParams P) {
     auto load_stage = [&](int st) {
       const int q_first = (qs_lo + st) * C::BM;
       const int left = rows_total - q_first;
-      const int buf = st % C::NS;
-      uint16_t* dst = lds + buf * C::STAGE;
-      tile_load<D, C::BM, C::NW>(dst, rows_rsrc<D>(qbase + int64_t(q_first) * rstride, rstride, left),
+      const int sl = st % C::NS;
+      tile_load<D, C::BM, C::NW>(ring + sl * C::TILE,
+                                 rows_rsrc<D>(qbase + int64_t(q_first) * rstride, rstride, left),
                                  rowbytes, w, lane);
-      tile_load<D, C::BM, C::NW>(dst + C::TILE,
+      tile_load<D, C::BM, C::NW>(ring + (C::NS + sl) * C::TILE,
                                  rows_rsrc<D>(dobase + int64_t(q_first) * rstride, rstride, left),
                                  rowbytes, w, lane);
       if (w < 2) {
         const float* src = (w == 0 ? P.nls : P.di) + voff + q_first;
-        vec64_load(vecs[buf][w], vec_rsrc(src, left), lane);
+        vec64_load(vecs[sl][w], vec_rsrc(src, left), lane);
       }
     };
-    auto qs_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
-    // stage st is read once it has landed (stage st+1 may still be in flight)
-    auto arrive = [&](int st) {
-      if (st + 1 < n_steps) wait_vmem_le<C::LOADS>();
-      else wait_vmem();
-      __syncthreads();
-    };
+    const int64_t e0 = (int64_t(kv0) + row0) * rstride + int64_t(h) * D;
 
-    // K, V of this wave's 32 keys, then the first two stages. Step it reads the
-    // rows of stage it and the columns of stage it-1, so the load issued at step it
-    // (stage it+2) goes to the buffer of stage it-2.
-    u32x4 kf[C::DS], vf[C::DS];
+    // One role per wave; both branches meet the same barriers. Step it: wait for
+    // stage it, barrier (every wave is done with step it-1, so the buffers of
+    // stage it-2 are free and the P of step it-1 is in LDS), load stage it+1.
+    auto run = [&](auto role) {
+      constexpr bool PW = decltype(role)::value;
+      // lane-dependent addresses are derived afresh for each tile (otherwise the
+      // compiler computes them once, before the tile loop, and keeps them live)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      KvAddr<D> ad;
+      {
+        const LaneOffsets<D> lo(ln);
+        const uint32_t rows_t = lds_addr(ring) + uint32_t(PW ? 0 : C::NS * C::TB);
+        const uint32_t cols_t = lds_addr(ring) + uint32_t(PW ? C::NS * C::TB : 0);
 #pragma unroll
-    for (int d = 0; d < C::DS; ++d) {
-      kf[d] = key_ok ? ld16(kbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
-      vf[d] = key_ok ? ld16(vbase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    }
+        for (int kc = 0; kc < C::DS; ++kc) ad.row[kc] = rows_t + lo.row[kc];
 #pragma unroll
-    for (int st = 0; st < C::NS - 2; ++st)
-      if (st < n_steps) load_stage(st);
-    f32x16 dv[C::NB], dk[C::NB];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      dv[nb] = f32x16{};
-      dk[nb] = f32x16{};
-    }
-
-    if (n_steps > 0) {
-      f32x16 s[C::IB], dp[C::IB];
-      u32x4 pp[2 * C::IB], pd[2 * C::IB], ppv[2 * C::IB], pdv[2 * C::IB];
-      // step 0
-      arrive(0);
-      if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
-      kv_scores<D>(qs_of(0), qs_of(0) + C::TILE * 2, lo, kf, vf, vecs[0][0], vecs[0][1], g, s, dp);
-      const int q00 = qs_lo * C::BM;
-      if (n_mask > 0)
-        kv_softmax<D, true, false>(s, dp, P.c, g, q00, jw, pp, pd, 0, 0, lo, ppv, pdv, dv, dk);
-      else
-        kv_softmax<D, false, false>(s, dp, P.c, g, q00, jw, pp, pd, 0, 0, lo, ppv, pdv, dv, dk);
-      // step it: its scores, then its softmax under the previous step's products
-      auto step = [&](int it, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-        for (int x = 0; x < 2 * C::IB; ++x) {
-          ppv[x] = pp[x];
-          pdv[x] = pd[x];
+        for (int nb = 0; nb < C::NB; ++nb) {
+          ad.col[nb][0] = cols_t + lo.col[nb][0];
+          ad.col[nb][1] = cols_t + lo.col[nb][1];
         }
-        arrive(it);  // also: every wave is done with stage it-2
-        if (it + C::NS - 2 < n_steps) load_stage(it + C::NS - 2);
-        const uint32_t qs = qs_of(it), qp = qs_of(it - 1);
-        const int buf = it % C::NS;
-        kv_scores<D>(qs, qs + C::TILE * 2, lo, kf, vf, vecs[buf][0], vecs[buf][1], g, s, dp);
-        kv_softmax<D, MASK, true>(s, dp, P.c, g, (qs_lo + it) * C::BM, jw, pp, pd, qp,
-                                  qp + C::TILE * 2, lo, ppv, pdv, dv, dk);
+        ad.xch = lds_addr(xch) + uint32_t((kw * C::PK * 64 + ln) * 16);
+        ad.vec = lds_addr(vecs) + uint32_t((PW ? 0 : C::BM) * 4 + (ln >> 5) * 16);
+      }
+      const uint16_t* obase = (PW ? P.k : P.v) + int64_t(kv0) * rstride + int64_t(h) * D;
+      u32x4 op[C::DS];
+#pragma unroll
+      for (int d = 0; d < C::DS; ++d)
+        op[d] = jw < L ? ld16(obase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+      load_stage(0);
+      f32x16 acc[C::NB];
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+      f32x16 s[C::IB];
+      u32x4 pk[C::PK];
+      auto step = [&](int it, auto stage) {
+        constexpr int S = decltype(stage)::value, SP = (S + C::NS - 1) % C::NS;
+        const bool prev = S != 0 || it > 0;
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 < n_steps) load_stage(it + 1);
+        if (PW) {
+          kv_scores<D, S>(ad, op, s);
+          if (prev) kv_products<D, SP>(ad, pk, acc);
+          const int q0 = (qs_lo + it) * C::BM;
+          if (CAUSAL && it < n_mask) kv_probs<D, true>(s, P.c, g, q0, jw, pk);
+          else kv_probs<D, false>(s, P.c, g, q0, jw, pk);
+          xch_put<D, S>(ad, pk);
+        } else {
+          if (prev) {
+            u32x4 pp[C::PK];
+            xch_get<D, SP>(ad, pp);
+            kv_dsoft<D>(s, pp, pk);
+          }
+          kv_scores<D, S>(ad, op, s);
+          if (prev) kv_products<D, SP>(ad, pk, acc);
+        }
       };
-      int it = 1;
-      for (; it < n_mask; ++it) step(it, std::true_type{});
-      for (; it < n_steps; ++it) step(it, std::false_type{});
-      const uint32_t ql = qs_of(n_steps - 1);
-      kv_accumulate<D>(ql, ql + C::TILE * 2, lo, pp, pd, dv, dk);
-    }
-    __syncthreads();  // every wave is done with the ring: it stages the output rows
-    {
-      const int row0 = key0 + w * 32;
-      const int64_t e0 = (int64_t(kv0) + row0) * rstride + int64_t(h) * D;
-      uint16_t* stage = lds + w * 32 * D;
-      store_rows<D>(stage, dv, 1.f, P.dv + e0, rstride, L - row0, lane);
-      store_rows<D>(stage, dk, P.scale, P.dk + e0, rstride, L - row0, lane);
-    }
-    __syncthreads();  // the next tile's first loads overwrite the first stages
+      // the last step's products, once its P is in LDS
+      auto tail = [&](auto stage) {
+        constexpr int S = decltype(stage)::value;
+        __syncthreads();
+        if (PW) {
+          kv_products<D, S>(ad, pk, acc);
+        } else {
+          u32x4 pp[C::PK];
+          xch_get<D, S>(ad, pp);
+          kv_dsoft<D>(s, pp, pk);
+          kv_products<D, S>(ad, pk, acc);
+        }
+      };
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      for (int it = 0; it < n_steps; it += 3) {
+        step(it, S0{});
+        if (it + 1 < n_steps) step(it + 1, S1{});
+        if (it + 2 < n_steps) step(it + 2, S2{});
+      }
+      const int last = (n_steps - 1) % C::NS;
+      if (last == 0) tail(S0{});
+      else if (last == 1) tail(S1{});
+      else tail(S2{});
+      __syncthreads();  // every wave is done with the ring: it stages the output rows
+      store_rows<D>(ring + w * 32 * D, acc, PW ? 1.f : P.scale, (PW ? P.dv : P.dk) + e0, rstride,
+                    L - row0, lane);
+      __syncthreads();  // the next tile's first loads overwrite the first stages
+    };
+    if (n_steps <= 0) continue;  // (uniform) a causal tile always has steps
+    if (pwave) run(std::true_type{});
+    else run(std::false_type{});
   }
 }
 
