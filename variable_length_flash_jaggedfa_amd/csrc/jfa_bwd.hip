@@ -242,9 +242,10 @@ dq_kernel(DqParams P) {
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
   for (int ti = t_begin; ti < t_end; ++ti) {
-    const int b = P.tiles[4 * ti + 0], h = P.tiles[4 * ti + 1], t = P.tiles[4 * ti + 2];
-    const int kv0 = P.offsets[b];
-    const int L = P.offsets[b + 1] - kv0;
+    const int b = uniform(P.tiles[4 * ti + 0]), h = uniform(P.tiles[4 * ti + 1]);
+    const int t = uniform(P.tiles[4 * ti + 2]);
+    const int kv0 = uniform(P.offsets[b]);
+    const int L = uniform(P.offsets[b + 1]) - kv0;
     const int q_first = t * C::BM;
     const int q_rows = min(C::BM, L - q_first);
     const int n_keys = CAUSAL ? min(L, q_first + q_rows) : L;
@@ -557,7 +558,8 @@ dkdv_kernel(KvParams P) {
 
     // One role per wave; both branches meet the same barriers. Step it: wait for
     // stage it, barrier (every wave is done with step it-1, so the buffers of
-    // stage it-2 are free and the P of step it-1 is in LDS), load stage it+1.
+    // stage it-2 are free and the P of step it-1 is in LDS); stage it+1 is loaded
+    // during the step.
     auto run = [&](auto role) {
       constexpr bool PW = decltype(role)::value;
       // lane-dependent addresses are derived afresh for each tile (otherwise the
@@ -595,10 +597,13 @@ dkdv_kernel(KvParams P) {
         const bool prev = S != 0 || it > 0;
         wait_vmem();
         __syncthreads();
-        if (it + 1 < n_steps) load_stage(it + 1);
         if (PW) {
           kv_scores<D, S>(ad, op, s);
           if (prev) kv_products<D, SP>(ad, pk, acc);
+          // the P waves issue their share of the next stage's loads after their
+          // products, the dS waves at the start of the step: the buffer->LDS
+          // traffic is spread over the step
+          if (it + 1 < n_steps) load_stage(it + 1);
           const int q0 = (qs_lo + it) * C::BM;
           if (CAUSAL && it < n_mask) kv_probs<D, true>(s, P.c, g, q0, jw, pk);
           else kv_probs<D, false>(s, P.c, g, q0, jw, pk);
@@ -609,6 +614,7 @@ dkdv_kernel(KvParams P) {
             xch_get<D, SP>(ad, pp);
             kv_dsoft<D>(s, pp, pk);
           }
+          if (it + 1 < n_steps) load_stage(it + 1);
           kv_scores<D, S>(ad, op, s);
           if (prev) kv_products<D, SP>(ad, pk, acc);
         }
