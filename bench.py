@@ -288,6 +288,7 @@ def main():
         w = r["w"]
         tag = w.name + ("_causal" if w.causal else "")
         if r["block"]:
+            tag = f"{w.name}_d{w.head_dim}"
             tb = T * w.num_heads * w.head_dim * 2
             cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
