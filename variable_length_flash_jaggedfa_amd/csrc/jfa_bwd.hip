@@ -521,47 +521,76 @@ dkdv_kernel(KvParams P) {
   const int64_t rstride = int64_t(P.H) * D;
   const int rowbytes = int(rstride * 2);
 
-  for (int ti = t_begin; ti < t_end; ++ti) {
-    const int b = uniform(P.tiles[4 * ti + 0]), h = uniform(P.tiles[4 * ti + 1]);
-    const int n = uniform(P.tiles[4 * ti + 2]);
-    const int kv0 = uniform(P.offsets[b]);
-    const int L = uniform(P.offsets[b + 1]) - kv0;
-    const int key0 = n * C::BN;
-    const int rows_total = BCAST ? P.lq : L;
-    const int row0 = key0 + kw * 32;
-    const int jw = row0 + li;  // this lane's key
-    const uint16_t* qbase = BCAST ? P.q + int64_t(h) * D : P.q + int64_t(kv0) * rstride + int64_t(h) * D;
-    const uint16_t* dobase = BCAST ? P.dout + int64_t(b) * P.lq * rstride + int64_t(h) * D
-                                   : P.dout + int64_t(kv0) * rstride + int64_t(h) * D;
-    const int64_t voff = BCAST ? (int64_t(b) * P.H + h) * P.lq : int64_t(h) * P.total_kv + kv0;
-    const int qs_lo = CAUSAL ? key0 / C::BM : 0;
-    const int n_steps = ceil_div(rows_total, C::BM) - qs_lo;
+  // what every wave derives from a tile of the schedule
+  struct Tile {
+    int b, h, kv0, L, key0, rows_total, qs_lo, n_steps, n_mask;
+    const uint16_t* qbase;
+    const uint16_t* dobase;
+    int64_t voff;
+  };
+  auto tile_of = [&](int ti) {
+    Tile T;
+    T.b = uniform(P.tiles[4 * ti + 0]);
+    T.h = uniform(P.tiles[4 * ti + 1]);
+    T.key0 = uniform(P.tiles[4 * ti + 2]) * C::BN;
+    T.kv0 = uniform(P.offsets[T.b]);
+    T.L = uniform(P.offsets[T.b + 1]) - T.kv0;
+    T.rows_total = BCAST ? P.lq : T.L;
+    T.qbase = BCAST ? P.q + int64_t(T.h) * D : P.q + int64_t(T.kv0) * rstride + int64_t(T.h) * D;
+    T.dobase = BCAST ? P.dout + int64_t(T.b) * P.lq * rstride + int64_t(T.h) * D
+                     : P.dout + int64_t(T.kv0) * rstride + int64_t(T.h) * D;
+    T.voff = BCAST ? (int64_t(T.b) * P.H + T.h) * P.lq : int64_t(T.h) * P.total_kv + T.kv0;
+    T.qs_lo = CAUSAL ? T.key0 / C::BM : 0;
+    // every tile has at least one step (lq >= 1; a causal tile starts on the
+    // diagonal of its own keys)
+    T.n_steps = ceil_div(T.rows_total, C::BM) - T.qs_lo;
     // causal steps that reach the diagonal need a mask; rows past the end read as
     // zeros and contribute nothing
-    const int n_mask = CAUSAL ? min(n_steps, C::BN / C::BM) : 0;
-    auto load_stage = [&](int st) {
-      const int q_first = (qs_lo + st) * C::BM;
-      const int left = rows_total - q_first;
-      const int sl = st % C::NS;
-      tile_load<D, C::BM, C::NW>(ring + sl * C::TILE,
-                                 rows_rsrc<D>(qbase + int64_t(q_first) * rstride, rstride, left),
-                                 rowbytes, w, lane);
-      tile_load<D, C::BM, C::NW>(ring + (C::NS + sl) * C::TILE,
-                                 rows_rsrc<D>(dobase + int64_t(q_first) * rstride, rstride, left),
-                                 rowbytes, w, lane);
-      if (w < 2) {
-        const float* src = (w == 0 ? P.nls : P.di) + voff + q_first;
-        vec64_load(vecs[sl][w], vec_rsrc(src, left), lane);
-      }
-    };
-    const int64_t e0 = (int64_t(kv0) + row0) * rstride + int64_t(h) * D;
+    T.n_mask = CAUSAL ? min(T.n_steps, C::BN / C::BM) : 0;
+    return T;
+  };
+  auto load_stage = [&](const Tile& T, int st) {
+    const int q_first = (T.qs_lo + st) * C::BM;
+    const int left = T.rows_total - q_first;
+    const int sl = st % C::NS;
+    tile_load<D, C::BM, C::NW>(ring + sl * C::TILE,
+                               rows_rsrc<D>(T.qbase + int64_t(q_first) * rstride, rstride, left),
+                               rowbytes, w, lane);
+    tile_load<D, C::BM, C::NW>(ring + (C::NS + sl) * C::TILE,
+                               rows_rsrc<D>(T.dobase + int64_t(q_first) * rstride, rstride, left),
+                               rowbytes, w, lane);
+    if (w < 2) {
+      const float* src = (w == 0 ? P.nls : P.di) + T.voff + q_first;
+      vec64_load(vecs[sl][w], vec_rsrc(src, left), lane);
+    }
+  };
 
-    // One role per wave; both branches meet the same barriers. Step it: wait for
-    // stage it, barrier (every wave is done with step it-1, so the buffers of
-    // stage it-2 are free and the P of step it-1 is in LDS); stage it+1 is loaded
-    // during the step.
-    auto run = [&](auto role) {
-      constexpr bool PW = decltype(role)::value;
+  // One role per wave, each walking all the slot's tiles; both meet the same
+  // barriers. Step it: wait for stage it, barrier (every wave is done with step
+  // it-1, so the buffers of stage it-2 are free and the P of step it-1 is in
+  // LDS); stage it+1 is loaded during the step. The first stage and the key
+  // operand of the next tile are loaded before this tile's output rows are
+  // stored, so their latency runs under the epilogue.
+  auto run = [&](auto role) {
+    constexpr bool PW = decltype(role)::value;
+    const uint16_t* kvsrc = PW ? P.k : P.v;  // the wave's 32-key operand: K or V
+    auto load_op = [&](const Tile& T, u32x4 (&op)[C::DS]) {
+      const int jw = T.key0 + kw * 32 + li;
+      const uint16_t* obase = kvsrc + int64_t(T.kv0) * rstride + int64_t(T.h) * D;
+#pragma unroll
+      for (int d = 0; d < C::DS; ++d)
+        op[d] = jw < T.L ? ld16(obase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    };
+    u32x4 op[C::DS];
+    Tile T{};
+    if (t_begin < t_end) {
+      T = tile_of(t_begin);
+      load_op(T, op);
+      load_stage(T, 0);
+    }
+    for (int ti = t_begin; ti < t_end; ++ti) {
+      const int row0 = T.key0 + kw * 32;
+      const int jw = row0 + li;  // this lane's key
       // lane-dependent addresses are derived afresh for each tile (otherwise the
       // compiler computes them once, before the tile loop, and keeps them live)
       int ln = lane;
@@ -581,21 +610,24 @@ dkdv_kernel(KvParams P) {
         ad.xch = lds_addr(xch) + uint32_t((kw * C::PK * 64 + ln) * 16);
         ad.vec = lds_addr(vecs) + uint32_t((PW ? 0 : C::BM) * 4 + (ln >> 5) * 16);
       }
-      const uint16_t* obase = (PW ? P.k : P.v) + int64_t(kv0) * rstride + int64_t(h) * D;
-      u32x4 op[C::DS];
-#pragma unroll
-      for (int d = 0; d < C::DS; ++d)
-        op[d] = jw < L ? ld16(obase + int64_t(jw) * rstride + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
-      load_stage(0);
       f32x16 acc[C::NB];
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+      // Take delivery of the key operand here, before the steps. Otherwise the
+      // compiler, which cannot see the buffer->LDS copies, places its wait for
+      // these loads inside the step loop, where it also drains the copy of the
+      // next stage issued just before.
+#pragma unroll
+      for (int d = 0; d < C::DS; ++d) asm volatile("" ::"v"(op[d]));
       f32x16 s[C::IB];
       u32x4 pk[C::PK];
       auto step = [&](int it, auto stage) {
         constexpr int S = decltype(stage)::value, SP = (S + C::NS - 1) % C::NS;
         const bool prev = S != 0 || it > 0;
-        wait_vmem();
+        // the first stage of a tile may still have the previous tile's D/16
+        // output stores behind it
+        if (S == 0 && it == 0 && ti > t_begin) wait_vmem_le<D / 16>();
+        else wait_vmem();
         __syncthreads();
         if (PW) {
           kv_scores<D, S>(ad, op, s);
@@ -603,9 +635,9 @@ dkdv_kernel(KvParams P) {
           // the P waves issue their share of the next stage's loads after their
           // products, the dS waves at the start of the step: the buffer->LDS
           // traffic is spread over the step
-          if (it + 1 < n_steps) load_stage(it + 1);
-          const int q0 = (qs_lo + it) * C::BM;
-          if (CAUSAL && it < n_mask) kv_probs<D, true>(s, P.c, g, q0, jw, pk);
+          if (it + 1 < T.n_steps) load_stage(T, it + 1);
+          const int q0 = (T.qs_lo + it) * C::BM;
+          if (CAUSAL && it < T.n_mask) kv_probs<D, true>(s, P.c, g, q0, jw, pk);
           else kv_probs<D, false>(s, P.c, g, q0, jw, pk);
           xch_put<D, S>(ad, pk);
         } else {
@@ -614,7 +646,7 @@ dkdv_kernel(KvParams P) {
             xch_get<D, SP>(ad, pp);
             kv_dsoft<D>(s, pp, pk);
           }
-          if (it + 1 < n_steps) load_stage(it + 1);
+          if (it + 1 < T.n_steps) load_stage(T, it + 1);
           kv_scores<D, S>(ad, op, s);
           if (prev) kv_products<D, SP>(ad, pk, acc);
         }
@@ -635,24 +667,34 @@ dkdv_kernel(KvParams P) {
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
       using S2 = std::integral_constant<int, 2>;
-      for (int it = 0; it < n_steps; it += 3) {
+      for (int it = 0; it < T.n_steps; it += 3) {
         step(it, S0{});
-        if (it + 1 < n_steps) step(it + 1, S1{});
-        if (it + 2 < n_steps) step(it + 2, S2{});
+        if (it + 1 < T.n_steps) step(it + 1, S1{});
+        if (it + 2 < T.n_steps) step(it + 2, S2{});
       }
-      const int last = (n_steps - 1) % C::NS;
+      const int last = (T.n_steps - 1) % C::NS;
       if (last == 0) tail(S0{});
       else if (last == 1) tail(S1{});
       else tail(S2{});
-      __syncthreads();  // every wave is done with the ring: it stages the output rows
-      store_rows<D>(ring + w * 32 * D, acc, PW ? 1.f : P.scale, (PW ? P.dv : P.dk) + e0, rstride,
-                    L - row0, lane);
-      __syncthreads();  // the next tile's first loads overwrite the first stages
-    };
-    if (n_steps <= 0) continue;  // (uniform) a causal tile always has steps
-    if (pwave) run(std::true_type{});
-    else run(std::false_type{});
-  }
+      __syncthreads();  // every wave is done with the ring and the exchange
+      const Tile Tc = T;
+      if (ti + 1 < t_end) {
+        T = tile_of(ti + 1);
+        load_op(T, op);
+        load_stage(T, 0);
+      }
+      // output rows staged in ring stages 1 and 2 (stage 0 is filling); the next
+      // tile's first barrier orders these reads before its loads of stage 1. The
+      // stores are counted (no other vector memory operation follows them before
+      // the next tile's first wait), so that wait need not drain them.
+      uint16_t* stg = ring + ((PW ? 0 : C::NS) + 1 + kw / 2) * C::TILE + (kw % 2) * 32 * D;
+      const int64_t e0 = (int64_t(Tc.kv0) + row0) * rstride + int64_t(Tc.h) * D;
+      store_rows_counted<D>(stg, acc, PW ? 1.f : P.scale, (PW ? P.dv : P.dk) + e0, rstride,
+                            Tc.L - row0, lane);
+    }
+  };
+  if (pwave) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 int grid_for(int64_t n4) {

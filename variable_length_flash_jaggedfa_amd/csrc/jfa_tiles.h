@@ -241,4 +241,39 @@ __device__ __forceinline__ void store_rows(uint16_t* stage, const f32x16 (&a)[D 
   }
 }
 
+// store_rows through buffer stores whose resource covers rows [0, nrows): rows
+// past the end fall outside it and are dropped by the hardware, so every wave
+// issues exactly D/16 store instructions whatever nrows is (a caller may count
+// them in s_waitcnt vmcnt).
+template <int D>
+__device__ __forceinline__ void store_rows_counted(uint16_t* stage, const f32x16 (&a)[D / 32],
+                                                   float mul, uint16_t* row0, int64_t rstride,
+                                                   int nrows, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5, li = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 wv;
+      wv[0] = pack_bf16(a[nb][q4 * 4 + 0] * mul, a[nb][q4 * 4 + 1] * mul);
+      wv[1] = pack_bf16(a[nb][q4 * 4 + 2] * mul, a[nb][q4 * 4 + 3] * mul);
+      st8(stage + Swz<D>::chunk(li, nb * 4 + q4) + g * 4, wv);
+    }
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR, r = lane / CPR;
+  const int nbytes = nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      row0, (short)0, __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + r;
+    const u32x4 v = ld16(stage + Swz<D>::chunk(row, c));
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, int(row * rstride * 2) + c * 16, 0, 0);
+  }
+}
+static_assert(32 / (64 / (128 / 8)) == 128 / 16 && 32 / (64 / (64 / 8)) == 64 / 16,
+              "store_rows_counted issues D/16 stores");
+
 }  // namespace jfa_dev
