@@ -133,6 +133,28 @@ def test_schedule_order_does_not_change_results(gpu):
         assert torch.equal(dqa, dqb) and torch.equal(dka, dkb) and torch.equal(dva, dvb)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_slot_counts_do_not_change_results(gpu, D):
+    """One workgroup walking every tile (each tile's first stage and key operand
+    are loaded while the previous tile's outputs are stored, across sequences
+    and heads) and far more workgroups than tiles (most walk none) give the same
+    bits as the default slot count, jagged and broadcast-Q."""
+    import torch
+    for w in (J.custom(RAGGED, 3, D, sigma=0.5, seed=21),
+              J.custom([50, 0, 300, 129, 1], 2, D, sigma=0.5, seed=22, kind="broadcast", lq=130)):
+        case = J.make_case(w)
+        a = GpuRun(case, gpu)
+        oa, la = a.forward()
+        ga = [x.clone() for x in a.backward()]
+        for slots in (1, 2048):
+            log(f"D={D} {w.kind} slots={slots}")
+            b = GpuRun(case, gpu, num_slots=slots)
+            ob, lb = b.forward()
+            assert torch.equal(oa, ob) and torch.equal(la, lb)
+            for x, y in zip(ga, b.backward()):
+                assert torch.equal(x, y)
+
+
 def test_run_to_run_bitwise(gpu):
     import torch
     for w in (J.custom(RAGGED, 2, 128, sigma=0.5, seed=15),
