@@ -134,15 +134,6 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
       pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
     }
   }
-  if (PREV) {
-#pragma unroll
-    for (int x = 0; x < C::NX; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, MASK ? 10 : 6, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 2 * C::KB, 0);
-    }
-  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
