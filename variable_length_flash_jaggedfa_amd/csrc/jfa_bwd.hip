@@ -77,19 +77,25 @@ __device__ __forceinline__ void dq_scores(uint32_t ks, uint32_t vs, const LaneOf
     s[kb] = f32x16{};
     dp[kb] = f32x16{};
   }
+  // row fragments are read one k-step ahead of their MFMAs
+  u32x4 ka[2][C::KB], va[2][C::KB];
+  auto read = [&](int d, int bf) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      ka[bf][kb] = rows_at<D>(ks, lo, kb * 32, d);
+      va[bf][kb] = rows_at<D>(vs, lo, kb * 32, d);
+    }
+  };
+  read(0, 0);
 #pragma unroll
   for (int d = 0; d < C::DS; ++d) {
-    u32x4 ka[C::KB], va[C::KB];
+    if (d + 1 < C::DS) read(d + 1, (d + 1) & 1);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-      ka[kb] = rows_at<D>(ks, lo, kb * 32, d);
-      va[kb] = rows_at<D>(vs, lo, kb * 32, d);
+      s[kb] = mfma32(ka[d & 1][kb], qf[d], s[kb]);
+      dp[kb] = mfma32(va[d & 1][kb], dof[d], dp[kb]);
     }
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      s[kb] = mfma32(ka[kb], qf[d], s[kb]);
-      dp[kb] = mfma32(va[kb], dof[d], dp[kb]);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
