@@ -36,6 +36,22 @@ struct BlkParams {
   float scale;
 };
 
+// The (64-token block, head) unit of this workgroup. At D = 128 neighbouring
+// workgroups take the heads of one block (together they read whole contiguous
+// rows of all heads); at D = 64 they take neighbouring blocks of one head. Each
+// order measured faster at its head dimension on the block-diagonal workload.
+template <int D>
+__device__ __forceinline__ void unit_of(int H, int& blk, int& h) {
+  if (D == 128) {
+    blk = blockIdx.x / H;
+    h = blockIdx.x % H;
+  } else {
+    const int nblk = gridDim.x / H;
+    blk = blockIdx.x % nblk;
+    h = blockIdx.x / nblk;
+  }
+}
+
 // Exact softmax of one 64-key tile held as S^T (keys along the registers, one
 // query per lane pair): returns P packed to bf16 as MFMA operands (keys in the
 // order of an accumulator tile) and keeps P in `s`.
@@ -69,9 +85,8 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * C::TILE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
-  // head-major order: neighbouring workgroups take neighbouring blocks of a head
-  const int nblk = gridDim.x / P.H;
-  const int blk = blockIdx.x % nblk, h = blockIdx.x / nblk;
+  int blk, h;
+  unit_of<D>(P.H, blk, h);
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
@@ -122,8 +137,8 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   uint16_t* dSt = Pt + kBS * kBS;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int nblk = gridDim.x / P.H;
-  const int blk = blockIdx.x % nblk, h = blockIdx.x / nblk;  // head-major order
+  int blk, h;
+  unit_of<D>(P.H, blk, h);
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
