@@ -626,9 +626,13 @@ dkdv_kernel(KvParams P) {
         if (S == 0 && it == 0 && ti > t_begin) wait_vmem_le<D / 16>();
         else wait_vmem();
         __syncthreads();
+        // each role's MFMA section runs at raised priority, its VALU section at
+        // the normal one
         if (PW) {
+          __builtin_amdgcn_s_setprio(1);
           kv_scores<D, S>(ad, op, s);
           if (prev) kv_products<D, SP>(ad, pk, acc);
+          __builtin_amdgcn_s_setprio(0);
           // the P waves issue their share of the next stage's loads after their
           // products, the dS waves at the start of the step: the buffer->LDS
           // traffic is spread over the step
@@ -644,8 +648,10 @@ dkdv_kernel(KvParams P) {
             kv_dsoft<D>(s, pp, pk);
           }
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
+          __builtin_amdgcn_s_setprio(1);
           kv_scores<D, S>(ad, op, s);
           if (prev) kv_products<D, SP>(ad, pk, acc);
+          __builtin_amdgcn_s_setprio(0);
         }
       };
       // the last step's products, once its P is in LDS
