@@ -127,15 +127,21 @@ KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "
 
 
 def kernel_source_digest():
-    """Digest of the kernel sources, or None when they are not present."""
+    """Digest of the kernel sources with // comments and blank lines removed (so a
+    comment edit does not orphan the counter records), or None when they are not
+    present."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         p = os.path.join(ROOT, "variable_length_flash_jaggedfa_amd", "csrc", name)
         if not os.path.exists(p):
             return None
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

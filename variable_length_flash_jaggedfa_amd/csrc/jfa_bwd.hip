@@ -7,7 +7,7 @@
 //
 //   dQ pass (query-tile outer, forward schedule). Each wave keeps 32 query rows
 //     of Q and dO in registers, computes Di for them, and streams the keys of
-//     its sequence through a 3-stage LDS ring: S^T = K Q^T and dP^T = V dO^T,
+//     its sequence through a 4-stage LDS ring: S^T = K Q^T and dP^T = V dO^T,
 //     P = 2^(S*scale*log2e - lse*log2e), dS = P * (dP - Di), dQ^T += K^T dS^T.
 //     dQ stays in registers and is written once; Di is written for the other pass.
 //   dK/dV pass (key-tile outer, backward schedule). Each 32-key block of a tile

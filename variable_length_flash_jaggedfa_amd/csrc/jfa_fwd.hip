@@ -5,8 +5,8 @@
 // KV-work-sorted tiles). A tile is 128 query rows of one (sequence, head); each
 // of the 4 waves owns 32 rows and two workgroups share a compute unit, so one
 // wave's softmax overlaps another wave's MFMAs on the same SIMD. Keys stream in
-// steps of 64 through a double-buffered LDS ring filled by direct global->LDS
-// loads issued one step ahead. Per step a
+// steps of 32 (D = 128) or 64 (D = 64) through a four-stage LDS ring filled by
+// direct buffer->LDS loads issued three steps ahead. Per step a
 // wave computes S^T = K Q^T (each lane holds the scores of one query row, so the
 // softmax statistics stay in the lane apart from one swap with lane ^ 32),
 // applies the online softmax in base 2 with the scale folded into the exponent
