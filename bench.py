@@ -46,8 +46,8 @@ def pairs_of(lengths, causal=False, lq=0, block=0):
 
 def variants_of(name):
     wl = J.standard_workloads()
-    if name == "gem":
-        return [wl["gem"], wl["gem_causal"]]
+    if name in ("gem", "gem_padded"):
+        return [wl[name], wl[name + "_causal"]]
     return [wl[name]]
 
 
@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
-                             "block64_d128", "imbalance"])
+                             "block64_d128", "imbalance", "gem_padded"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time forward + backward under every dealing order, interleaved")

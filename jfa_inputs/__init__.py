@@ -24,6 +24,9 @@ section 1):
               64-token block-diagonal.
   imbalance   B=2048: 102 lengths U{8192..16384} and 1946 lengths U{8..64},
               shuffled; H=16, D=128, sigma 0.5, non-causal.
+  gem_padded  the gem batch with every sequence as long as its longest one (the
+              padded-dense layout the jagged one avoids), causal and non-causal;
+              for timing the work a padded-dense run executes.
 """
 from __future__ import annotations
 
@@ -37,7 +40,9 @@ import numpy as np
 # stream ids
 S_LENGTHS, S_Q, S_K, S_V, S_DO, S_QDENSE = 0, 1, 2, 3, 4, 5
 
-WORKLOAD_IDS = {"tiny": 1, "gem": 2, "broadcast": 3, "block64": 4, "imbalance": 5}
+# gem_padded shares gem's id, so its lengths are the gem draw padded to the maximum
+WORKLOAD_IDS = {"tiny": 1, "gem": 2, "broadcast": 3, "block64": 4, "imbalance": 5,
+                "gem_padded": 2}
 
 
 @dataclass(frozen=True)
@@ -60,6 +65,7 @@ class Workload:
     mix_long_lo: int = 0
     mix_long_hi: int = 0
     fixed_lengths: tuple = ()
+    pad_to_max: bool = False          # every length replaced by the largest drawn
 
     @property
     def wid(self) -> int:
@@ -85,6 +91,10 @@ def standard_workloads():
                                  lo=1, hi=64),
         "imbalance": Workload("imbalance", 2048, 16, 128, 0.5, law="mix", lo=8, hi=64,
                               mix_long_frac=0.05, mix_long_lo=8192, mix_long_hi=16384),
+        "gem_padded": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
+                               hi=4096, pad_to_max=True),
+        "gem_padded_causal": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
+                                      hi=4096, pad_to_max=True, causal=True),
     }
 
 
@@ -118,6 +128,8 @@ def lengths(w: Workload) -> np.ndarray:
         raise ValueError(w.law)
     if w.force_first_short and B > 1:
         L[1] = 1
+    if w.pad_to_max and B > 0:
+        L[:] = L.max()
     return L
 
 

@@ -141,3 +141,14 @@ def test_folded_properties(name, kind):
     loads = np.array(R.slot_loads(sp, t))
     assert loads.max() <= loads.mean() + 2 * t[:, 3].max()
     assert loads.max() / loads.mean() < 1.06
+
+
+def test_padded_gem_recipe():
+    """The padded-dense comparison batch is the gem batch with every sequence as
+    long as the longest one (same B, H, D and draw)."""
+    wl = J.standard_workloads()
+    g, p = wl["gem"], wl["gem_padded"]
+    Lg, Lp = J.lengths(g), J.lengths(p)
+    assert (g.num_seqs, g.num_heads, g.head_dim) == (p.num_seqs, p.num_heads, p.head_dim)
+    assert np.all(Lp == Lg.max()) and Lp.shape == Lg.shape
+    assert wl["gem_padded_causal"].causal and not p.causal
