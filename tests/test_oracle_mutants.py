@@ -96,3 +96,52 @@ def test_backward_mutants_are_caught(monkeypatch, kind):
     monkeypatch.setattr(A, "seq_backward", _make_bwd_mutant(kind))
     assert _caught(T.test_backward_matches_torch_autograd, causal=False)
     assert _caught(T.test_backward_finite_differences_exhaustive_micro, causal=True)
+
+
+# ------------------------------------------------------------------ rotary
+from oracle import rotary as R  # noqa: E402
+from tests import test_oracle_rotary as TR  # noqa: E402
+
+_orig_rope = R.rope
+
+
+def _mut_rope(kind):
+    def rope(x, positions, base, inverse=False):
+        d = x.shape[-1]
+        if kind == "sin_sign":
+            return _orig_rope(x, positions, base, inverse=not inverse)
+        if kind == "interleaved":
+            perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+            y = _orig_rope(x[..., perm], positions, base, inverse)
+            out = np.empty_like(y)
+            out[..., perm] = y
+            return out
+        if kind == "freq_exponent":
+            return _orig_rope(x, np.asarray(positions, dtype=np.float64), base ** 0.5, inverse)
+        if kind == "no_inverse":
+            return _orig_rope(x, positions, base, False)
+        raise ValueError(kind)
+    return rope
+
+
+@pytest.mark.parametrize("kind", ["sin_sign", "interleaved", "freq_exponent", "no_inverse"])
+def test_rotary_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(R, "rope", _mut_rope(kind))
+    # every mutant fails the autograd comparison; the forward-only mutants also
+    # fail the worked value or the complex form, the backward one the finite
+    # differences
+    assert _caught(TR.test_block_rope_matches_torch_autograd, D=64)
+    if kind == "no_inverse":
+        assert _caught(TR.test_block_rope_finite_differences)
+    else:
+        assert _caught(TR.test_worked_rotation) or _caught(TR.test_matches_complex_form, D=64)
+
+
+def test_rotary_backward_without_inverse_rotation_is_caught(monkeypatch):
+    def bwd(q, k, v, do, offsets, scale, base, block=64):
+        pos = R.token_positions(offsets)
+        return R.block_diag_backward(R.rope(q, pos, base), R.rope(k, pos, base), v, do, offsets,
+                                     scale, block)
+    monkeypatch.setattr(R, "block_diag_rope_backward", bwd)
+    assert _caught(TR.test_block_rope_matches_torch_autograd, D=64)
+    assert _caught(TR.test_block_rope_finite_differences)
