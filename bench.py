@@ -59,6 +59,8 @@ def flags_of(w, jfa):
         f |= jfa.BROADCAST_Q
     if w.kind == "block64":
         f |= jfa.BLOCK_DIAG64
+    if w.rope_base:
+        f |= jfa.ROTARY
     return f
 
 
@@ -82,6 +84,7 @@ def cpu_baseline(case, variants, budget_s=15.0):
     """The fp64 oracle on a bounded sample of (sequence, head) units."""
     import threadpoolctl
     from oracle import attention as A
+    from oracle import rotary as R
     w0 = variants[0]
     off = case.offsets.astype(np.int64)
     rng = np.random.default_rng(0)
@@ -101,11 +104,18 @@ def cpu_baseline(case, variants, budget_s=15.0):
             else:
                 q_, do_ = f(case.q[s:e, h]), f(case.do[s:e, h])
                 npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block64" else 0)
+            if w.rope_base:
+                pos = np.arange(e - s)
+                q_ = R.rope(q_[:, None], pos, w.rope_base)[:, 0]
+                k_ = R.rope(k_[:, None], pos, w.rope_base)[:, 0]
             if w.kind == "block64":
                 for r0 in range(0, e - s, 64):
                     sl = slice(r0, r0 + 64)
                     A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
-                    A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
+                    dq_, dk_, _ = A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
+                    if w.rope_base:
+                        R.rope(dq_[:, None], pos[sl], w.rope_base, inverse=True)
+                        R.rope(dk_[:, None], pos[sl], w.rope_base, inverse=True)
             else:
                 A.seq_forward(q_, k_, v_, case.scale, w.causal)
                 A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
@@ -120,6 +130,57 @@ def cpu_baseline(case, variants, budget_s=15.0):
             "kind": "oracle",
             "sample": f"fp64 fwd+bwd of {units} random (sequence, head) units of the same batch "
                       f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+def compare_rope(case, w, q, k, v, do, run, dev, rounds):
+    """Rotary fused into the block kernels against (a) the plain block kernels on
+    the same batch, a lower bound, and (b) an unfused pipeline: the rotation of q
+    and k, and the backward rotation of dq and dk, as separate elementwise passes
+    in the common cos/sin-table form (x cos + rotate_half(x) sin, tables [T, 1, D]
+    in bf16) around the plain kernels. Interleaved round by round; medians."""
+    import torch
+    import variable_length_flash_jaggedfa_amd as jfa
+    plain = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, jfa.BLOCK_DIAG64, 0,
+                     device=dev)
+    D = w.head_dim
+    # positions inside the sequence, angles in float64, tables in bf16
+    off = case.offsets.astype(np.int64)
+    pos = np.concatenate([np.arange(e - s) for s, e in zip(off[:-1], off[1:])] or [np.zeros(0)])
+    ang = pos[:, None] * (w.rope_base ** (-np.arange(0, D, 2) / D))[None, :]
+    cos = torch.from_numpy(np.concatenate([np.cos(ang)] * 2, axis=1)[:, None]).to(dev, torch.bfloat16)
+    sin = torch.from_numpy(np.concatenate([np.sin(ang)] * 2, axis=1)[:, None]).to(dev, torch.bfloat16)
+
+    def rotate_half(x):
+        return torch.cat([-x[..., D // 2:], x[..., : D // 2]], dim=-1)
+
+    def rot(x, s):
+        return x * cos + rotate_half(x) * s
+
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    samples = {"fused": [], "plain": [], "unfused": []}
+    for _ in range(rounds):
+        for name in samples:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if name == "fused":
+                run["plan"].forward(q, k, v, out=o)
+                run["plan"].backward(q, k, v, o, do, dq=dq, dk=dk, dv=dv)
+            elif name == "plain":
+                plain.forward(q, k, v, out=o)
+                plain.backward(q, k, v, o, do, dq=dq, dk=dk, dv=dv)
+            else:
+                qr, kr = rot(q, sin), rot(k, sin)
+                plain.forward(qr, kr, v, out=o)
+                plain.backward(qr, kr, v, o, do, dq=dq, dk=dk, dv=dv)
+                rot(dq, -sin)
+                rot(dk, -sin)
+            e1.record()
+            torch.cuda.synchronize()
+            samples[name].append(e0.elapsed_time(e1))
+    res = {name: round(float(np.median(s)), 4) for name, s in samples.items()}
+    res["fused_over_plain"] = round(res["fused"] / res["plain"], 4)
+    res["unfused_over_fused"] = round(res["unfused"] / res["fused"], 4)
+    return res
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -170,10 +231,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
-                             "block64_d128", "imbalance", "gem_padded"])
+                             "block64_d128", "block64_rope_d64", "block64_rope_d128",
+                             "imbalance", "gem_padded"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time forward + backward under every dealing order, interleaved")
+    ap.add_argument("--compare-rope", action="store_true",
+                    help="rotary workloads: also time the plain block kernels on the same batch "
+                         "and an unfused pipeline (rotation by separate elementwise passes "
+                         "around the plain kernels), interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--digest", action="store_true",
@@ -222,7 +288,7 @@ def main():
         fl = flags_of(w, jfa)
         t0 = time.perf_counter()
         plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, fl, w.lq,
-                        order=order, device=dev)
+                        order=order, device=dev, rope_base=w.rope_base)
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
@@ -294,7 +360,7 @@ def main():
         w = r["w"]
         tag = w.name + ("_causal" if w.causal else "")
         if r["block"]:
-            tag = f"{w.name}_d{w.head_dim}"
+            tag = f"{w.name}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
             tb = T * w.num_heads * w.head_dim * 2
             cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
@@ -375,6 +441,10 @@ def main():
             compare[name]["beats_inorder_iqr"] = bool(
                 compare[name]["total_iqr"][1] < compare["inorder"]["total_iqr"][0])
 
+    rope_cmp = None
+    if args.compare_rope and w0.rope_base:
+        rope_cmp = compare_rope(case, w0, q, k, v, do, runs[0], dev, max(10, args.steps))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, variants)
@@ -402,6 +472,8 @@ def main():
     }
     if compare is not None:
         line["config"]["order_compare"] = compare
+    if rope_cmp is not None:
+        line["config"]["rope_compare"] = rope_cmp
     print(json.dumps(line), flush=True)
 
 

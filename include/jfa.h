@@ -11,6 +11,9 @@
  *   - 64-token block-diagonal attention, where each 64-token group attends only
  *     within itself, with a single-tile path that keeps no running statistics and
  *     stores no log-sum-exp ("TLX Block Attention", sections 1, 2 and 4);
+ *   - rotary position embeddings of Q and K applied inside the block-diagonal
+ *     kernels, so the rotated rows never travel through memory ("TLX Block
+ *     Attention", summary and the section on the memory-bandwidth bound);
  *   - a host scheduler that sorts tiles by KV work and deals them zigzag over the
  *     persistent workgroups ("Jagged Flash Attention for GEM", section on the
  *     GEM-specific optimisations).
@@ -26,6 +29,14 @@
  *               offsets: int32 [B + 1], offsets[0] = 0, non-decreasing.
  *   Maths       S = scale * Q K^T, P = softmax(S) per query row, out = P V.
  *               Causal: inside a sequence, query i attends keys j <= i.
+ *               Rotary: S = scale * rot(Q) rot(K)^T with the rows of Q and K
+ *               rotated by their token position p (index inside the sequence):
+ *               column pairs (i, i + D/2), i < D/2, turn by the angle
+ *               p * rope_base^(-2i/D), (x1, x2) -> (x1 cos a - x2 sin a,
+ *               x2 cos a + x1 sin a); V is not rotated, and dq, dk are the
+ *               gradients with respect to the unrotated q and k. The scores
+ *               depend only on position differences inside a 64-token group, so
+ *               the kernels count positions from the start of each group.
  *   Ownership   The caller allocates every host and device buffer (schedule arrays
  *               and workspace included). The library allocates nothing, keeps no
  *               pointer after a call returns, and enqueues work only on `stream`
@@ -58,6 +69,7 @@ typedef enum jfa_status {
 #define JFA_CAUSAL       1u  /* causal mask inside each sequence (jagged self-attention only) */
 #define JFA_BROADCAST_Q  2u  /* one dense Q [Lq,H,D] shared by every sequence (non-causal) */
 #define JFA_BLOCK_DIAG64 4u  /* 64-token block-diagonal self-attention (non-causal) */
+#define JFA_ROTARY       8u  /* rotary embeddings of Q and K (with BLOCK_DIAG64 only) */
 
 /* schedule kinds and dealing orders */
 #define JFA_KIND_FWD 0
@@ -76,10 +88,11 @@ typedef struct jfa_problem {
   int32_t head_dim;   /* D: 64 or 128 */
   int32_t max_len;    /* >= every sequence length (checked by jfa_schedule_count) */
   int32_t lq;         /* BROADCAST_Q: rows of the dense Q (>= 1); otherwise 0 */
-  uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 */
+  uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY */
   int64_t total_kv;   /* T = offsets[B], tokens in the packed K/V */
   float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
-  int32_t reserved;   /* must be 0 */
+  float rope_base;    /* ROTARY: base of the rotary frequencies, finite, in (1, 1e9];
+                         otherwise must be 0 */
 } jfa_problem;
 
 /* Rows of Q per forward tile (kind FWD) or of K/V per backward tile (kind BWD)

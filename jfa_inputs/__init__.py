@@ -66,6 +66,7 @@ class Workload:
     mix_long_hi: int = 0
     fixed_lengths: tuple = ()
     pad_to_max: bool = False          # every length replaced by the largest drawn
+    rope_base: float = 0.0            # block64: rotary embeddings with this base (0: none)
 
     @property
     def wid(self) -> int:
@@ -89,6 +90,11 @@ def standard_workloads():
                                 lo=1, hi=64),
         "block64_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block64", law="block64",
                                  lo=1, hi=64),
+        # the same batches with rotary embeddings fused in (same seeds and values)
+        "block64_rope_d64": Workload("block64", 1152, 4, 64, 1.0, kind="block64",
+                                     law="block64", lo=1, hi=64, rope_base=10000.0),
+        "block64_rope_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block64",
+                                      law="block64", lo=1, hi=64, rope_base=10000.0),
         "imbalance": Workload("imbalance", 2048, 16, 128, 0.5, law="mix", lo=8, hi=64,
                               mix_long_frac=0.05, mix_long_lo=8192, mix_long_hi=16384),
         "gem_padded": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
@@ -228,11 +234,11 @@ def make_case(w: Workload, with_do: bool = True) -> Case:
 
 
 def custom(lengths_, num_heads, head_dim, sigma=1.0, seed=0, kind="jagged", causal=False,
-           lq=0, name="custom") -> Workload:
+           lq=0, name="custom", rope_base=0.0) -> Workload:
     """A workload with explicitly given lengths (edge cases, small tests)."""
     L = tuple(int(x) for x in lengths_)
     return Workload(name, len(L), num_heads, head_dim, sigma, kind=kind, causal=causal,
-                    lq=lq, seed=seed, law="fixed", fixed_lengths=L)
+                    lq=lq, seed=seed, law="fixed", fixed_lengths=L, rope_base=rope_base)
 
 
 def to_torch_bf16(bits: np.ndarray):

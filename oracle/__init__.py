@@ -8,5 +8,6 @@ which holds no attention arithmetic.
 
   attention.py     exact softmax attention and its gradients, per sequence
   schedule_ref.py  the KV-work-sorted zigzag tile deal, in plain integers
+  rotary.py        block-diagonal attention of rotary-embedded queries and keys
 """
-from . import attention, schedule_ref  # noqa: F401
+from . import attention, rotary, schedule_ref  # noqa: F401

@@ -10,6 +10,7 @@ import numpy as np
 import jfa_inputs as J
 import variable_length_flash_jaggedfa_amd as jfa
 from oracle import attention as A
+from oracle import rotary as R
 
 OUT_TOL = 1e-2      # max |out - oracle|
 GRAD_TOL = 2e-2     # max |g - oracle| / max |oracle| for dq, dk, dv
@@ -29,6 +30,8 @@ def flags_of(w: J.Workload) -> int:
         f |= jfa.BROADCAST_Q
     if w.kind == "block64":
         f |= jfa.BLOCK_DIAG64
+    if w.rope_base:
+        f |= jfa.ROTARY
     return f
 
 
@@ -50,7 +53,8 @@ class GpuRun:
         self.case = case
         self.flags = flags_of(w)
         self.plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, self.flags,
-                             w.lq, order=order, num_slots=num_slots, device=dev)
+                             w.lq, order=order, num_slots=num_slots, device=dev,
+                             rope_base=w.rope_base)
         self.q = to_dev(case.q, dev)
         self.k = to_dev(case.k, dev)
         self.v = to_dev(case.v, dev)
@@ -80,6 +84,10 @@ def oracle_full(case: J.Case):
     if w.kind == "broadcast":
         out, lse = A.broadcast_forward(q, k, v, off, case.scale)
         dq, dk, dv = A.broadcast_backward(q, k, v, do, off, case.scale)
+    elif w.kind == "block64" and w.rope_base:
+        out = R.block_diag_rope_forward(q, k, v, off, case.scale, w.rope_base)
+        lse = None
+        dq, dk, dv = R.block_diag_rope_backward(q, k, v, do, off, case.scale, w.rope_base)
     elif w.kind == "block64":
         out = A.block_diag_forward(q, k, v, off, case.scale)
         lse = None

@@ -50,7 +50,14 @@ OFF = np.array([0, 10, 15], dtype=np.int32)
     (dict(num_heads=0), jfa.ERR_INVALID_ARG),
     (dict(scale=0.0), jfa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), jfa.ERR_INVALID_ARG),
-    (dict(flags=8), jfa.ERR_INVALID_ARG),
+    (dict(flags=16), jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.ROTARY, rope_base=10000.0), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64), jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64, rope_base=1.0),
+     jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64,
+          rope_base=float("inf")), jfa.ERR_INVALID_ARG),
+    (dict(rope_base=10000.0), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.CAUSAL | jfa.BROADCAST_Q, lq=4), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.CAUSAL), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BROADCAST_Q, lq=0), jfa.ERR_INVALID_ARG),
@@ -62,6 +69,12 @@ def test_schedule_count_rejects(kw, status):
     with pytest.raises(jfa.JfaError) as e:
         jfa.schedule_count(_p(**kw), OFF, jfa.KIND_FWD)
     assert e.value.status == status
+
+
+def test_rotary_block_problem_accepted():
+    p = _p(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64, rope_base=10000.0)
+    assert jfa.schedule_count(p, np.array([0, 64, 128], dtype=np.int32), jfa.KIND_FWD) == 2 * 2
+    assert jfa.bwd_workspace_bytes(p) == 0
 
 
 def test_offsets_checks():

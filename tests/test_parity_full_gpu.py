@@ -10,6 +10,7 @@ import pytest
 import jfa_inputs as J
 import variable_length_flash_jaggedfa_amd as jfa
 from oracle import attention as A
+from oracle import rotary as R
 from tests.gpu_common import (GRAD_TOL, LSE_TOL, OUT_TOL, GpuRun, bf16_to_f64, log, max_abs)
 
 pytestmark = pytest.mark.gpu
@@ -62,12 +63,19 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
                 got_o = bf16_to_f64(out[off[b]:off[b + 1], h])
                 got_l = lse[h, off[b]:off[b + 1]].cpu().numpy() if lse is not None else None
             if w.kind == "block64":
+                # rotary: rows rotated by their index in the sequence, gradients
+                # turned back afterwards
+                pos = np.arange(len(q_))
+                rot = (lambda x, inv=False: R.rope(x[:, None], pos, w.rope_base, inv)[:, 0]) \
+                    if w.rope_base else (lambda x, inv=False: x)
+                qr, kr = rot(q_), rot(k_)
                 o_ref = np.zeros_like(q_)
                 gq, gk, gv = np.zeros_like(q_), np.zeros_like(k_), np.zeros_like(v_)
                 for s0 in range(0, len(q_), 64):
                     sl = slice(s0, s0 + 64)
-                    o_ref[sl], _ = A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
-                    gq[sl], gk[sl], gv[sl] = A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
+                    o_ref[sl], _ = A.seq_forward(qr[sl], kr[sl], v_[sl], case.scale)
+                    gq[sl], gk[sl], gv[sl] = A.seq_backward(qr[sl], kr[sl], v_[sl], do_[sl], case.scale)
+                gq, gk = rot(gq, True), rot(gk, True)
                 l_ref = None
             else:
                 o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale, w.causal)
@@ -120,6 +128,11 @@ def test_block64_d64(gpu):
 
 def test_block64_d128(gpu):
     run_sampled("block64_d128", gpu, n_random=3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block64_rope(gpu, D):
+    run_sampled(f"block64_rope_d{D}", gpu, n_random=3)
 
 
 def test_imbalance(gpu):

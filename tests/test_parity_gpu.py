@@ -84,6 +84,24 @@ def test_block_diag(gpu, D):
     check_case(J.custom([64, 192, 128, 64 * 7], 2, D, seed=9, kind="block64"), gpu)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("base", [10000.0, 1.5, 1e9])
+def test_block_diag_rotary(gpu, D, base):
+    # base 1.5 turns every column pair by up to about 10 revolutions; 1e9 leaves the
+    # high columns nearly still
+    check_case(J.custom([64, 0, 192, 128, 64 * 7], 2, D, seed=9, kind="block64",
+                        rope_base=base), gpu)
+
+
+def test_block_diag_rotary_rows_are_not_plain_attention(gpu):
+    # the rotation is applied: rotary and plain block attention differ on the GPU
+    import torch
+    w = J.custom([128], 2, 64, seed=19, kind="block64")
+    o_plain, _ = GpuRun(J.make_case(w), gpu).forward()
+    o_rope, _ = GpuRun(J.make_case(w.with_(rope_base=10000.0)), gpu).forward()
+    assert not torch.equal(o_plain, o_rope)
+
+
 def test_single_long_sequence(gpu):
     check_case(J.custom([1000], 2, 128, sigma=0.5, seed=10), gpu)
     check_case(J.custom([1000], 2, 128, sigma=0.5, seed=10, causal=True), gpu)

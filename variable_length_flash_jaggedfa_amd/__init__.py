@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libjfa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-CAUSAL, BROADCAST_Q, BLOCK_DIAG64 = 1, 2, 4
+CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY = 1, 2, 4, 8
 KIND_FWD, KIND_BWD = 0, 1
 ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
@@ -39,7 +39,7 @@ class Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_len", ctypes.c_int32),
                 ("lq", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("total_kv", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float)]
 
 
 _lib = None
@@ -86,9 +86,10 @@ def _check(status: int):
         raise JfaError(status, lib().jfa_last_error().decode())
 
 
-def problem(num_seqs, num_heads, head_dim, max_len, total_kv, scale, flags=0, lq=0) -> Problem:
+def problem(num_seqs, num_heads, head_dim, max_len, total_kv, scale, flags=0, lq=0,
+            rope_base=0.0) -> Problem:
     return Problem(int(num_seqs), int(num_heads), int(head_dim), int(max_len), int(lq),
-                   int(flags), int(total_kv), float(scale), 0)
+                   int(flags), int(total_kv), float(scale), float(rope_base))
 
 
 def tile_rows(kind: int, head_dim: int, flags: int = 0) -> int:
@@ -180,7 +181,8 @@ class Schedule:
 class Plan:
     """Everything one jagged problem needs on the device, built once.
 
-    offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q.
+    offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q; rope_base
+    for ROTARY.
     Builds the FWD and BWD schedules on the host (folded zigzag by default: the
     work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired so
     that they run side by side), copies them
@@ -188,13 +190,13 @@ class Plan:
     """
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
-                 order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda"):
+                 order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda", rope_base=0.0):
         import torch
         off = _host_i32(offsets_host)
         L = np.diff(off.astype(np.int64))
         self.offsets_host = off
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
-                         int(off[-1]), scale, flags, lq)
+                         int(off[-1]), scale, flags, lq, rope_base)
         self.device = torch.device(device)
         self.offsets_dev = torch.from_numpy(off.copy()).to(self.device)
         self.block = bool(flags & BLOCK_DIAG64)

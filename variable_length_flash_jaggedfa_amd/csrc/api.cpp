@@ -79,7 +79,7 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   }
   FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
               p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
-              stream};
+              p->rope_base, stream};
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is stored)");
     if (p->total_kv == 0) return JFA_OK;
@@ -126,7 +126,8 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.kv_slot_ptr = kv_slot_ptr_dev; a.kv_tiles = kv_tiles_dev; a.kv_num_slots = kv_num_slots;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
-  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.passes = passes;
+  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.rope_base = p->rope_base;
+  a.passes = passes;
   a.stream = stream;
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is read)");

@@ -10,6 +10,13 @@
 // and 32 keys in the dK/dV phase. The kernels are bound by HBM traffic (the page
 // puts the arithmetic intensity far below the ridge point), so each unit reads
 // its operands once and writes its outputs once.
+//
+// With rotary embeddings (the page fuses them into these kernels) the rows of Q
+// and K are rotated inside the kernel after they arrive in LDS, and the backward
+// turns dQ and dK back before storing them, so the rotated rows never travel
+// through memory.
+#include <cmath>
+
 #include "jfa_internal.h"
 #include "jfa_tiles.h"
 
@@ -28,13 +35,85 @@ struct BlkCfg {
   static constexpr int TILE = kBS * D;  // one 64 x D tile
 };
 
+// Rotary angles. A row at position p has its column pair (i, i + D/2), i < D/2,
+// turned by p * theta_i with theta_i = base^(-2i/D). The scores and gradients
+// depend only on position differences, and two rows meet only inside one 64-token
+// group, so p counts from the start of the group (0..63): the same results as
+// positions counted from the start of the sequence, with small angles. Angles are
+// kept in revolutions, the unit of the hardware sine and cosine:
+// p * 2^(i * kr + kc) with kr = -2 log2(base) / D and kc = -log2(2 pi).
+struct Rope {
+  float kr, kc;
+};
+
 struct BlkParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* o; const uint16_t* dout;
   uint16_t* out; uint16_t* dq; uint16_t* dk; uint16_t* dv;
   int32_t H;
   float c;      // scale * log2(e)
   float scale;
+  Rope rope;    // rotary kernels only
 };
+
+__device__ __forceinline__ void rope_cs(float p, int i, const Rope& R, float& c, float& s) {
+  float rev = p * exp2_fast(float(i) * R.kr + R.kc);
+  rev -= rintf(rev);  // within half a revolution of zero
+  c = __builtin_amdgcn_cosf(rev);
+  s = __builtin_amdgcn_sinf(rev);
+}
+
+// Rotate the 64 rows of two swizzled 64 x D LDS tiles in place. Lane l takes row
+// l; the waves deal the 8-column chunks of the first half of a row between them,
+// each with its partner chunk D/2 columns on. Sixteen lanes read sixteen
+// consecutive rows at one logical chunk, the conflict-free pattern of the tiles.
+template <int D, int NW>
+__device__ __forceinline__ void rope_tiles(uint16_t* ta, uint16_t* tb, const Rope& R, int w, int lane) {
+  constexpr int CH = D / 16;
+  static_assert(CH % NW == 0, "chunks split evenly over the waves");
+  const float p = float(lane);
+#pragma unroll
+  for (int k = 0; k < CH / NW; ++k) {
+    const int c = w + k * NW;
+    float cs[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_cs(p, c * 8 + e, R, cs[e], sn[e]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint16_t* tile = t ? tb : ta;
+      uint16_t* pa = tile + Swz<D>::chunk(lane, c);
+      uint16_t* pb = tile + Swz<D>::chunk(lane, c + CH);
+      const u32x4 a = ld16(pa), b = ld16(pb);
+      u32x4 ya, yb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = bf16_lo(a[j]), a1 = bf16_hi(a[j]), b0 = bf16_lo(b[j]), b1 = bf16_hi(b[j]);
+        const float c0 = cs[2 * j], c1 = cs[2 * j + 1], s0 = sn[2 * j], s1 = sn[2 * j + 1];
+        ya[j] = pack_bf16(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+        yb[j] = pack_bf16(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+      }
+      st16(pa, ya);
+      st16(pb, yb);
+    }
+  }
+}
+
+// Turn gradients of rotated rows back (the transposed rotation) in an
+// accumulator set: tile nb holds columns nb*32 + (r/4)*8 + 4g + r%4 of this
+// lane's row at register r, so pair partners sit in tiles nb and nb + NB/2.
+template <int D>
+__device__ __forceinline__ void rope_back(f32x16 (&a)[D / 32], float p, int g, const Rope& R) {
+  constexpr int NB = D / 32;
+#pragma unroll
+  for (int nb = 0; nb < NB / 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float c, s;
+      rope_cs(p, nb * 32 + (r / 4) * 8 + 4 * g + (r % 4), R, c, s);
+      const float x1 = a[nb][r], x2 = a[nb + NB / 2][r];
+      a[nb][r] = x1 * c + x2 * s;
+      a[nb + NB / 2][r] = x2 * c - x1 * s;
+    }
+}
 
 // The (64-token block, head) unit of this workgroup. At D = 128 neighbouring
 // workgroups take the heads of one block (together they read whole contiguous
@@ -78,10 +157,11 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], float c) {
     for (int r = 0; r < 16; ++r) s[kb][r] *= inv;
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
-  // K, V, then the two waves' output staging tiles (32 x D each)
+  // K, V, then the two waves' output staging tiles (32 x D each; with ROPE they
+  // first hold the Q tile, wave w's half being its own 32 query rows)
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * C::TILE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
@@ -93,11 +173,22 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   tile_load<D, kBS, C::NW>(lds, rows_rsrc<D>(P.k + base, rstride, kBS), rowbytes, w, lane);
   tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D>(P.v + base, rstride, kBS), rowbytes, w, lane);
   u32x4 qf[C::DS];
-  const uint16_t* qrow = P.q + base + int64_t(w * 32 + li) * rstride;
+  if (ROPE) {
+    uint16_t* Qt = lds + 2 * C::TILE;
+    tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, kBS), rowbytes, w, lane);
+    wait_vmem();
+    __syncthreads();
+    rope_tiles<D, C::NW>(lds, Qt, P.rope, w, lane);
+    __syncthreads();
 #pragma unroll
-  for (int d = 0; d < C::DS; ++d) qf[d] = ld16(qrow + d * 16 + g * 8);
-  wait_vmem();
-  __syncthreads();
+    for (int d = 0; d < C::DS; ++d) qf[d] = frag_rows<D>(Qt, w * 32, d, li, g);
+  } else {
+    const uint16_t* qrow = P.q + base + int64_t(w * 32 + li) * rstride;
+#pragma unroll
+    for (int d = 0; d < C::DS; ++d) qf[d] = ld16(qrow + d * 16 + g * 8);
+    wait_vmem();
+    __syncthreads();
+  }
   // S^T = K Q^T for the 64 keys and this wave's 32 queries, fresh accumulators
   f32x16 s[2];
   s[0] = f32x16{};
@@ -124,7 +215,7 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
                 rstride, 32, lane);
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
   // K, V, Q, dO tiles (64 x D) and P^T, dS^T tiles (64 queries x 64 keys)
@@ -154,6 +245,11 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   for (int d = 0; d < C::DS; ++d) of[d] = ld16(orow + d * 16 + g * 8);
   wait_vmem();
   __syncthreads();
+  if (ROPE) {
+    // every product below then reads the rotated rows of Q and K
+    rope_tiles<D, C::NW>(Kt, Qt, P.rope, w, lane);
+    __syncthreads();
+  }
 
   // ---- query side (lane = query): S^T, dP^T, exact softmax, dS^T, dQ^T
   f32x16 s[2], dp[2];
@@ -206,6 +302,9 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
     for (int st = 0; st < 4; ++st) dqa[nb] = mfma32(frag_cols<D>(Kt, st * 16, nb * 32, lane), pds[st], dqa[nb]);
   }
   __syncthreads();
+  // dQ and dK of the rotated rows, turned back: row i of this lane is query i
+  // here and key i below, at the same position
+  if (ROPE) rope_back<D>(dqa, float(i), g, P.rope);
   // K and V are not read after this point: their tiles stage the outputs (each
   // wave a private 32 x D half of K for dQ, and of V for dV, then dK)
   store_rows<D>(Kt + w * (C::TILE / 2), dqa, P.scale, P.dq + base + int64_t(w * 32) * rstride, rstride,
@@ -231,7 +330,15 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   }
   uint16_t* vst = Vt + w * (C::TILE / 2);
   store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, 32, lane);
+  if (ROPE) rope_back<D>(ak, float(i), g, P.rope);
   store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, 32, lane);
+}
+
+Rope rope_consts(float base, int D) {
+  Rope R;
+  R.kr = float(-2.0 * std::log2(double(base)) / D);
+  R.kc = float(-std::log2(2.0 * M_PI));
+  return R;
 }
 
 template <int D>
@@ -244,10 +351,15 @@ jfa_status launch_fwd_t(const jfa::FwdLaunch& a) {
   P.H = a.num_heads;
   P.c = a.scale * kLog2e;
   P.scale = a.scale;
+  const bool rope = a.flags & JFA_ROTARY;
+  if (rope) P.rope = rope_consts(a.rope_base, D);
   const int64_t units = (a.total_kv / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
-  hipLaunchKernelGGL(block_fwd_kernel<D>, dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0,
-                     static_cast<hipStream_t>(a.stream), P);
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  if (rope)
+    hipLaunchKernelGGL((block_fwd_kernel<D, true>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
+  else
+    hipLaunchKernelGGL((block_fwd_kernel<D, false>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block fwd launch: ") + hipGetErrorString(e));
   return JFA_OK;
@@ -267,10 +379,15 @@ jfa_status launch_bwd_t(const jfa::BwdLaunch& a) {
   P.H = a.num_heads;
   P.c = a.scale * kLog2e;
   P.scale = a.scale;
+  const bool rope = a.flags & JFA_ROTARY;
+  if (rope) P.rope = rope_consts(a.rope_base, D);
   const int64_t units = (a.total_kv / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
-  hipLaunchKernelGGL(block_bwd_kernel<D>, dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0,
-                     static_cast<hipStream_t>(a.stream), P);
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  if (rope)
+    hipLaunchKernelGGL((block_bwd_kernel<D, true>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
+  else
+    hipLaunchKernelGGL((block_bwd_kernel<D, false>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block bwd launch: ") + hipGetErrorString(e));
   return JFA_OK;

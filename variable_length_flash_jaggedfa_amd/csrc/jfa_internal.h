@@ -34,6 +34,7 @@ struct FwdLaunch {
   int64_t total_kv;
   float scale;
   uint32_t flags;
+  float rope_base;  // ROTARY only
   void* stream;
 };
 
@@ -52,6 +53,7 @@ struct BwdLaunch {
   int64_t total_kv;
   float scale;
   uint32_t flags;
+  float rope_base;  // ROTARY only
   uint32_t passes;  // JFA_PASS_* mask
   void* stream;
 };

@@ -30,10 +30,9 @@ jfa_status check_problem(const jfa_problem* p) {
   if (p->num_heads < 1) return fail(JFA_ERR_INVALID_ARG, "num_heads < 1");
   if (p->max_len < 0) return fail(JFA_ERR_INVALID_ARG, "max_len < 0");
   if (p->total_kv < 0) return fail(JFA_ERR_INVALID_ARG, "total_kv < 0");
-  if (p->reserved != 0) return fail(JFA_ERR_INVALID_ARG, "reserved field must be 0");
   if (!(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(JFA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64;
+  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY;
   if (p->flags & ~known) return fail(JFA_ERR_INVALID_ARG, "unknown flag bits");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
@@ -41,6 +40,13 @@ jfa_status check_problem(const jfa_problem* p) {
              blk = p->flags & JFA_BLOCK_DIAG64;
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
   if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 with other flags");
+  if (p->flags & JFA_ROTARY) {
+    if (!blk) return fail(JFA_ERR_UNSUPPORTED, "ROTARY is implemented with BLOCK_DIAG64 only");
+    if (!(std::isfinite(p->rope_base) && p->rope_base > 1.f && p->rope_base <= 1e9f))
+      return fail(JFA_ERR_INVALID_ARG, "ROTARY needs rope_base finite and in (1, 1e9]");
+  } else if (p->rope_base != 0.f) {
+    return fail(JFA_ERR_INVALID_ARG, "rope_base must be 0 without ROTARY");
+  }
   if (bq && p->lq < 1) return fail(JFA_ERR_INVALID_ARG, "BROADCAST_Q needs lq >= 1");
   if (!bq && p->lq != 0) return fail(JFA_ERR_INVALID_ARG, "lq must be 0 without BROADCAST_Q");
   if (blk && (p->total_kv % kBlock))
