@@ -16,12 +16,14 @@ taken here, each the common form of rotary position embedding:
   * The position of a token is its index inside its own sequence.
   * The backward returns gradients with respect to the unrotated query and key
     rows: the gradients of the rotated rows, rotated back by the same angles.
+  * The same embedding applies to jagged self-attention (causal or not): the
+    attention of the rotated rows over the original offsets.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import block_diag_backward, block_diag_forward
+from .attention import block_diag_backward, block_diag_forward, jagged_backward, jagged_forward
 
 
 def rope_freqs(head_dim, base):
@@ -66,4 +68,18 @@ def block_diag_rope_backward(q, k, v, do, offsets, scale, base, block=64):
     pos = token_positions(offsets)
     dqr, dkr, dv = block_diag_backward(rope(q, pos, base), rope(k, pos, base), v, do, offsets,
                                        scale, block)
+    return rope(dqr, pos, base, inverse=True), rope(dkr, pos, base, inverse=True), dv
+
+
+def jagged_rope_forward(q, k, v, offsets, scale, base, causal=False):
+    """Jagged attention of the rotated queries and keys -> (out, lse)."""
+    pos = token_positions(offsets)
+    return jagged_forward(rope(q, pos, base), rope(k, pos, base), v, offsets, scale, causal)
+
+
+def jagged_rope_backward(q, k, v, do, offsets, scale, base, causal=False):
+    """(dq, dk, dv) with respect to the unrotated q and k."""
+    pos = token_positions(offsets)
+    dqr, dkr, dv = jagged_backward(rope(q, pos, base), rope(k, pos, base), v, do, offsets, scale,
+                                   causal)
     return rope(dqr, pos, base, inverse=True), rope(dkr, pos, base, inverse=True), dv

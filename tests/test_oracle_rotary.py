@@ -79,21 +79,31 @@ def test_token_positions():
     assert R.token_positions([0, 3, 3, 5]).tolist() == [0, 1, 2, 0, 1]
 
 
-def _sdpa_rope_autograd(q, k, v, do, off, scale, base):
+def _sdpa_rope_autograd(q, k, v, do, off, scale, base, mode="block"):
     """torch fp64: rows rotated in complex form, then SDPA with a mask keeping
-    pairs of one 64-token block; gradients by autograd."""
+    pairs of one 64-token block (mode "block"), of one sequence ("jagged") or of
+    one sequence with key <= query ("causal"); gradients by autograd."""
     T, H, D = q.shape
-    pos = torch.from_numpy(R.token_positions(off)).double()
+    pos_np = R.token_positions(off)
+    pos = torch.from_numpy(pos_np).double()
     theta = base ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
     rot = torch.polar(torch.ones(T, 1, D // 2, dtype=torch.float64), pos[:, None, None] * theta)
-    blk = torch.arange(T) // 64  # every sequence is a whole number of blocks
+    seg = torch.from_numpy(np.searchsorted(np.asarray(off), np.arange(T), side="right") - 1)
+    if mode == "block":
+        blk = torch.arange(T) // 64  # every sequence is a whole number of blocks
+        keep = blk[:, None] == blk[None, :]
+    else:
+        keep = seg[:, None] == seg[None, :]
+        if mode == "causal":
+            p_ = torch.from_numpy(pos_np)
+            keep &= p_[None, :] <= p_[:, None]
 
     def rotate(x):
         z = torch.complex(x[..., : D // 2], x[..., D // 2:]) * rot
         return torch.cat([z.real, z.imag], dim=-1)
 
     tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
-    mask = (blk[:, None] == blk[None, :])[None, None]
+    mask = keep[None, None]
     o = F.scaled_dot_product_attention(rotate(tq).transpose(0, 1)[None], rotate(tk).transpose(0, 1)[None],
                                        tv.transpose(0, 1)[None], attn_mask=mask, scale=scale)[0]
     o = o.transpose(0, 1)
@@ -142,3 +152,34 @@ def test_rotation_changes_the_result():
     a = A.block_diag_forward(q, k, v, off, sc)
     b = R.block_diag_rope_forward(q, k, v, off, sc, 10000.0)
     assert np.max(np.abs(a - b)) > 1e-3
+
+
+def jagged_case(lengths, H, D, seed=0):
+    w = J.custom(lengths, H, D, sigma=0.5, seed=seed)
+    c = J.make_case(w)
+    f = J.bf16_bits_to_f64
+    return f(c.q), f(c.k), f(c.v), f(c.do), c.offsets.astype(np.int64), c.scale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jagged_rope_matches_torch_autograd(causal):
+    q, k, v, do, off, sc = jagged_case([37, 0, 1, 150, 64], 2, 64, seed=8)
+    base = 10000.0
+    out, lse = R.jagged_rope_forward(q, k, v, off, sc, base, causal)
+    ref, rq, rk, rv = _sdpa_rope_autograd(q, k, v, do, off, sc, base,
+                                          "causal" if causal else "jagged")
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    dq, dk, dv = R.jagged_rope_backward(q, k, v, do, off, sc, base, causal)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.max(np.abs(a - b)) <= 1e-10
+
+
+def test_jagged_rope_long_positions_depend_on_differences_only():
+    # a sequence placed after another keeps its result: positions restart at every
+    # sequence, and a common shift of all positions would not change the scores
+    q, k, v, do, off, sc = jagged_case([300, 1000], 1, 64, seed=9)
+    out, lse = R.jagged_rope_forward(q, k, v, off, sc, 500.0, True)
+    s = 300
+    out1, lse1 = R.jagged_rope_forward(q[s:], k[s:], v[s:], np.array([0, 1000]), sc, 500.0, True)
+    assert np.max(np.abs(out[s:] - out1)) <= 1e-12
+    assert np.max(np.abs(lse[:, s:] - lse1)) <= 1e-12
