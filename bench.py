@@ -46,7 +46,7 @@ def pairs_of(lengths, causal=False, lq=0, block=0):
 
 def variants_of(name):
     wl = J.standard_workloads()
-    if name in ("gem", "gem_padded"):
+    if name in ("gem", "gem_padded", "gem_rope"):
         return [wl[name], wl[name + "_causal"]]
     return [wl[name]]
 
@@ -132,16 +132,20 @@ def cpu_baseline(case, variants, budget_s=15.0):
                       f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
 
 
-def compare_rope(case, w, q, k, v, do, run, dev, rounds):
-    """Rotary fused into the block kernels against (a) the plain block kernels on
-    the same batch, a lower bound, and (b) an unfused pipeline: the rotation of q
-    and k, and the backward rotation of dq and dk, as separate elementwise passes
-    in the common cos/sin-table form (x cos + rotate_half(x) sin, tables [T, 1, D]
-    in bf16) around the plain kernels. Interleaved round by round; medians."""
+def compare_rope(case, runs, q, k, v, do, dev, rounds, order):
+    """Rotary as the library runs it (fused into the block kernels; on the jagged
+    path a rotation pass plus the backward's epilogues) against (a) the plain
+    kernels on the same batch, a lower bound, and (b) an unfused pipeline: the
+    rotation of q and k, and the backward rotation of dq and dk, as separate
+    elementwise passes in the common cos/sin-table form (x cos + rotate_half(x) sin,
+    tables [T, 1, D] in bf16) around the plain kernels. Every variant of the
+    workload per sample; interleaved round by round; medians."""
     import torch
     import variable_length_flash_jaggedfa_amd as jfa
-    plain = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, jfa.BLOCK_DIAG64, 0,
-                     device=dev)
+    w = runs[0]["w"]
+    plains = [jfa.Plan(case.offsets, r["w"].num_heads, r["w"].head_dim, case.scale,
+                       flags_of(r["w"], jfa) & ~jfa.ROTARY, 0, order=order, device=dev)
+              for r in runs]
     D = w.head_dim
     # positions inside the sequence, angles in float64, tables in bf16
     off = case.offsets.astype(np.int64)
@@ -156,24 +160,26 @@ def compare_rope(case, w, q, k, v, do, run, dev, rounds):
     def rot(x, s):
         return x * cos + rotate_half(x) * s
 
-    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     samples = {"fused": [], "plain": [], "unfused": []}
     for _ in range(rounds):
         for name in samples:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            if name == "fused":
-                run["plan"].forward(q, k, v, out=o)
-                run["plan"].backward(q, k, v, o, do, dq=dq, dk=dk, dv=dv)
-            elif name == "plain":
-                plain.forward(q, k, v, out=o)
-                plain.backward(q, k, v, o, do, dq=dq, dk=dk, dv=dv)
-            else:
-                qr, kr = rot(q, sin), rot(k, sin)
-                plain.forward(qr, kr, v, out=o)
-                plain.backward(qr, kr, v, o, do, dq=dq, dk=dk, dv=dv)
-                rot(dq, -sin)
-                rot(dk, -sin)
+            for r, plain in zip(runs, plains):
+                o, lse = r["out"], r["lse"]
+                if name == "fused":
+                    r["plan"].forward(q, k, v, out=o, lse=lse)
+                    r["plan"].backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv)
+                elif name == "plain":
+                    plain.forward(q, k, v, out=o, lse=lse)
+                    plain.backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv)
+                else:
+                    qr, kr = rot(q, sin), rot(k, sin)
+                    plain.forward(qr, kr, v, out=o, lse=lse)
+                    plain.backward(qr, kr, v, o, do, lse, dq=dq, dk=dk, dv=dv)
+                    rot(dq, -sin)
+                    rot(dk, -sin)
             e1.record()
             torch.cuda.synchronize()
             samples[name].append(e0.elapsed_time(e1))
@@ -184,7 +190,8 @@ def compare_rope(case, w, q, k, v, do, run, dev, rounds):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip")
+KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip",
+                  "jfa_rope.h", "jfa_rope.hip")
 
 
 def kernel_source_digest():
@@ -231,7 +238,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
-                             "block64_d128", "block64_rope_d64", "block64_rope_d128",
+                             "block64_d128", "block64_rope_d64", "block64_rope_d128", "gem_rope",
                              "imbalance", "gem_padded"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
@@ -443,7 +450,7 @@ def main():
 
     rope_cmp = None
     if args.compare_rope and w0.rope_base:
-        rope_cmp = compare_rope(case, w0, q, k, v, do, runs[0], dev, max(10, args.steps))
+        rope_cmp = compare_rope(case, runs, q, k, v, do, dev, max(10, args.steps), order)
 
     cpu = None
     if not args.no_cpu_baseline:

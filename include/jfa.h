@@ -11,9 +11,12 @@
  *   - 64-token block-diagonal attention, where each 64-token group attends only
  *     within itself, with a single-tile path that keeps no running statistics and
  *     stores no log-sum-exp ("TLX Block Attention", sections 1, 2 and 4);
- *   - rotary position embeddings of Q and K applied inside the block-diagonal
- *     kernels, so the rotated rows never travel through memory ("TLX Block
- *     Attention", summary and the section on the memory-bandwidth bound);
+ *   - rotary position embeddings of Q and K ("TLX Block Attention", summary and
+ *     the section on the memory-bandwidth bound, where they are fused into the
+ *     attention kernels): inside the block-diagonal kernels the rotated rows never
+ *     travel through memory; on the jagged path one pass writes rotated copies of
+ *     q and k to the workspace and the backward turns dQ and dK back in its
+ *     epilogues;
  *   - a host scheduler that sorts tiles by KV work and deals them zigzag over the
  *     persistent workgroups ("Jagged Flash Attention for GEM", section on the
  *     GEM-specific optimisations).
@@ -35,8 +38,8 @@
  *               p * rope_base^(-2i/D), (x1, x2) -> (x1 cos a - x2 sin a,
  *               x2 cos a + x1 sin a); V is not rotated, and dq, dk are the
  *               gradients with respect to the unrotated q and k. The scores
- *               depend only on position differences inside a 64-token group, so
- *               the kernels count positions from the start of each group.
+ *               depend only on position differences, so the block-diagonal
+ *               kernels count positions from the start of each 64-token group.
  *   Ownership   The caller allocates every host and device buffer (schedule arrays
  *               and workspace included). The library allocates nothing, keeps no
  *               pointer after a call returns, and enqueues work only on `stream`
@@ -69,7 +72,7 @@ typedef enum jfa_status {
 #define JFA_CAUSAL       1u  /* causal mask inside each sequence (jagged self-attention only) */
 #define JFA_BROADCAST_Q  2u  /* one dense Q [Lq,H,D] shared by every sequence (non-causal) */
 #define JFA_BLOCK_DIAG64 4u  /* 64-token block-diagonal self-attention (non-causal) */
-#define JFA_ROTARY       8u  /* rotary embeddings of Q and K (with BLOCK_DIAG64 only) */
+#define JFA_ROTARY       8u  /* rotary embeddings of Q and K (not with BROADCAST_Q) */
 
 /* schedule kinds and dealing orders */
 #define JFA_KIND_FWD 0
@@ -151,8 +154,15 @@ jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32
  * lse, each rounded up to 256 bytes (-Di and -lse/scale, written by the dQ pass
  * and read by the dK/dV pass) and, for BROADCAST_Q, float32 dQ partials of
  * [G][Lq][H][D] where the B sequences are split into G = min(B, 64) contiguous
- * groups; 0 for BLOCK_DIAG64. */
+ * groups; for jagged ROTARY (without BLOCK_DIAG64) also two bf16 [T, H, D] regions,
+ * each rounded up to 256 bytes, for the rotated copies of q and k; 0 for
+ * BLOCK_DIAG64. 0 for an invalid problem. */
 size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
+
+/* Bytes of device workspace jfa_fwd needs: for jagged ROTARY (without
+ * BLOCK_DIAG64) two bf16 [T, H, D] regions, each rounded up to 256 bytes, that
+ * receive the rotated copies of q and k; 0 otherwise and for an invalid problem. */
+size_t jfa_fwd_workspace_bytes(const jfa_problem* p);
 
 /* Forward ("TLX Block Attention", section 2: the online-softmax loop; section 3,
  * pipeline order load -> Q K^T -> exp2 softmax -> P V -> epilogue).
@@ -162,13 +172,16 @@ size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
  *                (ignored, may be NULL, for BLOCK_DIAG64).
  *   out          device, bf16, written for every valid query row.
  *   lse          device float32; must be NULL for BLOCK_DIAG64, non-NULL otherwise.
+ *   workspace    device, >= jfa_fwd_workspace_bytes(p) bytes, 256-byte aligned;
+ *                contents on entry are ignored and clobbered (jagged ROTARY: the
+ *                rotated q and k). May be NULL when the size is 0.
  * A broadcast-Q sequence with no keys gets out = 0 and lse = -inf.
  * Precondition (not checked on the device): offsets_dev equals the host offsets
  * the schedule was built from. */
 jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
                    const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
                    const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward ("TLX Block Attention", sections 2 and 4; "Jagged Flash Attention for
  * GEM", backward / dQ section): P is rebuilt from Q, K and lse, Di = rowsum(dO*out)
@@ -204,8 +217,9 @@ jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const voi
 /* jfa_bwd restricted to some of its passes, so that each can be timed or
  * overlapped on its own. Same arguments as jfa_bwd plus `passes`, a non-zero
  * mask of JFA_PASS_*. JFA_PASS_DKDV alone is valid only after a JFA_PASS_DQ call
- * with the same problem, inputs and workspace on the same stream (it reads the Di
- * that pass left in the workspace); the library cannot check this. BLOCK_DIAG64
+ * with the same problem, inputs and workspace on the same stream (it reads the Di,
+ * and for jagged ROTARY the rotated q and k, that pass left in the workspace); the
+ * library cannot check this. BLOCK_DIAG64
  * runs one fused kernel and accepts JFA_PASS_ALL only (JFA_ERR_INVALID_ARG
  * otherwise). jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
 jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, const void* v,

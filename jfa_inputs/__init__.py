@@ -99,6 +99,11 @@ def standard_workloads():
                               mix_long_frac=0.05, mix_long_lo=8192, mix_long_hi=16384),
         "gem_padded": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
                                hi=4096, pad_to_max=True),
+        # the gem batches with rotary embeddings (same seeds and values)
+        "gem_rope": Workload("gem", 256, 8, 128, 0.5, law="loguniform", lo=16, hi=4096,
+                             rope_base=10000.0),
+        "gem_rope_causal": Workload("gem", 256, 8, 128, 0.5, law="loguniform", lo=16, hi=4096,
+                                    causal=True, rope_base=10000.0),
         "gem_padded_causal": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
                                       hi=4096, pad_to_max=True, causal=True),
     }

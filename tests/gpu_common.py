@@ -15,6 +15,15 @@ from oracle import rotary as R
 OUT_TOL = 1e-2      # max |out - oracle|
 GRAD_TOL = 2e-2     # max |g - oracle| / max |oracle| for dq, dk, dv
 LSE_TOL = 1e-3      # max |lse - oracle|
+# With rotary embeddings the kernels multiply the rotated rows of Q and K, which
+# are rounded to bf16 (the matrix cores take bf16 operands) where the oracle keeps
+# them exact: each score moves by up to ~2^-8 * scale * |q| |k|, on the order of
+# 1e-3 for the unit-variance rows of the tests, so the lse check gets twice the room.
+LSE_TOL_ROPE = 2e-3
+
+
+def lse_tol(w) -> float:
+    return LSE_TOL_ROPE if w.rope_base else LSE_TOL
 
 
 def log(msg):
@@ -92,6 +101,9 @@ def oracle_full(case: J.Case):
         out = A.block_diag_forward(q, k, v, off, case.scale)
         lse = None
         dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale)
+    elif w.rope_base:
+        out, lse = R.jagged_rope_forward(q, k, v, off, case.scale, w.rope_base, w.causal)
+        dq, dk, dv = R.jagged_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.causal)
     else:
         out, lse = A.jagged_forward(q, k, v, off, case.scale, w.causal)
         dq, dk, dv = A.jagged_backward(q, k, v, do, off, case.scale, w.causal)
@@ -114,12 +126,12 @@ def assert_out(got, ref, what="out"):
     assert e <= OUT_TOL, (what, e)
 
 
-def assert_lse(got, ref):
+def assert_lse(got, ref, tol=LSE_TOL):
     fin = np.isfinite(ref)
     assert np.array_equal(np.isfinite(got), fin)
     e = max_abs(got[fin], ref[fin])
-    log(f"  lse: max abs err {e:.3e} (tol {LSE_TOL})")
-    assert e <= LSE_TOL
+    log(f"  lse: max abs err {e:.3e} (tol {tol})")
+    assert e <= tol
 
 
 def assert_grad(got, ref, what):

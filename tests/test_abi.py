@@ -51,7 +51,8 @@ OFF = np.array([0, 10, 15], dtype=np.int32)
     (dict(scale=0.0), jfa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), jfa.ERR_INVALID_ARG),
     (dict(flags=16), jfa.ERR_INVALID_ARG),
-    (dict(flags=jfa.ROTARY, rope_base=10000.0), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.ROTARY | jfa.BROADCAST_Q, lq=4, rope_base=10000.0), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.ROTARY), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64, rope_base=1.0),
      jfa.ERR_INVALID_ARG),
@@ -95,20 +96,27 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
     nul = None
     fake = 4096  # aligned non-null fake address: never dereferenced on these paths
     # NULL q
-    s = L.jfa_fwd(ctypes.byref(p), nul, fake, fake, fake, fake, fake, 4, fake, fake, None)
+    s = L.jfa_fwd(ctypes.byref(p), nul, fake, fake, fake, fake, fake, 4, fake, fake, nul, 0, None)
     assert s == jfa.ERR_INVALID_ARG
     # misaligned k
-    s = L.jfa_fwd(ctypes.byref(p), fake, fake + 2, fake, fake, fake, fake, 4, fake, fake, None)
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake + 2, fake, fake, fake, fake, 4, fake, fake, nul, 0, None)
     assert s == jfa.ERR_INVALID_ARG and b"aligned" in L.jfa_last_error()
     # missing lse
-    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 4, fake, nul, None)
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 4, fake, nul, nul, 0, None)
     assert s == jfa.ERR_INVALID_ARG
     # zero slots
-    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 0, fake, fake, None)
+    s = L.jfa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 0, fake, fake, nul, 0, None)
     assert s == jfa.ERR_INVALID_ARG
+    # jagged rotary without its workspace
+    pr = _p(flags=jfa.ROTARY, rope_base=10000.0)
+    s = L.jfa_fwd(ctypes.byref(pr), fake, fake, fake, fake, fake, fake, 4, fake, fake, nul, 0, None)
+    assert s == jfa.ERR_WORKSPACE
+    s = L.jfa_fwd(ctypes.byref(pr), fake, fake, fake, fake, fake, fake, 4, fake, fake, fake + 16,
+                  1 << 20, None)
+    assert s == jfa.ERR_INVALID_ARG and b"256-byte" in L.jfa_last_error()
     # block-diagonal with an lse pointer
     pb = _p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)
-    s = L.jfa_fwd(ctypes.byref(pb), fake, fake, fake, nul, nul, nul, 0, fake, fake, None)
+    s = L.jfa_fwd(ctypes.byref(pb), fake, fake, fake, nul, nul, nul, 0, fake, fake, nul, 0, None)
     assert s == jfa.ERR_INVALID_ARG
     # backward: workspace too small
     s = L.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, 4,
@@ -132,7 +140,7 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
     assert s == jfa.ERR_INVALID_ARG and b"BLOCK_DIAG64" in L.jfa_last_error()
     # empty problems are no-ops that touch nothing
     p0 = _p(num_seqs=0, total_kv=0, max_len=0)
-    assert L.jfa_fwd(ctypes.byref(p0), nul, nul, nul, nul, nul, nul, 0, nul, nul, None) == jfa.OK
+    assert L.jfa_fwd(ctypes.byref(p0), nul, nul, nul, nul, nul, nul, 0, nul, nul, nul, 0, None) == jfa.OK
 
 
 def test_workspace_bytes():
@@ -143,6 +151,14 @@ def test_workspace_bytes():
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == \
         2 * r256(2 * 2 * 7 * 4) + 2 * 7 * 2 * 64 * 4
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)) == 0
+    # jagged rotary: two rotated bf16 [T, H, D] copies (q and k) in both workspaces
+    pr = _p(flags=jfa.ROTARY, rope_base=10000.0)
+    rot = r256(15 * 2 * 64 * 2)
+    assert jfa.fwd_workspace_bytes(pr) == 2 * rot
+    assert jfa.bwd_workspace_bytes(pr) == 2 * r256(2 * 15 * 4) + 2 * rot
+    assert jfa.fwd_workspace_bytes(_p()) == 0
+    pbr = _p(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64, rope_base=10000.0)
+    assert jfa.fwd_workspace_bytes(pbr) == 0 and jfa.bwd_workspace_bytes(pbr) == 0
 
 
 def test_tile_rows():

@@ -11,7 +11,8 @@ import jfa_inputs as J
 import variable_length_flash_jaggedfa_amd as jfa
 from oracle import attention as A
 from oracle import rotary as R
-from tests.gpu_common import (GRAD_TOL, LSE_TOL, OUT_TOL, GpuRun, bf16_to_f64, log, max_abs)
+from tests.gpu_common import (GRAD_TOL, LSE_TOL, OUT_TOL, GpuRun, bf16_to_f64, log, lse_tol,
+                              max_abs)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +63,12 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
                 do_ = _seq_slice(case.do, off, b, h)
                 got_o = bf16_to_f64(out[off[b]:off[b + 1], h])
                 got_l = lse[h, off[b]:off[b + 1]].cpu().numpy() if lse is not None else None
+            # rotary: rows rotated by their index in the sequence, gradients turned
+            # back afterwards
+            pos = np.arange(len(k_))
+            rot = (lambda x, inv=False: R.rope(x[:, None], pos, w.rope_base, inv)[:, 0]) \
+                if w.rope_base else (lambda x, inv=False: x)
             if w.kind == "block64":
-                # rotary: rows rotated by their index in the sequence, gradients
-                # turned back afterwards
-                pos = np.arange(len(q_))
-                rot = (lambda x, inv=False: R.rope(x[:, None], pos, w.rope_base, inv)[:, 0]) \
-                    if w.rope_base else (lambda x, inv=False: x)
                 qr, kr = rot(q_), rot(k_)
                 o_ref = np.zeros_like(q_)
                 gq, gk, gv = np.zeros_like(q_), np.zeros_like(k_), np.zeros_like(v_)
@@ -77,6 +78,10 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
                     gq[sl], gk[sl], gv[sl] = A.seq_backward(qr[sl], kr[sl], v_[sl], do_[sl], case.scale)
                 gq, gk = rot(gq, True), rot(gk, True)
                 l_ref = None
+            elif w.rope_base:
+                o_ref, l_ref = A.seq_forward(rot(q_), rot(k_), v_, case.scale, w.causal)
+                gq, gk, gv = A.seq_backward(rot(q_), rot(k_), v_, do_, case.scale, w.causal)
+                gq, gk = rot(gq, True), rot(gk, True)
             else:
                 o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale, w.causal)
                 gq, gk, gv = A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
@@ -105,7 +110,7 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
     log(f"  out {errs['out']:.3e} lse {errs['lse']:.3e} "
         + " ".join(f"{k} {errs[k] / refmax[k]:.3e}" for k in ("dq", "dk", "dv")))
     assert errs["out"] <= OUT_TOL
-    assert errs["lse"] <= LSE_TOL
+    assert errs["lse"] <= lse_tol(w)
     for k in ("dq", "dk", "dv"):
         assert errs[k] <= GRAD_TOL * refmax[k], k
 
@@ -116,6 +121,11 @@ def test_gem_noncausal(gpu):
 
 def test_gem_causal(gpu):
     run_sampled("gem_causal", gpu)
+
+
+@pytest.mark.parametrize("name", ["gem_rope", "gem_rope_causal"])
+def test_gem_rope(gpu, name):
+    run_sampled(name, gpu)
 
 
 def test_broadcast(gpu):

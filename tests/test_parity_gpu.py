@@ -9,7 +9,7 @@ import jfa_inputs as J
 import variable_length_flash_jaggedfa_amd as jfa
 from oracle import attention as A
 from tests.gpu_common import (GpuRun, assert_grad, assert_lse, assert_out, bf16_to_f64, log,
-                              oracle_full)
+                              lse_tol, oracle_full)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def check_case(w, dev, order=jfa.ORDER_FOLDED_ZIGZAG, num_slots=None, bwd=True):
     ref = oracle_full(case)
     assert_out(bf16_to_f64(out), ref[0])
     if lse is not None:
-        assert_lse(lse.cpu().numpy().astype(np.float64), ref[1])
+        assert_lse(lse.cpu().numpy().astype(np.float64), ref[1], lse_tol(w))
     if bwd:
         dq, dk, dv = run.backward()
         for name, g, r in (("dq", dq, ref[2]), ("dk", dk, ref[3]), ("dv", dv, ref[4])):
@@ -90,6 +90,19 @@ def test_block_diag_rotary(gpu, D, base):
     # base 1.5 turns every column pair by up to about 10 revolutions; 1e9 leaves the
     # high columns nearly still
     check_case(J.custom([64, 0, 192, 128, 64 * 7], 2, D, seed=9, kind="block64",
+                        rope_base=base), gpu)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jagged_rotary(gpu, D, causal):
+    check_case(J.custom(RAGGED, 3, D, sigma=0.5, seed=21, causal=causal, rope_base=10000.0), gpu)
+
+
+@pytest.mark.parametrize("base", [10000.0, 1.5])
+def test_jagged_rotary_long_positions(gpu, base):
+    # positions up to 4999: the angles of the lowest frequencies reach ~800 turns
+    check_case(J.custom([5000, 3, 0, 700], 1, 128, sigma=0.5, seed=22, causal=True,
                         rope_base=base), gpu)
 
 
@@ -209,7 +222,9 @@ def test_backward_passes_match_fused_call(gpu):
     """jfa_bwd_passes(DQ) then (DKDV) gives the bits of one jfa_bwd call."""
     import torch
     for w in (J.custom(RAGGED, 2, 128, sigma=0.5, seed=17, causal=True),
-              J.custom([50, 0, 300, 129], 2, 64, sigma=0.5, seed=17, kind="broadcast", lq=130)):
+              J.custom([50, 0, 300, 129], 2, 64, sigma=0.5, seed=17, kind="broadcast", lq=130),
+              # rotary: the dK/dV pass reads the rotated rows the dQ pass left behind
+              J.custom(RAGGED, 2, 64, sigma=0.5, seed=17, rope_base=10000.0)):
         log(f"case passes {w.kind} causal={w.causal} D={w.head_dim}")
         run = GpuRun(J.make_case(w), gpu)
         run.forward()

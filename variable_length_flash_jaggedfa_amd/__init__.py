@@ -65,7 +65,9 @@ def lib():
         L.jfa_schedule.restype = i32
         L.jfa_bwd_workspace_bytes.argtypes = [P]
         L.jfa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.jfa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.jfa_fwd_workspace_bytes.argtypes = [P]
+        L.jfa_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.jfa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.jfa_fwd.restype = i32
         L.jfa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                               vp, vp, ctypes.c_size_t, vp]
@@ -129,6 +131,14 @@ def bwd_workspace_bytes(p: Problem) -> int:
     return int(lib().jfa_bwd_workspace_bytes(ctypes.byref(p)))
 
 
+def fwd_workspace_bytes(p: Problem) -> int:
+    return int(lib().jfa_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def _ws_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -140,16 +150,16 @@ def _stream(stream) -> Optional[int]:
 
 
 def fwd(p: Problem, q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
-        stream=None):
+        workspace=None, stream=None):
     _check(lib().jfa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets_dev),
                          _ptr(slot_ptr_dev), _ptr(tiles_dev), int(num_slots), _ptr(out),
-                         _ptr(lse), _stream(stream)))
+                         _ptr(lse), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
         q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv, workspace,
         stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _check(lib().jfa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                          _ptr(lse), _ptr(offsets_dev), _ptr(q_slot_ptr_dev), _ptr(q_tiles_dev),
                          int(q_num_slots), _ptr(kv_slot_ptr_dev), _ptr(kv_tiles_dev),
@@ -160,7 +170,7 @@ def bwd(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tile
 def bwd_passes(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
                q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv, workspace,
                passes, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _check(lib().jfa_bwd_passes(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                 _ptr(dout), _ptr(lse), _ptr(offsets_dev), _ptr(q_slot_ptr_dev),
                                 _ptr(q_tiles_dev), int(q_num_slots), _ptr(kv_slot_ptr_dev),
@@ -215,6 +225,9 @@ class Plan:
         nbytes = bwd_workspace_bytes(self.p)
         self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=self.device)
                           if nbytes else None)
+        nbytes = fwd_workspace_bytes(self.p)
+        self.fwd_workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32,
+                                          device=self.device) if nbytes else None)
 
     @property
     def num_q_rows(self):
@@ -241,7 +254,7 @@ class Plan:
         s = self.sched.get(KIND_FWD)
         fwd(self.p, q, k, v, self.offsets_dev, s.slot_ptr_dev if s else None,
             s.tiles_dev if s else None, s.num_slots if s else 0, out,
-            None if self.block else lse, stream)
+            None if self.block else lse, self.fwd_workspace, stream)
         return out, (None if self.block else lse)
 
     def backward(self, q, k, v, out, dout, lse=None, dq=None, dk=None, dv=None, stream=None,

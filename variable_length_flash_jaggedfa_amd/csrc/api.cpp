@@ -36,6 +36,26 @@ jfa_status check_schedule_args(const jfa_problem* p, const int32_t* offsets, con
   return JFA_OK;
 }
 
+jfa_status check_workspace(void* workspace, size_t workspace_bytes, size_t ws) {
+  if (ws == 0) return JFA_OK;
+  if (!workspace || workspace_bytes < ws)
+    return fail(JFA_ERR_WORKSPACE, "workspace needs " + std::to_string(ws) + " bytes, got " +
+                                       std::to_string(workspace_bytes));
+  if (!aligned(workspace, 256)) return fail(JFA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return JFA_OK;
+}
+
+// Jagged ROTARY: rotated copies of q and k into `rot` (two rot_bytes regions),
+// walking the forward schedule given.
+jfa_status rotate_qk(const jfa_problem* p, const void* q, const void* k, char* rot,
+                     const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                     const int32_t* tiles_dev, int32_t num_slots, void* stream) {
+  RopeRowsLaunch r{q, k, rot, rot + rot_bytes(p), offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
+                   p->num_seqs, p->num_heads, p->head_dim, p->total_kv,
+                   rope_table(p->rope_base, p->head_dim), stream};
+  return launch_rope_rows(r);
+}
+
 }  // namespace
 
 extern "C" jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t flags,
@@ -64,7 +84,7 @@ extern "C" jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t
 extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
                               const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
                               const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   set_error("");
   if (jfa_status s = check_problem(p)) return s;
   const bool blk = p->flags & JFA_BLOCK_DIAG64;
@@ -87,6 +107,14 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   }
   if (jfa_status s = need(lse, "lse", 4)) return s;
   if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
+  if (jfa_status s = check_workspace(workspace, workspace_bytes, jfa_fwd_workspace_bytes(p))) return s;
+  if (rot_bytes(p) > 0 && p->total_kv > 0) {
+    char* rot = static_cast<char*>(workspace);
+    if (jfa_status s = rotate_qk(p, q, k, rot, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, stream))
+      return s;
+    a.q = rot;
+    a.k = rot + rot_bytes(p);
+  }
   return launch_fwd(a);
 }
 
@@ -136,13 +164,7 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   }
   if (q_rows(p) > 0 && !lse) return fail(JFA_ERR_INVALID_ARG, "lse is NULL");
   if (lse && !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
-  const size_t ws = jfa_bwd_workspace_bytes(p);
-  if (ws > 0) {
-    if (!workspace || workspace_bytes < ws)
-      return fail(JFA_ERR_WORKSPACE, "workspace needs " + std::to_string(ws) + " bytes, got " +
-                                         std::to_string(workspace_bytes));
-    if (!aligned(workspace, 256)) return fail(JFA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  }
+  if (jfa_status s = check_workspace(workspace, workspace_bytes, jfa_bwd_workspace_bytes(p))) return s;
   if (p->total_kv > 0) {
     if (jfa_status s = check_schedule_args(p, offsets_dev, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots))
       return s;
@@ -158,6 +180,21 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.nls = reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p));
   a.groups = bcast_groups(p->num_seqs);
   a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * di_bytes(p)) : nullptr;
+  RopeTab tab;
+  if (rot_bytes(p) > 0 && p->total_kv > 0) {
+    // the dQ pass rotates q and k into the workspace; the dK/dV pass reads the
+    // copies it left there
+    char* rot = static_cast<char*>(workspace) + 2 * di_bytes(p);
+    if (passes & JFA_PASS_DQ) {
+      if (jfa_status s = rotate_qk(p, q, k, rot, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+                                   q_num_slots, stream))
+        return s;
+    }
+    tab = rope_table(p->rope_base, p->head_dim);
+    a.q = rot;
+    a.k = rot + rot_bytes(p);
+    a.rope = &tab;
+  }
   return launch_bwd(a);
 }
 

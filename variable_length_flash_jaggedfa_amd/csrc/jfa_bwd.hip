@@ -22,9 +22,14 @@
 // workgroup a (query tile, head, group of sequences), accumulates on chip over
 // the group, stores one float32 partial per group, and a last kernel sums the
 // partials in a fixed order.
+//
+// With rotary embeddings the passes read rotated copies of Q and K and turn dQ
+// (dQ pass) and dK (dK/dV pass) back to the unrotated rows in registers just
+// before their rows are stored.
 #include <type_traits>
 
 #include "jfa_internal.h"
+#include "jfa_rope.h"
 #include "jfa_tiles.h"
 
 using namespace jfa_dev;
@@ -63,6 +68,7 @@ struct DqParams {
   float* dq_part;             // broadcast: [groups][Lq][H][D] float32 partials
   int32_t H, lq, total_kv, num_seqs, groups;
   float c, scale;
+  jfa::RopeTab rope;          // rotary kernels only
 };
 
 // S^T = K Q^T and dP^T = V dO^T for one step of BN keys (lane = query row).
@@ -227,14 +233,17 @@ __device__ __forceinline__ float load_row(const uint16_t* qrow, const uint16_t* 
   return pair_sum(di);  // Di = rowsum(dO * out)
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool ROPE>
 __global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dq_kernel(DqParams P) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+  __shared__ double rope_tab[ROPE ? D / 2 : 1];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
   const LaneOffsets<D> lo(lane);
+  // the main loop's barriers order this copy before the first epilogue reads it
+  if (ROPE && tid < D / 2) rope_tab[tid] = P.rope.rev[tid];
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
@@ -267,6 +276,7 @@ dq_kernel(DqParams P) {
                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, n_keys, n_free,
                          qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
     // dq_stream ended with a barrier: the ring is free to stage the output rows
+    if (ROPE) rope_back_rows<D>(acc, qpos, g, rope_tab);
     const int row0 = q_first + w * 32;
     store_rows<D>(lds + w * 32 * D, acc, P.scale,
                   P.dq + (int64_t(kv0) + row0) * rstride + int64_t(h) * D, rstride, L - row0, lane);
@@ -373,6 +383,7 @@ struct KvParams {
   uint16_t* dk; uint16_t* dv;
   int32_t H, lq, total_kv;
   float c, scale;
+  jfa::RopeTab rope;  // rotary kernels only
 };
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_rw_t;
@@ -500,7 +511,7 @@ __device__ __forceinline__ void xch_get(const KvAddr<D>& a, u32x4 (&pp)[KvCfg<D>
     pp[x] = lds_ld16(a.xch + uint32_t((S * C::NP * C::PK + x) * 64 * 16));
 }
 
-template <int D, bool CAUSAL, bool BCAST>
+template <int D, bool CAUSAL, bool BCAST, bool ROPE>
 __global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
@@ -509,8 +520,11 @@ dkdv_kernel(KvParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * C::NS * C::TILE];
   __shared__ __attribute__((aligned(16))) float vecs[C::NS][2][C::BM];  // -lse/scale, -Di per stage
   __shared__ u32x4 xch[C::NS][C::NP][C::PK * 64];  // packed P per stage and pair
+  __shared__ double rope_tab[ROPE ? D / 2 : 1];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
+  // the main loop's barriers order this copy before the first epilogue reads it
+  if (ROPE && tid < D / 2) rope_tab[tid] = P.rope.rev[tid];
   const bool pwave = w < C::NP;
   const int kw = pwave ? w : w - C::NP;  // 32-key block of the pair
   const int slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -690,6 +704,7 @@ dkdv_kernel(KvParams P) {
       // tile's first barrier orders these reads before its loads of stage 1. The
       // stores are counted (no other vector memory operation follows them before
       // the next tile's first wait), so that wait need not drain them.
+      if (ROPE && !PW) rope_back_rows<D>(acc, row0 + li, g, rope_tab);  // dK of the rotated keys
       uint16_t* stg = ring + ((PW ? 0 : C::NS) + 1 + kw / 2) * C::TILE + (kw % 2) * 32 * D;
       const int64_t e0 = (int64_t(Tc.kv0) + row0) * rstride + int64_t(Tc.h) * D;
       store_rows_counted<D>(stg, acc, PW ? 1.f : P.scale, (PW ? P.dv : P.dk) + e0, rstride,
@@ -705,7 +720,7 @@ int grid_for(int64_t n4) {
   return int(g < 8192 ? (g > 0 ? g : 1) : 8192);
 }
 
-template <int D, bool CAUSAL, bool BCAST>
+template <int D, bool CAUSAL, bool BCAST, bool ROPE>
 jfa_status launch_t(const jfa::BwdLaunch& a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float c = a.scale * kLog2e;
@@ -730,6 +745,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   dp.groups = a.groups;
   dp.c = c;
   dp.scale = a.scale;
+  if (ROPE) dp.rope = *a.rope;
   const bool run_dq = a.passes & JFA_PASS_DQ, run_kv = a.passes & JFA_PASS_DKDV;
   if (!run_dq) {
   } else if (BCAST) {
@@ -740,7 +756,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     hipLaunchKernelGGL(dq_reduce_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_part,
                        static_cast<uint16_t*>(a.dq), n4, a.groups, a.scale);
   } else if (a.total_kv > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st, dp);
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, ROPE>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st, dp);
   }
   if (run_kv && a.total_kv > 0) {
     KvParams kp{};
@@ -760,8 +776,9 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     kp.total_kv = int32_t(a.total_kv);
     kp.c = c;
     kp.scale = a.scale;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST>), dim3(a.kv_num_slots), dim3(KvCfg<D>::NT), 0,
-                       st, kp);
+    if (ROPE) kp.rope = *a.rope;
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST, ROPE>), dim3(a.kv_num_slots), dim3(KvCfg<D>::NT),
+                       0, st, kp);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("bwd launch: ") + hipGetErrorString(e));
@@ -771,8 +788,8 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
 template <int D, bool CAUSAL, bool BCAST>
 int occupancy_kv() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_kernel<D, CAUSAL, BCAST>, KvCfg<D>::NT,
-                                                   0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_kernel<D, CAUSAL, BCAST, false>,
+                                                   KvCfg<D>::NT, 0) != hipSuccess)
     return 0;
   return n;
 }
@@ -782,13 +799,15 @@ int occupancy_kv() {
 namespace jfa {
 
 jfa_status launch_bwd(const BwdLaunch& a) {
-  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q;
+  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, rope = a.rope != nullptr;
   if (a.head_dim == 128) {
-    if (bq) return launch_t<128, false, true>(a);
-    return causal ? launch_t<128, true, false>(a) : launch_t<128, false, false>(a);
+    if (bq) return launch_t<128, false, true, false>(a);
+    if (rope) return causal ? launch_t<128, true, false, true>(a) : launch_t<128, false, false, true>(a);
+    return causal ? launch_t<128, true, false, false>(a) : launch_t<128, false, false, false>(a);
   }
-  if (bq) return launch_t<64, false, true>(a);
-  return causal ? launch_t<64, true, false>(a) : launch_t<64, false, false>(a);
+  if (bq) return launch_t<64, false, true, false>(a);
+  if (rope) return causal ? launch_t<64, true, false, true>(a) : launch_t<64, false, false, true>(a);
+  return causal ? launch_t<64, true, false, false>(a) : launch_t<64, false, false, false>(a);
 }
 
 jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu) {

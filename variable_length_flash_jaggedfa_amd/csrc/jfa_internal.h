@@ -24,6 +24,13 @@ jfa_status fail(jfa_status s, const std::string& msg);
 // host validation of the problem descriptor (no HIP calls)
 jfa_status check_problem(const jfa_problem* p);
 
+// Rotary angle of one position step, in revolutions: rev[i] = base^(-2i/D) / (2 pi)
+// for i < D/2 (the jagged kernels form p * rev[i] in double precision).
+struct RopeTab {
+  double rev[64];
+};
+RopeTab rope_table(float base, int head_dim);
+
 // kernel launchers (defined in the .hip files); all arguments already validated
 struct FwdLaunch {
   const void* q; const void* k; const void* v;
@@ -55,6 +62,19 @@ struct BwdLaunch {
   uint32_t flags;
   float rope_base;  // ROTARY only
   uint32_t passes;  // JFA_PASS_* mask
+  const RopeTab* rope;  // jagged ROTARY: q and k are the rotated copies, dq and dk
+                        // are turned back in the epilogues; otherwise NULL
+  void* stream;
+};
+
+// Rotary pre-pass of the jagged path: q, k [T,H,D] -> rotated copies qr, kr,
+// walking the tiles of a forward schedule.
+struct RopeRowsLaunch {
+  const void* q; const void* k; void* qr; void* kr;
+  const int32_t* offsets; const int32_t* slot_ptr; const int32_t* tiles;
+  int32_t num_slots, num_seqs, num_heads, head_dim;
+  int64_t total_kv;
+  RopeTab tab;
   void* stream;
 };
 
@@ -62,11 +82,14 @@ struct BwdLaunch {
 int bcast_groups(int num_seqs);
 // bytes of the Di part of the backward workspace (rounded up to 256)
 size_t di_bytes(const jfa_problem* p);
+// bytes of one rotated [T,H,D] bf16 copy (rounded up to 256); 0 unless jagged ROTARY
+size_t rot_bytes(const jfa_problem* p);
 
 jfa_status launch_fwd(const FwdLaunch& a);
 jfa_status launch_bwd(const BwdLaunch& a);
 jfa_status launch_block_fwd(const FwdLaunch& a);
 jfa_status launch_block_bwd(const BwdLaunch& a);
+jfa_status launch_rope_rows(const RopeRowsLaunch& a);
 jfa_status fwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
 jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
 

@@ -41,7 +41,7 @@ jfa_status check_problem(const jfa_problem* p) {
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
   if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 with other flags");
   if (p->flags & JFA_ROTARY) {
-    if (!blk) return fail(JFA_ERR_UNSUPPORTED, "ROTARY is implemented with BLOCK_DIAG64 only");
+    if (bq) return fail(JFA_ERR_UNSUPPORTED, "ROTARY with BROADCAST_Q (the dense Q rows have no positions)");
     if (!(std::isfinite(p->rope_base) && p->rope_base > 1.f && p->rope_base <= 1e9f))
       return fail(JFA_ERR_INVALID_ARG, "ROTARY needs rope_base finite and in (1, 1e9]");
   } else if (p->rope_base != 0.f) {
@@ -288,6 +288,11 @@ size_t di_bytes(const jfa_problem* p) {
   return (size_t(n) * sizeof(float) + 255) / 256 * 256;
 }
 
+size_t rot_bytes(const jfa_problem* p) {
+  if (!(p->flags & JFA_ROTARY) || (p->flags & JFA_BLOCK_DIAG64)) return 0;
+  return (size_t(p->total_kv) * p->num_heads * p->head_dim * 2 + 255) / 256 * 256;
+}
+
 }  // namespace jfa
 
 extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
@@ -296,7 +301,12 @@ extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
   size_t bytes = 2 * di_bytes(p);  // -Di and -lse/scale, each laid out like lse
   if (p->flags & JFA_BROADCAST_Q)
     bytes += size_t(bcast_groups(p->num_seqs)) * p->lq * p->num_heads * p->head_dim * sizeof(float);
-  return bytes;
+  return bytes + 2 * rot_bytes(p);  // rotated q and k (jagged ROTARY)
+}
+
+extern "C" size_t jfa_fwd_workspace_bytes(const jfa_problem* p) {
+  if (!p || check_problem(p) != JFA_OK) return 0;
+  return 2 * rot_bytes(p);
 }
 
 extern "C" const char* jfa_status_string(jfa_status s) {
