@@ -365,7 +365,7 @@ def main():
     cands = []
     for r in runs:
         w = r["w"]
-        tag = w.name + ("_causal" if w.causal else "")
+        tag = w.name + ("_rope" if w.rope_base else "") + ("_causal" if w.causal else "")
         if r["block"]:
             tag = f"{w.name}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
             tb = T * w.num_heads * w.head_dim * 2
