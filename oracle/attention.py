@@ -16,6 +16,8 @@ Readings of points the pages leave open:
   * Natural-exponent softmax; the saved log-sum-exp is lse = m + ln(l)
     ("TLX Block Attention", section 2: L = m + log(l) kept for the backward).
   * Causal means: inside a sequence, query i attends keys j <= i.
+  * Sliding window (named by the pages as a modelling variant, never defined):
+    a causal window of W keys, query i attends keys j with i - W < j <= i.
   * Backward: P is rebuilt from Q and K, Di = rowsum(dO * O) ("TLX Block
     Attention", sections 2 and 4), dS = P * (dP - Di), dQ = scale dS K,
     dK = scale dS^T Q, dV = P^T dO.
@@ -45,24 +47,27 @@ def _row_blocks(n):
         yield r0, min(n, r0 + ROW_BLOCK)
 
 
-def _probs(q_blk, k, scale, causal, r0):
+def _probs(q_blk, k, scale, causal, r0, window=0):
     """Softmax probabilities P [rows, Lk] and the row max / row sum.
 
     Rows are queries r0..r0+rows-1 of the sequence; with causal, query i keeps
-    keys j <= i only.
+    keys j <= i only, and with a window W > 0 also only keys j > i - W.
     """
     s = scale * (q_blk @ k.T)
     if causal:
         i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
         j = np.arange(k.shape[0])[None, :]
-        s = np.where(j <= i, s, -np.inf)
+        keep = j <= i
+        if window:
+            keep &= j > i - window
+        s = np.where(keep, s, -np.inf)
     m = s.max(axis=1)
     e = np.exp(s - m[:, None])
     l = e.sum(axis=1)
     return e / l[:, None], m, l
 
 
-def seq_forward(q, k, v, scale, causal=False):
+def seq_forward(q, k, v, scale, causal=False, window=0):
     """One sequence, one head. q [Lq,D], k/v [Lk,D] -> out [Lq,D], lse [Lq]."""
     Lq, Lk = q.shape[0], k.shape[0]
     out = np.zeros((Lq, v.shape[1]))
@@ -70,13 +75,13 @@ def seq_forward(q, k, v, scale, causal=False):
     if Lq == 0 or Lk == 0:
         return out, lse
     for r0, r1 in _row_blocks(Lq):
-        p, m, l = _probs(q[r0:r1], k, scale, causal, r0)
+        p, m, l = _probs(q[r0:r1], k, scale, causal, r0, window)
         out[r0:r1] = p @ v
         lse[r0:r1] = m + np.log(l)
     return out, lse
 
 
-def seq_backward(q, k, v, do, scale, causal=False):
+def seq_backward(q, k, v, do, scale, causal=False, window=0):
     """Gradients of <out, dO> for one sequence and head -> dq, dk, dv."""
     Lq, Lk = q.shape[0], k.shape[0]
     dq = np.zeros_like(q)
@@ -85,7 +90,7 @@ def seq_backward(q, k, v, do, scale, causal=False):
     if Lq == 0 or Lk == 0:
         return dq, dk, dv
     for r0, r1 in _row_blocks(Lq):
-        p, _, _ = _probs(q[r0:r1], k, scale, causal, r0)
+        p, _, _ = _probs(q[r0:r1], k, scale, causal, r0, window)
         o = p @ v
         d_o = do[r0:r1]
         di = np.sum(d_o * o, axis=1)            # Di = rowsum(dO * O)
@@ -102,20 +107,20 @@ def _seqs(offsets):
     return [(int(off[b]), int(off[b + 1])) for b in range(len(off) - 1)]
 
 
-def jagged_forward(q, k, v, offsets, scale, causal=False):
+def jagged_forward(q, k, v, offsets, scale, causal=False, window=0):
     """Packed self-attention: q/k/v [T,H,D] -> out [T,H,D], lse [H,T]."""
     T, H, D = q.shape
     out = np.zeros((T, H, v.shape[2]))
     lse = np.full((H, T), -np.inf)
     for s, e in _seqs(offsets):
         for h in range(H):
-            o, l = seq_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale, causal)
+            o, l = seq_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale, causal, window)
             out[s:e, h] = o
             lse[h, s:e] = l
     return out, lse
 
 
-def jagged_backward(q, k, v, do, offsets, scale, causal=False):
+def jagged_backward(q, k, v, do, offsets, scale, causal=False, window=0):
     """Packed self-attention gradients -> dq, dk, dv, each [T,H,D]."""
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -123,7 +128,8 @@ def jagged_backward(q, k, v, do, offsets, scale, causal=False):
     H = q.shape[1]
     for s, e in _seqs(offsets):
         for h in range(H):
-            a, b_, c = seq_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale, causal)
+            a, b_, c = seq_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale, causal,
+                                    window)
             dq[s:e, h], dk[s:e, h], dv[s:e, h] = a, b_, c
     return dq, dk, dv
 

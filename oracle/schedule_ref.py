@@ -42,8 +42,13 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0):
-    """All tiles in generation order: list of (b, h, t, work)."""
+def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0, window=0):
+    """All tiles in generation order: list of (b, h, t, work).
+
+    With a causal window W the work counts only what the window leaves: a query
+    tile visits the keys from max(0, t*BM - W + 1) to its last row, a key tile is
+    attended by the queries from n*BN to min(L, (n+1)*BN - 1 + W).
+    """
     out = []
     for b, L in enumerate(int(x) for x in lengths):
         for h in range(num_heads):
@@ -54,11 +59,15 @@ def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0):
                 else:
                     for t in range(ceil_div(L, tile_rows)):
                         work = min(L, (t + 1) * tile_rows) if causal else L
+                        if causal and window:
+                            work -= max(0, t * tile_rows - window + 1)
                         out.append((b, h, t, work))
             else:
                 for n in range(ceil_div(L, tile_rows)):
                     if lq:
                         work = lq
+                    elif causal and window:
+                        work = min(L, (n + 1) * tile_rows - 1 + window) - n * tile_rows
                     else:
                         work = L - n * tile_rows if causal else L
                     out.append((b, h, n, work))
@@ -72,8 +81,8 @@ def _zigzag_rank(j, n):
 
 
 def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0,
-             groups=8):
-    tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq)
+             groups=8, window=0):
+    tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq, window)
     if order == ORDER_XCD_ZIGZAG:
         # Units are (sequence, head) pairs with the summed work of their tiles;
         # they are sorted by that work and dealt zigzag over the groups, then each

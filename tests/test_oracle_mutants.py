@@ -145,3 +145,40 @@ def test_rotary_backward_without_inverse_rotation_is_caught(monkeypatch):
     monkeypatch.setattr(R, "block_diag_rope_backward", bwd)
     assert _caught(TR.test_block_rope_matches_torch_autograd, D=64)
     assert _caught(TR.test_block_rope_finite_differences)
+
+
+# ------------------------------------------------------------------ window
+from tests import test_oracle_window as TW  # noqa: E402
+
+
+def _mut_probs_window_off_by_one(q_blk, k, scale, causal, r0, window=0):
+    s = scale * (q_blk @ k.T)
+    if causal:
+        i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
+        j = np.arange(k.shape[0])[None, :]
+        keep = j <= i
+        if window:
+            keep &= j >= i - window
+        s = np.where(keep, s, -np.inf)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "_probs", _mut_probs_window_off_by_one)
+    assert _caught(TW.test_window_closed_forms)
+    assert _caught(TW.test_window_matches_torch_sdpa_and_autograd, W=5)
+    assert _caught(TW.test_window_matches_loops)
+
+
+def test_window_work_mistake_is_caught(monkeypatch):
+    orig = TW.S.enumerate_tiles
+
+    def mutated(*a, **kw):
+        # query tiles credited with the whole causal prefix despite the window
+        kw = dict(kw, window=0) if a[2] == TW.S.KIND_FWD else kw
+        return orig(*a, **kw)
+    monkeypatch.setattr(TW.S, "enumerate_tiles", mutated)
+    assert _caught(TW.test_window_tile_work_brute_force, W=100)
