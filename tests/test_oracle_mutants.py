@@ -8,7 +8,7 @@ from oracle import attention as A
 from tests import test_oracle as T
 
 
-def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0):
+def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0, window=0):
     s = scale * (q_blk @ k.T)
     if causal:
         i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
@@ -21,12 +21,12 @@ def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0):
     return e / l[:, None], m, l
 
 
-def _mut_probs_no_scale(q_blk, k, scale, causal, r0):
-    return _orig_probs(q_blk, k, 1.0, causal, r0)
+def _mut_probs_no_scale(q_blk, k, scale, causal, r0, window=0):
+    return _orig_probs(q_blk, k, 1.0, causal, r0, window)
 
 
-def _mut_forward_lse_without_log(q, k, v, scale, causal=False):
-    out, lse = _orig_seq_forward(q, k, v, scale, causal)
+def _mut_forward_lse_without_log(q, k, v, scale, causal=False, window=0):
+    out, lse = _orig_seq_forward(q, k, v, scale, causal, window)
     # drop the log-sum term: lse = m only
     for r0, r1 in A._row_blocks(q.shape[0]):
         if k.shape[0]:
@@ -36,7 +36,7 @@ def _mut_forward_lse_without_log(q, k, v, scale, causal=False):
 
 
 def _make_bwd_mutant(kind):
-    def bwd(q, k, v, do, scale, causal=False):
+    def bwd(q, k, v, do, scale, causal=False, window=0):
         dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
         if q.shape[0] == 0 or k.shape[0] == 0:
             return dq, dk, dv
