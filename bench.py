@@ -33,8 +33,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def pairs_of(lengths, causal=False, lq=0, block=0):
+def pairs_of(lengths, causal=False, lq=0, block=0, window=0):
     L = np.asarray(lengths, dtype=np.int64)
+    if window:  # query i attends min(i + 1, W) keys
+        Wn = np.minimum(L, window)
+        return int((Wn * (Wn + 1) // 2 + (L - Wn) * window).sum())
     if block:
         return int(block * L.sum())
     if lq:
@@ -103,7 +106,8 @@ def cpu_baseline(case, variants, budget_s=15.0):
                 npairs = w.lq * (e - s)
             else:
                 q_, do_ = f(case.q[s:e, h]), f(case.do[s:e, h])
-                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block64" else 0)
+                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block64" else 0,
+                                  window=w.window)
             if w.rope_base:
                 pos = np.arange(e - s)
                 q_ = R.rope(q_[:, None], pos, w.rope_base)[:, 0]
@@ -117,8 +121,8 @@ def cpu_baseline(case, variants, budget_s=15.0):
                         R.rope(dq_[:, None], pos[sl], w.rope_base, inverse=True)
                         R.rope(dk_[:, None], pos[sl], w.rope_base, inverse=True)
             else:
-                A.seq_forward(q_, k_, v_, case.scale, w.causal)
-                A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
+                A.seq_forward(q_, k_, v_, case.scale, w.causal, w.window)
+                A.seq_backward(q_, k_, v_, do_, case.scale, w.causal, w.window)
             flops += 14.0 * npairs * w.head_dim
             units += 1
         if time.perf_counter() - t0 > budget_s:
@@ -144,7 +148,8 @@ def compare_rope(case, runs, q, k, v, do, dev, rounds, order):
     import variable_length_flash_jaggedfa_amd as jfa
     w = runs[0]["w"]
     plains = [jfa.Plan(case.offsets, r["w"].num_heads, r["w"].head_dim, case.scale,
-                       flags_of(r["w"], jfa) & ~jfa.ROTARY, 0, order=order, device=dev)
+                       flags_of(r["w"], jfa) & ~jfa.ROTARY, 0, order=order, device=dev,
+                       window=r["w"].window)
               for r in runs]
     D = w.head_dim
     # positions inside the sequence, angles in float64, tables in bf16
@@ -239,6 +244,7 @@ def main():
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
                              "block64_d128", "block64_rope_d64", "block64_rope_d128", "gem_rope",
+                             "gem_window",
                              "imbalance", "gem_padded"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
@@ -295,11 +301,12 @@ def main():
         fl = flags_of(w, jfa)
         t0 = time.perf_counter()
         plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, fl, w.lq,
-                        order=order, device=dev, rope_base=w.rope_base)
+                        order=order, device=dev, rope_base=w.rope_base, window=w.window)
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
-        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block64" else 0)
+        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block64" else 0,
+                          w.window)
         nhd = float(npairs) * w.num_heads * w.head_dim
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
                          block=w.kind == "block64", fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
@@ -308,7 +315,8 @@ def main():
     alt = None
     if args.compare_orders:
         alt = {name: [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
-                               w.lq, order=code, device=dev) for w in variants]
+                               w.lq, order=code, device=dev, rope_base=w.rope_base, window=w.window)
+                      for w in variants]
                for name, code in ORDERS.items()}
     torch.cuda.synchronize()
 
@@ -365,7 +373,8 @@ def main():
     cands = []
     for r in runs:
         w = r["w"]
-        tag = w.name + ("_rope" if w.rope_base else "") + ("_causal" if w.causal else "")
+        tag = w.name + ("_rope" if w.rope_base else "") + ("_causal" if w.causal else "") + \
+            (f"_w{w.window}" if w.window else "")
         if r["block"]:
             tag = f"{w.name}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
             tb = T * w.num_heads * w.head_dim * 2

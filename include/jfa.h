@@ -31,7 +31,9 @@
  *               each query row's scaled scores.
  *               offsets: int32 [B + 1], offsets[0] = 0, non-decreasing.
  *   Maths       S = scale * Q K^T, P = softmax(S) per query row, out = P V.
- *               Causal: inside a sequence, query i attends keys j <= i.
+ *               Causal: inside a sequence, query i attends keys j <= i; with a
+ *               window W > 0 only keys i - W < j <= i (a causal sliding window,
+ *               a modelling variant the pages name without defining).
  *               Rotary: S = scale * rot(Q) rot(K)^T with the rows of Q and K
  *               rotated by their token position p (index inside the sequence):
  *               column pairs (i, i + D/2), i < D/2, turn by the angle
@@ -96,6 +98,9 @@ typedef struct jfa_problem {
   float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
   float rope_base;    /* ROTARY: base of the rotary frequencies, finite, in (1, 1e9];
                          otherwise must be 0 */
+  int32_t window;     /* CAUSAL only: W > 0 restricts query i to keys i - W < j <= i
+                         (a causal sliding window); 0 = no window */
+  int32_t reserved;   /* must be 0 */
 } jfa_problem;
 
 /* Rows of Q per forward tile (kind FWD) or of K/V per backward tile (kind BWD)
@@ -120,10 +125,10 @@ jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host,
  * GEM-specific optimisations: sort by KV work, deal zigzag).
  *   Forward tile (b,h,t): query rows [t*BM, t*BM+BM) of sequence b (of the dense
  *     Q for BROADCAST_Q), head h; work = keys visited: L_b, or with CAUSAL
- *     min(L_b, (t+1)*BM).
+ *     min(L_b, (t+1)*BM), less max(0, t*BM - W + 1) with a window W.
  *   Backward tile (b,h,n): key rows [n*BN, n*BN+BN) of sequence b, head h;
  *     work = query rows that attend them: L_b (Lq for BROADCAST_Q), or with
- *     CAUSAL L_b - n*BN.
+ *     CAUSAL L_b - n*BN, or with a window min(L_b, (n+1)*BN - 1 + W) - n*BN.
  *   Generation order is b, then h, then t. ZIGZAG: stable sort by descending
  *   work, sorted position j goes to pass j / S, rank r = j % S, slot r on even
  *   passes and S-1-r on odd ones. INORDER: tile j goes to slot j % S.

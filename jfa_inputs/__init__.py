@@ -66,7 +66,8 @@ class Workload:
     mix_long_hi: int = 0
     fixed_lengths: tuple = ()
     pad_to_max: bool = False          # every length replaced by the largest drawn
-    rope_base: float = 0.0            # block64: rotary embeddings with this base (0: none)
+    rope_base: float = 0.0            # rotary embeddings with this base (0: none)
+    window: int = 0                   # causal sliding window of this many keys (0: none)
 
     @property
     def wid(self) -> int:
@@ -104,6 +105,9 @@ def standard_workloads():
                              rope_base=10000.0),
         "gem_rope_causal": Workload("gem", 256, 8, 128, 0.5, law="loguniform", lo=16, hi=4096,
                                     causal=True, rope_base=10000.0),
+        # the causal gem batch with a sliding window of 512 keys (same seeds and values)
+        "gem_window": Workload("gem", 256, 8, 128, 0.5, law="loguniform", lo=16, hi=4096,
+                               causal=True, window=512),
         "gem_padded_causal": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
                                       hi=4096, pad_to_max=True, causal=True),
     }
@@ -239,11 +243,12 @@ def make_case(w: Workload, with_do: bool = True) -> Case:
 
 
 def custom(lengths_, num_heads, head_dim, sigma=1.0, seed=0, kind="jagged", causal=False,
-           lq=0, name="custom", rope_base=0.0) -> Workload:
+           lq=0, name="custom", rope_base=0.0, window=0) -> Workload:
     """A workload with explicitly given lengths (edge cases, small tests)."""
     L = tuple(int(x) for x in lengths_)
     return Workload(name, len(L), num_heads, head_dim, sigma, kind=kind, causal=causal,
-                    lq=lq, seed=seed, law="fixed", fixed_lengths=L, rope_base=rope_base)
+                    lq=lq, seed=seed, law="fixed", fixed_lengths=L, rope_base=rope_base,
+                    window=window)
 
 
 def to_torch_bf16(bits: np.ndarray):

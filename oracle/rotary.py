@@ -71,15 +71,15 @@ def block_diag_rope_backward(q, k, v, do, offsets, scale, base, block=64):
     return rope(dqr, pos, base, inverse=True), rope(dkr, pos, base, inverse=True), dv
 
 
-def jagged_rope_forward(q, k, v, offsets, scale, base, causal=False):
+def jagged_rope_forward(q, k, v, offsets, scale, base, causal=False, window=0):
     """Jagged attention of the rotated queries and keys -> (out, lse)."""
     pos = token_positions(offsets)
-    return jagged_forward(rope(q, pos, base), rope(k, pos, base), v, offsets, scale, causal)
+    return jagged_forward(rope(q, pos, base), rope(k, pos, base), v, offsets, scale, causal, window)
 
 
-def jagged_rope_backward(q, k, v, do, offsets, scale, base, causal=False):
+def jagged_rope_backward(q, k, v, do, offsets, scale, base, causal=False, window=0):
     """(dq, dk, dv) with respect to the unrotated q and k."""
     pos = token_positions(offsets)
     dqr, dkr, dv = jagged_backward(rope(q, pos, base), rope(k, pos, base), v, do, offsets, scale,
-                                   causal)
+                                   causal, window)
     return rope(dqr, pos, base, inverse=True), rope(dkr, pos, base, inverse=True), dv

@@ -63,7 +63,7 @@ class GpuRun:
         self.flags = flags_of(w)
         self.plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, self.flags,
                              w.lq, order=order, num_slots=num_slots, device=dev,
-                             rope_base=w.rope_base)
+                             rope_base=w.rope_base, window=w.window)
         self.q = to_dev(case.q, dev)
         self.k = to_dev(case.k, dev)
         self.v = to_dev(case.v, dev)
@@ -102,11 +102,12 @@ def oracle_full(case: J.Case):
         lse = None
         dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale)
     elif w.rope_base:
-        out, lse = R.jagged_rope_forward(q, k, v, off, case.scale, w.rope_base, w.causal)
-        dq, dk, dv = R.jagged_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.causal)
+        out, lse = R.jagged_rope_forward(q, k, v, off, case.scale, w.rope_base, w.causal, w.window)
+        dq, dk, dv = R.jagged_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.causal,
+                                            w.window)
     else:
-        out, lse = A.jagged_forward(q, k, v, off, case.scale, w.causal)
-        dq, dk, dv = A.jagged_backward(q, k, v, do, off, case.scale, w.causal)
+        out, lse = A.jagged_forward(q, k, v, off, case.scale, w.causal, w.window)
+        dq, dk, dv = A.jagged_backward(q, k, v, do, off, case.scale, w.causal, w.window)
     return out, lse, dq, dk, dv
 
 

@@ -59,6 +59,8 @@ OFF = np.array([0, 10, 15], dtype=np.int32)
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64,
           rope_base=float("inf")), jfa.ERR_INVALID_ARG),
     (dict(rope_base=10000.0), jfa.ERR_INVALID_ARG),
+    (dict(window=-1, flags=jfa.CAUSAL), jfa.ERR_INVALID_ARG),
+    (dict(window=8), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.CAUSAL | jfa.BROADCAST_Q, lq=4), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.CAUSAL), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BROADCAST_Q, lq=0), jfa.ERR_INVALID_ARG),
@@ -183,6 +185,23 @@ def test_cpp_schedule_equals_reference(name, kind, order):
     sp, tl = jfa.schedule(p, off, kind, order, S)
     rows = jfa.tile_rows(kind, w.head_dim, flags)
     sp2, tl2 = R.schedule(L, H, kind, rows, order, S, w.causal, w.lq)
+    assert np.array_equal(sp, sp2)
+    assert np.array_equal(tl, tl2)
+
+
+@pytest.mark.parametrize("W", [1, 100, 512, 5000])
+@pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
+@pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
+                                   jfa.ORDER_FOLDED_ZIGZAG])
+def test_cpp_schedule_equals_reference_with_window(W, kind, order):
+    w = J.standard_workloads()["gem_window"]
+    L = J.lengths(w)
+    off = J.offsets_from_lengths(L)
+    p = jfa.problem(len(L), w.num_heads, w.head_dim, int(L.max()), int(off[-1]), 0.1, jfa.CAUSAL,
+                    window=W)
+    sp, tl = jfa.schedule(p, off, kind, order, 512)
+    rows = jfa.tile_rows(kind, w.head_dim, jfa.CAUSAL)
+    sp2, tl2 = R.schedule(L, w.num_heads, kind, rows, order, 512, True, window=W)
     assert np.array_equal(sp, sp2)
     assert np.array_equal(tl, tl2)
 

@@ -79,12 +79,13 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
                 gq, gk = rot(gq, True), rot(gk, True)
                 l_ref = None
             elif w.rope_base:
-                o_ref, l_ref = A.seq_forward(rot(q_), rot(k_), v_, case.scale, w.causal)
-                gq, gk, gv = A.seq_backward(rot(q_), rot(k_), v_, do_, case.scale, w.causal)
+                o_ref, l_ref = A.seq_forward(rot(q_), rot(k_), v_, case.scale, w.causal, w.window)
+                gq, gk, gv = A.seq_backward(rot(q_), rot(k_), v_, do_, case.scale, w.causal,
+                                            w.window)
                 gq, gk = rot(gq, True), rot(gk, True)
             else:
-                o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale, w.causal)
-                gq, gk, gv = A.seq_backward(q_, k_, v_, do_, case.scale, w.causal)
+                o_ref, l_ref = A.seq_forward(q_, k_, v_, case.scale, w.causal, w.window)
+                gq, gk, gv = A.seq_backward(q_, k_, v_, do_, case.scale, w.causal, w.window)
             errs["out"] = max(errs["out"], max_abs(got_o, o_ref))
             if l_ref is not None:
                 errs["lse"] = max(errs["lse"], max_abs(got_l, l_ref))
@@ -126,6 +127,10 @@ def test_gem_causal(gpu):
 @pytest.mark.parametrize("name", ["gem_rope", "gem_rope_causal"])
 def test_gem_rope(gpu, name):
     run_sampled(name, gpu)
+
+
+def test_gem_window(gpu):
+    run_sampled("gem_window", gpu)
 
 
 def test_broadcast(gpu):

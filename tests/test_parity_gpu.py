@@ -106,6 +106,34 @@ def test_jagged_rotary_long_positions(gpu, base):
                         rope_base=base), gpu)
 
 
+WINDOW_LENGTHS = [300, 1, 129, 64, 0, 700, 17, 128, 2, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [1, 33, 64, 100, 128, 129, 256, 5000])
+def test_jagged_sliding_window(gpu, D, W):
+    check_case(J.custom(WINDOW_LENGTHS, 2, D, sigma=0.5, seed=23, causal=True, window=W), gpu)
+
+
+def test_sliding_window_with_rotary(gpu):
+    check_case(J.custom(WINDOW_LENGTHS, 2, 128, sigma=0.5, seed=24, causal=True, window=200,
+                        rope_base=10000.0), gpu)
+
+
+def test_sliding_window_covering_every_sequence_is_causal(gpu):
+    # a window at least as long as every sequence gives the bits of plain causal
+    import torch
+    w = J.custom(WINDOW_LENGTHS, 2, 64, sigma=0.5, seed=25, causal=True)
+    ra = GpuRun(J.make_case(w), gpu)
+    rb = GpuRun(J.make_case(w.with_(window=1000)), gpu)
+    oa, la = ra.forward()
+    ob, lb = rb.forward()
+    ga, gb = ra.backward(), rb.backward()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+
+
 def test_block_diag_rotary_rows_are_not_plain_attention(gpu):
     # the rotation is applied: rotary and plain block attention differ on the GPU
     import torch
@@ -224,7 +252,8 @@ def test_backward_passes_match_fused_call(gpu):
     for w in (J.custom(RAGGED, 2, 128, sigma=0.5, seed=17, causal=True),
               J.custom([50, 0, 300, 129], 2, 64, sigma=0.5, seed=17, kind="broadcast", lq=130),
               # rotary: the dK/dV pass reads the rotated rows the dQ pass left behind
-              J.custom(RAGGED, 2, 64, sigma=0.5, seed=17, rope_base=10000.0)):
+              J.custom(RAGGED, 2, 64, sigma=0.5, seed=17, rope_base=10000.0),
+              J.custom(RAGGED, 2, 128, sigma=0.5, seed=17, causal=True, window=100)):
         log(f"case passes {w.kind} causal={w.causal} D={w.head_dim}")
         run = GpuRun(J.make_case(w), gpu)
         run.forward()

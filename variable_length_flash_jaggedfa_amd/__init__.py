@@ -39,7 +39,8 @@ class Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_len", ctypes.c_int32),
                 ("lq", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("total_kv", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("rope_base", ctypes.c_float)]
+                ("rope_base", ctypes.c_float), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -89,9 +90,9 @@ def _check(status: int):
 
 
 def problem(num_seqs, num_heads, head_dim, max_len, total_kv, scale, flags=0, lq=0,
-            rope_base=0.0) -> Problem:
+            rope_base=0.0, window=0) -> Problem:
     return Problem(int(num_seqs), int(num_heads), int(head_dim), int(max_len), int(lq),
-                   int(flags), int(total_kv), float(scale), float(rope_base))
+                   int(flags), int(total_kv), float(scale), float(rope_base), int(window), 0)
 
 
 def tile_rows(kind: int, head_dim: int, flags: int = 0) -> int:
@@ -192,7 +193,7 @@ class Plan:
     """Everything one jagged problem needs on the device, built once.
 
     offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q; rope_base
-    for ROTARY.
+    for ROTARY; window (CAUSAL only) for a causal sliding window of that many keys.
     Builds the FWD and BWD schedules on the host (folded zigzag by default: the
     work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired so
     that they run side by side), copies them
@@ -200,13 +201,14 @@ class Plan:
     """
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
-                 order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda", rope_base=0.0):
+                 order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda", rope_base=0.0,
+                 window=0):
         import torch
         off = _host_i32(offsets_host)
         L = np.diff(off.astype(np.int64))
         self.offsets_host = off
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
-                         int(off[-1]), scale, flags, lq, rope_base)
+                         int(off[-1]), scale, flags, lq, rope_base, window)
         self.device = torch.device(device)
         self.offsets_dev = torch.from_numpy(off.copy()).to(self.device)
         self.block = bool(flags & BLOCK_DIAG64)

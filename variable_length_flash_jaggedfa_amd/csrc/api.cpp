@@ -99,7 +99,7 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   }
   FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
               p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
-              p->rope_base, stream};
+              p->rope_base, p->window, stream};
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is stored)");
     if (p->total_kv == 0) return JFA_OK;
@@ -155,6 +155,7 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
   a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.rope_base = p->rope_base;
+  a.window = p->window;
   a.passes = passes;
   a.stream = stream;
   if (blk) {

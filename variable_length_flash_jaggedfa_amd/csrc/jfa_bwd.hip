@@ -68,6 +68,7 @@ struct DqParams {
   float* dq_part;             // broadcast: [groups][Lq][H][D] float32 partials
   int32_t H, lq, total_kv, num_seqs, groups;
   float c, scale;
+  int32_t window;             // causal sliding window (WIN kernels)
   jfa::RopeTab rope;          // rotary kernels only
 };
 
@@ -119,17 +120,17 @@ __device__ __forceinline__ void dq_accumulate(uint32_t ks, const LaneOffsets<D>&
 }
 
 // P = 2^(S c - lse2) and dS = P (dP - Di) for one step, packed to bf16 (keys past
-// the sequence end or, with CAUSAL, after the lane's query masked). With PREV the
-// dQ products of the previous step are issued in the same region so that these
-// VALU instructions run under them.
-template <int D, bool MASK, bool CAUSAL, bool PREV>
+// the sequence end or, with CAUSAL, after the lane's query masked; with WIN also
+// keys at or before qpos - win). With PREV the dQ products of the previous step
+// are issued in the same region so that these VALU instructions run under them.
+template <int D, bool MASK, bool CAUSAL, bool PREV, bool WIN = false>
 __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
                                            const f32x16 (&dp)[DqCfg<D>::KB], float lse2, float di,
                                            float c, int g, int key0, int n_keys, int qpos,
                                            u32x4 (&pds)[2 * DqCfg<D>::KB], uint32_t ks_prev,
                                            const LaneOffsets<D>& lo,
                                            const u32x4 (&pds_prev)[2 * DqCfg<D>::KB],
-                                           f32x16 (&acc)[DqCfg<D>::NB]) {
+                                           f32x16 (&acc)[DqCfg<D>::NB], int win = 0) {
   using C = DqCfg<D>;
   if (PREV) dq_accumulate<D>(ks_prev, lo, pds_prev, acc);
 #pragma unroll
@@ -140,8 +141,9 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
       float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -lse2));
       if (MASK) {
         const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-        p0 = (key >= n_keys || (CAUSAL && key > qpos)) ? 0.f : p0;
-        p1 = (key + 1 >= n_keys || (CAUSAL && key + 1 > qpos)) ? 0.f : p1;
+        p0 = (key >= n_keys || (CAUSAL && key > qpos) || (WIN && key <= qpos - win)) ? 0.f : p0;
+        p1 = (key + 1 >= n_keys || (CAUSAL && key + 1 > qpos) || (WIN && key + 1 <= qpos - win))
+                 ? 0.f : p1;
       }
       pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
     }
@@ -152,9 +154,11 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
 // Stream the keys [0, n_keys) of one (sequence, head) past one query tile. Step kt
 // reads the rows of stage kt and the columns of stage kt-1 of a four-stage ring,
 // so the load issued at step kt (stage kt+2) goes to the buffer of stage kt-2.
-template <int D, bool CAUSAL>
+// Steps [0, n_lo) (window edge) and [n_free, n_steps) (tail, diagonal) are masked.
+template <int D, bool CAUSAL, bool WIN = false>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
-                                          int64_t rstride, int L, int n_keys, int n_free,
+                                          int64_t rstride, int L, int n_keys, int n_lo, int n_free,
+                                          int win,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
@@ -188,10 +192,12 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     arrive(0);
     if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
     dq_scores<D>(ks_of(0), ks_of(0) + C::TILE * 2, lo, qf, dof, s, dp);
-    if (n_free == 0)
-      dq_softmax<D, true, CAUSAL, false>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv, acc);
+    if (n_lo > 0 || n_free == 0)
+      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+                                              acc, win);
     else
-      dq_softmax<D, false, CAUSAL, false>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv, acc);
+      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+                                               acc, win);
     auto step = [&](int kt, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
@@ -204,10 +210,12 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       __builtin_amdgcn_s_setprio(1);
       dq_scores<D>(ks, ks + C::TILE * 2, lo, qf, dof, s, dp);
       __builtin_amdgcn_s_setprio(0);
-      dq_softmax<D, MASK, CAUSAL, true>(s, dp, lse2, di, c, g, kt * C::BN, n_keys, qpos, pds,
-                                        ks_of(kt - 1), lo, pdv, acc);
+      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, di, c, g, kt * C::BN, n_keys, qpos, pds,
+                                             ks_of(kt - 1), lo, pdv, acc, win);
     };
     int kt = 1;
+    if (WIN)
+      for (; kt < n_lo; ++kt) step(kt, std::true_type{});
     for (; kt < n_free; ++kt) step(kt, std::false_type{});
     for (; kt < n_steps; ++kt) step(kt, std::true_type{});
     dq_accumulate<D>(ks_of(n_steps - 1), lo, pds, acc);
@@ -233,7 +241,7 @@ __device__ __forceinline__ float load_row(const uint16_t* qrow, const uint16_t* 
   return pair_sum(di);  // Di = rowsum(dO * out)
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, bool WIN>
 __global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dq_kernel(DqParams P) {
   using C = DqCfg<D>;
@@ -254,8 +262,14 @@ dq_kernel(DqParams P) {
     const int L = uniform(P.offsets[b + 1]) - kv0;
     const int q_first = t * C::BM;
     const int q_rows = min(C::BM, L - q_first);
-    const int n_keys = CAUSAL ? min(L, q_first + q_rows) : L;
-    const int n_free = min(ceil_div(n_keys, C::BN), (CAUSAL ? q_first : L) / C::BN);
+    // with a sliding window the keys are streamed from ks0, the start of the step
+    // holding key q_first - W + 1 (as in the forward), and counted from there
+    const int ks0 = WIN ? max(0, q_first - P.window + 1) / C::BN * C::BN : 0;
+    const int n_keys = (CAUSAL ? min(L, q_first + q_rows) : L) - ks0;
+    const int n_steps = ceil_div(n_keys, C::BN);
+    const int lo_edge = WIN ? q_first + C::BM - P.window - ks0 : 0;
+    const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
+    const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
     const int qpos = q_first + w * 32 + (lane & 31);
     const bool ok = qpos < L;
     const int64_t row = int64_t(kv0) + qpos;
@@ -272,9 +286,10 @@ dq_kernel(DqParams P) {
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
-    dq_stream<D, CAUSAL>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
-                         P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, n_keys, n_free,
-                         qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
+    dq_stream<D, CAUSAL, WIN>(lds, P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D,
+                              P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D, rstride, L - ks0,
+                              n_keys, n_lo, n_free, P.window, qf, dof, acc, lse2, di, P.c, w, lane,
+                              qpos - ks0, lo);
     // dq_stream ended with a barrier: the ring is free to stage the output rows
     if (ROPE) rope_back_rows<D>(acc, qpos, g, rope_tab);
     const int row0 = q_first + w * 32;
@@ -318,8 +333,8 @@ dq_bcast_kernel(DqParams P) {
     }
     if (L > 0)
       dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
-                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, L / C::BN,
-                          qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
+                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, 0, L / C::BN,
+                          0, qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;
@@ -383,6 +398,7 @@ struct KvParams {
   uint16_t* dk; uint16_t* dv;
   int32_t H, lq, total_kv;
   float c, scale;
+  int32_t window;     // causal sliding window (WIN kernels)
   jfa::RopeTab rope;  // rotary kernels only
 };
 
@@ -461,9 +477,9 @@ __device__ __forceinline__ void kv_products(const KvAddr<D>& a, const u32x4 (&y)
 
 // P = 2^(c S') packed to bf16 (keys after the query masked with MASK). Operand st
 // element k holds rows (st%2)*8 + 2k, +1 of 32-row block st/2.
-template <int D, bool MASK>
+template <int D, bool MASK, bool WIN = false>
 __device__ __forceinline__ void kv_probs(const f32x16 (&s)[KvCfg<D>::IB], float c, int g, int q0,
-                                         int jw, u32x4 (&pk)[KvCfg<D>::PK]) {
+                                         int jw, u32x4 (&pk)[KvCfg<D>::PK], int win = 0) {
   using C = KvCfg<D>;
 #pragma unroll
   for (int st = 0; st < C::PK; ++st)
@@ -473,9 +489,9 @@ __device__ __forceinline__ void kv_probs(const f32x16 (&s)[KvCfg<D>::IB], float 
       // register r holds row (r/4)*8 + 4g + r%4 of the block
       const int i = q0 + ib * 32 + (r / 4) * 8 + 4 * g + r % 4;
       float p0 = exp2_fast(s[ib][r] * c), p1 = exp2_fast(s[ib][r + 1] * c);
-      if (MASK) {
-        p0 = jw > i ? 0.f : p0;
-        p1 = jw > i + 1 ? 0.f : p1;
+      if (MASK) {  // query before the key, or (window) at least win rows after it
+        p0 = (jw > i || (WIN && i - jw >= win)) ? 0.f : p0;
+        p1 = (jw > i + 1 || (WIN && i + 1 - jw >= win)) ? 0.f : p1;
       }
       pk[st][k] = pack_bf16(p0, p1);
     }
@@ -511,7 +527,7 @@ __device__ __forceinline__ void xch_get(const KvAddr<D>& a, u32x4 (&pp)[KvCfg<D>
     pp[x] = lds_ld16(a.xch + uint32_t((S * C::NP * C::PK + x) * 64 * 16));
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool ROPE>
+template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN>
 __global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
@@ -534,7 +550,7 @@ dkdv_kernel(KvParams P) {
 
   // what every wave derives from a tile of the schedule
   struct Tile {
-    int b, h, kv0, L, key0, rows_total, qs_lo, n_steps, n_mask;
+    int b, h, kv0, L, key0, rows_total, qs_lo, n_steps, n_mask, n_hi;
     const uint16_t* qbase;
     const uint16_t* dobase;
     int64_t voff;
@@ -553,11 +569,15 @@ dkdv_kernel(KvParams P) {
     T.voff = BCAST ? (int64_t(T.b) * P.H + T.h) * P.lq : int64_t(T.h) * P.total_kv + T.kv0;
     T.qs_lo = CAUSAL ? T.key0 / C::BM : 0;
     // every tile has at least one step (lq >= 1; a causal tile starts on the
-    // diagonal of its own keys)
-    T.n_steps = ceil_div(T.rows_total, C::BM) - T.qs_lo;
-    // causal steps that reach the diagonal need a mask; rows past the end read as
-    // zeros and contribute nothing
+    // diagonal of its own keys); with a sliding window the queries past
+    // key0 + BN - 1 + W reach none of the tile's keys
+    const int q_end = WIN ? min(T.rows_total, T.key0 + C::BN - 1 + P.window) : T.rows_total;
+    T.n_steps = ceil_div(q_end, C::BM) - T.qs_lo;
+    // causal steps that reach the diagonal need a mask, and with a window the
+    // steps from the one holding query key0 + W on (rows past the end read as
+    // zeros and contribute nothing)
     T.n_mask = CAUSAL ? min(T.n_steps, C::BN / C::BM) : 0;
+    T.n_hi = WIN ? max(0, (T.key0 + P.window) / C::BM - T.qs_lo) : T.n_steps;
     return T;
   };
   auto load_stage = [&](const Tile& T, int st) {
@@ -652,8 +672,10 @@ dkdv_kernel(KvParams P) {
           // traffic is spread over the step
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
           const int q0 = (T.qs_lo + it) * C::BM;
-          if (CAUSAL && it < T.n_mask) kv_probs<D, true>(s, P.c, g, q0, jw, pk);
-          else kv_probs<D, false>(s, P.c, g, q0, jw, pk);
+          if (CAUSAL && (it < T.n_mask || (WIN && it >= T.n_hi)))
+            kv_probs<D, true, WIN>(s, P.c, g, q0, jw, pk, P.window);
+          else
+            kv_probs<D, false>(s, P.c, g, q0, jw, pk);
           xch_put<D, S>(ad, pk);
         } else {
           if (prev) {
@@ -720,7 +742,7 @@ int grid_for(int64_t n4) {
   return int(g < 8192 ? (g > 0 ? g : 1) : 8192);
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool ROPE>
+template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN>
 jfa_status launch_t(const jfa::BwdLaunch& a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float c = a.scale * kLog2e;
@@ -745,6 +767,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   dp.groups = a.groups;
   dp.c = c;
   dp.scale = a.scale;
+  dp.window = a.window;
   if (ROPE) dp.rope = *a.rope;
   const bool run_dq = a.passes & JFA_PASS_DQ, run_kv = a.passes & JFA_PASS_DKDV;
   if (!run_dq) {
@@ -756,7 +779,8 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     hipLaunchKernelGGL(dq_reduce_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_part,
                        static_cast<uint16_t*>(a.dq), n4, a.groups, a.scale);
   } else if (a.total_kv > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, ROPE>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st, dp);
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, ROPE, WIN>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st,
+                       dp);
   }
   if (run_kv && a.total_kv > 0) {
     KvParams kp{};
@@ -776,9 +800,10 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     kp.total_kv = int32_t(a.total_kv);
     kp.c = c;
     kp.scale = a.scale;
+    kp.window = a.window;
     if (ROPE) kp.rope = *a.rope;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST, ROPE>), dim3(a.kv_num_slots), dim3(KvCfg<D>::NT),
-                       0, st, kp);
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST, ROPE, WIN>), dim3(a.kv_num_slots),
+                       dim3(KvCfg<D>::NT), 0, st, kp);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("bwd launch: ") + hipGetErrorString(e));
@@ -788,7 +813,7 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
 template <int D, bool CAUSAL, bool BCAST>
 int occupancy_kv() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_kernel<D, CAUSAL, BCAST, false>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_kernel<D, CAUSAL, BCAST, false, false>,
                                                    KvCfg<D>::NT, 0) != hipSuccess)
     return 0;
   return n;
@@ -798,16 +823,20 @@ int occupancy_kv() {
 
 namespace jfa {
 
+template <int D>
+jfa_status launch_bwd_d(const BwdLaunch& a) {
+  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, rope = a.rope != nullptr,
+             win = a.window > 0;
+  if (bq) return launch_t<D, false, true, false, false>(a);
+  if (win)  // a window comes with CAUSAL
+    return rope ? launch_t<D, true, false, true, true>(a) : launch_t<D, true, false, false, true>(a);
+  if (rope)
+    return causal ? launch_t<D, true, false, true, false>(a) : launch_t<D, false, false, true, false>(a);
+  return causal ? launch_t<D, true, false, false, false>(a) : launch_t<D, false, false, false, false>(a);
+}
+
 jfa_status launch_bwd(const BwdLaunch& a) {
-  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, rope = a.rope != nullptr;
-  if (a.head_dim == 128) {
-    if (bq) return launch_t<128, false, true, false>(a);
-    if (rope) return causal ? launch_t<128, true, false, true>(a) : launch_t<128, false, false, true>(a);
-    return causal ? launch_t<128, true, false, false>(a) : launch_t<128, false, false, false>(a);
-  }
-  if (bq) return launch_t<64, false, true, false>(a);
-  if (rope) return causal ? launch_t<64, true, false, true>(a) : launch_t<64, false, false, true>(a);
-  return causal ? launch_t<64, true, false, false>(a) : launch_t<64, false, false, false>(a);
+  return a.head_dim == 128 ? launch_bwd_d<128>(a) : launch_bwd_d<64>(a);
 }
 
 jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu) {

@@ -50,19 +50,21 @@ struct FwdParams {
   uint16_t* out; float* lse;
   int32_t H, lq, total_kv;
   float c;  // scale * log2(e)
+  int32_t window;  // causal sliding window (WIN kernels)
 };
 
 // Scores of one step whose keys fall past the sequence end or, with CAUSAL,
-// after the lane's query position are set to -inf.
-template <int D, bool CAUSAL>
+// after the lane's query position (with WIN also at or before qpos - win) are
+// set to -inf.
+template <int D, bool CAUSAL, bool WIN>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[FwdCfg<D>::KB], int g, int key0, int n_keys,
-                                            int qpos) {
+                                            int qpos, int win) {
 #pragma unroll
   for (int kb = 0; kb < FwdCfg<D>::KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-      const bool dead = key >= n_keys || (CAUSAL && key > qpos);
+      const bool dead = key >= n_keys || (CAUSAL && key > qpos) || (WIN && key <= qpos - win);
       s[kb][r] = dead ? -INFINITY : s[kb][r];
     }
 }
@@ -120,13 +122,13 @@ __device__ __forceinline__ void update_max(float mx, float& m, float& l,
 //   B: issues O^T += V^T P^T interleaved with the masking and row max of the
 //      next step's scores.
 // Returns the next step's scaled row max (or -inf when there is no next step).
-template <int D, bool NEXT, bool MASK_NEXT, bool CAUSAL>
+template <int D, bool NEXT, bool MASK_NEXT, bool CAUSAL, bool WIN>
 __device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks_next,
                                           const u32x4 (&qf)[FwdCfg<D>::DS],
                                           const f32x16 (&sc)[FwdCfg<D>::KB],
                                           f32x16 (&sn)[FwdCfg<D>::KB], f32x16 (&o)[FwdCfg<D>::NB],
                                           float m, float& l, float c, int lane, int key_next,
-                                          int n_keys, int qpos) {
+                                          int n_keys, int qpos, int win) {
   using C = FwdCfg<D>;
   const int g = lane >> 5, li = lane & 31;
   // --- A. The step runs at raised wave priority: of the two waves sharing a
@@ -189,7 +191,7 @@ __device__ __forceinline__ float fwd_step(const uint16_t* vs, const uint16_t* ks
   for (int x = 0; x < C::NX; ++x) o[x % C::NB] = mfma32(vf[x], pf[x / C::NB], o[x % C::NB]);
   float mx = -INFINITY;
   if (NEXT) {
-    if (MASK_NEXT) mask_scores<D, CAUSAL>(sn, g, key_next, n_keys, qpos);
+    if (MASK_NEXT) mask_scores<D, CAUSAL, WIN>(sn, g, key_next, n_keys, qpos, win);
     mx = row_max<D>(sn);
   }
 #pragma unroll
@@ -208,7 +210,7 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool CAUSAL, bool BCAST>
+template <int D, bool CAUSAL, bool BCAST, bool WIN>
 __global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
   using C = FwdCfg<D>;
@@ -227,20 +229,31 @@ fwd_kernel(FwdParams P) {
     const int rows_total = BCAST ? P.lq : L;
     const int q_first = t * C::BM;
     const int q_rows = min(C::BM, rows_total - q_first);
-    const int n_keys = CAUSAL ? min(L, q_first + q_rows) : L;
+    // With a sliding window the steps start at the step holding key
+    // q_first - W + 1, the first key any row of the tile attends; keys, the key
+    // count and the query position used by the masks are counted from that
+    // step's first key, ks0. The first n_lo steps meet the window's lower edge
+    // and are masked like the diagonal ones.
+    const int ks0 = WIN ? max(0, q_first - P.window + 1) / C::BN * C::BN : 0;
+    const int n_keys = (CAUSAL ? min(L, q_first + q_rows) : L) - ks0;
     const int n_steps = ceil_div(n_keys, C::BN);
-    const int n_free = min(n_steps, (CAUSAL ? q_first : L) / C::BN);  // steps without a mask
+    const int lo_edge = WIN ? q_first + C::BM - P.window - ks0 : 0;
+    const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
+    // steps without a mask: [n_lo, n_free)
+    const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
     const int qpos = q_first + w * 32 + li;  // query position of this lane
-    const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
-    const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
+    const int qm = qpos - ks0;                // the same, counted from key ks0
+    const uint16_t* kbase = P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
+    const uint16_t* vbase = P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
+    const int Lk = L - ks0;
     const int rowbytes = int(rstride * 2);
     // stage st holds keys [st*BN, st*BN + BN): a resource starting at that row,
     // covering the rest of the sequence (keys past the end read as zero)
     auto load_stage = [&](int st) {
       uint16_t* buf = lds + (st % C::NS) * C::STAGE;
       const int64_t r0 = int64_t(st) * C::BN * rstride;
-      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
-      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, L - st * C::BN),
+      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, Lk - st * C::BN), rowbytes, w, lane);
+      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, Lk - st * C::BN),
                                  rowbytes, w, lane);
     };
     auto stage_ptr = [&](int st) { return lds + (st % C::NS) * C::STAGE; };
@@ -270,7 +283,7 @@ fwd_kernel(FwdParams P) {
       __syncthreads();
       f32x16 sc[C::KB], sn[C::KB];
       scores<D>(stage_ptr(0), qf, sc, li, g);
-      if (n_free == 0) mask_scores<D, CAUSAL>(sc, g, 0, n_keys, qpos);
+      if (n_lo > 0 || n_free == 0) mask_scores<D, CAUSAL, WIN>(sc, g, 0, n_keys, qm, P.window);
       m = pair_max(row_max<D>(sc)) * P.c;
 
       // before step kt (kt + 1 < n_steps): stage kt+1 must have landed, stage
@@ -283,39 +296,50 @@ fwd_kernel(FwdParams P) {
         if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
       };
       int kt = 0;
+      if (WIN) {
+        for (; kt + 1 < n_lo; ++kt) {  // the next step meets the window's lower edge
+          advance(kt);
+          const float mx = fwd_step<D, true, true, CAUSAL, WIN>(
+              stage_ptr(kt) + C::TILE, stage_ptr(kt + 1), qf, sc, sn, o, m, l, P.c, lane,
+              (kt + 1) * C::BN, n_keys, qm, P.window);
+          update_max<D>(mx, m, l, o);
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
+        }
+      }
       // two unmasked steps per iteration, the score registers swapping roles
       for (; kt + 2 < n_free; kt += 2) {
         advance(kt);
-        float mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+        float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                    qf, sc, sn, o, m, l, P.c, lane,
-                                                   (kt + 1) * C::BN, n_keys, qpos);
+                                                   (kt + 1) * C::BN, n_keys, qm, P.window);
         update_max<D>(mx, m, l, o);
         advance(kt + 1);
-        mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt + 1) + C::TILE, stage_ptr(kt + 2),
+        mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt + 1) + C::TILE, stage_ptr(kt + 2),
                                              qf, sn, sc, o, m, l, P.c, lane,
-                                             (kt + 2) * C::BN, n_keys, qpos);
+                                             (kt + 2) * C::BN, n_keys, qm, P.window);
         update_max<D>(mx, m, l, o);
       }
       for (; kt + 1 < n_free; ++kt) {  // the next step needs no mask
         advance(kt);
-        const float mx = fwd_step<D, true, false, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+        const float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                          qf, sc, sn, o, m, l, P.c, lane,
-                                                         (kt + 1) * C::BN, n_keys, qpos);
+                                                         (kt + 1) * C::BN, n_keys, qm, P.window);
         update_max<D>(mx, m, l, o);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
       }
       for (; kt + 1 < n_steps; ++kt) {  // the next step is the tail or on the diagonal
         advance(kt);
-        const float mx = fwd_step<D, true, true, CAUSAL>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+        const float mx = fwd_step<D, true, true, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                         qf, sc, sn, o, m, l, P.c, lane,
-                                                        (kt + 1) * C::BN, n_keys, qpos);
+                                                        (kt + 1) * C::BN, n_keys, qm, P.window);
         update_max<D>(mx, m, l, o);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
       }
-      fwd_step<D, false, false, CAUSAL>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
-                                        lane, 0, n_keys, qpos);
+      fwd_step<D, false, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
+                                        lane, 0, n_keys, qm, P.window);
     }
 
     // epilogue: out = O / l (bf16) through the wave's LDS staging tile, lse =
@@ -343,7 +367,7 @@ fwd_kernel(FwdParams P) {
   }
 }
 
-template <int D, bool CAUSAL, bool BCAST>
+template <int D, bool CAUSAL, bool BCAST, bool WIN>
 jfa_status launch_t(const jfa::FwdLaunch& a) {
   FwdParams P;
   P.q = static_cast<const uint16_t*>(a.q);
@@ -358,7 +382,8 @@ jfa_status launch_t(const jfa::FwdLaunch& a) {
   P.lq = a.lq;
   P.total_kv = int32_t(a.total_kv);
   P.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, BCAST>), dim3(a.num_slots), dim3(FwdCfg<D>::NT), 0,
+  P.window = a.window;
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, BCAST, WIN>), dim3(a.num_slots), dim3(FwdCfg<D>::NT), 0,
                      static_cast<hipStream_t>(a.stream), P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("fwd launch: ") + hipGetErrorString(e));
@@ -368,7 +393,7 @@ jfa_status launch_t(const jfa::FwdLaunch& a) {
 template <int D, bool CAUSAL, bool BCAST>
 int occupancy() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, CAUSAL, BCAST>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<D, CAUSAL, BCAST, false>,
                                                    FwdCfg<D>::NT, 0) != hipSuccess)
     return 0;
   return n;
@@ -379,13 +404,15 @@ int occupancy() {
 namespace jfa {
 
 jfa_status launch_fwd(const FwdLaunch& a) {
-  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q;
+  const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, win = a.window > 0;
   if (a.head_dim == 128) {
-    if (bq) return launch_t<128, false, true>(a);
-    return causal ? launch_t<128, true, false>(a) : launch_t<128, false, false>(a);
+    if (bq) return launch_t<128, false, true, false>(a);
+    if (win) return launch_t<128, true, false, true>(a);
+    return causal ? launch_t<128, true, false, false>(a) : launch_t<128, false, false, false>(a);
   }
-  if (bq) return launch_t<64, false, true>(a);
-  return causal ? launch_t<64, true, false>(a) : launch_t<64, false, false>(a);
+  if (bq) return launch_t<64, false, true, false>(a);
+  if (win) return launch_t<64, true, false, true>(a);
+  return causal ? launch_t<64, true, false, false>(a) : launch_t<64, false, false, false>(a);
 }
 
 jfa_status fwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu) {

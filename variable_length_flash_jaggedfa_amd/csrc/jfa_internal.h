@@ -42,6 +42,7 @@ struct FwdLaunch {
   float scale;
   uint32_t flags;
   float rope_base;  // ROTARY only
+  int32_t window;   // causal sliding window (0: none)
   void* stream;
 };
 
@@ -61,6 +62,7 @@ struct BwdLaunch {
   float scale;
   uint32_t flags;
   float rope_base;  // ROTARY only
+  int32_t window;   // causal sliding window (0: none)
   uint32_t passes;  // JFA_PASS_* mask
   const RopeTab* rope;  // jagged ROTARY: q and k are the rotated copies, dq and dk
                         // are turned back in the epilogues; otherwise NULL

@@ -40,6 +40,10 @@ jfa_status check_problem(const jfa_problem* p) {
              blk = p->flags & JFA_BLOCK_DIAG64;
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
   if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 with other flags");
+  if (p->window < 0) return fail(JFA_ERR_INVALID_ARG, "window < 0");
+  if (p->window > 0 && !causal)
+    return fail(JFA_ERR_UNSUPPORTED, "a sliding window needs CAUSAL (jagged self-attention)");
+  if (p->reserved != 0) return fail(JFA_ERR_INVALID_ARG, "reserved field must be 0");
   if (p->flags & JFA_ROTARY) {
     if (bq) return fail(JFA_ERR_UNSUPPORTED, "ROTARY with BROADCAST_Q (the dense Q rows have no positions)");
     if (!(std::isfinite(p->rope_base) && p->rope_base > 1.f && p->rope_base <= 1e9f))
@@ -98,13 +102,19 @@ std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t ki
         } else {
           for (int32_t t = 0, n = ceil_div(L, rows); t < n; ++t) {
             const int64_t end = int64_t(t + 1) * rows;
-            tiles.push_back({b, h, t, causal ? int32_t(std::min<int64_t>(L, end)) : L});
+            int64_t work = causal ? std::min<int64_t>(L, end) : L;
+            // a causal window leaves the keys from t*rows - W + 1 on
+            if (p->window > 0) work -= std::max<int64_t>(0, int64_t(t) * rows - p->window + 1);
+            tiles.push_back({b, h, t, int32_t(work)});
           }
         }
       } else {
         for (int32_t n = 0, m = ceil_div(L, rows); n < m; ++n) {
-          const int32_t work = lq ? lq : (causal ? L - n * rows : L);
-          tiles.push_back({b, h, n, work});
+          int64_t work = lq ? lq : (causal ? L - n * rows : L);
+          // a causal window: the queries from n*rows to (n+1)*rows - 1 + W reach it
+          if (p->window > 0)
+            work = std::min<int64_t>(L, int64_t(n + 1) * rows - 1 + p->window) - int64_t(n) * rows;
+          tiles.push_back({b, h, n, int32_t(work)});
         }
       }
     }
