@@ -60,7 +60,7 @@ def flags_of(w, jfa):
         f |= jfa.CAUSAL
     if w.kind == "broadcast":
         f |= jfa.BROADCAST_Q
-    if w.kind == "block64":
+    if w.kind == "block":
         f |= jfa.BLOCK_DIAG64
     if w.rope_base:
         f |= jfa.ROTARY
@@ -74,7 +74,7 @@ def padded_ratio(case, w):
     if len(L) == 0 or L.sum() == 0:
         return 1.0
     m = int(L.max())
-    if w.kind == "block64":
+    if w.kind == "block":
         return float(len(L) * m * 64) / float(64 * L.sum())
     if w.kind == "broadcast":
         return float(len(L) * m * w.lq) / float(w.lq * L.sum())
@@ -106,13 +106,13 @@ def cpu_baseline(case, variants, budget_s=15.0):
                 npairs = w.lq * (e - s)
             else:
                 q_, do_ = f(case.q[s:e, h]), f(case.do[s:e, h])
-                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block64" else 0,
+                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block" else 0,
                                   window=w.window)
             if w.rope_base:
                 pos = np.arange(e - s)
                 q_ = R.rope(q_[:, None], pos, w.rope_base)[:, 0]
                 k_ = R.rope(k_[:, None], pos, w.rope_base)[:, 0]
-            if w.kind == "block64":
+            if w.kind == "block":
                 for r0 in range(0, e - s, 64):
                     sl = slice(r0, r0 + 64)
                     A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
@@ -305,11 +305,11 @@ def main():
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
-        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block64" else 0,
+        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block" else 0,
                           w.window)
         nhd = float(npairs) * w.num_heads * w.head_dim
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
-                         block=w.kind == "block64", fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
+                         block=w.kind == "block", fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
                          dq_flops=6.0 * nhd, dkdv_flops=8.0 * nhd,
                          fwd_ms=[], bwd_ms=[], dq_ms=[], dkdv_ms=[]))
     alt = None

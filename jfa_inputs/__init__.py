@@ -52,12 +52,12 @@ class Workload:
     num_heads: int
     head_dim: int
     sigma: float
-    kind: str = "jagged"        # "jagged" | "broadcast" | "block64"
+    kind: str = "jagged"        # "jagged" | "broadcast" | "block" (block-diagonal)
     causal: bool = False
     lq: int = 0                 # dense Q rows for "broadcast"
     seed: int = 0
     # length law
-    law: str = "uniform"        # "uniform" | "loguniform" | "block64" | "mix" | "fixed"
+    law: str = "uniform"        # "uniform" | "loguniform" | "blocks" | "mix" | "fixed"
     lo: int = 1
     hi: int = 1
     force_first_short: bool = False   # tiny: lengths[1] = 1
@@ -68,6 +68,7 @@ class Workload:
     pad_to_max: bool = False          # every length replaced by the largest drawn
     rope_base: float = 0.0            # rotary embeddings with this base (0: none)
     window: int = 0                   # causal sliding window of this many keys (0: none)
+    block: int = 64                   # kind "block": tokens per diagonal block
 
     @property
     def wid(self) -> int:
@@ -87,15 +88,22 @@ def standard_workloads():
                                causal=True),
         "broadcast": Workload("broadcast", 1024, 8, 128, 0.5, kind="broadcast", lq=256,
                               law="loguniform", lo=32, hi=2048),
-        "block64_d64": Workload("block64", 1152, 4, 64, 1.0, kind="block64", law="block64",
+        "block64_d64": Workload("block64", 1152, 4, 64, 1.0, kind="block", law="blocks",
                                 lo=1, hi=64),
-        "block64_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block64", law="block64",
+        "block64_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block", law="blocks",
                                  lo=1, hi=64),
+        # other block sizes, lengths drawn so that the batch holds as many tokens
+        "block32_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block", law="blocks",
+                                 lo=1, hi=128, block=32),
+        "block128_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block", law="blocks",
+                                  lo=1, hi=32, block=128),
+        "block256_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block", law="blocks",
+                                  lo=1, hi=16, block=256),
         # the same batches with rotary embeddings fused in (same seeds and values)
-        "block64_rope_d64": Workload("block64", 1152, 4, 64, 1.0, kind="block64",
-                                     law="block64", lo=1, hi=64, rope_base=10000.0),
-        "block64_rope_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block64",
-                                      law="block64", lo=1, hi=64, rope_base=10000.0),
+        "block64_rope_d64": Workload("block64", 1152, 4, 64, 1.0, kind="block",
+                                     law="blocks", lo=1, hi=64, rope_base=10000.0),
+        "block64_rope_d128": Workload("block64", 1152, 4, 128, 1.0, kind="block",
+                                      law="blocks", lo=1, hi=64, rope_base=10000.0),
         "imbalance": Workload("imbalance", 2048, 16, 128, 0.5, law="mix", lo=8, hi=64,
                               mix_long_frac=0.05, mix_long_lo=8192, mix_long_hi=16384),
         "gem_padded": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
@@ -131,8 +139,8 @@ def lengths(w: Workload) -> np.ndarray:
         # P(L = n) proportional to ln((n+1)/n) on [lo, hi]
         u = rng.uniform(math.log(w.lo), math.log(w.hi + 1), size=B)
         L = np.clip(np.floor(np.exp(u)).astype(np.int64), w.lo, w.hi)
-    elif w.law == "block64":
-        L = 64 * rng.integers(w.lo, w.hi + 1, size=B, dtype=np.int64)
+    elif w.law == "blocks":
+        L = w.block * rng.integers(w.lo, w.hi + 1, size=B, dtype=np.int64)
     elif w.law == "mix":
         n_long = int(round(w.mix_long_frac * B))
         long_ = rng.integers(w.mix_long_lo, w.mix_long_hi + 1, size=n_long, dtype=np.int64)
@@ -243,12 +251,12 @@ def make_case(w: Workload, with_do: bool = True) -> Case:
 
 
 def custom(lengths_, num_heads, head_dim, sigma=1.0, seed=0, kind="jagged", causal=False,
-           lq=0, name="custom", rope_base=0.0, window=0) -> Workload:
+           lq=0, name="custom", rope_base=0.0, window=0, block=64) -> Workload:
     """A workload with explicitly given lengths (edge cases, small tests)."""
     L = tuple(int(x) for x in lengths_)
     return Workload(name, len(L), num_heads, head_dim, sigma, kind=kind, causal=causal,
                     lq=lq, seed=seed, law="fixed", fixed_lengths=L, rope_base=rope_base,
-                    window=window)
+                    window=window, block=block)
 
 
 def to_torch_bf16(bits: np.ndarray):

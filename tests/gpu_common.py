@@ -37,7 +37,7 @@ def flags_of(w: J.Workload) -> int:
         f |= jfa.CAUSAL
     if w.kind == "broadcast":
         f |= jfa.BROADCAST_Q
-    if w.kind == "block64":
+    if w.kind == "block":
         f |= jfa.BLOCK_DIAG64
     if w.rope_base:
         f |= jfa.ROTARY
@@ -93,11 +93,11 @@ def oracle_full(case: J.Case):
     if w.kind == "broadcast":
         out, lse = A.broadcast_forward(q, k, v, off, case.scale)
         dq, dk, dv = A.broadcast_backward(q, k, v, do, off, case.scale)
-    elif w.kind == "block64" and w.rope_base:
+    elif w.kind == "block" and w.rope_base:
         out = R.block_diag_rope_forward(q, k, v, off, case.scale, w.rope_base)
         lse = None
         dq, dk, dv = R.block_diag_rope_backward(q, k, v, do, off, case.scale, w.rope_base)
-    elif w.kind == "block64":
+    elif w.kind == "block":
         out = A.block_diag_forward(q, k, v, off, case.scale)
         lse = None
         dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale)

@@ -400,6 +400,18 @@ def test_block_diag_matches_masked_sdpa():
         assert np.max(np.abs(a - b)) <= 1e-10
 
 
+@pytest.mark.parametrize("bs", [32, 128, 256])
+def test_other_block_sizes_match_masked_sdpa(bs):
+    L = [bs, 3 * bs, 0, 2 * bs]
+    q, k, v, do, off, sc = case64(L, 2, 16, seed=23)
+    out = A.block_diag_forward(q, k, v, off, sc, block=bs)
+    ref, rq, rk, rv = sdpa_packed(q, k, v, off, sc, False, grad_do=do, block=bs)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    dq, dk, dv = A.block_diag_backward(q, k, v, do, off, sc, block=bs)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.max(np.abs(a - b)) <= 1e-10
+
+
 def test_block_diag_rejects_partial_blocks():
     with pytest.raises(ValueError):
         A.refine_offsets(np.array([0, 64, 100]))

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
 
 
 def block_case(lengths, H, D, seed=0):
-    w = J.custom(lengths, H, D, seed=seed, kind="block64")
+    w = J.custom(lengths, H, D, seed=seed, kind="block")
     c = J.make_case(w)
     f = J.bf16_bits_to_f64
     return f(c.q), f(c.k), f(c.v), f(c.do), c.offsets.astype(np.int64), c.scale

@@ -68,7 +68,7 @@ def run_sampled(name, gpu, n_random=2, heads=None, long_heads=None):
             pos = np.arange(len(k_))
             rot = (lambda x, inv=False: R.rope(x[:, None], pos, w.rope_base, inv)[:, 0]) \
                 if w.rope_base else (lambda x, inv=False: x)
-            if w.kind == "block64":
+            if w.kind == "block":
                 qr, kr = rot(q_), rot(k_)
                 o_ref = np.zeros_like(q_)
                 gq, gk, gv = np.zeros_like(q_), np.zeros_like(k_), np.zeros_like(v_)

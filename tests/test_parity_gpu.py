@@ -81,7 +81,7 @@ def test_broadcast_identical_copies(gpu):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_block_diag(gpu, D):
-    check_case(J.custom([64, 192, 128, 64 * 7], 2, D, seed=9, kind="block64"), gpu)
+    check_case(J.custom([64, 192, 128, 64 * 7], 2, D, seed=9, kind="block"), gpu)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -89,7 +89,7 @@ def test_block_diag(gpu, D):
 def test_block_diag_rotary(gpu, D, base):
     # base 1.5 turns every column pair by up to about 10 revolutions; 1e9 leaves the
     # high columns nearly still
-    check_case(J.custom([64, 0, 192, 128, 64 * 7], 2, D, seed=9, kind="block64",
+    check_case(J.custom([64, 0, 192, 128, 64 * 7], 2, D, seed=9, kind="block",
                         rope_base=base), gpu)
 
 
@@ -137,7 +137,7 @@ def test_sliding_window_covering_every_sequence_is_causal(gpu):
 def test_block_diag_rotary_rows_are_not_plain_attention(gpu):
     # the rotation is applied: rotary and plain block attention differ on the GPU
     import torch
-    w = J.custom([128], 2, 64, seed=19, kind="block64")
+    w = J.custom([128], 2, 64, seed=19, kind="block")
     o_plain, _ = GpuRun(J.make_case(w), gpu).forward()
     o_rope, _ = GpuRun(J.make_case(w.with_(rope_base=10000.0)), gpu).forward()
     assert not torch.equal(o_plain, o_rope)
@@ -229,7 +229,7 @@ def test_run_to_run_bitwise(gpu):
 
 
 def test_block_diag_matches_jagged_path_on_refined_offsets(gpu):
-    w = J.custom([64, 256, 128], 2, 128, seed=16, kind="block64")
+    w = J.custom([64, 256, 128], 2, 128, seed=16, kind="block")
     case = J.make_case(w)
     blk = GpuRun(case, gpu)
     ob, _ = blk.forward()
