@@ -61,10 +61,16 @@ def flags_of(w, jfa):
     if w.kind == "broadcast":
         f |= jfa.BROADCAST_Q
     if w.kind == "block":
-        f |= jfa.BLOCK_DIAG64
+        f |= jfa.BLOCK_DIAG64 if w.block == 64 else jfa.BLOCK_DIAG
     if w.rope_base:
         f |= jfa.ROTARY
     return f
+
+
+def plan_kw(w):
+    """Plan arguments beyond the flags."""
+    return dict(rope_base=w.rope_base, window=w.window,
+                block=w.block if w.kind == "block" and w.block != 64 else 0)
 
 
 def padded_ratio(case, w):
@@ -75,7 +81,7 @@ def padded_ratio(case, w):
         return 1.0
     m = int(L.max())
     if w.kind == "block":
-        return float(len(L) * m * 64) / float(64 * L.sum())
+        return float(len(L) * m) / float(L.sum())
     if w.kind == "broadcast":
         return float(len(L) * m * w.lq) / float(w.lq * L.sum())
     if w.causal:
@@ -106,15 +112,15 @@ def cpu_baseline(case, variants, budget_s=15.0):
                 npairs = w.lq * (e - s)
             else:
                 q_, do_ = f(case.q[s:e, h]), f(case.do[s:e, h])
-                npairs = pairs_of([e - s], w.causal, block=64 if w.kind == "block" else 0,
+                npairs = pairs_of([e - s], w.causal, block=w.block if w.kind == "block" else 0,
                                   window=w.window)
             if w.rope_base:
                 pos = np.arange(e - s)
                 q_ = R.rope(q_[:, None], pos, w.rope_base)[:, 0]
                 k_ = R.rope(k_[:, None], pos, w.rope_base)[:, 0]
             if w.kind == "block":
-                for r0 in range(0, e - s, 64):
-                    sl = slice(r0, r0 + 64)
+                for r0 in range(0, e - s, w.block):
+                    sl = slice(r0, r0 + w.block)
                     A.seq_forward(q_[sl], k_[sl], v_[sl], case.scale)
                     dq_, dk_, _ = A.seq_backward(q_[sl], k_[sl], v_[sl], do_[sl], case.scale)
                     if w.rope_base:
@@ -149,7 +155,7 @@ def compare_rope(case, runs, q, k, v, do, dev, rounds, order):
     w = runs[0]["w"]
     plains = [jfa.Plan(case.offsets, r["w"].num_heads, r["w"].head_dim, case.scale,
                        flags_of(r["w"], jfa) & ~jfa.ROTARY, 0, order=order, device=dev,
-                       window=r["w"].window)
+                       **dict(plan_kw(r["w"]), rope_base=0.0))
               for r in runs]
     D = w.head_dim
     # positions inside the sequence, angles in float64, tables in bf16
@@ -244,7 +250,7 @@ def main():
     ap.add_argument("--workload", default="gem",
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
                              "block64_d128", "block64_rope_d64", "block64_rope_d128", "gem_rope",
-                             "gem_window",
+                             "gem_window", "block32_d128", "block128_d128", "block256_d128",
                              "imbalance", "gem_padded"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
@@ -301,21 +307,23 @@ def main():
         fl = flags_of(w, jfa)
         t0 = time.perf_counter()
         plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, fl, w.lq,
-                        order=order, device=dev, rope_base=w.rope_base, window=w.window)
+                        order=order, device=dev, **plan_kw(w))
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
-        npairs = pairs_of(case.lengths, w.causal, w.lq, 64 if w.kind == "block" else 0,
+        npairs = pairs_of(case.lengths, w.causal, w.lq, w.block if w.kind == "block" else 0,
                           w.window)
         nhd = float(npairs) * w.num_heads * w.head_dim
+        # "block": the single-tile kernels of 32- and 64-token blocks (one fused
+        # backward); 128- and 256-token blocks run the jagged kernels
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
-                         block=w.kind == "block", fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
+                         block=plan.block, fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
                          dq_flops=6.0 * nhd, dkdv_flops=8.0 * nhd,
                          fwd_ms=[], bwd_ms=[], dq_ms=[], dkdv_ms=[]))
     alt = None
     if args.compare_orders:
         alt = {name: [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
-                               w.lq, order=code, device=dev, rope_base=w.rope_base, window=w.window)
+                               w.lq, order=code, device=dev, **plan_kw(w))
                       for w in variants]
                for name, code in ORDERS.items()}
     torch.cuda.synchronize()
@@ -367,19 +375,28 @@ def main():
 
     # dominant kernel: the launch with the largest mean duration. Algorithmic work
     # per launch: fwd 4*N*H*D (Q K^T, P V); dQ pass 6*N*H*D (S, dP, dQ); dK/dV pass
-    # 8*N*H*D (S, dP, dV, dK); the fused 64-token block kernels are HBM-bound and
-    # are credited with the bytes of the bf16 tensors they must move.
+    # 8*N*H*D (S, dP, dV, dK). Block-diagonal kernels are HBM-bound and are
+    # credited with the bytes they must move: the fused single-tile kernels the bf16
+    # tensors they read and write; with 128- or 256-token blocks the forward q, k, v,
+    # out and lse, the dQ pass q, k, v, out, dO, lse, dq, -Di, -lse/scale, the dK/dV
+    # pass q, k, v, dO, -Di, -lse/scale, dk, dv.
     T = int(case.offsets[-1])
     cands = []
     for r in runs:
         w = r["w"]
         tag = w.name + ("_rope" if w.rope_base else "") + ("_causal" if w.causal else "") + \
             (f"_w{w.window}" if w.window else "")
+        tb = T * w.num_heads * w.head_dim * 2
+        vb = T * w.num_heads * 4
+        if w.kind == "block":
+            tag = f"block{w.block}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
         if r["block"]:
-            tag = f"{w.name}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
-            tb = T * w.num_heads * w.head_dim * 2
             cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
+        elif w.kind == "block":
+            cands.append((np.mean(r["fwd_ms"]), "fwd_kernel", tag, "hbm", 4.0 * tb + vb))
+            cands.append((np.mean(r["dq_ms"]), "dq_kernel", tag, "hbm", 6.0 * tb + 3.0 * vb))
+            cands.append((np.mean(r["dkdv_ms"]), "dkdv_kernel", tag, "hbm", 6.0 * tb + 2.0 * vb))
         else:
             bc = "_bcast" if w.kind == "broadcast" else ""
             cands.append((np.mean(r["fwd_ms"]), "fwd_kernel", tag, "mfma", r["fwd_flops"]))

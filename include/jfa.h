@@ -10,7 +10,10 @@
  *     batch ("Jagged Flash Attention for GEM", backward / dQ section);
  *   - 64-token block-diagonal attention, where each 64-token group attends only
  *     within itself, with a single-tile path that keeps no running statistics and
- *     stores no log-sum-exp ("TLX Block Attention", sections 1, 2 and 4);
+ *     stores no log-sum-exp ("TLX Block Attention", sections 1, 2 and 4); 32-token
+ *     blocks run on the same single-tile kernels, 128- and 256-token blocks as
+ *     jagged attention over the blocks (the page contrasts 64-token blocks with a
+ *     256-token minimum tile elsewhere);
  *   - rotary position embeddings of Q and K ("TLX Block Attention", summary and
  *     the section on the memory-bandwidth bound, where they are fused into the
  *     attention kernels): inside the block-diagonal kernels the rotated rows never
@@ -75,6 +78,8 @@ typedef enum jfa_status {
 #define JFA_BROADCAST_Q  2u  /* one dense Q [Lq,H,D] shared by every sequence (non-causal) */
 #define JFA_BLOCK_DIAG64 4u  /* 64-token block-diagonal self-attention (non-causal) */
 #define JFA_ROTARY       8u  /* rotary embeddings of Q and K (not with BROADCAST_Q) */
+#define JFA_BLOCK_DIAG  16u  /* block-diagonal self-attention with blocks of
+                                jfa_problem.block tokens (32, 64, 128 or 256) */
 
 /* schedule kinds and dealing orders */
 #define JFA_KIND_FWD 0
@@ -93,18 +98,22 @@ typedef struct jfa_problem {
   int32_t head_dim;   /* D: 64 or 128 */
   int32_t max_len;    /* >= every sequence length (checked by jfa_schedule_count) */
   int32_t lq;         /* BROADCAST_Q: rows of the dense Q (>= 1); otherwise 0 */
-  uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY */
+  uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY |
+                         JFA_BLOCK_DIAG */
   int64_t total_kv;   /* T = offsets[B], tokens in the packed K/V */
   float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
   float rope_base;    /* ROTARY: base of the rotary frequencies, finite, in (1, 1e9];
                          otherwise must be 0 */
   int32_t window;     /* CAUSAL only: W > 0 restricts query i to keys i - W < j <= i
                          (a causal sliding window); 0 = no window */
-  int32_t reserved;   /* must be 0 */
+  int32_t block;      /* BLOCK_DIAG: tokens per block, 32, 64, 128 or 256; with
+                         BLOCK_DIAG64 alone 0 or 64; otherwise 0 */
 } jfa_problem;
 
 /* Rows of Q per forward tile (kind FWD) or of K/V per backward tile (kind BWD)
- * that the kernels use for this head_dim and flags; -1 if unsupported. */
+ * that the kernels use for this head_dim and flags; -1 if unsupported.
+ * BLOCK_DIAG64: 64 (the single-tile unit); BLOCK_DIAG: the jagged tile rows, which
+ * the 128- and 256-token blocks use. */
 int32_t jfa_tile_rows(int32_t kind, int32_t head_dim, uint32_t flags);
 
 /* Number of persistent workgroups (slots) the schedule should be dealt over on
@@ -115,9 +124,12 @@ jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t flags, int
 
 /* Validate the host offsets against the problem and count the tiles of `kind`.
  * Checks: offsets[0] == 0, non-decreasing, offsets[B] == total_kv, every length
- * <= max_len, and for BLOCK_DIAG64 every length a multiple of 64. For
- * BLOCK_DIAG64 the count is the number of (64-block, head) units; no schedule is
- * needed for that mode. The argument `offsets_host` is host memory, B+1 ints. */
+ * <= max_len, and for block-diagonal problems every length a multiple of the
+ * block size. For blocks of 32 or 64 tokens the count is the number of (64-token
+ * unit, head) pairs the single-tile kernels run (no schedule is needed); for
+ * blocks of 128 or 256 tokens it is the number of tiles of the jagged problem
+ * whose sequences are the blocks (in order), which jfa_schedule deals. The
+ * argument `offsets_host` is host memory, B+1 ints. */
 jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
                               int64_t* num_tiles);
 
@@ -150,7 +162,9 @@ jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* offsets_host,
  *   slot_ptr [num_slots + 1]: tiles of slot s are tiles[slot_ptr[s] .. slot_ptr[s+1]).
  *   tiles    [capacity][4] int32 (b, h, t, work), grouped by slot in dealing order.
  * `capacity` must be >= the count from jfa_schedule_count. Not valid for
- * BLOCK_DIAG64 (UNSUPPORTED). Host only; no HIP call. */
+ * BLOCK_DIAG64 or for blocks of 32 or 64 tokens (UNSUPPORTED). For 128- and
+ * 256-token blocks the tiles' b is the block index (sequences in order, blocks in
+ * order inside each). Host only; no HIP call. */
 jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
                         int32_t order, int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
                         int64_t capacity);
@@ -159,14 +173,18 @@ jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32
  * lse, each rounded up to 256 bytes (-Di and -lse/scale, written by the dQ pass
  * and read by the dK/dV pass) and, for BROADCAST_Q, float32 dQ partials of
  * [G][Lq][H][D] where the B sequences are split into G = min(B, 64) contiguous
- * groups; for jagged ROTARY (without BLOCK_DIAG64) also two bf16 [T, H, D] regions,
- * each rounded up to 256 bytes, for the rotated copies of q and k; 0 for
- * BLOCK_DIAG64. 0 for an invalid problem. */
+ * groups; for 128- or 256-token blocks also the block offsets, (T/block + 1)
+ * int32 rounded up to 256 bytes; for ROTARY (except on blocks of 32 or 64
+ * tokens) also two bf16 [T, H, D] regions, each rounded up to 256 bytes, for the
+ * rotated copies of q and k; 0 for blocks of 32 or 64 tokens. 0 for an invalid
+ * problem. */
 size_t jfa_bwd_workspace_bytes(const jfa_problem* p);
 
-/* Bytes of device workspace jfa_fwd needs: for jagged ROTARY (without
- * BLOCK_DIAG64) two bf16 [T, H, D] regions, each rounded up to 256 bytes, that
- * receive the rotated copies of q and k; 0 otherwise and for an invalid problem. */
+/* Bytes of device workspace jfa_fwd needs: for 128- or 256-token blocks the block
+ * offsets, (T/block + 1) int32 rounded up to 256 bytes; for ROTARY (except on
+ * blocks of 32 or 64 tokens) two bf16 [T, H, D] regions, each rounded up to 256
+ * bytes, that receive the rotated copies of q and k; 0 otherwise and for an
+ * invalid problem. */
 size_t jfa_fwd_workspace_bytes(const jfa_problem* p);
 
 /* Forward ("TLX Block Attention", section 2: the online-softmax loop; section 3,
@@ -174,9 +192,10 @@ size_t jfa_fwd_workspace_bytes(const jfa_problem* p);
  *   q, k, v      device, bf16, layouts above.
  *   offsets_dev  device copy of the offsets the schedule was built from.
  *   slot_ptr_dev, tiles_dev, num_slots: device copy of a FWD schedule
- *                (ignored, may be NULL, for BLOCK_DIAG64).
+ *                (ignored, may be NULL, for blocks of 32 or 64 tokens).
  *   out          device, bf16, written for every valid query row.
- *   lse          device float32; must be NULL for BLOCK_DIAG64, non-NULL otherwise.
+ *   lse          device float32; must be NULL for blocks of 32 or 64 tokens,
+ *                non-NULL otherwise ([H, T] for 128- and 256-token blocks).
  *   workspace    device, >= jfa_fwd_workspace_bytes(p) bytes, 256-byte aligned;
  *                contents on entry are ignored and clobbered (jagged ROTARY: the
  *                rotated q and k). May be NULL when the size is 0.
@@ -195,13 +214,14 @@ jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const voi
  * No memory atomics are used: dQ is produced by a pass over query tiles and
  * dK/dV by a pass over key tiles, so dK and dV (and dQ) are bitwise reproducible.
  *   out, dout    device bf16 (out as written by jfa_fwd).
- *   lse          device float32 from jfa_fwd; NULL for BLOCK_DIAG64 (the block
- *                path recomputes the softmax statistics instead).
+ *   lse          device float32 from jfa_fwd; NULL for blocks of 32 or 64 tokens
+ *                (that path recomputes the softmax statistics instead).
  *   q_slot_ptr_dev, q_tiles_dev, q_num_slots: device copy of a FWD schedule; the
- *                dQ pass walks these query tiles. Ignored for BROADCAST_Q and
- *                BLOCK_DIAG64 (may be NULL).
+ *                dQ pass walks these query tiles. Ignored for BROADCAST_Q and for
+ *                blocks of 32 or 64 tokens (may be NULL).
  *   kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots: device copy of a BWD schedule;
- *                the dK/dV pass walks these key tiles. Ignored for BLOCK_DIAG64.
+ *                the dK/dV pass walks these key tiles. Ignored for blocks of 32 or
+ *                64 tokens.
  *   dq, dk, dv   device bf16 outputs (dq is [Lq,H,D] for BROADCAST_Q).
  *   workspace    device, >= jfa_bwd_workspace_bytes(p) bytes, 256-byte aligned;
  *                contents on entry are ignored and clobbered. May be NULL when the
@@ -223,10 +243,9 @@ jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const voi
  * overlapped on its own. Same arguments as jfa_bwd plus `passes`, a non-zero
  * mask of JFA_PASS_*. JFA_PASS_DKDV alone is valid only after a JFA_PASS_DQ call
  * with the same problem, inputs and workspace on the same stream (it reads the Di,
- * and for jagged ROTARY the rotated q and k, that pass left in the workspace); the
- * library cannot check this. BLOCK_DIAG64
- * runs one fused kernel and accepts JFA_PASS_ALL only (JFA_ERR_INVALID_ARG
- * otherwise). jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
+ * and for ROTARY the rotated q and k, that pass left in the workspace); the
+ * library cannot check this. Blocks of 32 or 64 tokens run one fused kernel and
+ * accept JFA_PASS_ALL only (JFA_ERR_INVALID_ARG otherwise). jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
 jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, const void* v,
                           const void* out, const void* dout, const float* lse,
                           const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,

@@ -17,13 +17,19 @@ GRAD_TOL = 2e-2     # max |g - oracle| / max |oracle| for dq, dk, dv
 LSE_TOL = 1e-3      # max |lse - oracle|
 # With rotary embeddings the kernels multiply the rotated rows of Q and K, which
 # are rounded to bf16 (the matrix cores take bf16 operands) where the oracle keeps
-# them exact: each score moves by up to ~2^-8 * scale * |q| |k|, on the order of
-# 1e-3 for the unit-variance rows of the tests, so the lse check gets twice the room.
-LSE_TOL_ROPE = 2e-3
-
-
-def lse_tol(w) -> float:
-    return LSE_TOL_ROPE if w.rope_base else LSE_TOL
+# them exact. Rounding a row q moves it by a vector of independent errors of
+# standard deviation 2^-9/sqrt(3) per element (relative), so the scores of that
+# row, and its lse, move by about 2^-9/sqrt(3) * scale * |q| |k| / sqrt(D)
+# (rows of typical norm |q|, |k|). The rotary lse check allows six of those,
+# and never less than the plain bound.
+def lse_tol(w, case=None) -> float:
+    if not w.rope_base or case is None:
+        return LSE_TOL
+    f = J.bf16_bits_to_f32
+    nq = float(np.sqrt(np.mean(np.sum(f(case.q).astype(np.float64) ** 2, axis=-1))))
+    nk = float(np.sqrt(np.mean(np.sum(f(case.k).astype(np.float64) ** 2, axis=-1))))
+    sd = 2.0 ** -9 / np.sqrt(3.0) * case.scale * nq * nk / np.sqrt(w.head_dim)
+    return max(LSE_TOL, 6.0 * sd)
 
 
 def log(msg):
@@ -38,7 +44,7 @@ def flags_of(w: J.Workload) -> int:
     if w.kind == "broadcast":
         f |= jfa.BROADCAST_Q
     if w.kind == "block":
-        f |= jfa.BLOCK_DIAG64
+        f |= jfa.BLOCK_DIAG64 if w.block == 64 else jfa.BLOCK_DIAG
     if w.rope_base:
         f |= jfa.ROTARY
     return f
@@ -63,7 +69,8 @@ class GpuRun:
         self.flags = flags_of(w)
         self.plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, self.flags,
                              w.lq, order=order, num_slots=num_slots, device=dev,
-                             rope_base=w.rope_base, window=w.window)
+                             rope_base=w.rope_base, window=w.window,
+                             block=w.block if w.kind == "block" and w.block != 64 else 0)
         self.q = to_dev(case.q, dev)
         self.k = to_dev(case.k, dev)
         self.v = to_dev(case.v, dev)
@@ -94,13 +101,17 @@ def oracle_full(case: J.Case):
         out, lse = A.broadcast_forward(q, k, v, off, case.scale)
         dq, dk, dv = A.broadcast_backward(q, k, v, do, off, case.scale)
     elif w.kind == "block" and w.rope_base:
-        out = R.block_diag_rope_forward(q, k, v, off, case.scale, w.rope_base)
-        lse = None
-        dq, dk, dv = R.block_diag_rope_backward(q, k, v, do, off, case.scale, w.rope_base)
+        out = R.block_diag_rope_forward(q, k, v, off, case.scale, w.rope_base, w.block)
+        dq, dk, dv = R.block_diag_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.block)
+        # blocks of 128 or 256 tokens run as jagged attention over the blocks and
+        # keep an lse: that of each block as its own sequence
+        lse = (R.jagged_rope_forward(q, k, v, A.refine_offsets(off, w.block), case.scale,
+                                     w.rope_base)[1] if w.block > 64 else None)
     elif w.kind == "block":
-        out = A.block_diag_forward(q, k, v, off, case.scale)
-        lse = None
-        dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale)
+        out = A.block_diag_forward(q, k, v, off, case.scale, w.block)
+        dq, dk, dv = A.block_diag_backward(q, k, v, do, off, case.scale, w.block)
+        lse = (A.jagged_forward(q, k, v, A.refine_offsets(off, w.block), case.scale)[1]
+               if w.block > 64 else None)
     elif w.rope_base:
         out, lse = R.jagged_rope_forward(q, k, v, off, case.scale, w.rope_base, w.causal, w.window)
         dq, dk, dv = R.jagged_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.causal,
@@ -115,14 +126,28 @@ def max_abs(a, b):
     return float(np.max(np.abs(a - b))) if a.size else 0.0
 
 
+# Extra out allowance, relative to the reference, for the block-size extension
+# workloads (blocks other than 64 tokens): a query there averages fewer values, so
+# outputs of unit-variance data reach 4 and more, where one bf16 rounding of the
+# stored output alone (half a grid step, 2^-9 relative) is 1.6e-2, above the
+# absolute bar. Those cases get 1e-2 + 2^-8 |ref| per element.
+def out_rel(w) -> float:
+    return 2.0 ** -8 if w.kind == "block" and w.block != 64 else 0.0
+
+
+def out_excess(got, ref, rel):
+    """max over elements of |got - ref| - rel * |ref| (the absolute part of the error)."""
+    return float(np.max(np.abs(got - ref) - rel * np.abs(ref))) if got.size else 0.0
+
+
 def rel_err(g, o):
     m = float(np.max(np.abs(o))) if o.size else 0.0
     return max_abs(g, o) / m if m > 0 else max_abs(g, o)
 
 
-def assert_out(got, ref, what="out"):
-    e = max_abs(got, ref)
-    log(f"  {what}: max abs err {e:.3e} (tol {OUT_TOL})")
+def assert_out(got, ref, what="out", rel=0.0):
+    e = out_excess(got, ref, rel)
+    log(f"  {what}: max abs err {e:.3e} (tol {OUT_TOL}" + (f" + {rel:.2e} |ref|)" if rel else ")"))
     assert np.all(np.isfinite(got)), what
     assert e <= OUT_TOL, (what, e)
 

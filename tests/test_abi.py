@@ -50,7 +50,13 @@ OFF = np.array([0, 10, 15], dtype=np.int32)
     (dict(num_heads=0), jfa.ERR_INVALID_ARG),
     (dict(scale=0.0), jfa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), jfa.ERR_INVALID_ARG),
-    (dict(flags=16), jfa.ERR_INVALID_ARG),
+    (dict(flags=32), jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.BLOCK_DIAG, block=48, total_kv=96, max_len=96), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BLOCK_DIAG64, block=128, total_kv=128, max_len=128), jfa.ERR_INVALID_ARG),
+    (dict(block=64), jfa.ERR_INVALID_ARG),
+    (dict(flags=jfa.BLOCK_DIAG | jfa.CAUSAL, block=128, total_kv=128, max_len=128),
+     jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BLOCK_DIAG, block=128, total_kv=192, max_len=192), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.ROTARY | jfa.BROADCAST_Q, lq=4, rope_base=10000.0), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.ROTARY), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64), jfa.ERR_INVALID_ARG),
@@ -72,6 +78,36 @@ def test_schedule_count_rejects(kw, status):
     with pytest.raises(jfa.JfaError) as e:
         jfa.schedule_count(_p(**kw), OFF, jfa.KIND_FWD)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("bs", [32, 128, 256])
+def test_other_block_sizes(bs):
+    L = np.array([bs, 3 * bs, 0, 2 * bs])
+    off = J.offsets_from_lengths(L)
+    p = _p(num_seqs=4, flags=jfa.BLOCK_DIAG, block=bs, total_kv=int(off[-1]), max_len=3 * bs)
+    with pytest.raises(jfa.JfaError):  # a length that is not a multiple of the block
+        jfa.schedule_count(p, np.array([0, bs + 1, 3 * bs, 3 * bs, int(off[-1])], dtype=np.int32),
+                           jfa.KIND_FWD)
+    n = jfa.schedule_count(p, off, jfa.KIND_FWD)
+    r256 = lambda x: (x + 255) // 256 * 256
+    if bs <= 64:   # 64-token units of the single-tile kernels, no schedule
+        assert n == -(-int(off[-1]) // 64) * 2
+        with pytest.raises(jfa.JfaError):
+            jfa.schedule(p, off, jfa.KIND_FWD, jfa.ORDER_ZIGZAG, 8)
+        assert jfa.fwd_workspace_bytes(p) == 0 and jfa.bwd_workspace_bytes(p) == 0
+        return
+    # the jagged tiles of the blocks, dealt as the reference deals blocks as sequences
+    nb = int(off[-1]) // bs
+    for kind in (jfa.KIND_FWD, jfa.KIND_BWD):
+        rows = jfa.tile_rows(kind, 64, jfa.BLOCK_DIAG)
+        assert jfa.schedule_count(p, off, kind) == nb * 2 * -(-bs // rows)
+        for order in (jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_FOLDED_ZIGZAG):
+            sp, tl = jfa.schedule(p, off, kind, order, 8)
+            sp2, tl2 = R.schedule([bs] * nb, 2, kind, rows, order, 8)
+            assert np.array_equal(sp, sp2) and np.array_equal(tl, tl2)
+    T = int(off[-1])
+    assert jfa.fwd_workspace_bytes(p) == r256((nb + 1) * 4)
+    assert jfa.bwd_workspace_bytes(p) == 2 * r256(2 * T * 4) + r256((nb + 1) * 4)
 
 
 def test_rotary_block_problem_accepted():
@@ -139,7 +175,7 @@ def test_fwd_bwd_reject_bad_pointers_before_any_hip_call():
         assert s == jfa.ERR_INVALID_ARG and b"passes" in L.jfa_last_error()
     s = L.jfa_bwd_passes(ctypes.byref(pb), fake, fake, fake, fake, fake, nul, fake, nul, nul, 0,
                          nul, nul, 0, fake, fake, fake, nul, 0, jfa.PASS_DQ, None)
-    assert s == jfa.ERR_INVALID_ARG and b"BLOCK_DIAG64" in L.jfa_last_error()
+    assert s == jfa.ERR_INVALID_ARG and b"fused backward" in L.jfa_last_error()
     # empty problems are no-ops that touch nothing
     p0 = _p(num_seqs=0, total_kv=0, max_len=0)
     assert L.jfa_fwd(ctypes.byref(p0), nul, nul, nul, nul, nul, nul, 0, nul, nul, nul, 0, None) == jfa.OK

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libjfa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY = 1, 2, 4, 8
+CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY, BLOCK_DIAG = 1, 2, 4, 8, 16
 KIND_FWD, KIND_BWD = 0, 1
 ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
@@ -40,7 +40,7 @@ class Problem(ctypes.Structure):
                 ("lq", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("total_kv", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("window", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("block", ctypes.c_int32)]
 
 
 _lib = None
@@ -90,9 +90,10 @@ def _check(status: int):
 
 
 def problem(num_seqs, num_heads, head_dim, max_len, total_kv, scale, flags=0, lq=0,
-            rope_base=0.0, window=0) -> Problem:
+            rope_base=0.0, window=0, block=0) -> Problem:
     return Problem(int(num_seqs), int(num_heads), int(head_dim), int(max_len), int(lq),
-                   int(flags), int(total_kv), float(scale), float(rope_base), int(window), 0)
+                   int(flags), int(total_kv), float(scale), float(rope_base), int(window),
+                   int(block))
 
 
 def tile_rows(kind: int, head_dim: int, flags: int = 0) -> int:
@@ -193,7 +194,8 @@ class Plan:
     """Everything one jagged problem needs on the device, built once.
 
     offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q; rope_base
-    for ROTARY; window (CAUSAL only) for a causal sliding window of that many keys.
+    for ROTARY; window (CAUSAL only) for a causal sliding window of that many keys;
+    block (BLOCK_DIAG) for the tokens per diagonal block.
     Builds the FWD and BWD schedules on the host (folded zigzag by default: the
     work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired so
     that they run side by side), copies them
@@ -202,16 +204,19 @@ class Plan:
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
                  order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda", rope_base=0.0,
-                 window=0):
+                 window=0, block=0):
         import torch
         off = _host_i32(offsets_host)
         L = np.diff(off.astype(np.int64))
         self.offsets_host = off
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
-                         int(off[-1]), scale, flags, lq, rope_base, window)
+                         int(off[-1]), scale, flags, lq, rope_base, window, block)
         self.device = torch.device(device)
         self.offsets_dev = torch.from_numpy(off.copy()).to(self.device)
-        self.block = bool(flags & BLOCK_DIAG64)
+        bs = 64 if flags & BLOCK_DIAG64 else (block if flags & BLOCK_DIAG else 0)
+        # blocks of 32 or 64 tokens: single-tile kernels, no schedule and no lse;
+        # blocks of 128 or 256 tokens are scheduled as jagged tiles over the blocks
+        self.block = 0 < bs <= 64
         self.sched = {}
         if self.block:
             schedule_count(self.p, off, KIND_FWD)  # validates the offsets

@@ -45,15 +45,29 @@ jfa_status check_workspace(void* workspace, size_t workspace_bytes, size_t ws) {
   return JFA_OK;
 }
 
-// Jagged ROTARY: rotated copies of q and k into `rot` (two rot_bytes regions),
-// walking the forward schedule given.
+// ROTARY on the tiled path: rotated copies of q and k into `rot` (two rot_bytes
+// regions), walking the forward schedule given over `num_seqs` sequences.
 jfa_status rotate_qk(const jfa_problem* p, const void* q, const void* k, char* rot,
-                     const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                     const int32_t* offsets_dev, int32_t num_seqs, const int32_t* slot_ptr_dev,
                      const int32_t* tiles_dev, int32_t num_slots, void* stream) {
   RopeRowsLaunch r{q, k, rot, rot + rot_bytes(p), offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
-                   p->num_seqs, p->num_heads, p->head_dim, p->total_kv,
+                   num_seqs, p->num_heads, p->head_dim, p->total_kv,
                    rope_table(p->rope_base, p->head_dim), stream};
   return launch_rope_rows(r);
+}
+
+// 128- and 256-token blocks run as the jagged problem whose sequences are the
+// blocks: their offsets go to the head of `ws`, and the launch reads them.
+template <typename Launch>
+jfa_status as_block_sequences(const jfa_problem* p, char*& ws, Launch& a, void* stream) {
+  const int64_t nb = p->total_kv / p->block;
+  int32_t* boff = reinterpret_cast<int32_t*>(ws);
+  if (jfa_status s = launch_block_offsets(boff, nb, p->block, stream)) return s;
+  ws += block_offsets_bytes(p);
+  a.offsets = boff;
+  a.num_seqs = int32_t(nb);
+  a.flags &= ~(JFA_BLOCK_DIAG | JFA_BLOCK_DIAG64);
+  return JFA_OK;
 }
 
 }  // namespace
@@ -87,7 +101,7 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
                               void* workspace, size_t workspace_bytes, void* stream) {
   set_error("");
   if (jfa_status s = check_problem(p)) return s;
-  const bool blk = p->flags & JFA_BLOCK_DIAG64;
+  const bool blk = unit_blocks(p);
   if (p->num_seqs == 0 || (q_rows(p) == 0 && p->total_kv == 0)) return JFA_OK;  // nothing to do
   if (q_rows(p) > 0) {
     if (jfa_status s = need(q, "q")) return s;
@@ -99,21 +113,25 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   }
   FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
               p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
-              p->rope_base, p->window, stream};
+              p->rope_base, p->window, block_size(p), stream};
   if (blk) {
-    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is stored)");
+    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for blocks of 32 or 64 tokens (no lse is stored)");
     if (p->total_kv == 0) return JFA_OK;
     return launch_block_fwd(a);
   }
   if (jfa_status s = need(lse, "lse", 4)) return s;
   if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
   if (jfa_status s = check_workspace(workspace, workspace_bytes, jfa_fwd_workspace_bytes(p))) return s;
+  char* ws = static_cast<char*>(workspace);
+  if (tiled_blocks(p) && p->total_kv > 0) {
+    if (jfa_status s = as_block_sequences(p, ws, a, stream)) return s;
+  }
   if (rot_bytes(p) > 0 && p->total_kv > 0) {
-    char* rot = static_cast<char*>(workspace);
-    if (jfa_status s = rotate_qk(p, q, k, rot, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, stream))
+    if (jfa_status s = rotate_qk(p, q, k, ws, a.offsets, a.num_seqs, slot_ptr_dev, tiles_dev,
+                                 num_slots, stream))
       return s;
-    a.q = rot;
-    a.k = rot + rot_bytes(p);
+    a.q = ws;
+    a.k = ws + rot_bytes(p);
   }
   return launch_fwd(a);
 }
@@ -130,9 +148,10 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   if (jfa_status s = check_problem(p)) return s;
   if (passes == 0 || (passes & ~JFA_PASS_ALL))
     return fail(JFA_ERR_INVALID_ARG, "passes must be a non-zero mask of JFA_PASS_DQ | JFA_PASS_DKDV");
-  if ((p->flags & JFA_BLOCK_DIAG64) && passes != JFA_PASS_ALL)
-    return fail(JFA_ERR_INVALID_ARG, "BLOCK_DIAG64 runs one fused backward kernel: passes must be JFA_PASS_ALL");
-  const bool blk = p->flags & JFA_BLOCK_DIAG64;
+  if (unit_blocks(p) && passes != JFA_PASS_ALL)
+    return fail(JFA_ERR_INVALID_ARG,
+                "blocks of 32 or 64 tokens run one fused backward kernel: passes must be JFA_PASS_ALL");
+  const bool blk = unit_blocks(p);
   const bool bq = p->flags & JFA_BROADCAST_Q;
   if (p->num_seqs == 0) return JFA_OK;
   if (q_rows(p) > 0) {
@@ -156,10 +175,11 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
   a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.rope_base = p->rope_base;
   a.window = p->window;
+  a.block = block_size(p);
   a.passes = passes;
   a.stream = stream;
   if (blk) {
-    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for BLOCK_DIAG64 (no lse is read)");
+    if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for blocks of 32 or 64 tokens (no lse is read)");
     if (p->total_kv == 0) return JFA_OK;
     return launch_block_bwd(a);
   }
@@ -181,13 +201,17 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.nls = reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p));
   a.groups = bcast_groups(p->num_seqs);
   a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * di_bytes(p)) : nullptr;
+  char* ws = static_cast<char*>(workspace) + 2 * di_bytes(p);  // after -Di and -lse/scale
+  if (tiled_blocks(p) && p->total_kv > 0) {
+    if (jfa_status s = as_block_sequences(p, ws, a, stream)) return s;
+  }
   RopeTab tab;
   if (rot_bytes(p) > 0 && p->total_kv > 0) {
     // the dQ pass rotates q and k into the workspace; the dK/dV pass reads the
     // copies it left there
-    char* rot = static_cast<char*>(workspace) + 2 * di_bytes(p);
+    char* rot = ws;
     if (passes & JFA_PASS_DQ) {
-      if (jfa_status s = rotate_qk(p, q, k, rot, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+      if (jfa_status s = rotate_qk(p, q, k, rot, a.offsets, a.num_seqs, q_slot_ptr_dev, q_tiles_dev,
                                    q_num_slots, stream))
         return s;
     }

@@ -11,6 +11,11 @@
 // puts the arithmetic intensity far below the ridge point), so each unit reads
 // its operands once and writes its outputs once.
 //
+// 32-token blocks run on the same kernels: a 64-token unit then holds two blocks
+// (block boundaries fall on multiples of 32 tokens everywhere), and each wave,
+// whose 32 query rows are one block, masks the other block's keys; the last unit
+// may hold a single block. Blocks of 128 or 256 tokens run on the jagged kernels.
+//
 // With rotary embeddings (the page fuses them into these kernels) the rows of Q
 // and K are rotated inside the kernel after they arrive in LDS, and the backward
 // turns dQ and dK back before storing them, so the rotated rows never travel
@@ -50,10 +55,30 @@ struct BlkParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; const uint16_t* o; const uint16_t* dout;
   uint16_t* out; uint16_t* dq; uint16_t* dk; uint16_t* dv;
   int32_t H;
-  float c;      // scale * log2(e)
+  int32_t rows;  // tokens T (the last 32-token-block unit may hold 32 of them)
+  float c;       // scale * log2(e)
   float scale;
-  Rope rope;    // rotary kernels only
+  Rope rope;     // rotary kernels only
 };
+
+// Rows of this unit that exist: 64, or with 32-token blocks up to 64.
+template <int BS>
+__device__ __forceinline__ int unit_rows(int rows, int blk) {
+  return BS == kBS ? kBS : min(kBS, rows - blk * kBS);
+}
+
+// With 32-token blocks, a wave's queries (its block) meet only their own keys.
+template <int BS>
+__device__ __forceinline__ void mask_other_block(f32x16 (&s)[2], int w) {
+  if (BS == 32) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb != w) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+      }
+  }
+}
 
 __device__ __forceinline__ void rope_cs(float p, int i, const Rope& R, float& c, float& s) {
   float rev = p * exp2_fast(float(i) * R.kr + R.kc);
@@ -157,7 +182,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[2], float c) {
     for (int r = 0; r < 16; ++r) s[kb][r] *= inv;
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, int BS>
 __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
   // K, V, then the two waves' output staging tiles (32 x D each; with ROPE they
@@ -170,12 +195,13 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
-  tile_load<D, kBS, C::NW>(lds, rows_rsrc<D>(P.k + base, rstride, kBS), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D>(P.v + base, rstride, kBS), rowbytes, w, lane);
+  const int nrows = unit_rows<BS>(P.rows, blk);
+  tile_load<D, kBS, C::NW>(lds, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
   u32x4 qf[C::DS];
   if (ROPE) {
     uint16_t* Qt = lds + 2 * C::TILE;
-    tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, kBS), rowbytes, w, lane);
+    tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
     wait_vmem();
     __syncthreads();
     rope_tiles<D, C::NW>(lds, Qt, P.rope, w, lane);
@@ -184,8 +210,9 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
     for (int d = 0; d < C::DS; ++d) qf[d] = frag_rows<D>(Qt, w * 32, d, li, g);
   } else {
     const uint16_t* qrow = P.q + base + int64_t(w * 32 + li) * rstride;
+    const bool ok = w * 32 + li < nrows;
 #pragma unroll
-    for (int d = 0; d < C::DS; ++d) qf[d] = ld16(qrow + d * 16 + g * 8);
+    for (int d = 0; d < C::DS; ++d) qf[d] = ok ? ld16(qrow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
     wait_vmem();
     __syncthreads();
   }
@@ -197,6 +224,7 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   for (int d = 0; d < C::DS; ++d)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(frag_rows<D>(lds, kb * 32, d, li, g), qf[d], s[kb]);
+  mask_other_block<BS>(s, w);
   // one tile: the row max and sum are exact at once, nothing is rescaled
   tile_softmax(s, P.c);
   u32x4 pf[4];
@@ -212,10 +240,10 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
     for (int st = 0; st < 4; ++st) o[nb] = mfma32(frag_cols<D>(lds + C::TILE, st * 16, nb * 32, lane), pf[st], o[nb]);
   }
   store_rows<D>(lds + 2 * C::TILE + w * (C::TILE / 2), o, 1.f, P.out + base + int64_t(w * 32) * rstride,
-                rstride, 32, lane);
+                rstride, nrows - w * 32, lane);
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, int BS>
 __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   using C = BlkCfg<D>;
   // K, V, Q, dO tiles (64 x D) and P^T, dS^T tiles (64 queries x 64 keys)
@@ -233,16 +261,17 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   const int64_t rstride = int64_t(P.H) * D;
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
-  tile_load<D, kBS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, kBS), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, kBS), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, kBS), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, kBS), rowbytes, w, lane);
+  const int nrows = unit_rows<BS>(P.rows, blk);
+  tile_load<D, kBS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, nrows), rowbytes, w, lane);
   // out fragments of this lane's query row, for Di = rowsum(dO * out)
   const int i = w * 32 + li;
   u32x4 of[C::DS];
   const uint16_t* orow = P.o + base + int64_t(i) * rstride;
 #pragma unroll
-  for (int d = 0; d < C::DS; ++d) of[d] = ld16(orow + d * 16 + g * 8);
+  for (int d = 0; d < C::DS; ++d) of[d] = i < nrows ? ld16(orow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
   wait_vmem();
   __syncthreads();
   if (ROPE) {
@@ -273,6 +302,7 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
     }
   }
   di = pair_sum(di);
+  mask_other_block<BS>(s, w);
   tile_softmax(s, P.c);  // statistics recomputed here: no lse is stored or read
   u32x4 pds[4];
 #pragma unroll
@@ -308,7 +338,7 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   // K and V are not read after this point: their tiles stage the outputs (each
   // wave a private 32 x D half of K for dQ, and of V for dV, then dK)
   store_rows<D>(Kt + w * (C::TILE / 2), dqa, P.scale, P.dq + base + int64_t(w * 32) * rstride, rstride,
-                32, lane);
+                nrows - w * 32, lane);
 
   // ---- key side (lane = key): dV^T = dO^T P, dK^T = Q^T dS
   u32x4 pb[4], db[4];
@@ -329,9 +359,9 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
     }
   }
   uint16_t* vst = Vt + w * (C::TILE / 2);
-  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, 32, lane);
+  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, nrows - w * 32, lane);
   if (ROPE) rope_back<D>(ak, float(i), g, P.rope);
-  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, 32, lane);
+  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, nrows - w * 32, lane);
 }
 
 Rope rope_consts(float base, int D) {
@@ -353,13 +383,18 @@ jfa_status launch_fwd_t(const jfa::FwdLaunch& a) {
   P.scale = a.scale;
   const bool rope = a.flags & JFA_ROTARY;
   if (rope) P.rope = rope_consts(a.rope_base, D);
-  const int64_t units = (a.total_kv / kBS) * a.num_heads;
+  P.rows = int32_t(a.total_kv);
+  const int64_t units = ((a.total_kv + kBS - 1) / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
-  if (rope)
-    hipLaunchKernelGGL((block_fwd_kernel<D, true>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
-  else
-    hipLaunchKernelGGL((block_fwd_kernel<D, false>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
+  const dim3 grid{unsigned(units)}, block{unsigned(BlkCfg<D>::NT)};
+  if (a.block == 32) {
+    if (rope) hipLaunchKernelGGL((block_fwd_kernel<D, true, 32>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((block_fwd_kernel<D, false, 32>), grid, block, 0, st, P);
+  } else {
+    if (rope) hipLaunchKernelGGL((block_fwd_kernel<D, true, kBS>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((block_fwd_kernel<D, false, kBS>), grid, block, 0, st, P);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block fwd launch: ") + hipGetErrorString(e));
   return JFA_OK;
@@ -381,21 +416,40 @@ jfa_status launch_bwd_t(const jfa::BwdLaunch& a) {
   P.scale = a.scale;
   const bool rope = a.flags & JFA_ROTARY;
   if (rope) P.rope = rope_consts(a.rope_base, D);
-  const int64_t units = (a.total_kv / kBS) * a.num_heads;
+  P.rows = int32_t(a.total_kv);
+  const int64_t units = ((a.total_kv + kBS - 1) / kBS) * a.num_heads;
   if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
-  if (rope)
-    hipLaunchKernelGGL((block_bwd_kernel<D, true>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
-  else
-    hipLaunchKernelGGL((block_bwd_kernel<D, false>), dim3(unsigned(units)), dim3(BlkCfg<D>::NT), 0, st, P);
+  const dim3 grid{unsigned(units)}, block{unsigned(BlkCfg<D>::NT)};
+  if (a.block == 32) {
+    if (rope) hipLaunchKernelGGL((block_bwd_kernel<D, true, 32>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((block_bwd_kernel<D, false, 32>), grid, block, 0, st, P);
+  } else {
+    if (rope) hipLaunchKernelGGL((block_bwd_kernel<D, true, kBS>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((block_bwd_kernel<D, false, kBS>), grid, block, 0, st, P);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("block bwd launch: ") + hipGetErrorString(e));
   return JFA_OK;
 }
 
+__global__ void __launch_bounds__(256) block_offsets_kernel(int32_t* out, int32_t n, int32_t block) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i <= n) out[i] = i * block;
+}
+
 }  // namespace
 
 namespace jfa {
+
+jfa_status launch_block_offsets(int32_t* out, int64_t n, int32_t block, void* stream) {
+  if (n >= INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "too many blocks");
+  hipLaunchKernelGGL(block_offsets_kernel, dim3(unsigned(n / 256 + 1)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), out, int32_t(n), block);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, std::string("block offsets launch: ") + hipGetErrorString(e));
+  return JFA_OK;
+}
 
 jfa_status launch_block_fwd(const FwdLaunch& a) {
   return a.head_dim == 128 ? launch_fwd_t<128>(a) : launch_fwd_t<64>(a);

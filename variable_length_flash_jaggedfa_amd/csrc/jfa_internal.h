@@ -24,6 +24,21 @@ jfa_status fail(jfa_status s, const std::string& msg);
 // host validation of the problem descriptor (no HIP calls)
 jfa_status check_problem(const jfa_problem* p);
 
+// Tokens per diagonal block of a validated problem (0 if not block-diagonal).
+inline int block_size(const jfa_problem* p) {
+  if (p->flags & JFA_BLOCK_DIAG) return p->block;
+  return (p->flags & JFA_BLOCK_DIAG64) ? kBlock : 0;
+}
+// blocks that one single-tile unit covers (32 or 64 tokens): no schedule, no lse
+inline bool unit_blocks(const jfa_problem* p) {
+  const int bs = block_size(p);
+  return bs > 0 && bs <= kBlock;
+}
+// blocks run as jagged attention over the blocks (128 or 256 tokens)
+inline bool tiled_blocks(const jfa_problem* p) { return block_size(p) > kBlock; }
+// bytes of the block offsets of a tiled-block problem (rounded up to 256), else 0
+size_t block_offsets_bytes(const jfa_problem* p);
+
 // Rotary angle of one position step, in revolutions: rev[i] = base^(-2i/D) / (2 pi)
 // for i < D/2 (the jagged kernels form p * rev[i] in double precision).
 struct RopeTab {
@@ -43,6 +58,7 @@ struct FwdLaunch {
   uint32_t flags;
   float rope_base;  // ROTARY only
   int32_t window;   // causal sliding window (0: none)
+  int32_t block;    // single-tile block kernels: tokens per block (32 or 64)
   void* stream;
 };
 
@@ -63,6 +79,7 @@ struct BwdLaunch {
   uint32_t flags;
   float rope_base;  // ROTARY only
   int32_t window;   // causal sliding window (0: none)
+  int32_t block;    // single-tile block kernels: tokens per block (32 or 64)
   uint32_t passes;  // JFA_PASS_* mask
   const RopeTab* rope;  // jagged ROTARY: q and k are the rotated copies, dq and dk
                         // are turned back in the epilogues; otherwise NULL
@@ -92,6 +109,8 @@ jfa_status launch_bwd(const BwdLaunch& a);
 jfa_status launch_block_fwd(const FwdLaunch& a);
 jfa_status launch_block_bwd(const BwdLaunch& a);
 jfa_status launch_rope_rows(const RopeRowsLaunch& a);
+// offsets of consecutive blocks of `block` tokens: out[i] = i * block, i <= n
+jfa_status launch_block_offsets(int32_t* out, int64_t n, int32_t block, void* stream);
 jfa_status fwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
 jfa_status bwd_slots_per_cu(int head_dim, uint32_t flags, int* per_cu);
 

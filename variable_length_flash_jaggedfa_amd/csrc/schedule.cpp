@@ -32,18 +32,25 @@ jfa_status check_problem(const jfa_problem* p) {
   if (p->total_kv < 0) return fail(JFA_ERR_INVALID_ARG, "total_kv < 0");
   if (!(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(JFA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY;
+  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY | JFA_BLOCK_DIAG;
   if (p->flags & ~known) return fail(JFA_ERR_INVALID_ARG, "unknown flag bits");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   const bool causal = p->flags & JFA_CAUSAL, bq = p->flags & JFA_BROADCAST_Q,
-             blk = p->flags & JFA_BLOCK_DIAG64;
+             blk = p->flags & (JFA_BLOCK_DIAG64 | JFA_BLOCK_DIAG);
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
-  if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 with other flags");
+  if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "block-diagonal with other flags");
+  if (p->flags & JFA_BLOCK_DIAG) {
+    if (p->block != 32 && p->block != 64 && p->block != 128 && p->block != 256)
+      return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG needs block 32, 64, 128 or 256");
+    if ((p->flags & JFA_BLOCK_DIAG64) && p->block != 64)
+      return fail(JFA_ERR_INVALID_ARG, "BLOCK_DIAG64 with a block other than 64");
+  } else if ((p->flags & JFA_BLOCK_DIAG64) ? (p->block != 0 && p->block != 64) : p->block != 0) {
+    return fail(JFA_ERR_INVALID_ARG, "block must be 0 (or 64 with BLOCK_DIAG64) without BLOCK_DIAG");
+  }
   if (p->window < 0) return fail(JFA_ERR_INVALID_ARG, "window < 0");
   if (p->window > 0 && !causal)
     return fail(JFA_ERR_UNSUPPORTED, "a sliding window needs CAUSAL (jagged self-attention)");
-  if (p->reserved != 0) return fail(JFA_ERR_INVALID_ARG, "reserved field must be 0");
   if (p->flags & JFA_ROTARY) {
     if (bq) return fail(JFA_ERR_UNSUPPORTED, "ROTARY with BROADCAST_Q (the dense Q rows have no positions)");
     if (!(std::isfinite(p->rope_base) && p->rope_base > 1.f && p->rope_base <= 1e9f))
@@ -53,8 +60,8 @@ jfa_status check_problem(const jfa_problem* p) {
   }
   if (bq && p->lq < 1) return fail(JFA_ERR_INVALID_ARG, "BROADCAST_Q needs lq >= 1");
   if (!bq && p->lq != 0) return fail(JFA_ERR_INVALID_ARG, "lq must be 0 without BROADCAST_Q");
-  if (blk && (p->total_kv % kBlock))
-    return fail(JFA_ERR_INVALID_ARG, "BLOCK_DIAG64 needs total_kv % 64 == 0");
+  if (blk && (p->total_kv % block_size(p)))
+    return fail(JFA_ERR_INVALID_ARG, "block-diagonal needs total_kv to be a multiple of the block");
   // element counts must stay addressable with 64-bit offsets and tiles in int32
   const double elems = double(std::max<int64_t>(p->total_kv, p->lq)) * p->num_heads * p->head_dim;
   if (elems > 4.0e15) return fail(JFA_ERR_INVALID_ARG, "problem too large");
@@ -79,9 +86,9 @@ jfa_status check_offsets(const jfa_problem* p, const int32_t* off) {
     if (L < 0) return fail(JFA_ERR_INVALID_ARG, "offsets decrease at sequence " + std::to_string(b));
     if (L > p->max_len)
       return fail(JFA_ERR_INVALID_ARG, "sequence " + std::to_string(b) + " longer than max_len");
-    if ((p->flags & JFA_BLOCK_DIAG64) && (L % kBlock))
-      return fail(JFA_ERR_INVALID_ARG,
-                  "BLOCK_DIAG64: length of sequence " + std::to_string(b) + " is not a multiple of 64");
+    if (block_size(p) > 0 && (L % block_size(p)))
+      return fail(JFA_ERR_INVALID_ARG, "block-diagonal: length of sequence " + std::to_string(b) +
+                                           " is not a multiple of the block size");
   }
   if (off[p->num_seqs] != p->total_kv) return fail(JFA_ERR_INVALID_ARG, "offsets[B] != total_kv");
   return JFA_OK;
@@ -142,8 +149,13 @@ extern "C" jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* of
   if (!num_tiles) return fail(JFA_ERR_INVALID_ARG, "num_tiles is NULL");
   if (kind != JFA_KIND_FWD && kind != JFA_KIND_BWD) return fail(JFA_ERR_INVALID_ARG, "bad kind");
   if (jfa_status s = check_offsets(p, offsets_host)) return s;
-  if (p->flags & JFA_BLOCK_DIAG64) {
-    *num_tiles = (p->total_kv / kBlock) * p->num_heads;
+  if (unit_blocks(p)) {  // (64-token unit, head) pairs; 32-token blocks pair up in a unit
+    *num_tiles = ((p->total_kv + kBlock - 1) / kBlock) * p->num_heads;
+    return JFA_OK;
+  }
+  if (tiled_blocks(p)) {  // the jagged tiles of the blocks
+    const int32_t rows = jfa_tile_rows(kind, p->head_dim, JFA_BLOCK_DIAG);
+    *num_tiles = (p->total_kv / p->block) * p->num_heads * ceil_div(p->block, rows);
     return JFA_OK;
   }
   const bool lqmode = (p->flags & JFA_BROADCAST_Q) && kind == JFA_KIND_FWD;
@@ -163,8 +175,8 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
                                    int32_t* tiles_out, int64_t capacity) {
   int64_t count = 0;
   if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
-  if (p->flags & JFA_BLOCK_DIAG64)
-    return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG64 runs without a schedule");
+  if (unit_blocks(p))
+    return fail(JFA_ERR_UNSUPPORTED, "blocks of 32 or 64 tokens run without a schedule");
   if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG &&
       order != JFA_ORDER_FOLDED_ZIGZAG)
     return fail(JFA_ERR_INVALID_ARG, "bad order");
@@ -173,7 +185,21 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   if (count > 0 && !tiles_out) return fail(JFA_ERR_INVALID_ARG, "tiles is NULL");
   if (capacity < count) return fail(JFA_ERR_INVALID_ARG, "tiles capacity too small");
 
-  const std::vector<Tile> tiles = enumerate(p, offsets_host, kind);
+  // 128- and 256-token blocks: the tiles of the jagged problem whose sequences are
+  // the blocks, in order
+  jfa_problem pb = *p;
+  std::vector<int32_t> boff;
+  if (tiled_blocks(p)) {
+    const int32_t nb = int32_t(p->total_kv / p->block);
+    boff.resize(size_t(nb) + 1);
+    for (int32_t i = 0; i <= nb; ++i) boff[i] = i * p->block;
+    pb.num_seqs = nb;
+    pb.max_len = p->block;
+    pb.flags = p->flags & ~(JFA_BLOCK_DIAG | JFA_BLOCK_DIAG64);
+    pb.block = 0;
+  }
+  const std::vector<Tile> tiles = tiled_blocks(p) ? enumerate(&pb, boff.data(), kind)
+                                                  : enumerate(p, offsets_host, kind);
   std::vector<int32_t> idx;      // tiles in dealing order
   std::vector<int32_t> slot_of;  // slot of idx[j]
   auto by_work = [&](int32_t a, int32_t b) { return tiles[a].work > tiles[b].work; };
@@ -299,24 +325,29 @@ size_t di_bytes(const jfa_problem* p) {
 }
 
 size_t rot_bytes(const jfa_problem* p) {
-  if (!(p->flags & JFA_ROTARY) || (p->flags & JFA_BLOCK_DIAG64)) return 0;
+  if (!(p->flags & JFA_ROTARY) || unit_blocks(p)) return 0;
   return (size_t(p->total_kv) * p->num_heads * p->head_dim * 2 + 255) / 256 * 256;
+}
+
+size_t block_offsets_bytes(const jfa_problem* p) {
+  if (!tiled_blocks(p)) return 0;
+  return (size_t(p->total_kv / p->block + 1) * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 }  // namespace jfa
 
 extern "C" size_t jfa_bwd_workspace_bytes(const jfa_problem* p) {
   if (!p || check_problem(p) != JFA_OK) return 0;
-  if (p->flags & JFA_BLOCK_DIAG64) return 0;
-  size_t bytes = 2 * di_bytes(p);  // -Di and -lse/scale, each laid out like lse
+  if (unit_blocks(p)) return 0;
+  size_t bytes = 2 * di_bytes(p) + block_offsets_bytes(p);  // -Di, -lse/scale; block offsets
   if (p->flags & JFA_BROADCAST_Q)
     bytes += size_t(bcast_groups(p->num_seqs)) * p->lq * p->num_heads * p->head_dim * sizeof(float);
-  return bytes + 2 * rot_bytes(p);  // rotated q and k (jagged ROTARY)
+  return bytes + 2 * rot_bytes(p);  // rotated q and k (ROTARY)
 }
 
 extern "C" size_t jfa_fwd_workspace_bytes(const jfa_problem* p) {
   if (!p || check_problem(p) != JFA_OK) return 0;
-  return 2 * rot_bytes(p);
+  return block_offsets_bytes(p) + 2 * rot_bytes(p);
 }
 
 extern "C" const char* jfa_status_string(jfa_status s) {
