@@ -168,6 +168,17 @@ def test_tile_boundaries(gpu):
                         causal=True), gpu)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_partial_last_tiles(gpu, D, causal):
+    # last query tiles that end inside each of the four 32-row waves (and tiles
+    # whose later waves hold no row), last key tiles that end inside each
+    # 32-key block: causal waves stop at different steps, waves and key blocks
+    # with no row do no work
+    lengths = [1, 31, 32, 33, 95, 96, 97, 160, 161, 223, 224, 225, 383, 415]
+    check_case(J.custom(lengths, 2, D, sigma=0.5, seed=28, causal=causal), gpu)
+
+
 def test_all_length_one(gpu):
     check_case(J.custom([1] * 40, 2, 64, seed=12), gpu)
 

@@ -155,10 +155,12 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
 // reads the rows of stage kt and the columns of stage kt-1 of a four-stage ring,
 // so the load issued at step kt (stage kt+2) goes to the buffer of stage kt-2.
 // Steps [0, n_lo) (window edge) and [n_free, n_steps) (tail, diagonal) are masked.
+// The wave computes steps [0, n_own) only and meets the barriers and issues its
+// loads for the rest.
 template <int D, bool CAUSAL, bool WIN = false>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
                                           int64_t rstride, int L, int n_keys, int n_lo, int n_free,
-                                          int win,
+                                          int n_own, int win,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
@@ -215,10 +217,14 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     };
     int kt = 1;
     if (WIN)
-      for (; kt < n_lo; ++kt) step(kt, std::true_type{});
-    for (; kt < n_free; ++kt) step(kt, std::false_type{});
-    for (; kt < n_steps; ++kt) step(kt, std::true_type{});
-    dq_accumulate<D>(ks_of(n_steps - 1), lo, pds, acc);
+      for (; kt < min(n_lo, n_own); ++kt) step(kt, std::true_type{});
+    for (; kt < min(n_free, n_own); ++kt) step(kt, std::false_type{});
+    for (; kt < n_own; ++kt) step(kt, std::true_type{});
+    dq_accumulate<D>(ks_of(n_own - 1), lo, pds, acc);
+    for (; kt < n_steps; ++kt) {  // the steps this wave leaves out
+      arrive(kt);
+      if (kt + C::NS - 2 < n_steps) load_stage(kt + C::NS - 2);
+    }
   }
   __syncthreads();  // the next stream's first loads overwrite the first stages
 }
@@ -272,6 +278,9 @@ dq_kernel(DqParams P) {
     const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
     const int qpos = q_first + w * 32 + (lane & 31);
     const bool ok = qpos < L;
+    // steps this wave computes: all, or one when the tile has no row for it
+    // (nothing of it is stored)
+    const int n_own = w * 32 < q_rows ? n_steps : 1;
     const int64_t row = int64_t(kv0) + qpos;
     const int64_t eoff = row * rstride + int64_t(h) * D;
     u32x4 qf[C::DS], dof[C::DS];
@@ -288,8 +297,8 @@ dq_kernel(DqParams P) {
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
     dq_stream<D, CAUSAL, WIN>(lds, P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D,
                               P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D, rstride, L - ks0,
-                              n_keys, n_lo, n_free, P.window, qf, dof, acc, lse2, di, P.c, w, lane,
-                              qpos - ks0, lo);
+                              n_keys, n_lo, n_free, n_own, P.window, qf, dof, acc, lse2, di, P.c, w,
+                              lane, qpos - ks0, lo);
     // dq_stream ended with a barrier: the ring is free to stage the output rows
     if (ROPE) rope_back_rows<D>(acc, qpos, g, rope_tab);
     const int row0 = q_first + w * 32;
@@ -334,7 +343,8 @@ dq_bcast_kernel(DqParams P) {
     if (L > 0)
       dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
                           P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, 0, L / C::BN,
-                          0, qf, dof, acc, lse2, di, P.c, w, lane, qpos, lo);
+                          t * C::BM + w * 32 < P.lq ? ceil_div(L, C::BN) : 1, 0, qf, dof, acc, lse2,
+                          di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;
@@ -706,15 +716,28 @@ dkdv_kernel(KvParams P) {
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
       using S2 = std::integral_constant<int, 2>;
-      for (int it = 0; it < T.n_steps; it += 3) {
-        step(it, S0{});
-        if (it + 1 < T.n_steps) step(it + 1, S1{});
-        if (it + 2 < T.n_steps) step(it + 2, S2{});
+      if (row0 >= T.L) {
+        // no key of the sequence in this pair's block (last tile of a sequence):
+        // the pair only meets the barriers and issues its share of the loads;
+        // its zero accumulators are stored range-checked, i.e. not at all
+        for (int it = 0; it < T.n_steps; ++it) {
+          if (it == 0 && ti > t_begin) wait_vmem_le<D / 16>();
+          else wait_vmem();
+          __syncthreads();
+          if (it + 1 < T.n_steps) load_stage(T, it + 1);
+        }
+        __syncthreads();  // the tail's barrier
+      } else {
+        for (int it = 0; it < T.n_steps; it += 3) {
+          step(it, S0{});
+          if (it + 1 < T.n_steps) step(it + 1, S1{});
+          if (it + 2 < T.n_steps) step(it + 2, S2{});
+        }
+        const int last = (T.n_steps - 1) % C::NS;
+        if (last == 0) tail(S0{});
+        else if (last == 1) tail(S1{});
+        else tail(S2{});
       }
-      const int last = (T.n_steps - 1) % C::NS;
-      if (last == 0) tail(S0{});
-      else if (last == 1) tail(S1{});
-      else tail(S2{});
       __syncthreads();  // every wave is done with the ring and the exchange
       const Tile Tc = T;
       if (ti + 1 < t_end) {

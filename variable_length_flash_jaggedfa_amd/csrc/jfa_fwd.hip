@@ -243,6 +243,13 @@ fwd_kernel(FwdParams P) {
     const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
     const int qpos = q_first + w * 32 + li;  // query position of this lane
     const int qm = qpos - ks0;                // the same, counted from key ks0
+    // Steps this wave computes: all, or one when the tile has no row for it
+    // (last tile of a sequence; nothing of it is stored). A wave that computes
+    // fewer still meets the workgroup's barriers and issues its share of every
+    // stage's loads. Causal kernels compute every step: stopping causal waves
+    // after their own diagonal step saves no time, because the waves of a
+    // workgroup move in lock-step and a step lasts as long as its busiest wave.
+    const int n_own = CAUSAL || w * 32 < q_rows ? n_steps : 1;
     const uint16_t* kbase = P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
     const int Lk = L - ks0;
@@ -296,6 +303,7 @@ fwd_kernel(FwdParams P) {
         if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
       };
       int kt = 0;
+      const int n_free_own = CAUSAL ? n_free : min(n_free, n_own);
       if (WIN) {
         for (; kt + 1 < n_lo; ++kt) {  // the next step meets the window's lower edge
           advance(kt);
@@ -308,7 +316,7 @@ fwd_kernel(FwdParams P) {
         }
       }
       // two unmasked steps per iteration, the score registers swapping roles
-      for (; kt + 2 < n_free; kt += 2) {
+      for (; kt + 2 < n_free_own; kt += 2) {
         advance(kt);
         float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                    qf, sc, sn, o, m, l, P.c, lane,
@@ -320,7 +328,7 @@ fwd_kernel(FwdParams P) {
                                              (kt + 2) * C::BN, n_keys, qm, P.window);
         update_max<D>(mx, m, l, o);
       }
-      for (; kt + 1 < n_free; ++kt) {  // the next step needs no mask
+      for (; kt + 1 < n_free_own; ++kt) {  // the next step needs no mask
         advance(kt);
         const float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                          qf, sc, sn, o, m, l, P.c, lane,
@@ -329,7 +337,7 @@ fwd_kernel(FwdParams P) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
       }
-      for (; kt + 1 < n_steps; ++kt) {  // the next step is the tail or on the diagonal
+      for (; kt + 1 < (CAUSAL ? n_steps : n_own); ++kt) {  // the next step is the tail or on the diagonal
         advance(kt);
         const float mx = fwd_step<D, true, true, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                         qf, sc, sn, o, m, l, P.c, lane,
@@ -340,6 +348,8 @@ fwd_kernel(FwdParams P) {
       }
       fwd_step<D, false, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
                                         lane, 0, n_keys, qm, P.window);
+      if (!CAUSAL)
+        for (; kt + 1 < n_steps; ++kt) advance(kt);  // the steps this wave leaves out
     }
 
     // epilogue: out = O / l (bf16) through the wave's LDS staging tile, lse =
