@@ -1,7 +1,7 @@
 """Benchmark of the jagged flash attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gem] [--order zigzag]
-                    [--compare-orders] [--no-cpu-baseline]
+                    [--compare-orders] [--no-cpu-baseline] [--no-mfma-probe]
 
 A step is one forward and one backward pass of every variant of the workload
 over the same device-resident synthetic batch (default: the GEM-like jagged
@@ -11,8 +11,10 @@ before the timed region, and their build time is reported separately.
 
 Prints ONE JSON line: throughput in TFLOP/s counting only unpadded FLOPs
 (forward 4*N*H*D, backward 10*N*H*D, N = attended (query, key) pairs), the
-fraction of the bf16 dense MFMA peak, a roofline entry for the dominant pass and
-the CPU oracle timed on a bounded sample.
+fraction of the bf16 dense MFMA peak, a roofline entry for the dominant pass,
+the CPU oracle timed on a bounded sample, and (`mfma_probe`) the bf16 MFMA rate
+and core clock a matrix-core-only kernel sustains on the same GPU right after the
+timed region, with the step's and the dominant kernel's rates as fractions of it.
 """
 from __future__ import annotations
 
@@ -200,6 +202,38 @@ def compare_rope(case, runs, q, k, v, do, dev, rounds, order):
     return res
 
 
+def mfma_probe(dev, jfa, iters=150000, reps=3):
+    """The bf16 MFMA rate the chip sustains and its core clock meanwhile: the
+    library's matrix-core probe (one workgroup of four waves per compute unit,
+    one wave per SIMD, four independent chains of 32x32x16 MFMAs per wave; about
+    9 ms, the length of a step), timed with events after the timed region.
+    clock_ghz = core-clock counter / 100 MHz counter over each workgroup's loop
+    (median over workgroups); realtime_mhz = the 100 MHz counter's span over all
+    loops divided by the event time (a check of its rate)."""
+    import torch
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs * 4, dtype=torch.int64, device=dev)
+    flops = float(wgs) * 4 * 4 * iters * 32768
+    times = []
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        jfa.probe_mfma(iters, wgs, sink, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        if i > 0:
+            times.append(e0.elapsed_time(e1))
+    c = clocks.view(wgs, 4).cpu().numpy().astype(np.float64)
+    ms = float(np.median(times))
+    span = c[:, 3].max() - c[:, 2].min()
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_spec_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "clock_ghz": round(float(np.median(c[:, 0] / c[:, 1])) * 0.1, 3),
+            "realtime_mhz": round(float(span) / (times[-1] * 1e-3) / 1e6, 1),
+            "ms": round(ms, 4), "workgroups": wgs, "iters": iters}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip",
                   "jfa_rope.h", "jfa_rope.hip")
@@ -260,6 +294,8 @@ def main():
                          "and an unfused pipeline (rotation by separate elementwise passes "
                          "around the plain kernels), interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the matrix-core probe that reports the sustained bf16 MFMA rate and clock")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--digest", action="store_true",
                     help="print the kernel-source digest that traffic records are keyed by")
@@ -478,6 +514,12 @@ def main():
     if args.compare_rope and w0.rope_base:
         rope_cmp = compare_rope(case, runs, q, k, v, do, dev, max(10, args.steps), order)
 
+    probe = None if args.no_mfma_probe else mfma_probe(dev, jfa)
+    if probe is not None:
+        probe["value_frac_of_probe"] = round(value / probe["tflops"], 4)
+        if roofline["bound"] == "mfma":
+            probe["roofline_kernel_frac_of_probe"] = round(roofline["achieved"] / probe["tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, variants)
@@ -502,6 +544,7 @@ def main():
                    "per_variant": per_variant},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mfma_probe": probe,
     }
     if compare is not None:
         line["config"]["order_compare"] = compare

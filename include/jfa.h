@@ -254,6 +254,24 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
                           int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, uint32_t passes, void* stream);
 
+/* Matrix-core probe (measurement only; not a step of the attention path): a
+ * kernel of `workgroups` workgroups of four waves, each wave running four
+ * independent chains of `iters` bf16 32x32x16 MFMAs (32768 FLOP each) on
+ * register operands, so the benchmark can report the MFMA rate the chip
+ * sustains and its core clock beside the published dense peak.
+ *   iters       1 .. 2^24
+ *   workgroups  1 .. 65536 (at most one is resident per compute unit; one per
+ *               compute unit puts one wave on every SIMD)
+ *   sink        device float32 [workgroups * 256], written (keeps the products live)
+ *   clocks      device uint64 [workgroups * 4]: per workgroup, the core-clock
+ *               counter (s_memtime) and the constant-rate counter
+ *               (s_memrealtime) elapsed over wave 0's loop, then the
+ *               constant-rate counter's values at the loop's start and end
+ * Host checks only (INVALID_ARG on a bad count, a NULL or a misaligned
+ * pointer); asynchronous on `stream`. FLOP per call = workgroups*4*4*iters*32768. */
+jfa_status jfa_probe_mfma(int32_t iters, int32_t workgroups, float* sink, uint64_t* clocks,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* jfa_status_string(jfa_status s);
 

@@ -296,3 +296,13 @@ def test_schedule_rejects_block_mode_and_small_capacity():
     s = L.jfa_schedule(ctypes.byref(pb), off.ctypes.data, jfa.KIND_FWD, jfa.ORDER_ZIGZAG, 4,
                        sp.ctypes.data, tl.ctypes.data, 8)
     assert s == jfa.ERR_UNSUPPORTED
+
+
+def test_probe_rejects_bad_arguments_before_any_hip_call():
+    L = jfa.lib()
+    ok = ctypes.c_void_p(256)  # never dereferenced: every call below fails its host checks
+    for iters, wgs, sink, clocks in ((0, 1, ok, ok), (1 << 25, 1, ok, ok), (1, 0, ok, ok),
+                                     (1, 70000, ok, ok), (1, 1, None, ok), (1, 1, ok, None),
+                                     (1, 1, ctypes.c_void_p(258), ok),
+                                     (1, 1, ok, ctypes.c_void_p(260))):
+        assert L.jfa_probe_mfma(iters, wgs, sink, clocks, None) == jfa.ERR_INVALID_ARG

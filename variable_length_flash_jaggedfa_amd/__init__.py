@@ -76,6 +76,8 @@ def lib():
         L.jfa_bwd_passes.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp,
                                      vp, vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp]
         L.jfa_bwd_passes.restype = i32
+        L.jfa_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
+        L.jfa_probe_mfma.restype = i32
         L.jfa_status_string.argtypes = [i32]
         L.jfa_status_string.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
@@ -178,6 +180,13 @@ def bwd_passes(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev,
                                 _ptr(q_tiles_dev), int(q_num_slots), _ptr(kv_slot_ptr_dev),
                                 _ptr(kv_tiles_dev), int(kv_num_slots), _ptr(dq), _ptr(dk),
                                 _ptr(dv), _ptr(workspace), ws_bytes, int(passes),
+                                _stream(stream)))
+
+
+def probe_mfma(iters: int, workgroups: int, sink, clocks, stream=None):
+    """Matrix-core throughput probe (measurement only): `sink` float32
+    [workgroups*256] and `clocks` int64 [workgroups*4] device tensors."""
+    _check(lib().jfa_probe_mfma(int(iters), int(workgroups), _ptr(sink), _ptr(clocks),
                                 _stream(stream)))
 
 
