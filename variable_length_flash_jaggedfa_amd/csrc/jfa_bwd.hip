@@ -74,7 +74,7 @@ struct DqParams {
 
 // S^T = K Q^T and dP^T = V dO^T for one step of BN keys (lane = query row).
 template <int D>
-__device__ __forceinline__ void dq_scores(uint32_t ks, uint32_t vs, const LaneOffsets<D>& lo,
+__device__ __forceinline__ void dq_scores(uint32_t ks, const LaneOffsets<D>& lo,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&s)[DqCfg<D>::KB], f32x16 (&dp)[DqCfg<D>::KB]) {
@@ -84,13 +84,16 @@ __device__ __forceinline__ void dq_scores(uint32_t ks, uint32_t vs, const LaneOf
     s[kb] = f32x16{};
     dp[kb] = f32x16{};
   }
-  // row fragments are read one k-step ahead of their MFMAs
+  // row fragments are read one k-step ahead of their MFMAs; the K and V
+  // fragments of one k-step share their address (the V tile follows the K tile
+  // at a fixed distance, an immediate offset), one add per k-step
   u32x4 ka[2][C::KB], va[2][C::KB];
   auto read = [&](int d, int bf) {
+    const uint32_t a = ks + lo.row[d];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-      ka[bf][kb] = rows_at<D>(ks, lo, kb * 32, d);
-      va[bf][kb] = rows_at<D>(vs, lo, kb * 32, d);
+      ka[bf][kb] = lds_ld16(a + uint32_t(kb * 32 * D * 2));
+      va[bf][kb] = lds_ld16(a + uint32_t(C::TILE * 2 + kb * 32 * D * 2));
     }
   };
   read(0, 0);
@@ -112,10 +115,20 @@ __device__ __forceinline__ void dq_accumulate(uint32_t ks, const LaneOffsets<D>&
                                               const u32x4 (&pds)[2 * DqCfg<D>::KB],
                                               f32x16 (&acc)[DqCfg<D>::NB]) {
   using C = DqCfg<D>;
+  // one address per column block and half, shared by the step's 16-key groups
+  // (whose distance is an immediate offset)
+  uint32_t a[C::NB][2];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    a[nb][0] = ks + lo.col[nb][0];
+    a[nb][1] = ks + lo.col[nb][1];
+  }
 #pragma unroll
   for (int x = 0; x < C::NX; ++x) {
     const int st = x / C::NB, nb = x % C::NB;
-    acc[nb] = mfma32(cols_at<D>(ks, lo, st * 16, nb * 32), pds[st], acc[nb]);
+    const uint32_t off = uint32_t(st * 16 * D * 2);
+    const u32x2 lo2 = lds_tr8(a[nb][0] + off), hi2 = lds_tr8(a[nb][1] + off);
+    acc[nb] = mfma32(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pds[st], acc[nb]);
   }
 }
 
@@ -193,7 +206,7 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
     arrive(0);
     if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
-    dq_scores<D>(ks_of(0), ks_of(0) + C::TILE * 2, lo, qf, dof, s, dp);
+    dq_scores<D>(ks_of(0), lo, qf, dof, s, dp);
     if (n_lo > 0 || n_free == 0)
       dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
                                               acc, win);
@@ -210,7 +223,7 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       // the MFMA-only phase runs at raised priority, so that on a shared SIMD
       // the other wave's softmax fills the gaps
       __builtin_amdgcn_s_setprio(1);
-      dq_scores<D>(ks, ks + C::TILE * 2, lo, qf, dof, s, dp);
+      dq_scores<D>(ks, lo, qf, dof, s, dp);
       __builtin_amdgcn_s_setprio(0);
       dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, di, c, g, kt * C::BN, n_keys, qpos, pds,
                                              ks_of(kt - 1), lo, pdv, acc, win);
