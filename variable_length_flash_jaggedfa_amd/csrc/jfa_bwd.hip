@@ -663,6 +663,14 @@ dkdv_kernel(KvParams P) {
         }
         ad.xch = lds_addr(xch) + uint32_t((kw * C::PK * 64 + ln) * 16);
         ad.vec = lds_addr(vecs) + uint32_t((PW ? 0 : C::BM) * 4 + (ln >> 5) * 16);
+        // Keep each tensor's ring offset inside these registers. Left visible,
+        // the compiler moves it into the immediate of every read, and for the
+        // dO ring's later stages (48 KB + stage offset) that immediate no
+        // longer fits the 16-bit field, so each read gets an add of its own.
+#pragma unroll
+        for (int kc = 0; kc < C::DS; ++kc) asm volatile("" : "+v"(ad.row[kc]));
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(ad.col[nb][0]), "+v"(ad.col[nb][1]));
       }
       f32x16 acc[C::NB];
 #pragma unroll
