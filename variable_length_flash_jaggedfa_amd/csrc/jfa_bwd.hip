@@ -146,6 +146,12 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
                                            f32x16 (&acc)[DqCfg<D>::NB], int win = 0) {
   using C = DqCfg<D>;
   if (PREV) dq_accumulate<D>(ks_prev, lo, pds_prev, acc);
+  // Register r of block kb holds key key0 + 4g + e, e = kb*32 + (r/4)*8 + r%4 (a
+  // constant). The key is dead past the sequence end or, with CAUSAL, after the
+  // query (e > hi), and with WIN at or before qpos - win (e <= wl).
+  const int kbase = key0 + 4 * g;
+  const int hi = (CAUSAL ? min(n_keys - 1, qpos) : n_keys - 1) - kbase;
+  const int wl = qpos - win - kbase;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
@@ -153,10 +159,9 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
       float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -lse2));
       float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -lse2));
       if (MASK) {
-        const int key = key0 + kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-        p0 = (key >= n_keys || (CAUSAL && key > qpos) || (WIN && key <= qpos - win)) ? 0.f : p0;
-        p1 = (key + 1 >= n_keys || (CAUSAL && key + 1 > qpos) || (WIN && key + 1 <= qpos - win))
-                 ? 0.f : p1;
+        const int e = kb * 32 + (r / 4) * 8 + (r % 4);
+        p0 = (e > hi || (WIN && e <= wl)) ? 0.f : p0;
+        p1 = (e + 1 > hi || (WIN && e + 1 <= wl)) ? 0.f : p1;
       }
       pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
     }
@@ -504,17 +509,21 @@ template <int D, bool MASK, bool WIN = false>
 __device__ __forceinline__ void kv_probs(const f32x16 (&s)[KvCfg<D>::IB], float c, int g, int q0,
                                          int jw, u32x4 (&pk)[KvCfg<D>::PK], int win = 0) {
   using C = KvCfg<D>;
+  // Register r of block ib holds query q0 + 4g + e, e = ib*32 + (r/4)*8 + r%4 (a
+  // constant). It is masked when the key comes after the query (e < dk) and,
+  // with a window, when the query is win or more rows after the key (e >= dw):
+  // one compare with a constant per element.
+  const int dk = jw - q0 - 4 * g, dw = dk + win;
 #pragma unroll
   for (int st = 0; st < C::PK; ++st)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int ib = st / 2, r = (st % 2) * 8 + 2 * k;
-      // register r holds row (r/4)*8 + 4g + r%4 of the block
-      const int i = q0 + ib * 32 + (r / 4) * 8 + 4 * g + r % 4;
+      const int e = ib * 32 + (r / 4) * 8 + r % 4;
       float p0 = exp2_fast(s[ib][r] * c), p1 = exp2_fast(s[ib][r + 1] * c);
-      if (MASK) {  // query before the key, or (window) at least win rows after it
-        p0 = (jw > i || (WIN && i - jw >= win)) ? 0.f : p0;
-        p1 = (jw > i + 1 || (WIN && i + 1 - jw >= win)) ? 0.f : p1;
+      if (MASK) {
+        p0 = (e < dk || (WIN && e >= dw)) ? 0.f : p0;
+        p1 = (e + 1 < dk || (WIN && e + 1 >= dw)) ? 0.f : p1;
       }
       pk[st][k] = pack_bf16(p0, p1);
     }
