@@ -72,18 +72,17 @@ struct DqParams {
   jfa::RopeTab rope;          // rotary kernels only
 };
 
-// S^T = K Q^T and dP^T = V dO^T for one step of BN keys (lane = query row).
+// S^T = K Q^T and dP^T - Di = V dO^T - Di for one step of BN keys (lane = query
+// row): the first dP product takes `ndi` (every element -Di of the lane's row)
+// as its accumulator input, so dS = P * dP' needs no subtraction.
 template <int D>
 __device__ __forceinline__ void dq_scores(uint32_t ks, const LaneOffsets<D>& lo,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
-                                          const u32x4 (&dof)[DqCfg<D>::DS],
+                                          const u32x4 (&dof)[DqCfg<D>::DS], const f32x16& ndi,
                                           f32x16 (&s)[DqCfg<D>::KB], f32x16 (&dp)[DqCfg<D>::KB]) {
   using C = DqCfg<D>;
 #pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
-    s[kb] = f32x16{};
-    dp[kb] = f32x16{};
-  }
+  for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
   // row fragments are read one k-step ahead of their MFMAs; the K and V
   // fragments of one k-step share their address (the V tile follows the K tile
   // at a fixed distance, an immediate offset), one add per k-step
@@ -103,7 +102,7 @@ __device__ __forceinline__ void dq_scores(uint32_t ks, const LaneOffsets<D>& lo,
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
       s[kb] = mfma32(ka[d & 1][kb], qf[d], s[kb]);
-      dp[kb] = mfma32(va[d & 1][kb], dof[d], dp[kb]);
+      dp[kb] = mfma32(va[d & 1][kb], dof[d], d == 0 ? ndi : dp[kb]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -132,13 +131,13 @@ __device__ __forceinline__ void dq_accumulate(uint32_t ks, const LaneOffsets<D>&
   }
 }
 
-// P = 2^(S c - lse2) and dS = P (dP - Di) for one step, packed to bf16 (keys past
+// P = 2^(S c - lse2) and dS = P dP' (dP' = dP - Di) for one step, packed to bf16 (keys past
 // the sequence end or, with CAUSAL, after the lane's query masked; with WIN also
 // keys at or before qpos - win). With PREV the dQ products of the previous step
 // are issued in the same region so that these VALU instructions run under them.
 template <int D, bool MASK, bool CAUSAL, bool PREV, bool WIN = false>
 __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
-                                           const f32x16 (&dp)[DqCfg<D>::KB], float lse2, float di,
+                                           const f32x16 (&dp)[DqCfg<D>::KB], float lse2,
                                            float c, int g, int key0, int n_keys, int qpos,
                                            u32x4 (&pds)[2 * DqCfg<D>::KB], uint32_t ks_prev,
                                            const LaneOffsets<D>& lo,
@@ -163,7 +162,7 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
         p0 = (e > hi || (WIN && e <= wl)) ? 0.f : p0;
         p1 = (e + 1 > hi || (WIN && e + 1 <= wl)) ? 0.f : p1;
       }
-      pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * (dp[kb][r] - di), p1 * (dp[kb][r + 1] - di));
+      pds[kb * 2 + r / 8][(r % 8) / 2] = pack_bf16(p0 * dp[kb][r], p1 * dp[kb][r + 1]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -209,14 +208,17 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
   if (n_steps > 0) {
     f32x16 s[C::KB], dp[C::KB];
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
+    f32x16 ndi;  // -Di of the lane's row, the first dP product's accumulator input
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndi[r] = -di;
     arrive(0);
     if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
-    dq_scores<D>(ks_of(0), lo, qf, dof, s, dp);
+    dq_scores<D>(ks_of(0), lo, qf, dof, ndi, s, dp);
     if (n_lo > 0 || n_free == 0)
-      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
                                               acc, win);
     else
-      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, di, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
                                                acc, win);
     auto step = [&](int kt, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -228,9 +230,9 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       // the MFMA-only phase runs at raised priority, so that on a shared SIMD
       // the other wave's softmax fills the gaps
       __builtin_amdgcn_s_setprio(1);
-      dq_scores<D>(ks, lo, qf, dof, s, dp);
+      dq_scores<D>(ks, lo, qf, dof, ndi, s, dp);
       __builtin_amdgcn_s_setprio(0);
-      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, di, c, g, kt * C::BN, n_keys, qpos, pds,
+      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, c, g, kt * C::BN, n_keys, qpos, pds,
                                              ks_of(kt - 1), lo, pdv, acc, win);
     };
     int kt = 1;
