@@ -1,0 +1,73 @@
+"""The benchmark credits FLOPs from its count of attended (query, key) pairs
+(forward 4*N*H*D, backward 10*N*H*D). The count is pinned here against explicit
+attention masks, built per sequence from the mask definitions the oracle
+applies: causal keeps j <= i, a window W also keeps only j > i - W, block
+diagonal keeps i and j in the same block, broadcast attends Lq dense queries to
+every key."""
+import numpy as np
+import pytest
+
+import bench
+from oracle import attention as A
+
+
+def masked_pairs(L, causal=False, lq=0, block=0, window=0):
+    n = 0
+    for l in L:
+        if lq:
+            n += int(np.ones((lq, l), dtype=bool).sum())
+            continue
+        i = np.arange(l)[:, None]
+        j = np.arange(l)[None, :]
+        keep = np.ones((l, l), dtype=bool)
+        if block:
+            keep &= (i // block) == (j // block)
+        if causal:
+            keep &= j <= i
+        if window:
+            keep &= j > i - window
+        n += int(keep.sum())
+    return n
+
+
+LENGTHS = [0, 1, 2, 31, 64, 65, 127, 128, 129, 300, 511]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_self_attention_pairs(causal):
+    rng = np.random.default_rng(3)
+    L = LENGTHS + list(rng.integers(0, 400, size=8))
+    assert bench.pairs_of(L, causal=causal) == masked_pairs(L, causal=causal)
+    assert bench.pairs_of(L, causal=causal) == A.pair_count(L, causal=causal)
+
+
+@pytest.mark.parametrize("W", [1, 2, 33, 128, 129, 5000])
+def test_causal_window_pairs(W):
+    assert bench.pairs_of(LENGTHS, causal=True, window=W) == masked_pairs(LENGTHS, causal=True, window=W)
+
+
+def test_window_covering_every_sequence_is_causal():
+    assert bench.pairs_of(LENGTHS, causal=True, window=max(LENGTHS)) == masked_pairs(LENGTHS, causal=True)
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_block_diagonal_pairs(bs):
+    L = [bs, 0, 3 * bs, 7 * bs, 2 * bs]
+    assert bench.pairs_of(L, block=bs) == masked_pairs(L, block=bs)
+
+
+def test_broadcast_pairs():
+    L = [0, 1, 50, 300]
+    assert bench.pairs_of(L, lq=256) == masked_pairs(L, lq=256)
+
+
+def test_padding_ratio_counts_padded_pairs():
+    # every sequence padded to the longest: B * Lmax^2 (causal: B * Lmax(Lmax+1)/2)
+    class Case:
+        lengths = np.array([3, 5, 8])
+    g = bench.variants_of("gem")
+    assert [w.causal for w in g] == [False, True]
+    r_nc = bench.padded_ratio(Case, g[0])
+    r_c = bench.padded_ratio(Case, g[1])
+    assert r_nc == pytest.approx(3 * 64 / masked_pairs([3, 5, 8]))
+    assert r_c == pytest.approx(3 * 36 / masked_pairs([3, 5, 8], causal=True))
