@@ -351,9 +351,12 @@ def main():
                           w.window)
         nhd = float(npairs) * w.num_heads * w.head_dim
         # "block": the single-tile kernels of 32- and 64-token blocks (one fused
-        # backward); 128- and 256-token blocks run the jagged kernels
+        # backward); 128- and 256-token blocks run the jagged kernels, except the
+        # backward of 128-token blocks without rotary ("fused_bwd": one kernel)
+        fused_bwd = plan.block or (w.kind == "block" and w.block == 128 and not w.rope_base)
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
-                         block=plan.block, fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
+                         block=plan.block, fused_bwd=fused_bwd,
+                         fwd_flops=4.0 * nhd, bwd_flops=10.0 * nhd,
                          dq_flops=6.0 * nhd, dkdv_flops=8.0 * nhd,
                          fwd_ms=[], bwd_ms=[], dq_ms=[], dkdv_ms=[]))
     alt = None
@@ -375,7 +378,7 @@ def main():
             ev[1].record()
             bargs = (q, k, v, r["out"], do, r["lse"])
             bkw = dict(dq=r["dq"], dk=r["dk"], dv=r["dv"])
-            if r["block"]:
+            if r["fused_bwd"]:
                 r["plan"].backward(*bargs, **bkw)
                 ev[2].record()
             else:
@@ -398,7 +401,7 @@ def main():
             e0, e1, e2, e3 = r["_ev"]
             r["fwd_ms"].append(e0.elapsed_time(e1))
             r["bwd_ms"].append(e1.elapsed_time(e3))
-            if not r["block"]:
+            if not r["fused_bwd"]:
                 r["dq_ms"].append(e1.elapsed_time(e2))
                 r["dkdv_ms"].append(e2.elapsed_time(e3))
     torch.cuda.synchronize()
@@ -431,8 +434,11 @@ def main():
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
         elif w.kind == "block":
             cands.append((np.mean(r["fwd_ms"]), "fwd_kernel", tag, "hbm", 4.0 * tb + vb))
-            cands.append((np.mean(r["dq_ms"]), "dq_kernel", tag, "hbm", 6.0 * tb + 3.0 * vb))
-            cands.append((np.mean(r["dkdv_ms"]), "dkdv_kernel", tag, "hbm", 6.0 * tb + 2.0 * vb))
+            if r["fused_bwd"]:  # 128-token blocks: reads q, k, v, out, dO; writes dq, dk, dv
+                cands.append((np.mean(r["bwd_ms"]), "block128_bwd_kernel", tag, "hbm", 8.0 * tb))
+            else:
+                cands.append((np.mean(r["dq_ms"]), "dq_kernel", tag, "hbm", 6.0 * tb + 3.0 * vb))
+                cands.append((np.mean(r["dkdv_ms"]), "dkdv_kernel", tag, "hbm", 6.0 * tb + 2.0 * vb))
         else:
             bc = "_bcast" if w.kind == "broadcast" else ""
             cands.append((np.mean(r["fwd_ms"]), "fwd_kernel", tag, "mfma", r["fwd_flops"]))
@@ -463,7 +469,7 @@ def main():
                                               round(float(np.max(r["fwd_ms"])), 4)]
         per_variant[tag]["bwd_ms_min_max"] = [round(float(np.min(r["bwd_ms"])), 4),
                                               round(float(np.max(r["bwd_ms"])), 4)]
-        if not r["block"]:
+        if not r["fused_bwd"]:
             per_variant[tag]["dq_ms"] = round(float(np.median(r["dq_ms"])), 4)
             per_variant[tag]["dkdv_ms"] = round(float(np.median(r["dkdv_ms"])), 4)
 

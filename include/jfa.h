@@ -245,7 +245,11 @@ jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const voi
  * with the same problem, inputs and workspace on the same stream (it reads the Di,
  * and for ROTARY the rotated q and k, that pass left in the workspace); the
  * library cannot check this. Blocks of 32 or 64 tokens run one fused kernel and
- * accept JFA_PASS_ALL only (JFA_ERR_INVALID_ARG otherwise). jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
+ * accept JFA_PASS_ALL only (JFA_ERR_INVALID_ARG otherwise). For 128-token blocks
+ * without ROTARY, JFA_PASS_ALL runs one single-tile kernel ("TLX Block
+ * Attention", sections 2 and 4: lse and workspace are checked but not read),
+ * while the passes called apart run the two jagged passes; the two agree within
+ * rounding, not bit for bit. jfa_bwd(...) is jfa_bwd_passes(..., JFA_PASS_ALL, stream). */
 jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, const void* v,
                           const void* out, const void* dout, const float* lse,
                           const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,

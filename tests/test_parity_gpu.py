@@ -292,6 +292,27 @@ def test_backward_passes_match_fused_call(gpu):
         assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_block128_single_kernel_matches_jagged_passes(gpu, D):
+    """128-token blocks: the single-tile backward (one call) and the two jagged
+    passes called apart agree, and both match the oracle (checked by
+    test_other_block_sizes for the single call)."""
+    import torch
+    w = J.custom([128, 0, 3 * 128, 7 * 128, 2 * 128], 2, D, seed=29, kind="block", block=128)
+    log(f"case block128 passes D={D}")
+    run = GpuRun(J.make_case(w), gpu)
+    run.forward()
+    dq1, dk1, dv1 = (x.clone() for x in run.backward())
+    plan = run.plan
+    q, k, v, out, do, lse = run.q, run.k, run.v, run.out_dev, run.do, run.lse_dev
+    dq2, dk2, dv2 = (torch.full_like(x, float("nan")) for x in (dq1, dk1, dv1))
+    plan.backward(q, k, v, out, do, lse, dq=dq2, dk=dk2, dv=dv2, passes=jfa.PASS_DQ)
+    plan.backward(q, k, v, out, do, lse, dq=dq2, dk=dk2, dv=dv2, passes=jfa.PASS_DKDV)
+    torch.cuda.synchronize()
+    for n, a_, b_ in (("dq", dq1, dq2), ("dk", dk1, dk2), ("dv", dv1, dv2)):
+        assert_grad(bf16_to_f64(a_), bf16_to_f64(b_), n + " single kernel vs passes")
+
+
 @pytest.mark.parametrize("D,L", [(128, 129), (64, 300), (128, 128)])
 def test_broadcast_one_sequence_matches_jagged(gpu, D, L):
     """Broadcast-Q with one sequence and Lq = L is jagged self-attention on the same

@@ -202,6 +202,12 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
   a.groups = bcast_groups(p->num_seqs);
   a.dq_part = bq ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * di_bytes(p)) : nullptr;
   char* ws = static_cast<char*>(workspace) + 2 * di_bytes(p);  // after -Di and -lse/scale
+  // The whole backward of 128-token blocks without rotary is one single-tile
+  // kernel (a block is one tile: no lse read, no workspace used); the arguments
+  // are checked as for the two passes, which a caller may still run apart.
+  if (block_size(p) == 128 && !(p->flags & JFA_ROTARY) && passes == JFA_PASS_ALL &&
+      p->total_kv > 0)
+    return launch_block128_bwd(a);
   if (tiled_blocks(p) && p->total_kv > 0) {
     if (jfa_status s = as_block_sequences(p, ws, a, stream)) return s;
   }

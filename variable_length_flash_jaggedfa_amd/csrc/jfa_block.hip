@@ -14,7 +14,9 @@
 // 32-token blocks run on the same kernels: a 64-token unit then holds two blocks
 // (block boundaries fall on multiples of 32 tokens everywhere), and each wave,
 // whose 32 query rows are one block, masks the other block's keys; the last unit
-// may hold a single block. Blocks of 128 or 256 tokens run on the jagged kernels.
+// may hold a single block. Blocks of 128 or 256 tokens run on the jagged kernels,
+// except the whole backward of 128-token blocks without rotary, which runs as one
+// single-tile kernel below.
 //
 // With rotary embeddings (the page fuses them into these kernels) the rows of Q
 // and K are rotated inside the kernel after they arrive in LDS, and the backward
@@ -433,6 +435,194 @@ jfa_status launch_bwd_t(const jfa::BwdLaunch& a) {
   return JFA_OK;
 }
 
+// 128-token blocks: the single-tile backward above with four waves ("TLX Block
+// Attention", sections 2 and 4: one tile per block, statistics recomputed exactly,
+// Di inline, no lse read, no atomics). Wave w owns query rows 32w..32w+31 on the
+// query side (its score tile spans all 128 keys) and keys 32w..32w+31 on the key
+// side. K, V, Q and dO stay in LDS. Once every wave has its dQ, the P^T and dS^T
+// tiles (128 queries x 128 keys, bf16) are written: at D = 128 over K and V (the
+// same size, and no longer read), at D = 64 to LDS of their own.
+template <int D>
+struct Blk128Cfg {
+  static constexpr int BS = 128;
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int DS = D / 16;
+  static constexpr int NB = D / 32;
+  static constexpr int KB = BS / 32;                    // 32-key blocks of a score tile
+  static constexpr int TILE = BS * D;                   // one 128 x D tile
+  static constexpr int PT = BS * BS;                    // one 128 x 128 tile
+  static constexpr int EXTRA = D == 128 ? 0 : 2 * PT;   // P^T, dS^T beyond the four tiles
+};
+
+// Exact softmax over the KB 32-key blocks of a score tile held as S^T (one query
+// per lane pair); P is left in `s`.
+template <int KB>
+__device__ __forceinline__ void tile_softmax_kb(f32x16 (&s)[KB], float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = pair_max(mx) * c;  // scale > 0, so the max commutes with it
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(__builtin_fmaf(s[kb][r], c, -mx));
+      s[kb][r] = p;
+      rs += p;
+    }
+  const float inv = 1.f / pair_sum(rs);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] *= inv;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) block128_bwd_kernel(BlkParams P) {
+  using C = Blk128Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * C::TILE + C::EXTRA];
+  uint16_t* Kt = lds;
+  uint16_t* Vt = Kt + C::TILE;
+  uint16_t* Qt = Vt + C::TILE;
+  uint16_t* dOt = Qt + C::TILE;
+  uint16_t* Pt = D == 128 ? Kt : lds + 4 * C::TILE;  // written only after K and V are done
+  uint16_t* dSt = Pt + C::PT;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
+  int blk, h;
+  unit_of<D>(P.H, blk, h);
+  const int64_t rstride = int64_t(P.H) * D;
+  const int64_t base = int64_t(blk) * C::BS * rstride + int64_t(h) * D;
+  const int rowbytes = int(rstride * 2);
+  const int nrows = min(C::BS, P.rows - blk * C::BS);  // 128: every length is a multiple of it
+  tile_load<D, C::BS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, nrows), rowbytes, w, lane);
+  // out fragments of this lane's query row, for Di = rowsum(dO * out)
+  const int i = w * 32 + li;
+  u32x4 of[C::DS];
+  const uint16_t* orow = P.o + base + int64_t(i) * rstride;
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d) of[d] = i < nrows ? ld16(orow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+  wait_vmem();
+  __syncthreads();
+
+  // ---- query side (lane = query): S^T, dP^T over all 128 keys, exact softmax,
+  // dS^T = P (dP - Di), dQ^T = K^T dS^T
+  f32x16 s[C::KB], dp[C::KB];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    s[kb] = f32x16{};
+    dp[kb] = f32x16{};
+  }
+  float di = 0.f;
+#pragma unroll
+  for (int d = 0; d < C::DS; ++d) {
+    const u32x4 qf = frag_rows<D>(Qt, w * 32, d, li, g);
+    const u32x4 dof = frag_rows<D>(dOt, w * 32, d, li, g);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      di += bf16_lo(dof[e2]) * bf16_lo(of[d][e2]) + bf16_hi(dof[e2]) * bf16_hi(of[d][e2]);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = mfma32(frag_rows<D>(Kt, kb * 32, d, li, g), qf, s[kb]);
+      dp[kb] = mfma32(frag_rows<D>(Vt, kb * 32, d, li, g), dof, dp[kb]);
+    }
+  }
+  di = pair_sum(di);
+  tile_softmax_kb<C::KB>(s, P.c);
+  // P and dS packed to bf16 with keys in accumulator order: operand st holds keys
+  // st*16 .. st*16+15 of this lane's query
+  u32x4 pps[2 * C::KB], pds[2 * C::KB];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsv[e] = s[kb][q4 * 4 + e] * (dp[kb][q4 * 4 + e] - di);
+      const int st = kb * 2 + q4 / 2, hw = (q4 % 2) * 2;
+      pps[st][hw] = pack_bf16(s[kb][q4 * 4 + 0], s[kb][q4 * 4 + 1]);
+      pps[st][hw + 1] = pack_bf16(s[kb][q4 * 4 + 2], s[kb][q4 * 4 + 3]);
+      pds[st][hw] = pack_bf16(dsv[0], dsv[1]);
+      pds[st][hw + 1] = pack_bf16(dsv[2], dsv[3]);
+    }
+  f32x16 dqa[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    dqa[nb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 2 * C::KB; ++st)
+      dqa[nb] = mfma32(frag_cols<D>(Kt, st * 16, nb * 32, lane), pds[st], dqa[nb]);
+  }
+  __syncthreads();  // every wave is done reading K and V
+  // dQ rows leave through this wave's 32 x D quarter of the K tile
+  store_rows<D>(Kt + w * 32 * D, dqa, P.scale, P.dq + base + int64_t(w * 32) * rstride, rstride,
+                nrows - w * 32, lane);
+  __syncthreads();  // the staging is read back before P^T overwrites it
+  // P^T and dS^T rows: query i, keys j0..j0+3
+#pragma unroll
+  for (int st = 0; st < 2 * C::KB; ++st)
+#pragma unroll
+    for (int hw = 0; hw < 4; hw += 2) {
+      const int j0 = (st / 2) * 32 + ((st % 2) * 2 + hw / 2) * 8 + g * 4;
+      st8(Pt + Swz<C::BS>::chunk(i, j0 >> 3) + (j0 & 7), u32x2{pps[st][hw], pps[st][hw + 1]});
+      st8(dSt + Swz<C::BS>::chunk(i, j0 >> 3) + (j0 & 7), u32x2{pds[st][hw], pds[st][hw + 1]});
+    }
+  __syncthreads();
+
+  // ---- key side (lane = key): dV^T = dO^T P, dK^T = Q^T dS over all 128 queries
+  f32x16 av[C::NB], ak[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    av[nb] = f32x16{};
+    ak[nb] = f32x16{};
+  }
+#pragma unroll
+  for (int st = 0; st < 2 * C::KB; ++st) {
+    const u32x4 pb = frag_cols<C::BS>(Pt, st * 16, w * 32, lane);
+    const u32x4 db = frag_cols<C::BS>(dSt, st * 16, w * 32, lane);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      av[nb] = mfma32(frag_cols<D>(dOt, st * 16, nb * 32, lane), pb, av[nb]);
+      ak[nb] = mfma32(frag_cols<D>(Qt, st * 16, nb * 32, lane), db, ak[nb]);
+    }
+  }
+  __syncthreads();  // every wave is done with P^T and dS^T before the staging below
+  uint16_t* vst = Vt + w * 32 * D;
+  store_rows<D>(vst, av, 1.f, P.dv + base + int64_t(w * 32) * rstride, rstride, nrows - w * 32, lane);
+  store_rows<D>(vst, ak, P.scale, P.dk + base + int64_t(w * 32) * rstride, rstride, nrows - w * 32, lane);
+}
+
+template <int D>
+jfa_status launch_b128_t(const jfa::BwdLaunch& a) {
+  BlkParams P{};
+  P.q = static_cast<const uint16_t*>(a.q);
+  P.k = static_cast<const uint16_t*>(a.k);
+  P.v = static_cast<const uint16_t*>(a.v);
+  P.o = static_cast<const uint16_t*>(a.out);
+  P.dout = static_cast<const uint16_t*>(a.dout);
+  P.dq = static_cast<uint16_t*>(a.dq);
+  P.dk = static_cast<uint16_t*>(a.dk);
+  P.dv = static_cast<uint16_t*>(a.dv);
+  P.H = a.num_heads;
+  P.c = a.scale * kLog2e;
+  P.scale = a.scale;
+  P.rows = int32_t(a.total_kv);
+  const int64_t units = (a.total_kv / Blk128Cfg<D>::BS) * a.num_heads;
+  if (units > INT32_MAX) return jfa::fail(JFA_ERR_INVALID_ARG, "too many block units");
+  hipLaunchKernelGGL((block128_bwd_kernel<D>), dim3(unsigned(units)), dim3(Blk128Cfg<D>::NT), 0,
+                     static_cast<hipStream_t>(a.stream), P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("128-block bwd launch: ") + hipGetErrorString(e));
+  return JFA_OK;
+}
+
 __global__ void __launch_bounds__(256) block_offsets_kernel(int32_t* out, int32_t n, int32_t block) {
   const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
   if (i <= n) out[i] = i * block;
@@ -457,6 +647,10 @@ jfa_status launch_block_fwd(const FwdLaunch& a) {
 
 jfa_status launch_block_bwd(const BwdLaunch& a) {
   return a.head_dim == 128 ? launch_bwd_t<128>(a) : launch_bwd_t<64>(a);
+}
+
+jfa_status launch_block128_bwd(const BwdLaunch& a) {
+  return a.head_dim == 128 ? launch_b128_t<128>(a) : launch_b128_t<64>(a);
 }
 
 }  // namespace jfa

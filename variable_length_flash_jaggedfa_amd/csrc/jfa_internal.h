@@ -108,6 +108,7 @@ jfa_status launch_fwd(const FwdLaunch& a);
 jfa_status launch_bwd(const BwdLaunch& a);
 jfa_status launch_block_fwd(const FwdLaunch& a);
 jfa_status launch_block_bwd(const BwdLaunch& a);
+jfa_status launch_block128_bwd(const BwdLaunch& a);  // whole backward, 128-token blocks, no rotary
 jfa_status launch_rope_rows(const RopeRowsLaunch& a);
 // offsets of consecutive blocks of `block` tokens: out[i] = i * block, i <= n
 jfa_status launch_block_offsets(int32_t* out, int64_t n, int32_t block, void* stream);
