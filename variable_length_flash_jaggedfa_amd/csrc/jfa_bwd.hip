@@ -227,8 +227,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       arrive(kt);  // also: every wave is done with stage kt-2
       if (kt + C::NS - 2 < n_steps) load_stage(kt + C::NS - 2);
       const uint32_t ks = ks_of(kt);
-      // the MFMA-only phase runs at raised priority, so that on a shared SIMD
-      // the other wave's softmax fills the gaps
+      // the MFMA-only phase runs at raised priority: on a shared SIMD it issues
+      // ahead of the other wave's softmax
       __builtin_amdgcn_s_setprio(1);
       dq_scores<D>(ks, lo, qf, dof, ndi, s, dp);
       __builtin_amdgcn_s_setprio(0);

@@ -4,7 +4,8 @@
 // it ("Jagged Flash Attention for GEM": persistent kernel fed by a zigzag deal of
 // KV-work-sorted tiles). A tile is 128 query rows of one (sequence, head); each
 // of the 4 waves owns 32 rows and two workgroups share a compute unit, so one
-// wave's softmax overlaps another wave's MFMAs on the same SIMD. Keys stream in
+// wave's LDS and memory waits are covered by the other wave on its SIMD (its
+// MFMA and VALU work barely overlap: kept lean, not hidden). Keys stream in
 // steps of 32 (D = 128) or 64 (D = 64) through a four-stage LDS ring filled by
 // direct buffer->LDS loads issued three steps ahead. Per step a
 // wave computes S^T = K Q^T (each lane holds the scores of one query row, so the
