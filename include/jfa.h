@@ -54,6 +54,15 @@
  *               checked on the host before any HIP call, so on any error nothing
  *               is enqueued. jfa_last_error() gives a thread-local message.
  *   Threads     Calls are thread-safe; calls on one stream execute in order.
+ *   Diagnostics Read from the environment on every call:
+ *               JFA_VALIDATE=1  jfa_fwd / jfa_bwd / jfa_bwd_passes first
+ *                 synchronise `stream`, copy the device offsets and schedules back
+ *                 and check the precondition the kernels rely on (offsets start at
+ *                 0, never decrease, end at total_kv, no length above max_len; the
+ *                 tiles cover every (sequence, head, tile index) exactly once). A mismatch
+ *                 returns JFA_ERR_INVALID_ARG with nothing enqueued. Costs a
+ *                 synchronisation and blocking copies: for debugging.
+ *               JFA_LOG=1  one line per call of those entry points on stderr.
  */
 #ifndef JFA_H
 #define JFA_H
@@ -200,8 +209,8 @@ size_t jfa_fwd_workspace_bytes(const jfa_problem* p);
  *                contents on entry are ignored and clobbered (jagged ROTARY: the
  *                rotated q and k). May be NULL when the size is 0.
  * A broadcast-Q sequence with no keys gets out = 0 and lse = -inf.
- * Precondition (not checked on the device): offsets_dev equals the host offsets
- * the schedule was built from. */
+ * Precondition (not checked on the device; JFA_VALIDATE=1 checks it on the host):
+ * offsets_dev equals the host offsets the schedule was built from. */
 jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
                    const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
                    const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,

@@ -110,6 +110,38 @@ def test_other_block_sizes(bs):
     assert jfa.bwd_workspace_bytes(p) == 2 * r256(2 * T * 4) + r256((nb + 1) * 4)
 
 
+def test_addressing_limits():
+    """The kernels address one tile (at most 256 token rows of one head) through
+    32-bit buffer resources: 256 rows of all heads must span < 2^31 bytes, so
+    H * D * 2 * 256 >= 2^31 is rejected before anything runs. A long sequence
+    itself is fine: the resource covers only the tile being loaded, not the rest
+    of the sequence (whose span may exceed 4 GiB, e.g. L >= 2^20 at H = 16,
+    D = 128, or L >= 2^18 at H = 64)."""
+    # largest accepted head count at D = 128: 2^22 / 128 - 1 = 32767
+    for H, ok in ((32767, True), (32768, False), (16, True)):
+        p = _p(num_seqs=1, num_heads=H, head_dim=128, max_len=8, total_kv=8)
+        if ok:
+            assert jfa.schedule_count(p, np.array([0, 8], dtype=np.int32), jfa.KIND_FWD) == H
+        else:
+            with pytest.raises(jfa.JfaError) as e:
+                jfa.schedule_count(p, np.array([0, 8], dtype=np.int32), jfa.KIND_FWD)
+            assert e.value.status == jfa.ERR_UNSUPPORTED
+            assert jfa.bwd_workspace_bytes(p) == 0 and jfa.fwd_workspace_bytes(p) == 0
+    # one sequence whose rows of one head span more than 4 GiB: accepted (the tile
+    # count is exact; nothing is allocated here)
+    for H, L in ((16, (1 << 20) + 1), (64, (1 << 18) + 1), (64, (1 << 21) + 77)):
+        p = _p(num_seqs=1, num_heads=H, head_dim=128, max_len=L, total_kv=L)
+        assert ((L - 1) * H + 1) * 128 * 2 > 1 << 32
+        off = np.array([0, L], dtype=np.int32)
+        assert jfa.schedule_count(p, off, jfa.KIND_FWD) == H * -(-L // 128)
+        assert jfa.schedule_count(p, off, jfa.KIND_BWD) == H * -(-L // 128)
+    # broadcast-Q out rows B * Lq * H * D past the element bound
+    p = _p(num_seqs=1 << 20, num_heads=64, head_dim=128, lq=1 << 20, flags=jfa.BROADCAST_Q,
+           max_len=0, total_kv=0)
+    with pytest.raises(jfa.JfaError):
+        jfa.schedule_count(p, np.zeros((1 << 20) + 1, dtype=np.int32), jfa.KIND_FWD)
+
+
 def test_rotary_block_problem_accepted():
     p = _p(flags=jfa.BLOCK_DIAG64 | jfa.ROTARY, total_kv=128, max_len=64, rope_base=10000.0)
     assert jfa.schedule_count(p, np.array([0, 64, 128], dtype=np.int32), jfa.KIND_FWD) == 2 * 2

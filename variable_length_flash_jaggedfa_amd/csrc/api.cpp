@@ -3,7 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "jfa_internal.h"
 
@@ -42,6 +46,89 @@ jfa_status check_workspace(void* workspace, size_t workspace_bytes, size_t ws) {
     return fail(JFA_ERR_WORKSPACE, "workspace needs " + std::to_string(ws) + " bytes, got " +
                                        std::to_string(workspace_bytes));
   if (!aligned(workspace, 256)) return fail(JFA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return JFA_OK;
+}
+
+// ---- diagnostics switched on by the environment (read on every call)
+//   JFA_VALIDATE=1  before launching, copy the device offsets and schedule back
+//                   (a stream synchronisation and blocking copies) and check the
+//                   precondition the kernels rely on: under these device offsets
+//                   the tiles cover every (sequence, head, tile index) exactly once.
+//   JFA_LOG=1       one line per entry-point call on stderr.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+
+void log_call(const char* what, const jfa_problem* p, int32_t slots_a, int32_t slots_b,
+              uint32_t passes) {
+  if (!env_on("JFA_LOG")) return;
+  std::fprintf(stderr,
+               "jfa: %s B=%d H=%d D=%d T=%lld lq=%d flags=0x%x window=%d block=%d slots=%d/%d "
+               "passes=%u\n",
+               what, p->num_seqs, p->num_heads, p->head_dim, (long long)p->total_kv, p->lq,
+               p->flags, p->window, p->block, slots_a, slots_b, passes);
+}
+
+// Checks one device schedule of `kind` against the device offsets (see above).
+// Runs before anything is enqueued, so a failure leaves the stream untouched.
+jfa_status validate_schedule(const jfa_problem* p, const int32_t* offsets_dev,
+                             const int32_t* slot_ptr_dev, const int32_t* tiles_dev,
+                             int32_t num_slots, int32_t kind, void* stream) {
+  const char* which = kind == JFA_KIND_FWD ? "forward" : "backward";
+  auto bad = [&](const std::string& m) {
+    return fail(JFA_ERR_INVALID_ARG, std::string("JFA_VALIDATE: ") + which + " schedule: " + m);
+  };
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: stream synchronisation failed");
+  const int64_t B = p->num_seqs;
+  std::vector<int32_t> off(size_t(B) + 1), sp(size_t(num_slots) + 1);
+  if (hipMemcpy(off.data(), offsets_dev, off.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(sp.data(), slot_ptr_dev, sp.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of offsets or slot_ptr failed");
+  if (off[0] != 0) return bad("offsets[0] != 0");
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t L = int64_t(off[b + 1]) - off[b];
+    if (L < 0) return bad("offsets decrease at sequence " + std::to_string(b));
+    if (L > p->max_len) return bad("sequence " + std::to_string(b) + " longer than max_len");
+    if (block_size(p) > 0 && L % block_size(p))
+      return bad("sequence " + std::to_string(b) + " is not a whole number of blocks");
+  }
+  if (off[B] != p->total_kv) return bad("offsets[B] != total_kv");
+  if (sp[0] != 0) return bad("slot_ptr[0] != 0");
+  for (int32_t s = 0; s < num_slots; ++s)
+    if (sp[s + 1] < sp[s]) return bad("slot_ptr decreases at slot " + std::to_string(s));
+  const int64_t n = sp[num_slots];
+  std::vector<int32_t> tl(size_t(n) * 4);
+  if (n > 0 && hipMemcpy(tl.data(), tiles_dev, tl.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of tiles failed");
+  // 128- and 256-token blocks are scheduled over the blocks as sequences
+  const bool tb = tiled_blocks(p);
+  const int64_t nseq = tb ? p->total_kv / p->block : B;
+  const int32_t rows = jfa_tile_rows(kind, p->head_dim, tb ? JFA_BLOCK_DIAG : p->flags);
+  const bool dense_q = (p->flags & JFA_BROADCAST_Q) && kind == JFA_KIND_FWD;
+  // tiles each (sequence, head) needs under these offsets, as prefix sums
+  std::vector<int64_t> first(size_t(nseq) + 1, 0);
+  for (int64_t b = 0; b < nseq; ++b) {
+    const int64_t L = tb ? p->block : int64_t(off[b + 1]) - off[b];
+    first[b + 1] = first[b] + ((dense_q ? p->lq : L) + rows - 1) / rows;
+  }
+  if (first[nseq] * p->num_heads != n)
+    return bad(std::to_string(n) + " tiles where the offsets need " +
+               std::to_string(first[nseq] * p->num_heads));
+  std::vector<char> seen(size_t(n), 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t b = tl[4 * i], h = tl[4 * i + 1], t = tl[4 * i + 2];
+    if (b < 0 || b >= nseq || h < 0 || h >= p->num_heads || t < 0)
+      return bad("tile " + std::to_string(i) + " names a sequence or head that does not exist");
+    const int64_t have = first[b + 1] - first[b];
+    if (t >= have)
+      return bad("tile " + std::to_string(i) + " (sequence " + std::to_string(b) + ", index " +
+                 std::to_string(t) + ") lies past the sequence's rows");
+    char& mark = seen[size_t(h * first[nseq] + first[b] + t)];
+    if (mark) return bad("tile " + std::to_string(i) + " appears twice");
+    mark = 1;
+  }
   return JFA_OK;
 }
 
@@ -111,6 +198,7 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
     if (jfa_status s = need(k, "k")) return s;
     if (jfa_status s = need(v, "v")) return s;
   }
+  log_call("fwd", p, num_slots, 0, 0);
   FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
               p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
               p->rope_base, p->window, block_size(p), stream};
@@ -122,6 +210,11 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   if (jfa_status s = need(lse, "lse", 4)) return s;
   if (jfa_status s = check_schedule_args(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots)) return s;
   if (jfa_status s = check_workspace(workspace, workspace_bytes, jfa_fwd_workspace_bytes(p))) return s;
+  if (env_on("JFA_VALIDATE")) {
+    if (jfa_status s = validate_schedule(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
+                                         JFA_KIND_FWD, stream))
+      return s;
+  }
   char* ws = static_cast<char*>(workspace);
   if (tiled_blocks(p) && p->total_kv > 0) {
     if (jfa_status s = as_block_sequences(p, ws, a, stream)) return s;
@@ -166,6 +259,7 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
     if (jfa_status s = need(dk, "dk")) return s;
     if (jfa_status s = need(dv, "dv")) return s;
   }
+  log_call("bwd", p, q_num_slots, kv_num_slots, passes);
   BwdLaunch a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
   a.offsets = offsets_dev;
@@ -197,6 +291,16 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
     if (jfa_status s = need(offsets_dev, "offsets_dev", 4)) return s;
   }
   if (q_rows(p) == 0 && p->total_kv == 0) return JFA_OK;
+  if (env_on("JFA_VALIDATE") && p->total_kv > 0) {
+    if (jfa_status s = validate_schedule(p, offsets_dev, kv_slot_ptr_dev, kv_tiles_dev,
+                                         kv_num_slots, JFA_KIND_BWD, stream))
+      return s;
+    if (!bq) {
+      if (jfa_status s = validate_schedule(p, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+                                           q_num_slots, JFA_KIND_FWD, stream))
+        return s;
+    }
+  }
   a.di = static_cast<float*>(workspace);
   a.nls = reinterpret_cast<float*>(static_cast<char*>(workspace) + di_bytes(p));
   a.groups = bcast_groups(p->num_seqs);

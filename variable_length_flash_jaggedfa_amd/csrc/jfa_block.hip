@@ -198,12 +198,12 @@ __global__ void __launch_bounds__(128) block_fwd_kernel(BlkParams P) {
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
   const int nrows = unit_rows<BS>(P.rows, blk);
-  tile_load<D, kBS, C::NW>(lds, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(lds, rows_rsrc<D, kBS>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(lds + C::TILE, rows_rsrc<D, kBS>(P.v + base, rstride, nrows), rowbytes, w, lane);
   u32x4 qf[C::DS];
   if (ROPE) {
     uint16_t* Qt = lds + 2 * C::TILE;
-    tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
+    tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D, kBS>(P.q + base, rstride, nrows), rowbytes, w, lane);
     wait_vmem();
     __syncthreads();
     rope_tiles<D, C::NW>(lds, Qt, P.rope, w, lane);
@@ -264,10 +264,10 @@ __global__ void __launch_bounds__(128) block_bwd_kernel(BlkParams P) {
   const int64_t base = int64_t(blk) * kBS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
   const int nrows = unit_rows<BS>(P.rows, blk);
-  tile_load<D, kBS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, kBS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Kt, rows_rsrc<D, kBS>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Vt, rows_rsrc<D, kBS>(P.v + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(Qt, rows_rsrc<D, kBS>(P.q + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, kBS, C::NW>(dOt, rows_rsrc<D, kBS>(P.dout + base, rstride, nrows), rowbytes, w, lane);
   // out fragments of this lane's query row, for Di = rowsum(dO * out)
   const int i = w * 32 + li;
   u32x4 of[C::DS];
@@ -499,10 +499,10 @@ __global__ void __launch_bounds__(256) block128_bwd_kernel(BlkParams P) {
   const int64_t base = int64_t(blk) * C::BS * rstride + int64_t(h) * D;
   const int rowbytes = int(rstride * 2);
   const int nrows = min(C::BS, P.rows - blk * C::BS);  // 128: every length is a multiple of it
-  tile_load<D, C::BS, C::NW>(Kt, rows_rsrc<D>(P.k + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, C::BS, C::NW>(Vt, rows_rsrc<D>(P.v + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, C::BS, C::NW>(Qt, rows_rsrc<D>(P.q + base, rstride, nrows), rowbytes, w, lane);
-  tile_load<D, C::BS, C::NW>(dOt, rows_rsrc<D>(P.dout + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(Kt, rows_rsrc<D, C::BS>(P.k + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(Vt, rows_rsrc<D, C::BS>(P.v + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(Qt, rows_rsrc<D, C::BS>(P.q + base, rstride, nrows), rowbytes, w, lane);
+  tile_load<D, C::BS, C::NW>(dOt, rows_rsrc<D, C::BS>(P.dout + base, rstride, nrows), rowbytes, w, lane);
   // out fragments of this lane's query row, for Di = rowsum(dO * out)
   const int i = w * 32 + li;
   u32x4 of[C::DS];

@@ -192,8 +192,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
   auto load_stage = [&](int st) {
     uint16_t* buf = lds + (st % C::NS) * C::STAGE;
     const int64_t r0 = int64_t(st) * C::BN * rstride;
-    tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
-    tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, L - st * C::BN),
+    tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
+    tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - st * C::BN),
                                rowbytes, w, lane);
   };
   auto ks_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
@@ -324,6 +324,10 @@ dq_kernel(DqParams P) {
     const int row0 = q_first + w * 32;
     store_rows<D>(lds + w * 32 * D, acc, P.scale,
                   P.dq + (int64_t(kv0) + row0) * rstride + int64_t(h) * D, rstride, L - row0, lane);
+    // the staging tiles lie in ring stages 0 and 1, which the next tile's first
+    // loads (issued by every wave) overwrite: no wave may start them before all
+    // waves have read their rows back
+    __syncthreads();
   }
 }
 
@@ -619,14 +623,14 @@ dkdv_kernel(KvParams P) {
     const int left = T.rows_total - q_first;
     const int sl = st % C::NS;
     tile_load<D, C::BM, C::NW>(ring + sl * C::TILE,
-                               rows_rsrc<D>(T.qbase + int64_t(q_first) * rstride, rstride, left),
+                               rows_rsrc<D, C::BM>(T.qbase + int64_t(q_first) * rstride, rstride, left),
                                rowbytes, w, lane);
     tile_load<D, C::BM, C::NW>(ring + (C::NS + sl) * C::TILE,
-                               rows_rsrc<D>(T.dobase + int64_t(q_first) * rstride, rstride, left),
+                               rows_rsrc<D, C::BM>(T.dobase + int64_t(q_first) * rstride, rstride, left),
                                rowbytes, w, lane);
     if (w < 2) {
       const float* src = (w == 0 ? P.nls : P.di) + T.voff + q_first;
-      vec64_load(vecs[sl][w], vec_rsrc(src, left), lane);
+      vec64_load(vecs[sl][w], vec_rsrc<C::BM>(src, left), lane);
     }
   };
 

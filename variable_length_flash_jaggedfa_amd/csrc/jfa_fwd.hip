@@ -260,8 +260,8 @@ fwd_kernel(FwdParams P) {
     auto load_stage = [&](int st) {
       uint16_t* buf = lds + (st % C::NS) * C::STAGE;
       const int64_t r0 = int64_t(st) * C::BN * rstride;
-      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D>(kbase + r0, rstride, Lk - st * C::BN), rowbytes, w, lane);
-      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D>(vbase + r0, rstride, Lk - st * C::BN),
+      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, Lk - st * C::BN), rowbytes, w, lane);
+      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, Lk - st * C::BN),
                                  rowbytes, w, lane);
     };
     auto stage_ptr = [&](int st) { return lds + (st % C::NS) * C::STAGE; };

@@ -62,16 +62,21 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int nbytes) {
   return r;
 }
 
-// Buffer resource over rows [0, nrows) of a bf16 matrix whose rows are `rstride`
-// elements apart and D elements wide.
-template <int D>
+// Buffer resource over rows [0, min(nrows, ROWS)) of a bf16 matrix whose rows
+// are `rstride` elements apart and D elements wide. ROWS is the tile the caller
+// addresses through it: `nrows` may be the rest of a long sequence, whose span
+// would not fit the 32-bit size word, while the tile's own span always does
+// (the host rejects problems whose ROWS rows of all heads reach 2^31 bytes).
+template <int D, int ROWS>
 __device__ __forceinline__ i32x4 rows_rsrc(const uint16_t* base, int64_t rstride, int nrows) {
-  return make_rsrc(base, nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0);
+  const int n = nrows < ROWS ? nrows : ROWS;
+  return make_rsrc(base, n > 0 ? int((int64_t(n - 1) * rstride + D) * 2) : 0);
 }
 
-// Buffer resource over n floats.
+// Buffer resource over min(n, N) floats (N: the entries the caller addresses).
+template <int N>
 __device__ __forceinline__ i32x4 vec_rsrc(const float* base, int n) {
-  return make_rsrc(base, n > 0 ? n * 4 : 0);
+  return make_rsrc(base, n > 0 ? (n < N ? n : N) * 4 : 0);
 }
 
 // LDS byte address of a pointer into __shared__ memory: the low 32 bits of its
@@ -241,7 +246,7 @@ __device__ __forceinline__ void store_rows(uint16_t* stage, const f32x16 (&a)[D 
   }
 }
 
-// store_rows through buffer stores whose resource covers rows [0, nrows): rows
+// store_rows through buffer stores whose resource covers rows [0, min(nrows, 32)): rows
 // past the end fall outside it and are dropped by the hardware, so every wave
 // issues exactly D/16 store instructions whatever nrows is (a caller may count
 // them in s_waitcnt vmcnt).
@@ -263,7 +268,9 @@ __device__ __forceinline__ void store_rows_counted(uint16_t* stage, const f32x16
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;  // rows per store instruction
   const int c = lane % CPR, r = lane / CPR;
-  const int nbytes = nrows > 0 ? int((int64_t(nrows - 1) * rstride + D) * 2) : 0;
+  // only the wave's 32 rows are addressed: the resource never spans more
+  const int nr = nrows < 32 ? nrows : 32;
+  const int nbytes = nr > 0 ? int((int64_t(nr - 1) * rstride + D) * 2) : 0;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       row0, (short)0, __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
 #pragma unroll

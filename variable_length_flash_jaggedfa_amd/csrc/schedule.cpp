@@ -65,7 +65,15 @@ jfa_status check_problem(const jfa_problem* p) {
   // element counts must stay addressable with 64-bit offsets and tiles in int32
   const double elems = double(std::max<int64_t>(p->total_kv, p->lq)) * p->num_heads * p->head_dim;
   if (elems > 4.0e15) return fail(JFA_ERR_INVALID_ARG, "problem too large");
+  if (bq && double(p->num_seqs) * p->lq * p->num_heads * p->head_dim > 4.0e15)
+    return fail(JFA_ERR_INVALID_ARG, "problem too large (broadcast-Q out rows)");
   if (p->total_kv > INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "total_kv exceeds int32");
+  // The kernels address one tile of at most 256 rows of one head through a
+  // buffer resource whose size and offsets are 32-bit: 256 token rows of all
+  // heads (256 * H * D bf16 values) must stay below 2^31 bytes.
+  if (int64_t(p->num_heads) * p->head_dim * 2 * 256 >= (int64_t(1) << 31))
+    return fail(JFA_ERR_UNSUPPORTED, "num_heads * head_dim too large: 256 token rows of all heads "
+                                     "must span less than 2^31 bytes");
   return JFA_OK;
 }
 
@@ -150,12 +158,16 @@ extern "C" jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* of
   if (kind != JFA_KIND_FWD && kind != JFA_KIND_BWD) return fail(JFA_ERR_INVALID_ARG, "bad kind");
   if (jfa_status s = check_offsets(p, offsets_host)) return s;
   if (unit_blocks(p)) {  // (64-token unit, head) pairs; 32-token blocks pair up in a unit
-    *num_tiles = ((p->total_kv + kBlock - 1) / kBlock) * p->num_heads;
+    const int64_t n = ((p->total_kv + kBlock - 1) / kBlock) * p->num_heads;
+    if (n > INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "too many tiles");
+    *num_tiles = n;
     return JFA_OK;
   }
   if (tiled_blocks(p)) {  // the jagged tiles of the blocks
     const int32_t rows = jfa_tile_rows(kind, p->head_dim, JFA_BLOCK_DIAG);
-    *num_tiles = (p->total_kv / p->block) * p->num_heads * ceil_div(p->block, rows);
+    const int64_t n = (p->total_kv / p->block) * p->num_heads * ceil_div(p->block, rows);
+    if (n > INT32_MAX) return fail(JFA_ERR_INVALID_ARG, "too many tiles");
+    *num_tiles = n;
     return JFA_OK;
   }
   const bool lqmode = (p->flags & JFA_BROADCAST_Q) && kind == JFA_KIND_FWD;
