@@ -267,6 +267,31 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
                           int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, uint32_t passes, void* stream);
 
+/* Bytes of the static device scratch array jfa_bwd_noalloc uses as its workspace
+ * (32 MiB, held by every GPU the library runs on until the process ends). */
+#define JFA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* jfa_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the workspace is a static device array of
+ * JFA_NOALLOC_SCRATCH_BYTES bytes in the library, and nothing is allocated.
+ * Same arguments, results and errors as jfa_bwd otherwise; the caller still
+ * provides every input and output buffer. A problem whose
+ * jfa_bwd_workspace_bytes exceeds JFA_NOALLOC_SCRATCH_BYTES is rejected with
+ * JFA_ERR_WORKSPACE before anything is enqueued (jagged problems up to about
+ * H * T = 4M query rows fit; broadcast-Q up to about
+ * 2 * B * H * Lq + min(B, 64) * Lq * H * D floats). Each GPU has one array,
+ * shared by every call on it: calls that overlap on one GPU (different streams
+ * or threads) race, calls on one stream do not. Nothing in it needs clearing
+ * between calls (the backward writes every workspace entry before reading it).
+ * The first call on a device looks up that device's copy of the array. */
+jfa_status jfa_bwd_noalloc(const jfa_problem* p, const void* q, const void* k, const void* v,
+                           const void* out, const void* dout, const float* lse,
+                           const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
+                           const int32_t* q_tiles_dev, int32_t q_num_slots,
+                           const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                           int32_t kv_num_slots, void* dq, void* dk, void* dv, void* stream);
+
 /* Matrix-core probe (measurement only; not a step of the attention path): a
  * kernel of `workgroups` workgroups of four waves, each wave running four
  * independent chains of `iters` bf16 32x32x16 MFMAs (32768 FLOP each) on

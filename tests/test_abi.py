@@ -338,3 +338,21 @@ def test_probe_rejects_bad_arguments_before_any_hip_call():
                                      (1, 1, ctypes.c_void_p(258), ok),
                                      (1, 1, ok, ctypes.c_void_p(260))):
         assert L.jfa_probe_mfma(iters, wgs, sink, clocks, None) == jfa.ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_oversized_problem_on_host():
+    """jfa_bwd_noalloc refuses a problem whose workspace exceeds its static scratch
+    array before any HIP call (so this runs without a GPU)."""
+    import ctypes
+    L = jfa.lib()
+    T = 5 << 20
+    p = jfa.problem(1, 1, 128, T, T, 0.088)
+    assert jfa.bwd_workspace_bytes(p) > jfa.NOALLOC_SCRATCH_BYTES
+    st = L.jfa_bwd_noalloc(ctypes.byref(p), *([None] * 9), 0, None, None, 0, None, None, None,
+                           None)
+    assert st == jfa.ERR_WORKSPACE
+    assert b"static scratch" in L.jfa_last_error()
+    p = jfa.problem(1, 1, 96, 8, 8, 0.1)  # an invalid problem: the usual error first
+    st = L.jfa_bwd_noalloc(ctypes.byref(p), *([None] * 9), 0, None, None, 0, None, None, None,
+                           None)
+    assert st == jfa.ERR_UNSUPPORTED

@@ -76,6 +76,9 @@ def lib():
         L.jfa_bwd_passes.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp,
                                      vp, vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp]
         L.jfa_bwd_passes.restype = i32
+        L.jfa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
+                                      vp, vp, vp, vp]
+        L.jfa_bwd_noalloc.restype = i32
         L.jfa_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
         L.jfa_probe_mfma.restype = i32
         L.jfa_status_string.argtypes = [i32]
@@ -181,6 +184,20 @@ def bwd_passes(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev,
                                 _ptr(kv_tiles_dev), int(kv_num_slots), _ptr(dq), _ptr(dk),
                                 _ptr(dv), _ptr(workspace), ws_bytes, int(passes),
                                 _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # JFA_NOALLOC_SCRATCH_BYTES
+
+
+def bwd_noalloc(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
+                q_num_slots, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv,
+                stream=None):
+    """jfa_bwd with the library's static scratch array as its workspace."""
+    _check(lib().jfa_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(dout), _ptr(lse), _ptr(offsets_dev), _ptr(q_slot_ptr_dev),
+                                 _ptr(q_tiles_dev), int(q_num_slots), _ptr(kv_slot_ptr_dev),
+                                 _ptr(kv_tiles_dev), int(kv_num_slots), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _stream(stream)))
 
 
 def probe_mfma(iters: int, workgroups: int, sink, clocks, stream=None):
@@ -291,4 +308,17 @@ class Plan:
             bwd(*args, stream)
         else:
             bwd_passes(*args, passes, stream)
+        return dq, dk, dv
+
+    def backward_noalloc(self, q, k, v, out, dout, lse=None, dq=None, dk=None, dv=None,
+                         stream=None):
+        """The backward through jfa_bwd_noalloc (the library's static scratch array
+        instead of the plan's workspace); the outputs must be given to allocate
+        nothing here either."""
+        sq, skv = self.sched.get(KIND_FWD), self.sched.get(KIND_BWD)
+        bwd_noalloc(self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
+                    sq.slot_ptr_dev if sq else None, sq.tiles_dev if sq else None,
+                    sq.num_slots if sq else 0, skv.slot_ptr_dev if skv else None,
+                    skv.tiles_dev if skv else None, skv.num_slots if skv else 0, dq, dk, dv,
+                    stream)
         return dq, dk, dv

@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-a
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 SOURCES = ["schedule.cpp", "api.cpp", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip", "jfa_rope.hip",
-           "jfa_probe.hip"]
+           "jfa_probe.hip", "jfa_noalloc.hip"]
 
 
 def hipcc() -> str:
