@@ -9,5 +9,7 @@ which holds no attention arithmetic.
   attention.py     exact softmax attention and its gradients, per sequence
   schedule_ref.py  the KV-work-sorted zigzag tile deal, in plain integers
   rotary.py        block-diagonal attention of rotary-embedded queries and keys
+  pool.py          the oracle over a whole workload in worker processes (sub-batches of
+                   sequences; comparison with stored results)
 """
 from . import attention, rotary, schedule_ref  # noqa: F401

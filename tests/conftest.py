@@ -22,7 +22,21 @@ def gpu_available() -> bool:
 
 @pytest.fixture(scope="session")
 def gpu():
+    # the oracle's worker processes fork from a server started before this process
+    # touches the GPU (no worker is a copy of a process holding the device)
+    from oracle import pool
+    pool.start_server()
     if not gpu_available():
         pytest.skip("no GPU visible")
     import torch
     return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def oracle_pool(gpu):
+    """Worker processes (one per core, at most 16) that run the fp64 oracle."""
+    from oracle import pool
+    p = pool.make_pool()
+    yield p
+    p.terminate()
+    p.join()

@@ -126,13 +126,17 @@ def max_abs(a, b):
     return float(np.max(np.abs(a - b))) if a.size else 0.0
 
 
-# Extra out allowance, relative to the reference, for the block-size extension
-# workloads (blocks other than 64 tokens): a query there averages fewer values, so
-# outputs of unit-variance data reach 4 and more, where one bf16 rounding of the
-# stored output alone (half a grid step, 2^-9 relative) is 1.6e-2, above the
-# absolute bar. Those cases get 1e-2 + 2^-8 |ref| per element.
+# Extra out allowance for the rounding of the stored bf16 output: out is returned in
+# bf16, and one round-to-nearest of a value of magnitude |ref| moves it by up to
+# half a bf16 step, at most 2^-8 |ref| (2^-9 relative is the typical bound, 2^-8 at
+# the bottom of a binade). At |out| >= 4 (which unit-variance data with few keys per
+# query reaches, e.g. 64-token blocks at D = 64, and more so smaller blocks) that
+# rounding alone exceeds the absolute 1e-2. The out check is therefore
+# |got - ref| <= 1e-2 + 2^-8 |ref| per element for every workload: the 1e-2 bounds
+# the arithmetic, the second term the final rounding (which is below 1e-3 for the
+# |out| < 0.25 of the sigma = 0.5 workloads).
 def out_rel(w) -> float:
-    return 2.0 ** -8 if w.kind == "block" and w.block != 64 else 0.0
+    return 2.0 ** -8
 
 
 def out_excess(got, ref, rel):
