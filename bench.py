@@ -205,6 +205,42 @@ def mfma_probe(dev, jfa, iters=150000, reps=3):
             "ms": round(ms, 4), "workgroups": wgs, "iters": iters}
 
 
+def copy_probe(dev, jfa, mib=2048, reps=10):
+    """The HBM bandwidth a plain streaming copy sustains, timed with events after the
+    timed region: the library's copy probe (16-byte non-temporal loads and stores,
+    four in flight per thread) over `mib` MiB at several grid sizes, the best median
+    kept, beside torch's own copy kernel. Reads and writes `mib` MiB each."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(fn):
+        times = []
+        for i in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i > 0:
+                times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    best = None
+    for per_cu in (4, 8, 16, 32):
+        ms = timed(lambda: jfa.probe_copy(src, dst, cus * per_cu))
+        if best is None or ms < best[0]:
+            best = (ms, per_cu)
+    torch_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    gbs = lambda ms: 2.0 * n * 4 / (ms * 1e-3) / 1e9
+    return {"gbs": round(gbs(best[0]), 1), "mib": mib, "ms": round(best[0], 4),
+            "workgroups_per_cu": best[1], "frac_of_spec_peak": round(gbs(best[0]) / PEAK_HBM_GBS, 4),
+            "torch_copy_gbs": round(gbs(torch_ms), 1)}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip",
                   "jfa_rope.h", "jfa_rope.hip")
@@ -266,7 +302,8 @@ def main():
                          "around the plain kernels), interleaved")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true",
-                    help="skip the matrix-core probe that reports the sustained bf16 MFMA rate and clock")
+                    help="skip the matrix-core probe (sustained bf16 MFMA rate and clock) and the "
+                         "HBM copy probe (practical memory bandwidth)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--digest", action="store_true",
                     help="print the kernel-source digest that traffic records are keyed by")
@@ -537,6 +574,9 @@ def main():
         rope_cmp = compare_rope(case, runs, q, k, v, do, dev, max(10, args.steps), order)
 
     probe = None if args.no_mfma_probe else mfma_probe(dev, jfa)
+    hbm = None if args.no_mfma_probe else copy_probe(dev, jfa)
+    if hbm is not None and roofline["bound"] == "hbm":
+        roofline["frac_of_copy"] = round(roofline["achieved"] / hbm["gbs"], 4)
     if probe is not None:
         probe["value_frac_of_probe"] = round(value / probe["tflops"], 4)
         if roofline["bound"] == "mfma":
@@ -570,6 +610,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "mfma_probe": probe,
+        "hbm_copy_probe": hbm,
     }
     if compare is not None:
         line["config"]["order_compare"] = compare

@@ -181,8 +181,8 @@ jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32
 /* Bytes of device workspace jfa_bwd needs: two float32 row vectors laid out like
  * lse, each rounded up to 256 bytes (-Di and -lse/scale, written by the dQ pass
  * and read by the dK/dV pass) and, for BROADCAST_Q, float32 dQ partials of
- * [G][Lq][H][D] where the B sequences are split into G = min(B, 64) contiguous
- * groups; for 128- or 256-token blocks also the block offsets, (T/block + 1)
+ * [G][Lq][H][D] where the B sequences are split into G = min(B, 128) contiguous
+ * groups (each holding about T/G keys); for 128- or 256-token blocks also the block offsets, (T/block + 1)
  * int32 rounded up to 256 bytes; for ROTARY (except on blocks of 32 or 64
  * tokens) also two bf16 [T, H, D] regions, each rounded up to 256 bytes, for the
  * rotated copies of q and k; 0 for blocks of 32 or 64 tokens. 0 for an invalid
@@ -280,7 +280,7 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
  * jfa_bwd_workspace_bytes exceeds JFA_NOALLOC_SCRATCH_BYTES is rejected with
  * JFA_ERR_WORKSPACE before anything is enqueued (jagged problems up to about
  * H * T = 4M query rows fit; broadcast-Q up to about
- * 2 * B * H * Lq + min(B, 64) * Lq * H * D floats). Each GPU has one array,
+ * 2 * B * H * Lq + min(B, 128) * Lq * H * D floats). Each GPU has one array,
  * shared by every call on it: calls that overlap on one GPU (different streams
  * or threads) race, calls on one stream do not. Nothing in it needs clearing
  * between calls (the backward writes every workspace entry before reading it).
@@ -309,6 +309,15 @@ jfa_status jfa_bwd_noalloc(const jfa_problem* p, const void* q, const void* k, c
  * pointer); asynchronous on `stream`. FLOP per call = workgroups*4*4*iters*32768. */
 jfa_status jfa_probe_mfma(int32_t iters, int32_t workgroups, float* sink, uint64_t* clocks,
                          void* stream);
+
+/* HBM copy probe (measurement only; not a step of the attention path): copies
+ * `bytes` bytes from `src` to `dst` (device memory, 16-byte aligned, bytes a
+ * multiple of 16) with 16-byte non-temporal loads and stores, `workgroups`
+ * workgroups of 256 threads striding over the buffers, so the benchmark can
+ * report the bandwidth a plain stream sustains beside the published 8 TB/s.
+ * Host checks only (INVALID_ARG); asynchronous on `stream`. */
+jfa_status jfa_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t workgroups,
+                          void* stream);
 
 /* Static text for a status code. */
 const char* jfa_status_string(jfa_status s);

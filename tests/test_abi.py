@@ -217,7 +217,7 @@ def test_workspace_bytes():
     r256 = lambda n: (n + 255) // 256 * 256
     # jagged: -Di and -lse/scale, each [H, T]
     assert jfa.bwd_workspace_bytes(_p()) == 2 * r256(2 * 15 * 4)
-    # broadcast: two [B, H, Lq] vectors + min(B, 64) partials of [Lq, H, D]
+    # broadcast: two [B, H, Lq] vectors + min(B, 128) partials of [Lq, H, D]
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BROADCAST_Q, lq=7)) == \
         2 * r256(2 * 2 * 7 * 4) + 2 * 7 * 2 * 64 * 4
     assert jfa.bwd_workspace_bytes(_p(flags=jfa.BLOCK_DIAG64, total_kv=128, max_len=64)) == 0

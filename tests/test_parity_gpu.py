@@ -339,3 +339,35 @@ def test_broadcast_one_sequence_matches_jagged(gpu, D, L):
         if first is None:
             first = dqb
         assert torch.equal(first, dqb)
+
+
+def test_validate_env_checks_device_schedule(gpu, monkeypatch):
+    """JFA_VALIDATE=1: a consistent call gives the same bits as without it; device
+    offsets that do not match the schedule are refused before anything runs."""
+    import torch
+    w = J.custom([300, 1, 129, 0, 64], 2, 128, sigma=0.5, seed=29, causal=True)
+    run = GpuRun(J.make_case(w), gpu)
+    out, lse = run.forward()
+    dq, dk, dv = run.backward()
+    monkeypatch.setenv("JFA_VALIDATE", "1")
+    out2, lse2 = run.plan.forward(run.q, run.k, run.v)
+    grads2 = run.plan.backward(run.q, run.k, run.v, out2, run.do, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for a, b in zip((dq, dk, dv), grads2):
+        assert torch.equal(a, b)
+    # sequence 0 shortened on the device only: its tiles no longer match
+    bad = run.plan.offsets_dev.clone()
+    bad[1] = 100
+    good = run.plan.offsets_dev
+    run.plan.offsets_dev = bad
+    try:
+        with pytest.raises(jfa.JfaError) as e:
+            run.plan.forward(run.q, run.k, run.v, out=out2, lse=lse2)
+        assert e.value.status == jfa.ERR_INVALID_ARG and "JFA_VALIDATE" in str(e.value)
+        with pytest.raises(jfa.JfaError):
+            run.plan.backward(run.q, run.k, run.v, out2, run.do, lse2)
+    finally:
+        run.plan.offsets_dev = good
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)  # the refused calls wrote nothing

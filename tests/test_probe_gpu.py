@@ -32,3 +32,27 @@ def test_probe_counters_and_rate(gpu):
     # a SIMD's matrix core does at most one 32x32x16 product per 32 core cycles,
     # and each of the workgroup's waves (one per SIMD) issues 4 x iters of them
     assert np.median(c[:, 0]) >= iters * 4 * 32 * 0.99
+
+
+def test_copy_probe_copies(gpu):
+    """The HBM copy probe moves every byte (ragged tail, several grid sizes) and
+    reports a bandwidth below the 8 TB/s spec."""
+    import torch
+    import variable_length_flash_jaggedfa_amd as jfa
+    n = (37 << 20) + 12  # floats: a size that is no multiple of the grid's stride
+    src = torch.arange(n, dtype=torch.float32, device=gpu)
+    for wgs in (1, 7, 2048):
+        dst = torch.zeros_like(src)
+        jfa.probe_copy(src, dst, wgs)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), wgs
+    big = torch.ones(256 << 20, dtype=torch.float32, device=gpu)
+    out = torch.empty_like(big)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    jfa.probe_copy(big, out, 2048)
+    e0.record()
+    jfa.probe_copy(big, out, 2048)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    assert 500 < gbs < 8000, gbs

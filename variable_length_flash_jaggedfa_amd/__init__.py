@@ -79,6 +79,8 @@ def lib():
         L.jfa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
                                       vp, vp, vp, vp]
         L.jfa_bwd_noalloc.restype = i32
+        L.jfa_probe_copy.argtypes = [vp, vp, ctypes.c_uint64, i32, vp]
+        L.jfa_probe_copy.restype = i32
         L.jfa_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
         L.jfa_probe_mfma.restype = i32
         L.jfa_status_string.argtypes = [i32]
@@ -198,6 +200,13 @@ def bwd_noalloc(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_slot_ptr_dev
                                  _ptr(q_tiles_dev), int(q_num_slots), _ptr(kv_slot_ptr_dev),
                                  _ptr(kv_tiles_dev), int(kv_num_slots), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _stream(stream)))
+
+
+def probe_copy(src, dst, workgroups: int, stream=None):
+    """HBM copy probe (measurement only): src -> dst, equal-sized device tensors."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes
+    _check(lib().jfa_probe_copy(_ptr(src), _ptr(dst), nbytes, int(workgroups), _stream(stream)))
 
 
 def probe_mfma(iters: int, workgroups: int, sink, clocks, stream=None):

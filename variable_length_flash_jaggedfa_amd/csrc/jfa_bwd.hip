@@ -42,10 +42,12 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 // ---------------------------------------------------------------- dQ pass
-template <int D>
+// NW waves of 32 query rows each: 4 for the jagged pass (the forward tiles of 128
+// rows), 8 for broadcast-Q (256 dense query rows share one key stream).
+template <int D, int NW_ = jfa::kFwdBM / 32>
 struct DqCfg {
-  static constexpr int BM = jfa::kFwdBM;         // query rows per tile (forward tiles)
-  static constexpr int NW = BM / 32;             // waves, 32 rows each
+  static constexpr int NW = NW_;                 // waves, 32 rows each
+  static constexpr int BM = 32 * NW;             // query rows per tile
   static constexpr int NT = 64 * NW;
   static constexpr int BN = D == 128 ? 32 : 64;  // keys per step
   static constexpr int KB = BN / 32;
@@ -174,7 +176,37 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
 // Steps [0, n_lo) (window edge) and [n_free, n_steps) (tail, diagonal) are masked.
 // The wave computes steps [0, n_own) only and meets the barriers and issues its
 // loads for the rest.
-template <int D, bool CAUSAL, bool WIN = false>
+// Stage st of the key stream: keys [st*BN, st*BN + BN) of K and V into ring
+// buffer st % NS, through buffer->LDS copies issued by all NW waves (keys at or
+// past L arrive as zeros).
+template <int D, int NW>
+__device__ __forceinline__ void dq_load_stage(uint16_t* lds, const uint16_t* kbase,
+                                              const uint16_t* vbase, int64_t rstride, int L, int st,
+                                              int w, int lane) {
+  using C = DqCfg<D, NW>;
+  uint16_t* buf = lds + (st % C::NS) * C::STAGE;
+  const int64_t r0 = int64_t(st) * C::BN * rstride;
+  const int rowbytes = int(rstride * 2);
+  tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - st * C::BN), rowbytes,
+                             w, lane);
+  tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - st * C::BN),
+                             rowbytes, w, lane);
+}
+
+// The first NS - 2 stages of a key stream, issued ahead of dq_stream<..., true>
+// so that their latency overlaps the caller's own loads (the query rows).
+template <int D, int NW>
+__device__ __forceinline__ void dq_stream_issue(uint16_t* lds, const uint16_t* kbase,
+                                                const uint16_t* vbase, int64_t rstride, int L,
+                                                int n_keys, int w, int lane) {
+  using C = DqCfg<D, NW>;
+  const int n_steps = ceil_div(n_keys, C::BN);
+#pragma unroll
+  for (int st = 0; st < C::NS - 2; ++st)
+    if (st < n_steps) dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
+}
+
+template <int D, bool CAUSAL, bool WIN = false, int NW = DqCfg<D>::NW, bool PRE = false>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
                                           int64_t rstride, int L, int n_keys, int n_lo, int n_free,
                                           int n_own, int win,
@@ -183,18 +215,13 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
                                           float c, int w, int lane, int qpos,
                                           const LaneOffsets<D>& lo) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, NW>;
   static_assert(C::NS == 4, "the ring below assumes four stages");
   const int g = lane >> 5;
   const int n_steps = ceil_div(n_keys, C::BN);
-  const int rowbytes = int(rstride * 2);
   const uint32_t lds0 = lds_addr(lds);
   auto load_stage = [&](int st) {
-    uint16_t* buf = lds + (st % C::NS) * C::STAGE;
-    const int64_t r0 = int64_t(st) * C::BN * rstride;
-    tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - st * C::BN), rowbytes, w, lane);
-    tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - st * C::BN),
-                               rowbytes, w, lane);
+    dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
   };
   auto ks_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
   auto arrive = [&](int st) {
@@ -202,9 +229,7 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     else wait_vmem();
     __syncthreads();
   };
-#pragma unroll
-  for (int st = 0; st < C::NS - 2; ++st)
-    if (st < n_steps) load_stage(st);
+  if (!PRE) dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, n_keys, w, lane);
   if (n_steps > 0) {
     f32x16 s[C::KB], dp[C::KB];
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
@@ -247,6 +272,22 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     }
   }
   __syncthreads();  // the next stream's first loads overwrite the first stages
+}
+
+// dO fragments of one query row (zero past the end) and its Di = rowsum(dO * out).
+template <int D>
+__device__ __forceinline__ float load_do_row(const uint16_t* orow, const uint16_t* dorow, bool ok,
+                                             int g, u32x4 (&dof)[DqCfg<D>::DS]) {
+  float di = 0.f;
+#pragma unroll
+  for (int d = 0; d < DqCfg<D>::DS; ++d) {
+    dof[d] = ok ? ld16(dorow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    const u32x4 of = ok ? ld16(orow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      di += bf16_lo(dof[d][e2]) * bf16_lo(of[e2]) + bf16_hi(dof[d][e2]) * bf16_hi(of[e2]);
+  }
+  return pair_sum(di);
 }
 
 // Q and dO fragments of one query row (zero past the end) and its Di.
@@ -303,6 +344,10 @@ dq_kernel(DqParams P) {
     const int n_own = w * 32 < q_rows ? n_steps : 1;
     const int64_t row = int64_t(kv0) + qpos;
     const int64_t eoff = row * rstride + int64_t(h) * D;
+    const uint16_t* kbase = P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
+    const uint16_t* vbase = P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
+    // the first key stages are in flight while the query rows load
+    dq_stream_issue<D, C::NW>(lds, kbase, vbase, rstride, L - ks0, n_keys, w, lane);
     u32x4 qf[C::DS], dof[C::DS];
     const float di = load_row<D>(P.q + eoff, P.o + eoff, P.dout + eoff, ok, g, qf, dof);
     const int64_t vidx = int64_t(h) * P.total_kv + row;
@@ -315,8 +360,7 @@ dq_kernel(DqParams P) {
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
-    dq_stream<D, CAUSAL, WIN>(lds, P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D,
-                              P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D, rstride, L - ks0,
+    dq_stream<D, CAUSAL, WIN, C::NW, true>(lds, kbase, vbase, rstride, L - ks0,
                               n_keys, n_lo, n_free, n_own, P.window, qf, dof, acc, lse2, di, P.c, w,
                               lane, qpos - ks0, lo);
     // dq_stream ended with a barrier: the ring is free to stage the output rows
@@ -331,44 +375,93 @@ dq_kernel(DqParams P) {
   }
 }
 
-// Broadcast-Q: workgroup (query tile, head, sequence group).
-template <int D>
-__global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+// Waves per broadcast-Q dQ workgroup: four (128 query rows), two workgroups per
+// compute unit, so that one workgroup's waits at a sequence boundary (its dO rows,
+// then its first key stages) run under the other's products.
+constexpr int kBcastDqWaves = 4;
+
+// First b in [0, B] with offsets[b] >= target (offsets non-decreasing, offsets[B]
+// >= target): a 64-way search by the whole wave, one round of loads per level.
+__device__ __forceinline__ int lower_bound_wave(const int32_t* off, int B, int64_t target, int lane) {
+  int lo = 0, hi = B;  // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int n = hi - lo;
+    const int stride = (n + 63) / 64;
+    const int idx = lo + lane * stride;
+    const bool ge = idx >= hi || int64_t(off[idx]) >= target;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ge);  // set from the first lane on
+    const int first = m ? __builtin_ctzll(m) : 64;
+    if (first == 0) {
+      hi = lo;
+    } else {
+      const int before = lo + (first - 1) * stride;  // off[before] < target
+      hi = first < 64 ? min(hi, lo + first * stride) : hi;
+      lo = before + 1;
+    }
+  }
+  return lo;
+}
+
+// Broadcast-Q dQ: workgroup (query tile of BM = 32 NW rows, head, sequence
+// group). The waves own 32 dense query rows each and share one key stream; Q is
+// loaded once per workgroup, and per sequence the waves load their dO and out
+// rows (Di) and lse. The sequences are split into `groups` contiguous groups
+// holding about the same number of keys (group g: the sequences whose first key
+// lies in [g T / G, (g+1) T / G)), so the workgroups carry similar work; each
+// writes one float32 partial of dQ. The query tiles of one (head, group) get
+// neighbouring workgroup numbers on one XCD (workgroup w runs on XCD w % 8), so
+// they stream the same K and V side by side through one L2.
+template <int D, int NW>
+__global__ void __launch_bounds__((DqCfg<D, NW>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 dq_bcast_kernel(DqParams P) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5;
   const LaneOffsets<D> lo(lane);
   const int n_qt = ceil_div(P.lq, C::BM);
-  const int t = blockIdx.x % n_qt, h = (blockIdx.x / n_qt) % P.H, grp = blockIdx.x / (n_qt * P.H);
-  const int b0 = int(int64_t(grp) * P.num_seqs / P.groups);
-  const int b1 = int(int64_t(grp + 1) * P.num_seqs / P.groups);
+  const int u = xcd_slot(blockIdx.x, gridDim.x);  // consecutive u share an XCD
+  const int t = u % n_qt, h = (u / n_qt) % P.H, grp = u / (n_qt * P.H);
+  const int64_t T = P.total_kv;
+  const int b0 = uniform(lower_bound_wave(P.offsets, P.num_seqs, int64_t(grp) * T / P.groups, lane));
+  const int b1 = grp + 1 == P.groups
+                     ? P.num_seqs
+                     : uniform(lower_bound_wave(P.offsets, P.num_seqs,
+                                                int64_t(grp + 1) * T / P.groups, lane));
   const int64_t rstride = int64_t(P.H) * D;
   const int qpos = t * C::BM + w * 32 + (lane & 31);
   const bool ok = qpos < P.lq;
-  const uint16_t* qrow = P.q + int64_t(qpos) * rstride + int64_t(h) * D;
+  u32x4 qf[C::DS];
+  {
+    const uint16_t* qrow = P.q + int64_t(qpos) * rstride + int64_t(h) * D;
+#pragma unroll
+    for (int d = 0; d < C::DS; ++d) qf[d] = ok ? ld16(qrow + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
+  }
+  // waves with no query row compute one step per sequence (nothing of it is kept)
+  const bool own = t * C::BM + w * 32 < P.lq;
   f32x16 acc[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
   for (int b = b0; b < b1; ++b) {
-    const int kv0 = P.offsets[b];
-    const int L = P.offsets[b + 1] - kv0;
+    const int kv0 = uniform(P.offsets[b]);
+    const int L = uniform(P.offsets[b + 1]) - kv0;
     const int64_t oeff = (int64_t(b) * P.lq + qpos) * rstride + int64_t(h) * D;
-    u32x4 qf[C::DS], dof[C::DS];
-    const float di = load_row<D>(qrow, P.o + oeff, P.dout + oeff, ok, g, qf, dof);
+    const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
+    const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
+    // the sequence's first key stages are in flight while its dO and out rows load
+    dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, L, w, lane);
+    u32x4 dof[C::DS];
+    const float di = load_do_row<D>(P.o + oeff, P.dout + oeff, ok, g, dof);
     const int64_t vidx = (int64_t(b) * P.H + h) * P.lq + qpos;
     const float lse = ok ? P.lse[vidx] : 0.f;
-    const float lse2 = lse * kLog2e;
     if (ok && g == 0) {
       P.di[vidx] = -di;
       P.nls[vidx] = -lse / P.scale;
     }
     if (L > 0)
-      dq_stream<D, false>(lds, P.k + int64_t(kv0) * rstride + int64_t(h) * D,
-                          P.v + int64_t(kv0) * rstride + int64_t(h) * D, rstride, L, L, 0, L / C::BN,
-                          t * C::BM + w * 32 < P.lq ? ceil_div(L, C::BN) : 1, 0, qf, dof, acc, lse2,
-                          di, P.c, w, lane, qpos, lo);
+      dq_stream<D, false, false, NW, true>(lds, kbase, vbase, rstride, L, L, 0,
+                                    L / C::BN, own ? ceil_div(L, C::BN) : 1, 0, qf, dof, acc,
+                                    lse * kLog2e, di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;
@@ -831,9 +924,10 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   const bool run_dq = a.passes & JFA_PASS_DQ, run_kv = a.passes & JFA_PASS_DKDV;
   if (!run_dq) {
   } else if (BCAST) {
-    const int n_qt = (a.lq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-    hipLaunchKernelGGL(dq_bcast_kernel<D>, dim3(n_qt * a.num_heads * a.groups), dim3(DqCfg<D>::NT),
-                       0, st, dp);
+    using BC = DqCfg<D, kBcastDqWaves>;
+    const int n_qt = (a.lq + BC::BM - 1) / BC::BM;
+    hipLaunchKernelGGL((dq_bcast_kernel<D, kBcastDqWaves>), dim3(n_qt * a.num_heads * a.groups),
+                       dim3(BC::NT), 0, st, dp);
     const int64_t n4 = int64_t(a.lq) * a.num_heads * D / 4;
     hipLaunchKernelGGL(dq_reduce_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_part,
                        static_cast<uint16_t*>(a.dq), n4, a.groups, a.scale);

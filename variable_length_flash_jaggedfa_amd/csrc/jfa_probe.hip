@@ -1,7 +1,8 @@
-// Matrix-core throughput and clock probe for gfx950. Measurement only: no step
-// of the attention path runs here. It gives the benchmark the bf16 MFMA rate the
-// chip actually sustains, and the core clock it sustains it at, beside the
-// published dense peak (which assumes 2.4 GHz).
+// Matrix-core throughput and clock probe, and an HBM copy probe, for gfx950.
+// Measurement only: no step of the attention path runs here. They give the
+// benchmark the bf16 MFMA rate the chip actually sustains (and the core clock it
+// sustains it at) beside the published dense peak, which assumes 2.4 GHz, and the
+// memory bandwidth a plain streaming copy reaches beside the 8 TB/s spec.
 //
 // Every wave runs four independent accumulation chains of
 // v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 multiply-adds, 32768 FLOP each) for
@@ -65,7 +66,50 @@ __global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(int iters, fl
   }
 }
 
+// Streaming copy for the HBM probe: each thread moves UNROLL 16-byte vectors per
+// pass (all loads issued before the stores, so a wave keeps UNROLL loads in
+// flight), grid-striding over n16 vectors. Every access is at an index < n16.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ void __launch_bounds__(kCopyThreads) copy_probe_kernel(const u32x4* __restrict__ src,
+                                                                  u32x4* __restrict__ dst,
+                                                                  int64_t n16) {
+  const int64_t step = int64_t(gridDim.x) * kCopyThreads * kCopyUnroll;
+  for (int64_t base = int64_t(blockIdx.x) * kCopyThreads * kCopyUnroll + threadIdx.x; base < n16;
+       base += step) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + int64_t(u) * kCopyThreads;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + int64_t(u) * kCopyThreads;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" jfa_status jfa_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t workgroups,
+                                     void* stream) {
+  jfa::set_error("");
+  if (!src || !dst) return jfa::fail(JFA_ERR_INVALID_ARG, "src and dst must be device pointers");
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16 || bytes % 16)
+    return jfa::fail(JFA_ERR_INVALID_ARG, "src, dst and bytes must be multiples of 16");
+  if (workgroups < 1 || workgroups > 65536)
+    return jfa::fail(JFA_ERR_INVALID_ARG, "workgroups must be in [1, 65536]");
+  if (bytes == 0) return JFA_OK;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3(workgroups), dim3(kCopyThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), int64_t(bytes / 16));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("copy probe launch: ") + hipGetErrorString(e));
+  return JFA_OK;
+}
 
 extern "C" jfa_status jfa_probe_mfma(int32_t iters, int32_t workgroups, float* sink,
                                      uint64_t* clocks, void* stream) {

@@ -328,7 +328,7 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
 
 namespace jfa {
 
-int bcast_groups(int num_seqs) { return num_seqs < 1 ? 1 : (num_seqs < 64 ? num_seqs : 64); }
+int bcast_groups(int num_seqs) { return num_seqs < 1 ? 1 : (num_seqs < 128 ? num_seqs : 128); }
 
 size_t di_bytes(const jfa_problem* p) {
   const int64_t n = (p->flags & JFA_BROADCAST_Q) ? int64_t(p->num_seqs) * p->num_heads * p->lq
