@@ -269,6 +269,9 @@ def measured_traffic(kernel, variant):
     """HBM bytes per launch of `kernel` on `variant`, from the scaled FETCH_SIZE +
     WRITE_SIZE counters recorded in profiles/hbm_traffic.txt, or None when no
     record exists or the kernel sources changed since the counters were taken."""
+    if " + " in kernel:  # a pass of several kernels: the sum of their records
+        parts = [measured_traffic(k, variant) for k in kernel.split(" + ")]
+        return None if any(x is None for x in parts) else sum(parts)
     if not os.path.exists(TRAFFIC_FILE):
         return None
     digest = kernel_source_digest()

@@ -24,6 +24,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-a
           # no packed fp32 instructions in device code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
+# Per-source flags. The backward passes schedule better with the instruction-level
+# parallelism strategy of the machine scheduler (dQ pass about 2% faster, dK/dV
+# pass unchanged, measured A/B on the GEM workload); the forward keeps the default
+# (1-4% slower with it).
+EXTRA = {"jfa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 SOURCES = ["schedule.cpp", "api.cpp", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip", "jfa_rope.hip",
            "jfa_probe.hip", "jfa_noalloc.hip"]
 
@@ -38,7 +43,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
