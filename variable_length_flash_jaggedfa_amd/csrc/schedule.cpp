@@ -137,6 +137,28 @@ std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t ki
   return tiles;
 }
 
+// Indices 0..n-1 ordered by descending key, ties in ascending index (a stable
+// sort). Keys are KV work, non-negative and bounded by the longest sequence (or
+// Lq), so a counting sort over the key range does it in linear time; a range
+// beyond 2^22 falls back to a comparison sort.
+std::vector<int32_t> order_by_desc(const std::vector<int32_t>& key) {
+  const size_t n = key.size();
+  std::vector<int32_t> idx(n);
+  int32_t mx = 0;
+  for (int32_t k : key) mx = std::max(mx, k);
+  if (mx > (1 << 22)) {
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return key[a] > key[b]; });
+    return idx;
+  }
+  // start[k]: first output position of key k, larger keys first
+  std::vector<int64_t> start(size_t(mx) + 2, 0);
+  for (int32_t k : key) ++start[size_t(mx - k) + 1];
+  for (size_t i = 1; i < start.size(); ++i) start[i] += start[i - 1];
+  for (size_t i = 0; i < n; ++i) idx[size_t(start[size_t(mx - key[i])]++)] = int32_t(i);
+  return idx;
+}
+
 }  // namespace
 }  // namespace jfa
 
@@ -214,7 +236,6 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
                                                   : enumerate(p, offsets_host, kind);
   std::vector<int32_t> idx;      // tiles in dealing order
   std::vector<int32_t> slot_of;  // slot of idx[j]
-  auto by_work = [&](int32_t a, int32_t b) { return tiles[a].work > tiles[b].work; };
   if (order == JFA_ORDER_XCD_ZIGZAG) {
     constexpr int32_t X = kXcds;
     if (num_slots % X) return fail(JFA_ERR_INVALID_ARG, "XCD_ZIGZAG needs num_slots % 8 == 0");
@@ -230,21 +251,24 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
     }
     unit_first.push_back(int32_t(tiles.size()));
     const int32_t nu = int32_t(unit_work.size());
-    std::vector<int32_t> uorder(nu);
-    std::iota(uorder.begin(), uorder.end(), 0);
-    std::stable_sort(uorder.begin(), uorder.end(),
-                     [&](int32_t a, int32_t b) { return unit_work[a] > unit_work[b]; });
+    const std::vector<int32_t> uorder = order_by_desc(unit_work);
     std::vector<int32_t> group_of(nu);
     for (int32_t j = 0; j < nu; ++j) {
       const int32_t pass = j / X, r = j % X;
       group_of[uorder[j]] = (pass & 1) ? X - 1 - r : r;
     }
     for (int32_t x = 0; x < X; ++x) {
-      std::vector<int32_t> gt;  // this group's tiles, generation order
+      std::vector<int32_t> g0;  // this group's tiles, generation order
       for (int32_t u = 0; u < nu; ++u)
         if (group_of[u] == x)
-          for (int32_t i = unit_first[u]; i < unit_first[u + 1]; ++i) gt.push_back(i);
-      std::stable_sort(gt.begin(), gt.end(), by_work);
+          for (int32_t i = unit_first[u]; i < unit_first[u + 1]; ++i) g0.push_back(i);
+      std::vector<int32_t> gw(g0.size());
+      for (size_t j = 0; j < g0.size(); ++j) gw[j] = tiles[g0[j]].work;
+      std::vector<int32_t> gt(g0.size());
+      {
+        const std::vector<int32_t> o = order_by_desc(gw);
+        for (size_t j = 0; j < o.size(); ++j) gt[j] = g0[o[j]];
+      }
       for (size_t j = 0; j < gt.size(); ++j) {
         const int64_t pass = int64_t(j) / sx;
         const int32_t r = int32_t(int64_t(j) % sx);
@@ -287,10 +311,7 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
     }
     const int32_t ni = int32_t(item_work.size());
     item_first.push_back(int32_t(item_tiles.size()));
-    std::vector<int32_t> iorder(ni);
-    std::iota(iorder.begin(), iorder.end(), 0);
-    std::stable_sort(iorder.begin(), iorder.end(),
-                     [&](int32_t a, int32_t b) { return item_work[a] > item_work[b]; });
+    const std::vector<int32_t> iorder = order_by_desc(item_work);
     for (int32_t j = 0; j < ni; ++j) {
       const int32_t pass = j / num_slots, r = j % num_slots;
       const int32_t sl = (pass & 1) ? num_slots - 1 - r : r;
@@ -301,10 +322,15 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
       }
     }
   } else {
-    idx.resize(tiles.size());
-    std::iota(idx.begin(), idx.end(), 0);
     // descending work; ties keep generation order
-    if (order == JFA_ORDER_ZIGZAG) std::stable_sort(idx.begin(), idx.end(), by_work);
+    if (order == JFA_ORDER_ZIGZAG) {
+      std::vector<int32_t> w(tiles.size());
+      for (size_t j = 0; j < tiles.size(); ++j) w[j] = tiles[j].work;
+      idx = order_by_desc(w);
+    } else {
+      idx.resize(tiles.size());
+      std::iota(idx.begin(), idx.end(), 0);
+    }
     // deal: sorted position j -> pass j / S, rank r = j % S
     slot_of.resize(idx.size());
     for (size_t j = 0; j < idx.size(); ++j) {
