@@ -323,10 +323,10 @@ dq_kernel(DqParams P) {
   const int t_begin = P.slot_ptr[slot], t_end = P.slot_ptr[slot + 1];
   const int64_t rstride = int64_t(P.H) * D;
   for (int ti = t_begin; ti < t_end; ++ti) {
-    const int b = uniform(P.tiles[4 * ti + 0]), h = uniform(P.tiles[4 * ti + 1]);
-    const int t = uniform(P.tiles[4 * ti + 2]);
-    const int kv0 = uniform(P.offsets[b]);
-    const int L = uniform(P.offsets[b + 1]) - kv0;
+    const int b = sload(P.tiles + 4 * ti + 0), h = sload(P.tiles + 4 * ti + 1);
+    const int t = sload(P.tiles + 4 * ti + 2);
+    const int kv0 = sload(P.offsets + b);
+    const int L = sload(P.offsets + b + 1) - kv0;
     const int q_first = t * C::BM;
     const int q_rows = min(C::BM, L - q_first);
     // with a sliding window the keys are streamed from ks0, the start of the step
@@ -443,8 +443,8 @@ dq_bcast_kernel(DqParams P) {
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
   for (int b = b0; b < b1; ++b) {
-    const int kv0 = uniform(P.offsets[b]);
-    const int L = uniform(P.offsets[b + 1]) - kv0;
+    const int kv0 = sload(P.offsets + b);
+    const int L = sload(P.offsets + b + 1) - kv0;
     const int64_t oeff = (int64_t(b) * P.lq + qpos) * rstride + int64_t(h) * D;
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
@@ -680,19 +680,27 @@ dkdv_kernel(KvParams P) {
   const int rowbytes = int(rstride * 2);
 
   // what every wave derives from a tile of the schedule
-  struct Tile {
-    int b, h, kv0, L, key0, rows_total, qs_lo, n_steps, n_mask, n_hi;
+  struct Entry {  // what the schedule and the offsets give for a tile
+    int b, h, kv0, L, key0;
+  };
+  struct Tile : Entry {
+    int rows_total, qs_lo, n_steps, n_mask, n_hi;
     const uint16_t* qbase;
     const uint16_t* dobase;
     int64_t voff;
   };
-  auto tile_of = [&](int ti) {
+  auto entry_of = [&](int ti) {
+    Entry E;
+    E.b = sload(P.tiles + 4 * ti + 0);
+    E.h = sload(P.tiles + 4 * ti + 1);
+    E.key0 = sload(P.tiles + 4 * ti + 2) * C::BN;
+    E.kv0 = sload(P.offsets + E.b);
+    E.L = sload(P.offsets + E.b + 1) - E.kv0;
+    return E;
+  };
+  auto tile_of = [&](const Entry& E) {
     Tile T;
-    T.b = uniform(P.tiles[4 * ti + 0]);
-    T.h = uniform(P.tiles[4 * ti + 1]);
-    T.key0 = uniform(P.tiles[4 * ti + 2]) * C::BN;
-    T.kv0 = uniform(P.offsets[T.b]);
-    T.L = uniform(P.offsets[T.b + 1]) - T.kv0;
+    static_cast<Entry&>(T) = E;
     T.rows_total = BCAST ? P.lq : T.L;
     T.qbase = BCAST ? P.q + int64_t(T.h) * D : P.q + int64_t(T.kv0) * rstride + int64_t(T.h) * D;
     T.dobase = BCAST ? P.dout + int64_t(T.b) * P.lq * rstride + int64_t(T.h) * D
@@ -730,13 +738,21 @@ dkdv_kernel(KvParams P) {
   // One role per wave, each walking all the slot's tiles; both meet the same
   // barriers. Step it: wait for stage it, barrier (every wave is done with step
   // it-1, so the buffers of stage it-2 are free and the P of step it-1 is in
-  // LDS); stage it+1 is loaded during the step. The first stage and the key
-  // operand of the next tile are loaded before this tile's output rows are
-  // stored, so their latency runs under the epilogue.
+  // LDS); stage it+1 is loaded during the step. The next tile's first stage is
+  // loaded before this tile's output rows are stored, so its latency runs under
+  // the stores, and so is its key operand, except with broadcast-Q (EARLY).
+  // There every tile has only lq/64 steps, and the epilogue, where that key
+  // operand's 32 rows x 32 bytes per load instruction queue up behind every
+  // wave's stage loads and stores in the CU's vector memory path, is a large
+  // share of the tile: the operand is loaded in the last step instead, once that
+  // step's scores have read the current one (dK/dV pass 8% faster on 4-step
+  // tiles; 3-5% slower on the long tiles of self-attention, where the test in
+  // every step costs more than the epilogue saves).
   auto run = [&](auto role) {
     constexpr bool PW = decltype(role)::value;
+    constexpr bool EARLY = BCAST;
     const uint16_t* kvsrc = PW ? P.k : P.v;  // the wave's 32-key operand: K or V
-    auto load_op = [&](const Tile& T, u32x4 (&op)[C::DS]) {
+    auto load_op = [&](const Entry& T, u32x4 (&op)[C::DS]) {
       const int jw = T.key0 + kw * 32 + li;
       const uint16_t* obase = kvsrc + int64_t(T.kv0) * rstride + int64_t(T.h) * D;
 #pragma unroll
@@ -746,11 +762,21 @@ dkdv_kernel(KvParams P) {
     u32x4 op[C::DS];
     Tile T{};
     if (t_begin < t_end) {
-      T = tile_of(t_begin);
+      T = tile_of(entry_of(t_begin));
       load_op(T, op);
       load_stage(T, 0);
     }
     for (int ti = t_begin; ti < t_end; ++ti) {
+      // EARLY: the next tile's schedule entry, read at the start of this one and
+      // kept in vector registers (scalar ones are all taken by the steps). Its
+      // scalar loads are waited for here: left outstanding into the steps, they
+      // would turn every counted wait for the steps' LDS reads into a full wait
+      // (scalar loads return out of order on the same counter).
+      Entry En{};
+      if (EARLY) {
+        if (ti + 1 < t_end) En = entry_of(ti + 1);
+        asm volatile("" : "+v"(En.b), "+v"(En.h), "+v"(En.kv0), "+v"(En.L), "+v"(En.key0));
+      }
       const int row0 = T.key0 + kw * 32;
       const int jw = row0 + li;  // this lane's key
       // lane-dependent addresses are derived afresh for each tile (otherwise the
@@ -791,6 +817,9 @@ dkdv_kernel(KvParams P) {
       for (int d = 0; d < C::DS; ++d) asm volatile("" ::"v"(op[d]));
       f32x16 s[C::IB];
       u32x4 pk[C::PK];
+      // the next tile's key operand (op is dead once the last scores are in);
+      // after the slot's last tile En is all zeros, so no lane loads
+      auto next_op = [&]() { load_op(En, op); };
       auto step = [&](int it, auto stage) {
         constexpr int S = decltype(stage)::value, SP = (S + C::NS - 1) % C::NS;
         const bool prev = S != 0 || it > 0;
@@ -804,6 +833,7 @@ dkdv_kernel(KvParams P) {
         if (PW) {
           __builtin_amdgcn_s_setprio(1);
           kv_scores<D, S>(ad, op, s);
+          if (EARLY && it + 1 == T.n_steps) next_op();
           if (prev) kv_products<D, SP>(ad, pk, acc);
           __builtin_amdgcn_s_setprio(0);
           // the P waves issue their share of the next stage's loads after their
@@ -825,6 +855,7 @@ dkdv_kernel(KvParams P) {
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
           __builtin_amdgcn_s_setprio(1);
           kv_scores<D, S>(ad, op, s);
+          if (EARLY && it + 1 == T.n_steps) next_op();
           if (prev) kv_products<D, SP>(ad, pk, acc);
           __builtin_amdgcn_s_setprio(0);
         }
@@ -855,6 +886,7 @@ dkdv_kernel(KvParams P) {
           __syncthreads();
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
         }
+        if (EARLY) next_op();
         __syncthreads();  // the tail's barrier
       } else {
         for (int it = 0; it < T.n_steps; it += 3) {
@@ -870,8 +902,13 @@ dkdv_kernel(KvParams P) {
       __syncthreads();  // every wave is done with the ring and the exchange
       const Tile Tc = T;
       if (ti + 1 < t_end) {
-        T = tile_of(ti + 1);
-        load_op(T, op);
+        if (EARLY) {
+          T = tile_of(Entry{uniform(En.b), uniform(En.h), uniform(En.kv0), uniform(En.L),
+                            uniform(En.key0)});
+        } else {
+          T = tile_of(entry_of(ti + 1));
+          load_op(T, op);
+        }
         load_stage(T, 0);
       }
       // output rows staged in ring stages 1 and 2 (stage 0 is filling); the next

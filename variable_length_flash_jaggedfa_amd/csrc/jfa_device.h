@@ -58,6 +58,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 // compiler cannot prove this for loads from buffers the kernel may also write).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A schedule or offsets entry the whole wave reads at one address, loaded into a
+// scalar register through the scalar data cache. The pointer is taken as constant
+// memory, which the compiler may read with scalar loads wherever the address is
+// uniform: the schedule and offsets are written before the launch and never
+// while a kernel runs. (Through the vector path, each tile's two dependent
+// lookups cost two round trips to L2 and a wait on every vector load in flight.)
+__device__ __forceinline__ int sload(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }

@@ -54,10 +54,10 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(RopeRowsParams P) {
   const int n = P.slot_ptr[P.num_slots];
   const int64_t rstride = int64_t(P.H) * D;
   for (int ti = blockIdx.x; ti < n; ti += gridDim.x) {
-    const int b = uniform(P.tiles[4 * ti + 0]), h = uniform(P.tiles[4 * ti + 1]);
-    const int t = uniform(P.tiles[4 * ti + 2]);
-    const int kv0 = uniform(P.offsets[b]);
-    const int L = uniform(P.offsets[b + 1]) - kv0;
+    const int b = sload(P.tiles + 4 * ti + 0), h = sload(P.tiles + 4 * ti + 1);
+    const int t = sload(P.tiles + 4 * ti + 2);
+    const int kv0 = sload(P.offsets + b);
+    const int L = sload(P.offsets + b + 1) - kv0;
     for (int it = threadIdx.x; it < ITEMS; it += 256) {
       const int r = t * jfa::kFwdBM + it / CH, c = it % CH;
       if (r >= L) break;  // later items of this thread lie further down the tile
