@@ -738,16 +738,17 @@ dkdv_kernel(KvParams P) {
   // One role per wave, each walking all the slot's tiles; both meet the same
   // barriers. Step it: wait for stage it, barrier (every wave is done with step
   // it-1, so the buffers of stage it-2 are free and the P of step it-1 is in
-  // LDS); stage it+1 is loaded during the step. The next tile's first stage is
-  // loaded before this tile's output rows are stored, so its latency runs under
-  // the stores, and so is its key operand, except with broadcast-Q (EARLY).
-  // There every tile has only lq/64 steps, and the epilogue, where that key
-  // operand's 32 rows x 32 bytes per load instruction queue up behind every
-  // wave's stage loads and stores in the CU's vector memory path, is a large
-  // share of the tile: the operand is loaded in the last step instead, once that
-  // step's scores have read the current one (dK/dV pass 8% faster on 4-step
-  // tiles; 3-5% slower on the long tiles of self-attention, where the test in
-  // every step costs more than the epilogue saves).
+  // LDS); stage it+1 is loaded during the step. The next tile's key operand is
+  // loaded once the last scores have read the current one: its 32 rows x 32
+  // bytes per load instruction are the tile's costliest accesses for the CU's
+  // vector memory path, and issued in the epilogue they queued up behind every
+  // wave's stage loads and stores there. With broadcast-Q (EARLY), where a tile
+  // has only lq/64 steps and the epilogue is a large share of it, they are
+  // issued inside the last step, under its products (dK/dV pass 8% faster on
+  // 4-step tiles); otherwise after the step loop, under the tail (a test in
+  // every step cost the long self-attention tiles 3-5%; after the loop the
+  // causal pass gains 3%). The next tile's first stage is loaded before this
+  // tile's output rows are stored, so its latency runs under the stores.
   auto run = [&](auto role) {
     constexpr bool PW = decltype(role)::value;
     constexpr bool EARLY = BCAST;
@@ -767,16 +768,14 @@ dkdv_kernel(KvParams P) {
       load_stage(T, 0);
     }
     for (int ti = t_begin; ti < t_end; ++ti) {
-      // EARLY: the next tile's schedule entry, read at the start of this one and
-      // kept in vector registers (scalar ones are all taken by the steps). Its
-      // scalar loads are waited for here: left outstanding into the steps, they
-      // would turn every counted wait for the steps' LDS reads into a full wait
+      // The next tile's schedule entry, read at the start of this one and kept
+      // in vector registers (scalar ones are all taken by the steps). Its scalar
+      // loads are waited for here: left outstanding into the steps, they would
+      // turn every counted wait for the steps' LDS reads into a full wait
       // (scalar loads return out of order on the same counter).
       Entry En{};
-      if (EARLY) {
-        if (ti + 1 < t_end) En = entry_of(ti + 1);
-        asm volatile("" : "+v"(En.b), "+v"(En.h), "+v"(En.kv0), "+v"(En.L), "+v"(En.key0));
-      }
+      if (ti + 1 < t_end) En = entry_of(ti + 1);
+      asm volatile("" : "+v"(En.b), "+v"(En.h), "+v"(En.kv0), "+v"(En.L), "+v"(En.key0));
       const int row0 = T.key0 + kw * 32;
       const int jw = row0 + li;  // this lane's key
       // lane-dependent addresses are derived afresh for each tile (otherwise the
@@ -886,7 +885,7 @@ dkdv_kernel(KvParams P) {
           __syncthreads();
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
         }
-        if (EARLY) next_op();
+        next_op();
         __syncthreads();  // the tail's barrier
       } else {
         for (int it = 0; it < T.n_steps; it += 3) {
@@ -894,6 +893,7 @@ dkdv_kernel(KvParams P) {
           if (it + 1 < T.n_steps) step(it + 1, S1{});
           if (it + 2 < T.n_steps) step(it + 2, S2{});
         }
+        if (!EARLY) next_op();
         const int last = (T.n_steps - 1) % C::NS;
         if (last == 0) tail(S0{});
         else if (last == 1) tail(S1{});
@@ -902,13 +902,8 @@ dkdv_kernel(KvParams P) {
       __syncthreads();  // every wave is done with the ring and the exchange
       const Tile Tc = T;
       if (ti + 1 < t_end) {
-        if (EARLY) {
-          T = tile_of(Entry{uniform(En.b), uniform(En.h), uniform(En.kv0), uniform(En.L),
-                            uniform(En.key0)});
-        } else {
-          T = tile_of(entry_of(ti + 1));
-          load_op(T, op);
-        }
+        T = tile_of(Entry{uniform(En.b), uniform(En.h), uniform(En.kv0), uniform(En.L),
+                          uniform(En.key0)});
         load_stage(T, 0);
       }
       // output rows staged in ring stages 1 and 2 (stage 0 is filling); the next
