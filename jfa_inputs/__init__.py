@@ -27,6 +27,12 @@ section 1):
   gem_padded  the gem batch with every sequence as long as its longest one (the
               padded-dense layout the jagged one avoids), causal and non-causal;
               for timing the work a padded-dense run executes.
+  sparse      block-sparse self-attention over 64-token blocks: B=1152, L ~
+              U{1..4096} (the last block of a sequence partial), H=4, D in
+              {64,128}, sigma 1; each query block attends its own key block and
+              each other key block of its sequence with probability 0.3, about
+              70% of the block pairs of a long sequence masked (the sparsity the
+              block-attention page reports for its workloads, section 1).
 """
 from __future__ import annotations
 
@@ -38,11 +44,12 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # stream ids
-S_LENGTHS, S_Q, S_K, S_V, S_DO, S_QDENSE = 0, 1, 2, 3, 4, 5
+S_LENGTHS, S_Q, S_K, S_V, S_DO, S_QDENSE, S_MASK = 0, 1, 2, 3, 4, 5, 6
+SPARSE_BLOCK = 64
 
 # gem_padded shares gem's id, so its lengths are the gem draw padded to the maximum
 WORKLOAD_IDS = {"tiny": 1, "gem": 2, "broadcast": 3, "block64": 4, "imbalance": 5,
-                "gem_padded": 2}
+                "gem_padded": 2, "sparse": 6}
 
 
 @dataclass(frozen=True)
@@ -52,7 +59,7 @@ class Workload:
     num_heads: int
     head_dim: int
     sigma: float
-    kind: str = "jagged"        # "jagged" | "broadcast" | "block" (block-diagonal)
+    kind: str = "jagged"        # "jagged" | "broadcast" | "block" (block-diagonal) | "sparse"
     causal: bool = False
     lq: int = 0                 # dense Q rows for "broadcast"
     seed: int = 0
@@ -69,6 +76,7 @@ class Workload:
     rope_base: float = 0.0            # rotary embeddings with this base (0: none)
     window: int = 0                   # causal sliding window of this many keys (0: none)
     block: int = 64                   # kind "block": tokens per diagonal block
+    density: float = 0.0              # kind "sparse": chance of each off-diagonal block pair
 
     @property
     def wid(self) -> int:
@@ -118,6 +126,10 @@ def standard_workloads():
                                causal=True, window=512),
         "gem_padded_causal": Workload("gem_padded", 256, 8, 128, 0.5, law="loguniform", lo=16,
                                       hi=4096, pad_to_max=True, causal=True),
+        "sparse_d128": Workload("sparse", 1152, 4, 128, 1.0, kind="sparse", law="uniform",
+                                lo=1, hi=4096, density=0.3),
+        "sparse_d64": Workload("sparse", 1152, 4, 64, 1.0, kind="sparse", law="uniform",
+                               lo=1, hi=4096, density=0.3),
     }
 
 
@@ -163,6 +175,22 @@ def offsets_from_lengths(L) -> np.ndarray:
     np.cumsum(L, out=off[1:])
     assert off[-1] < 2**31
     return off.astype(np.int32)
+
+
+def sparse_mask_seq(w: Workload, b: int, L: int) -> np.ndarray:
+    """Block mask of sequence b (uint8 [n, n], n = ceil(L / 64)): row = query
+    block, column = key block; the diagonal always set, every other entry set with
+    probability w.density."""
+    n = -(-int(L) // SPARSE_BLOCK)
+    m = (_rng(w, S_MASK, b).random((n, n)) < w.density)
+    m |= np.eye(n, dtype=bool)
+    return m.astype(np.uint8)
+
+
+def sparse_mask_flat(w: Workload, L) -> np.ndarray:
+    """Every sequence's block mask, row-major, concatenated (uint8)."""
+    parts = [sparse_mask_seq(w, b, int(n)).ravel() for b, n in enumerate(L)]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint8)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -225,6 +253,7 @@ class Case:
     v: np.ndarray       # [T,H,D]
     do: np.ndarray      # [T,H,D] or [B,Lq,H,D] for broadcast
     scale: float        # float32 value of 1/sqrt(D)
+    mask: np.ndarray = None  # kind "sparse": the flat block masks (uint8)
 
     @property
     def max_len(self) -> int:
@@ -247,16 +276,17 @@ def make_case(w: Workload, with_do: bool = True) -> Case:
         do = packed_values(w, S_DO, L) if with_do else None
     k = packed_values(w, S_K, L)
     v = packed_values(w, S_V, L)
-    return Case(w, L, off, q, k, v, do, softmax_scale(w.head_dim))
+    mask = sparse_mask_flat(w, L) if w.kind == "sparse" else None
+    return Case(w, L, off, q, k, v, do, softmax_scale(w.head_dim), mask)
 
 
 def custom(lengths_, num_heads, head_dim, sigma=1.0, seed=0, kind="jagged", causal=False,
-           lq=0, name="custom", rope_base=0.0, window=0, block=64) -> Workload:
+           lq=0, name="custom", rope_base=0.0, window=0, block=64, density=0.0) -> Workload:
     """A workload with explicitly given lengths (edge cases, small tests)."""
     L = tuple(int(x) for x in lengths_)
     return Workload(name, len(L), num_heads, head_dim, sigma, kind=kind, causal=causal,
                     lq=lq, seed=seed, law="fixed", fixed_lengths=L, rope_base=rope_base,
-                    window=window, block=block)
+                    window=window, block=block, density=density)
 
 
 def to_torch_bf16(bits: np.ndarray):

@@ -29,10 +29,21 @@ Readings of points the pages leave open:
     attention over offsets refined to every 64 tokens; no lse is produced.
   * A broadcast sequence with no keys yields out = 0, lse = -inf, and adds nothing
     to dQ (convention; the pages do not cover it).
+  * Block-sparse (the pages name block-sparse patterns as a modelling variant and
+    contrast a 256-token minimum tile with the 64-token blocks their models need,
+    "TLX Block Attention", section 1; "Jagged Flash Attention for GEM", the
+    section on generative models): each sequence is cut into 64-token blocks
+    (the last one partial), and a boolean matrix per sequence says which key
+    blocks each query block attends; query i attends key j of its own sequence
+    iff mask[i // 64][j // 64]. No causal rule inside. A query row whose blocks
+    allow no key gets out = 0 and lse = -inf and contributes nothing to the
+    gradients (the same convention as an empty broadcast sequence).
 
 Layouts: packed tensors are [T, H, D] (token-major, no padding) with int32
 offsets [B+1]; jagged lse is [H, T]; broadcast Q/dQ are [Lq, H, D], broadcast
-out/dO are [B, Lq, H, D] and broadcast lse is [B, H, Lq].
+out/dO are [B, Lq, H, D] and broadcast lse is [B, H, Lq]. Block-sparse masks are
+a list with one [n_b, n_b] boolean array per sequence, n_b = ceil(L_b / 64); the
+flat form concatenates them row-major (uint8).
 All array arguments are float64 (bf16 inputs widened exactly).
 """
 from __future__ import annotations
@@ -40,6 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 ROW_BLOCK = 1024
+SPARSE_BLOCK = 64
 
 
 def _row_blocks(n):
@@ -47,27 +59,31 @@ def _row_blocks(n):
         yield r0, min(n, r0 + ROW_BLOCK)
 
 
-def _probs(q_blk, k, scale, causal, r0, window=0):
+def _probs(q_blk, k, scale, causal, r0, window=0, bmask=None):
     """Softmax probabilities P [rows, Lk] and the row max / row sum.
 
     Rows are queries r0..r0+rows-1 of the sequence; with causal, query i keeps
-    keys j <= i only, and with a window W > 0 also only keys j > i - W.
+    keys j <= i only, and with a window W > 0 also only keys j > i - W. With a
+    block mask, query i keeps key j iff bmask[i // 64, j // 64]. A row that keeps
+    no key has P = 0, max -inf and sum 0.
     """
     s = scale * (q_blk @ k.T)
+    i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
+    j = np.arange(k.shape[0])[None, :]
     if causal:
-        i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
-        j = np.arange(k.shape[0])[None, :]
         keep = j <= i
         if window:
             keep &= j > i - window
         s = np.where(keep, s, -np.inf)
+    if bmask is not None:
+        s = np.where(bmask[i // SPARSE_BLOCK, j // SPARSE_BLOCK], s, -np.inf)
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    e = np.exp(s - np.where(np.isfinite(m), m, 0.0)[:, None])
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    return e / np.where(l > 0, l, 1.0)[:, None], m, l
 
 
-def seq_forward(q, k, v, scale, causal=False, window=0):
+def seq_forward(q, k, v, scale, causal=False, window=0, bmask=None):
     """One sequence, one head. q [Lq,D], k/v [Lk,D] -> out [Lq,D], lse [Lq]."""
     Lq, Lk = q.shape[0], k.shape[0]
     out = np.zeros((Lq, v.shape[1]))
@@ -75,13 +91,14 @@ def seq_forward(q, k, v, scale, causal=False, window=0):
     if Lq == 0 or Lk == 0:
         return out, lse
     for r0, r1 in _row_blocks(Lq):
-        p, m, l = _probs(q[r0:r1], k, scale, causal, r0, window)
+        p, m, l = _probs(q[r0:r1], k, scale, causal, r0, window, bmask)
         out[r0:r1] = p @ v
-        lse[r0:r1] = m + np.log(l)
+        with np.errstate(divide="ignore"):
+            lse[r0:r1] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return out, lse
 
 
-def seq_backward(q, k, v, do, scale, causal=False, window=0):
+def seq_backward(q, k, v, do, scale, causal=False, window=0, bmask=None):
     """Gradients of <out, dO> for one sequence and head -> dq, dk, dv."""
     Lq, Lk = q.shape[0], k.shape[0]
     dq = np.zeros_like(q)
@@ -90,7 +107,7 @@ def seq_backward(q, k, v, do, scale, causal=False, window=0):
     if Lq == 0 or Lk == 0:
         return dq, dk, dv
     for r0, r1 in _row_blocks(Lq):
-        p, _, _ = _probs(q[r0:r1], k, scale, causal, r0, window)
+        p, _, _ = _probs(q[r0:r1], k, scale, causal, r0, window, bmask)
         o = p @ v
         d_o = do[r0:r1]
         di = np.sum(d_o * o, axis=1)            # Di = rowsum(dO * O)
@@ -165,6 +182,47 @@ def broadcast_backward(qd, k, v, do, offsets, scale):
     return dq, dk, dv
 
 
+def sparse_masks(offsets, flat):
+    """Per-sequence block masks ([n_b, n_b] bool, n_b = ceil(L_b / 64)) from the
+    flat row-major concatenation."""
+    flat = np.asarray(flat).reshape(-1)
+    masks, pos = [], 0
+    for s, e in _seqs(offsets):
+        n = -(-(e - s) // SPARSE_BLOCK)
+        masks.append(flat[pos:pos + n * n].reshape(n, n).astype(bool))
+        pos += n * n
+    if pos != flat.size:
+        raise ValueError("flat mask size does not match the offsets")
+    return masks
+
+
+def block_sparse_forward(q, k, v, offsets, scale, masks):
+    """Block-sparse self-attention: q/k/v [T,H,D], one block mask per sequence
+    -> out [T,H,D], lse [H,T]."""
+    T, H, D = q.shape
+    out = np.zeros((T, H, v.shape[2]))
+    lse = np.full((H, T), -np.inf)
+    for (s, e), bm in zip(_seqs(offsets), masks):
+        for h in range(H):
+            o, l = seq_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale, bmask=bm)
+            out[s:e, h] = o
+            lse[h, s:e] = l
+    return out, lse
+
+
+def block_sparse_backward(q, k, v, do, offsets, scale, masks):
+    """Block-sparse self-attention gradients -> dq, dk, dv, each [T,H,D]."""
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    H = q.shape[1]
+    for (s, e), bm in zip(_seqs(offsets), masks):
+        for h in range(H):
+            a, b_, c = seq_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale, bmask=bm)
+            dq[s:e, h], dk[s:e, h], dv[s:e, h] = a, b_, c
+    return dq, dk, dv
+
+
 def refine_offsets(offsets, block=64):
     """Offsets split at every `block` tokens inside each sequence.
 
@@ -189,13 +247,23 @@ def block_diag_backward(q, k, v, do, offsets, scale, block=64):
 
 
 # ---------------------------------------------------------------- counters
-def pair_count(lengths, causal=False, lq=0, block=0):
+def pair_count(lengths, causal=False, lq=0, block=0, masks=None):
     """Number of unmasked (query, key) pairs the attention evaluates.
 
     self-attention: sum L^2 (causal: sum L(L+1)/2); broadcast: sum Lq*L;
-    block-diagonal: block * sum L.
+    block-diagonal: block * sum L; block-sparse: the pairs of every allowed
+    (query block, key block), the last block of a sequence counting its own rows.
     """
     L = np.asarray(lengths, dtype=np.int64)
+    if masks is not None:
+        total = 0
+        for n, bm in zip(L, masks):
+            nb = bm.shape[0]
+            rows = np.full(nb, SPARSE_BLOCK, dtype=np.int64)
+            if nb:
+                rows[-1] = n - SPARSE_BLOCK * (nb - 1)
+            total += int(rows @ bm.astype(np.int64) @ rows)
+        return total
     if block:
         return int(block * L.sum())
     if lq:

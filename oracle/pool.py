@@ -91,13 +91,19 @@ def _sub_inputs(w, off, b0, b1):
         do = packed(J.S_DO, w.lq).reshape(b1 - b0, w.lq, w.num_heads, w.head_dim)
     else:
         q, do = packed(J.S_Q), packed(J.S_DO)
+    if w.kind == "sparse":
+        masks = [J.sparse_mask_seq(w, b, int(L[b - b0])).astype(bool) for b in range(b0, b1)]
+        return q, k, v, do, loff, masks
     return q, k, v, do, loff
 
 
-def oracle_sub(w, scale, q, k, v, do, loff):
+def oracle_sub(w, scale, q, k, v, do, loff, masks=None):
     """The oracle on one sub-batch: (out, lse or None, dq, dk, dv), as the oracle's
     whole-workload functions define them."""
-    if w.kind == "broadcast":
+    if w.kind == "sparse":
+        out, lse = A.block_sparse_forward(q, k, v, loff, scale, masks)
+        dq, dk, dv = A.block_sparse_backward(q, k, v, do, loff, scale, masks)
+    elif w.kind == "broadcast":
         out, lse = A.broadcast_forward(q, k, v, loff, scale)
         dq, dk, dv = A.broadcast_backward(q, k, v, do, loff, scale)
     elif w.kind == "block" and w.rope_base:
@@ -142,8 +148,7 @@ def _task(args):
     partial dQ for broadcast-Q)."""
     w, scale, off, b0, b1, rdir, out_rel = args
     t0 = time.perf_counter()
-    q, k, v, do, loff = _sub_inputs(w, off, b0, b1)
-    out, lse, dq, dk, dv = oracle_sub(w, scale, q, k, v, do, loff)
+    out, lse, dq, dk, dv = oracle_sub(w, scale, *_sub_inputs(w, off, b0, b1))
     res = {"b0": b0, "b1": b1, "seconds": time.perf_counter() - t0}
     if rdir is None:
         return res
@@ -188,7 +193,7 @@ def tasks_of(w, off, per_task=None):
     B = len(off) - 1
     L = np.diff(np.asarray(off, dtype=np.int64))
     if per_task is None:
-        per_task = 1 if w.kind == "jagged" else (8 if w.kind == "broadcast" else 16)
+        per_task = 1 if w.kind in ("jagged", "sparse") else (8 if w.kind == "broadcast" else 16)
     ranges = [(b, min(B, b + per_task)) for b in range(0, B, per_task)]
     if per_task == 1:
         ranges.sort(key=lambda r: -int(L[r[0]]))

@@ -8,7 +8,7 @@ from oracle import attention as A
 from tests import test_oracle as T
 
 
-def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0, window=0):
+def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0, window=0, bmask=None):
     s = scale * (q_blk @ k.T)
     if causal:
         i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
@@ -21,12 +21,12 @@ def _mut_probs_causal_off_by_one(q_blk, k, scale, causal, r0, window=0):
     return e / l[:, None], m, l
 
 
-def _mut_probs_no_scale(q_blk, k, scale, causal, r0, window=0):
-    return _orig_probs(q_blk, k, 1.0, causal, r0, window)
+def _mut_probs_no_scale(q_blk, k, scale, causal, r0, window=0, bmask=None):
+    return _orig_probs(q_blk, k, 1.0, causal, r0, window, bmask)
 
 
-def _mut_forward_lse_without_log(q, k, v, scale, causal=False, window=0):
-    out, lse = _orig_seq_forward(q, k, v, scale, causal, window)
+def _mut_forward_lse_without_log(q, k, v, scale, causal=False, window=0, bmask=None):
+    out, lse = _orig_seq_forward(q, k, v, scale, causal, window, bmask)
     # drop the log-sum term: lse = m only
     for r0, r1 in A._row_blocks(q.shape[0]):
         if k.shape[0]:
@@ -36,7 +36,7 @@ def _mut_forward_lse_without_log(q, k, v, scale, causal=False, window=0):
 
 
 def _make_bwd_mutant(kind):
-    def bwd(q, k, v, do, scale, causal=False, window=0):
+    def bwd(q, k, v, do, scale, causal=False, window=0, bmask=None):
         dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
         if q.shape[0] == 0 or k.shape[0] == 0:
             return dq, dk, dv
@@ -151,7 +151,7 @@ def test_rotary_backward_without_inverse_rotation_is_caught(monkeypatch):
 from tests import test_oracle_window as TW  # noqa: E402
 
 
-def _mut_probs_window_off_by_one(q_blk, k, scale, causal, r0, window=0):
+def _mut_probs_window_off_by_one(q_blk, k, scale, causal, r0, window=0, bmask=None):
     s = scale * (q_blk @ k.T)
     if causal:
         i = np.arange(r0, r0 + q_blk.shape[0])[:, None]
@@ -182,3 +182,32 @@ def test_window_work_mistake_is_caught(monkeypatch):
         return orig(*a, **kw)
     monkeypatch.setattr(TW.S, "enumerate_tiles", mutated)
     assert _caught(TW.test_window_tile_work_brute_force, W=100)
+
+
+# ------------------------------------------------------------------ block-sparse
+from tests import test_oracle_sparse as TS  # noqa: E402
+
+
+def _mut_probs_sparse(kind):
+    def probs(q_blk, k, scale, causal, r0, window=0, bmask=None):
+        if bmask is not None:
+            if kind == "transposed":
+                bmask = bmask.T
+            elif kind == "block_off_by_one":
+                # a query takes the block of the next row (i + 1) // 64
+                n = q_blk.shape[0]
+                out = [_orig_probs(q_blk[r:r + 1], k, scale, causal, r0 + r + 1, window, bmask)
+                       if (r0 + r + 1) // 64 < bmask.shape[0] else
+                       _orig_probs(q_blk[r:r + 1], k, scale, causal, r0 + r, window, bmask)
+                       for r in range(n)]
+                return (np.concatenate([o[0] for o in out]), np.concatenate([o[1] for o in out]),
+                        np.concatenate([o[2] for o in out]))
+        return _orig_probs(q_blk, k, scale, causal, r0, window, bmask)
+    return probs
+
+
+@pytest.mark.parametrize("kind", ["transposed", "block_off_by_one"])
+def test_sparse_mask_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(A, "_probs", _mut_probs_sparse(kind))
+    assert _caught(TS.test_sparse_matches_sdpa, seed=0)
+    assert _caught(TS.test_matches_python_loops)
