@@ -89,6 +89,9 @@ typedef enum jfa_status {
 #define JFA_ROTARY       8u  /* rotary embeddings of Q and K (not with BROADCAST_Q) */
 #define JFA_BLOCK_DIAG  16u  /* block-diagonal self-attention with blocks of
                                 jfa_problem.block tokens (32, 64, 128 or 256) */
+#define JFA_BLOCK_SPARSE 32u /* block-sparse self-attention over 64-token blocks
+                                (jfa_problem.block = 64, no other flag): see the
+                                jfa_sparse_* entry points */
 
 /* schedule kinds and dealing orders */
 #define JFA_KIND_FWD 0
@@ -108,7 +111,7 @@ typedef struct jfa_problem {
   int32_t max_len;    /* >= every sequence length (checked by jfa_schedule_count) */
   int32_t lq;         /* BROADCAST_Q: rows of the dense Q (>= 1); otherwise 0 */
   uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY |
-                         JFA_BLOCK_DIAG */
+                         JFA_BLOCK_DIAG, or JFA_BLOCK_SPARSE alone */
   int64_t total_kv;   /* T = offsets[B], tokens in the packed K/V */
   float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
   float rope_base;    /* ROTARY: base of the rotary frequencies, finite, in (1, 1e9];
@@ -116,7 +119,7 @@ typedef struct jfa_problem {
   int32_t window;     /* CAUSAL only: W > 0 restricts query i to keys i - W < j <= i
                          (a causal sliding window); 0 = no window */
   int32_t block;      /* BLOCK_DIAG: tokens per block, 32, 64, 128 or 256; with
-                         BLOCK_DIAG64 alone 0 or 64; otherwise 0 */
+                         BLOCK_DIAG64 alone 0 or 64; BLOCK_SPARSE: 64; otherwise 0 */
 } jfa_problem;
 
 /* Rows of Q per forward tile (kind FWD) or of K/V per backward tile (kind BWD)
@@ -263,6 +266,80 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
                           const void* out, const void* dout, const float* lse,
                           const int32_t* offsets_dev, const int32_t* q_slot_ptr_dev,
                           const int32_t* q_tiles_dev, int32_t q_num_slots,
+                          const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                          int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, uint32_t passes, void* stream);
+
+/* ---- Block-sparse attention (JFA_BLOCK_SPARSE)
+ * The pages name block-sparse patterns as a modelling variant and contrast a
+ * 256-token minimum tile with the 64-token blocks their models need ("TLX Block
+ * Attention", section 1; "Jagged Flash Attention for GEM", the section on
+ * generative models). Here each sequence b of L_b tokens is cut into
+ * n_b = ceil(L_b / 64) blocks of 64 tokens (the last one partial) and an
+ * n_b x n_b byte matrix says which key blocks each query block attends: query i
+ * attends key j of its own sequence iff mask_b[i / 64][j / 64] != 0, with no
+ * causal rule inside. The mask (host memory) holds every sequence's matrix
+ * row-major (row = query block), concatenated in sequence order: sum of n_b^2
+ * bytes. A query row whose blocks attend no key gets out = 0 and lse = -inf, and
+ * adds nothing to the gradients. The problem has flags = JFA_BLOCK_SPARSE only,
+ * block = 64; its tiles are those of jagged self-attention (jfa_schedule_count).
+ *
+ * The kernels walk step lists built on the host from the mask. A unit is (b, t)
+ * for each sequence b and tile index t (128 query rows for kind FWD, 128 keys for
+ * kind BWD: the 64-token blocks 2t and 2t+1), units in order of b, then t.
+ *   seq_base [B + 1]      first unit of sequence b (seq_base[B] = units).
+ *   list_ptr [units + 1]  unit u's entries are entries[list_ptr[u] .. list_ptr[u+1]).
+ *   entries               int32: bits 0..27 the other side's block index (FWD: key
+ *                         block c; BWD: query block r), ascending; bit 28 set when
+ *                         the unit's block 2t pairs with it (FWD: mask[2t][c];
+ *                         BWD: mask[r][2t]), bit 29 likewise for block 2t+1.
+ *                         Blocks paired with neither are left out. */
+typedef struct jfa_sparse_lists_dev {
+  const int32_t* seq_base;  /* device copies of the arrays above, 4-byte aligned */
+  const int32_t* list_ptr;
+  const int32_t* entries;
+} jfa_sparse_lists_dev;
+
+/* Sizes of the step lists of `kind`: *num_units = seq_base[B] (the units) and
+ * *num_entries. Checks the problem (BLOCK_SPARSE), the offsets as
+ * jfa_schedule_count does, and mask_bytes == sum of n_b^2. Host only. */
+jfa_status jfa_sparse_lists_count(const jfa_problem* p, const int32_t* offsets_host,
+                                  const uint8_t* mask_host, int64_t mask_bytes, int32_t kind,
+                                  int64_t* num_units, int64_t* num_entries);
+
+/* Build the step lists of `kind` from the host mask into caller-allocated host
+ * arrays: seq_base [B + 1], list_ptr [num_units + 1], entries [num_entries]
+ * (entries_capacity >= num_entries). Host only; no HIP call. */
+jfa_status jfa_sparse_lists(const jfa_problem* p, const int32_t* offsets_host,
+                            const uint8_t* mask_host, int64_t mask_bytes, int32_t kind,
+                            int32_t* seq_base, int32_t* list_ptr, int32_t* entries,
+                            int64_t entries_capacity);
+
+/* jfa_schedule for a BLOCK_SPARSE problem: the same tiles, orders and outputs, a
+ * tile's work being 64 times the length of its unit's list (list_ptr_host from
+ * jfa_sparse_lists of the same kind). Host only. */
+jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host,
+                               const int32_t* list_ptr_host, int32_t kind, int32_t order,
+                               int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
+                               int64_t capacity);
+
+/* Block-sparse forward: as jfa_fwd with the FWD step lists (device) and no
+ * workspace; a tile visits only the key blocks its list names. Preconditions as
+ * for jfa_fwd, and the lists are those of the offsets and mask the schedule was
+ * built from (not checked on the device). */
+jfa_status jfa_fwd_sparse(const jfa_problem* p, const void* q, const void* k, const void* v,
+                          const int32_t* offsets_dev, const jfa_sparse_lists_dev* lists,
+                          const int32_t* slot_ptr_dev, const int32_t* tiles_dev,
+                          int32_t num_slots, void* out, float* lse, void* stream);
+
+/* Block-sparse backward: as jfa_bwd_passes with the FWD step lists (q_lists, for
+ * the dQ pass over the FWD schedule) and the BWD step lists (kv_lists, for the
+ * dK/dV pass over the BWD schedule); workspace of jfa_bwd_workspace_bytes(p). */
+jfa_status jfa_bwd_sparse(const jfa_problem* p, const void* q, const void* k, const void* v,
+                          const void* out, const void* dout, const float* lse,
+                          const int32_t* offsets_dev, const jfa_sparse_lists_dev* q_lists,
+                          const int32_t* q_slot_ptr_dev, const int32_t* q_tiles_dev,
+                          int32_t q_num_slots, const jfa_sparse_lists_dev* kv_lists,
                           const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
                           int32_t kv_num_slots, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, uint32_t passes, void* stream);

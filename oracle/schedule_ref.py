@@ -27,6 +27,10 @@ Readings of what the page leaves open:
     of one (sequence, head) form one item whose work is their sum (the middle
     tile of an odd count stands alone); an item's tiles go to one slot, in that
     order. Without causal masking every tile is an item.
+  * Block-sparse attention (64-token blocks, one block mask per sequence): a
+    tile covers two blocks (128 query rows, or 128 keys); its step list names the
+    other side's blocks that pair with either of them, ascending, and its work is
+    64 times the list's length (the keys, or query rows, it visits).
 Output: slot_ptr [S+1] and tiles [N,4] = (b, h, t, work), grouped by slot, in the
 order each slot received them.
 """
@@ -35,6 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 KIND_FWD, KIND_BWD = 0, 1
+SPARSE_BLOCK, SPARSE_BIT = 64, 28
 ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 
 
@@ -42,14 +47,54 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0, window=0):
+def sparse_lists(lengths, masks, kind, tile_rows=128):
+    """Block-sparse step lists: (seq_base, list_ptr, entries) as int32 arrays.
+
+    One list per (sequence b, tile t), in that order; tile t covers the blocks
+    2t and 2t+1 (query blocks for KIND_FWD, key blocks for KIND_BWD). Its entries
+    are the other side's blocks c, ascending, that pair with either: the block
+    index plus bit 28 when block 2t pairs with c (FWD: masks[b][2t, c]; BWD:
+    masks[b][c, 2t]) and bit 29 for block 2t+1. seq_base[b] is the first list of
+    sequence b.
+    """
+    seq_base, list_ptr, entries = [], [0], []
+    for L, m in zip((int(x) for x in lengths), masks):
+        seq_base.append(len(list_ptr) - 1)
+        n = m.shape[0]
+        for t in range(ceil_div(L, tile_rows)):
+            for c in range(n):
+                code = c
+                for i, blk in enumerate((2 * t, 2 * t + 1)):
+                    if blk < n and (m[blk, c] if kind == KIND_FWD else m[c, blk]):
+                        code |= 1 << (SPARSE_BIT + i)
+                if code != c:
+                    entries.append(code)
+            list_ptr.append(len(entries))
+    seq_base.append(len(list_ptr) - 1)
+    return (np.asarray(seq_base, dtype=np.int32), np.asarray(list_ptr, dtype=np.int32),
+            np.asarray(entries, dtype=np.int64).astype(np.int32))
+
+
+def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0, window=0,
+                    sparse_list_ptr=None):
     """All tiles in generation order: list of (b, h, t, work).
 
     With a causal window W the work counts only what the window leaves: a query
     tile visits the keys from max(0, t*BM - W + 1) to its last row, a key tile is
-    attended by the queries from n*BN to min(L, (n+1)*BN - 1 + W).
+    attended by the queries from n*BN to min(L, (n+1)*BN - 1 + W). With block-sparse
+    step lists (list_ptr of sparse_lists) a tile's work is 64 times its list's length.
     """
     out = []
+    if sparse_list_ptr is not None:
+        u = 0
+        for b, L in enumerate(int(x) for x in lengths):
+            n = ceil_div(L, tile_rows)
+            for h in range(num_heads):
+                for t in range(n):
+                    out.append((b, h, t, SPARSE_BLOCK * int(sparse_list_ptr[u + t + 1]
+                                                            - sparse_list_ptr[u + t])))
+            u += n
+        return out
     for b, L in enumerate(int(x) for x in lengths):
         for h in range(num_heads):
             if kind == KIND_FWD:
@@ -81,8 +126,9 @@ def _zigzag_rank(j, n):
 
 
 def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0,
-             groups=8, window=0):
-    tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq, window)
+             groups=8, window=0, sparse_list_ptr=None):
+    tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq, window,
+                            sparse_list_ptr)
     if order == ORDER_XCD_ZIGZAG:
         # Units are (sequence, head) pairs with the summed work of their tiles;
         # they are sorted by that work and dealt zigzag over the groups, then each

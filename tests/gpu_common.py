@@ -47,6 +47,8 @@ def flags_of(w: J.Workload) -> int:
         f |= jfa.BLOCK_DIAG64 if w.block == 64 else jfa.BLOCK_DIAG
     if w.rope_base:
         f |= jfa.ROTARY
+    if w.kind == "sparse":
+        f |= jfa.BLOCK_SPARSE
     return f
 
 
@@ -70,7 +72,8 @@ class GpuRun:
         self.plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, self.flags,
                              w.lq, order=order, num_slots=num_slots, device=dev,
                              rope_base=w.rope_base, window=w.window,
-                             block=w.block if w.kind == "block" and w.block != 64 else 0)
+                             block=w.block if w.kind == "block" and w.block != 64 else 0,
+                             block_mask=case.mask)
         self.q = to_dev(case.q, dev)
         self.k = to_dev(case.k, dev)
         self.v = to_dev(case.v, dev)

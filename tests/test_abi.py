@@ -50,7 +50,7 @@ OFF = np.array([0, 10, 15], dtype=np.int32)
     (dict(num_heads=0), jfa.ERR_INVALID_ARG),
     (dict(scale=0.0), jfa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), jfa.ERR_INVALID_ARG),
-    (dict(flags=32), jfa.ERR_INVALID_ARG),
+    (dict(flags=64), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.BLOCK_DIAG, block=48, total_kv=96, max_len=96), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BLOCK_DIAG64, block=128, total_kv=128, max_len=128), jfa.ERR_INVALID_ARG),
     (dict(block=64), jfa.ERR_INVALID_ARG),

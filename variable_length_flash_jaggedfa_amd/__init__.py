@@ -6,7 +6,8 @@ device memory and the stream). If libjfa.so has not been built, every entry
 point raises: there is no fallback path.
 
 Low-level names mirror the C ABI (tile_rows, default_slots, schedule_count,
-schedule, bwd_workspace_bytes, fwd, bwd). `Plan` bundles the host schedule,
+schedule, bwd_workspace_bytes, fwd, bwd, and the block-sparse sparse_lists,
+schedule_sparse, fwd_sparse, bwd_sparse). `Plan` bundles the host schedule,
 its device copy and the workspace for one problem.
 """
 from __future__ import annotations
@@ -22,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libjfa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY, BLOCK_DIAG = 1, 2, 4, 8, 16
+CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY, BLOCK_DIAG, BLOCK_SPARSE = 1, 2, 4, 8, 16, 32
 KIND_FWD, KIND_BWD = 0, 1
 ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
 PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
@@ -41,6 +42,11 @@ class Problem(ctypes.Structure):
                 ("total_kv", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("window", ctypes.c_int32),
                 ("block", ctypes.c_int32)]
+
+
+class SparseListsDev(ctypes.Structure):
+    _fields_ = [("seq_base", ctypes.c_void_p), ("list_ptr", ctypes.c_void_p),
+                ("entries", ctypes.c_void_p)]
 
 
 _lib = None
@@ -79,6 +85,19 @@ def lib():
         L.jfa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
                                       vp, vp, vp, vp]
         L.jfa_bwd_noalloc.restype = i32
+        SL = ctypes.POINTER(SparseListsDev)
+        L.jfa_sparse_lists_count.argtypes = [P, vp, vp, i64, i32, ctypes.POINTER(i64),
+                                             ctypes.POINTER(i64)]
+        L.jfa_sparse_lists_count.restype = i32
+        L.jfa_sparse_lists.argtypes = [P, vp, vp, i64, i32, vp, vp, vp, i64]
+        L.jfa_sparse_lists.restype = i32
+        L.jfa_schedule_sparse.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, i64]
+        L.jfa_schedule_sparse.restype = i32
+        L.jfa_fwd_sparse.argtypes = [P, vp, vp, vp, vp, SL, vp, vp, i32, vp, vp, vp]
+        L.jfa_fwd_sparse.restype = i32
+        L.jfa_bwd_sparse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, SL, vp, vp, i32, SL, vp, vp,
+                                     i32, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp]
+        L.jfa_bwd_sparse.restype = i32
         L.jfa_probe_copy.argtypes = [vp, vp, ctypes.c_uint64, i32, vp]
         L.jfa_probe_copy.restype = i32
         L.jfa_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
@@ -134,6 +153,64 @@ def schedule(p: Problem, offsets_host, kind: int, order: int, num_slots: int):
     _check(lib().jfa_schedule(ctypes.byref(p), off.ctypes.data, kind, order, num_slots,
                               slot_ptr.ctypes.data, tiles.ctypes.data, n))
     return slot_ptr, tiles[:n]
+
+
+def _host_u8(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint8).reshape(-1)
+
+
+def sparse_lists(p: Problem, offsets_host, mask_host, kind: int):
+    """Block-sparse step lists of `kind` -> (seq_base [B+1], list_ptr [units+1],
+    entries), int32 host arrays."""
+    off, m = _host_i32(offsets_host), _host_u8(mask_host)
+    nu, ne = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().jfa_sparse_lists_count(ctypes.byref(p), off.ctypes.data, m.ctypes.data, m.size,
+                                        kind, ctypes.byref(nu), ctypes.byref(ne)))
+    seq_base = np.zeros(p.num_seqs + 1, dtype=np.int32)
+    list_ptr = np.zeros(nu.value + 1, dtype=np.int32)
+    entries = np.zeros(max(ne.value, 1), dtype=np.int32)
+    _check(lib().jfa_sparse_lists(ctypes.byref(p), off.ctypes.data, m.ctypes.data, m.size, kind,
+                                  seq_base.ctypes.data, list_ptr.ctypes.data,
+                                  entries.ctypes.data, ne.value))
+    return seq_base, list_ptr, entries[:ne.value]
+
+
+def schedule_sparse(p: Problem, offsets_host, list_ptr_host, kind: int, order: int,
+                    num_slots: int):
+    """Block-sparse host tile schedule -> (slot_ptr int32 [S+1], tiles int32 [N,4])."""
+    off, lp = _host_i32(offsets_host), _host_i32(list_ptr_host)
+    n = schedule_count(p, off, kind)
+    slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+    tiles = np.zeros((max(n, 1), 4), dtype=np.int32)
+    _check(lib().jfa_schedule_sparse(ctypes.byref(p), off.ctypes.data, lp.ctypes.data, kind,
+                                     order, num_slots, slot_ptr.ctypes.data, tiles.ctypes.data,
+                                     n))
+    return slot_ptr, tiles[:n]
+
+
+def _lists(dev):
+    """(seq_base, list_ptr, entries) device tensors -> jfa_sparse_lists_dev."""
+    return SparseListsDev(*(_ptr(t) for t in dev))
+
+
+def fwd_sparse(p: Problem, q, k, v, offsets_dev, lists_dev, slot_ptr_dev, tiles_dev, num_slots,
+               out, lse, stream=None):
+    sl = _lists(lists_dev)
+    _check(lib().jfa_fwd_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets_dev),
+                                ctypes.byref(sl), _ptr(slot_ptr_dev), _ptr(tiles_dev),
+                                int(num_slots), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def bwd_sparse(p: Problem, q, k, v, out, dout, lse, offsets_dev, q_lists_dev, q_slot_ptr_dev,
+               q_tiles_dev, q_num_slots, kv_lists_dev, kv_slot_ptr_dev, kv_tiles_dev,
+               kv_num_slots, dq, dk, dv, workspace, passes=PASS_ALL, stream=None):
+    ql, kl = _lists(q_lists_dev), _lists(kv_lists_dev)
+    _check(lib().jfa_bwd_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(dout), _ptr(lse), _ptr(offsets_dev), ctypes.byref(ql),
+                                _ptr(q_slot_ptr_dev), _ptr(q_tiles_dev), int(q_num_slots),
+                                ctypes.byref(kl), _ptr(kv_slot_ptr_dev), _ptr(kv_tiles_dev),
+                                int(kv_num_slots), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                _ws_bytes(workspace), int(passes), _stream(stream)))
 
 
 def bwd_workspace_bytes(p: Problem) -> int:
@@ -223,6 +300,8 @@ class Schedule:
     num_slots: int
     slot_ptr_dev: object = None
     tiles_dev: object = None
+    lists: tuple = None       # BLOCK_SPARSE: host (seq_base, list_ptr, entries)
+    lists_dev: tuple = None   # and their device copies
 
 
 class Plan:
@@ -230,7 +309,9 @@ class Plan:
 
     offsets_host: int32 [B+1] (numpy); H, D; flags; lq for broadcast-Q; rope_base
     for ROTARY; window (CAUSAL only) for a causal sliding window of that many keys;
-    block (BLOCK_DIAG) for the tokens per diagonal block.
+    block (BLOCK_DIAG) for the tokens per diagonal block; block_mask (BLOCK_SPARSE)
+    for the flat uint8 block masks of every sequence (row-major n_b x n_b each,
+    n_b = ceil(L_b / 64)), from which the step lists of both kinds are built.
     Builds the FWD and BWD schedules on the host (folded zigzag by default: the
     work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired so
     that they run side by side), copies them
@@ -239,11 +320,14 @@ class Plan:
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
                  order=ORDER_FOLDED_ZIGZAG, num_slots=None, device="cuda", rope_base=0.0,
-                 window=0, block=0):
+                 window=0, block=0, block_mask=None):
         import torch
         off = _host_i32(offsets_host)
         L = np.diff(off.astype(np.int64))
         self.offsets_host = off
+        self.sparse = bool(flags & BLOCK_SPARSE)
+        if self.sparse:
+            block = 64
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
                          int(off[-1]), scale, flags, lq, rope_base, window, block)
         self.device = torch.device(device)
@@ -258,8 +342,18 @@ class Plan:
         else:
             for kind in (KIND_FWD, KIND_BWD):
                 S = num_slots or default_slots(kind, head_dim, flags, self.device.index or 0)
-                sp, tl = schedule(self.p, off, kind, order, S)
+                lists = None
+                if self.sparse:
+                    lists = sparse_lists(self.p, off, block_mask, kind)
+                    sp, tl = schedule_sparse(self.p, off, lists[1], kind, order, S)
+                else:
+                    sp, tl = schedule(self.p, off, kind, order, S)
                 sch = Schedule(sp, tl, S)
+                if lists is not None:
+                    sch.lists = lists
+                    # an empty entries array still needs a valid device pointer
+                    sch.lists_dev = tuple(torch.from_numpy(a if a.size else np.zeros(1, np.int32))
+                                          .to(self.device) for a in lists)
                 sch.slot_ptr_dev = torch.from_numpy(sp).to(self.device)
                 sch.tiles_dev = torch.from_numpy(np.ascontiguousarray(tl)).to(self.device) \
                     if len(tl) else torch.zeros((1, 4), dtype=torch.int32, device=self.device)
@@ -294,6 +388,10 @@ class Plan:
         if not self.block and lse is None:
             lse = torch.empty(self._lse_shape(), dtype=torch.float32, device=self.device)
         s = self.sched.get(KIND_FWD)
+        if self.sparse:
+            fwd_sparse(self.p, q, k, v, self.offsets_dev, s.lists_dev, s.slot_ptr_dev,
+                       s.tiles_dev, s.num_slots, out, lse, stream)
+            return out, lse
         fwd(self.p, q, k, v, self.offsets_dev, s.slot_ptr_dev if s else None,
             s.tiles_dev if s else None, s.num_slots if s else 0, out,
             None if self.block else lse, self.fwd_workspace, stream)
@@ -308,6 +406,12 @@ class Plan:
         dk = dk if dk is not None else torch.empty_like(k)
         dv = dv if dv is not None else torch.empty_like(v)
         sq, skv = self.sched.get(KIND_FWD), self.sched.get(KIND_BWD)
+        if self.sparse:
+            bwd_sparse(self.p, q, k, v, out, dout, lse, self.offsets_dev, sq.lists_dev,
+                       sq.slot_ptr_dev, sq.tiles_dev, sq.num_slots, skv.lists_dev,
+                       skv.slot_ptr_dev, skv.tiles_dev, skv.num_slots, dq, dk, dv,
+                       self.workspace, passes, stream)
+            return dq, dk, dv
         args = (self.p, q, k, v, out, dout, None if self.block else lse, self.offsets_dev,
                 sq.slot_ptr_dev if sq else None, sq.tiles_dev if sq else None,
                 sq.num_slots if sq else 0, skv.slot_ptr_dev if skv else None,

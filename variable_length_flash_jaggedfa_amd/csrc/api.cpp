@@ -182,11 +182,23 @@ extern "C" jfa_status jfa_default_slots(int32_t kind, int32_t head_dim, uint32_t
   return JFA_OK;
 }
 
-extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
-                              const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
-                              const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  set_error("");
+namespace {
+
+// device step lists of a BLOCK_SPARSE problem: present exactly when the flag is
+jfa_status check_lists(const jfa_problem* p, const jfa_sparse_lists_dev* sp, const char* which) {
+  const bool sparse = p->flags & JFA_BLOCK_SPARSE;
+  if (!sparse && sp) return fail(JFA_ERR_INVALID_ARG, std::string(which) + " given without BLOCK_SPARSE");
+  if (!sparse) return JFA_OK;
+  if (!sp) return fail(JFA_ERR_INVALID_ARG, std::string("BLOCK_SPARSE needs ") + which);
+  if (jfa_status s = need(sp->seq_base, "seq_base", 4)) return s;
+  if (jfa_status s = need(sp->list_ptr, "list_ptr", 4)) return s;
+  return need(sp->entries, "entries", 4);
+}
+
+jfa_status fwd_impl(const jfa_problem* p, const void* q, const void* k, const void* v,
+                    const int32_t* offsets_dev, const jfa_sparse_lists_dev* sp,
+                    const int32_t* slot_ptr_dev, const int32_t* tiles_dev, int32_t num_slots,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (jfa_status s = check_problem(p)) return s;
   const bool blk = unit_blocks(p);
   if (p->num_seqs == 0 || (q_rows(p) == 0 && p->total_kv == 0)) return JFA_OK;  // nothing to do
@@ -198,10 +210,19 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
     if (jfa_status s = need(k, "k")) return s;
     if (jfa_status s = need(v, "v")) return s;
   }
+  if (jfa_status s = check_lists(p, sp, "forward step lists")) return s;
   log_call("fwd", p, num_slots, 0, 0);
-  FwdLaunch a{q, k, v, offsets_dev, slot_ptr_dev, tiles_dev, num_slots, out, lse,
-              p->num_seqs, p->num_heads, p->head_dim, p->lq, p->total_kv, p->scale, p->flags,
-              p->rope_base, p->window, block_size(p), stream};
+  FwdLaunch a{};
+  a.q = q; a.k = k; a.v = v;
+  a.offsets = offsets_dev; a.slot_ptr = slot_ptr_dev; a.tiles = tiles_dev; a.num_slots = num_slots;
+  a.out = out; a.lse = lse;
+  a.num_seqs = p->num_seqs; a.num_heads = p->num_heads; a.head_dim = p->head_dim; a.lq = p->lq;
+  a.total_kv = p->total_kv; a.scale = p->scale; a.flags = p->flags; a.rope_base = p->rope_base;
+  a.window = p->window; a.block = block_size(p);
+  if (sp) {
+    a.sp_base = sp->seq_base; a.sp_ptr = sp->list_ptr; a.sp_ent = sp->entries;
+  }
+  a.stream = stream;
   if (blk) {
     if (lse) return fail(JFA_ERR_INVALID_ARG, "lse must be NULL for blocks of 32 or 64 tokens (no lse is stored)");
     if (p->total_kv == 0) return JFA_OK;
@@ -229,15 +250,37 @@ extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k
   return launch_fwd(a);
 }
 
-extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k,
-                                     const void* v, const void* out, const void* dout,
-                                     const float* lse, const int32_t* offsets_dev,
-                                     const int32_t* q_slot_ptr_dev, const int32_t* q_tiles_dev,
-                                     int32_t q_num_slots, const int32_t* kv_slot_ptr_dev,
-                                     const int32_t* kv_tiles_dev, int32_t kv_num_slots, void* dq,
-                                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                     uint32_t passes, void* stream) {
+}  // namespace
+
+extern "C" jfa_status jfa_fwd(const jfa_problem* p, const void* q, const void* k, const void* v,
+                              const int32_t* offsets_dev, const int32_t* slot_ptr_dev,
+                              const int32_t* tiles_dev, int32_t num_slots, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   set_error("");
+  return fwd_impl(p, q, k, v, offsets_dev, nullptr, slot_ptr_dev, tiles_dev, num_slots, out, lse,
+                  workspace, workspace_bytes, stream);
+}
+
+extern "C" jfa_status jfa_fwd_sparse(const jfa_problem* p, const void* q, const void* k,
+                                     const void* v, const int32_t* offsets_dev,
+                                     const jfa_sparse_lists_dev* lists, const int32_t* slot_ptr_dev,
+                                     const int32_t* tiles_dev, int32_t num_slots, void* out,
+                                     float* lse, void* stream) {
+  set_error("");
+  if (!lists) return fail(JFA_ERR_INVALID_ARG, "lists is NULL");
+  return fwd_impl(p, q, k, v, offsets_dev, lists, slot_ptr_dev, tiles_dev, num_slots, out, lse,
+                  nullptr, 0, stream);
+}
+
+namespace {
+
+jfa_status bwd_impl(const jfa_problem* p, const void* q, const void* k, const void* v,
+                    const void* out, const void* dout, const float* lse, const int32_t* offsets_dev,
+                    const jfa_sparse_lists_dev* q_sp, const int32_t* q_slot_ptr_dev,
+                    const int32_t* q_tiles_dev, int32_t q_num_slots,
+                    const jfa_sparse_lists_dev* kv_sp, const int32_t* kv_slot_ptr_dev,
+                    const int32_t* kv_tiles_dev, int32_t kv_num_slots, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, uint32_t passes, void* stream) {
   if (jfa_status s = check_problem(p)) return s;
   if (passes == 0 || (passes & ~JFA_PASS_ALL))
     return fail(JFA_ERR_INVALID_ARG, "passes must be a non-zero mask of JFA_PASS_DQ | JFA_PASS_DKDV");
@@ -259,8 +302,16 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
     if (jfa_status s = need(dk, "dk")) return s;
     if (jfa_status s = need(dv, "dv")) return s;
   }
+  if (jfa_status s = check_lists(p, q_sp, "query-tile step lists")) return s;
+  if (jfa_status s = check_lists(p, kv_sp, "key-tile step lists")) return s;
   log_call("bwd", p, q_num_slots, kv_num_slots, passes);
   BwdLaunch a{};
+  if (q_sp) {
+    a.q_sp_base = q_sp->seq_base; a.q_sp_ptr = q_sp->list_ptr; a.q_sp_ent = q_sp->entries;
+  }
+  if (kv_sp) {
+    a.kv_sp_base = kv_sp->seq_base; a.kv_sp_ptr = kv_sp->list_ptr; a.kv_sp_ent = kv_sp->entries;
+  }
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
   a.offsets = offsets_dev;
   a.q_slot_ptr = q_slot_ptr_dev; a.q_tiles = q_tiles_dev; a.q_num_slots = q_num_slots;
@@ -331,6 +382,39 @@ extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const 
     a.rope = &tab;
   }
   return launch_bwd(a);
+}
+
+}  // namespace
+
+extern "C" jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k,
+                                     const void* v, const void* out, const void* dout,
+                                     const float* lse, const int32_t* offsets_dev,
+                                     const int32_t* q_slot_ptr_dev, const int32_t* q_tiles_dev,
+                                     int32_t q_num_slots, const int32_t* kv_slot_ptr_dev,
+                                     const int32_t* kv_tiles_dev, int32_t kv_num_slots, void* dq,
+                                     void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     uint32_t passes, void* stream) {
+  set_error("");
+  return bwd_impl(p, q, k, v, out, dout, lse, offsets_dev, nullptr, q_slot_ptr_dev, q_tiles_dev,
+                  q_num_slots, nullptr, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv,
+                  workspace, workspace_bytes, passes, stream);
+}
+
+extern "C" jfa_status jfa_bwd_sparse(const jfa_problem* p, const void* q, const void* k,
+                                     const void* v, const void* out, const void* dout,
+                                     const float* lse, const int32_t* offsets_dev,
+                                     const jfa_sparse_lists_dev* q_lists,
+                                     const int32_t* q_slot_ptr_dev, const int32_t* q_tiles_dev,
+                                     int32_t q_num_slots, const jfa_sparse_lists_dev* kv_lists,
+                                     const int32_t* kv_slot_ptr_dev, const int32_t* kv_tiles_dev,
+                                     int32_t kv_num_slots, void* dq, void* dk, void* dv,
+                                     void* workspace, size_t workspace_bytes, uint32_t passes,
+                                     void* stream) {
+  set_error("");
+  if (!q_lists || !kv_lists) return fail(JFA_ERR_INVALID_ARG, "q_lists or kv_lists is NULL");
+  return bwd_impl(p, q, k, v, out, dout, lse, offsets_dev, q_lists, q_slot_ptr_dev, q_tiles_dev,
+                  q_num_slots, kv_lists, kv_slot_ptr_dev, kv_tiles_dev, kv_num_slots, dq, dk, dv,
+                  workspace, workspace_bytes, passes, stream);
 }
 
 extern "C" jfa_status jfa_bwd(const jfa_problem* p, const void* q, const void* k, const void* v,

@@ -72,6 +72,29 @@ struct DqParams {
   float c, scale;
   int32_t window;             // causal sliding window (WIN kernels)
   jfa::RopeTab rope;          // rotary kernels only
+  const int32_t* sp_base; const int32_t* sp_ptr; const int32_t* sp_ent;  // SPARSE kernels
+};
+
+// Keys of a dQ-pass stream. Dense: step st covers keys [st*BN, st*BN + BN) and
+// the masks count n_keys keys. Block-sparse: step st lies in the key block that
+// entry st / SPB of the tile's list names, and a wave whose query block (entry
+// bit `bit`) does not attend it masks every key of the step.
+template <int BN>
+struct StreamKeys {
+  const int32_t* ent;  // SPARSE: the tile's entries
+  int n_keys;          // keys the masks count (dense), sequence length (sparse)
+  int bit;             // SPARSE: kSpBit + the wave's query block in the tile
+  template <bool SPARSE>
+  __device__ __forceinline__ int key(int st) const {
+    if (!SPARSE) return st * BN;
+    constexpr int SPB = jfa::kSpBlock / BN;
+    return (sload(ent + st / SPB) & jfa::kSpIdx) * jfa::kSpBlock + (st % SPB) * BN;
+  }
+  template <bool SPARSE>
+  __device__ __forceinline__ int count(int st) const {
+    if (!SPARSE) return n_keys;
+    return (sload(ent + st / (jfa::kSpBlock / BN)) >> bit) & 1 ? n_keys : 0;
+  }
 };
 
 // S^T = K Q^T and dP^T - Di = V dO^T - Di for one step of BN keys (lane = query
@@ -182,34 +205,37 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
 template <int D, int NW>
 __device__ __forceinline__ void dq_load_stage(uint16_t* lds, const uint16_t* kbase,
                                               const uint16_t* vbase, int64_t rstride, int L, int st,
-                                              int w, int lane) {
+                                              int key, int w, int lane) {
   using C = DqCfg<D, NW>;
   uint16_t* buf = lds + (st % C::NS) * C::STAGE;
-  const int64_t r0 = int64_t(st) * C::BN * rstride;
+  const int64_t r0 = int64_t(key) * rstride;
   const int rowbytes = int(rstride * 2);
-  tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - st * C::BN), rowbytes,
-                             w, lane);
-  tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - st * C::BN),
+  tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - key), rowbytes, w,
+                             lane);
+  tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - key),
                              rowbytes, w, lane);
 }
 
 // The first NS - 2 stages of a key stream, issued ahead of dq_stream<..., true>
 // so that their latency overlaps the caller's own loads (the query rows).
-template <int D, int NW>
+template <int D, int NW, bool SPARSE = false>
 __device__ __forceinline__ void dq_stream_issue(uint16_t* lds, const uint16_t* kbase,
                                                 const uint16_t* vbase, int64_t rstride, int L,
-                                                int n_keys, int w, int lane) {
+                                                int n_steps, const StreamKeys<DqCfg<D, NW>::BN>& ks,
+                                                int w, int lane) {
   using C = DqCfg<D, NW>;
-  const int n_steps = ceil_div(n_keys, C::BN);
 #pragma unroll
   for (int st = 0; st < C::NS - 2; ++st)
-    if (st < n_steps) dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
+    if (st < n_steps)
+      dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, ks.template key<SPARSE>(st), w, lane);
 }
 
-template <int D, bool CAUSAL, bool WIN = false, int NW = DqCfg<D>::NW, bool PRE = false>
+template <int D, bool CAUSAL, bool WIN = false, int NW = DqCfg<D>::NW, bool PRE = false,
+          bool SPARSE = false>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
-                                          int64_t rstride, int L, int n_keys, int n_lo, int n_free,
-                                          int n_own, int win,
+                                          int64_t rstride, int L, int n_steps,
+                                          const StreamKeys<DqCfg<D, NW>::BN>& ks, int n_lo,
+                                          int n_free, int n_own, int win,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
@@ -218,10 +244,11 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
   using C = DqCfg<D, NW>;
   static_assert(C::NS == 4, "the ring below assumes four stages");
   const int g = lane >> 5;
-  const int n_steps = ceil_div(n_keys, C::BN);
   const uint32_t lds0 = lds_addr(lds);
+  auto key_of = [&](int st) { return ks.template key<SPARSE>(st); };
+  auto count_of = [&](int st) { return ks.template count<SPARSE>(st); };
   auto load_stage = [&](int st) {
-    dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
+    dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, key_of(st), w, lane);
   };
   auto ks_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
   auto arrive = [&](int st) {
@@ -229,7 +256,7 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     else wait_vmem();
     __syncthreads();
   };
-  if (!PRE) dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, n_keys, w, lane);
+  if (!PRE) dq_stream_issue<D, NW, SPARSE>(lds, kbase, vbase, rstride, L, n_steps, ks, w, lane);
   if (n_steps > 0) {
     f32x16 s[C::KB], dp[C::KB];
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
@@ -240,11 +267,11 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
     dq_scores<D>(ks_of(0), lo, qf, dof, ndi, s, dp);
     if (n_lo > 0 || n_free == 0)
-      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
-                                              acc, win);
+      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, c, g, key_of(0), count_of(0), qpos,
+                                              pds, 0, lo, pdv, acc, win);
     else
-      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
-                                               acc, win);
+      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, ks.n_keys, qpos, pds, 0, lo,
+                                               pdv, acc, win);
     auto step = [&](int kt, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
@@ -257,8 +284,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       __builtin_amdgcn_s_setprio(1);
       dq_scores<D>(ks, lo, qf, dof, ndi, s, dp);
       __builtin_amdgcn_s_setprio(0);
-      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, c, g, kt * C::BN, n_keys, qpos, pds,
-                                             ks_of(kt - 1), lo, pdv, acc, win);
+      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, c, g, key_of(kt), count_of(kt), qpos,
+                                             pds, ks_of(kt - 1), lo, pdv, acc, win);
     };
     int kt = 1;
     if (WIN)
@@ -308,7 +335,9 @@ __device__ __forceinline__ float load_row(const uint16_t* qrow, const uint16_t* 
   return pair_sum(di);  // Di = rowsum(dO * out)
 }
 
-template <int D, bool CAUSAL, bool ROPE, bool WIN>
+// SPARSE: the tile streams the key blocks of its step list (block-sparse
+// attention), every step masked as in the forward.
+template <int D, bool CAUSAL, bool ROPE, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dq_kernel(DqParams P) {
   using C = DqCfg<D>;
@@ -333,10 +362,18 @@ dq_kernel(DqParams P) {
     // holding key q_first - W + 1 (as in the forward), and counted from there
     const int ks0 = WIN ? max(0, q_first - P.window + 1) / C::BN * C::BN : 0;
     const int n_keys = (CAUSAL ? min(L, q_first + q_rows) : L) - ks0;
-    const int n_steps = ceil_div(n_keys, C::BN);
+    int e_first = 0, n_ent = 0;
+    if (SPARSE) {
+      const int u = sload(P.sp_base + b) + t;
+      e_first = sload(P.sp_ptr + u);
+      n_ent = sload(P.sp_ptr + u + 1) - e_first;
+    }
+    const int n_steps = SPARSE ? n_ent * (jfa::kSpBlock / C::BN) : ceil_div(n_keys, C::BN);
     const int lo_edge = WIN ? q_first + C::BM - P.window - ks0 : 0;
     const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
-    const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
+    const int n_free =
+        SPARSE ? 0 : max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
+    const StreamKeys<C::BN> ks{SPARSE ? P.sp_ent + e_first : nullptr, n_keys, jfa::kSpBit + w / 2};
     const int qpos = q_first + w * 32 + (lane & 31);
     const bool ok = qpos < L;
     // steps this wave computes: all, or one when the tile has no row for it
@@ -347,7 +384,7 @@ dq_kernel(DqParams P) {
     const uint16_t* kbase = P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
     // the first key stages are in flight while the query rows load
-    dq_stream_issue<D, C::NW>(lds, kbase, vbase, rstride, L - ks0, n_keys, w, lane);
+    dq_stream_issue<D, C::NW, SPARSE>(lds, kbase, vbase, rstride, L - ks0, n_steps, ks, w, lane);
     u32x4 qf[C::DS], dof[C::DS];
     const float di = load_row<D>(P.q + eoff, P.o + eoff, P.dout + eoff, ok, g, qf, dof);
     const int64_t vidx = int64_t(h) * P.total_kv + row;
@@ -360,9 +397,9 @@ dq_kernel(DqParams P) {
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
-    dq_stream<D, CAUSAL, WIN, C::NW, true>(lds, kbase, vbase, rstride, L - ks0,
-                              n_keys, n_lo, n_free, n_own, P.window, qf, dof, acc, lse2, di, P.c, w,
-                              lane, qpos - ks0, lo);
+    dq_stream<D, CAUSAL, WIN, C::NW, true, SPARSE>(lds, kbase, vbase, rstride, L - ks0, n_steps,
+                                                   ks, n_lo, n_free, n_own, P.window, qf, dof, acc,
+                                                   lse2, di, P.c, w, lane, qpos - ks0, lo);
     // dq_stream ended with a barrier: the ring is free to stage the output rows
     if (ROPE) rope_back_rows<D>(acc, qpos, g, rope_tab);
     const int row0 = q_first + w * 32;
@@ -449,7 +486,9 @@ dq_bcast_kernel(DqParams P) {
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
     // the sequence's first key stages are in flight while its dO and out rows load
-    dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, L, w, lane);
+    const int n_steps = ceil_div(L, C::BN);
+    const StreamKeys<C::BN> ks{nullptr, L, 0};
+    dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, n_steps, ks, w, lane);
     u32x4 dof[C::DS];
     const float di = load_do_row<D>(P.o + oeff, P.dout + oeff, ok, g, dof);
     const int64_t vidx = (int64_t(b) * P.H + h) * P.lq + qpos;
@@ -459,9 +498,9 @@ dq_bcast_kernel(DqParams P) {
       P.nls[vidx] = -lse / P.scale;
     }
     if (L > 0)
-      dq_stream<D, false, false, NW, true>(lds, kbase, vbase, rstride, L, L, 0,
-                                    L / C::BN, own ? ceil_div(L, C::BN) : 1, 0, qf, dof, acc,
-                                    lse * kLog2e, di, P.c, w, lane, qpos, lo);
+      dq_stream<D, false, false, NW, true>(lds, kbase, vbase, rstride, L, n_steps, ks, 0,
+                                           L / C::BN, own ? n_steps : 1, 0, qf, dof, acc,
+                                           lse * kLog2e, di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;
@@ -527,6 +566,7 @@ struct KvParams {
   float c, scale;
   int32_t window;     // causal sliding window (WIN kernels)
   jfa::RopeTab rope;  // rotary kernels only
+  const int32_t* sp_base; const int32_t* sp_ptr; const int32_t* sp_ent;  // SPARSE kernels
 };
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_rw_t;
@@ -658,10 +698,16 @@ __device__ __forceinline__ void xch_get(const KvAddr<D>& a, u32x4 (&pp)[KvCfg<D>
     pp[x] = lds_ld16(a.xch + uint32_t((S * C::NP * C::PK + x) * 64 * 16));
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN>
+// SPARSE (block-sparse attention): a tile's steps are the 64-row query blocks of
+// its step list, in ascending order; a pair whose 64-key block a step's query
+// block does not attend sets its P to zero (so dS is zero too); a tile whose list
+// is empty stores zeros.
+template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dkdv_kernel(KvParams P) {
   using C = KvCfg<D>;
+  static_assert(!SPARSE || (C::BM == jfa::kSpBlock && C::BN == 2 * jfa::kSpBlock),
+                "a sparse step is one query block and a tile two key blocks");
   static_assert(C::NS == 3, "the ring below loads one stage ahead and unrolls by three");
   // Q ring then dO ring; the output rows are staged over both at the end of a tile
   __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * C::NS * C::TILE];
@@ -682,6 +728,7 @@ dkdv_kernel(KvParams P) {
   // what every wave derives from a tile of the schedule
   struct Entry {  // what the schedule and the offsets give for a tile
     int b, h, kv0, L, key0;
+    int e_first, n_ent;  // SPARSE: the tile's step list
   };
   struct Tile : Entry {
     int rows_total, qs_lo, n_steps, n_mask, n_hi;
@@ -696,6 +743,12 @@ dkdv_kernel(KvParams P) {
     E.key0 = sload(P.tiles + 4 * ti + 2) * C::BN;
     E.kv0 = sload(P.offsets + E.b);
     E.L = sload(P.offsets + E.b + 1) - E.kv0;
+    E.e_first = E.n_ent = 0;
+    if (SPARSE) {
+      const int u = sload(P.sp_base + E.b) + E.key0 / C::BN;
+      E.e_first = sload(P.sp_ptr + u);
+      E.n_ent = sload(P.sp_ptr + u + 1) - E.e_first;
+    }
     return E;
   };
   auto tile_of = [&](const Entry& E) {
@@ -717,10 +770,14 @@ dkdv_kernel(KvParams P) {
     // zeros and contribute nothing)
     T.n_mask = CAUSAL ? min(T.n_steps, C::BN / C::BM) : 0;
     T.n_hi = WIN ? max(0, (T.key0 + P.window) / C::BM - T.qs_lo) : T.n_steps;
+    if (SPARSE) T.n_steps = T.n_hi = T.n_ent;  // may be 0
     return T;
   };
+  // SPARSE: entry st of a tile's step list
+  auto sp_entry = [&](const Tile& T, int st) { return sload(P.sp_ent + T.e_first + st); };
   auto load_stage = [&](const Tile& T, int st) {
-    const int q_first = (T.qs_lo + st) * C::BM;
+    const int q_first =
+        SPARSE ? (sp_entry(T, st) & jfa::kSpIdx) * jfa::kSpBlock : (T.qs_lo + st) * C::BM;
     const int left = T.rows_total - q_first;
     const int sl = st % C::NS;
     tile_load<D, C::BM, C::NW>(ring + sl * C::TILE,
@@ -765,7 +822,7 @@ dkdv_kernel(KvParams P) {
     if (t_begin < t_end) {
       T = tile_of(entry_of(t_begin));
       load_op(T, op);
-      load_stage(T, 0);
+      if (!SPARSE || T.n_steps > 0) load_stage(T, 0);
     }
     for (int ti = t_begin; ti < t_end; ++ti) {
       // The next tile's schedule entry, read at the start of this one and kept
@@ -776,6 +833,7 @@ dkdv_kernel(KvParams P) {
       Entry En{};
       if (ti + 1 < t_end) En = entry_of(ti + 1);
       asm volatile("" : "+v"(En.b), "+v"(En.h), "+v"(En.kv0), "+v"(En.L), "+v"(En.key0));
+      if (SPARSE) asm volatile("" : "+v"(En.e_first), "+v"(En.n_ent));
       const int row0 = T.key0 + kw * 32;
       const int jw = row0 + li;  // this lane's key
       // lane-dependent addresses are derived afresh for each tile (otherwise the
@@ -844,6 +902,10 @@ dkdv_kernel(KvParams P) {
             kv_probs<D, true, WIN>(s, P.c, g, q0, jw, pk, P.window);
           else
             kv_probs<D, false>(s, P.c, g, q0, jw, pk);
+          if (SPARSE && !((sp_entry(T, it) >> (jfa::kSpBit + kw / 2)) & 1)) {
+#pragma unroll
+            for (int x = 0; x < C::PK; ++x) pk[x] = u32x4{0, 0, 0, 0};
+          }
           xch_put<D, S>(ad, pk);
         } else {
           if (prev) {
@@ -887,6 +949,10 @@ dkdv_kernel(KvParams P) {
         }
         next_op();
         __syncthreads();  // the tail's barrier
+      } else if (SPARSE && T.n_steps == 0) {
+        // no query block attends the tile's keys: zero dK and dV
+        next_op();
+        __syncthreads();  // the tail's barrier
       } else {
         for (int it = 0; it < T.n_steps; it += 3) {
           step(it, S0{});
@@ -903,8 +969,8 @@ dkdv_kernel(KvParams P) {
       const Tile Tc = T;
       if (ti + 1 < t_end) {
         T = tile_of(Entry{uniform(En.b), uniform(En.h), uniform(En.kv0), uniform(En.L),
-                          uniform(En.key0)});
-        load_stage(T, 0);
+                          uniform(En.key0), uniform(En.e_first), uniform(En.n_ent)});
+        if (!SPARSE || T.n_steps > 0) load_stage(T, 0);
       }
       // output rows staged in ring stages 1 and 2 (stage 0 is filling); the next
       // tile's first barrier orders these reads before its loads of stage 1. The
@@ -926,7 +992,7 @@ int grid_for(int64_t n4) {
   return int(g < 8192 ? (g > 0 ? g : 1) : 8192);
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN>
+template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN, bool SPARSE = false>
 jfa_status launch_t(const jfa::BwdLaunch& a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const float c = a.scale * kLog2e;
@@ -952,6 +1018,9 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
   dp.c = c;
   dp.scale = a.scale;
   dp.window = a.window;
+  dp.sp_base = a.q_sp_base;
+  dp.sp_ptr = a.q_sp_ptr;
+  dp.sp_ent = a.q_sp_ent;
   if (ROPE) dp.rope = *a.rope;
   const bool run_dq = a.passes & JFA_PASS_DQ, run_kv = a.passes & JFA_PASS_DKDV;
   if (!run_dq) {
@@ -964,8 +1033,8 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     hipLaunchKernelGGL(dq_reduce_kernel, dim3(grid_for(n4)), dim3(256), 0, st, a.dq_part,
                        static_cast<uint16_t*>(a.dq), n4, a.groups, a.scale);
   } else if (a.total_kv > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, ROPE, WIN>), dim3(a.q_num_slots), dim3(DqCfg<D>::NT), 0, st,
-                       dp);
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, ROPE, WIN, SPARSE>), dim3(a.q_num_slots),
+                       dim3(DqCfg<D>::NT), 0, st, dp);
   }
   if (run_kv && a.total_kv > 0) {
     KvParams kp{};
@@ -986,8 +1055,11 @@ jfa_status launch_t(const jfa::BwdLaunch& a) {
     kp.c = c;
     kp.scale = a.scale;
     kp.window = a.window;
+    kp.sp_base = a.kv_sp_base;
+    kp.sp_ptr = a.kv_sp_ptr;
+    kp.sp_ent = a.kv_sp_ent;
     if (ROPE) kp.rope = *a.rope;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST, ROPE, WIN>), dim3(a.kv_num_slots),
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BCAST, ROPE, WIN, SPARSE>), dim3(a.kv_num_slots),
                        dim3(KvCfg<D>::NT), 0, st, kp);
   }
   const hipError_t e = hipGetLastError();
@@ -1013,6 +1085,7 @@ jfa_status launch_bwd_d(const BwdLaunch& a) {
   const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, rope = a.rope != nullptr,
              win = a.window > 0;
   if (bq) return launch_t<D, false, true, false, false>(a);
+  if (a.flags & JFA_BLOCK_SPARSE) return launch_t<D, false, false, false, false, true>(a);
   if (win)  // a window comes with CAUSAL
     return rope ? launch_t<D, true, false, true, true>(a) : launch_t<D, true, false, false, true>(a);
   if (rope)

@@ -52,6 +52,7 @@ struct FwdParams {
   int32_t H, lq, total_kv;
   float c;  // scale * log2(e)
   int32_t window;  // causal sliding window (WIN kernels)
+  const int32_t* sp_base; const int32_t* sp_ptr; const int32_t* sp_ent;  // SPARSE kernels
 };
 
 // Scores of one step whose keys fall past the sequence end or, with CAUSAL,
@@ -211,7 +212,11 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool WIN>
+// SPARSE (block-sparse attention over 64-token blocks): a tile's steps walk the
+// key blocks its step list names, in ascending order, instead of the whole
+// sequence; every step is masked, a wave's scores wholly when its query block
+// does not attend the step's key block, and past the sequence end.
+template <int D, bool CAUSAL, bool BCAST, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
   using C = FwdCfg<D>;
@@ -237,11 +242,30 @@ fwd_kernel(FwdParams P) {
     // and are masked like the diagonal ones.
     const int ks0 = WIN ? max(0, q_first - P.window + 1) / C::BN * C::BN : 0;
     const int n_keys = (CAUSAL ? min(L, q_first + q_rows) : L) - ks0;
-    const int n_steps = ceil_div(n_keys, C::BN);
+    // SPARSE: the tile's entries [e_first, e_first + n_ent), SPB steps each
+    constexpr int SPB = SPARSE ? jfa::kSpBlock / C::BN : 1;
+    int e_first = 0, n_ent = 0;
+    if (SPARSE) {
+      const int u = sload(P.sp_base + b) + t;
+      e_first = sload(P.sp_ptr + u);
+      n_ent = sload(P.sp_ptr + u + 1) - e_first;
+    }
+    const int n_steps = SPARSE ? n_ent * SPB : ceil_div(n_keys, C::BN);
     const int lo_edge = WIN ? q_first + C::BM - P.window - ks0 : 0;
     const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
     // steps without a mask: [n_lo, n_free)
-    const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
+    const int n_free =
+        SPARSE ? 0 : max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
+    // first key of step st (counted from ks0) and the key count its mask uses:
+    // SPARSE masks every key of a block the wave's query block does not attend
+    auto key_of = [&](int st) {
+      if (!SPARSE) return st * C::BN;
+      return (sload(P.sp_ent + e_first + st / SPB) & jfa::kSpIdx) * jfa::kSpBlock + (st % SPB) * C::BN;
+    };
+    auto nk_of = [&](int st) {
+      if (!SPARSE) return n_keys;
+      return (sload(P.sp_ent + e_first + st / SPB) >> (jfa::kSpBit + w / 2)) & 1 ? L : 0;
+    };
     const int qpos = q_first + w * 32 + li;  // query position of this lane
     const int qm = qpos - ks0;                // the same, counted from key ks0
     // Steps this wave computes: all, or one when the tile has no row for it
@@ -259,9 +283,10 @@ fwd_kernel(FwdParams P) {
     // covering the rest of the sequence (keys past the end read as zero)
     auto load_stage = [&](int st) {
       uint16_t* buf = lds + (st % C::NS) * C::STAGE;
-      const int64_t r0 = int64_t(st) * C::BN * rstride;
-      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, Lk - st * C::BN), rowbytes, w, lane);
-      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, Lk - st * C::BN),
+      const int key = key_of(st);
+      const int64_t r0 = int64_t(key) * rstride;
+      tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, Lk - key), rowbytes, w, lane);
+      tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, Lk - key),
                                  rowbytes, w, lane);
     };
     auto stage_ptr = [&](int st) { return lds + (st % C::NS) * C::STAGE; };
@@ -291,7 +316,8 @@ fwd_kernel(FwdParams P) {
       __syncthreads();
       f32x16 sc[C::KB], sn[C::KB];
       scores<D>(stage_ptr(0), qf, sc, li, g);
-      if (n_lo > 0 || n_free == 0) mask_scores<D, CAUSAL, WIN>(sc, g, 0, n_keys, qm, P.window);
+      if (n_lo > 0 || n_free == 0)
+        mask_scores<D, CAUSAL, WIN>(sc, g, key_of(0), nk_of(0), qm, P.window);
       m = pair_max(row_max<D>(sc)) * P.c;
 
       // before step kt (kt + 1 < n_steps): stage kt+1 must have landed, stage
@@ -342,7 +368,7 @@ fwd_kernel(FwdParams P) {
         advance(kt);
         const float mx = fwd_step<D, true, true, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
                                                         qf, sc, sn, o, m, l, P.c, lane,
-                                                        (kt + 1) * C::BN, n_keys, qm, P.window);
+                                                        key_of(kt + 1), nk_of(kt + 1), qm, P.window);
         update_max<D>(mx, m, l, o);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
@@ -378,7 +404,7 @@ fwd_kernel(FwdParams P) {
   }
 }
 
-template <int D, bool CAUSAL, bool BCAST, bool WIN>
+template <int D, bool CAUSAL, bool BCAST, bool WIN, bool SPARSE = false>
 jfa_status launch_t(const jfa::FwdLaunch& a) {
   FwdParams P;
   P.q = static_cast<const uint16_t*>(a.q);
@@ -394,7 +420,10 @@ jfa_status launch_t(const jfa::FwdLaunch& a) {
   P.total_kv = int32_t(a.total_kv);
   P.c = a.scale * kLog2e;
   P.window = a.window;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, BCAST, WIN>), dim3(a.num_slots), dim3(FwdCfg<D>::NT), 0,
+  P.sp_base = a.sp_base;
+  P.sp_ptr = a.sp_ptr;
+  P.sp_ent = a.sp_ent;
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, BCAST, WIN, SPARSE>), dim3(a.num_slots), dim3(FwdCfg<D>::NT), 0,
                      static_cast<hipStream_t>(a.stream), P);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return jfa::fail(JFA_ERR_HIP, std::string("fwd launch: ") + hipGetErrorString(e));
@@ -416,6 +445,9 @@ namespace jfa {
 
 jfa_status launch_fwd(const FwdLaunch& a) {
   const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, win = a.window > 0;
+  if (a.flags & JFA_BLOCK_SPARSE)
+    return a.head_dim == 128 ? launch_t<128, false, false, false, true>(a)
+                             : launch_t<64, false, false, false, true>(a);
   if (a.head_dim == 128) {
     if (bq) return launch_t<128, false, true, false>(a);
     if (win) return launch_t<128, true, false, true>(a);

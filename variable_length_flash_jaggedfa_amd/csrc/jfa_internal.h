@@ -16,6 +16,12 @@ constexpr int kBwdBN = 128;    // key rows per backward tile (4 waves x 32 keys)
 constexpr int kBwdBM = 64;     // query rows per backward query step
 constexpr int kBlock = 64;     // block-diagonal group size
 constexpr int kXcds = 8;       // accelerator complex dies (separate L2s) on MI355X
+// Block-sparse step lists: an entry is the other side's 64-token block index in
+// the low bits and, in bits kSpBit and kSpBit + 1, which of the tile's two
+// blocks pair with it.
+constexpr int kSpBlock = 64;
+constexpr int kSpBit = 28;
+constexpr int32_t kSpIdx = (1 << kSpBit) - 1;
 
 // thread-local error text
 void set_error(const std::string& msg);
@@ -59,6 +65,8 @@ struct FwdLaunch {
   float rope_base;  // ROTARY only
   int32_t window;   // causal sliding window (0: none)
   int32_t block;    // single-tile block kernels: tokens per block (32 or 64)
+  // BLOCK_SPARSE: the forward step lists (seq_base [B+1], list_ptr, entries)
+  const int32_t* sp_base; const int32_t* sp_ptr; const int32_t* sp_ent;
   void* stream;
 };
 
@@ -83,6 +91,10 @@ struct BwdLaunch {
   uint32_t passes;  // JFA_PASS_* mask
   const RopeTab* rope;  // jagged ROTARY: q and k are the rotated copies, dq and dk
                         // are turned back in the epilogues; otherwise NULL
+  // BLOCK_SPARSE: the step lists of the query tiles (dQ pass) and of the key
+  // tiles (dK/dV pass): seq_base [B+1], list_ptr, entries
+  const int32_t* q_sp_base; const int32_t* q_sp_ptr; const int32_t* q_sp_ent;
+  const int32_t* kv_sp_base; const int32_t* kv_sp_ptr; const int32_t* kv_sp_ent;
   void* stream;
 };
 

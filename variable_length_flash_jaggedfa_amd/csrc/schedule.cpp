@@ -32,7 +32,8 @@ jfa_status check_problem(const jfa_problem* p) {
   if (p->total_kv < 0) return fail(JFA_ERR_INVALID_ARG, "total_kv < 0");
   if (!(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(JFA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  const uint32_t known = JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY | JFA_BLOCK_DIAG;
+  const uint32_t known =
+      JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY | JFA_BLOCK_DIAG | JFA_BLOCK_SPARSE;
   if (p->flags & ~known) return fail(JFA_ERR_INVALID_ARG, "unknown flag bits");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
@@ -40,7 +41,11 @@ jfa_status check_problem(const jfa_problem* p) {
              blk = p->flags & (JFA_BLOCK_DIAG64 | JFA_BLOCK_DIAG);
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
   if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "block-diagonal with other flags");
-  if (p->flags & JFA_BLOCK_DIAG) {
+  if (p->flags & JFA_BLOCK_SPARSE) {
+    if (p->flags != JFA_BLOCK_SPARSE)
+      return fail(JFA_ERR_UNSUPPORTED, "BLOCK_SPARSE combines with no other flag");
+    if (p->block != kSpBlock) return fail(JFA_ERR_INVALID_ARG, "BLOCK_SPARSE needs block = 64");
+  } else if (p->flags & JFA_BLOCK_DIAG) {
     if (p->block != 32 && p->block != 64 && p->block != 128 && p->block != 256)
       return fail(JFA_ERR_UNSUPPORTED, "BLOCK_DIAG needs block 32, 64, 128 or 256");
     if ((p->flags & JFA_BLOCK_DIAG64) && p->block != 64)
@@ -102,14 +107,26 @@ jfa_status check_offsets(const jfa_problem* p, const int32_t* off) {
   return JFA_OK;
 }
 
-// Tiles in generation order (b, then h, then t).
-std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t kind) {
+// Tiles in generation order (b, then h, then t). With `sp_ptr` (block-sparse step
+// lists, one list per (b, t) in that order, see sparse_lists) a tile's work is its
+// list's length times the 64 keys (or query rows) of each entry.
+std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t kind,
+                            const int32_t* sp_ptr = nullptr) {
   const bool causal = p->flags & JFA_CAUSAL;
   const int32_t lq = (p->flags & JFA_BROADCAST_Q) ? p->lq : 0;
   const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
   std::vector<Tile> tiles;
+  int64_t u0 = 0;  // first (b, t) unit of sequence b
   for (int32_t b = 0; b < p->num_seqs; ++b) {
     const int32_t L = off[b + 1] - off[b];
+    if (sp_ptr) {
+      const int32_t n = ceil_div(L, rows);
+      for (int32_t h = 0; h < p->num_heads; ++h)
+        for (int32_t t = 0; t < n; ++t)
+          tiles.push_back({b, h, t, (sp_ptr[u0 + t + 1] - sp_ptr[u0 + t]) * kSpBlock});
+      u0 += n;
+      continue;
+    }
     for (int32_t h = 0; h < p->num_heads; ++h) {
       if (kind == JFA_KIND_FWD) {
         if (lq) {
@@ -204,13 +221,13 @@ extern "C" jfa_status jfa_schedule_count(const jfa_problem* p, const int32_t* of
   return JFA_OK;
 }
 
-extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
-                                   int32_t order, int32_t num_slots, int32_t* slot_ptr,
-                                   int32_t* tiles_out, int64_t capacity) {
-  int64_t count = 0;
-  if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
-  if (unit_blocks(p))
-    return fail(JFA_ERR_UNSUPPORTED, "blocks of 32 or 64 tokens run without a schedule");
+namespace {
+
+jfa_status deal(const jfa_problem* p, const std::vector<Tile>& tiles, int32_t order,
+                int32_t num_slots, int32_t* slot_ptr, int32_t* tiles_out);
+
+jfa_status check_deal_args(int64_t count, int32_t order, int32_t num_slots, int32_t* slot_ptr,
+                           int32_t* tiles_out, int64_t capacity) {
   if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG &&
       order != JFA_ORDER_FOLDED_ZIGZAG)
     return fail(JFA_ERR_INVALID_ARG, "bad order");
@@ -218,6 +235,114 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   if (!slot_ptr) return fail(JFA_ERR_INVALID_ARG, "slot_ptr is NULL");
   if (count > 0 && !tiles_out) return fail(JFA_ERR_INVALID_ARG, "tiles is NULL");
   if (capacity < count) return fail(JFA_ERR_INVALID_ARG, "tiles capacity too small");
+  return JFA_OK;
+}
+
+// Blocks of a sequence of L tokens, and its mask's first byte in the flat array.
+int64_t sp_blocks(int64_t L) { return (L + kSpBlock - 1) / kSpBlock; }
+
+jfa_status check_sparse(const jfa_problem* p, const int32_t* off, const uint8_t* mask,
+                        int64_t mask_bytes, int32_t kind) {
+  if (jfa_status s = check_problem(p)) return s;
+  if (!(p->flags & JFA_BLOCK_SPARSE)) return fail(JFA_ERR_INVALID_ARG, "problem is not BLOCK_SPARSE");
+  if (kind != JFA_KIND_FWD && kind != JFA_KIND_BWD) return fail(JFA_ERR_INVALID_ARG, "bad kind");
+  if (jfa_status s = check_offsets(p, off)) return s;
+  int64_t need = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int64_t n = sp_blocks(int64_t(off[b + 1]) - off[b]);
+    need += n * n;
+  }
+  if (mask_bytes != need)
+    return fail(JFA_ERR_INVALID_ARG, "mask_bytes is " + std::to_string(mask_bytes) + ", the offsets need " +
+                                         std::to_string(need) + " (sum of n_b^2)");
+  if (need > 0 && !mask) return fail(JFA_ERR_INVALID_ARG, "mask_host is NULL");
+  return JFA_OK;
+}
+
+// The step lists of `kind` (see jfa_sparse_lists); with null outputs only counts.
+void sparse_lists(const jfa_problem* p, const int32_t* off, const uint8_t* mask, int32_t kind,
+                  int32_t* seq_base, int32_t* list_ptr, int32_t* entries, int64_t* n_units,
+                  int64_t* n_entries) {
+  const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);  // two 64-token blocks
+  int64_t u = 0, e = 0, m0 = 0;
+  if (list_ptr) list_ptr[0] = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int64_t L = int64_t(off[b + 1]) - off[b], n = sp_blocks(L);
+    const uint8_t* mb = mask + m0;
+    if (seq_base) seq_base[b] = int32_t(u);
+    for (int64_t t = 0, nt = (L + rows - 1) / rows; t < nt; ++t, ++u) {
+      const int64_t a0 = 2 * t, a1 = 2 * t + 1;  // the unit's two blocks
+      for (int64_t c = 0; c < n; ++c) {
+        // FWD: key block c for query blocks a0, a1; BWD: query block c for key blocks a0, a1
+        const bool x0 = kind == JFA_KIND_FWD ? mb[a0 * n + c] : mb[c * n + a0];
+        const bool x1 = a1 < n && (kind == JFA_KIND_FWD ? mb[a1 * n + c] : mb[c * n + a1]);
+        if (!x0 && !x1) continue;
+        if (entries) entries[e] = int32_t(c) | (int32_t(x0) << kSpBit) | (int32_t(x1) << (kSpBit + 1));
+        ++e;
+      }
+      if (list_ptr) list_ptr[u + 1] = int32_t(e);
+    }
+    m0 += n * n;
+  }
+  if (seq_base) seq_base[p->num_seqs] = int32_t(u);
+  *n_units = u;
+  *n_entries = e;
+}
+
+}  // namespace
+
+extern "C" jfa_status jfa_sparse_lists_count(const jfa_problem* p, const int32_t* offsets_host,
+                                             const uint8_t* mask_host, int64_t mask_bytes,
+                                             int32_t kind, int64_t* num_units,
+                                             int64_t* num_entries) {
+  set_error("");
+  if (jfa_status s = check_sparse(p, offsets_host, mask_host, mask_bytes, kind)) return s;
+  if (!num_units || !num_entries) return fail(JFA_ERR_INVALID_ARG, "num_units or num_entries is NULL");
+  sparse_lists(p, offsets_host, mask_host, kind, nullptr, nullptr, nullptr, num_units, num_entries);
+  if (*num_entries > INT32_MAX || *num_units > INT32_MAX)
+    return fail(JFA_ERR_INVALID_ARG, "too many step-list entries");
+  return JFA_OK;
+}
+
+extern "C" jfa_status jfa_sparse_lists(const jfa_problem* p, const int32_t* offsets_host,
+                                       const uint8_t* mask_host, int64_t mask_bytes, int32_t kind,
+                                       int32_t* seq_base, int32_t* list_ptr, int32_t* entries,
+                                       int64_t entries_capacity) {
+  int64_t nu = 0, ne = 0;
+  if (jfa_status s = jfa_sparse_lists_count(p, offsets_host, mask_host, mask_bytes, kind, &nu, &ne))
+    return s;
+  if (!seq_base || !list_ptr || (ne > 0 && !entries))
+    return fail(JFA_ERR_INVALID_ARG, "seq_base, list_ptr or entries is NULL");
+  if (entries_capacity < ne) return fail(JFA_ERR_INVALID_ARG, "entries capacity too small");
+  sparse_lists(p, offsets_host, mask_host, kind, seq_base, list_ptr, entries, &nu, &ne);
+  return JFA_OK;
+}
+
+extern "C" jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host,
+                                          const int32_t* list_ptr_host, int32_t kind, int32_t order,
+                                          int32_t num_slots, int32_t* slot_ptr, int32_t* tiles_out,
+                                          int64_t capacity) {
+  set_error("");
+  if (jfa_status s = check_problem(p)) return s;
+  if (!(p->flags & JFA_BLOCK_SPARSE)) return fail(JFA_ERR_INVALID_ARG, "problem is not BLOCK_SPARSE");
+  int64_t count = 0;
+  if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
+  if (jfa_status s = check_deal_args(count, order, num_slots, slot_ptr, tiles_out, capacity)) return s;
+  if (!list_ptr_host) return fail(JFA_ERR_INVALID_ARG, "list_ptr_host is NULL");
+  return deal(p, enumerate(p, offsets_host, kind, list_ptr_host), order, num_slots, slot_ptr,
+              tiles_out);
+}
+
+extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
+                                   int32_t order, int32_t num_slots, int32_t* slot_ptr,
+                                   int32_t* tiles_out, int64_t capacity) {
+  int64_t count = 0;
+  if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
+  if (unit_blocks(p))
+    return fail(JFA_ERR_UNSUPPORTED, "blocks of 32 or 64 tokens run without a schedule");
+  if (p->flags & JFA_BLOCK_SPARSE)
+    return fail(JFA_ERR_INVALID_ARG, "BLOCK_SPARSE schedules come from jfa_schedule_sparse");
+  if (jfa_status s = check_deal_args(count, order, num_slots, slot_ptr, tiles_out, capacity)) return s;
 
   // 128- and 256-token blocks: the tiles of the jagged problem whose sequences are
   // the blocks, in order
@@ -232,8 +357,15 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
     pb.flags = p->flags & ~(JFA_BLOCK_DIAG | JFA_BLOCK_DIAG64);
     pb.block = 0;
   }
-  const std::vector<Tile> tiles = tiled_blocks(p) ? enumerate(&pb, boff.data(), kind)
-                                                  : enumerate(p, offsets_host, kind);
+  return deal(p, tiled_blocks(p) ? enumerate(&pb, boff.data(), kind) : enumerate(p, offsets_host, kind),
+              order, num_slots, slot_ptr, tiles_out);
+}
+
+namespace {
+
+// Deal the tiles (generation order) over the slots by `order` (see jfa_schedule).
+jfa_status deal(const jfa_problem* p, const std::vector<Tile>& tiles, int32_t order,
+                int32_t num_slots, int32_t* slot_ptr, int32_t* tiles_out) {
   std::vector<int32_t> idx;      // tiles in dealing order
   std::vector<int32_t> slot_of;  // slot of idx[j]
   if (order == JFA_ORDER_XCD_ZIGZAG) {
@@ -351,6 +483,8 @@ extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_
   }
   return JFA_OK;
 }
+
+}  // namespace
 
 namespace jfa {
 
