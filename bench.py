@@ -49,6 +49,22 @@ def pairs_of(lengths, causal=False, lq=0, block=0, window=0):
     return int((L * L).sum())
 
 
+def sparse_pairs(lengths, flat_mask):
+    """Attended pairs of block-sparse attention: for each sequence, the rows of
+    every allowed (query block, key block) pair times its columns (64, or what the
+    partial last block holds)."""
+    total, pos = 0, 0
+    for n in np.asarray(lengths, dtype=np.int64):
+        nb = -(-int(n) // 64)
+        m = np.asarray(flat_mask[pos:pos + nb * nb], dtype=np.int64).reshape(nb, nb)
+        pos += nb * nb
+        rows = np.full(nb, 64, dtype=np.int64)
+        if nb:
+            rows[-1] = int(n) - 64 * (nb - 1)
+        total += int(rows @ m @ rows)
+    return total
+
+
 def variants_of(name):
     wl = J.standard_workloads()
     if name in ("gem", "gem_padded", "gem_rope"):
@@ -66,13 +82,16 @@ def flags_of(w, jfa):
         f |= jfa.BLOCK_DIAG64 if w.block == 64 else jfa.BLOCK_DIAG
     if w.rope_base:
         f |= jfa.ROTARY
+    if w.kind == "sparse":
+        f |= jfa.BLOCK_SPARSE
     return f
 
 
-def plan_kw(w):
+def plan_kw(w, case):
     """Plan arguments beyond the flags."""
     return dict(rope_base=w.rope_base, window=w.window,
-                block=w.block if w.kind == "block" and w.block != 64 else 0)
+                block=w.block if w.kind == "block" and w.block != 64 else 0,
+                block_mask=case.mask if w.kind == "sparse" else None)
 
 
 def padded_ratio(case, w):
@@ -82,6 +101,8 @@ def padded_ratio(case, w):
     if len(L) == 0 or L.sum() == 0:
         return 1.0
     m = int(L.max())
+    if w.kind == "sparse":  # padded dense attention against the pairs the masks keep
+        return float(len(L) * m * m) / float(max(1, sparse_pairs(L, case.mask)))
     if w.kind == "block":
         return float(len(L) * m) / float(L.sum())
     if w.kind == "broadcast":
@@ -103,7 +124,11 @@ def cpu_baseline(case, variants, pool, budget_s=16.0):
     for w in variants:
         done, dt = OP.time_sample(pool, w, case.scale, off, budget_s / len(variants))
         L = np.diff(off)[np.asarray(done, dtype=np.int64)]
-        npairs = pairs_of(L, w.causal, w.lq, w.block if w.kind == "block" else 0, w.window)
+        if w.kind == "sparse":
+            npairs = sum(sparse_pairs([n], J.sparse_mask_seq(w, int(b), int(n)).ravel())
+                         for b, n in zip(done, L))
+        else:
+            npairs = pairs_of(L, w.causal, w.lq, w.block if w.kind == "block" else 0, w.window)
         flops += 14.0 * npairs * w.num_heads * w.head_dim
         secs += dt
         n_done += len(done)
@@ -128,7 +153,7 @@ def compare_rope(case, runs, q, k, v, do, dev, rounds, order):
     w = runs[0]["w"]
     plains = [jfa.Plan(case.offsets, r["w"].num_heads, r["w"].head_dim, case.scale,
                        flags_of(r["w"], jfa) & ~jfa.ROTARY, 0, order=order, device=dev,
-                       **dict(plan_kw(r["w"]), rope_base=0.0))
+                       **dict(plan_kw(r["w"], case), rope_base=0.0))
               for r in runs]
     D = w.head_dim
     # positions inside the sequence, angles in float64, tables in bf16
@@ -295,7 +320,7 @@ def main():
                     choices=["gem", "gem_causal", "tiny", "broadcast", "block64_d64",
                              "block64_d128", "block64_rope_d64", "block64_rope_d128", "gem_rope",
                              "gem_window", "block32_d128", "block128_d128", "block256_d128",
-                             "imbalance", "gem_padded"])
+                             "imbalance", "gem_padded", "sparse_d128", "sparse_d64"])
     ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time forward + backward under every dealing order, interleaved")
@@ -362,12 +387,13 @@ def main():
         fl = flags_of(w, jfa)
         t0 = time.perf_counter()
         plan = jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, fl, w.lq,
-                        order=order, device=dev, **plan_kw(w))
+                        order=order, device=dev, **plan_kw(w, case))
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
-        npairs = pairs_of(case.lengths, w.causal, w.lq, w.block if w.kind == "block" else 0,
-                          w.window)
+        npairs = (sparse_pairs(case.lengths, case.mask) if w.kind == "sparse" else
+                  pairs_of(case.lengths, w.causal, w.lq, w.block if w.kind == "block" else 0,
+                           w.window))
         nhd = float(npairs) * w.num_heads * w.head_dim
         # "block": the single-tile kernels of 32- and 64-token blocks (one fused
         # backward); 128- and 256-token blocks run the jagged kernels, except the
@@ -378,7 +404,11 @@ def main():
         if not plan.block:
             for kind, sc in plan.sched.items():
                 t1 = time.perf_counter()
-                jfa.schedule(plan.p, case.offsets, kind, order, sc.num_slots)
+                if plan.sparse:  # the step lists and the schedule built from them
+                    lp = jfa.sparse_lists(plan.p, case.offsets, case.mask, kind)[1]
+                    jfa.schedule_sparse(plan.p, case.offsets, lp, kind, order, sc.num_slots)
+                else:
+                    jfa.schedule(plan.p, case.offsets, kind, order, sc.num_slots)
                 jfa_schedule_ms += (time.perf_counter() - t1) * 1e3
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
                          block=plan.block, fused_bwd=fused_bwd,
@@ -388,7 +418,7 @@ def main():
     alt = None
     if args.compare_orders:
         alt = {name: [jfa.Plan(case.offsets, w.num_heads, w.head_dim, case.scale, flags_of(w, jfa),
-                               w.lq, order=code, device=dev, **plan_kw(w))
+                               w.lq, order=code, device=dev, **plan_kw(w, case))
                       for w in variants]
                for name, code in ORDERS.items()}
     torch.cuda.synchronize()

@@ -71,3 +71,16 @@ def test_padding_ratio_counts_padded_pairs():
     r_c = bench.padded_ratio(Case, g[1])
     assert r_nc == pytest.approx(3 * 64 / masked_pairs([3, 5, 8]))
     assert r_c == pytest.approx(3 * 36 / masked_pairs([3, 5, 8], causal=True))
+
+
+def test_block_sparse_pairs():
+    """Block-sparse: the pairs of the token mask each block mask expands to."""
+    rng = np.random.default_rng(3)
+    L = LENGTHS
+    masks = [rng.random((-(-l // 64),) * 2) < 0.4 for l in L]
+    flat = np.concatenate([m.astype(np.uint8).ravel() for m in masks])
+    want = 0
+    for l, m in zip(L, masks):
+        i = np.arange(l)
+        want += int(m[i[:, None] // 64, i[None, :] // 64].sum())
+    assert bench.sparse_pairs(L, flat) == want == A.pair_count(L, masks=masks)

@@ -257,7 +257,29 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     __syncthreads();
   };
   if (!PRE) dq_stream_issue<D, NW, SPARSE>(lds, kbase, vbase, rstride, L, n_steps, ks, w, lane);
-  if (n_steps > 0) {
+  if (SPARSE) {
+    // Block-sparse: each step whole (S, dP, dS and the dQ products on the one
+    // stage); a wave whose query block does not attend the step's key block
+    // skips it, leaving its SIMD's matrix core to the other workgroup.
+    f32x16 s[C::KB], dp[C::KB];
+    u32x4 pds[2 * C::KB];
+    f32x16 ndi;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndi[r] = -di;
+    for (int kt = 0; kt < n_steps; ++kt) {
+      arrive(kt);  // also: every wave is done with stage kt-1
+      if (kt + C::NS - 2 < n_steps) load_stage(kt + C::NS - 2);
+      const int nk = count_of(kt);
+      if (kt < n_own && nk > 0) {
+        __builtin_amdgcn_s_setprio(1);
+        dq_scores<D>(ks_of(kt), lo, qf, dof, ndi, s, dp);
+        __builtin_amdgcn_s_setprio(0);
+        dq_softmax<D, true, false, false>(s, dp, lse2, c, g, key_of(kt), nk, qpos, pds, 0, lo, pds,
+                                          acc);
+        dq_accumulate<D>(ks_of(kt), lo, pds, acc);
+      }
+    }
+  } else if (n_steps > 0) {
     f32x16 s[C::KB], dp[C::KB];
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
     f32x16 ndi;  // -Di of the lane's row, the first dP product's accumulator input
@@ -700,8 +722,8 @@ __device__ __forceinline__ void xch_get(const KvAddr<D>& a, u32x4 (&pp)[KvCfg<D>
 
 // SPARSE (block-sparse attention): a tile's steps are the 64-row query blocks of
 // its step list, in ascending order; a pair whose 64-key block a step's query
-// block does not attend sets its P to zero (so dS is zero too); a tile whose list
-// is empty stores zeros.
+// block does not attend skips that step's products (its SIMD's matrix core serves
+// the other waves meanwhile); a tile whose list is empty stores zeros.
 template <int D, bool CAUSAL, bool BCAST, bool ROPE, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(KvCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dkdv_kernel(KvParams P) {
@@ -728,9 +750,9 @@ dkdv_kernel(KvParams P) {
   // what every wave derives from a tile of the schedule
   struct Entry {  // what the schedule and the offsets give for a tile
     int b, h, kv0, L, key0;
-    int e_first, n_ent;  // SPARSE: the tile's step list
   };
   struct Tile : Entry {
+    int e_first;  // SPARSE: the tile's step list starts here (n_steps entries)
     int rows_total, qs_lo, n_steps, n_mask, n_hi;
     const uint16_t* qbase;
     const uint16_t* dobase;
@@ -743,12 +765,6 @@ dkdv_kernel(KvParams P) {
     E.key0 = sload(P.tiles + 4 * ti + 2) * C::BN;
     E.kv0 = sload(P.offsets + E.b);
     E.L = sload(P.offsets + E.b + 1) - E.kv0;
-    E.e_first = E.n_ent = 0;
-    if (SPARSE) {
-      const int u = sload(P.sp_base + E.b) + E.key0 / C::BN;
-      E.e_first = sload(P.sp_ptr + u);
-      E.n_ent = sload(P.sp_ptr + u + 1) - E.e_first;
-    }
     return E;
   };
   auto tile_of = [&](const Entry& E) {
@@ -770,7 +786,12 @@ dkdv_kernel(KvParams P) {
     // zeros and contribute nothing)
     T.n_mask = CAUSAL ? min(T.n_steps, C::BN / C::BM) : 0;
     T.n_hi = WIN ? max(0, (T.key0 + P.window) / C::BM - T.qs_lo) : T.n_steps;
-    if (SPARSE) T.n_steps = T.n_hi = T.n_ent;  // may be 0
+    T.e_first = 0;
+    if (SPARSE) {  // the tile's step list (possibly empty)
+      const int u = sload(P.sp_base + T.b) + T.key0 / C::BN;
+      T.e_first = sload(P.sp_ptr + u);
+      T.n_steps = T.n_hi = sload(P.sp_ptr + u + 1) - T.e_first;
+    }
     return T;
   };
   // SPARSE: entry st of a tile's step list
@@ -833,7 +854,6 @@ dkdv_kernel(KvParams P) {
       Entry En{};
       if (ti + 1 < t_end) En = entry_of(ti + 1);
       asm volatile("" : "+v"(En.b), "+v"(En.h), "+v"(En.kv0), "+v"(En.L), "+v"(En.key0));
-      if (SPARSE) asm volatile("" : "+v"(En.e_first), "+v"(En.n_ent));
       const int row0 = T.key0 + kw * 32;
       const int jw = row0 + li;  // this lane's key
       // lane-dependent addresses are derived afresh for each tile (otherwise the
@@ -887,37 +907,39 @@ dkdv_kernel(KvParams P) {
         __syncthreads();
         // each role's MFMA section runs at raised priority, its VALU section at
         // the normal one
+        // SPARSE: whether the pair's key block pairs with the query block of this
+        // step (cur) and of the previous one (was); the others are skipped
+        const bool cur = !SPARSE || ((sp_entry(T, it) >> (jfa::kSpBit + kw / 2)) & 1);
+        const bool was = prev && (!SPARSE || ((sp_entry(T, it - 1) >> (jfa::kSpBit + kw / 2)) & 1));
         if (PW) {
           __builtin_amdgcn_s_setprio(1);
-          kv_scores<D, S>(ad, op, s);
+          if (cur) kv_scores<D, S>(ad, op, s);
           if (EARLY && it + 1 == T.n_steps) next_op();
-          if (prev) kv_products<D, SP>(ad, pk, acc);
+          if (was) kv_products<D, SP>(ad, pk, acc);
           __builtin_amdgcn_s_setprio(0);
           // the P waves issue their share of the next stage's loads after their
           // products, the dS waves at the start of the step: the buffer->LDS
           // traffic is spread over the step
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
           const int q0 = (T.qs_lo + it) * C::BM;
-          if (CAUSAL && (it < T.n_mask || (WIN && it >= T.n_hi)))
-            kv_probs<D, true, WIN>(s, P.c, g, q0, jw, pk, P.window);
-          else
-            kv_probs<D, false>(s, P.c, g, q0, jw, pk);
-          if (SPARSE && !((sp_entry(T, it) >> (jfa::kSpBit + kw / 2)) & 1)) {
-#pragma unroll
-            for (int x = 0; x < C::PK; ++x) pk[x] = u32x4{0, 0, 0, 0};
+          if (cur) {
+            if (CAUSAL && (it < T.n_mask || (WIN && it >= T.n_hi)))
+              kv_probs<D, true, WIN>(s, P.c, g, q0, jw, pk, P.window);
+            else
+              kv_probs<D, false>(s, P.c, g, q0, jw, pk);
+            xch_put<D, S>(ad, pk);
           }
-          xch_put<D, S>(ad, pk);
         } else {
-          if (prev) {
+          if (was) {
             u32x4 pp[C::PK];
             xch_get<D, SP>(ad, pp);
             kv_dsoft<D>(s, pp, pk);
           }
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
           __builtin_amdgcn_s_setprio(1);
-          kv_scores<D, S>(ad, op, s);
+          if (cur) kv_scores<D, S>(ad, op, s);
           if (EARLY && it + 1 == T.n_steps) next_op();
-          if (prev) kv_products<D, SP>(ad, pk, acc);
+          if (was) kv_products<D, SP>(ad, pk, acc);
           __builtin_amdgcn_s_setprio(0);
         }
       };
@@ -925,6 +947,10 @@ dkdv_kernel(KvParams P) {
       auto tail = [&](auto stage) {
         constexpr int S = decltype(stage)::value;
         __syncthreads();
+        // SPARSE: no query block attends the tile's keys (no step): zero dK, dV
+        if (SPARSE && (T.n_steps == 0 ||
+                       !((sp_entry(T, T.n_steps - 1) >> (jfa::kSpBit + kw / 2)) & 1)))
+          return;
         if (PW) {
           kv_products<D, S>(ad, pk, acc);
         } else {
@@ -949,10 +975,6 @@ dkdv_kernel(KvParams P) {
         }
         next_op();
         __syncthreads();  // the tail's barrier
-      } else if (SPARSE && T.n_steps == 0) {
-        // no query block attends the tile's keys: zero dK and dV
-        next_op();
-        __syncthreads();  // the tail's barrier
       } else {
         for (int it = 0; it < T.n_steps; it += 3) {
           step(it, S0{});
@@ -960,7 +982,7 @@ dkdv_kernel(KvParams P) {
           if (it + 2 < T.n_steps) step(it + 2, S2{});
         }
         if (!EARLY) next_op();
-        const int last = (T.n_steps - 1) % C::NS;
+        const int last = (T.n_steps - 1) % C::NS;  // -1 (the last branch) with no step
         if (last == 0) tail(S0{});
         else if (last == 1) tail(S1{});
         else tail(S2{});
@@ -969,7 +991,7 @@ dkdv_kernel(KvParams P) {
       const Tile Tc = T;
       if (ti + 1 < t_end) {
         T = tile_of(Entry{uniform(En.b), uniform(En.h), uniform(En.kv0), uniform(En.L),
-                          uniform(En.key0), uniform(En.e_first), uniform(En.n_ent)});
+                          uniform(En.key0)});
         if (!SPARSE || T.n_steps > 0) load_stage(T, 0);
       }
       // output rows staged in ring stages 1 and 2 (stage 0 is filling); the next
