@@ -485,6 +485,8 @@ def main():
         vb = T * w.num_heads * 4
         if w.kind == "block":
             tag = f"block{w.block}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
+        if w.kind == "sparse":
+            tag = f"sparse_d{w.head_dim}"
         if r["block"]:
             cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))
