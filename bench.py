@@ -321,7 +321,10 @@ def main():
                              "block64_d128", "block64_rope_d64", "block64_rope_d128", "gem_rope",
                              "gem_window", "block32_d128", "block128_d128", "block256_d128",
                              "imbalance", "gem_padded", "sparse_d128", "sparse_d64"])
-    ap.add_argument("--order", default="folded", choices=["zigzag", "inorder", "xcd", "folded"])
+    ap.add_argument("--order", default="default",
+                    choices=["default", "zigzag", "inorder", "xcd", "folded"],
+                    help="dealing order; default: the plan's own (folded zigzag, in-order for "
+                         "block-sparse)")
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time forward + backward under every dealing order, interleaved")
     ap.add_argument("--compare-rope", action="store_true",
@@ -378,7 +381,7 @@ def main():
     do = J.to_torch_bf16(case.do).to(dev)
     ORDERS = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
               "xcd": jfa.ORDER_XCD_ZIGZAG, "folded": jfa.ORDER_FOLDED_ZIGZAG}
-    order = ORDERS[args.order]
+    order = ORDERS.get(args.order)  # None: the plan's default
 
     runs = []
     sched_ms = 0.0
@@ -406,9 +409,9 @@ def main():
                 t1 = time.perf_counter()
                 if plan.sparse:  # the step lists and the schedule built from them
                     lp = jfa.sparse_lists(plan.p, case.offsets, case.mask, kind)[1]
-                    jfa.schedule_sparse(plan.p, case.offsets, lp, kind, order, sc.num_slots)
+                    jfa.schedule_sparse(plan.p, case.offsets, lp, kind, plan.order, sc.num_slots)
                 else:
-                    jfa.schedule(plan.p, case.offsets, kind, order, sc.num_slots)
+                    jfa.schedule(plan.p, case.offsets, kind, plan.order, sc.num_slots)
                 jfa_schedule_ms += (time.perf_counter() - t1) * 1e3
         runs.append(dict(w=w, plan=plan, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
                          block=plan.block, fused_bwd=fused_bwd,
@@ -632,7 +635,8 @@ def main():
         "config": {"workload": args.workload, "B": w0.num_seqs, "H": w0.num_heads,
                    "D": w0.head_dim, "T": T, "lq": w0.lq,
                    "variants": [("causal" if w.causal else "noncausal") for w in variants],
-                   "order": args.order, "seed": args.seed,
+                   "order": {v_: k_ for k_, v_ in ORDERS.items()}[runs[0]["plan"].order],
+                   "seed": args.seed,
                    "flops_per_step": flops_step,
                    "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
                    "event_ms_per_step": round(float(ev_ms), 4),

@@ -64,7 +64,7 @@ def bf16_to_f64(t):
 class GpuRun:
     """Inputs uploaded once; fwd and bwd results copied back as float64."""
 
-    def __init__(self, case: J.Case, dev, order=jfa.ORDER_FOLDED_ZIGZAG, num_slots=None):
+    def __init__(self, case: J.Case, dev, order=None, num_slots=None):
         import torch
         w = case.w
         self.case = case
