@@ -35,9 +35,10 @@ Readings of points the pages leave open:
     section on generative models): each sequence is cut into 64-token blocks
     (the last one partial), and a boolean matrix per sequence says which key
     blocks each query block attends; query i attends key j of its own sequence
-    iff mask[i // 64][j // 64]. No causal rule inside. A query row whose blocks
-    allow no key gets out = 0 and lse = -inf and contributes nothing to the
-    gradients (the same convention as an empty broadcast sequence).
+    iff mask[i // 64][j // 64], and with causal also only if j <= i (the
+    generative-model case the GEM page names). A query row that keeps no key
+    gets out = 0 and lse = -inf and contributes nothing to the gradients (the
+    same convention as an empty broadcast sequence).
 
 Layouts: packed tensors are [T, H, D] (token-major, no padding) with int32
 offsets [B+1]; jagged lse is [H, T]; broadcast Q/dQ are [Lq, H, D], broadcast
@@ -196,7 +197,7 @@ def sparse_masks(offsets, flat):
     return masks
 
 
-def block_sparse_forward(q, k, v, offsets, scale, masks):
+def block_sparse_forward(q, k, v, offsets, scale, masks, causal=False):
     """Block-sparse self-attention: q/k/v [T,H,D], one block mask per sequence
     -> out [T,H,D], lse [H,T]."""
     T, H, D = q.shape
@@ -204,13 +205,13 @@ def block_sparse_forward(q, k, v, offsets, scale, masks):
     lse = np.full((H, T), -np.inf)
     for (s, e), bm in zip(_seqs(offsets), masks):
         for h in range(H):
-            o, l = seq_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale, bmask=bm)
+            o, l = seq_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale, causal, bmask=bm)
             out[s:e, h] = o
             lse[h, s:e] = l
     return out, lse
 
 
-def block_sparse_backward(q, k, v, do, offsets, scale, masks):
+def block_sparse_backward(q, k, v, do, offsets, scale, masks, causal=False):
     """Block-sparse self-attention gradients -> dq, dk, dv, each [T,H,D]."""
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -218,7 +219,8 @@ def block_sparse_backward(q, k, v, do, offsets, scale, masks):
     H = q.shape[1]
     for (s, e), bm in zip(_seqs(offsets), masks):
         for h in range(H):
-            a, b_, c = seq_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale, bmask=bm)
+            a, b_, c = seq_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale, causal,
+                                    bmask=bm)
             dq[s:e, h], dk[s:e, h], dv[s:e, h] = a, b_, c
     return dq, dk, dv
 
@@ -262,7 +264,13 @@ def pair_count(lengths, causal=False, lq=0, block=0, masks=None):
             rows = np.full(nb, SPARSE_BLOCK, dtype=np.int64)
             if nb:
                 rows[-1] = n - SPARSE_BLOCK * (nb - 1)
-            total += int(rows @ bm.astype(np.int64) @ rows)
+            if causal:
+                # below the diagonal blocks whole; on it the block's own causal count
+                m = np.tril(bm, -1).astype(np.int64)
+                total += int(rows @ m @ rows)
+                total += int(sum(int(r) * (int(r) + 1) // 2 for r, d in zip(rows, np.diag(bm)) if d))
+            else:
+                total += int(rows @ bm.astype(np.int64) @ rows)
         return total
     if block:
         return int(block * L.sum())

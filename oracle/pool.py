@@ -101,8 +101,8 @@ def oracle_sub(w, scale, q, k, v, do, loff, masks=None):
     """The oracle on one sub-batch: (out, lse or None, dq, dk, dv), as the oracle's
     whole-workload functions define them."""
     if w.kind == "sparse":
-        out, lse = A.block_sparse_forward(q, k, v, loff, scale, masks)
-        dq, dk, dv = A.block_sparse_backward(q, k, v, do, loff, scale, masks)
+        out, lse = A.block_sparse_forward(q, k, v, loff, scale, masks, w.causal)
+        dq, dk, dv = A.block_sparse_backward(q, k, v, do, loff, scale, masks, w.causal)
     elif w.kind == "broadcast":
         out, lse = A.broadcast_forward(q, k, v, loff, scale)
         dq, dk, dv = A.broadcast_backward(q, k, v, do, loff, scale)

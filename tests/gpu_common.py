@@ -105,8 +105,8 @@ def oracle_full(case: J.Case):
         dq, dk, dv = A.broadcast_backward(q, k, v, do, off, case.scale)
     elif w.kind == "sparse":
         masks = A.sparse_masks(off, case.mask)
-        out, lse = A.block_sparse_forward(q, k, v, off, case.scale, masks)
-        dq, dk, dv = A.block_sparse_backward(q, k, v, do, off, case.scale, masks)
+        out, lse = A.block_sparse_forward(q, k, v, off, case.scale, masks, w.causal)
+        dq, dk, dv = A.block_sparse_backward(q, k, v, do, off, case.scale, masks, w.causal)
     elif w.kind == "block" and w.rope_base:
         out = R.block_diag_rope_forward(q, k, v, off, case.scale, w.rope_base, w.block)
         dq, dk, dv = R.block_diag_rope_backward(q, k, v, do, off, case.scale, w.rope_base, w.block)

@@ -38,6 +38,8 @@ CASES = [
     J.custom([64, 192, 0, 128], 2, 64, seed=35, kind="block"),
     J.custom([128, 256, 0], 2, 64, seed=36, kind="block", block=128),
     J.custom([70, 1, 0, 200, 130], 2, 64, sigma=0.5, seed=37, kind="sparse", density=0.4),
+    J.custom([70, 1, 0, 200, 130], 2, 64, sigma=0.5, seed=38, kind="sparse", density=0.4,
+             causal=True),
 ]
 
 

@@ -189,3 +189,59 @@ def test_flat_masks_round_trip():
     assert all(np.array_equal(a, b) for a, b in zip(masks, back))
     with pytest.raises(ValueError):
         A.sparse_masks(off, flat[:-1])
+
+
+def _causal(off, keep):
+    T = int(off[-1])
+    seg = np.repeat(np.arange(len(off) - 1), np.diff(off))
+    pos = np.arange(T) - np.asarray(off)[seg]
+    return keep & (pos[None, :] <= pos[:, None])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_causal_sparse_matches_sdpa(seed):
+    """With causal, query i keeps key j iff its block mask allows the pair and
+    j <= i (every query block keeps its own block here, so every row has a key)."""
+    lengths = [1, 64, 65, 130, 200]
+    q, k, v, do, off, _ = case64(lengths, 2, 16, seed=seed + 20)
+    masks = rand_masks(lengths, seed + 20, density=0.4)
+    keep = _causal(off, token_mask(off, masks))
+    rows = np.arange(int(off[-1]))
+    o_ref, dq_ref, dk_ref, dv_ref = sdpa(q, k, v, do, keep, rows)
+    out, lse = A.block_sparse_forward(q, k, v, off, SC, masks, causal=True)
+    dq, dk, dv = A.block_sparse_backward(q, k, v, do, off, SC, masks, causal=True)
+    assert np.max(np.abs(out - o_ref)) <= 1e-12
+    for got, ref in ((dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
+        assert np.max(np.abs(got - ref)) <= 1e-11
+
+
+def test_causal_all_ones_is_plain_causal():
+    lengths = [1, 63, 64, 65, 190]
+    q, k, v, do, off, _ = case64(lengths, 2, 16, seed=21)
+    masks = [np.ones((-(-L // BLK),) * 2, dtype=bool) for L in lengths]
+    out, lse = A.block_sparse_forward(q, k, v, off, SC, masks, causal=True)
+    o2, l2 = A.jagged_forward(q, k, v, off, SC, True)
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+    for a, b in zip(A.block_sparse_backward(q, k, v, do, off, SC, masks, causal=True),
+                    A.jagged_backward(q, k, v, do, off, SC, True)):
+        assert np.array_equal(a, b)
+
+
+def test_causal_rows_without_keys():
+    """A query block whose own block and every earlier block are masked keeps no
+    key under causal (block 0 of a sequence whose mask row 0 is all zero)."""
+    lengths = [130]
+    q, k, v, do, off, _ = case64(lengths, 1, 8, seed=22)
+    bm = np.array([[0, 1, 1], [1, 1, 0], [0, 1, 1]], bool)
+    out, lse = A.block_sparse_forward(q, k, v, off, SC, [bm], causal=True)
+    dq, _, _ = A.block_sparse_backward(q, k, v, do, off, SC, [bm], causal=True)
+    assert np.all(out[:64] == 0) and np.all(np.isneginf(lse[:, :64])) and np.all(dq[:64] == 0)
+    assert np.all(np.isfinite(lse[:, 64:]))
+
+
+def test_causal_pair_count_is_the_expanded_mask():
+    lengths = [1, 64, 65, 130, 0, 200]
+    masks = rand_masks(lengths, 23, density=0.3, diag=False)
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    assert A.pair_count(lengths, causal=True, masks=masks) == \
+        int(_causal(off, token_mask(off, masks)).sum())
