@@ -49,10 +49,11 @@ def pairs_of(lengths, causal=False, lq=0, block=0, window=0):
     return int((L * L).sum())
 
 
-def sparse_pairs(lengths, flat_mask):
+def sparse_pairs(lengths, flat_mask, causal=False):
     """Attended pairs of block-sparse attention: for each sequence, the rows of
     every allowed (query block, key block) pair times its columns (64, or what the
-    partial last block holds)."""
+    partial last block holds); with causal only the pairs below the block diagonal
+    and, on it, each block's r(r+1)/2."""
     total, pos = 0, 0
     for n in np.asarray(lengths, dtype=np.int64):
         nb = -(-int(n) // 64)
@@ -61,13 +62,17 @@ def sparse_pairs(lengths, flat_mask):
         rows = np.full(nb, 64, dtype=np.int64)
         if nb:
             rows[-1] = int(n) - 64 * (nb - 1)
-        total += int(rows @ m @ rows)
+        if causal:
+            total += int(rows @ np.tril(m, -1) @ rows)
+            total += int(sum(int(r) * (int(r) + 1) // 2 for r, d in zip(rows, np.diag(m)) if d))
+        else:
+            total += int(rows @ m @ rows)
     return total
 
 
 def variants_of(name):
     wl = J.standard_workloads()
-    if name in ("gem", "gem_padded", "gem_rope"):
+    if name in ("gem", "gem_padded", "gem_rope", "sparse_d128"):
         return [wl[name], wl[name + "_causal"]]
     return [wl[name]]
 
@@ -125,7 +130,7 @@ def cpu_baseline(case, variants, pool, budget_s=16.0):
         done, dt = OP.time_sample(pool, w, case.scale, off, budget_s / len(variants))
         L = np.diff(off)[np.asarray(done, dtype=np.int64)]
         if w.kind == "sparse":
-            npairs = sum(sparse_pairs([n], J.sparse_mask_seq(w, int(b), int(n)).ravel())
+            npairs = sum(sparse_pairs([n], J.sparse_mask_seq(w, int(b), int(n)).ravel(), w.causal)
                          for b, n in zip(done, L))
         else:
             npairs = pairs_of(L, w.causal, w.lq, w.block if w.kind == "block" else 0, w.window)
@@ -394,7 +399,7 @@ def main():
         sched_ms += (time.perf_counter() - t0) * 1e3
         out, lse = plan.forward(q, k, v)
         dq, dk, dv = plan.backward(q, k, v, out, do, lse)
-        npairs = (sparse_pairs(case.lengths, case.mask) if w.kind == "sparse" else
+        npairs = (sparse_pairs(case.lengths, case.mask, w.causal) if w.kind == "sparse" else
                   pairs_of(case.lengths, w.causal, w.lq, w.block if w.kind == "block" else 0,
                            w.window))
         nhd = float(npairs) * w.num_heads * w.head_dim
@@ -489,7 +494,7 @@ def main():
         if w.kind == "block":
             tag = f"block{w.block}{'_rope' if w.rope_base else ''}_d{w.head_dim}"
         if w.kind == "sparse":
-            tag = f"sparse_d{w.head_dim}"
+            tag = f"sparse_d{w.head_dim}" + ("_causal" if w.causal else "")
         if r["block"]:
             cands.append((np.mean(r["fwd_ms"]), "block_fwd_kernel", tag, "hbm", 4.0 * tb))
             cands.append((np.mean(r["bwd_ms"]), "block_bwd_kernel", tag, "hbm", 8.0 * tb))

@@ -90,8 +90,8 @@ typedef enum jfa_status {
 #define JFA_BLOCK_DIAG  16u  /* block-diagonal self-attention with blocks of
                                 jfa_problem.block tokens (32, 64, 128 or 256) */
 #define JFA_BLOCK_SPARSE 32u /* block-sparse self-attention over 64-token blocks
-                                (jfa_problem.block = 64, no other flag): see the
-                                jfa_sparse_* entry points */
+                                (jfa_problem.block = 64; CAUSAL the only other
+                                flag): see the jfa_sparse_* entry points */
 
 /* schedule kinds and dealing orders */
 #define JFA_KIND_FWD 0
@@ -111,13 +111,14 @@ typedef struct jfa_problem {
   int32_t max_len;    /* >= every sequence length (checked by jfa_schedule_count) */
   int32_t lq;         /* BROADCAST_Q: rows of the dense Q (>= 1); otherwise 0 */
   uint32_t flags;     /* JFA_CAUSAL | JFA_BROADCAST_Q | JFA_BLOCK_DIAG64 | JFA_ROTARY |
-                         JFA_BLOCK_DIAG, or JFA_BLOCK_SPARSE alone */
+                         JFA_BLOCK_DIAG, or JFA_BLOCK_SPARSE [| JFA_CAUSAL] */
   int64_t total_kv;   /* T = offsets[B], tokens in the packed K/V */
   float scale;        /* softmax scale applied to Q K^T, finite and > 0 */
   float rope_base;    /* ROTARY: base of the rotary frequencies, finite, in (1, 1e9];
                          otherwise must be 0 */
   int32_t window;     /* CAUSAL only: W > 0 restricts query i to keys i - W < j <= i
-                         (a causal sliding window); 0 = no window */
+                         (a causal sliding window); 0 = no window; 0 with
+                         BLOCK_SPARSE */
   int32_t block;      /* BLOCK_DIAG: tokens per block, 32, 64, 128 or 256; with
                          BLOCK_DIAG64 alone 0 or 64; BLOCK_SPARSE: 64; otherwise 0 */
 } jfa_problem;
@@ -277,12 +278,13 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
  * generative models). Here each sequence b of L_b tokens is cut into
  * n_b = ceil(L_b / 64) blocks of 64 tokens (the last one partial) and an
  * n_b x n_b byte matrix says which key blocks each query block attends: query i
- * attends key j of its own sequence iff mask_b[i / 64][j / 64] != 0, with no
- * causal rule inside. The mask (host memory) holds every sequence's matrix
- * row-major (row = query block), concatenated in sequence order: sum of n_b^2
- * bytes. A query row whose blocks attend no key gets out = 0 and lse = -inf, and
- * adds nothing to the gradients. The problem has flags = JFA_BLOCK_SPARSE only,
- * block = 64; its tiles are those of jagged self-attention (jfa_schedule_count).
+ * attends key j of its own sequence iff mask_b[i / 64][j / 64] != 0, and with
+ * JFA_CAUSAL also j <= i (the block mask and the causal rule both hold). The mask
+ * (host memory) holds every sequence's matrix row-major (row = query block),
+ * concatenated in sequence order: sum of n_b^2 bytes. A query row that attends no
+ * key gets out = 0 and lse = -inf, and adds nothing to the gradients. The problem
+ * has flags = JFA_BLOCK_SPARSE, optionally | JFA_CAUSAL, block = 64, window = 0;
+ * its tiles are those of jagged self-attention (jfa_schedule_count).
  *
  * The kernels walk step lists built on the host from the mask. A unit is (b, t)
  * for each sequence b and tile index t (128 query rows for kind FWD, 128 keys for
@@ -293,7 +295,11 @@ jfa_status jfa_bwd_passes(const jfa_problem* p, const void* q, const void* k, co
  *                         block c; BWD: query block r), ascending; bit 28 set when
  *                         the unit's block 2t pairs with it (FWD: mask[2t][c];
  *                         BWD: mask[r][2t]), bit 29 likewise for block 2t+1.
- *                         Blocks paired with neither are left out. */
+ *                         With CAUSAL a bit is also cleared where the causal
+ *                         rule masks the whole block pair (FWD: bit 28 when
+ *                         c > 2t, bit 29 when c > 2t+1; BWD: bit 28 when r < 2t,
+ *                         bit 29 when r < 2t+1). Blocks paired with neither are
+ *                         left out. */
 typedef struct jfa_sparse_lists_dev {
   const int32_t* seq_base;  /* device copies of the arrays above, 4-byte aligned */
   const int32_t* list_ptr;

@@ -32,7 +32,8 @@ section 1):
               {64,128}, sigma 1; each query block attends its own key block and
               each other key block of its sequence with probability 0.3, about
               70% of the block pairs of a long sequence masked (the sparsity the
-              block-attention page reports for its workloads, section 1).
+              block-attention page reports for its workloads, section 1); at
+              D=128 also causal (the same masks, keys after the query dropped).
 """
 from __future__ import annotations
 
@@ -130,6 +131,9 @@ def standard_workloads():
                                 lo=1, hi=4096, density=0.3),
         "sparse_d64": Workload("sparse", 1152, 4, 64, 1.0, kind="sparse", law="uniform",
                                lo=1, hi=4096, density=0.3),
+        # the sparse_d128 batch (same seeds, values and masks) with causal masking
+        "sparse_d128_causal": Workload("sparse", 1152, 4, 128, 1.0, kind="sparse",
+                                       law="uniform", lo=1, hi=4096, density=0.3, causal=True),
     }
 
 

@@ -130,10 +130,19 @@ _MAPS = {}
 
 
 def _result(rdir, name):
-    key = (rdir, name)
+    """The stored result `name` of rdir, memory-mapped once per file: the key holds
+    the file's identity (inode, size, modification time), so a directory removed
+    and made again under the same path, or a file written anew, is mapped afresh."""
+    path = os.path.join(rdir, name + ".npy")
+    try:
+        st = os.stat(path)
+    except FileNotFoundError:
+        return None
+    key = (path, st.st_ino, st.st_size, st.st_mtime_ns)
     if key not in _MAPS:
-        path = os.path.join(rdir, name + ".npy")
-        _MAPS[key] = np.load(path, mmap_mode="r") if os.path.exists(path) else None
+        for old in [k for k in _MAPS if k[0] == path]:
+            del _MAPS[old]
+        _MAPS[key] = np.load(path, mmap_mode="r")
     return _MAPS[key]
 
 

@@ -47,15 +47,15 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def sparse_lists(lengths, masks, kind, tile_rows=128):
+def sparse_lists(lengths, masks, kind, tile_rows=128, causal=False):
     """Block-sparse step lists: (seq_base, list_ptr, entries) as int32 arrays.
 
     One list per (sequence b, tile t), in that order; tile t covers the blocks
     2t and 2t+1 (query blocks for KIND_FWD, key blocks for KIND_BWD). Its entries
     are the other side's blocks c, ascending, that pair with either: the block
     index plus bit 28 when block 2t pairs with c (FWD: masks[b][2t, c]; BWD:
-    masks[b][c, 2t]) and bit 29 for block 2t+1. seq_base[b] is the first list of
-    sequence b.
+    masks[b][c, 2t]) and bit 29 for block 2t+1. With causal a key block never
+    pairs with an earlier query block. seq_base[b] is the first list of sequence b.
     """
     seq_base, list_ptr, entries = [], [0], []
     for L, m in zip((int(x) for x in lengths), masks):
@@ -65,7 +65,8 @@ def sparse_lists(lengths, masks, kind, tile_rows=128):
             for c in range(n):
                 code = c
                 for i, blk in enumerate((2 * t, 2 * t + 1)):
-                    if blk < n and (m[blk, c] if kind == KIND_FWD else m[c, blk]):
+                    qb, kb = (blk, c) if kind == KIND_FWD else (c, blk)
+                    if blk < n and m[qb, kb] and not (causal and kb > qb):
                         code |= 1 << (SPARSE_BIT + i)
                 if code != c:
                     entries.append(code)

@@ -1,4 +1,5 @@
 import os
+import shutil
 import sys
 
 import pytest
@@ -40,3 +41,12 @@ def oracle_pool(gpu):
     yield p
     p.terminate()
     p.join()
+
+
+@pytest.fixture
+def result_dir(tmp_path):
+    """A directory for one test's result files (several GB for a full batch),
+    removed when the test ends, passed or not, so that a session's full-batch
+    tests do not fill the disk between them."""
+    yield str(tmp_path)
+    shutil.rmtree(tmp_path, ignore_errors=True)

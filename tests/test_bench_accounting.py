@@ -84,3 +84,17 @@ def test_block_sparse_pairs():
         i = np.arange(l)
         want += int(m[i[:, None] // 64, i[None, :] // 64].sum())
     assert bench.sparse_pairs(L, flat) == want == A.pair_count(L, masks=masks)
+
+
+def test_causal_block_sparse_pairs():
+    rng = np.random.default_rng(4)
+    L = LENGTHS
+    masks = [rng.random((-(-l // 64),) * 2) < 0.4 for l in L]
+    flat = np.concatenate([m.astype(np.uint8).ravel() for m in masks])
+    want = 0
+    for l, m in zip(L, masks):
+        i = np.arange(l)
+        keep = m[i[:, None] // 64, i[None, :] // 64] & (i[None, :] <= i[:, None])
+        want += int(keep.sum())
+    assert bench.sparse_pairs(L, flat, causal=True) == want == \
+        A.pair_count(L, causal=True, masks=masks)

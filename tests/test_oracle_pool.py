@@ -89,3 +89,20 @@ def test_pool_flags_nonfinite(workers, tmp_path):
     np.save(os.path.join(str(tmp_path), "out.npy"), out)
     r = P.compare(workers, w, case.scale, case.offsets, str(tmp_path))
     assert not r["finite"]
+
+
+def test_pool_maps_a_remade_directory_afresh(workers, tmp_path):
+    """Results of one workload stored, compared, the directory removed and made
+    again under the same path with another workload's results (another head
+    dimension): the workers must read the new files, not their maps of the old."""
+    import shutil
+    rdir = str(tmp_path / "res")
+    for w in (CASES[0].with_(head_dim=64), CASES[0].with_(head_dim=128, seed=41)):
+        os.makedirs(rdir)
+        case = J.make_case(w)
+        res = oracle_full(case)
+        _store(rdir, case, res, w)
+        for _ in range(2):  # every worker sees this directory at least once
+            r = P.compare(workers, w, case.scale, case.offsets, rdir, per_task=1)
+            assert r["finite"] and r["dk"] <= 2.0 ** -8 * float(np.abs(res[3]).max()) + 1e-12
+        shutil.rmtree(rdir)

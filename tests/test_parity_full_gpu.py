@@ -138,7 +138,7 @@ def _bits(t):
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_full(name, gpu, pool, tmp):
+def run_full(name, gpu, pool, rdir):
     """Every element of the workload's GPU results against the oracle."""
     from oracle import pool as OP
     w = J.standard_workloads()[name]
@@ -148,7 +148,6 @@ def run_full(name, gpu, pool, tmp):
     run = GpuRun(case, gpu)
     out, lse = run.forward()
     dq, dk, dv = run.backward()
-    rdir = str(tmp)
     for nm, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
         np.save(os.path.join(rdir, nm + ".npy"), _bits(t))
     if lse is not None:
@@ -177,8 +176,8 @@ def run_full(name, gpu, pool, tmp):
 @pytest.mark.parametrize("name", ["gem", "gem_causal", "broadcast", "block64_d64",
                                   "block64_d128", "block32_d128", "block128_d128",
                                   "block256_d128", "block64_rope_d64", "block64_rope_d128"])
-def test_every_element(gpu, oracle_pool, tmp_path, name):
-    run_full(name, gpu, oracle_pool, tmp_path)
+def test_every_element(gpu, oracle_pool, result_dir, name):
+    run_full(name, gpu, oracle_pool, result_dir)
 
 
 @pytest.mark.parametrize("name", ["gem_rope", "gem_rope_causal"])

@@ -95,9 +95,59 @@ def test_workload_masks_match_flat_draw():
         pos += nb * nb
 
 
+def test_hand_worked_causal_lists():
+    """The 130-token sequence of the hand-worked case with causal masking: the
+    forward drops key block 2 of query tile 0 (it lies after query block 0) and
+    the backward drops query block 0 of key tile 1 (it lies before key block 2),
+    which leaves that key tile an empty list."""
+    L = [130, 64]
+    masks = [np.array([[1, 0, 1], [0, 0, 0], [1, 1, 0]], bool), np.array([[1]], bool)]
+    p, off = _problem(L, flags=jfa.BLOCK_SPARSE | jfa.CAUSAL)
+    fwd = ([0, 2, 3], [0, 1, 3, 4], [0 | B28, 0 | B28, 1 | B28, 0 | B28])
+    bwd = ([0, 2, 3], [0, 2, 2, 3], [0 | B28, 2 | B28 | B29, 0 | B28])
+    for kind, want in ((jfa.KIND_FWD, fwd), (jfa.KIND_BWD, bwd)):
+        got = jfa.sparse_lists(p, off, _flat(masks), kind)
+        ref = R.sparse_lists(L, masks, kind, causal=True)
+        for g, r, w in zip(got, ref, want):
+            assert list(g) == list(r) == w, kind
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
+def test_causal_lists_are_the_lower_triangle(seed, kind):
+    """Causal lists equal the plain lists of the mask with the block pairs above
+    the diagonal cleared, and the reference's."""
+    rng = np.random.default_rng(200 + seed)
+    L = rng.integers(0, 900, size=30)
+    L[2] = 0
+    masks = _masks(L, 10 + seed, density=[0.4, 1.0][seed])
+    p, off = _problem(L, flags=jfa.BLOCK_SPARSE | jfa.CAUSAL)
+    got = jfa.sparse_lists(p, off, _flat(masks), kind)
+    ref = R.sparse_lists(L, masks, kind, causal=True)
+    tril = [np.tril(m) for m in masks]
+    pl, _ = _problem(L)
+    via = jfa.sparse_lists(pl, off, _flat(tril), kind)
+    for g, r, v in zip(got, ref, via):
+        assert np.array_equal(g, r) and np.array_equal(g, v)
+
+
+@pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
+def test_causal_sparse_schedule_equals_reference(kind):
+    w = J.standard_workloads()["sparse_d128_causal"].with_(num_seqs=300)
+    L = J.lengths(w)
+    masks = [J.sparse_mask_seq(w, b, int(n)).astype(bool) for b, n in enumerate(L)]
+    p, off = _problem(L, H=w.num_heads, flags=jfa.BLOCK_SPARSE | jfa.CAUSAL)
+    sb, lp, ent = jfa.sparse_lists(p, off, _flat(masks), kind)
+    for order in (jfa.ORDER_INORDER, jfa.ORDER_FOLDED_ZIGZAG):
+        sp, tl = jfa.schedule_sparse(p, off, lp, kind, order, 512)
+        sp2, tl2 = R.schedule(L, w.num_heads, kind, 128, order, 512, sparse_list_ptr=lp,
+                              causal=True)
+        assert np.array_equal(sp, sp2) and np.array_equal(tl, tl2)
+
+
 @pytest.mark.parametrize("kw,status", [
-    (dict(flags=jfa.BLOCK_SPARSE | jfa.CAUSAL), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BLOCK_SPARSE | jfa.ROTARY), jfa.ERR_UNSUPPORTED),
+    (dict(flags=jfa.BLOCK_SPARSE | jfa.BROADCAST_Q), jfa.ERR_UNSUPPORTED),
     (dict(flags=jfa.BLOCK_SPARSE, block=0), jfa.ERR_INVALID_ARG),
     (dict(flags=jfa.BLOCK_SPARSE, block=128), jfa.ERR_INVALID_ARG),
 ])

@@ -4,12 +4,13 @@ Small cases compare every element of out, lse, dQ, dK and dV with the fp64
 oracle: ragged lengths (1-token and empty sequences, partial last blocks,
 sequences of several query and key tiles), D = 64 and 128, masks from empty to
 full, query blocks that attend nothing (out 0, lse -inf, dQ 0) and key blocks
-that nobody attends (dK = dV = 0). Identities: an all-ones mask gives the plain
-non-causal kernels' results bit for bit (the same steps in the same order); a
-diagonal mask gives the block-diagonal mode's results within rounding. The
-benchmark's batch (B = 1152, L ~ U{1..4096}, density 0.3, D = 128 and 64), in
-its launch configuration, is compared element by element in full against the
-oracle run by the worker pool."""
+that nobody attends (dK = dV = 0), each with and without causal masking.
+Identities: an all-ones mask gives the plain kernels' results bit for bit, causal
+or not (the same steps in the same order); a diagonal mask gives the
+block-diagonal mode's results within rounding. The benchmark's batches (B = 1152,
+L ~ U{1..4096}, density 0.3, D = 128 and 64, and D = 128 causal), in their launch
+configuration, are compared element by element in full against the oracle run
+by the worker pool."""
 import numpy as np
 import pytest
 
@@ -50,8 +51,9 @@ def _run(case, gpu):
     return out, lse, dq, dk, dv
 
 
-def _case_with_mask(lengths, D, seed, mask_fn):
-    w = J.custom(lengths, 2, D, sigma=1.0, seed=seed, kind="sparse", density=0.3)
+def _case_with_mask(lengths, D, seed, mask_fn, causal=False):
+    w = J.custom(lengths, 2, D, sigma=1.0, seed=seed, kind="sparse", density=0.3,
+                 causal=causal)
     c = J.make_case(w)
     parts, pos = [], 0
     for b, n in enumerate(c.lengths):
@@ -64,17 +66,19 @@ def _case_with_mask(lengths, D, seed, mask_fn):
 LENGTHS = [1, 0, 64, 65, 130, 200, 333, 511]
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("density", [0.0, 0.3, 1.0])
-def test_random_masks(gpu, D, density):
+def test_random_masks(gpu, D, density, causal):
     rng = np.random.default_rng(int(density * 10) + D)
-    case = _case_with_mask(LENGTHS, D, 5, lambda b, n: rng.random((n, n)) < density)
-    log(f"sparse D={D} density={density}: lengths {LENGTHS}")
+    case = _case_with_mask(LENGTHS, D, 5, lambda b, n: rng.random((n, n)) < density, causal)
+    log(f"sparse D={D} density={density} causal={causal}: lengths {LENGTHS}")
     _check(case, oracle_full(case), _run(case, gpu))
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
-def test_empty_rows_and_columns(gpu, D):
+def test_empty_rows_and_columns(gpu, D, causal):
     """Query blocks with no key (out 0, lse -inf, dQ 0) and key blocks nobody
     attends (dK = dV = 0), on top of a random pattern."""
     rng = np.random.default_rng(9)
@@ -85,7 +89,7 @@ def test_empty_rows_and_columns(gpu, D):
             m[1, :] = False      # query block 1 attends nothing
             m[:, n - 1] = False  # the last key block is attended by nobody
         return m
-    case = _case_with_mask([130, 300, 64, 511], D, 6, mask)
+    case = _case_with_mask([130, 300, 64, 511], D, 6, mask, causal)
     res = oracle_full(case)
     g = _run(case, gpu)
     _check(case, res, g)
@@ -98,11 +102,12 @@ def test_empty_rows_and_columns(gpu, D):
             assert np.all(dk[s:int(off[b + 1])] == 0) and np.all(dv[s:int(off[b + 1])] == 0)
 
 
-def test_all_ones_mask_is_the_plain_kernels_bitwise(gpu):
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_mask_is_the_plain_kernels_bitwise(gpu, causal):
     import torch
-    case = _case_with_mask(LENGTHS, 128, 7, lambda b, n: np.ones((n, n), bool))
+    case = _case_with_mask(LENGTHS, 128, 7, lambda b, n: np.ones((n, n), bool), causal)
     gs = _run(case, gpu)
-    plain = J.custom(LENGTHS, 2, 128, sigma=1.0, seed=7)
+    plain = J.custom(LENGTHS, 2, 128, sigma=1.0, seed=7, causal=causal)
     cp = J.make_case(plain)
     assert np.array_equal(cp.q, case.q) and np.array_equal(cp.do, case.do)
     gp = _run(cp, gpu)
@@ -124,8 +129,8 @@ def test_diagonal_mask_is_block_diagonal(gpu):
         assert max_abs(a, b) <= (OUT_TOL if nm == "out" else GRAD_TOL * m)
 
 
-@pytest.mark.parametrize("name", ["sparse_d128", "sparse_d64"])
-def test_every_element_benchmark_batch(gpu, oracle_pool, tmp_path, name):
+@pytest.mark.parametrize("name", ["sparse_d128", "sparse_d64", "sparse_d128_causal"])
+def test_every_element_benchmark_batch(gpu, oracle_pool, result_dir, name):
     """Every element of out, lse, dQ, dK and dV of the benchmark's batch."""
     from tests.test_parity_full_gpu import _bits
     from oracle import pool as OP
@@ -135,7 +140,7 @@ def test_every_element_benchmark_batch(gpu, oracle_pool, tmp_path, name):
     case = J.make_case(w)
     log(f"{name} every element: B={w.num_seqs} T={int(case.offsets[-1])}")
     out, lse, dq, dk, dv = _run(case, gpu)
-    rdir = str(tmp_path)
+    rdir = result_dir
     for nm, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
         np.save(os.path.join(rdir, nm + ".npy"), _bits(t))
     np.save(os.path.join(rdir, "lse.npy"), lse.cpu().numpy())

@@ -274,8 +274,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
         __builtin_amdgcn_s_setprio(1);
         dq_scores<D>(ks_of(kt), lo, qf, dof, ndi, s, dp);
         __builtin_amdgcn_s_setprio(0);
-        dq_softmax<D, true, false, false>(s, dp, lse2, c, g, key_of(kt), nk, qpos, pds, 0, lo, pds,
-                                          acc);
+        dq_softmax<D, true, CAUSAL, false>(s, dp, lse2, c, g, key_of(kt), nk, qpos, pds, 0, lo,
+                                           pds, acc);
         dq_accumulate<D>(ks_of(kt), lo, pds, acc);
       }
     }
@@ -921,7 +921,8 @@ dkdv_kernel(KvParams P) {
           // products, the dS waves at the start of the step: the buffer->LDS
           // traffic is spread over the step
           if (it + 1 < T.n_steps) load_stage(T, it + 1);
-          const int q0 = (T.qs_lo + it) * C::BM;
+          const int q0 = SPARSE ? (sp_entry(T, it) & jfa::kSpIdx) * jfa::kSpBlock
+                                : (T.qs_lo + it) * C::BM;
           if (cur) {
             if (CAUSAL && (it < T.n_mask || (WIN && it >= T.n_hi)))
               kv_probs<D, true, WIN>(s, P.c, g, q0, jw, pk, P.window);
@@ -1107,7 +1108,9 @@ jfa_status launch_bwd_d(const BwdLaunch& a) {
   const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, rope = a.rope != nullptr,
              win = a.window > 0;
   if (bq) return launch_t<D, false, true, false, false>(a);
-  if (a.flags & JFA_BLOCK_SPARSE) return launch_t<D, false, false, false, false, true>(a);
+  if (a.flags & JFA_BLOCK_SPARSE)
+    return causal ? launch_t<D, true, false, false, false, true>(a)
+                  : launch_t<D, false, false, false, false, true>(a);
   if (win)  // a window comes with CAUSAL
     return rope ? launch_t<D, true, false, true, true>(a) : launch_t<D, true, false, false, true>(a);
   if (rope)

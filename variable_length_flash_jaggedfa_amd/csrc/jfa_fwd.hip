@@ -445,9 +445,11 @@ namespace jfa {
 
 jfa_status launch_fwd(const FwdLaunch& a) {
   const bool causal = a.flags & JFA_CAUSAL, bq = a.flags & JFA_BROADCAST_Q, win = a.window > 0;
-  if (a.flags & JFA_BLOCK_SPARSE)
-    return a.head_dim == 128 ? launch_t<128, false, false, false, true>(a)
-                             : launch_t<64, false, false, false, true>(a);
+  if (a.flags & JFA_BLOCK_SPARSE) {
+    if (a.head_dim == 128)
+      return causal ? launch_t<128, true, false, false, true>(a) : launch_t<128, false, false, false, true>(a);
+    return causal ? launch_t<64, true, false, false, true>(a) : launch_t<64, false, false, false, true>(a);
+  }
   if (a.head_dim == 128) {
     if (bq) return launch_t<128, false, true, false>(a);
     if (win) return launch_t<128, true, false, true>(a);

@@ -42,8 +42,9 @@ jfa_status check_problem(const jfa_problem* p) {
   if (causal && bq) return fail(JFA_ERR_UNSUPPORTED, "CAUSAL with BROADCAST_Q");
   if (blk && (causal || bq)) return fail(JFA_ERR_UNSUPPORTED, "block-diagonal with other flags");
   if (p->flags & JFA_BLOCK_SPARSE) {
-    if (p->flags != JFA_BLOCK_SPARSE)
-      return fail(JFA_ERR_UNSUPPORTED, "BLOCK_SPARSE combines with no other flag");
+    if (p->flags & ~(JFA_BLOCK_SPARSE | JFA_CAUSAL))
+      return fail(JFA_ERR_UNSUPPORTED, "BLOCK_SPARSE combines with CAUSAL only");
+    if (p->window != 0) return fail(JFA_ERR_UNSUPPORTED, "BLOCK_SPARSE with a sliding window");
     if (p->block != kSpBlock) return fail(JFA_ERR_INVALID_ARG, "BLOCK_SPARSE needs block = 64");
   } else if (p->flags & JFA_BLOCK_DIAG) {
     if (p->block != 32 && p->block != 64 && p->block != 128 && p->block != 256)
@@ -264,6 +265,7 @@ void sparse_lists(const jfa_problem* p, const int32_t* off, const uint8_t* mask,
                   int32_t* seq_base, int32_t* list_ptr, int32_t* entries, int64_t* n_units,
                   int64_t* n_entries) {
   const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);  // two 64-token blocks
+  const bool causal = p->flags & JFA_CAUSAL;  // no key block after the query block
   int64_t u = 0, e = 0, m0 = 0;
   if (list_ptr) list_ptr[0] = 0;
   for (int32_t b = 0; b < p->num_seqs; ++b) {
@@ -274,8 +276,10 @@ void sparse_lists(const jfa_problem* p, const int32_t* off, const uint8_t* mask,
       const int64_t a0 = 2 * t, a1 = 2 * t + 1;  // the unit's two blocks
       for (int64_t c = 0; c < n; ++c) {
         // FWD: key block c for query blocks a0, a1; BWD: query block c for key blocks a0, a1
-        const bool x0 = kind == JFA_KIND_FWD ? mb[a0 * n + c] : mb[c * n + a0];
-        const bool x1 = a1 < n && (kind == JFA_KIND_FWD ? mb[a1 * n + c] : mb[c * n + a1]);
+        const bool fwd = kind == JFA_KIND_FWD;
+        const bool x0 = (fwd ? mb[a0 * n + c] : mb[c * n + a0]) && !(causal && (fwd ? c > a0 : c < a0));
+        const bool x1 = a1 < n && (fwd ? mb[a1 * n + c] : mb[c * n + a1]) &&
+                        !(causal && (fwd ? c > a1 : c < a1));
         if (!x0 && !x1) continue;
         if (entries) entries[e] = int32_t(c) | (int32_t(x0) << kSpBit) | (int32_t(x1) << (kSpBit + 1));
         ++e;
