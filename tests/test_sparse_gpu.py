@@ -103,6 +103,18 @@ def test_empty_rows_and_columns(gpu, D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_lists_longer_than_64_blocks(gpu, causal):
+    """Sequences of more than 64 blocks (4096 tokens), dense enough that a tile's
+    list holds more than 64 entries: the kernels read a tile's entries 64 at a
+    time."""
+    rng = np.random.default_rng(31)
+    L = [4500, 70, 4353]
+    case = _case_with_mask(L, 128, 11, lambda b, n: rng.random((n, n)) < 0.8, causal)
+    log(f"sparse long lists causal={causal}: lengths {L}")
+    _check(case, oracle_full(case), _run(case, gpu))
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_mask_is_the_plain_kernels_bitwise(gpu, causal):
     import torch
     case = _case_with_mask(LENGTHS, 128, 7, lambda b, n: np.ones((n, n), bool), causal)

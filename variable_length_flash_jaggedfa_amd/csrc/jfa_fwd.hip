@@ -216,6 +216,42 @@ __device__ __forceinline__ void wait_vmem_le() {
 // key blocks its step list names, in ascending order, instead of the whole
 // sequence; every step is masked, a wave's scores wholly when its query block
 // does not attend the step's key block, and past the sequence end.
+// Block-sparse: the key blocks one query block of a tile attends, in list order:
+// the tile's entries that carry the block's bit, read 64 at a time (one per lane)
+// and taken from the ballot of that bit.
+struct BlockWalk {
+  const int32_t* ent;  // the tile's entries
+  int n_ent, bit, lane;
+  int base;            // index of the loaded chunk's first entry
+  uint64_t left;       // entries of the chunk with the bit, not yet taken
+  int v;               // the lane's entry of the chunk
+  __device__ __forceinline__ void load(int b0) {
+    base = b0;
+    const int e = b0 + lane;
+    v = e < n_ent ? ent[e] : 0;
+    left = __builtin_amdgcn_ballot_w64((v >> bit) & 1);
+  }
+  // the next key block (only called while one is left; block 0 past the list)
+  __device__ __forceinline__ int next() {
+    while (left == 0 && base + 64 < n_ent) load(base + 64);
+    if (left == 0) return 0;
+    const int i = __builtin_ctzll(left);
+    left &= left - 1;
+    return __builtin_amdgcn_readlane(v, i) & jfa::kSpIdx;
+  }
+};
+
+// Number of the tile's entries that carry bit `bit` (uniform).
+__device__ __forceinline__ int count_bit(const int32_t* ent, int n_ent, int bit, int lane) {
+  int n = 0;
+  for (int b0 = 0; b0 < n_ent; b0 += 64) {
+    const int e = b0 + lane;
+    const int v = e < n_ent ? ent[e] : 0;
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64((v >> bit) & 1));
+  }
+  return n;
+}
+
 template <int D, bool CAUSAL, bool BCAST, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
@@ -300,13 +336,60 @@ fwd_kernel(FwdParams P) {
       for (int d = 0; d < C::DS; ++d)
         qf[d] = ok ? ld16(P.q + qrow * rstride + int64_t(h) * D + d * 16 + g * 8) : u32x4{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st)
-      if (st < n_steps) load_stage(st);
     f32x16 o[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x16{};
     float m = -INFINITY, l = 0.f;
+
+    if (SPARSE) {
+      // The wave pair p = w / 2 holds query block 2t + p (rows 64p .. 64p + 63 of
+      // the tile) and walks only the key blocks that block attends, SPB steps
+      // each, on ring stages 2p and 2p + 1; the two pairs meet at every step's
+      // barrier. A step: wait for the pair's stage, barrier (every wave is done
+      // with the previous step, whose stages the next loads reuse), load the
+      // pair's next step, then the scores, mask, row max, probabilities and
+      // products of this one.
+      const int pr = w >> 1, wp = w & 1;
+      const int32_t* ent = P.sp_ent + e_first;
+      const int n0 = count_bit(ent, n_ent, jfa::kSpBit, lane) * SPB;
+      const int n1 = count_bit(ent, n_ent, jfa::kSpBit + 1, lane) * SPB;
+      const int n_all = max(n0, n1), n_mine = pr ? n1 : n0;
+      const bool own = CAUSAL || w * 32 < q_rows;  // the wave holds rows of the tile
+      BlockWalk walk{ent, n_ent, jfa::kSpBit + pr, lane, 0, 0, 0};
+      walk.load(0);
+      auto load_pair = [&](int st, int key) {
+        uint16_t* buf = lds + (2 * pr + (st & 1)) * C::STAGE;
+        const int64_t r0 = int64_t(key) * rstride;
+        tile_load<D, C::BN, 2>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, Lk - key), rowbytes, wp,
+                               lane);
+        tile_load<D, C::BN, 2>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, Lk - key),
+                               rowbytes, wp, lane);
+      };
+      int blk = n_mine > 0 ? walk.next() : 0;
+      if (n_mine > 0) load_pair(0, blk * jfa::kSpBlock);
+      for (int st = 0; st < n_all; ++st) {
+        wait_vmem();
+        __syncthreads();
+        const int key = blk * jfa::kSpBlock + (st % SPB) * C::BN;
+        if (st + 1 < n_mine) {
+          if ((st + 1) % SPB == 0) blk = walk.next();
+          load_pair(st + 1, blk * jfa::kSpBlock + ((st + 1) % SPB) * C::BN);
+        }
+        if (st < n_mine && own) {
+          const uint16_t* stage = lds + (2 * pr + (st & 1)) * C::STAGE;
+          f32x16 sc[C::KB], sn[C::KB];
+          scores<D>(stage, qf, sc, li, g);
+          mask_scores<D, CAUSAL, false>(sc, g, key, L, qm, 0);
+          const float mx = pair_max(row_max<D>(sc)) * P.c;
+          update_max<D>(mx, m, l, o);
+          fwd_step<D, false, false, CAUSAL, false>(stage + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
+                                                   lane, 0, L, qm, 0);
+        }
+      }
+    } else {
+#pragma unroll
+    for (int st = 0; st < C::NS - 1; ++st)
+      if (st < n_steps) load_stage(st);
 
     if (n_steps > 0) {
       // first step's scores: wait for stage 0 only
@@ -377,6 +460,7 @@ fwd_kernel(FwdParams P) {
                                         lane, 0, n_keys, qm, P.window);
       if (!CAUSAL)
         for (; kt + 1 < n_steps; ++kt) advance(kt);  // the steps this wave leaves out
+    }
     }
 
     // epilogue: out = O / l (bf16) through the wave's LDS staging tile, lse =
