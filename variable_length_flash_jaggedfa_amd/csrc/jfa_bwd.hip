@@ -30,6 +30,7 @@
 
 #include "jfa_internal.h"
 #include "jfa_rope.h"
+#include "jfa_sparse.h"
 #include "jfa_tiles.h"
 
 using namespace jfa_dev;
@@ -73,28 +74,6 @@ struct DqParams {
   int32_t window;             // causal sliding window (WIN kernels)
   jfa::RopeTab rope;          // rotary kernels only
   const int32_t* sp_base; const int32_t* sp_ptr; const int32_t* sp_ent;  // SPARSE kernels
-};
-
-// Keys of a dQ-pass stream. Dense: step st covers keys [st*BN, st*BN + BN) and
-// the masks count n_keys keys. Block-sparse: step st lies in the key block that
-// entry st / SPB of the tile's list names, and a wave whose query block (entry
-// bit `bit`) does not attend it masks every key of the step.
-template <int BN>
-struct StreamKeys {
-  const int32_t* ent;  // SPARSE: the tile's entries
-  int n_keys;          // keys the masks count (dense), sequence length (sparse)
-  int bit;             // SPARSE: kSpBit + the wave's query block in the tile
-  template <bool SPARSE>
-  __device__ __forceinline__ int key(int st) const {
-    if (!SPARSE) return st * BN;
-    constexpr int SPB = jfa::kSpBlock / BN;
-    return (sload(ent + st / SPB) & jfa::kSpIdx) * jfa::kSpBlock + (st % SPB) * BN;
-  }
-  template <bool SPARSE>
-  __device__ __forceinline__ int count(int st) const {
-    if (!SPARSE) return n_keys;
-    return (sload(ent + st / (jfa::kSpBlock / BN)) >> bit) & 1 ? n_keys : 0;
-  }
 };
 
 // S^T = K Q^T and dP^T - Di = V dO^T - Di for one step of BN keys (lane = query
@@ -205,37 +184,34 @@ __device__ __forceinline__ void dq_softmax(const f32x16 (&s)[DqCfg<D>::KB],
 template <int D, int NW>
 __device__ __forceinline__ void dq_load_stage(uint16_t* lds, const uint16_t* kbase,
                                               const uint16_t* vbase, int64_t rstride, int L, int st,
-                                              int key, int w, int lane) {
+                                              int w, int lane) {
   using C = DqCfg<D, NW>;
   uint16_t* buf = lds + (st % C::NS) * C::STAGE;
-  const int64_t r0 = int64_t(key) * rstride;
+  const int64_t r0 = int64_t(st) * C::BN * rstride;
   const int rowbytes = int(rstride * 2);
-  tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - key), rowbytes, w,
-                             lane);
-  tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - key),
+  tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - st * C::BN), rowbytes,
+                             w, lane);
+  tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - st * C::BN),
                              rowbytes, w, lane);
 }
 
 // The first NS - 2 stages of a key stream, issued ahead of dq_stream<..., true>
 // so that their latency overlaps the caller's own loads (the query rows).
-template <int D, int NW, bool SPARSE = false>
+template <int D, int NW>
 __device__ __forceinline__ void dq_stream_issue(uint16_t* lds, const uint16_t* kbase,
                                                 const uint16_t* vbase, int64_t rstride, int L,
-                                                int n_steps, const StreamKeys<DqCfg<D, NW>::BN>& ks,
-                                                int w, int lane) {
+                                                int n_keys, int w, int lane) {
   using C = DqCfg<D, NW>;
+  const int n_steps = ceil_div(n_keys, C::BN);
 #pragma unroll
   for (int st = 0; st < C::NS - 2; ++st)
-    if (st < n_steps)
-      dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, ks.template key<SPARSE>(st), w, lane);
+    if (st < n_steps) dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
 }
 
-template <int D, bool CAUSAL, bool WIN = false, int NW = DqCfg<D>::NW, bool PRE = false,
-          bool SPARSE = false>
+template <int D, bool CAUSAL, bool WIN = false, int NW = DqCfg<D>::NW, bool PRE = false>
 __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, const uint16_t* vbase,
-                                          int64_t rstride, int L, int n_steps,
-                                          const StreamKeys<DqCfg<D, NW>::BN>& ks, int n_lo,
-                                          int n_free, int n_own, int win,
+                                          int64_t rstride, int L, int n_keys, int n_lo, int n_free,
+                                          int n_own, int win,
                                           const u32x4 (&qf)[DqCfg<D>::DS],
                                           const u32x4 (&dof)[DqCfg<D>::DS],
                                           f32x16 (&acc)[DqCfg<D>::NB], float lse2, float di,
@@ -244,11 +220,10 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
   using C = DqCfg<D, NW>;
   static_assert(C::NS == 4, "the ring below assumes four stages");
   const int g = lane >> 5;
+  const int n_steps = ceil_div(n_keys, C::BN);
   const uint32_t lds0 = lds_addr(lds);
-  auto key_of = [&](int st) { return ks.template key<SPARSE>(st); };
-  auto count_of = [&](int st) { return ks.template count<SPARSE>(st); };
   auto load_stage = [&](int st) {
-    dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, key_of(st), w, lane);
+    dq_load_stage<D, NW>(lds, kbase, vbase, rstride, L, st, w, lane);
   };
   auto ks_of = [&](int st) { return lds0 + uint32_t((st % C::NS) * C::STAGE * 2); };
   auto arrive = [&](int st) {
@@ -256,30 +231,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     else wait_vmem();
     __syncthreads();
   };
-  if (!PRE) dq_stream_issue<D, NW, SPARSE>(lds, kbase, vbase, rstride, L, n_steps, ks, w, lane);
-  if (SPARSE) {
-    // Block-sparse: each step whole (S, dP, dS and the dQ products on the one
-    // stage); a wave whose query block does not attend the step's key block
-    // skips it, leaving its SIMD's matrix core to the other workgroup.
-    f32x16 s[C::KB], dp[C::KB];
-    u32x4 pds[2 * C::KB];
-    f32x16 ndi;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ndi[r] = -di;
-    for (int kt = 0; kt < n_steps; ++kt) {
-      arrive(kt);  // also: every wave is done with stage kt-1
-      if (kt + C::NS - 2 < n_steps) load_stage(kt + C::NS - 2);
-      const int nk = count_of(kt);
-      if (kt < n_own && nk > 0) {
-        __builtin_amdgcn_s_setprio(1);
-        dq_scores<D>(ks_of(kt), lo, qf, dof, ndi, s, dp);
-        __builtin_amdgcn_s_setprio(0);
-        dq_softmax<D, true, CAUSAL, false>(s, dp, lse2, c, g, key_of(kt), nk, qpos, pds, 0, lo,
-                                           pds, acc);
-        dq_accumulate<D>(ks_of(kt), lo, pds, acc);
-      }
-    }
-  } else if (n_steps > 0) {
+  if (!PRE) dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, n_keys, w, lane);
+  if (n_steps > 0) {
     f32x16 s[C::KB], dp[C::KB];
     u32x4 pds[2 * C::KB], pdv[2 * C::KB];
     f32x16 ndi;  // -Di of the lane's row, the first dP product's accumulator input
@@ -289,11 +242,11 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
     if (C::NS - 2 < n_steps) load_stage(C::NS - 2);
     dq_scores<D>(ks_of(0), lo, qf, dof, ndi, s, dp);
     if (n_lo > 0 || n_free == 0)
-      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, c, g, key_of(0), count_of(0), qpos,
-                                              pds, 0, lo, pdv, acc, win);
+      dq_softmax<D, true, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+                                              acc, win);
     else
-      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, ks.n_keys, qpos, pds, 0, lo,
-                                               pdv, acc, win);
+      dq_softmax<D, false, CAUSAL, false, WIN>(s, dp, lse2, c, g, 0, n_keys, qpos, pds, 0, lo, pdv,
+                                               acc, win);
     auto step = [&](int kt, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
@@ -306,8 +259,8 @@ __device__ __forceinline__ void dq_stream(uint16_t* lds, const uint16_t* kbase, 
       __builtin_amdgcn_s_setprio(1);
       dq_scores<D>(ks, lo, qf, dof, ndi, s, dp);
       __builtin_amdgcn_s_setprio(0);
-      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, c, g, key_of(kt), count_of(kt), qpos,
-                                             pds, ks_of(kt - 1), lo, pdv, acc, win);
+      dq_softmax<D, MASK, CAUSAL, true, WIN>(s, dp, lse2, c, g, kt * C::BN, n_keys, qpos, pds,
+                                             ks_of(kt - 1), lo, pdv, acc, win);
     };
     int kt = 1;
     if (WIN)
@@ -395,7 +348,6 @@ dq_kernel(DqParams P) {
     const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
     const int n_free =
         SPARSE ? 0 : max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
-    const StreamKeys<C::BN> ks{SPARSE ? P.sp_ent + e_first : nullptr, n_keys, jfa::kSpBit + w / 2};
     const int qpos = q_first + w * 32 + (lane & 31);
     const bool ok = qpos < L;
     // steps this wave computes: all, or one when the tile has no row for it
@@ -405,8 +357,37 @@ dq_kernel(DqParams P) {
     const int64_t eoff = row * rstride + int64_t(h) * D;
     const uint16_t* kbase = P.k + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + (int64_t(kv0) + ks0) * rstride + int64_t(h) * D;
-    // the first key stages are in flight while the query rows load
-    dq_stream_issue<D, C::NW, SPARSE>(lds, kbase, vbase, rstride, L - ks0, n_steps, ks, w, lane);
+    // SPARSE: the wave pair pr = w / 2 holds query block 2t + pr and walks only
+    // the key blocks that block attends, SPB steps each, on ring stages 2pr and
+    // 2pr + 1 (loaded by the pair's two waves); the pairs meet at every step's
+    // barrier
+    constexpr int SPB = jfa::kSpBlock / C::BN;
+    const int pr = w >> 1;
+    int n_all = 0, n_mine = 0, blk = 0;
+    BlockWalk walk{P.sp_ent + e_first, n_ent, jfa::kSpBit + pr, lane, 0, 0, 0};
+    auto load_pair = [&](int st, int key) {
+      uint16_t* buf = lds + (2 * pr + (st & 1)) * C::STAGE;
+      const int64_t r0 = int64_t(key) * rstride;
+      const int rowbytes = int(rstride * 2);
+      tile_load<D, C::BN, 2>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, L - key), rowbytes, w & 1,
+                             lane);
+      tile_load<D, C::BN, 2>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, L - key),
+                             rowbytes, w & 1, lane);
+    };
+    if (SPARSE) {
+      const int n0 = count_bit(P.sp_ent + e_first, n_ent, jfa::kSpBit, lane) * SPB;
+      const int n1 = count_bit(P.sp_ent + e_first, n_ent, jfa::kSpBit + 1, lane) * SPB;
+      n_all = max(n0, n1);
+      n_mine = pr ? n1 : n0;
+      walk.load(0);
+      if (n_mine > 0) {
+        blk = walk.next();
+        load_pair(0, blk * jfa::kSpBlock);
+      }
+    } else {
+      // the first key stages are in flight while the query rows load
+      dq_stream_issue<D, C::NW>(lds, kbase, vbase, rstride, L - ks0, n_keys, w, lane);
+    }
     u32x4 qf[C::DS], dof[C::DS];
     const float di = load_row<D>(P.q + eoff, P.o + eoff, P.dout + eoff, ok, g, qf, dof);
     const int64_t vidx = int64_t(h) * P.total_kv + row;
@@ -419,10 +400,41 @@ dq_kernel(DqParams P) {
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
-    dq_stream<D, CAUSAL, WIN, C::NW, true, SPARSE>(lds, kbase, vbase, rstride, L - ks0, n_steps,
-                                                   ks, n_lo, n_free, n_own, P.window, qf, dof, acc,
-                                                   lse2, di, P.c, w, lane, qpos - ks0, lo);
-    // dq_stream ended with a barrier: the ring is free to stage the output rows
+    if (SPARSE) {
+      // a step: wait for the pair's stage, barrier (every wave is done with the
+      // previous step, whose stages the next loads reuse), load the pair's next
+      // step, then S, dP, dS and the dQ products of this one
+      const bool own = w * 32 < q_rows;  // the wave holds rows of the tile
+      f32x16 ndi;  // -Di of the lane's row, the first dP product's accumulator input
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ndi[r] = -di;
+      const uint32_t lds0 = lds_addr(lds);
+      for (int st = 0; st < n_all; ++st) {
+        wait_vmem();
+        __syncthreads();
+        const int key = blk * jfa::kSpBlock + (st % SPB) * C::BN;
+        if (st + 1 < n_mine) {
+          if ((st + 1) % SPB == 0) blk = walk.next();
+          load_pair(st + 1, blk * jfa::kSpBlock + ((st + 1) % SPB) * C::BN);
+        }
+        if (st < n_mine && own) {
+          const uint32_t kst = lds0 + uint32_t((2 * pr + (st & 1)) * C::STAGE * 2);
+          f32x16 sc[C::KB], dp[C::KB];
+          u32x4 pds[2 * C::KB];
+          __builtin_amdgcn_s_setprio(1);
+          dq_scores<D>(kst, lo, qf, dof, ndi, sc, dp);
+          __builtin_amdgcn_s_setprio(0);
+          dq_softmax<D, true, CAUSAL, false>(sc, dp, lse2, P.c, g, key, L, qpos, pds, 0, lo, pds, acc);
+          dq_accumulate<D>(kst, lo, pds, acc);
+        }
+      }
+      __syncthreads();  // every wave is done with the ring before it stages the rows
+    } else {
+      dq_stream<D, CAUSAL, WIN, C::NW, true>(lds, kbase, vbase, rstride, L - ks0, n_keys, n_lo,
+                                             n_free, n_own, P.window, qf, dof, acc, lse2, di, P.c,
+                                             w, lane, qpos - ks0, lo);
+    }
+    // the key stream ended with a barrier: the ring is free to stage the output rows
     if (ROPE) rope_back_rows<D>(acc, qpos, g, rope_tab);
     const int row0 = q_first + w * 32;
     store_rows<D>(lds + w * 32 * D, acc, P.scale,
@@ -508,9 +520,7 @@ dq_bcast_kernel(DqParams P) {
     const uint16_t* kbase = P.k + int64_t(kv0) * rstride + int64_t(h) * D;
     const uint16_t* vbase = P.v + int64_t(kv0) * rstride + int64_t(h) * D;
     // the sequence's first key stages are in flight while its dO and out rows load
-    const int n_steps = ceil_div(L, C::BN);
-    const StreamKeys<C::BN> ks{nullptr, L, 0};
-    dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, n_steps, ks, w, lane);
+    dq_stream_issue<D, NW>(lds, kbase, vbase, rstride, L, L, w, lane);
     u32x4 dof[C::DS];
     const float di = load_do_row<D>(P.o + oeff, P.dout + oeff, ok, g, dof);
     const int64_t vidx = (int64_t(b) * P.H + h) * P.lq + qpos;
@@ -520,9 +530,9 @@ dq_bcast_kernel(DqParams P) {
       P.nls[vidx] = -lse / P.scale;
     }
     if (L > 0)
-      dq_stream<D, false, false, NW, true>(lds, kbase, vbase, rstride, L, n_steps, ks, 0,
-                                           L / C::BN, own ? n_steps : 1, 0, qf, dof, acc,
-                                           lse * kLog2e, di, P.c, w, lane, qpos, lo);
+      dq_stream<D, false, false, NW, true>(lds, kbase, vbase, rstride, L, L, 0,
+                                    L / C::BN, own ? ceil_div(L, C::BN) : 1, 0, qf, dof, acc,
+                                    lse * kLog2e, di, P.c, w, lane, qpos, lo);
   }
   if (ok) {
     float* prow = P.dq_part + ((int64_t(grp) * P.lq + qpos) * P.H + h) * D;

@@ -18,6 +18,7 @@
 // the tail step and the causal diagonal ("Jagged Flash Attention for GEM": loop
 // peeling).
 #include "jfa_internal.h"
+#include "jfa_sparse.h"
 #include "jfa_tiles.h"
 
 using namespace jfa_dev;
@@ -216,42 +217,6 @@ __device__ __forceinline__ void wait_vmem_le() {
 // key blocks its step list names, in ascending order, instead of the whole
 // sequence; every step is masked, a wave's scores wholly when its query block
 // does not attend the step's key block, and past the sequence end.
-// Block-sparse: the key blocks one query block of a tile attends, in list order:
-// the tile's entries that carry the block's bit, read 64 at a time (one per lane)
-// and taken from the ballot of that bit.
-struct BlockWalk {
-  const int32_t* ent;  // the tile's entries
-  int n_ent, bit, lane;
-  int base;            // index of the loaded chunk's first entry
-  uint64_t left;       // entries of the chunk with the bit, not yet taken
-  int v;               // the lane's entry of the chunk
-  __device__ __forceinline__ void load(int b0) {
-    base = b0;
-    const int e = b0 + lane;
-    v = e < n_ent ? ent[e] : 0;
-    left = __builtin_amdgcn_ballot_w64((v >> bit) & 1);
-  }
-  // the next key block (only called while one is left; block 0 past the list)
-  __device__ __forceinline__ int next() {
-    while (left == 0 && base + 64 < n_ent) load(base + 64);
-    if (left == 0) return 0;
-    const int i = __builtin_ctzll(left);
-    left &= left - 1;
-    return __builtin_amdgcn_readlane(v, i) & jfa::kSpIdx;
-  }
-};
-
-// Number of the tile's entries that carry bit `bit` (uniform).
-__device__ __forceinline__ int count_bit(const int32_t* ent, int n_ent, int bit, int lane) {
-  int n = 0;
-  for (int b0 = 0; b0 < n_ent; b0 += 64) {
-    const int e = b0 + lane;
-    const int v = e < n_ent ? ent[e] : 0;
-    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64((v >> bit) & 1));
-  }
-  return n;
-}
-
 template <int D, bool CAUSAL, bool BCAST, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
