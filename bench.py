@@ -272,8 +272,8 @@ def copy_probe(dev, jfa, mib=2048, reps=10):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_block.hip",
-                  "jfa_rope.h", "jfa_rope.hip")
+KERNEL_SOURCES = ("jfa_device.h", "jfa_tiles.h", "jfa_sparse.h", "jfa_fwd.hip", "jfa_bwd.hip",
+                  "jfa_block.hip", "jfa_rope.h", "jfa_rope.hip")
 
 
 def kernel_source_digest():
