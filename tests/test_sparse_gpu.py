@@ -103,15 +103,39 @@ def test_empty_rows_and_columns(gpu, D, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_lists_longer_than_64_blocks(gpu, causal):
+@pytest.mark.parametrize("D", [64, 128])
+def test_lists_longer_than_64_blocks(gpu, D, causal):
     """Sequences of more than 64 blocks (4096 tokens), dense enough that a tile's
     list holds more than 64 entries: the kernels read a tile's entries 64 at a
     time."""
     rng = np.random.default_rng(31)
     L = [4500, 70, 4353]
-    case = _case_with_mask(L, 128, 11, lambda b, n: rng.random((n, n)) < 0.8, causal)
-    log(f"sparse long lists causal={causal}: lengths {L}")
+    case = _case_with_mask(L, D, 11, lambda b, n: rng.random((n, n)) < 0.8, causal)
+    log(f"sparse long lists D={D} causal={causal}: lengths {L}")
     _check(case, oracle_full(case), _run(case, gpu))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_slot_counts_do_not_change_results(gpu, D, causal):
+    """One workgroup walking every tile in turn (each tile's first loads issued
+    behind the previous tile's stores, the two wave pairs of a tile walking lists
+    of different lengths) and far more workgroups than tiles give the bits of the
+    default slot count."""
+    import torch
+    rng = np.random.default_rng(41 + D)
+    case = _case_with_mask(LENGTHS + [700, 3], D, 12, lambda b, n: rng.random((n, n)) < 0.4,
+                           causal)
+    a = GpuRun(case, gpu)
+    oa, la = a.forward()
+    ga = [x.clone() for x in a.backward()]
+    for slots in (1, 2048):
+        log(f"sparse D={D} causal={causal} slots={slots}")
+        b = GpuRun(case, gpu, num_slots=slots)
+        ob, lb = b.forward()
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
+        for x, y in zip(ga, b.backward()):
+            assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -13,6 +13,7 @@ its device copy and the workspace for one problem.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -126,7 +127,11 @@ def tile_rows(kind: int, head_dim: int, flags: int = 0) -> int:
     return int(lib().jfa_tile_rows(kind, head_dim, flags))
 
 
+@functools.lru_cache(maxsize=None)
 def default_slots(kind: int, head_dim: int, flags: int = 0, device: int = 0) -> int:
+    """Persistent workgroups for a schedule of `kind` on `device` (the device's
+    compute units times the kernel's resident workgroups per unit; fixed for the
+    process, so kept once asked)."""
     n = ctypes.c_int32(0)
     _check(lib().jfa_default_slots(kind, head_dim, flags, device, ctypes.byref(n)))
     return int(n.value)
@@ -338,7 +343,23 @@ class Plan:
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
                          int(off[-1]), scale, flags, lq, rope_base, window, block)
         self.device = torch.device(device)
-        self.offsets_dev = torch.from_numpy(off.copy()).to(self.device)
+        # Every int32 array the kernels read (the offsets, the schedules and the
+        # step lists) goes to the device in one copy, each array at a 256-byte
+        # boundary of the packed buffer and at least one element long (an empty
+        # array still needs a valid device pointer).
+        packed, spans = [], []
+
+        def put(a):
+            a = np.ascontiguousarray(a, dtype=np.int32).ravel()
+            if a.size == 0:
+                a = np.zeros(1, np.int32)
+            pos = sum(x.size for x in packed)
+            packed.append(a)
+            packed.append(np.zeros((-a.size) % 64, np.int32))
+            spans.append((pos, a.size))
+            return len(spans) - 1
+
+        i_off = put(off)
         bs = 64 if flags & BLOCK_DIAG64 else (block if flags & BLOCK_DIAG else 0)
         # blocks of 32 or 64 tokens: single-tile kernels, no schedule and no lse;
         # blocks of 128 or 256 tokens are scheduled as jagged tiles over the blocks
@@ -358,13 +379,22 @@ class Plan:
                 sch = Schedule(sp, tl, S)
                 if lists is not None:
                     sch.lists = lists
-                    # an empty entries array still needs a valid device pointer
-                    sch.lists_dev = tuple(torch.from_numpy(a if a.size else np.zeros(1, np.int32))
-                                          .to(self.device) for a in lists)
-                sch.slot_ptr_dev = torch.from_numpy(sp).to(self.device)
-                sch.tiles_dev = torch.from_numpy(np.ascontiguousarray(tl)).to(self.device) \
-                    if len(tl) else torch.zeros((1, 4), dtype=torch.int32, device=self.device)
+                    sch.lists_dev = tuple(put(a) for a in lists)
+                sch.slot_ptr_dev = put(sp)
+                sch.tiles_dev = put(tl if len(tl) else np.zeros((1, 4), np.int32))
                 self.sched[kind] = sch
+        dev = torch.from_numpy(np.concatenate(packed)).to(self.device)
+
+        def view(i):
+            pos, n = spans[i]
+            return dev[pos:pos + n]
+
+        self.offsets_dev = view(i_off)
+        for sch in self.sched.values():
+            if sch.lists_dev is not None:
+                sch.lists_dev = tuple(view(i) for i in sch.lists_dev)
+            sch.slot_ptr_dev = view(sch.slot_ptr_dev)
+            sch.tiles_dev = view(sch.tiles_dev).view(-1, 4)
         nbytes = bwd_workspace_bytes(self.p)
         self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=self.device)
                           if nbytes else None)
