@@ -3,11 +3,11 @@ benchmark times (default slot count, folded zigzag schedule).
 
 The GEM-like batch (causal and not), the broadcast-Q batch and the
 block-diagonal batches (64-token blocks at D = 64 and 128, the other block sizes
-and rotary blocks) are compared element by element in full: every output row of
-every (sequence, head), lse, and dQ/dK/dV, against the fp64 oracle run over the
-whole batch by a pool of worker processes (broadcast-Q: dQ summed over all 1024
-sequences for every head). The rotary and sliding-window variants of the GEM
-batch are compared on a sample of (sequence, head) slices. On the imbalance
+and rotary blocks) and the rotary and sliding-window variants of the GEM batch
+are compared element by element in full: every output row of every (sequence,
+head), lse, and dQ/dK/dV, against the fp64 oracle run over the whole batch by a
+pool of worker processes (broadcast-Q: dQ summed over all 1024 sequences for
+every head). On the imbalance
 workload (4.6e14 FLOPs) every short sequence is compared in full, plus seeded
 long slices and identities that hold at any size, checked over the whole output
 on the GPU."""
@@ -175,18 +175,10 @@ def run_full(name, gpu, pool, rdir):
 
 @pytest.mark.parametrize("name", ["gem", "gem_causal", "broadcast", "block64_d64",
                                   "block64_d128", "block32_d128", "block128_d128",
-                                  "block256_d128", "block64_rope_d64", "block64_rope_d128"])
+                                  "block256_d128", "block64_rope_d64", "block64_rope_d128",
+                                  "gem_rope", "gem_rope_causal", "gem_window"])
 def test_every_element(gpu, oracle_pool, result_dir, name):
     run_full(name, gpu, oracle_pool, result_dir)
-
-
-@pytest.mark.parametrize("name", ["gem_rope", "gem_rope_causal"])
-def test_gem_rope(gpu, name):
-    run_sampled(name, gpu)
-
-
-def test_gem_window(gpu):
-    run_sampled("gem_window", gpu)
 
 
 def test_imbalance(gpu):
