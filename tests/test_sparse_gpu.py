@@ -138,6 +138,18 @@ def test_slot_counts_do_not_change_results(gpu, D, causal):
             assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("lengths", [[0, 0, 0], []], ids=["all-empty", "no-sequences"])
+def test_empty_batches(gpu, lengths):
+    """A batch of empty sequences and a batch of none: forward and backward run
+    (causal or not) and return empty outputs."""
+    for causal in (False, True):
+        case = _case_with_mask(lengths, 128, 3, lambda b, n: np.ones((n, n), bool), causal)
+        out, lse, dq, dk, dv = _run(case, gpu)
+        for t in (out, dq, dk, dv):
+            assert tuple(t.shape) == (0, 2, 128)
+        assert lse.numel() == 0
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_mask_is_the_plain_kernels_bitwise(gpu, causal):
     import torch
