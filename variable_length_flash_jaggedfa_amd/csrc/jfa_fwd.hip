@@ -244,6 +244,7 @@ fwd_kernel(FwdParams P) {
     const int ks0 = WIN ? max(0, q_first - P.window + 1) / C::BN * C::BN : 0;
     const int n_keys = (CAUSAL ? min(L, q_first + q_rows) : L) - ks0;
     // SPARSE: the tile's entries [e_first, e_first + n_ent), SPB steps each
+    // (the union of the two query blocks' lists, a bit per block)
     constexpr int SPB = SPARSE ? jfa::kSpBlock / C::BN : 1;
     int e_first = 0, n_ent = 0;
     if (SPARSE) {
@@ -251,22 +252,11 @@ fwd_kernel(FwdParams P) {
       e_first = sload(P.sp_ptr + u);
       n_ent = sload(P.sp_ptr + u + 1) - e_first;
     }
-    const int n_steps = SPARSE ? n_ent * SPB : ceil_div(n_keys, C::BN);
+    const int n_steps = ceil_div(n_keys, C::BN);  // dense kernels
     const int lo_edge = WIN ? q_first + C::BM - P.window - ks0 : 0;
     const int n_lo = lo_edge > 0 ? min(n_steps, ceil_div(lo_edge, C::BN)) : 0;
     // steps without a mask: [n_lo, n_free)
-    const int n_free =
-        SPARSE ? 0 : max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
-    // first key of step st (counted from ks0) and the key count its mask uses:
-    // SPARSE masks every key of a block the wave's query block does not attend
-    auto key_of = [&](int st) {
-      if (!SPARSE) return st * C::BN;
-      return (sload(P.sp_ent + e_first + st / SPB) & jfa::kSpIdx) * jfa::kSpBlock + (st % SPB) * C::BN;
-    };
-    auto nk_of = [&](int st) {
-      if (!SPARSE) return n_keys;
-      return (sload(P.sp_ent + e_first + st / SPB) >> (jfa::kSpBit + w / 2)) & 1 ? L : 0;
-    };
+    const int n_free = max(n_lo, min(n_steps, ((CAUSAL ? q_first : L) - ks0) / C::BN));
     const int qpos = q_first + w * 32 + li;  // query position of this lane
     const int qm = qpos - ks0;                // the same, counted from key ks0
     // Steps this wave computes: all, or one when the tile has no row for it
@@ -284,7 +274,7 @@ fwd_kernel(FwdParams P) {
     // covering the rest of the sequence (keys past the end read as zero)
     auto load_stage = [&](int st) {
       uint16_t* buf = lds + (st % C::NS) * C::STAGE;
-      const int key = key_of(st);
+      const int key = st * C::BN;
       const int64_t r0 = int64_t(key) * rstride;
       tile_load<D, C::BN, C::NW>(buf, rows_rsrc<D, C::BN>(kbase + r0, rstride, Lk - key), rowbytes, w, lane);
       tile_load<D, C::BN, C::NW>(buf + C::TILE, rows_rsrc<D, C::BN>(vbase + r0, rstride, Lk - key),
@@ -353,79 +343,78 @@ fwd_kernel(FwdParams P) {
       }
     } else {
 #pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st)
-      if (st < n_steps) load_stage(st);
+      for (int st = 0; st < C::NS - 1; ++st)
+        if (st < n_steps) load_stage(st);
 
-    if (n_steps > 0) {
-      // first step's scores: wait for stage 0 only
-      if (n_steps >= 3) wait_vmem_le<2 * C::LOADS>();
-      else if (n_steps == 2) wait_vmem_le<C::LOADS>();
-      else wait_vmem();
-      __syncthreads();
-      f32x16 sc[C::KB], sn[C::KB];
-      scores<D>(stage_ptr(0), qf, sc, li, g);
-      if (n_lo > 0 || n_free == 0)
-        mask_scores<D, CAUSAL, WIN>(sc, g, key_of(0), nk_of(0), qm, P.window);
-      m = pair_max(row_max<D>(sc)) * P.c;
-
-      // before step kt (kt + 1 < n_steps): stage kt+1 must have landed, stage
-      // kt+2 may still be in flight; the barrier also means every wave is done
-      // with stage kt-1, whose buffer the load of stage kt+3 reuses
-      auto advance = [&](int kt) {
-        if (kt + 2 < n_steps) wait_vmem_le<C::LOADS>();
+      if (n_steps > 0) {
+        // first step's scores: wait for stage 0 only
+        if (n_steps >= 3) wait_vmem_le<2 * C::LOADS>();
+        else if (n_steps == 2) wait_vmem_le<C::LOADS>();
         else wait_vmem();
         __syncthreads();
-        if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
-      };
-      int kt = 0;
-      const int n_free_own = CAUSAL ? n_free : min(n_free, n_own);
-      if (WIN) {
-        for (; kt + 1 < n_lo; ++kt) {  // the next step meets the window's lower edge
+        f32x16 sc[C::KB], sn[C::KB];
+        scores<D>(stage_ptr(0), qf, sc, li, g);
+        if (n_lo > 0 || n_free == 0) mask_scores<D, CAUSAL, WIN>(sc, g, 0, n_keys, qm, P.window);
+        m = pair_max(row_max<D>(sc)) * P.c;
+
+        // before step kt (kt + 1 < n_steps): stage kt+1 must have landed, stage
+        // kt+2 may still be in flight; the barrier also means every wave is done
+        // with stage kt-1, whose buffer the load of stage kt+3 reuses
+        auto advance = [&](int kt) {
+          if (kt + 2 < n_steps) wait_vmem_le<C::LOADS>();
+          else wait_vmem();
+          __syncthreads();
+          if (kt + C::NS - 1 < n_steps) load_stage(kt + C::NS - 1);
+        };
+        int kt = 0;
+        const int n_free_own = CAUSAL ? n_free : min(n_free, n_own);
+        if (WIN) {
+          for (; kt + 1 < n_lo; ++kt) {  // the next step meets the window's lower edge
+            advance(kt);
+            const float mx = fwd_step<D, true, true, CAUSAL, WIN>(
+                stage_ptr(kt) + C::TILE, stage_ptr(kt + 1), qf, sc, sn, o, m, l, P.c, lane,
+                (kt + 1) * C::BN, n_keys, qm, P.window);
+            update_max<D>(mx, m, l, o);
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
+          }
+        }
+        // two unmasked steps per iteration, the score registers swapping roles
+        for (; kt + 2 < n_free_own; kt += 2) {
           advance(kt);
-          const float mx = fwd_step<D, true, true, CAUSAL, WIN>(
-              stage_ptr(kt) + C::TILE, stage_ptr(kt + 1), qf, sc, sn, o, m, l, P.c, lane,
-              (kt + 1) * C::BN, n_keys, qm, P.window);
+          float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                     qf, sc, sn, o, m, l, P.c, lane,
+                                                     (kt + 1) * C::BN, n_keys, qm, P.window);
+          update_max<D>(mx, m, l, o);
+          advance(kt + 1);
+          mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt + 1) + C::TILE, stage_ptr(kt + 2),
+                                               qf, sn, sc, o, m, l, P.c, lane,
+                                               (kt + 2) * C::BN, n_keys, qm, P.window);
+          update_max<D>(mx, m, l, o);
+        }
+        for (; kt + 1 < n_free_own; ++kt) {  // the next step needs no mask
+          advance(kt);
+          const float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                           qf, sc, sn, o, m, l, P.c, lane,
+                                                           (kt + 1) * C::BN, n_keys, qm, P.window);
           update_max<D>(mx, m, l, o);
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
         }
-      }
-      // two unmasked steps per iteration, the score registers swapping roles
-      for (; kt + 2 < n_free_own; kt += 2) {
-        advance(kt);
-        float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
-                                                   qf, sc, sn, o, m, l, P.c, lane,
-                                                   (kt + 1) * C::BN, n_keys, qm, P.window);
-        update_max<D>(mx, m, l, o);
-        advance(kt + 1);
-        mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt + 1) + C::TILE, stage_ptr(kt + 2),
-                                             qf, sn, sc, o, m, l, P.c, lane,
-                                             (kt + 2) * C::BN, n_keys, qm, P.window);
-        update_max<D>(mx, m, l, o);
-      }
-      for (; kt + 1 < n_free_own; ++kt) {  // the next step needs no mask
-        advance(kt);
-        const float mx = fwd_step<D, true, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
-                                                         qf, sc, sn, o, m, l, P.c, lane,
-                                                         (kt + 1) * C::BN, n_keys, qm, P.window);
-        update_max<D>(mx, m, l, o);
+        for (; kt + 1 < (CAUSAL ? n_steps : n_own); ++kt) {  // the next step is the tail or on the diagonal
+          advance(kt);
+          const float mx = fwd_step<D, true, true, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
+                                                          qf, sc, sn, o, m, l, P.c, lane,
+                                                          (kt + 1) * C::BN, n_keys, qm, P.window);
+          update_max<D>(mx, m, l, o);
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
+          for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
+        }
+        fwd_step<D, false, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
+                                          lane, 0, n_keys, qm, P.window);
+        if (!CAUSAL)
+          for (; kt + 1 < n_steps; ++kt) advance(kt);  // the steps this wave leaves out
       }
-      for (; kt + 1 < (CAUSAL ? n_steps : n_own); ++kt) {  // the next step is the tail or on the diagonal
-        advance(kt);
-        const float mx = fwd_step<D, true, true, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, stage_ptr(kt + 1),
-                                                        qf, sc, sn, o, m, l, P.c, lane,
-                                                        key_of(kt + 1), nk_of(kt + 1), qm, P.window);
-        update_max<D>(mx, m, l, o);
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) sc[kb] = sn[kb];
-      }
-      fwd_step<D, false, false, CAUSAL, WIN>(stage_ptr(kt) + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
-                                        lane, 0, n_keys, qm, P.window);
-      if (!CAUSAL)
-        for (; kt + 1 < n_steps; ++kt) advance(kt);  // the steps this wave leaves out
-    }
     }
 
     // epilogue: out = O / l (bf16) through the wave's LDS staging tile, lse =
