@@ -201,3 +201,34 @@ def test_device_calls_reject_missing_lists_before_any_hip_call():
     s = Lb.jfa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, 4,
                    fake, fake, 4, fake, fake, fake, fake, 1 << 20, None)
     assert s == jfa.ERR_INVALID_ARG and b"BLOCK_SPARSE" in Lb.jfa_last_error()
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_plan_packs_its_device_arrays(sparse):
+    """A plan sends the offsets, both schedules and (block-sparse) both kinds of
+    step lists in one copy: each view holds its host array exactly, starts on a
+    256-byte boundary of the packed buffer, and an empty array still gets one
+    element (a valid pointer). Built with CPU tensors and an explicit slot count,
+    so no device is needed."""
+    L = np.array([130, 0, 64, 700, 1, 257])
+    off = J.offsets_from_lengths(L)
+    flags = jfa.BLOCK_SPARSE | jfa.CAUSAL if sparse else jfa.CAUSAL
+    masks = _flat(_masks(L, 5, density=0.5)) if sparse else None
+    plan = jfa.Plan(off, 2, 128, 0.1, flags, num_slots=24, device="cpu", block_mask=masks)
+    base = plan.offsets_dev.data_ptr()
+    views = [(plan.offsets_dev, off)]
+    p = plan.p
+    for kind, sch in plan.sched.items():
+        if sparse:
+            sb, lp, ent = jfa.sparse_lists(p, off, masks, kind)
+            sp, tl = jfa.schedule_sparse(p, off, lp, kind, plan.order, 24)
+            for dev, host in zip(sch.lists_dev, (sb, lp, ent)):
+                views.append((dev, host if host.size else np.zeros(1, np.int32)))
+        else:
+            sp, tl = jfa.schedule(p, off, kind, plan.order, 24)
+        views.append((sch.slot_ptr_dev, sp))
+        views.append((sch.tiles_dev, tl))
+        assert tuple(sch.tiles_dev.shape) == (len(tl), 4)
+    for dev, host in views:
+        assert np.array_equal(dev.numpy().reshape(-1), np.asarray(host).reshape(-1))
+        assert (dev.data_ptr() - base) % 256 == 0
