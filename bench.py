@@ -327,9 +327,9 @@ def main():
                              "gem_window", "block32_d128", "block128_d128", "block256_d128",
                              "imbalance", "gem_padded", "sparse_d128", "sparse_d64"])
     ap.add_argument("--order", default="default",
-                    choices=["default", "zigzag", "inorder", "xcd", "folded"],
-                    help="dealing order; default: the plan's own (folded zigzag, in-order for "
-                         "block-sparse)")
+                    choices=["default", "zigzag", "inorder", "xcd", "folded", "xcd_inorder"],
+                    help="dealing order; default: the plan's own (folded zigzag; balanced "
+                         "in-order for block-sparse)")
     ap.add_argument("--compare-orders", action="store_true",
                     help="also time forward + backward under every dealing order, interleaved")
     ap.add_argument("--compare-rope", action="store_true",
@@ -385,7 +385,8 @@ def main():
     v = J.to_torch_bf16(case.v).to(dev)
     do = J.to_torch_bf16(case.do).to(dev)
     ORDERS = {"zigzag": jfa.ORDER_ZIGZAG, "inorder": jfa.ORDER_INORDER,
-              "xcd": jfa.ORDER_XCD_ZIGZAG, "folded": jfa.ORDER_FOLDED_ZIGZAG}
+              "xcd": jfa.ORDER_XCD_ZIGZAG, "folded": jfa.ORDER_FOLDED_ZIGZAG,
+              "xcd_inorder": jfa.ORDER_XCD_INORDER}
     order = ORDERS.get(args.order)  # None: the plan's default
 
     runs = []
@@ -413,8 +414,9 @@ def main():
             for kind, sc in plan.sched.items():
                 t1 = time.perf_counter()
                 if plan.sparse:  # the step lists and the schedule built from them
-                    lp = jfa.sparse_lists(plan.p, case.offsets, case.mask, kind)[1]
-                    jfa.schedule_sparse(plan.p, case.offsets, lp, kind, plan.order, sc.num_slots)
+                    _, lp, ent = jfa.sparse_lists(plan.p, case.offsets, case.mask, kind)
+                    jfa.schedule_sparse(plan.p, case.offsets, lp, ent, kind, plan.order,
+                                        sc.num_slots)
                 else:
                     jfa.schedule(plan.p, case.offsets, kind, plan.order, sc.num_slots)
                 jfa_schedule_ms += (time.perf_counter() - t1) * 1e3

@@ -103,6 +103,13 @@ typedef enum jfa_status {
                                   work over the XCDs; num_slots % 8 == 0 */
 #define JFA_ORDER_FOLDED_ZIGZAG 3 /* ZIGZAG over items; with CAUSAL an item is the pair
                                      of tiles a and n-1-a of one (sequence, head) */
+#define JFA_ORDER_XCD_INORDER 4 /* (sequence, head) units in generation order, each to
+                                   the XCD (group of num_slots / 8 consecutive slots;
+                                   one group of all slots if num_slots % 8 != 0) with
+                                   the least work dealt so far, its tiles in order each
+                                   to that group's least-loaded slot; ties to the lower
+                                   group or slot. Keeps the tiles of a unit together in
+                                   time and on one L2 while balancing the slots */
 
 typedef struct jfa_problem {
   int32_t num_seqs;   /* B >= 0 */
@@ -321,13 +328,17 @@ jfa_status jfa_sparse_lists(const jfa_problem* p, const int32_t* offsets_host,
                             int32_t* seq_base, int32_t* list_ptr, int32_t* entries,
                             int64_t entries_capacity);
 
-/* jfa_schedule for a BLOCK_SPARSE problem: the same tiles, orders and outputs, a
- * tile's work being 64 times the length of its unit's list (list_ptr_host from
- * jfa_sparse_lists of the same kind). Host only. */
+/* jfa_schedule for a BLOCK_SPARSE problem: the same tiles, orders and outputs.
+ * list_ptr_host and entries_host are the lists of the same kind from
+ * jfa_sparse_lists (entries_host may be NULL for kind BWD). A BWD tile's work is
+ * 64 times its list's length (the dK/dV pass walks the whole list); a FWD tile's
+ * is 64 times the larger number of its entries that carry bit 28 or bit 29 (the
+ * forward and the dQ pass walk the two blocks' entries side by side). Returns
+ * INVALID_ARG if list_ptr_host[0] != 0 or the list pointers decrease. Host only. */
 jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host,
-                               const int32_t* list_ptr_host, int32_t kind, int32_t order,
-                               int32_t num_slots, int32_t* slot_ptr, int32_t* tiles,
-                               int64_t capacity);
+                               const int32_t* list_ptr_host, const int32_t* entries_host,
+                               int32_t kind, int32_t order, int32_t num_slots, int32_t* slot_ptr,
+                               int32_t* tiles, int64_t capacity);
 
 /* Block-sparse forward: as jfa_fwd with the FWD step lists (device) and no
  * workspace; a tile visits only the key blocks its list names. Preconditions as

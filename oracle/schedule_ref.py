@@ -29,8 +29,16 @@ Readings of what the page leaves open:
     order. Without causal masking every tile is an item.
   * Block-sparse attention (64-token blocks, one block mask per sequence): a
     tile covers two blocks (128 query rows, or 128 keys); its step list names the
-    other side's blocks that pair with either of them, ascending, and its work is
-    64 times the list's length (the keys, or query rows, it visits).
+    other side's blocks that pair with either of them, ascending. A key tile's
+    work is 64 times its list's length (the query rows it visits); a query tile's
+    two blocks walk their own entries side by side, so its work is 64 times the
+    longer of the two (the entries carrying bit 28, or bit 29).
+  * The balanced in-order variant (an MI355X refinement for tiles whose cost
+    depends on L2 sharing within a (sequence, head)): (sequence, head) units in
+    generation order, each to the group of slots (one per XCD) with the least
+    work dealt so far, the lower group on ties; the unit's tiles, in order, each
+    to the least-loaded slot of that group, the lower slot on ties. With a slot
+    count that is not a multiple of 8 all slots form one group.
 Output: slot_ptr [S+1] and tiles [N,4] = (b, h, t, work), grouped by slot, in the
 order each slot received them.
 """
@@ -40,7 +48,7 @@ import numpy as np
 
 KIND_FWD, KIND_BWD = 0, 1
 SPARSE_BLOCK, SPARSE_BIT = 64, 28
-ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG, ORDER_XCD_INORDER = 0, 1, 2, 3, 4
 
 
 def ceil_div(a, b):
@@ -77,13 +85,15 @@ def sparse_lists(lengths, masks, kind, tile_rows=128, causal=False):
 
 
 def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0, window=0,
-                    sparse_list_ptr=None):
+                    sparse_list_ptr=None, sparse_entries=None):
     """All tiles in generation order: list of (b, h, t, work).
 
     With a causal window W the work counts only what the window leaves: a query
     tile visits the keys from max(0, t*BM - W + 1) to its last row, a key tile is
     attended by the queries from n*BN to min(L, (n+1)*BN - 1 + W). With block-sparse
-    step lists (list_ptr of sparse_lists) a tile's work is 64 times its list's length.
+    step lists (list_ptr and entries of sparse_lists) a key tile's work is 64 times
+    its list's length and a query tile's 64 times the number of its entries that
+    carry bit 28 or bit 29, whichever is larger.
     """
     out = []
     if sparse_list_ptr is not None:
@@ -92,8 +102,14 @@ def enumerate_tiles(lengths, num_heads, kind, tile_rows, causal=False, lq=0, win
             n = ceil_div(L, tile_rows)
             for h in range(num_heads):
                 for t in range(n):
-                    out.append((b, h, t, SPARSE_BLOCK * int(sparse_list_ptr[u + t + 1]
-                                                            - sparse_list_ptr[u + t])))
+                    lo, hi = int(sparse_list_ptr[u + t]), int(sparse_list_ptr[u + t + 1])
+                    if kind == KIND_FWD:
+                        e = [int(x) for x in sparse_entries[lo:hi]]
+                        steps = max(sum((x >> SPARSE_BIT) & 1 for x in e),
+                                    sum((x >> (SPARSE_BIT + 1)) & 1 for x in e))
+                    else:
+                        steps = hi - lo
+                    out.append((b, h, t, SPARSE_BLOCK * steps))
             u += n
         return out
     for b, L in enumerate(int(x) for x in lengths):
@@ -127,9 +143,35 @@ def _zigzag_rank(j, n):
 
 
 def schedule(lengths, num_heads, kind, tile_rows, order, num_slots, causal=False, lq=0,
-             groups=8, window=0, sparse_list_ptr=None):
+             groups=8, window=0, sparse_list_ptr=None, sparse_entries=None):
     tiles = enumerate_tiles(lengths, num_heads, kind, tile_rows, causal, lq, window,
-                            sparse_list_ptr)
+                            sparse_list_ptr, sparse_entries)
+    if order == ORDER_XCD_INORDER:
+        # (sequence, head) units in generation order: each to the least-loaded
+        # group, its tiles in order each to the least-loaded slot of the group
+        ng = groups if num_slots % groups == 0 else 1
+        per = num_slots // ng
+        group_load = [0] * ng
+        slot_load = [0] * num_slots
+        per_slot = [[] for _ in range(num_slots)]
+        g = 0
+        while g < len(tiles):
+            e = g
+            while e < len(tiles) and tiles[e][:2] == tiles[g][:2]:
+                e += 1
+            x = min(range(ng), key=lambda i: (group_load[i], i))
+            group_load[x] += sum(t[3] for t in tiles[g:e])
+            for t in tiles[g:e]:
+                s = min(range(x * per, (x + 1) * per), key=lambda i: (slot_load[i], i))
+                slot_load[s] += t[3]
+                per_slot[s].append(t)
+            g = e
+        slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
+        flat = []
+        for s in range(num_slots):
+            flat.extend(per_slot[s])
+            slot_ptr[s + 1] = len(flat)
+        return slot_ptr, np.asarray(flat, dtype=np.int32).reshape(-1, 4)
     if order == ORDER_XCD_ZIGZAG:
         # Units are (sequence, head) pairs with the summed work of their tiles;
         # they are sorted by that work and dealt zigzag over the groups, then each

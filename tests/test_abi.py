@@ -241,7 +241,7 @@ def test_tile_rows():
 @pytest.mark.parametrize("name", ["tiny", "gem", "gem_causal", "broadcast", "imbalance"])
 @pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
 @pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
-                                   jfa.ORDER_FOLDED_ZIGZAG])
+                                   jfa.ORDER_FOLDED_ZIGZAG, jfa.ORDER_XCD_INORDER])
 def test_cpp_schedule_equals_reference(name, kind, order):
     w = J.standard_workloads()[name]
     L = J.lengths(w)
@@ -260,7 +260,7 @@ def test_cpp_schedule_equals_reference(name, kind, order):
 @pytest.mark.parametrize("W", [1, 100, 512, 5000])
 @pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
 @pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
-                                   jfa.ORDER_FOLDED_ZIGZAG])
+                                   jfa.ORDER_FOLDED_ZIGZAG, jfa.ORDER_XCD_INORDER])
 def test_cpp_schedule_equals_reference_with_window(W, kind, order):
     w = J.standard_workloads()["gem_window"]
     L = J.lengths(w)

@@ -152,3 +152,59 @@ def test_padded_gem_recipe():
     assert (g.num_seqs, g.num_heads, g.head_dim) == (p.num_seqs, p.num_heads, p.head_dim)
     assert np.all(Lp == Lg.max()) and Lp.shape == Lg.shape
     assert wl["gem_padded_causal"].causal and not p.causal
+
+
+def _slots(sp, t):
+    return [[tuple(x) for x in t[sp[s]:sp[s + 1]].tolist()] for s in range(len(sp) - 1)]
+
+
+def test_hand_worked_xcd_inorder():
+    """Lengths 300, 100, 200, one head, 128-row forward tiles (work = L each):
+    units (0,0) with three tiles of 300, (1,0) with one of 100, (2,0) with two
+    of 200.
+    16 slots: 8 groups of 2. Unit (0,0) goes to group 0: its tiles to slots 0,
+    1, then 0 again (both at 300, the lower slot). Unit (1,0) to group 1 (group
+    0 holds 900, the others 0): slot 2. Unit (2,0) to group 2: slots 4 and 5.
+    3 slots (not a multiple of 8): one group. Unit (0,0) fills slots 0, 1, 2;
+    unit (1,0) goes to slot 0 (all at 300); unit (2,0) to slots 1 and 2 (300
+    each, then 500 / 300)."""
+    L = [300, 100, 200]
+    sp, t = R.schedule(L, 1, R.KIND_FWD, 128, R.ORDER_XCD_INORDER, 16)
+    want = [[] for _ in range(16)]
+    want[0] = [(0, 0, 0, 300), (0, 0, 2, 300)]
+    want[1] = [(0, 0, 1, 300)]
+    want[2] = [(1, 0, 0, 100)]
+    want[4] = [(2, 0, 0, 200)]
+    want[5] = [(2, 0, 1, 200)]
+    assert _slots(sp, t) == want
+    sp, t = R.schedule(L, 1, R.KIND_FWD, 128, R.ORDER_XCD_INORDER, 3)
+    assert _slots(sp, t) == [[(0, 0, 0, 300), (1, 0, 0, 100)],
+                             [(0, 0, 1, 300), (2, 0, 0, 200)],
+                             [(0, 0, 2, 300), (2, 0, 1, 200)]]
+
+
+@pytest.mark.parametrize("name", ["gem", "gem_causal", "broadcast"])
+@pytest.mark.parametrize("kind", [R.KIND_FWD, R.KIND_BWD])
+def test_xcd_inorder_properties(name, kind):
+    """Every tile once; a (sequence, head) unit on one group of slots; a slot's
+    tiles in generation order; within a group the slot loads differ by at most
+    the largest tile's work (each tile went to the least-loaded slot)."""
+    w = J.standard_workloads()[name]
+    L = J.lengths(w)
+    S, X = 512, 8
+    sp, t = R.schedule(L, w.num_heads, kind, 128, R.ORDER_XCD_INORDER, S, w.causal, w.lq)
+    sp0, t0 = R.schedule(L, w.num_heads, kind, 128, R.ORDER_INORDER, S, w.causal, w.lq)
+    key = lambda a: sorted(map(tuple, a.tolist()))
+    assert key(t) == key(t0)
+    per = S // X
+    home = {}
+    for s in range(S):
+        rows = t[sp[s]:sp[s + 1]].tolist()
+        for b, h, _, _ in rows:
+            assert home.setdefault((b, h), s // per) == s // per
+        gen = [(b, h, tt) for b, h, tt, _ in rows]
+        assert gen == sorted(gen)
+    big = int(t[:, 3].max())
+    for x in range(X):
+        loads = [int(t[sp[s]:sp[s + 1], 3].sum()) for s in range(x * per, (x + 1) * per)]
+        assert max(loads) - min(loads) <= big

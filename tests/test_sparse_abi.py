@@ -66,19 +66,26 @@ def test_lists_equal_reference(seed, kind):
 
 @pytest.mark.parametrize("kind", [jfa.KIND_FWD, jfa.KIND_BWD])
 @pytest.mark.parametrize("order", [jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
-                                   jfa.ORDER_FOLDED_ZIGZAG])
+                                   jfa.ORDER_FOLDED_ZIGZAG, jfa.ORDER_XCD_INORDER])
 def test_sparse_schedule_equals_reference(kind, order):
     w = J.standard_workloads()["sparse_d128"].with_(num_seqs=300)
     L = J.lengths(w)
     masks = [J.sparse_mask_seq(w, b, int(n)).astype(bool) for b, n in enumerate(L)]
     p, off = _problem(L, H=w.num_heads)
     sb, lp, ent = jfa.sparse_lists(p, off, _flat(masks), kind)
-    sp, tl = jfa.schedule_sparse(p, off, lp, kind, order, 512)
-    sp2, tl2 = R.schedule(L, w.num_heads, kind, 128, order, 512, sparse_list_ptr=lp)
+    sp, tl = jfa.schedule_sparse(p, off, lp, ent, kind, order, 512)
+    sp2, tl2 = R.schedule(L, w.num_heads, kind, 128, order, 512, sparse_list_ptr=lp,
+                          sparse_entries=ent)
     assert np.array_equal(sp, sp2) and np.array_equal(tl, tl2)
-    # the same tiles as plain attention, each worth 64 x its list's length
+    # the same tiles as plain attention; a key tile is worth 64 x its list's
+    # length, a query tile 64 x the longer of its two blocks' lists
     assert len(tl) == jfa.schedule_count(p, off, kind)
-    assert tl[:, 3].sum() == w.num_heads * 64 * len(ent)
+    if kind == jfa.KIND_BWD:
+        assert tl[:, 3].sum() == w.num_heads * 64 * len(ent)
+    else:
+        longer = [max(int(((ent[a:b] >> 28) & 1).sum()), int(((ent[a:b] >> 29) & 1).sum()))
+                  for a, b in zip(lp[:-1], lp[1:])]
+        assert tl[:, 3].sum() == w.num_heads * 64 * sum(longer)
 
 
 def test_workload_masks_match_flat_draw():
@@ -138,10 +145,10 @@ def test_causal_sparse_schedule_equals_reference(kind):
     masks = [J.sparse_mask_seq(w, b, int(n)).astype(bool) for b, n in enumerate(L)]
     p, off = _problem(L, H=w.num_heads, flags=jfa.BLOCK_SPARSE | jfa.CAUSAL)
     sb, lp, ent = jfa.sparse_lists(p, off, _flat(masks), kind)
-    for order in (jfa.ORDER_INORDER, jfa.ORDER_FOLDED_ZIGZAG):
-        sp, tl = jfa.schedule_sparse(p, off, lp, kind, order, 512)
+    for order in (jfa.ORDER_INORDER, jfa.ORDER_FOLDED_ZIGZAG, jfa.ORDER_XCD_INORDER):
+        sp, tl = jfa.schedule_sparse(p, off, lp, ent, kind, order, 512)
         sp2, tl2 = R.schedule(L, w.num_heads, kind, 128, order, 512, sparse_list_ptr=lp,
-                              causal=True)
+                              sparse_entries=ent, causal=True)
         assert np.array_equal(sp, sp2) and np.array_equal(tl, tl2)
 
 
@@ -172,6 +179,12 @@ def test_host_calls_reject_bad_arguments():
     with pytest.raises(jfa.JfaError) as e:  # lists of a problem that is not sparse
         jfa.sparse_lists(pd, off, m, jfa.KIND_FWD)
     assert e.value.status == jfa.ERR_INVALID_ARG
+    sb, lp, ent = jfa.sparse_lists(p, off, m, jfa.KIND_FWD)
+    bad = lp.copy()
+    bad[1], bad[2] = bad[2], bad[1] - 1  # a decreasing list pointer
+    with pytest.raises(jfa.JfaError) as e:
+        jfa.schedule_sparse(p, off, bad, ent, jfa.KIND_FWD, jfa.ORDER_INORDER, 8)
+    assert e.value.status == jfa.ERR_INVALID_ARG and "list_ptr" in str(e.value)
 
 
 def test_device_calls_reject_missing_lists_before_any_hip_call():
@@ -221,7 +234,7 @@ def test_plan_packs_its_device_arrays(sparse):
     for kind, sch in plan.sched.items():
         if sparse:
             sb, lp, ent = jfa.sparse_lists(p, off, masks, kind)
-            sp, tl = jfa.schedule_sparse(p, off, lp, kind, plan.order, 24)
+            sp, tl = jfa.schedule_sparse(p, off, lp, ent, kind, plan.order, 24)
             for dev, host in zip(sch.lists_dev, (sb, lp, ent)):
                 views.append((dev, host if host.size else np.zeros(1, np.int32)))
         else:

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libjfa.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 CAUSAL, BROADCAST_Q, BLOCK_DIAG64, ROTARY, BLOCK_DIAG, BLOCK_SPARSE = 1, 2, 4, 8, 16, 32
 KIND_FWD, KIND_BWD = 0, 1
-ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG = 0, 1, 2, 3
+ORDER_INORDER, ORDER_ZIGZAG, ORDER_XCD_ZIGZAG, ORDER_FOLDED_ZIGZAG, ORDER_XCD_INORDER = 0, 1, 2, 3, 4
 PASS_DQ, PASS_DKDV, PASS_ALL = 1, 2, 3
 
 
@@ -92,7 +92,7 @@ def lib():
         L.jfa_sparse_lists_count.restype = i32
         L.jfa_sparse_lists.argtypes = [P, vp, vp, i64, i32, vp, vp, vp, i64]
         L.jfa_sparse_lists.restype = i32
-        L.jfa_schedule_sparse.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, i64]
+        L.jfa_schedule_sparse.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, i64]
         L.jfa_schedule_sparse.restype = i32
         L.jfa_fwd_sparse.argtypes = [P, vp, vp, vp, vp, SL, vp, vp, i32, vp, vp, vp]
         L.jfa_fwd_sparse.restype = i32
@@ -180,16 +180,18 @@ def sparse_lists(p: Problem, offsets_host, mask_host, kind: int):
     return seq_base, list_ptr, entries[:ne.value]
 
 
-def schedule_sparse(p: Problem, offsets_host, list_ptr_host, kind: int, order: int,
+def schedule_sparse(p: Problem, offsets_host, list_ptr_host, entries_host, kind: int, order: int,
                     num_slots: int):
-    """Block-sparse host tile schedule -> (slot_ptr int32 [S+1], tiles int32 [N,4])."""
+    """Block-sparse host tile schedule from the step lists of `kind` (list_ptr and
+    entries of sparse_lists) -> (slot_ptr int32 [S+1], tiles int32 [N,4])."""
     off, lp = _host_i32(offsets_host), _host_i32(list_ptr_host)
+    ent = _host_i32(entries_host if entries_host is not None and len(entries_host) else [0])
     n = schedule_count(p, off, kind)
     slot_ptr = np.zeros(num_slots + 1, dtype=np.int32)
     tiles = np.zeros((max(n, 1), 4), dtype=np.int32)
-    _check(lib().jfa_schedule_sparse(ctypes.byref(p), off.ctypes.data, lp.ctypes.data, kind,
-                                     order, num_slots, slot_ptr.ctypes.data, tiles.ctypes.data,
-                                     n))
+    _check(lib().jfa_schedule_sparse(ctypes.byref(p), off.ctypes.data, lp.ctypes.data,
+                                     ent.ctypes.data, kind, order, num_slots,
+                                     slot_ptr.ctypes.data, tiles.ctypes.data, n))
     return slot_ptr, tiles[:n]
 
 
@@ -319,12 +321,11 @@ class Plan:
     n_b = ceil(L_b / 64)), from which the step lists of both kinds are built.
     Builds the FWD and BWD schedules on the host (by default the folded zigzag:
     the work-sorted zigzag deal, with the tiles of a causal (sequence, head) paired
-    so that they run side by side; for BLOCK_SPARSE in-order dispatch, which keeps
-    the tiles of one (sequence, head) on neighbouring slots of one XCD: their
-    step lists differ in length, so a work-sorted deal scatters them and they
-    share less K/V in L2 (the sparse forward is bound by that traffic; in-order
-    measured 4.5% faster per step)), copies them
-    and the offsets to the device, and allocates the dQ workspace.
+    so that they run side by side; for BLOCK_SPARSE the balanced in-order deal,
+    which keeps the tiles of one (sequence, head) together in time and on one XCD:
+    their step lists differ, so a work-sorted deal scatters them and they share
+    less K/V in L2), copies them and the offsets to the device, and allocates the
+    dQ workspace.
     """
 
     def __init__(self, offsets_host, num_heads, head_dim, scale, flags=0, lq=0,
@@ -338,7 +339,7 @@ class Plan:
         if self.sparse:
             block = 64
         if order is None:
-            order = ORDER_INORDER if self.sparse else ORDER_FOLDED_ZIGZAG
+            order = ORDER_XCD_INORDER if self.sparse else ORDER_FOLDED_ZIGZAG
         self.order = order
         self.p = problem(len(L), num_heads, head_dim, int(L.max()) if len(L) else 0,
                          int(off[-1]), scale, flags, lq, rope_base, window, block)
@@ -373,7 +374,7 @@ class Plan:
                 lists = None
                 if self.sparse:
                     lists = sparse_lists(self.p, off, block_mask, kind)
-                    sp, tl = schedule_sparse(self.p, off, lists[1], kind, order, S)
+                    sp, tl = schedule_sparse(self.p, off, lists[1], lists[2], kind, order, S)
                 else:
                     sp, tl = schedule(self.p, off, kind, order, S)
                 sch = Schedule(sp, tl, S)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstring>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -108,11 +109,13 @@ jfa_status check_offsets(const jfa_problem* p, const int32_t* off) {
   return JFA_OK;
 }
 
-// Tiles in generation order (b, then h, then t). With `sp_ptr` (block-sparse step
-// lists, one list per (b, t) in that order, see sparse_lists) a tile's work is its
-// list's length times the 64 keys (or query rows) of each entry.
+// Tiles in generation order (b, then h, then t). With `sp_ptr` and `sp_ent`
+// (block-sparse step lists, one list per (b, t) in that order, see sparse_lists)
+// a key tile's work is its list's length times the 64 query rows of each entry,
+// and a query tile's the 64 keys times the larger number of entries that carry
+// one of its two blocks' bits (its two wave pairs walk those side by side).
 std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t kind,
-                            const int32_t* sp_ptr = nullptr) {
+                            const int32_t* sp_ptr = nullptr, const int32_t* sp_ent = nullptr) {
   const bool causal = p->flags & JFA_CAUSAL;
   const int32_t lq = (p->flags & JFA_BROADCAST_Q) ? p->lq : 0;
   const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
@@ -122,9 +125,22 @@ std::vector<Tile> enumerate(const jfa_problem* p, const int32_t* off, int32_t ki
     const int32_t L = off[b + 1] - off[b];
     if (sp_ptr) {
       const int32_t n = ceil_div(L, rows);
+      std::vector<int32_t> work(size_t(n > 0 ? n : 0));
+      for (int32_t t = 0; t < n; ++t) {
+        const int32_t lo = sp_ptr[u0 + t], hi = sp_ptr[u0 + t + 1];
+        int32_t steps = hi - lo;
+        if (kind == JFA_KIND_FWD) {
+          int32_t c0 = 0, c1 = 0;
+          for (int32_t e = lo; e < hi; ++e) {
+            c0 += (sp_ent[e] >> kSpBit) & 1;
+            c1 += (sp_ent[e] >> (kSpBit + 1)) & 1;
+          }
+          steps = std::max(c0, c1);
+        }
+        work[size_t(t)] = steps * kSpBlock;
+      }
       for (int32_t h = 0; h < p->num_heads; ++h)
-        for (int32_t t = 0; t < n; ++t)
-          tiles.push_back({b, h, t, (sp_ptr[u0 + t + 1] - sp_ptr[u0 + t]) * kSpBlock});
+        for (int32_t t = 0; t < n; ++t) tiles.push_back({b, h, t, work[size_t(t)]});
       u0 += n;
       continue;
     }
@@ -230,7 +246,7 @@ jfa_status deal(const jfa_problem* p, const std::vector<Tile>& tiles, int32_t or
 jfa_status check_deal_args(int64_t count, int32_t order, int32_t num_slots, int32_t* slot_ptr,
                            int32_t* tiles_out, int64_t capacity) {
   if (order != JFA_ORDER_INORDER && order != JFA_ORDER_ZIGZAG && order != JFA_ORDER_XCD_ZIGZAG &&
-      order != JFA_ORDER_FOLDED_ZIGZAG)
+      order != JFA_ORDER_FOLDED_ZIGZAG && order != JFA_ORDER_XCD_INORDER)
     return fail(JFA_ERR_INVALID_ARG, "bad order");
   if (num_slots < 1) return fail(JFA_ERR_INVALID_ARG, "num_slots < 1");
   if (!slot_ptr) return fail(JFA_ERR_INVALID_ARG, "slot_ptr is NULL");
@@ -323,9 +339,9 @@ extern "C" jfa_status jfa_sparse_lists(const jfa_problem* p, const int32_t* offs
 }
 
 extern "C" jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host,
-                                          const int32_t* list_ptr_host, int32_t kind, int32_t order,
-                                          int32_t num_slots, int32_t* slot_ptr, int32_t* tiles_out,
-                                          int64_t capacity) {
+                                          const int32_t* list_ptr_host, const int32_t* entries_host,
+                                          int32_t kind, int32_t order, int32_t num_slots,
+                                          int32_t* slot_ptr, int32_t* tiles_out, int64_t capacity) {
   set_error("");
   if (jfa_status s = check_problem(p)) return s;
   if (!(p->flags & JFA_BLOCK_SPARSE)) return fail(JFA_ERR_INVALID_ARG, "problem is not BLOCK_SPARSE");
@@ -333,8 +349,19 @@ extern "C" jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* o
   if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
   if (jfa_status s = check_deal_args(count, order, num_slots, slot_ptr, tiles_out, capacity)) return s;
   if (!list_ptr_host) return fail(JFA_ERR_INVALID_ARG, "list_ptr_host is NULL");
-  return deal(p, enumerate(p, offsets_host, kind, list_ptr_host), order, num_slots, slot_ptr,
-              tiles_out);
+  // the units (two blocks each) of the offsets: list_ptr_host has one more entry
+  int64_t units = 0;
+  const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
+  for (int32_t b = 0; b < p->num_seqs; ++b)
+    units += ceil_div(int64_t(offsets_host[b + 1]) - offsets_host[b], rows);
+  if (list_ptr_host[0] != 0) return fail(JFA_ERR_INVALID_ARG, "list_ptr[0] != 0");
+  for (int64_t u = 0; u < units; ++u)
+    if (list_ptr_host[u + 1] < list_ptr_host[u])
+      return fail(JFA_ERR_INVALID_ARG, "list_ptr decreases at unit " + std::to_string(u));
+  if (kind == JFA_KIND_FWD && list_ptr_host[units] > 0 && !entries_host)
+    return fail(JFA_ERR_INVALID_ARG, "entries_host is NULL");
+  return deal(p, enumerate(p, offsets_host, kind, list_ptr_host, entries_host), order, num_slots,
+              slot_ptr, tiles_out);
 }
 
 extern "C" jfa_status jfa_schedule(const jfa_problem* p, const int32_t* offsets_host, int32_t kind,
@@ -372,7 +399,37 @@ jfa_status deal(const jfa_problem* p, const std::vector<Tile>& tiles, int32_t or
                 int32_t num_slots, int32_t* slot_ptr, int32_t* tiles_out) {
   std::vector<int32_t> idx;      // tiles in dealing order
   std::vector<int32_t> slot_of;  // slot of idx[j]
-  if (order == JFA_ORDER_XCD_ZIGZAG) {
+  if (order == JFA_ORDER_XCD_INORDER) {
+    // (sequence, head) units in generation order, each to the group of slots
+    // (one group per XCD; one group of all slots when their number is not a
+    // multiple of 8) with the least work dealt so far, the lower group on ties;
+    // the unit's tiles, in order, each to the least-loaded slot of that group,
+    // the lower slot on ties.
+    const int32_t X = num_slots % kXcds ? 1 : kXcds;
+    const int32_t sx = num_slots / X;
+    using Load = std::pair<int64_t, int32_t>;  // (work dealt, slot)
+    std::vector<std::priority_queue<Load, std::vector<Load>, std::greater<Load>>> free_slot(X);
+    for (int32_t x = 0; x < X; ++x)
+      for (int32_t i = 0; i < sx; ++i) free_slot[x].push({0, x * sx + i});
+    std::vector<int64_t> group_work(X, 0);
+    size_t u0 = 0;
+    while (u0 < tiles.size()) {
+      size_t u1 = u0 + 1;
+      while (u1 < tiles.size() && tiles[u1].b == tiles[u0].b && tiles[u1].h == tiles[u0].h) ++u1;
+      int32_t x = 0;
+      for (int32_t y = 1; y < X; ++y)
+        if (group_work[y] < group_work[x]) x = y;
+      for (size_t i = u0; i < u1; ++i) {
+        const Load l = free_slot[x].top();
+        free_slot[x].pop();
+        free_slot[x].push({l.first + tiles[i].work, l.second});
+        group_work[x] += tiles[i].work;
+        idx.push_back(int32_t(i));
+        slot_of.push_back(l.second);
+      }
+      u0 = u1;
+    }
+  } else if (order == JFA_ORDER_XCD_ZIGZAG) {
     constexpr int32_t X = kXcds;
     if (num_slots % X) return fail(JFA_ERR_INVALID_ARG, "XCD_ZIGZAG needs num_slots % 8 == 0");
     const int32_t sx = num_slots / X;
