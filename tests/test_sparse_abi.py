@@ -245,3 +245,26 @@ def test_plan_packs_its_device_arrays(sparse):
     for dev, host in views:
         assert np.array_equal(dev.numpy().reshape(-1), np.asarray(host).reshape(-1))
         assert (dev.data_ptr() - base) % 256 == 0
+
+
+def test_schedule_sparse_entries_argument():
+    """Key-tile schedules need no entries (NULL is accepted); query-tile schedules
+    read them for their work and reject NULL when the lists are not empty."""
+    L = [130, 64]
+    p, off = _problem(L)
+    m = _flat(_masks(L, 7))
+    Lb = jfa.lib()
+    S = 8
+    sp = np.zeros(S + 1, np.int32)
+    for kind in (jfa.KIND_BWD, jfa.KIND_FWD):
+        _, lp, ent = jfa.sparse_lists(p, off, m, kind)
+        n = jfa.schedule_count(p, off, kind)
+        tl = np.zeros((n, 4), np.int32)
+        s = Lb.jfa_schedule_sparse(ctypes.byref(p), off.ctypes.data, lp.ctypes.data, None, kind,
+                                   jfa.ORDER_XCD_INORDER, S, sp.ctypes.data, tl.ctypes.data, n)
+        if kind == jfa.KIND_BWD:
+            assert s == jfa.OK
+            want = jfa.schedule_sparse(p, off, lp, ent, kind, jfa.ORDER_XCD_INORDER, S)
+            assert np.array_equal(sp, want[0]) and np.array_equal(tl, want[1])
+        else:
+            assert s == jfa.ERR_INVALID_ARG and b"entries_host" in Lb.jfa_last_error()
