@@ -310,8 +310,9 @@ __device__ __forceinline__ float load_row(const uint16_t* qrow, const uint16_t* 
   return pair_sum(di);  // Di = rowsum(dO * out)
 }
 
-// SPARSE: the tile streams the key blocks of its step list (block-sparse
-// attention), every step masked as in the forward.
+// SPARSE (block-sparse attention): each wave pair walks the key blocks its own
+// query block attends (the entries of the tile's step list that carry its bit),
+// every step masked as in the forward.
 template <int D, bool CAUSAL, bool ROPE, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(DqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 dq_kernel(DqParams P) {

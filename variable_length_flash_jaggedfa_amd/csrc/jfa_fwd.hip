@@ -213,10 +213,11 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// SPARSE (block-sparse attention over 64-token blocks): a tile's steps walk the
-// key blocks its step list names, in ascending order, instead of the whole
-// sequence; every step is masked, a wave's scores wholly when its query block
-// does not attend the step's key block, and past the sequence end.
+// SPARSE (block-sparse attention over 64-token blocks): instead of the whole
+// sequence, each wave pair of a tile walks the key blocks its own query block
+// attends (the entries of the tile's step list that carry its bit), in
+// ascending order; every step is masked (past the sequence end and, with
+// CAUSAL, after the query).
 template <int D, bool CAUSAL, bool BCAST, bool WIN, bool SPARSE = false>
 __global__ void __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_kernel(FwdParams P) {
