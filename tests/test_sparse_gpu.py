@@ -138,6 +138,29 @@ def test_slot_counts_do_not_change_results(gpu, D, causal):
             assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_orders_do_not_change_results(gpu, causal):
+    """Every dealing order gives the bits of the default (balanced in-order)
+    order: a tile's results do not depend on its slot or on the tiles before it."""
+    import torch
+    import variable_length_flash_jaggedfa_amd as jfa
+    rng = np.random.default_rng(61)
+    case = _case_with_mask(LENGTHS + [900, 5], 128, 13, lambda b, n: rng.random((n, n)) < 0.35,
+                           causal)
+    a = GpuRun(case, gpu)
+    assert a.plan.order == jfa.ORDER_XCD_INORDER
+    oa, la = a.forward()
+    ga = [x.clone() for x in a.backward()]
+    for order in (jfa.ORDER_INORDER, jfa.ORDER_ZIGZAG, jfa.ORDER_XCD_ZIGZAG,
+                  jfa.ORDER_FOLDED_ZIGZAG):
+        log(f"sparse causal={causal} order={order}")
+        b = GpuRun(case, gpu, order=order)
+        ob, lb = b.forward()
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
+        for x, y in zip(ga, b.backward()):
+            assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("lengths", [[0, 0, 0], []], ids=["all-empty", "no-sequences"])
 def test_empty_batches(gpu, lengths):
     """A batch of empty sequences and a batch of none: forward and backward run
