@@ -352,7 +352,7 @@ def main():
         return
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(sequences would shard across GPUs with no exchange except one dQ all-reduce "
               "for broadcast-Q)", file=sys.stderr)
         sys.exit(2)

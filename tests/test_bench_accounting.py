@@ -4,6 +4,8 @@ attention masks, built per sequence from the mask definitions the oracle
 applies: causal keeps j <= i, a window W also keeps only j > i - W, block
 diagonal keeps i and j in the same block, broadcast attends Lq dense queries to
 every key."""
+import os
+
 import numpy as np
 import pytest
 
@@ -98,3 +100,15 @@ def test_causal_block_sparse_pairs():
         want += int(keep.sum())
     assert bench.sparse_pairs(L, flat, causal=True) == want == \
         A.pair_count(L, causal=True, masks=masks)
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: asked for more it says so and exits with status 2
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
