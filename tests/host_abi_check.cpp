@@ -137,7 +137,7 @@ static void fuzz_scheduler() {
     const int32_t S = 1 + int(rng() % 600);
     for (int32_t kind : {JFA_KIND_FWD, JFA_KIND_BWD})
       for (int32_t order : {JFA_ORDER_INORDER, JFA_ORDER_ZIGZAG, JFA_ORDER_XCD_ZIGZAG,
-                            JFA_ORDER_FOLDED_ZIGZAG})
+                            JFA_ORDER_FOLDED_ZIGZAG, JFA_ORDER_XCD_INORDER})
         check_schedule(p, off, kind, order, order == JFA_ORDER_XCD_ZIGZAG ? S / 8 * 8 + 8 * (S < 8) : S,
                        rng);
     // a bad order, too small a capacity, and broken offsets are rejected
@@ -291,8 +291,71 @@ static void limits() {
   CHECK(jfa_schedule_count(nullptr, off.data(), JFA_KIND_FWD, &n) == JFA_ERR_INVALID_ARG, "null");
 }
 
+// Block-sparse lists and schedules on random masks: the counts agree with the
+// lists, every list is ascending with only valid bits, every tile is dealt once,
+// and a query tile's work is 64 x the longer of its two blocks' lists.
+static void fuzz_sparse() {
+  std::mt19937 rng(99);
+  for (int it = 0; it < 200; ++it) {
+    const int B = int(rng() % 12);
+    const int H = 1 + int(rng() % 3);
+    std::vector<int32_t> off(size_t(B) + 1, 0);
+    int maxL = 0;
+    int64_t mbytes = 0;
+    for (int b = 0; b < B; ++b) {
+      const int L = (rng() % 5 == 0) ? 0 : 1 + int(rng() % 900);
+      off[b + 1] = off[b] + L;
+      maxL = std::max(maxL, L);
+      const int64_t nb = (L + 63) / 64;
+      mbytes += nb * nb;
+    }
+    std::vector<uint8_t> mask(size_t(std::max<int64_t>(mbytes, 1)));
+    const int density = int(rng() % 101);
+    for (auto& x : mask) x = uint8_t(int(rng() % 100) < density);
+    const uint32_t flags = JFA_BLOCK_SPARSE | ((rng() % 2) ? JFA_CAUSAL : 0u);
+    jfa_problem p = make(B, H, 128, maxL, off[B], flags, 0, 0, 64);
+    for (int32_t kind : {JFA_KIND_FWD, JFA_KIND_BWD}) {
+      int64_t nu = -1, ne = -1;
+      CHECK(jfa_sparse_lists_count(&p, off.data(), mask.data(), mbytes, kind, &nu, &ne) == JFA_OK,
+            "sparse count");
+      if (nu < 0) continue;
+      std::vector<int32_t> sb(size_t(B) + 1), lp(size_t(nu) + 1), ent(size_t(std::max<int64_t>(ne, 1)));
+      CHECK(jfa_sparse_lists(&p, off.data(), mask.data(), mbytes, kind, sb.data(), lp.data(),
+                             ent.data(), ne) == JFA_OK, "sparse lists");
+      CHECK(lp[0] == 0 && lp[nu] == ne && sb[B] == nu, "list ends");
+      for (int64_t u = 0; u < nu; ++u)
+        for (int32_t e = lp[u]; e < lp[u + 1]; ++e) {
+          CHECK((ent[e] >> 30) == 0 && (ent[e] >> 28) != 0, "entry bits");
+          if (e > lp[u]) CHECK((ent[e] & 0x0FFFFFFF) > (ent[e - 1] & 0x0FFFFFFF), "ascending");
+        }
+      int64_t n = 0;
+      jfa_schedule_count(&p, off.data(), kind, &n);
+      const int32_t S = 1 + int(rng() % 100);
+      for (int32_t order : {JFA_ORDER_INORDER, JFA_ORDER_ZIGZAG, JFA_ORDER_FOLDED_ZIGZAG,
+                            JFA_ORDER_XCD_INORDER}) {
+        std::vector<int32_t> sp(size_t(S) + 1), tl(size_t(std::max<int64_t>(n, 1)) * 4);
+        CHECK(jfa_schedule_sparse(&p, off.data(), lp.data(), ent.data(), kind, order, S, sp.data(),
+                                  tl.data(), n) == JFA_OK, "sparse schedule order %d", order);
+        CHECK(sp[0] == 0 && sp[S] == n, "sparse slot_ptr ends");
+        int64_t work = 0, want = 0;
+        for (int64_t i = 0; i < n; ++i) work += tl[4 * i + 3];
+        for (int64_t u = 0; u < nu; ++u) {
+          int32_t c0 = 0, c1 = 0;
+          for (int32_t e = lp[u]; e < lp[u + 1]; ++e) {
+            c0 += (ent[e] >> 28) & 1;
+            c1 += (ent[e] >> 29) & 1;
+          }
+          want += int64_t(H) * 64 * (kind == JFA_KIND_FWD ? std::max(c0, c1) : lp[u + 1] - lp[u]);
+        }
+        CHECK(work == want, "sparse work %lld vs %lld", (long long)work, (long long)want);
+      }
+    }
+  }
+}
+
 int main() {
   fuzz_scheduler();
+  fuzz_sparse();
   entry_points();
   limits();
   if (g_failed) {
