@@ -55,11 +55,15 @@
  *               is enqueued. jfa_last_error() gives a thread-local message.
  *   Threads     Calls are thread-safe; calls on one stream execute in order.
  *   Diagnostics Read from the environment on every call:
- *               JFA_VALIDATE=1  jfa_fwd / jfa_bwd / jfa_bwd_passes first
- *                 synchronise `stream`, copy the device offsets and schedules back
- *                 and check the precondition the kernels rely on (offsets start at
- *                 0, never decrease, end at total_kv, no length above max_len; the
- *                 tiles cover every (sequence, head, tile index) exactly once). A mismatch
+ *               JFA_VALIDATE=1  jfa_fwd / jfa_bwd / jfa_bwd_passes (and the
+ *                 sparse calls) first synchronise `stream`, copy the device offsets
+ *                 and schedules back and check the precondition the kernels rely on
+ *                 (offsets start at 0, never decrease, end at total_kv, no length
+ *                 above max_len; the tiles cover every (sequence, head, tile index)
+ *                 exactly once; block-sparse step lists: seq_base gives each
+ *                 sequence's first unit, list_ptr starts at 0 and never decreases,
+ *                 every entry names a block pair of its sequence, ascending within
+ *                 its list). A mismatch
  *                 returns JFA_ERR_INVALID_ARG with nothing enqueued. Costs a
  *                 synchronisation and blocking copies: for debugging.
  *               JFA_LOG=1  one line per call of those entry points on stderr.
@@ -343,7 +347,7 @@ jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host
 /* Block-sparse forward: as jfa_fwd with the FWD step lists (device) and no
  * workspace; a tile visits only the key blocks its list names. Preconditions as
  * for jfa_fwd, and the lists are those of the offsets and mask the schedule was
- * built from (not checked on the device). */
+ * built from (not checked on the device; JFA_VALIDATE=1 checks their structure). */
 jfa_status jfa_fwd_sparse(const jfa_problem* p, const void* q, const void* k, const void* v,
                           const int32_t* offsets_dev, const jfa_sparse_lists_dev* lists,
                           const int32_t* slot_ptr_dev, const int32_t* tiles_dev,

@@ -161,6 +161,50 @@ def test_orders_do_not_change_results(gpu, causal):
             assert torch.equal(x, y)
 
 
+def test_validate_checks_the_step_lists(gpu, monkeypatch):
+    """With JFA_VALIDATE=1 valid lists give the same bits; lists corrupted on the
+    device (a list pointer past its successor, an entry naming a block past its
+    sequence, a wrong first unit) are refused before any launch, forward and
+    backward."""
+    import torch
+    import variable_length_flash_jaggedfa_amd as jfa
+    rng = np.random.default_rng(71)
+    case = _case_with_mask([130, 300, 64, 511], 64, 14, lambda b, n: rng.random((n, n)) < 0.5)
+    run = GpuRun(case, gpu)
+    out, lse = run.forward()
+    grads = [x.clone() for x in run.backward()]
+    monkeypatch.setenv("JFA_VALIDATE", "1")
+    out2, lse2 = run.plan.forward(run.q, run.k, run.v)
+    grads2 = run.plan.backward(run.q, run.k, run.v, out2, run.do, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for a_, b_ in zip(grads, grads2):
+        assert torch.equal(a_, b_)
+    for kind in (jfa.KIND_FWD, jfa.KIND_BWD):
+        sch = run.plan.sched[kind]
+        good = sch.lists_dev
+        sb, lp, ent = (t.clone() for t in good)
+        bad_lp = lp.clone()
+        bad_lp[1] = int(lp[2]) + 1
+        bad_ent = ent.clone()
+        bad_ent[0] = (int(ent[0]) & ~((1 << 28) - 1)) | 9  # block 9 of a 130-token sequence
+        bad_sb = sb.clone()
+        bad_sb[1] += 1
+        for lists in ((sb, bad_lp, ent), (sb, lp, bad_ent), (bad_sb, lp, ent)):
+            sch.lists_dev = lists
+            try:
+                with pytest.raises(jfa.JfaError) as e:
+                    if kind == jfa.KIND_FWD:
+                        run.plan.forward(run.q, run.k, run.v, out=out2, lse=lse2)
+                    else:
+                        run.plan.backward(run.q, run.k, run.v, out2, run.do, lse2)
+                assert e.value.status == jfa.ERR_INVALID_ARG and "step lists" in str(e.value)
+            finally:
+                sch.lists_dev = good
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)  # the refused calls wrote nothing
+
+
 @pytest.mark.parametrize("lengths", [[0, 0, 0], []], ids=["all-empty", "no-sequences"])
 def test_empty_batches(gpu, lengths):
     """A batch of empty sequences and a batch of none: forward and backward run

@@ -53,7 +53,8 @@ jfa_status check_workspace(void* workspace, size_t workspace_bytes, size_t ws) {
 //   JFA_VALIDATE=1  before launching, copy the device offsets and schedule back
 //                   (a stream synchronisation and blocking copies) and check the
 //                   precondition the kernels rely on: under these device offsets
-//                   the tiles cover every (sequence, head, tile index) exactly once.
+//                   the tiles cover every (sequence, head, tile index) exactly once;
+//                   block-sparse step lists are checked against the offsets too.
 //   JFA_LOG=1       one line per entry-point call on stderr.
 bool env_on(const char* name) {
   const char* v = std::getenv(name);
@@ -128,6 +129,57 @@ jfa_status validate_schedule(const jfa_problem* p, const int32_t* offsets_dev,
     char& mark = seen[size_t(h * first[nseq] + first[b] + t)];
     if (mark) return bad("tile " + std::to_string(i) + " appears twice");
     mark = 1;
+  }
+  return JFA_OK;
+}
+
+// JFA_VALIDATE for block-sparse step lists of `kind` on the device: copied back
+// and checked against the device offsets for what the kernels rely on: seq_base
+// holds each sequence's first unit (two 64-token blocks per unit), list_ptr
+// starts at 0 and never decreases, and every entry carries one or both block
+// bits, no other high bit, a block of its own sequence (and bit kSpBit + 1 only
+// where the unit has a second block), ascending within its list.
+jfa_status validate_lists(const jfa_problem* p, const int32_t* offsets_dev,
+                          const jfa_sparse_lists_dev* sp, int32_t kind, void* stream) {
+  const char* which = kind == JFA_KIND_FWD ? "forward" : "backward";
+  auto bad = [&](const std::string& m) {
+    return fail(JFA_ERR_INVALID_ARG, std::string("JFA_VALIDATE: ") + which + " step lists: " + m);
+  };
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: stream synchronisation failed");
+  const int64_t B = p->num_seqs;
+  std::vector<int32_t> off(size_t(B) + 1), base(size_t(B) + 1);
+  if (hipMemcpy(off.data(), offsets_dev, off.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(base.data(), sp->seq_base, base.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of offsets or seq_base failed");
+  int64_t units = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    if (base[b] != units) return bad("seq_base[" + std::to_string(b) + "] is not the sequence's first unit");
+    units += (int64_t(off[b + 1]) - off[b] + 2 * kSpBlock - 1) / (2 * kSpBlock);
+  }
+  if (base[B] != units) return bad("seq_base[B] is not the number of units");
+  std::vector<int32_t> lp(size_t(units) + 1);
+  if (hipMemcpy(lp.data(), sp->list_ptr, lp.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of list_ptr failed");
+  if (lp[0] != 0) return bad("list_ptr[0] != 0");
+  for (int64_t u = 0; u < units; ++u)
+    if (lp[u + 1] < lp[u]) return bad("list_ptr decreases at unit " + std::to_string(u));
+  std::vector<int32_t> ent(static_cast<size_t>(lp[units]));
+  if (!ent.empty() &&
+      hipMemcpy(ent.data(), sp->entries, ent.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of entries failed");
+  int64_t u = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t nb = (int64_t(off[b + 1]) - off[b] + kSpBlock - 1) / kSpBlock;
+    for (int64_t t = 0; t < (nb + 1) / 2; ++t, ++u)
+      for (int32_t e = lp[u]; e < lp[u + 1]; ++e) {
+        const int32_t x = ent[size_t(e)], blk = x & kSpIdx, bits = (x >> kSpBit) & 3;
+        if ((x >> (kSpBit + 2)) != 0 || bits == 0 || blk >= nb || ((bits & 2) && 2 * t + 1 >= nb))
+          return bad("entry " + std::to_string(e) + " of unit " + std::to_string(u) +
+                     " does not name a block pair of its sequence");
+        if (e > lp[u] && blk <= (ent[size_t(e) - 1] & kSpIdx))
+          return bad("the list of unit " + std::to_string(u) + " is not ascending");
+      }
   }
   return JFA_OK;
 }
@@ -235,6 +287,9 @@ jfa_status fwd_impl(const jfa_problem* p, const void* q, const void* k, const vo
     if (jfa_status s = validate_schedule(p, offsets_dev, slot_ptr_dev, tiles_dev, num_slots,
                                          JFA_KIND_FWD, stream))
       return s;
+    if (sp) {
+      if (jfa_status s = validate_lists(p, offsets_dev, sp, JFA_KIND_FWD, stream)) return s;
+    }
   }
   char* ws = static_cast<char*>(workspace);
   if (tiled_blocks(p) && p->total_kv > 0) {
@@ -350,6 +405,12 @@ jfa_status bwd_impl(const jfa_problem* p, const void* q, const void* k, const vo
       if (jfa_status s = validate_schedule(p, offsets_dev, q_slot_ptr_dev, q_tiles_dev,
                                            q_num_slots, JFA_KIND_FWD, stream))
         return s;
+    }
+    if (q_sp) {
+      if (jfa_status s = validate_lists(p, offsets_dev, q_sp, JFA_KIND_FWD, stream)) return s;
+    }
+    if (kv_sp) {
+      if (jfa_status s = validate_lists(p, offsets_dev, kv_sp, JFA_KIND_BWD, stream)) return s;
     }
   }
   a.di = static_cast<float*>(workspace);
