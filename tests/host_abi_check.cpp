@@ -243,6 +243,50 @@ static void entry_points() {
                          JFA_PASS_ALL, nullptr) == JFA_ERR_INVALID_ARG, "validate slot_ptr");
   }
   CHECK(g_launches == before, "nothing launched on validation errors");
+
+  // JFA_VALIDATE with block-sparse step lists: good lists pass; a decreasing list
+  // pointer, an over-long list (checked before any entry is read, so the copy
+  // stays inside the entries array) and an entry past its sequence are refused
+  {
+    const std::vector<int32_t> so = {0, 130, 130, 450};
+    jfa_problem sp_p = make(3, 2, 64, 320, 450, JFA_BLOCK_SPARSE, 0, 0, 64);
+    std::vector<uint8_t> mk;
+    for (int64_t nb : {3, 0, 5})
+      for (int64_t i = 0; i < nb * nb; ++i) mk.push_back(uint8_t((i * 7) % 3 != 0));
+    int64_t nu = 0, ne = 0;
+    CHECK(jfa_sparse_lists_count(&sp_p, so.data(), mk.data(), int64_t(mk.size()), JFA_KIND_FWD, &nu,
+                                 &ne) == JFA_OK, "validate sparse count");
+    std::vector<int32_t> sb(4), lp(size_t(nu) + 1), en(size_t(std::max<int64_t>(ne, 1)));
+    CHECK(jfa_sparse_lists(&sp_p, so.data(), mk.data(), int64_t(mk.size()), JFA_KIND_FWD, sb.data(),
+                           lp.data(), en.data(), ne) == JFA_OK, "validate sparse lists");
+    int64_t nt = 0;
+    jfa_schedule_count(&sp_p, so.data(), JFA_KIND_FWD, &nt);
+    const int32_t SS = 4;
+    std::vector<int32_t> ssp(SS + 1), stl(size_t(std::max<int64_t>(nt, 1)) * 4);
+    CHECK(jfa_schedule_sparse(&sp_p, so.data(), lp.data(), en.data(), JFA_KIND_FWD,
+                              JFA_ORDER_XCD_INORDER, SS, ssp.data(), stl.data(), nt) == JFA_OK,
+          "validate sparse schedule");
+    auto fwd_with = [&](const std::vector<int32_t>& l, const std::vector<int32_t>& e) {
+      jfa_sparse_lists_dev d{sb.data(), l.data(), e.data()};
+      return jfa_fwd_sparse(&sp_p, buf[0], buf[1], buf[2], so.data(), &d, ssp.data(), stl.data(), SS,
+                            buf[3], lse, nullptr);
+    };
+    before = g_launches;
+    CHECK(fwd_with(lp, en) == JFA_OK, "validated sparse fwd");
+    CHECK(g_launches == before + 1, "validated sparse call launches");
+    before = g_launches;
+    std::vector<int32_t> l2 = lp;
+    l2[1] = l2[2] + 1;
+    CHECK(fwd_with(l2, en) == JFA_ERR_INVALID_ARG, "validate decreasing list_ptr");
+    l2 = lp;
+    for (size_t i = 1; i < l2.size(); ++i) l2[i] += 1000;  // every later list 1000 longer
+    l2[0] = 0;
+    CHECK(fwd_with(l2, en) == JFA_ERR_INVALID_ARG, "validate over-long list");
+    std::vector<int32_t> e2 = en;
+    e2[0] = (e2[0] & ~((1 << 28) - 1)) | 7;  // block 7 of a 3-block sequence
+    CHECK(fwd_with(lp, e2) == JFA_ERR_INVALID_ARG, "validate entry past its sequence");
+    CHECK(g_launches == before, "nothing launched on list validation errors");
+  }
   unsetenv("JFA_VALIDATE");
 
   // broadcast-Q, block-diagonal and rotary problems: workspace sizes and launches

@@ -162,8 +162,16 @@ jfa_status validate_lists(const jfa_problem* p, const int32_t* offsets_dev,
   if (hipMemcpy(lp.data(), sp->list_ptr, lp.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(JFA_ERR_HIP, "JFA_VALIDATE: copy of list_ptr failed");
   if (lp[0] != 0) return bad("list_ptr[0] != 0");
-  for (int64_t u = 0; u < units; ++u)
-    if (lp[u + 1] < lp[u]) return bad("list_ptr decreases at unit " + std::to_string(u));
+  // a list names each block of its sequence at most once: bound every list (and
+  // so the entries copied below) before reading any entry
+  for (int64_t b = 0, u = 0; b < B; ++b) {
+    const int64_t nb = (int64_t(off[b + 1]) - off[b] + kSpBlock - 1) / kSpBlock;
+    for (int64_t t = 0; t < (nb + 1) / 2; ++t, ++u) {
+      if (lp[u + 1] < lp[u]) return bad("list_ptr decreases at unit " + std::to_string(u));
+      if (lp[u + 1] - lp[u] > nb)
+        return bad("the list of unit " + std::to_string(u) + " is longer than its sequence's blocks");
+    }
+  }
   std::vector<int32_t> ent(static_cast<size_t>(lp[units]));
   if (!ent.empty() &&
       hipMemcpy(ent.data(), sp->entries, ent.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
