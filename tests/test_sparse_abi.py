@@ -185,6 +185,11 @@ def test_host_calls_reject_bad_arguments():
     with pytest.raises(jfa.JfaError) as e:
         jfa.schedule_sparse(p, off, bad, ent, jfa.KIND_FWD, jfa.ORDER_INORDER, 8)
     assert e.value.status == jfa.ERR_INVALID_ARG and "list_ptr" in str(e.value)
+    long_ = lp.copy()
+    long_[1:] += 50  # the first list longer than its sequence has blocks
+    with pytest.raises(jfa.JfaError) as e:
+        jfa.schedule_sparse(p, off, long_, ent, jfa.KIND_FWD, jfa.ORDER_INORDER, 8)
+    assert e.value.status == jfa.ERR_INVALID_ARG and "longer" in str(e.value)
 
 
 def test_device_calls_reject_missing_lists_before_any_hip_call():

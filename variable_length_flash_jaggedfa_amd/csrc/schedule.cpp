@@ -349,15 +349,21 @@ extern "C" jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* o
   if (jfa_status s = jfa_schedule_count(p, offsets_host, kind, &count)) return s;
   if (jfa_status s = check_deal_args(count, order, num_slots, slot_ptr, tiles_out, capacity)) return s;
   if (!list_ptr_host) return fail(JFA_ERR_INVALID_ARG, "list_ptr_host is NULL");
-  // the units (two blocks each) of the offsets: list_ptr_host has one more entry
-  int64_t units = 0;
+  // the units (two blocks each) of the offsets: list_ptr_host has one more
+  // entry; a list names each block of its sequence at most once
   const int32_t rows = jfa_tile_rows(kind, p->head_dim, p->flags);
-  for (int32_t b = 0; b < p->num_seqs; ++b)
-    units += ceil_div(int64_t(offsets_host[b + 1]) - offsets_host[b], rows);
   if (list_ptr_host[0] != 0) return fail(JFA_ERR_INVALID_ARG, "list_ptr[0] != 0");
-  for (int64_t u = 0; u < units; ++u)
-    if (list_ptr_host[u + 1] < list_ptr_host[u])
-      return fail(JFA_ERR_INVALID_ARG, "list_ptr decreases at unit " + std::to_string(u));
+  int64_t units = 0;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    const int64_t L = int64_t(offsets_host[b + 1]) - offsets_host[b];
+    for (int64_t t = 0, n = ceil_div(L, rows); t < n; ++t, ++units) {
+      const int64_t len = int64_t(list_ptr_host[units + 1]) - list_ptr_host[units];
+      if (len < 0) return fail(JFA_ERR_INVALID_ARG, "list_ptr decreases at unit " + std::to_string(units));
+      if (len > sp_blocks(L))
+        return fail(JFA_ERR_INVALID_ARG, "the list of unit " + std::to_string(units) +
+                                             " is longer than its sequence's blocks");
+    }
+  }
   if (kind == JFA_KIND_FWD && list_ptr_host[units] > 0 && !entries_host)
     return fail(JFA_ERR_INVALID_ARG, "entries_host is NULL");
   return deal(p, enumerate(p, offsets_host, kind, list_ptr_host, entries_host), order, num_slots,
