@@ -338,7 +338,8 @@ jfa_status jfa_sparse_lists(const jfa_problem* p, const int32_t* offsets_host,
  * 64 times its list's length (the dK/dV pass walks the whole list); a FWD tile's
  * is 64 times the larger number of its entries that carry bit 28 or bit 29 (the
  * forward and the dQ pass walk the two blocks' entries side by side). Returns
- * INVALID_ARG if list_ptr_host[0] != 0 or the list pointers decrease. Host only. */
+ * INVALID_ARG if list_ptr_host[0] != 0, the list pointers decrease or a list is
+ * longer than its sequence has 64-token blocks. Host only. */
 jfa_status jfa_schedule_sparse(const jfa_problem* p, const int32_t* offsets_host,
                                const int32_t* list_ptr_host, const int32_t* entries_host,
                                int32_t kind, int32_t order, int32_t num_slots, int32_t* slot_ptr,
