@@ -117,6 +117,22 @@ def padded_ratio(case, w):
     return float(len(L) * m * m) / float((L * L).sum())
 
 
+def predicted_balance(plan, jfa):
+    """The deal's own prediction of its balance: per schedule kind, the busiest
+    slot's summed tile work (the scheduler's estimates) over the mean slot's.
+    Plans without a schedule (64-token blocks) give an empty dict."""
+    res = {}
+    for kind, tag in ((jfa.KIND_FWD, "fwd"), (jfa.KIND_BWD, "bwd")):
+        sc = plan.sched.get(kind)
+        if sc is None or len(sc.tiles) == 0:
+            continue
+        w_ = np.concatenate([[0], np.cumsum(np.asarray(sc.tiles)[:, 3].astype(np.int64))])
+        ptr = np.asarray(sc.slot_ptr, dtype=np.int64)
+        loads = w_[ptr[1:]] - w_[ptr[:-1]]
+        res[tag] = round(float(loads.max() / loads.mean()), 4)
+    return res
+
+
 def cpu_baseline(case, variants, pool, budget_s=16.0):
     """The fp64 oracle (forward and backward of whole sequences, all heads) on a
     bounded random sample of the same batch, one single-threaded worker process
@@ -581,6 +597,9 @@ def main():
         if not r["fused_bwd"]:
             per_variant[tag]["dq_ms"] = round(float(np.median(r["dq_ms"])), 4)
             per_variant[tag]["dkdv_ms"] = round(float(np.median(r["dkdv_ms"])), 4)
+        bal = predicted_balance(r["plan"], jfa)
+        if bal:
+            per_variant[tag]["predicted_max_over_mean_load"] = bal
 
     compare = None
     if alt is not None:
@@ -610,14 +629,8 @@ def main():
             compare[name]["total_iqr"] = [round(float(np.percentile(d["total"], 25)), 4),
                                           round(float(np.percentile(d["total"], 75)), 4)]
         for name, plans in alt.items():
-            # predicted balance: busiest slot's KV work over the mean, per schedule kind
-            for kind, tag in ((jfa.KIND_FWD, "fwd"), (jfa.KIND_BWD, "bwd")):
-                sc = plans[0].sched.get(kind)
-                if sc is None or len(sc.tiles) == 0:
-                    continue
-                w_ = np.concatenate([[0], np.cumsum(sc.tiles[:, 3].astype(np.int64))])
-                loads = w_[sc.slot_ptr[1:]] - w_[sc.slot_ptr[:-1]]
-                compare[name][f"{tag}_max_over_mean_load"] = round(float(loads.max() / loads.mean()), 4)
+            for tag, x in predicted_balance(plans[0], jfa).items():
+                compare[name][f"{tag}_max_over_mean_load"] = x
         base = compare["inorder"]["total"]
         for name in compare:
             compare[name]["speedup_vs_inorder"] = round(base / compare[name]["total"], 4)

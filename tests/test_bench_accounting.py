@@ -112,3 +112,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=root)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_predicted_balance_of_a_hand_dealt_schedule():
+    """Busiest slot over the mean slot, from the tiles' work column: slots hold
+    works (3, 1), (2) and () -> loads 4, 2, 0, mean 2, ratio 2; a kind without
+    tiles is left out."""
+    from types import SimpleNamespace
+
+    import variable_length_flash_jaggedfa_amd as jfa
+    tiles = np.array([[0, 0, 0, 3], [0, 0, 1, 1], [1, 0, 0, 2]], dtype=np.int32)
+    fwd = jfa.Schedule(np.array([0, 2, 3, 3], dtype=np.int32), tiles, 3)
+    bwd = jfa.Schedule(np.array([0, 0], dtype=np.int32), np.zeros((0, 4), np.int32), 1)
+    plan = SimpleNamespace(sched={jfa.KIND_FWD: fwd, jfa.KIND_BWD: bwd})
+    assert bench.predicted_balance(plan, jfa) == {"fwd": 2.0}
+    assert bench.predicted_balance(SimpleNamespace(sched={}), jfa) == {}
