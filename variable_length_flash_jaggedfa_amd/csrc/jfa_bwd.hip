@@ -425,7 +425,12 @@ dq_kernel(DqParams P) {
           __builtin_amdgcn_s_setprio(1);
           dq_scores<D>(kst, lo, qf, dof, ndi, sc, dp);
           __builtin_amdgcn_s_setprio(0);
-          dq_softmax<D, true, CAUSAL, false>(sc, dp, lse2, P.c, g, key, L, qpos, pds, 0, lo, pds, acc);
+          // masked only where a key can be past the end or after a query (as in
+          // the forward)
+          if (key + C::BN > L || (CAUSAL && key + C::BN - 1 > q_first + w * 32))
+            dq_softmax<D, true, CAUSAL, false>(sc, dp, lse2, P.c, g, key, L, qpos, pds, 0, lo, pds, acc);
+          else
+            dq_softmax<D, false, CAUSAL, false>(sc, dp, lse2, P.c, g, key, L, qpos, pds, 0, lo, pds, acc);
           dq_accumulate<D>(kst, lo, pds, acc);
         }
       }

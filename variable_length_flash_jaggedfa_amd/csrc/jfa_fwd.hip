@@ -335,7 +335,11 @@ fwd_kernel(FwdParams P) {
           const uint16_t* stage = lds + (2 * pr + (st & 1)) * C::STAGE;
           f32x16 sc[C::KB], sn[C::KB];
           scores<D>(stage, qf, sc, li, g);
-          mask_scores<D, CAUSAL, false>(sc, g, key, L, qm, 0);
+          // only the sequence's last block holds keys past its end, and with
+          // CAUSAL only a step reaching past the wave's first row holds keys
+          // after a query: the other steps need no mask
+          if (key + C::BN > L || (CAUSAL && key + C::BN - 1 > q_first + w * 32))
+            mask_scores<D, CAUSAL, false>(sc, g, key, L, qm, 0);
           const float mx = pair_max(row_max<D>(sc)) * P.c;
           update_max<D>(mx, m, l, o);
           fwd_step<D, false, false, CAUSAL, false>(stage + C::TILE, nullptr, qf, sc, sn, o, m, l, P.c,
